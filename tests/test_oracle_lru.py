@@ -1,0 +1,83 @@
+"""Pins for the oracle's shared LRU cache simulator.
+
+Checked against a textbook ordered-dict LRU (tests/textbook_lru.py) fed the
+same access order, and against cases whose hit counts are known in closed form.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.textbook_lru import TextbookLRU
+
+
+def _drive_both(S, E, L, steps, seed, max_active):
+    r = np.random.default_rng(seed)
+    sim = oracle.SharedLRU(S)
+    tb = TextbookLRU(S)
+    for step in range(steps):
+        for layer in range(L):
+            n = int(r.integers(1, max_active + 1))
+            experts = sorted(r.choice(E, size=n, replace=False).tolist())
+            waves, recs = sim.resolve(step, layer, E, experts)
+            keys = [layer * E + e for e in experts]
+            hits0 = [kk for kk in keys if kk in tb.od]
+            seq = sorted(hits0) + sorted(kk for kk in keys if kk not in tb.od)
+            assert [rc.key for rc in recs] == seq
+            for pos, (rc, kk) in enumerate(zip(recs, seq)):
+                hit, slot, victim = tb.access(kk)
+                assert (rc.hit, rc.slot, rc.victim, rc.wave) == (int(hit), slot, victim, pos // S)
+            # each wave's experts are resident together when that wave runs
+            for w in waves:
+                assert len(w) <= S
+                assert len({s for _, s in w}) == len(w)
+    return sim
+
+
+@pytest.mark.parametrize("S,E,L,max_active", [(8, 16, 1, 14), (4, 10, 3, 6), (16, 32, 4, 10), (1, 5, 2, 3)])
+def test_lru_matches_textbook(S, E, L, max_active):
+    _drive_both(S, E, L, steps=60, seed=S * 100 + E, max_active=max_active)
+
+
+def test_lru_cyclic_s_plus_one_never_hits():
+    S = 5
+    sim = oracle.SharedLRU(S)
+    for step in range(40):
+        _, recs = sim.resolve(step, 0, 100, [step % (S + 1)])
+        assert recs[0].hit == 0
+        if step >= S:
+            assert recs[0].victim == (step + 1) % (S + 1)  # the least recent key is the next one wanted
+
+
+def test_lru_compulsory_only():
+    S, E = 16, 12
+    sim = oracle.SharedLRU(S)
+    r = np.random.default_rng(3)
+    for step in range(50):
+        sim.resolve(step, 0, E, sorted(r.choice(E, 4, replace=False).tolist()))
+    misses = sum(1 for rc in sim.trace if not rc.hit)
+    assert misses == len({rc.key for rc in sim.trace})  # <= S distinct keys: only first-touch misses
+
+
+def test_lru_working_set_resident_after_step():
+    S, E, L = 8, 32, 3
+    sim = oracle.SharedLRU(S)
+    r = np.random.default_rng(4)
+    for step in range(30):
+        for layer in range(L):
+            ex = sorted(r.choice(E, int(r.integers(1, S + 1)), replace=False).tolist())
+            sim.resolve(step, layer, E, ex)
+            assert all(layer * E + e in sim.key_slot for e in ex)
+
+
+def test_lru_waves_and_hits_first():
+    S, E = 3, 10
+    sim = oracle.SharedLRU(S)
+    sim.resolve(0, 0, E, [1, 2])
+    waves, recs = sim.resolve(1, 0, E, [0, 1, 2, 3, 4, 5])
+    # hits (1, 2) first, then misses ascending; waves of S consecutive accesses
+    assert [rc.key for rc in recs] == [1, 2, 0, 3, 4, 5]
+    assert [rc.wave for rc in recs] == [0, 0, 0, 1, 1, 1]
+    assert [rc.hit for rc in recs] == [1, 1, 0, 0, 0, 0]
+    # wave 1 evicts the entries of wave 0, least recent first
+    assert [rc.victim for rc in recs[3:]] == [1, 2, 0]
+    assert waves == [[(1, 0), (2, 1), (0, 2)], [(3, 0), (4, 1), (5, 2)]]
