@@ -1,0 +1,275 @@
+/*
+ * moe.h -- C ABI of the routed expert layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer: a router picks k experts per token, the selected (layer, expert)
+ * pairs are resolved against a shared LRU expert cache held in GPU memory,
+ * missing experts are copied from a pinned host-resident pool, tokens are
+ * grouped by expert, every expert runs a SwiGLU FFN, and the expert outputs
+ * are combined with the routing weights.
+ *
+ * Sources. Page "FreeToken-rtx-4090" (freetoken.wiki), sections "Overview",
+ * "How the MoE Memory Hierarchy Works" and its component table; page
+ * "FreeToken-benchmark", section "How FreeToken Serves Large MoE Models". The
+ * pages describe the system (host pool, elastic GPU cache keyed by
+ * layer-and-expert, shared LRU in decode, full-layer double buffering in
+ * prefill, fills over a measured PCIe path) but not the arithmetic of the
+ * layer; the arithmetic each call performs is stated with the call.
+ *
+ * Conventions (all calls):
+ *  - Return value: MOE_OK (0) or a negative MOE_E* code; moe_last_error()
+ *    then holds a message for the calling thread. No call aborts the process
+ *    and no C++ exception crosses this interface.
+ *  - "device" pointers are GPU memory (hipMalloc or a torch CUDA tensor),
+ *    "host" pointers are CPU memory. The caller owns every buffer it passes;
+ *    the library never frees caller memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls taking a stream only enqueue work; they return before it runs.
+ *  - Matrices are row-major. bf16 is the 16-bit brain float (upper half of an
+ *    IEEE fp32), fp16 is IEEE binary16.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,     /* null or inconsistent argument */
+  MOE_ECAPACITY = -2,  /* cache has no slots, or a request exceeds its capacity */
+  MOE_EHIP = -3,       /* a HIP runtime call failed; its text is in moe_last_error() */
+  MOE_ENOMEM = -4,     /* host or device allocation failed */
+  MOE_ESTATE = -5      /* object used in a state that does not allow the call */
+};
+
+/* Activation / router element types. */
+enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
+
+/* Expert weight formats (the layout of one expert blob, see moe_pack_expert). */
+enum { MOE_W_F32 = 0, MOE_W_BF16 = 1, MOE_W_INT4 = 2 };
+
+/* FFN kernel choice for moe_ffn. */
+enum { MOE_FFN_AUTO = 0, MOE_FFN_DECODE = 1, MOE_FFN_PREFILL = 2 };
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Interface version (increments on any incompatible change). */
+int moe_abi_version(void);
+
+/* ------------------------------------------------------------------------ *
+ * Routing: router logits, top-k, combine weights and grouping by expert.
+ *
+ * Page "FreeToken-rtx-4090", section "How the MoE Memory Hierarchy Works":
+ * each token activates a small subset of a layer's routed experts (six of
+ * 256 in the model described). The pages do not define the gate; this call
+ * computes the standard linear gate with softmax weights:
+ *   l[t,e]   = sum_h x[t,h] * Wr[h,e] + bias[e]       (fp32 accumulation)
+ *   S_t      = the k largest l[t,.], largest first; equal values go to the
+ *              lower expert index; -0 equals +0
+ *   w[t,j]   = exp(l[t,S_t[j]] - l[t,S_t[0]]) / sum_j' exp(l[t,S_t[j']] - l[t,S_t[0]])
+ *   counts[e]   = number of (t, j) with S_t[j] = e
+ *   offsets[e]  = sum_{e' < e} counts[e'],  offsets[E] = T*k
+ *   perm_pos[t,j] = offsets[e] + #{t' < t : e in S_t'}   (e = S_t[j])
+ *   perm_src[perm_pos[t,j]] = t
+ * i.e. rows are grouped by ascending expert and, inside a group, ascending
+ * token.
+ *
+ * x        device [T, H], element type `dtype` (MOE_DT_F32 or MOE_DT_BF16)
+ * Wr       device [H, E], same element type as x
+ * bias     device [E] fp32, or NULL for no bias
+ * topk_idx device out int32 [T, k]      topk_w device out fp32 [T, k]
+ * logits   device out fp32 [T, E] or NULL
+ * counts   device out int32 [E]         offsets device out int32 [E+1]
+ * perm_src device out int32 [T*k]       perm_pos device out int32 [T, k]
+ * workspace device scratch of at least moe_route_workspace_size(T,H,E,k) bytes
+ * Limits: 1 <= k <= min(E, 16), 1 <= E <= 1024, H % 8 == 0, T >= 0 (T = 0 is a
+ * no-op that still writes counts = offsets = 0).
+ * Errors: MOE_EINVAL for null required pointers or limits violated,
+ * MOE_EHIP if a launch fails.
+ * ------------------------------------------------------------------------ */
+size_t moe_route_workspace_size(int T, int H, int E, int k);
+int moe_route(const void* x, int dtype, const void* Wr, const float* bias,
+              int T, int H, int E, int k,
+              int32_t* topk_idx, float* topk_w, float* logits,
+              int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_pos,
+              void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Expert blobs and the host pool.
+ *
+ * Page "FreeToken-rtx-4090": the complete expert pool lives in host memory
+ * and is the source of truth ("Overview"; "How the MoE Memory Hierarchy
+ * Works"), a cache entry is one complete layer-and-expert unit, and startup
+ * loads weights straight into their final host layout (the phase table, row
+ * "Startup"). Here one expert is one contiguous blob in the kernels' own
+ * layout, so a cache fill is a single host-to-device copy.
+ *
+ * Canonical expert: W1, W3 [H, I] and W2 [I, H]; the expert computes
+ *   y = (silu(x W1) * (x W3)) W2,  silu(z) = z / (1 + exp(-z)).
+ * For MOE_W_INT4 the weights are q * s with int8 codes q in [-7, 7] of the
+ * same shapes and fp16 scales s1, s3 [H/128, I], s2 [I/128, H]: one scale per
+ * 128 consecutive rows (the reduction dimension K) and output column.
+ *
+ * moe_expert_bytes: size of one blob. Requirements: H and I multiples of 32
+ * (bf16), of 128 (int4), I a multiple of 8; any H, I >= 1 for fp32.
+ * moe_pack_expert: writes one blob from canonical device arrays, on `stream`.
+ *   MOE_W_F32:  W1, W3, W2 fp32 device;  s1, s3, s2 ignored (NULL)
+ *   MOE_W_BF16: W1, W3, W2 bf16 device;  s* ignored
+ *   MOE_W_INT4: W1, W3, W2 are int8 codes (device), s1, s3, s2 fp16 device
+ *   blob: device out, moe_expert_bytes() bytes; the caller may then copy it
+ *   into a pool or a cache slot.
+ * moe_pool_alloc: page-locked host memory (hipHostMalloc) for the pool;
+ *   returns NULL and sets *status on failure. Free with moe_pool_free.
+ * ------------------------------------------------------------------------ */
+size_t moe_expert_bytes(int wfmt, int H, int I);
+int moe_pack_expert(int wfmt, int H, int I, const void* W1, const void* W3, const void* W2,
+                    const void* s1, const void* s3, const void* s2, void* blob, void* stream);
+void* moe_pool_alloc(size_t bytes, int* status);
+int moe_pool_free(void* pool);
+
+/* ------------------------------------------------------------------------ *
+ * Shared LRU expert cache (host policy).
+ *
+ * Page "FreeToken-rtx-4090", section "How the MoE Memory Hierarchy Works": a
+ * cache entry is a logical layer-and-expert pair, and decode keeps recently
+ * selected experts in one LRU cache shared across layers and tokens that
+ * changes with the routing; page "FreeToken-benchmark", section "How
+ * FreeToken Serves Large MoE Models", the decode paragraph. Key = layer*E +
+ * expert; the cache has S slots of equal size in GPU memory.
+ *
+ * cache_resolve runs one layer-step on the host:
+ *   W  = the given experts (ascending, unique) as keys layer*E + e
+ *   hits = W keys resident at entry, misses = the others
+ *   access order = hits ascending, then misses ascending; each access is
+ *   least-recently-used bookkeeping; a miss takes the lowest free slot, else
+ *   the slot of the least recently used entry (the victim, which is evicted)
+ *   the accesses form waves of at most S consecutive entries: all entries of
+ *   a wave are resident together; run a wave's FFN before filling the next.
+ * Outputs (host arrays of capacity n): work_e[i], work_slot[i], work_wave[i]
+ * in access order; misses[0..*n_miss) in access order; *n_waves.
+ * Every access is appended to the cache's trace (moe_cache_trace).
+ * Errors: MOE_EINVAL (null, layer or expert out of range, experts not
+ * ascending or not unique), MOE_ECAPACITY (S == 0 at create).
+ *
+ * moe_cache_invalidate: drop a key (e.g. after a failed fill) so that it is
+ * not left half-resident; its slot becomes free. MOE_EINVAL if not resident.
+ * moe_cache_slot_of: *slot = slot of key or -1.
+ * A handle must not be used from two threads at once.
+ * ------------------------------------------------------------------------ */
+typedef struct moe_cache moe_cache_t;
+typedef struct { int32_t key, slot, victim, wave; } moe_miss_t;
+typedef struct { int32_t step, layer, key, hit, slot, victim, wave; } moe_trace_t;
+
+moe_cache_t* moe_cache_create(int L, int E, int S, int* status);
+int moe_cache_destroy(moe_cache_t* cache);
+int cache_resolve(moe_cache_t* cache, int step, int layer, const int32_t* experts, int n,
+                  int32_t* work_e, int32_t* work_slot, int32_t* work_wave,
+                  moe_miss_t* misses, int* n_miss, int* n_waves);
+int moe_cache_trace(const moe_cache_t* cache, moe_trace_t* out, int64_t max_records, int64_t* n_records);
+int moe_cache_clear_trace(moe_cache_t* cache);
+int moe_cache_invalidate(moe_cache_t* cache, int key);
+int moe_cache_slot_of(const moe_cache_t* cache, int key, int* slot);
+int moe_cache_stats(const moe_cache_t* cache, int64_t* hits, int64_t* misses);
+
+/* ------------------------------------------------------------------------ *
+ * Miss fills over the host link.
+ *
+ * Page "FreeToken-rtx-4090", component table row "PCIe link" (only the misses
+ * chosen for GPU execution move) and the paragraph after it (a missing expert
+ * can be copied into the cache and executed on the GPU).
+ *
+ * cache_fill_async: for each miss, copies blob `key` of the pool
+ * (pool + key*blob_stride, blob_bytes bytes; pinned host memory) to slot
+ * `slot` (slot_base + slot*slot_stride; device). Ordering: the copies start
+ * only after all work enqueued on compute_stream before this call (which
+ * includes every earlier reader of a victim slot), run on fill_stream, and
+ * work enqueued on compute_stream after this call waits for them.
+ * fill_stream may equal compute_stream. Uses the cache's own events.
+ * Errors: MOE_EINVAL (null), MOE_EHIP (copy or event failure; the caller
+ * should then moe_cache_invalidate the affected keys).
+ * ------------------------------------------------------------------------ */
+int cache_fill_async(moe_cache_t* cache, const moe_miss_t* misses, int n,
+                     const void* pool, size_t blob_stride, size_t blob_bytes,
+                     void* slot_base, size_t slot_stride,
+                     void* fill_stream, void* compute_stream);
+
+/* ------------------------------------------------------------------------ *
+ * Grouped expert FFN.
+ *
+ * Runs each listed expert on its group of rows:
+ *   for row r in [row_begin, row_begin + rows) of item i (expert blob at
+ *   slot_base + slot*slot_stride):
+ *     xr = x[perm_src[r], :]
+ *     y_perm[r, :] = (silu(xr W1) * (xr W3)) W2          (fp32 out)
+ * Accumulation is fp32. In the bf16 matrix-core kernels the SwiGLU product
+ * is rounded to bf16 before the W2 product; in the int4 kernel x and that
+ * product are rounded to fp16 and the int4 codes enter the matrix product
+ * exactly, the fp16 scale being applied to each 128-row partial sum.
+ *
+ * x        device [T, H] (dtype as for moe_route)   perm_src device int32 [T*k]
+ * work     HOST array of n_work items {expert, slot, row_begin, rows}; items
+ *          must not overlap in rows; rows >= 0
+ * slot_base device base of the expert blobs; slot_stride bytes between slots
+ * wfmt     MOE_W_F32 (x fp32), MOE_W_BF16 or MOE_W_INT4 (x bf16)
+ * y_perm   device out fp32 [rows_total, H] (only listed rows are written)
+ * workspace device scratch, >= moe_ffn_workspace_size(rows_total, H, I, wfmt)
+ *          bytes, where rows_total bounds every row index used
+ * mode     MOE_FFN_AUTO picks the matrix-vector kernels when every group has
+ *          at most 32 rows and the tiled matrix-core GEMM otherwise.
+ * Errors: MOE_EINVAL for null pointers, unsupported shapes or formats.
+ * ------------------------------------------------------------------------ */
+typedef struct { int32_t expert, slot, row_begin, rows; } moe_work_t;
+
+size_t moe_ffn_workspace_size(int rows_total, int H, int I, int wfmt);
+int moe_ffn(const void* x, int dtype, const int32_t* perm_src,
+            const moe_work_t* work, int n_work,
+            const void* slot_base, size_t slot_stride, int wfmt, int H, int I,
+            float* y_perm, void* workspace, size_t ws_bytes, int mode, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Weighted combine: out[t, :] = sum_{j=0..k-1} topk_w[t,j] * y_perm[perm_pos[t,j], :]
+ * summed in ascending j in fp32 (no atomics: the result is deterministic).
+ * y_perm device fp32 [T*k, H]; perm_pos device int32 [T, k]; topk_w device
+ * fp32 [T, k]; out device [T, H] of out_dtype (MOE_DT_F32 or MOE_DT_BF16).
+ * ------------------------------------------------------------------------ */
+int moe_combine(const float* y_perm, const int32_t* perm_pos, const float* topk_w,
+                int T, int k, int H, void* out, int out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Prefill double buffering.
+ *
+ * Page "FreeToken-rtx-4090", phase table row "Prefill" and the paragraph after
+ * it, and page "FreeToken-benchmark", section "How FreeToken Serves Large MoE
+ * Models": during prefill the next layer's experts stream over PCIe while the
+ * GPU computes the current layer.
+ *
+ * A pipe owns two device buffers of layer_bytes each (allocated at create)
+ * and copies layer l's experts (pool + l*layer_stride, layer_bytes bytes,
+ * pinned host) into buffer l % 2 on its own copy stream.
+ * moe_pipe_begin_layer(l, compute_stream): makes compute_stream wait until
+ *   layer l is resident (starting its copy if it was not started), then starts
+ *   the copy of layer l+1 into the other buffer once the compute of layer l-1
+ *   (recorded by moe_pipe_end_layer) has finished with that buffer.
+ *   *buffer receives the device address of layer l's experts.
+ * moe_pipe_end_layer(l, compute_stream): records that the compute enqueued so
+ *   far for layer l is the last reader of its buffer.
+ * moe_pipe_copy_ms: elapsed copy time of layer l (valid after its copy ended).
+ * Layers must be visited in order 0, 1, ..., n_layers-1.
+ * ------------------------------------------------------------------------ */
+typedef struct moe_pipe moe_pipe_t;
+moe_pipe_t* moe_pipe_create(const void* pool, size_t layer_stride, size_t layer_bytes,
+                            int n_layers, int* status);
+int moe_pipe_destroy(moe_pipe_t* pipe);
+int moe_pipe_begin_layer(moe_pipe_t* pipe, int layer, void* compute_stream, void** buffer);
+int moe_pipe_end_layer(moe_pipe_t* pipe, int layer, void* compute_stream);
+int moe_pipe_copy_ms(moe_pipe_t* pipe, int layer, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

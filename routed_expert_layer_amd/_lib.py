@@ -1,0 +1,296 @@
+"""ctypes binding of libmoe.so: one Python function per C entry point, same names.
+
+Only argument marshalling happens here (tensor -> pointer, sizes, stream
+handles, status codes -> exceptions); every step of the layer runs in the HIP
+library. If the library is missing this module raises on import -- there is no
+fallback implementation.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ECAPACITY, MOE_EHIP, MOE_ENOMEM, MOE_ESTATE = 0, -1, -2, -3, -4, -5
+MOE_DT_F32, MOE_DT_BF16 = 0, 1
+MOE_W_F32, MOE_W_BF16, MOE_W_INT4 = 0, 1, 2
+MOE_FFN_AUTO, MOE_FFN_DECODE, MOE_FFN_PREFILL = 0, 1, 2
+
+# Every symbol include/moe.h declares.
+SYMBOLS = [
+    "moe_last_error", "moe_abi_version", "moe_route_workspace_size", "moe_route", "moe_expert_bytes",
+    "moe_pack_expert", "moe_pool_alloc", "moe_pool_free", "moe_cache_create", "moe_cache_destroy", "cache_resolve",
+    "moe_cache_trace", "moe_cache_clear_trace", "moe_cache_invalidate", "moe_cache_slot_of", "moe_cache_stats",
+    "cache_fill_async", "moe_ffn_workspace_size", "moe_ffn", "moe_combine", "moe_pipe_create", "moe_pipe_destroy",
+    "moe_pipe_begin_layer", "moe_pipe_end_layer", "moe_pipe_copy_ms",
+]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built (run routed_expert_layer_amd/build.py); there is no fallback path")
+
+_lib = ctypes.CDLL(LIB_PATH)
+P = ctypes.c_void_p
+I32 = ctypes.c_int
+I64 = ctypes.c_int64
+SZ = ctypes.c_size_t
+PI = ctypes.POINTER(ctypes.c_int)
+PI64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_sig("moe_last_error", ctypes.c_char_p)
+_sig("moe_abi_version", I32)
+_sig("moe_route_workspace_size", SZ, I32, I32, I32, I32)
+_sig("moe_route", I32, P, I32, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P)
+_sig("moe_expert_bytes", SZ, I32, I32, I32)
+_sig("moe_pack_expert", I32, I32, I32, I32, P, P, P, P, P, P, P, P)
+_sig("moe_pool_alloc", P, SZ, PI)
+_sig("moe_pool_free", I32, P)
+_sig("moe_cache_create", P, I32, I32, I32, PI)
+_sig("moe_cache_destroy", I32, P)
+_sig("cache_resolve", I32, P, I32, I32, P, I32, P, P, P, P, PI, PI)
+_sig("moe_cache_trace", I32, P, P, I64, PI64)
+_sig("moe_cache_clear_trace", I32, P)
+_sig("moe_cache_invalidate", I32, P, I32)
+_sig("moe_cache_slot_of", I32, P, I32, PI)
+_sig("moe_cache_stats", I32, P, PI64, PI64)
+_sig("cache_fill_async", I32, P, P, I32, P, SZ, SZ, P, SZ, P, P)
+_sig("moe_ffn_workspace_size", SZ, I32, I32, I32, I32)
+_sig("moe_ffn", I32, P, I32, P, P, I32, P, SZ, I32, I32, I32, P, P, SZ, I32, P)
+_sig("moe_combine", I32, P, P, P, I32, I32, I32, P, I32, P)
+_sig("moe_pipe_create", P, P, SZ, SZ, I32, PI)
+_sig("moe_pipe_destroy", I32, P)
+_sig("moe_pipe_begin_layer", I32, P, I32, P, ctypes.POINTER(ctypes.c_void_p))
+_sig("moe_pipe_end_layer", I32, P, I32, P)
+_sig("moe_pipe_copy_ms", I32, P, I32, ctypes.POINTER(ctypes.c_float))
+
+
+def _check(code, what=""):
+    if code != MOE_OK:
+        raise MoEError(code, (what + ": " if what else "") + _lib.moe_last_error().decode())
+    return code
+
+
+def _ptr(t):
+    """Device/host address of a torch tensor, numpy array, int address or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return MOE_DT_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_DT_BF16
+    raise ValueError(f"unsupported activation dtype {t.dtype}")
+
+
+def moe_last_error():
+    return _lib.moe_last_error().decode()
+
+
+def moe_abi_version():
+    return _lib.moe_abi_version()
+
+
+# ---------------------------------------------------------------------------
+def moe_route_workspace_size(T, H, E, k):
+    return _lib.moe_route_workspace_size(T, H, E, k)
+
+
+def moe_route(x, Wr, bias, k, topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos, workspace, stream=None):
+    T, H = x.shape
+    E = Wr.shape[1]
+    _check(_lib.moe_route(_ptr(x), _dtype_code(x), _ptr(Wr), _ptr(bias), T, H, E, k, _ptr(topk_idx), _ptr(topk_w),
+                          _ptr(logits), _ptr(counts), _ptr(offsets), _ptr(perm_src), _ptr(perm_pos), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream)), "moe_route")
+
+
+# ---------------------------------------------------------------------------
+def moe_expert_bytes(wfmt, H, I):
+    return _lib.moe_expert_bytes(wfmt, H, I)
+
+
+def moe_pack_expert(wfmt, H, I, W1, W3, W2, s1, s3, s2, blob, stream=None):
+    _check(_lib.moe_pack_expert(wfmt, H, I, _ptr(W1), _ptr(W3), _ptr(W2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(blob),
+                                _stream(stream)), "moe_pack_expert")
+
+
+def moe_pool_alloc(nbytes):
+    st = ctypes.c_int(0)
+    p = _lib.moe_pool_alloc(nbytes, ctypes.byref(st))
+    if not p:
+        raise MoEError(st.value, _lib.moe_last_error().decode())
+    return p
+
+
+def moe_pool_free(addr):
+    _check(_lib.moe_pool_free(addr), "moe_pool_free")
+
+
+# ---------------------------------------------------------------------------
+class MoeCache:
+    """Owner of a moe_cache_t handle."""
+
+    def __init__(self, L, E, S):
+        st = ctypes.c_int(0)
+        self.h = _lib.moe_cache_create(L, E, S, ctypes.byref(st))
+        if not self.h:
+            raise MoEError(st.value, _lib.moe_last_error().decode())
+        self.L, self.E, self.S = L, E, S
+
+    def close(self):
+        if self.h:
+            _lib.moe_cache_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+
+def moe_cache_create(L, E, S):
+    return MoeCache(L, E, S)
+
+
+def moe_cache_destroy(cache):
+    cache.close()
+
+
+def cache_resolve(cache, step, layer, experts):
+    """Returns (work_e, work_slot, work_wave, misses [n_miss, 4] = key, slot, victim, wave; n_waves)."""
+    ex = np.ascontiguousarray(np.asarray(experts, dtype=np.int32))
+    n = len(ex)
+    we = np.empty(max(n, 1), np.int32)
+    ws = np.empty(max(n, 1), np.int32)
+    ww = np.empty(max(n, 1), np.int32)
+    ms = np.empty((max(n, 1), 4), np.int32)
+    nm, nw = ctypes.c_int(0), ctypes.c_int(0)
+    _check(_lib.cache_resolve(cache.h, step, layer, ex.ctypes.data, n, we.ctypes.data, ws.ctypes.data,
+                              ww.ctypes.data, ms.ctypes.data, ctypes.byref(nm), ctypes.byref(nw)), "cache_resolve")
+    return we[:n], ws[:n], ww[:n], ms[:nm.value], nw.value
+
+
+def moe_cache_trace(cache):
+    """All trace records as an int32 array [n, 7] = step, layer, key, hit, slot, victim, wave."""
+    n = ctypes.c_int64(0)
+    _check(_lib.moe_cache_trace(cache.h, None, 0, ctypes.byref(n)), "moe_cache_trace")
+    out = np.empty((max(n.value, 1), 7), np.int32)
+    _check(_lib.moe_cache_trace(cache.h, out.ctypes.data, n.value, ctypes.byref(n)), "moe_cache_trace")
+    return out[:n.value]
+
+
+def moe_cache_clear_trace(cache):
+    _check(_lib.moe_cache_clear_trace(cache.h), "moe_cache_clear_trace")
+
+
+def moe_cache_invalidate(cache, key):
+    _check(_lib.moe_cache_invalidate(cache.h, key), "moe_cache_invalidate")
+
+
+def moe_cache_slot_of(cache, key):
+    s = ctypes.c_int(0)
+    _check(_lib.moe_cache_slot_of(cache.h, key, ctypes.byref(s)), "moe_cache_slot_of")
+    return s.value
+
+
+def moe_cache_stats(cache):
+    h, m = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib.moe_cache_stats(cache.h, ctypes.byref(h), ctypes.byref(m)), "moe_cache_stats")
+    return h.value, m.value
+
+
+def cache_fill_async(cache, misses, pool, blob_stride, blob_bytes, slot_base, slot_stride, fill_stream=None,
+                     compute_stream=None):
+    ms = np.ascontiguousarray(np.asarray(misses, dtype=np.int32).reshape(-1, 4))
+    _check(_lib.cache_fill_async(cache.h, ms.ctypes.data if len(ms) else None, len(ms), _ptr(pool), blob_stride,
+                                 blob_bytes, _ptr(slot_base), slot_stride, _stream(fill_stream),
+                                 _stream(compute_stream)), "cache_fill_async")
+
+
+# ---------------------------------------------------------------------------
+def moe_ffn_workspace_size(rows_total, H, I, wfmt):
+    return _lib.moe_ffn_workspace_size(rows_total, H, I, wfmt)
+
+
+def moe_ffn(x, perm_src, work, slot_base, slot_stride, wfmt, H, I, y_perm, workspace, mode=MOE_FFN_AUTO,
+            stream=None):
+    """work: int32 array [n, 4] of (expert, slot, row_begin, rows)."""
+    w = np.ascontiguousarray(np.asarray(work, dtype=np.int32).reshape(-1, 4))
+    _check(_lib.moe_ffn(_ptr(x), _dtype_code(x), _ptr(perm_src), w.ctypes.data if len(w) else None, len(w),
+                        _ptr(slot_base), slot_stride, wfmt, H, I, _ptr(y_perm), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), mode, _stream(stream)), "moe_ffn")
+
+
+def moe_combine(y_perm, perm_pos, topk_w, out, stream=None):
+    T, k = perm_pos.shape
+    H = y_perm.shape[1]
+    _check(_lib.moe_combine(_ptr(y_perm), _ptr(perm_pos), _ptr(topk_w), T, k, H, _ptr(out), _dtype_code(out),
+                            _stream(stream)), "moe_combine")
+
+
+# ---------------------------------------------------------------------------
+class MoePipe:
+    def __init__(self, pool, layer_stride, layer_bytes, n_layers):
+        st = ctypes.c_int(0)
+        self.h = _lib.moe_pipe_create(_ptr(pool), layer_stride, layer_bytes, n_layers, ctypes.byref(st))
+        if not self.h:
+            raise MoEError(st.value, _lib.moe_last_error().decode())
+
+    def close(self):
+        if self.h:
+            _lib.moe_pipe_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+
+def moe_pipe_create(pool, layer_stride, layer_bytes, n_layers):
+    return MoePipe(pool, layer_stride, layer_bytes, n_layers)
+
+
+def moe_pipe_destroy(pipe):
+    pipe.close()
+
+
+def moe_pipe_begin_layer(pipe, layer, stream=None):
+    buf = ctypes.c_void_p(0)
+    _check(_lib.moe_pipe_begin_layer(pipe.h, layer, _stream(stream), ctypes.byref(buf)), "moe_pipe_begin_layer")
+    return buf.value
+
+
+def moe_pipe_end_layer(pipe, layer, stream=None):
+    _check(_lib.moe_pipe_end_layer(pipe.h, layer, _stream(stream)), "moe_pipe_end_layer")
+
+
+def moe_pipe_copy_ms(pipe, layer):
+    ms = ctypes.c_float(0)
+    _check(_lib.moe_pipe_copy_ms(pipe.h, layer, ctypes.byref(ms)), "moe_pipe_copy_ms")
+    return ms.value

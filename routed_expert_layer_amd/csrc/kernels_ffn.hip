@@ -1,0 +1,450 @@
+// Grouped SwiGLU expert FFN: y = (silu(x W1) * (x W3)) W2 for each listed
+// expert over its group of rows.
+//
+// Decode (few rows per expert) is bound by streaming the expert's weights
+// from HBM: the matrix-vector kernels give each workgroup one 16-row tile of
+// a weight matrix, split its K range over four waves, and feed every 1 KiB
+// weight fragment straight from a coalesced global load into a 16x16x32
+// matrix-core instruction whose other operand holds the (<= 16) tokens.
+// Prefill (many rows per expert) runs a tiled matrix-core GEMM with both
+// operands staged in LDS.
+#include "dev_common.hpp"
+#include "moe_kernels.hpp"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// fp32 weights: plain VALU kernels (small correctness configurations).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void ffn1_f32_kernel(const float* __restrict__ x, const int32_t* __restrict__ perm_src,
+                                                       const WorkArgs wa, const char* __restrict__ slot_base,
+                                                       size_t slot_stride, int H, int I, float* __restrict__ hbuf) {
+  const int4 it = wa.item[blockIdx.y];
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int m = idx / I, i = idx - (idx / I) * I;
+  if (m >= it.z) return;
+  const float* W1 = reinterpret_cast<const float*>(slot_base + (size_t)it.x * slot_stride);
+  const float* W3 = W1 + (size_t)H * I;
+  const float* xr = x + (size_t)perm_src[it.y + m] * H;
+  float g = 0.f, u = 0.f;
+  for (int h = 0; h < H; ++h) {
+    g = fmaf(xr[h], W1[(size_t)h * I + i], g);
+    u = fmaf(xr[h], W3[(size_t)h * I + i], u);
+  }
+  hbuf[(size_t)(it.y + m) * I + i] = silu(g) * u;
+}
+
+__global__ __launch_bounds__(256) void ffn2_f32_kernel(const float* __restrict__ hbuf, const WorkArgs wa,
+                                                       const char* __restrict__ slot_base, size_t slot_stride, int H,
+                                                       int I, float* __restrict__ y) {
+  const int4 it = wa.item[blockIdx.y];
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int m = idx / H, n = idx - (idx / H) * H;
+  if (m >= it.z) return;
+  const float* W2 = reinterpret_cast<const float*>(slot_base + (size_t)it.x * slot_stride) + 2 * (size_t)H * I;
+  const float* hr = hbuf + (size_t)(it.y + m) * I;
+  float acc = 0.f;
+  for (int i = 0; i < I; ++i) acc = fmaf(hr[i], W2[(size_t)i * H + n], acc);
+  y[(size_t)(it.y + m) * H + n] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 decode kernels.
+// ---------------------------------------------------------------------------
+constexpr int kU = 8;  // fragments in flight per wave
+
+// Gate/up: workgroup = one 16-row tile of P1 (8 gate + 8 up columns) of one
+// item; wave w reduces fragments [KC*w/4, KC*(w+1)/4).
+__global__ __launch_bounds__(256) void ffn1_decode_bf16(const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ perm_src, const WorkArgs wa,
+                                                        const char* __restrict__ slot_base, size_t slot_stride, int H,
+                                                        int I, uint16_t* __restrict__ hbuf) {
+  const int NT = I / 8;
+  const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
+  const int4 it = wa.item[item];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KC = H / 32;
+  const int c0 = (KC * wave) >> 2, c1 = (KC * (wave + 1)) >> 2;
+  const char* wp = slot_base + (size_t)it.x * slot_stride + (size_t)tile * KC * 1024 + lane * 16;
+  const int kq = (lane >> 4) * 8;
+  __shared__ f32x4_t red[4][64];
+  for (int m0 = 0; m0 < it.z; m0 += 16) {
+    const int m = m0 + (lane & 15);
+    const bool valid = m < it.z;
+    const uint16_t* xr = x + (size_t)(valid ? perm_src[it.y + m] : 0) * H + kq;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    int c = c0;
+    for (; c + kU <= c1; c += kU) {
+      u32x4_t a[kU], b[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        a[u] = ld16_nt(wp + (size_t)(c + u) * 1024);
+        b[u] = valid ? ld16(xr + (c + u) * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) acc = mfma_bf16(a[u], b[u], acc);
+    }
+    for (; c < c1; ++c) {
+      const u32x4_t a = ld16_nt(wp + (size_t)c * 1024);
+      const u32x4_t b = valid ? ld16(xr + c * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      acc = mfma_bf16(a, b, acc);
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && valid) {
+      const f32x4_t s = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+      const int i0 = 8 * tile + 2 * (lane >> 4);
+      const uint32_t packed =
+          (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
+      *reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0) = packed;
+    }
+    __syncthreads();
+  }
+}
+
+// Down projection: workgroup = one 16-row tile of P2 (16 output columns).
+__global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restrict__ hbuf, const WorkArgs wa,
+                                                        const char* __restrict__ slot_base, size_t slot_stride,
+                                                        size_t p2_off, int H, int I, float* __restrict__ y) {
+  const int NT = H / 16;
+  const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
+  const int4 it = wa.item[item];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KC = I / 32;
+  const int c0 = (KC * wave) >> 2, c1 = (KC * (wave + 1)) >> 2;
+  const char* wp = slot_base + (size_t)it.x * slot_stride + p2_off + (size_t)tile * KC * 1024 + lane * 16;
+  const int kq = (lane >> 4) * 8;
+  __shared__ f32x4_t red[4][64];
+  for (int m0 = 0; m0 < it.z; m0 += 16) {
+    const int m = m0 + (lane & 15);
+    const bool valid = m < it.z;
+    const uint16_t* hr = hbuf + (size_t)(it.y + (valid ? m : 0)) * I + kq;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    int c = c0;
+    for (; c + kU <= c1; c += kU) {
+      u32x4_t a[kU], b[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        a[u] = ld16_nt(wp + (size_t)(c + u) * 1024);
+        b[u] = valid ? ld16(hr + (c + u) * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) acc = mfma_bf16(a[u], b[u], acc);
+    }
+    for (; c < c1; ++c) {
+      const u32x4_t a = ld16_nt(wp + (size_t)c * 1024);
+      const u32x4_t b = valid ? ld16(hr + c * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      acc = mfma_bf16(a, b, acc);
+    }
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && valid) {
+      const f32x4_t s = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+      *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// int4 decode kernels (x and the SwiGLU product in fp16, codes exact in fp16,
+// one fp16 scale per 128-row block applied to that block's partial sum).
+// ---------------------------------------------------------------------------
+constexpr int kUG = 2;  // 128-row blocks in flight per wave
+
+// Gathered activations, converted to fp16: xg[r, :] = fp16(x[perm_src[r], :]).
+__global__ __launch_bounds__(256) void gather_f16_kernel(const uint16_t* __restrict__ x,
+                                                         const int32_t* __restrict__ perm_src, const WorkArgs wa,
+                                                         int H, uint16_t* __restrict__ xg) {
+  const int4 it = wa.item[blockIdx.y];
+  const int H8 = H / 8;
+  for (int idx = blockIdx.x * 256 + threadIdx.x; idx < it.z * H8; idx += gridDim.x * 256) {
+    const int m = idx / H8, c = idx - (idx / H8) * H8;
+    const u32x4_t v = ld16(x + (size_t)perm_src[it.y + m] * H + 8 * c);
+    u32x4_t o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float lo = __uint_as_float(v[p] << 16), hi = __uint_as_float(v[p] & 0xFFFF0000u);
+      o[p] = (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+    }
+    *reinterpret_cast<u32x4_t*>(xg + (size_t)(it.y + m) * H + 8 * c) = o;
+  }
+}
+
+__device__ __forceinline__ void int4_block(const char* qp, const char* sp, const uint16_t* br, bool valid,
+                                           f32x4_t& acc) {
+  const u32x4_t a = ld16_nt(qp);
+  // The four fp16 scales are read as two 32-bit words and widened one by one
+  // (a two-element fp16 vector view of the 64-bit load was miscompiled into
+  // mixed-precision FMAs that all read the first word).
+  const uint32_t sc0 = reinterpret_cast<const uint32_t*>(sp)[0];
+  const uint32_t sc1 = reinterpret_cast<const uint32_t*>(sp)[1];
+  u32x4_t b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = valid ? ld16(br + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+  f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t = mfma_f16(int4x8_to_f16x8(a[j]), b[j], t);
+  acc[0] = fmaf(t[0], f16_bits_to_f32(sc0 & 0xFFFFu), acc[0]);
+  acc[1] = fmaf(t[1], f16_bits_to_f32(sc0 >> 16), acc[1]);
+  acc[2] = fmaf(t[2], f16_bits_to_f32(sc1 & 0xFFFFu), acc[2]);
+  acc[3] = fmaf(t[3], f16_bits_to_f32(sc1 >> 16), acc[3]);
+}
+
+__global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restrict__ xg, const WorkArgs wa,
+                                                        const char* __restrict__ slot_base, size_t slot_stride,
+                                                        size_t p1s_off, int H, int I, uint16_t* __restrict__ hbuf) {
+  const int NT = I / 8;
+  const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
+  const int4 it = wa.item[item];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KG = H / 128;
+  const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
+  const char* blob = slot_base + (size_t)it.x * slot_stride;
+  const char* qp = blob + (size_t)tile * KG * 1024 + lane * 16;
+  const char* sp = blob + p1s_off + (size_t)tile * KG * 32 + (lane >> 4) * 8;
+  const int kq = (lane >> 4) * 8;
+  __shared__ f32x4_t red[4][64];
+  for (int m0 = 0; m0 < it.z; m0 += 16) {
+    const int m = m0 + (lane & 15);
+    const bool valid = m < it.z;
+    const uint16_t* xr = xg + (size_t)(it.y + (valid ? m : 0)) * H + kq;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll kUG
+    for (int g = g0; g < g1; ++g) int4_block(qp + (size_t)g * 1024, sp + (size_t)g * 32, xr + 128 * g, valid, acc);
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && valid) {
+      const f32x4_t s = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+      const int i0 = 8 * tile + 2 * (lane >> 4);
+      const uint32_t packed =
+          (uint32_t)f32_to_f16_bits(silu(s[0]) * s[1]) | ((uint32_t)f32_to_f16_bits(silu(s[2]) * s[3]) << 16);
+      *reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0) = packed;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restrict__ hbuf, const WorkArgs wa,
+                                                        const char* __restrict__ slot_base, size_t slot_stride,
+                                                        size_t p2_off, size_t p2s_off, int H, int I,
+                                                        float* __restrict__ y) {
+  const int NT = H / 16;
+  const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
+  const int4 it = wa.item[item];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KG = I / 128;
+  const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
+  const char* blob = slot_base + (size_t)it.x * slot_stride;
+  const char* qp = blob + p2_off + (size_t)tile * KG * 1024 + lane * 16;
+  const char* sp = blob + p2s_off + (size_t)tile * KG * 32 + (lane >> 4) * 8;
+  const int kq = (lane >> 4) * 8;
+  __shared__ f32x4_t red[4][64];
+  for (int m0 = 0; m0 < it.z; m0 += 16) {
+    const int m = m0 + (lane & 15);
+    const bool valid = m < it.z;
+    const uint16_t* hr = hbuf + (size_t)(it.y + (valid ? m : 0)) * I + kq;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll kUG
+    for (int g = g0; g < g1; ++g) int4_block(qp + (size_t)g * 1024, sp + (size_t)g * 32, hr + 128 * g, valid, acc);
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0 && valid) {
+      const f32x4_t s = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+      *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 prefill GEMM. Tile: 128 weight rows x 128 tokens x 64 K, 4 waves each
+// computing 64 x 64 with 16 matrix-core instructions per 32-wide K chunk.
+// Both operands are staged in LDS in fragment order (two stages), so every
+// LDS read is one conflict-free 16-byte access per lane.
+// PHASE 1: A = gate/up rows (N = 2I, K = H), B = x rows through perm_src,
+//          epilogue silu(gate) * up -> bf16 h.
+// PHASE 2: A = down rows (N = H, K = I), B = h rows, epilogue -> fp32 y.
+// ---------------------------------------------------------------------------
+template <int PHASE>
+__global__ __launch_bounds__(256, 2) void ffn_gemm_bf16(const uint16_t* __restrict__ bsrc,
+                                                       const int32_t* __restrict__ perm_src, const WorkArgs wa,
+                                                       const char* __restrict__ slot_base, size_t slot_stride,
+                                                       size_t mat_off, int N, int K, int H, int I,
+                                                       uint16_t* __restrict__ hout, float* __restrict__ yout) {
+  __shared__ __attribute__((aligned(16))) char lds[2][32768];
+  const int NTB = N / kGemmBN;
+  const int mtg = blockIdx.x / NTB, nt = blockIdx.x - (blockIdx.x / NTB) * NTB;
+  int item = 0;
+  while (item + 1 < wa.n && wa.tile_prefix[item + 1] <= mtg) ++item;
+  const int4 it = wa.item[item];
+  const int mt = mtg - wa.tile_prefix[item];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int KC = K / 32, KT = K / 64;
+  const int ldb = (PHASE == 1) ? H : I;
+
+  // A (weights): 16 fragments per stage, 4 per thread.
+  const char* abase = slot_base + (size_t)it.x * slot_stride + mat_off;
+  size_t a_off[4];
+  int a_lds[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int id = r * 256 + tid, f = id >> 6, l = id & 63;
+    a_off[r] = ((size_t)(nt * 8 + (f >> 1)) * KC + (f & 1)) * 1024 + l * 16;
+    a_lds[r] = f * 1024 + l * 16;
+  }
+  // B (tokens): 128 rows x 64 K per stage, 4 x 16 bytes per thread.
+  const uint16_t* brow[4];
+  bool bval[4];
+  int b_lds[4], b_k[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int id = r * 256 + tid, row = id >> 3, ch = id & 7;
+    const int mloc = mt * kGemmBM + row;
+    bval[r] = mloc < it.z;
+    size_t src_row = 0;
+    if (bval[r]) src_row = (PHASE == 1) ? (size_t)perm_src[it.y + mloc] : (size_t)(it.y + mloc);
+    brow[r] = bsrc + src_row * ldb;
+    b_k[r] = ch * 8;
+    b_lds[r] = 16384 + ((row >> 4) * 2 + (ch >> 2)) * 1024 + ((ch & 3) * 16 + (row & 15)) * 16;
+  }
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  u32x4_t ra[4], rb[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ra[r] = ld16(abase + a_off[r] + (size_t)kt * 2048);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rb[r] = bval[r] ? ld16(brow[r] + kt * 64 + b_k[r]) : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4_t*>(&lds[st][a_lds[r]]) = ra[r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4_t*>(&lds[st][b_lds[r]]) = rb[r];
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      u32x4_t fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = *reinterpret_cast<const u32x4_t*>(&lds[st][((wn * 4 + i) * 2 + kc) * 1024 + lane * 16]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *reinterpret_cast<const u32x4_t*>(&lds[st][16384 + ((wm * 4 + j) * 2 + kc) * 1024 + lane * 16]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+    }
+    if (kt + 1 < KT) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int mloc = mt * kGemmBM + (wm * 4 + j) * 16 + (lane & 15);
+    if (mloc >= it.z) continue;
+    const size_t row = (size_t)(it.y + mloc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ntile = nt * 8 + wn * 4 + i;
+      const f32x4_t s = acc[i][j];
+      if constexpr (PHASE == 1) {
+        const int i0 = 8 * ntile + 2 * (lane >> 4);
+        const uint32_t packed =
+            (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
+        *reinterpret_cast<uint32_t*>(hout + row * I + i0) = packed;
+      } else {
+        *reinterpret_cast<f32x4_t*>(yout + row * H + 16 * ntile + 4 * (lane >> 4)) = s;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool prefill_supported(int wfmt, int H, int I) {
+  return wfmt == 1 && (2 * I) % kGemmBN == 0 && H % kGemmBN == 0 && H % 64 == 0 && I % 64 == 0;
+}
+
+hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, const WorkArgs& wa,
+                             const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y,
+                             hipStream_t s) {
+  if (wa.n == 0) return hipSuccess;
+  const BlobLayout L = blob_layout(wfmt, H, I);
+  if (wfmt == 0) {
+    int maxrows = 0;
+    for (int i = 0; i < wa.n; ++i) maxrows = wa.item[i].z > maxrows ? wa.item[i].z : maxrows;
+    if (maxrows == 0) return hipSuccess;
+    hipLaunchKernelGGL(ffn1_f32_kernel, dim3((maxrows * I + 255) / 256, wa.n), dim3(256), 0, s,
+                       static_cast<const float*>(x), perm_src, wa, slot_base, slot_stride, H, I,
+                       static_cast<float*>(hbuf));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ffn2_f32_kernel, dim3((maxrows * H + 255) / 256, wa.n), dim3(256), 0, s,
+                       static_cast<const float*>(hbuf), wa, slot_base, slot_stride, H, I, y);
+    return hipGetLastError();
+  }
+  if (wfmt == 1) {
+    hipLaunchKernelGGL(ffn1_decode_bf16, dim3(wa.n * (I / 8)), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                       perm_src, wa, slot_base, slot_stride, H, I, static_cast<uint16_t*>(hbuf));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ffn2_decode_bf16, dim3(wa.n * (H / 16)), dim3(256), 0, s, static_cast<const uint16_t*>(hbuf),
+                       wa, slot_base, slot_stride, L.p2, H, I, y);
+    return hipGetLastError();
+  }
+  // int4
+  hipLaunchKernelGGL(gather_f16_kernel, dim3(4, wa.n), dim3(256), 0, s, static_cast<const uint16_t*>(x), perm_src, wa,
+                     H, static_cast<uint16_t*>(xg));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ffn1_decode_int4, dim3(wa.n * (I / 8)), dim3(256), 0, s, static_cast<const uint16_t*>(xg), wa,
+                     slot_base, slot_stride, L.p1s, H, I, static_cast<uint16_t*>(hbuf));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ffn2_decode_int4, dim3(wa.n * (H / 16)), dim3(256), 0, s, static_cast<const uint16_t*>(hbuf), wa,
+                     slot_base, slot_stride, L.p2, L.p2s, H, I, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,
+                              size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s) {
+  if (wa.n == 0) return hipSuccess;
+  const BlobLayout L = blob_layout(1, H, I);
+  int tot = 0;
+  for (int i = 0; i < wa.n; ++i) {
+    wa.tile_prefix[i] = tot;
+    tot += (wa.item[i].z + kGemmBM - 1) / kGemmBM;
+  }
+  wa.tile_prefix[wa.n] = tot;
+  wa.total_tiles = tot;
+  if (tot == 0) return hipSuccess;
+  hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3(tot * ((2 * I) / kGemmBN)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), perm_src, wa, slot_base, slot_stride, L.p1, 2 * I, H, H, I,
+                     static_cast<uint16_t*>(hbuf), y);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ffn_gemm_bf16<2>, dim3(tot * (H / kGemmBN)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(hbuf), perm_src, wa, slot_base, slot_stride, L.p2, H, I, H, I,
+                     static_cast<uint16_t*>(hbuf), y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

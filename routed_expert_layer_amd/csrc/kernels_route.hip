@@ -1,0 +1,291 @@
+// Routing kernels: gate logits, wave-level top-k with softmax weights, and
+// the stable grouping of (token, slot) pairs by expert.
+//
+// Page "FreeToken-rtx-4090", section "How the MoE Memory Hierarchy Works":
+// each token activates a few of a layer's routed experts. The gate itself is
+// not defined on the pages; these kernels compute the linear gate
+// l = x.Wr + b, the k largest logits (ties to the lower expert index) and
+// softmax weights renormalised over the selected k.
+#include "dev_common.hpp"
+#include "moe_kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kRouterTok = 16;   // tokens per router block
+constexpr int kMaxEPerLane = 16; // E <= 1024
+
+template <bool BF16>
+__device__ __forceinline__ float ldv(const void* p, size_t i) {
+  if constexpr (BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  else return reinterpret_cast<const float*>(p)[i];
+}
+
+// Partial logits over a slice of H: partial[z][t][e] = sum_{h in slice z} x[t,h] Wr[h,e].
+// Block: 256 threads = 4 groups of 64 experts-lanes; each group owns 4 tokens.
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_partial_kernel(const void* __restrict__ x, const void* __restrict__ Wr,
+                                                             int T, int H, int E, int hchunk,
+                                                             float* __restrict__ partial) {
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int t0 = blockIdx.y * kRouterTok + grp * 4;
+  const int h0 = blockIdx.z * hchunk;
+  const int h1 = min(H, h0 + hchunk);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (e < E) {
+    const int nt = min(4, T - t0);
+    for (int h = h0; h < h1; ++h) {
+      const float w = ldv<BF16>(Wr, (size_t)h * E + e);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i < nt) acc[i] = fmaf(ldv<BF16>(x, (size_t)(t0 + i) * H + h), w, acc[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (t0 + i < T) partial[((size_t)blockIdx.z * T + t0 + i) * E + e] = acc[i];
+  }
+}
+
+// Max of a 64-bit key over the wave. Inside each row of 16 lanes the
+// butterfly uses DPP (quad permutes, then row rotations by 4 and 8); the four
+// row maxima are then read with v_readlane.
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v, int ctrl_id) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  uint32_t lo2, hi2;
+  switch (ctrl_id) {
+    case 0:
+      lo2 = __builtin_amdgcn_update_dpp(0, (int)lo, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+      hi2 = __builtin_amdgcn_update_dpp(0, (int)hi, 0xB1, 0xF, 0xF, false);
+      break;
+    case 1:
+      lo2 = __builtin_amdgcn_update_dpp(0, (int)lo, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+      hi2 = __builtin_amdgcn_update_dpp(0, (int)hi, 0x4E, 0xF, 0xF, false);
+      break;
+    case 2:
+      lo2 = __builtin_amdgcn_update_dpp(0, (int)lo, 0x124, 0xF, 0xF, false);  // row_ror:4
+      hi2 = __builtin_amdgcn_update_dpp(0, (int)hi, 0x124, 0xF, 0xF, false);
+      break;
+    default:
+      lo2 = __builtin_amdgcn_update_dpp(0, (int)lo, 0x128, 0xF, 0xF, false);  // row_ror:8
+      hi2 = __builtin_amdgcn_update_dpp(0, (int)hi, 0x128, 0xF, 0xF, false);
+      break;
+  }
+  uint64_t o = ((uint64_t)hi2 << 32) | lo2;
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_step(v, 0);
+  v = dpp_max_step(v, 1);
+  v = dpp_max_step(v, 2);
+  v = dpp_max_step(v, 3);
+  uint64_t best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+    uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+    uint64_t o = ((uint64_t)hi << 32) | lo;
+    best = o > best ? o : best;
+  }
+  return best;
+}
+
+// Order-preserving map of an fp32 value to uint32 (-0 is folded into +0 first).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// One wave per token: sum the partial logits, add the bias, select the top k
+// by k rounds of a wave-wide maximum of (value, ~expert) keys, then the
+// softmax weights over the selected logits.
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int nsplit,
+                                                   const float* __restrict__ bias, int T, int E, int k,
+                                                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                   float* __restrict__ logits) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;  // uniform per wave
+  uint64_t key[kMaxEPerLane];
+#pragma unroll
+  for (int v = 0; v < kMaxEPerLane; ++v) {
+    const int e = v * 64 + lane;
+    key[v] = 0;
+    if (e < E) {
+      float l = 0.f;
+      for (int z = 0; z < nsplit; ++z) l += partial[((size_t)z * T + t) * E + e];
+      if (bias) l += bias[e];
+      if (logits) logits[(size_t)t * E + e] = l;
+      key[v] = ((uint64_t)float_key(l) << 32) | (uint32_t)(~(uint32_t)e);
+    }
+  }
+  // k rounds; round j's winner is kept by lane j. The softmax denominator
+  // is accumulated in round order from the (wave-uniform) winning values.
+  float v0 = 0.f, den = 0.f, my_v = 0.f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t local = 0;
+#pragma unroll
+    for (int v = 0; v < kMaxEPerLane; ++v) local = key[v] > local ? key[v] : local;
+    const uint64_t best = wave_max_u64(local);
+#pragma unroll
+    for (int v = 0; v < kMaxEPerLane; ++v)
+      if (key[v] == best) key[v] = 0;
+    const float val = key_float((uint32_t)(best >> 32));
+    if (j == 0) v0 = val;
+    den += expf(val - v0);
+    if (lane == j) {
+      my_e = (int)(~(uint32_t)best);
+      my_v = val;
+    }
+  }
+  if (lane < k) {
+    topk_idx[(size_t)t * k + lane] = my_e;
+    topk_w[(size_t)t * k + lane] = expf(my_v - v0) / den;
+  }
+}
+
+// Grouping by expert in one workgroup. Tokens are taken in chunks of 64 (one
+// wave, one bit per token): for every expert a 64-bit mask of the chunk's
+// tokens that chose it (LDS atomic OR, order independent) gives both the
+// chunk's count and, through a popcount of the lower lanes, each token's
+// rank inside the chunk. Chunk bases are a prefix sum over chunks.
+__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k,
+                                                       int nwaves, int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+                                                       int32_t* __restrict__ perm_pos, int32_t* __restrict__ hist,
+                                                       uint64_t* __restrict__ bits) {
+  extern __shared__ uint64_t smem[];  // nwaves * E masks, then E+1 ints
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nchunks = (T + 63) / 64;
+  uint64_t* bm = smem + (size_t)wave * E;
+  int32_t* cnt = reinterpret_cast<int32_t*>(smem + (size_t)nwaves * E);
+  const bool active = wave < nwaves;
+  // phase 1: per-chunk masks and counts
+  for (int r = 0; r * nwaves < nchunks; ++r) {
+    const int c = r * nwaves + wave;
+    if (active && c < nchunks)
+      for (int e = lane; e < E; e += 64) bm[e] = 0;
+    __syncthreads();
+    if (active && c < nchunks) {
+      const int t = c * 64 + lane;
+      if (t < T)
+        for (int j = 0; j < k; ++j) atomicOr((unsigned long long*)&bm[topk_idx[(size_t)t * k + j]], 1ull << lane);
+    }
+    __syncthreads();
+    if (active && c < nchunks)
+      for (int e = lane; e < E; e += 64) {
+        const uint64_t b = bm[e];
+        bits[(size_t)c * E + e] = b;
+        hist[(size_t)c * E + e] = __popcll(b);
+      }
+    __syncthreads();
+  }
+  // phase 2: totals per expert, exclusive prefix over experts
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int s = 0;
+    for (int c = 0; c < nchunks; ++c) s += hist[(size_t)c * E + e];
+    cnt[e] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      const int v = cnt[e];
+      counts[e] = v;
+      offsets[e] = run;
+      cnt[e] = run;
+      run += v;
+    }
+    offsets[E] = run;
+  }
+  __syncthreads();
+  // phase 3: base of every (chunk, expert)
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = cnt[e];
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = hist[(size_t)c * E + e];
+      hist[(size_t)c * E + e] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  // phase 4: positions
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c = wave; c < nchunks && active; c += nwaves) {
+    const int t = c * 64 + lane;
+    if (t < T)
+      for (int j = 0; j < k; ++j) {
+        const int e = topk_idx[(size_t)t * k + j];
+        const int pos = hist[(size_t)c * E + e] + __popcll(bits[(size_t)c * E + e] & below);
+        perm_pos[(size_t)t * k + j] = pos;
+        perm_src[pos] = t;
+      }
+  }
+}
+
+struct RoutePlan {
+  int gx, gy, nsplit, hchunk;
+  size_t partial_bytes, hist_off, bits_off, total;
+};
+
+RoutePlan plan_route(int T, int H, int E) {
+  RoutePlan p{};
+  p.gx = (E + 63) / 64;
+  p.gy = (T + kRouterTok - 1) / kRouterTok;
+  const int blocks = p.gx * (p.gy > 0 ? p.gy : 1);
+  int ns = (512 + blocks - 1) / blocks;
+  const int max_ns = H / 32 > 0 ? H / 32 : 1;
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  p.hchunk = (H + ns - 1) / ns;
+  p.nsplit = (H + p.hchunk - 1) / p.hchunk;
+  const int nchunks = (T + 63) / 64;
+  p.partial_bytes = align_up((size_t)p.nsplit * T * E * sizeof(float), 256);
+  p.hist_off = p.partial_bytes;
+  p.bits_off = align_up(p.hist_off + (size_t)nchunks * E * sizeof(int32_t), 256);
+  p.total = align_up(p.bits_off + (size_t)nchunks * E * sizeof(uint64_t), 256) + 256;
+  return p;
+}
+
+}  // namespace
+
+size_t route_workspace_bytes(int T, int H, int E, int k) {
+  (void)k;
+  return plan_route(T, H, E).total;
+}
+
+hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
+                        int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
+                        int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s) {
+  const RoutePlan p = plan_route(T, H, E);
+  char* w = static_cast<char*>(ws);
+  float* partial = reinterpret_cast<float*>(w);
+  int32_t* hist = reinterpret_cast<int32_t*>(w + p.hist_off);
+  uint64_t* bits = reinterpret_cast<uint64_t*>(w + p.bits_off);
+  if (T > 0) {
+    dim3 grid(p.gx, p.gy, p.nsplit);
+    if (bf16)
+      hipLaunchKernelGGL(router_partial_kernel<true>, grid, dim3(256), 0, s, x, Wr, T, H, E, p.hchunk, partial);
+    else
+      hipLaunchKernelGGL(router_partial_kernel<false>, grid, dim3(256), 0, s, x, Wr, T, H, E, p.hchunk, partial);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, partial, p.nsplit, bias, T, E, k, topk_idx,
+                       topk_w, logits);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  int nwaves = 16;
+  while (nwaves > 1 && (size_t)nwaves * E * 8 + (E + 1) * 4 > 64 * 1024) nwaves /= 2;
+  const size_t lds = (size_t)nwaves * E * 8 + (size_t)(E + 1) * 4;
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, topk_idx, T, E, k, nwaves, counts, offsets, perm_src,
+                     perm_pos, hist, bits);
+  return hipGetLastError();
+}
+
+}  // namespace moe

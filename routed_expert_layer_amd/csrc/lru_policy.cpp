@@ -1,0 +1,67 @@
+#include "lru_policy.hpp"
+
+namespace moe {
+
+SharedLru::SharedLru(int n_keys, int S)
+    : S_(S), key_slot_(n_keys, -1), slot_key_(S, -1), prev_(S, -1), next_(S, -1) {
+  for (int s = 0; s < S; ++s) free_.insert(s);
+}
+
+void SharedLru::unlink(int s) {
+  int p = prev_[s], n = next_[s];
+  if (p >= 0) next_[p] = n; else lru_ = n;
+  if (n >= 0) prev_[n] = p; else mru_ = p;
+  prev_[s] = next_[s] = -1;
+}
+
+void SharedLru::push_mru(int s) {
+  prev_[s] = mru_;
+  next_[s] = -1;
+  if (mru_ >= 0) next_[mru_] = s; else lru_ = s;
+  mru_ = s;
+}
+
+void SharedLru::resolve(const int32_t* keys, int n, std::vector<Access>& out) {
+  // Hits are decided before any access of this layer-step is made.
+  std::vector<int32_t> order;
+  order.reserve(n);
+  for (int i = 0; i < n; ++i) if (key_slot_[keys[i]] >= 0) order.push_back(keys[i]);
+  const size_t n_hits = order.size();
+  for (int i = 0; i < n; ++i) if (key_slot_[keys[i]] < 0) order.push_back(keys[i]);
+  for (size_t pos = 0; pos < order.size(); ++pos) {
+    const int32_t key = order[pos];
+    Access a{key, pos < n_hits ? 1 : 0, -1, -1, static_cast<int32_t>(pos / S_)};
+    if (a.hit) {
+      a.slot = key_slot_[key];
+      unlink(a.slot);
+      ++hits_;
+    } else {
+      if (!free_.empty()) {
+        a.slot = *free_.begin();
+        free_.erase(free_.begin());
+      } else {
+        a.slot = lru_;
+        unlink(a.slot);
+        a.victim = slot_key_[a.slot];
+        key_slot_[a.victim] = -1;
+      }
+      slot_key_[a.slot] = key;
+      key_slot_[key] = a.slot;
+      ++misses_;
+    }
+    push_mru(a.slot);
+    out.push_back(a);
+  }
+}
+
+bool SharedLru::invalidate(int key) {
+  int s = key_slot_[key];
+  if (s < 0) return false;
+  unlink(s);
+  key_slot_[key] = -1;
+  slot_key_[s] = -1;
+  free_.insert(s);
+  return true;
+}
+
+}  // namespace moe

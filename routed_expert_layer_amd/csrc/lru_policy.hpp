@@ -1,0 +1,43 @@
+// Shared LRU policy over (layer, expert) keys: host-only C++, no HIP.
+//
+// Page "FreeToken-rtx-4090", section "How the MoE Memory Hierarchy Works": a
+// cache entry is a logical layer-and-expert pair and decode keeps recently
+// selected experts in one LRU cache shared across layers and tokens. One
+// layer-step touches its working set hits-first then misses, each ascending;
+// a miss takes the lowest free slot, else the least recently used entry's
+// slot; accesses are cut into waves of at most S entries.
+#pragma once
+#include <cstdint>
+#include <set>
+#include <vector>
+
+namespace moe {
+
+struct Access {
+  int32_t key, hit, slot, victim, wave;
+};
+
+class SharedLru {
+ public:
+  SharedLru(int n_keys, int S);
+  // One layer-step over ascending unique keys; appends to `out` in access order.
+  void resolve(const int32_t* keys, int n, std::vector<Access>& out);
+  int slot_of(int key) const { return key_slot_[key]; }
+  bool invalidate(int key);  // returns false if the key is not resident
+  int capacity() const { return S_; }
+  int64_t hits() const { return hits_; }
+  int64_t misses() const { return misses_; }
+
+ private:
+  void unlink(int slot);
+  void push_mru(int slot);
+  int S_;
+  std::vector<int32_t> key_slot_;  // key -> slot or -1
+  std::vector<int32_t> slot_key_;  // slot -> key or -1
+  std::vector<int32_t> prev_, next_;  // recency list over occupied slots
+  int lru_ = -1, mru_ = -1;
+  std::set<int> free_;
+  int64_t hits_ = 0, misses_ = 0;
+};
+
+}  // namespace moe

@@ -1,0 +1,96 @@
+// Internal interface between the C ABI (abi.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Expert blob layouts.
+//
+// bf16 (MOE_W_BF16): two weight matrices stored as matrix-core fragments.
+//   P1 = the gate and up projections, N1 = 2I output rows, K1 = H.
+//   P2 = the down projection,        N2 = H  output rows, K2 = I.
+//   A matrix with N rows and K columns is cut into N/16 row tiles; a row tile
+//   is K/32 fragments of 1 KiB, in K order; fragment byte 16*l..16*l+15
+//   holds row (l % 16) of the tile, columns 32c + 8(l/16) .. +7 (8 bf16).
+//   This is the A-operand register layout of v_mfma_f32_16x16x32_bf16, so
+//   one wave streams a fragment with a single coalesced 1 KiB load.
+//   P1 row r of tile t (q = (r%16)/4, s = r%4) is column i = 8t + 2q + s/2
+//   of W1 (s even) or W3 (s odd): the accumulator lane that ends up with
+//   rows 4q..4q+3 holds gate and up values of two consecutive i.
+//   P2 row n is column n of W2.
+// int4 (MOE_W_INT4): the same row order. A row tile is K/128 blocks of 1 KiB;
+//   block g, byte 16*l..16*l+15 = four 32-bit words, word j holding the codes
+//   of row (l%16), columns 128g + 32j + 8(l/16) + 0..7 as nibbles
+//   (nibble p, bits 4p..4p+3): code(k0),code(k2),code(k4),code(k6),
+//   code(k1),code(k3),code(k5),code(k7); nibble = q + 8.
+//   Scales: per row tile and block, the 16 rows' fp16 scales (32 B).
+//   Sections: [P1 codes][P1 scales][P2 codes][P2 scales], 256-B aligned.
+// fp32 (MOE_W_F32): W1 [H,I], W3 [H,I], W2 [I,H] row-major, concatenated.
+// ---------------------------------------------------------------------------
+struct BlobLayout {
+  size_t p1, p1s, p2, p2s, bytes;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline BlobLayout blob_layout(int wfmt, int H, int I) {
+  BlobLayout b{};
+  const size_t HI = (size_t)H * I;
+  if (wfmt == 0) {  // fp32
+    b.p1 = 0; b.p2 = 2 * HI * 4; b.bytes = 3 * HI * 4;
+  } else if (wfmt == 1) {  // bf16
+    b.p1 = 0; b.p2 = 2 * HI * 2; b.bytes = 3 * HI * 2;
+  } else {  // int4
+    b.p1 = 0;
+    b.p1s = align_up(b.p1 + HI, 256);                       // 2HI codes * 0.5 B
+    b.p2 = align_up(b.p1s + (size_t)(2 * I / 16) * (H / 128) * 32, 256);
+    b.p2s = align_up(b.p2 + HI / 2, 256);
+    b.bytes = align_up(b.p2s + (size_t)(H / 16) * (I / 128) * 32, 256);
+  }
+  return b;
+}
+
+// P1 row r (0..2I-1) -> (matrix 0 = W1 / 1 = W3, column i).
+__host__ __device__ inline void p1_row_source(int r, int& mat, int& i) {
+  const int t = r >> 4, rr = r & 15, q = rr >> 2, s = rr & 3;
+  i = 8 * t + 2 * q + (s >> 1);
+  mat = s & 1;
+}
+
+// Work items passed by value in the kernel arguments.
+constexpr int kMaxItems = 64;
+struct WorkArgs {
+  int n;
+  int total_tiles;
+  int tile_prefix[kMaxItems + 1];  // prefix sums of per-item tile counts (prefill GEMM)
+  int4 item[kMaxItems];            // {slot, row_begin, rows, expert}
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (return hipError_t of the launch).
+// ---------------------------------------------------------------------------
+size_t route_workspace_bytes(int T, int H, int E, int k);
+hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
+                        int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
+                        int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s);
+
+hipError_t launch_pack(int wfmt, int H, int I, const void* W1, const void* W3, const void* W2,
+                       const void* s1, const void* s3, const void* s2, void* blob, hipStream_t s);
+
+hipError_t launch_combine(const float* y_perm, const int32_t* perm_pos, const float* w, int T, int k, int H,
+                          void* out, bool out_bf16, hipStream_t s);
+
+// FFN: decode (matrix-vector) kernels for groups of <= 16*? rows, prefill GEMM otherwise.
+hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, const WorkArgs& wa,
+                             const char* slot_base, size_t slot_stride, int H, int I,
+                             void* hbuf, void* xg, float* y, hipStream_t s);
+hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,
+                              size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s);
+bool prefill_supported(int wfmt, int H, int I);
+constexpr int kGemmBM = 128;  // tokens per GEMM tile
+constexpr int kGemmBN = 128;  // output rows per GEMM tile
+
+}  // namespace moe

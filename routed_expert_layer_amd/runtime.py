@@ -1,0 +1,187 @@
+"""Sequencing of the C-ABI calls into a decode layer-step and a prefill layer.
+
+No arithmetic of the layer happens here: routing, expert FFN and combine run in
+the HIP library, the cache policy in its C++ host code, and the fills as
+host-to-device copies it issues. This module owns the buffers (torch device
+tensors, page-locked host memory from the library) and the order of calls.
+
+Page "FreeToken-rtx-4090": the complete expert pool lives in host memory, the
+GPU holds a cache of complete layer-and-expert entries (section "How the MoE
+Memory Hierarchy Works"); decode resolves each step's experts against a shared
+LRU and moves only the missing ones (component table, rows "GPU memory" and
+"PCIe link"); prefill streams the next layer's experts while the current layer
+computes (phase table, row "Prefill").
+"""
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+WFMT = {"f32": L.MOE_W_F32, "bf16": L.MOE_W_BF16, "int4": L.MOE_W_INT4}
+
+
+def _align(v, a):
+    return (v + a - 1) // a * a
+
+
+def host_view(addr, nbytes):
+    """A CPU uint8 tensor over library-owned page-locked memory (no copy)."""
+    buf = (ctypes.c_uint8 * nbytes).from_address(addr)
+    return torch.frombuffer(buf, dtype=torch.uint8, count=nbytes)
+
+
+class ExpertStore:
+    """All experts of L layers as packed blobs in one page-locked host pool.
+
+    Blob of (layer, expert) sits at key * stride, key = layer * E + expert.
+    """
+
+    def __init__(self, n_layers, E, H, I, wfmt):
+        self.L, self.E, self.H, self.I = n_layers, E, H, I
+        self.wfmt = WFMT[wfmt] if isinstance(wfmt, str) else wfmt
+        self.blob = L.moe_expert_bytes(self.wfmt, H, I)
+        if self.blob == 0:
+            raise ValueError(f"unsupported expert shape {H}x{I} for format {wfmt}")
+        self.stride = _align(self.blob, 4096)
+        self.nbytes = n_layers * E * self.stride
+        self.pool = L.moe_pool_alloc(self.nbytes)
+        self.view = host_view(self.pool, self.nbytes)
+
+    def layer_addr(self, layer):
+        return self.pool + layer * self.E * self.stride
+
+    def pack_layer(self, layer, make_expert, device="cuda", batch=16):
+        """Pack every expert of `layer` into the pool.
+
+        make_expert(e) returns canonical device tensors: (W1, W3, W2) for fp32/bf16,
+        or a dict with q1, q3, q2 (int8) and s1, s3, s2 (fp16) for int4.
+        """
+        stage = torch.empty(batch * self.stride, dtype=torch.uint8, device=device)
+        for e0 in range(0, self.E, batch):
+            n = min(batch, self.E - e0)
+            for j in range(n):
+                w = make_expert(e0 + j)
+                dst = stage[j * self.stride:]
+                if self.wfmt == L.MOE_W_INT4:
+                    L.moe_pack_expert(self.wfmt, self.H, self.I, w["q1"], w["q3"], w["q2"], w["s1"], w["s3"],
+                                      w["s2"], dst)
+                else:
+                    L.moe_pack_expert(self.wfmt, self.H, self.I, w[0], w[1], w[2], None, None, None, dst)
+            off = (layer * self.E + e0) * self.stride
+            self.view[off:off + n * self.stride].copy_(stage[:n * self.stride])
+        torch.cuda.synchronize()
+
+    def close(self):
+        if self.pool:
+            self.view = None
+            L.moe_pool_free(self.pool)
+            self.pool = None
+
+
+class RouteBuffers:
+    """Device outputs of moe_route for up to T tokens."""
+
+    def __init__(self, T, H, E, k, device="cuda", keep_logits=False):
+        self.T, self.H, self.E, self.k = T, H, E, k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_idx = torch.empty((T, k), **i32)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=device) if keep_logits else None
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.perm_src = torch.empty(max(T * k, 1), **i32)
+        self.perm_pos = torch.empty((T, k), **i32)
+        self.ws = torch.empty(L.moe_route_workspace_size(T, H, E, k), dtype=torch.uint8, device=device)
+        self.counts_host = torch.empty(E, dtype=torch.int32, pin_memory=True)
+
+    def route(self, x, Wr, bias, stream=None):
+        T = x.shape[0]
+        assert T <= self.T
+        L.moe_route(x, Wr, bias, self.k, self.topk_idx[:T], self.topk_w[:T],
+                    None if self.logits is None else self.logits[:T], self.counts, self.offsets, self.perm_src,
+                    self.perm_pos[:T], self.ws, stream)
+
+    def fetch_counts(self, stream=None):
+        """Device-to-host copy of the per-expert counts; waits for it (the one sync point)."""
+        s = stream or torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            self.counts_host.copy_(self.counts, non_blocking=True)
+        s.synchronize()
+        c = self.counts_host.numpy().astype(np.int64)
+        off = np.zeros(len(c) + 1, np.int64)
+        np.cumsum(c, out=off[1:])
+        return c, off
+
+
+class DecodeLayer:
+    """Decode path: route -> host LRU -> fills -> grouped FFN -> combine, for one cache."""
+
+    def __init__(self, store, n_slots, T, k, act, device="cuda", keep_logits=False):
+        self.store, self.S, self.k = store, n_slots, k
+        self.H, self.I, self.E = store.H, store.I, store.E
+        self.act = act
+        self.rb = RouteBuffers(T, self.H, self.E, k, device, keep_logits)
+        self.cache = L.MoeCache(store.L, store.E, n_slots)
+        self.slots = torch.empty(n_slots * store.stride, dtype=torch.uint8, device=device)
+        rows = T * k
+        self.y_perm = torch.empty((max(rows, 1), self.H), dtype=torch.float32, device=device)
+        self.ffn_ws = torch.empty(L.moe_ffn_workspace_size(rows, self.H, self.I, store.wfmt), dtype=torch.uint8,
+                                  device=device)
+        self.out = torch.empty((T, self.H), dtype=torch.float32, device=device)
+        self.fill_stream = torch.cuda.Stream(device=device)
+        self.n_fills = 0
+
+    def step(self, step, layer, x, Wr, bias, stream=None):
+        s = stream or torch.cuda.current_stream()
+        T = x.shape[0]
+        rb = self.rb
+        rb.route(x, Wr, bias, s)
+        counts, off = rb.fetch_counts(s)
+        experts = np.nonzero(counts)[0].astype(np.int32)
+        we, wslot, wwave, misses, n_waves = L.cache_resolve(self.cache, step, layer, experts)
+        for w in range(n_waves):
+            m = misses[misses[:, 3] == w]
+            if len(m):
+                L.cache_fill_async(self.cache, m, self.store.pool, self.store.stride, self.store.blob, self.slots,
+                                   self.store.stride, self.fill_stream, s)
+                self.n_fills += len(m)
+            sel = wwave == w
+            e = we[sel]
+            work = np.stack([e, wslot[sel], off[e], counts[e]], axis=1).astype(np.int32)
+            L.moe_ffn(x, rb.perm_src, work, self.slots, self.store.stride, self.store.wfmt, self.H, self.I,
+                      self.y_perm, self.ffn_ws, L.MOE_FFN_AUTO, s)
+        L.moe_combine(self.y_perm, rb.perm_pos[:T], rb.topk_w[:T], self.out[:T], s)
+        return self.out[:T]
+
+    def trace(self):
+        return L.moe_cache_trace(self.cache)
+
+
+class PrefillLayer:
+    """Prefill path over a layer whose experts are all resident (blob of expert e at base + e*stride)."""
+
+    def __init__(self, H, I, E, k, T, stride, device="cuda", keep_logits=False, mode=L.MOE_FFN_AUTO):
+        self.H, self.I, self.E, self.k, self.stride, self.mode = H, I, E, k, stride, mode
+        self.rb = RouteBuffers(T, H, E, k, device, keep_logits)
+        rows = T * k
+        self.y_perm = torch.empty((max(rows, 1), H), dtype=torch.float32, device=device)
+        self.ffn_ws = torch.empty(L.moe_ffn_workspace_size(rows, H, I, L.MOE_W_BF16), dtype=torch.uint8,
+                                  device=device)
+        self.out = torch.empty((T, H), dtype=torch.float32, device=device)
+        self.last_counts = None
+
+    def forward(self, x, Wr, bias, layer_base, wfmt=L.MOE_W_BF16, stream=None):
+        s = stream or torch.cuda.current_stream()
+        T = x.shape[0]
+        rb = self.rb
+        rb.route(x, Wr, bias, s)
+        counts, off = rb.fetch_counts(s)
+        self.last_counts = counts
+        e = np.nonzero(counts)[0]
+        work = np.stack([e, e, off[e], counts[e]], axis=1).astype(np.int32)
+        L.moe_ffn(x, rb.perm_src, work, layer_base, self.stride, wfmt, self.H, self.I, self.y_perm, self.ffn_ws,
+                  self.mode, s)
+        L.moe_combine(self.y_perm, rb.perm_pos[:T], rb.topk_w[:T], self.out[:T], s)
+        return self.out[:T]

@@ -1,0 +1,193 @@
+"""GPU parity of each kernel stage against the oracle, with the oracle's inputs
+injected per stage (routing, grouped FFN, combine) at sizes the oracle checks
+element by element: several tiles plus ragged tails, empty groups, k = 1 and
+k = E, every weight format.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.parity import check_close, check_permutation, check_routing, np64, npi
+from workloads import CONFIGS, gen
+
+pytestmark = pytest.mark.gpu
+
+dev = "cuda"
+
+
+@pytest.fixture(scope="module")
+def L():
+    from routed_expert_layer_amd import _lib
+    return _lib
+
+
+def cfg_like(base, **kw):
+    return dataclasses.replace(CONFIGS[base], **kw)
+
+
+# ---------------------------------------------------------------------------
+# Routing
+# ---------------------------------------------------------------------------
+ROUTE_CASES = [
+    # name, base config, overrides
+    ("tiny_f32", "tiny_f32_h256_e16", {}),
+    ("decode_bf16_t1", "decode_bf16_h4096_e256", {}),
+    ("stack_bf16_t4", "stack48_bf16_h2048_e128", {}),
+    ("ragged_bf16_t300", "decode_bf16_h4096_e256", dict(name="ragged300", T=300, H=512, E=64, k=6)),
+    ("k1", "tiny_f32_h256_e16", dict(name="k1", T=77, k=1)),
+    ("k_eq_e", "tiny_f32_h256_e16", dict(name="kE", T=70, E=8, k=8)),
+    ("e_not_mult64_bf16", "decode_bf16_h4096_e256", dict(name="e100", T=130, H=256, E=100, k=5, zipf_s=1.5)),
+    ("t0", "tiny_f32_h256_e16", dict(name="t0", T=0)),
+]
+
+
+@pytest.mark.parametrize("name,base,kw", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_parity(L, name, base, kw):
+    from routed_expert_layer_amd.runtime import RouteBuffers
+    cfg = cfg_like(base, **kw)
+    print(f"route case {name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} {cfg.act}", flush=True)
+    rb = RouteBuffers(max(cfg.T, 1), cfg.H, cfg.E, cfg.k, dev, keep_logits=True)
+    Wr = gen.router_weight(cfg, 0, dev)
+    steps = 4 if cfg.T > 1 else 16
+    for step in range(steps):
+        b = gen.router_bias(cfg, 0, step, dev)
+        x = gen.tokens(cfg, step, 0, dev)
+        rb.route(x, Wr, b)
+        torch.cuda.synchronize()
+        T = cfg.T
+        counts = npi(rb.counts)
+        offsets = npi(rb.offsets)
+        if T == 0:
+            assert counts.sum() == 0 and np.all(offsets == 0)
+            continue
+        l64 = oracle.router_logits(x, Wr, b)
+        check_close(np64(rb.logits[:T]), l64, "logits", rel_l2=1e-5, max_abs_rms=1e-4)
+        idx = npi(rb.topk_idx[:T])
+        check_routing(idx, np64(rb.topk_w[:T]), l64, cfg.k)
+        check_permutation(idx, counts, offsets, npi(rb.perm_src[:T * cfg.k]), npi(rb.perm_pos[:T]), cfg.E)
+
+
+def test_route_ties_and_signed_zero(L):
+    """Exact ties (all-zero gate) go to the lower expert index; -0 equals +0."""
+    from routed_expert_layer_amd.runtime import RouteBuffers
+    T, H, E, k = 65, 64, 20, 4
+    rb = RouteBuffers(T, H, E, k, dev, keep_logits=True)
+    x = torch.zeros((T, H), dtype=torch.float32, device=dev)
+    Wr = torch.zeros((H, E), dtype=torch.float32, device=dev)
+    b = torch.zeros(E, dtype=torch.float32, device=dev)
+    b[5] = -0.0
+    b[7] = 1.0
+    b[9] = 1.0
+    rb.route(x, Wr, b)
+    torch.cuda.synchronize()
+    idx = npi(rb.topk_idx)
+    assert np.all(idx == np.array([7, 9, 0, 1]))
+    w = np64(rb.topk_w)
+    e = np.exp(-1.0)
+    assert np.allclose(w, np.array([1, 1, e, e]) / (2 + 2 * e), atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Grouped expert FFN (teacher-forced routing)
+# ---------------------------------------------------------------------------
+def _experts(cfg, n, wfmt):
+    out = []
+    for e in range(n):
+        if wfmt == "int4":
+            out.append(gen.expert_int4(cfg, 0, e, dev))
+        else:
+            out.append(gen.expert_weights(cfg, 0, e, dev))
+    return out
+
+
+def _canon64(w, wfmt, group=128):
+    if wfmt == "int4":
+        return (oracle.dequant_int4(w["q1"], w["s1"], group), oracle.dequant_int4(w["q3"], w["s3"], group),
+                oracle.dequant_int4(w["q2"], w["s2"], group))
+    return tuple(np64(t) for t in w)
+
+
+FFN_CASES = [
+    # name, wfmt, H, I, rows per expert, mode
+    ("f32_tiny", "f32", 256, 128, [3, 0, 1, 8, 2], "auto"),
+    ("bf16_decode", "bf16", 512, 256, [1, 0, 6, 16, 17, 2, 33], "decode"),
+    ("bf16_decode_k_odd", "bf16", 384, 160, [5, 1, 0, 9], "decode"),
+    ("bf16_prefill", "bf16", 512, 256, [130, 0, 1, 127, 128, 300, 17], "prefill"),
+    ("bf16_prefill_c3shape", "bf16", 2048, 768, [70, 3, 129], "prefill"),
+    ("int4_decode", "int4", 512, 256, [1, 8, 0, 3, 20], "decode"),
+    ("int4_decode_wide", "int4", 1024, 384, [2, 16, 5], "decode"),
+]
+
+
+@pytest.mark.parametrize("name,wfmt,H,I,rows,mode", FFN_CASES, ids=[c[0] for c in FFN_CASES])
+def test_ffn_parity(L, name, wfmt, H, I, rows, mode):
+    print(f"ffn case {name}: {wfmt} H={H} I={I} rows={rows} mode={mode}", flush=True)
+    act = "f32" if wfmt == "f32" else "bf16"
+    cfg = cfg_like("tiny_f32_h256_e16", name=f"ffn_{name}", H=H, I=I, E=len(rows), act=act, wfmt=wfmt)
+    E = len(rows)
+    T = max(40, max(rows))
+    x = gen.tokens(cfg, 0, 0, dev, T=T)
+    r = np.random.default_rng(len(name))
+    perm_src = np.concatenate([r.integers(0, T, size=n) for n in rows]).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    wf = {"f32": L.MOE_W_F32, "bf16": L.MOE_W_BF16, "int4": L.MOE_W_INT4}[wfmt]
+    blob = L.moe_expert_bytes(wf, H, I)
+    stride = (blob + 4095) // 4096 * 4096
+    slot_of = [(e + 1) % E for e in range(E)]  # non-identity slot mapping
+    slots = torch.zeros(E * stride, dtype=torch.uint8, device=dev)
+    ex = _experts(cfg, E, wfmt)
+    for e in range(E):
+        w = ex[e]
+        dst = slots[slot_of[e] * stride:]
+        if wfmt == "int4":
+            L.moe_pack_expert(wf, H, I, w["q1"], w["q3"], w["q2"], w["s1"], w["s3"], w["s2"], dst)
+        else:
+            L.moe_pack_expert(wf, H, I, w[0], w[1], w[2], None, None, None, dst)
+    work = np.array([[e, slot_of[e], off[e], rows[e]] for e in range(E)], dtype=np.int32)
+    rows_total = int(off[-1])
+    y = torch.full((rows_total, H), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(L.moe_ffn_workspace_size(rows_total, H, I, wf), dtype=torch.uint8, device=dev)
+    ps = torch.from_numpy(perm_src).to(dev)
+    m = {"auto": L.MOE_FFN_AUTO, "decode": L.MOE_FFN_DECODE, "prefill": L.MOE_FFN_PREFILL}[mode]
+    L.moe_ffn(x, ps, work, slots, stride, wf, H, I, y, ws, m)
+    torch.cuda.synchronize()
+    yg = np64(y)
+    x64 = np64(x)
+    for e in range(E):
+        a, b = off[e], off[e + 1]
+        if b == a:
+            continue
+        ref = oracle.swiglu_expert(x64[perm_src[a:b]], *_canon64(ex[e], wfmt))
+        check_close(yg[a:b], ref, f"{name} expert {e}")
+
+
+def test_ffn_zero_work_is_noop(L):
+    y = torch.zeros((4, 256), dtype=torch.float32, device=dev)
+    ws = torch.empty(1024, dtype=torch.uint8, device=dev)
+    x = torch.zeros((4, 256), dtype=torch.bfloat16, device=dev)
+    L.moe_ffn(x, torch.zeros(4, dtype=torch.int32, device=dev), np.zeros((0, 4), np.int32), y, 1 << 20,
+              L.MOE_W_BF16, 256, 128, y, ws)
+    torch.cuda.synchronize()
+    assert float(y.abs().sum()) == 0.0
+
+
+# ---------------------------------------------------------------------------
+# Combine
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,k,H,out_bf16", [(1, 6, 4096, False), (37, 2, 256, False), (5, 3, 130, True)])
+def test_combine_parity(L, T, k, H, out_bf16):
+    g = torch.Generator(device=dev).manual_seed(T * 1000 + H)
+    y = torch.randn((T * k, H), generator=g, device=dev)
+    perm_pos = torch.randperm(T * k, generator=g, device=dev).to(torch.int32).reshape(T, k)
+    w = torch.rand((T, k), generator=g, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16 if out_bf16 else torch.float32, device=dev)
+    L.moe_combine(y, perm_pos, w, out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(np64(y), npi(perm_pos), np64(w))
+    if out_bf16:
+        check_close(np64(out), ref, "combine bf16", rel_l2=4e-3)
+    else:
+        check_close(np64(out), ref, "combine", rel_l2=1e-6, max_abs_rms=1e-5)
