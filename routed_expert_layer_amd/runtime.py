@@ -133,7 +133,18 @@ class DecodeLayer:
         self.fill_stream = torch.cuda.Stream(device=device)
         self.n_fills = 0
 
-    def step(self, step, layer, x, Wr, bias, stream=None):
+    def algorithmic_bytes(self, work):
+        """Bytes the expert FFN must move for a work list: each listed expert's
+        weights once, plus its rows of x (read), the SwiGLU product (write and
+        read) and y (write)."""
+        a = 2 if self.act == "bf16" else 4
+        h = 2 if self.store.wfmt != L.MOE_W_F32 else 4
+        rows = int(np.sum(work[:, 3]))
+        return len(work) * self.store.blob + rows * (self.H * a + 2 * self.I * h + self.H * 4)
+
+    def step(self, step, layer, x, Wr, bias, stream=None, timer=None):
+        """One layer-step. `timer`, if given, gets timer.begin(stream) and
+        timer.end(stream, algorithmic_bytes) around every expert-FFN call."""
         s = stream or torch.cuda.current_stream()
         T = x.shape[0]
         rb = self.rb
@@ -150,8 +161,12 @@ class DecodeLayer:
             sel = wwave == w
             e = we[sel]
             work = np.stack([e, wslot[sel], off[e], counts[e]], axis=1).astype(np.int32)
+            if timer is not None:
+                timer.begin(s)
             L.moe_ffn(x, rb.perm_src, work, self.slots, self.store.stride, self.store.wfmt, self.H, self.I,
                       self.y_perm, self.ffn_ws, L.MOE_FFN_AUTO, s)
+            if timer is not None:
+                timer.end(s, self.algorithmic_bytes(work))
         L.moe_combine(self.y_perm, rb.perm_pos[:T], rb.topk_w[:T], self.out[:T], s)
         return self.out[:T]
 
@@ -172,7 +187,7 @@ class PrefillLayer:
         self.out = torch.empty((T, H), dtype=torch.float32, device=device)
         self.last_counts = None
 
-    def forward(self, x, Wr, bias, layer_base, wfmt=L.MOE_W_BF16, stream=None):
+    def forward(self, x, Wr, bias, layer_base, wfmt=L.MOE_W_BF16, stream=None, timer=None):
         s = stream or torch.cuda.current_stream()
         T = x.shape[0]
         rb = self.rb
@@ -181,7 +196,11 @@ class PrefillLayer:
         self.last_counts = counts
         e = np.nonzero(counts)[0]
         work = np.stack([e, e, off[e], counts[e]], axis=1).astype(np.int32)
+        if timer is not None:
+            timer.begin(s)
         L.moe_ffn(x, rb.perm_src, work, layer_base, self.stride, wfmt, self.H, self.I, self.y_perm, self.ffn_ws,
                   self.mode, s)
+        if timer is not None:
+            timer.end(s, 6.0 * self.H * self.I * int(counts.sum()))  # expert FLOPs of the routed pairs
         L.moe_combine(self.y_perm, rb.perm_pos[:T], rb.topk_w[:T], self.out[:T], s)
         return self.out[:T]

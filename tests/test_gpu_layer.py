@@ -1,0 +1,195 @@
+"""End-to-end GPU parity of the layer on the workload configurations.
+
+Routing, permutation and the cache trace are compared on every step; the
+layer output is compared on every step for the tiny config and on seeded
+samples of steps / tokens at full size, where the oracle evaluates only the
+experts the sampled tokens use.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.parity import check_close, check_permutation, check_routing, np64, npi
+from workloads import CONFIGS, gen
+
+pytestmark = pytest.mark.gpu
+dev = "cuda"
+
+
+class ExpertCache64:
+    """fp64 canonical weights of experts, regenerated on demand (bounded)."""
+
+    def __init__(self, cfg, layer, cap=48):
+        self.cfg, self.layer, self.cap, self.d = cfg, layer, cap, {}
+
+    def __call__(self, e):
+        e = int(e)
+        if e not in self.d:
+            if len(self.d) >= self.cap:
+                self.d.pop(next(iter(self.d)))
+            if self.cfg.wfmt == "int4":
+                w = gen.expert_int4(self.cfg, self.layer, e, dev)
+                g = self.cfg.group
+                self.d[e] = (oracle.dequant_int4(w["q1"], w["s1"], g), oracle.dequant_int4(w["q3"], w["s3"], g),
+                             oracle.dequant_int4(w["q2"], w["s2"], g))
+            else:
+                self.d[e] = tuple(np64(t) for t in gen.expert_weights(self.cfg, self.layer, e, dev))
+        return self.d[e]
+
+
+def oracle_out_rows(x64, idx, l64, tokens, get_expert):
+    """Oracle outputs of the listed tokens for the given selection (fp64 weights of that selection)."""
+    w = oracle.topk_weights(l64[tokens], idx[tokens])
+    out = np.zeros((len(tokens), x64.shape[1]))
+    for n, t in enumerate(tokens):
+        for j, e in enumerate(idx[t]):
+            out[n] += w[n, j] * oracle.swiglu_expert(x64[t:t + 1], *get_expert(e))[0]
+    return out
+
+
+def make_store(cfg, layers):
+    from routed_expert_layer_amd.runtime import ExpertStore
+    store = ExpertStore(cfg.L, cfg.E, cfg.H, cfg.I, cfg.wfmt)
+    for layer in layers:
+        print(f"  packing layer {layer} ({cfg.E} experts)", flush=True)
+        if cfg.wfmt == "int4":
+            store.pack_layer(layer, lambda e: gen.expert_int4(cfg, layer, e, dev))
+        else:
+            store.pack_layer(layer, lambda e: gen.expert_weights(cfg, layer, e, dev))
+    return store
+
+
+def run_decode(cfg, steps, out_check, check_all_outputs=False):
+    """Drive DecodeLayer over `steps` x all layers; check routing, trace, and sampled outputs."""
+    from routed_expert_layer_amd.runtime import DecodeLayer
+    print(f"decode {cfg.name}: L={cfg.L} T={cfg.T} steps={steps} S={cfg.S} {cfg.wfmt}", flush=True)
+    store = make_store(cfg, range(cfg.L))
+    try:
+        dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev, keep_logits=True)
+        Wr = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
+        sim = oracle.SharedLRU(cfg.S)
+        experts64 = {}
+        for step in range(steps):
+            for layer in range(cfg.L):
+                b = gen.router_bias(cfg, layer, step, dev)
+                x = gen.tokens(cfg, step, layer, dev)
+                out = dl.step(step, layer, x, Wr[layer], b)
+                torch.cuda.synchronize()
+                l64 = oracle.router_logits(x, Wr[layer], b)
+                idx = npi(dl.rb.topk_idx[:cfg.T])
+                check_routing(idx, np64(dl.rb.topk_w[:cfg.T]), l64, cfg.k)
+                counts, _, _, _ = check_permutation(idx, npi(dl.rb.counts), npi(dl.rb.offsets),
+                                                    npi(dl.rb.perm_src[:cfg.T * cfg.k]), npi(dl.rb.perm_pos[:cfg.T]),
+                                                    cfg.E)
+                sim.resolve(step, layer, cfg.E, np.nonzero(counts)[0])
+                if check_all_outputs or (step, layer) in out_check:
+                    ge = experts64.setdefault(layer, ExpertCache64(cfg, layer))
+                    ref = oracle_out_rows(np64(x), idx, l64, list(range(cfg.T)), ge)
+                    check_close(np64(out), ref, f"{cfg.name} step {step} layer {layer}")
+        trace = dl.trace()
+        ref = np.array([[r.step, r.layer, r.key, r.hit, r.slot, r.victim, r.wave] for r in sim.trace], np.int64)
+        assert trace.shape == ref.shape, f"trace length {trace.shape} vs {ref.shape}"
+        assert np.array_equal(trace, ref), "cache trace differs from the oracle's LRU"
+        hits, misses = int(ref[:, 3].sum()), int((1 - ref[:, 3]).sum())
+        print(f"  trace ok: {len(ref)} accesses, hit rate {hits / max(len(ref), 1):.3f}, fills {dl.n_fills}, "
+              f"waves>1 in {int((ref[:, 6] > 0).sum())} accesses", flush=True)
+        assert dl.n_fills == misses
+        return ref
+    finally:
+        store.close()
+
+
+def test_tiny_fp32_all_steps():
+    cfg = CONFIGS["tiny_f32_h256_e16"]
+    ref = run_decode(cfg, cfg.steps, set(), check_all_outputs=True)
+    assert (ref[:, 6] > 0).any(), "the tiny config should exercise multi-wave layer-steps"
+
+
+@pytest.mark.timeout(600)
+def test_decode_bf16_full():
+    cfg = CONFIGS["decode_bf16_h4096_e256"]
+    run_decode(cfg, cfg.steps, {(s, 0) for s in (0, 1, 2, 63, 511, 1023)})
+
+
+@pytest.mark.timeout(600)
+def test_stack48_bf16_cut():
+    cfg = CONFIGS["stack48_bf16_h2048_e128"]
+    r = np.random.default_rng(3)
+    sample = {(int(s), int(l)) for s, l in zip(r.integers(0, 40, 6), r.integers(0, 48, 6))}
+    run_decode(cfg, 40, sample)
+
+
+@pytest.mark.timeout(600)
+def test_decode_int4_cut():
+    cfg = CONFIGS["decode_int4_t8_l8"]
+    run_decode(cfg, 48, {(0, 0), (5, 3), (47, 7)})
+
+
+def _prefill_check(cfg, layer, pl, x, Wr, b, n_sample=24):
+    T = cfg.T
+    l64 = oracle.router_logits(x, Wr, b)
+    idx = npi(pl.rb.topk_idx[:T])
+    check_routing(idx, np64(pl.rb.topk_w[:T]), l64, cfg.k)
+    check_permutation(idx, npi(pl.rb.counts), npi(pl.rb.offsets), npi(pl.rb.perm_src[:T * cfg.k]),
+                      npi(pl.rb.perm_pos[:T]), cfg.E)
+    r = np.random.default_rng(1000 + layer)
+    tokens = sorted(r.choice(T, n_sample, replace=False).tolist())
+    # include tokens of the smallest and largest groups
+    counts = npi(pl.rb.counts)
+    for e in (int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30)))):
+        tokens.append(int(np.nonzero((idx == e).any(1))[0][0]))
+    tokens = sorted(set(tokens))
+    ref = oracle_out_rows(np64(x), idx, l64, tokens, ExpertCache64(cfg, layer, cap=64))
+    check_close(np64(pl.out[tokens]), ref, f"{cfg.name} layer {layer}")
+    return counts
+
+
+@pytest.mark.timeout(600)
+def test_prefill_4096_resident():
+    from routed_expert_layer_amd import _lib as L
+    from routed_expert_layer_amd.runtime import PrefillLayer
+    cfg = CONFIGS["prefill_bf16_t4096_e256"]
+    blob = L.moe_expert_bytes(L.MOE_W_BF16, cfg.H, cfg.I)
+    stride = (blob + 4095) // 4096 * 4096
+    buf = torch.empty(cfg.E * stride, dtype=torch.uint8, device=dev)
+    for e in range(cfg.E):
+        W1, W3, W2 = gen.expert_weights(cfg, 0, e, dev)
+        L.moe_pack_expert(L.MOE_W_BF16, cfg.H, cfg.I, W1, W3, W2, None, None, None, buf[e * stride:])
+    pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, stride, dev, keep_logits=True)
+    Wr = gen.router_weight(cfg, 0, dev)
+    b = gen.router_bias(cfg, 0, 0, dev)
+    x = gen.tokens(cfg, 0, 0, dev)
+    pl.forward(x, Wr, b, buf)
+    torch.cuda.synchronize()
+    counts = _prefill_check(cfg, 0, pl, x, Wr, b)
+    print(f"  tokens per expert: min {counts.min()} max {counts.max()} mean {counts.mean():.1f}", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_16384_double_buffered():
+    from routed_expert_layer_amd import _lib as L
+    from routed_expert_layer_amd.runtime import PrefillLayer
+    cfg = CONFIGS["prefill_db_bf16_t16384_l8"]
+    store = make_store(cfg, range(cfg.L))
+    try:
+        layer_bytes = cfg.E * store.stride
+        pipe = L.MoePipe(store.pool, layer_bytes, layer_bytes, cfg.L)
+        pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, store.stride, dev, keep_logits=True)
+        s = torch.cuda.current_stream()
+        for layer in range(cfg.L):
+            Wr = gen.router_weight(cfg, layer, dev)
+            b = gen.router_bias(cfg, layer, 0, dev)
+            x = gen.tokens(cfg, 0, layer, dev)
+            base = L.moe_pipe_begin_layer(pipe, layer, s)
+            pl.forward(x, Wr, b, base)
+            L.moe_pipe_end_layer(pipe, layer, s)
+            torch.cuda.synchronize()
+            counts = _prefill_check(cfg, layer, pl, x, Wr, b, n_sample=8)
+            print(f"  layer {layer}: active experts {int((counts > 0).sum())}, max group {counts.max()}, "
+                  f"copy {L.moe_pipe_copy_ms(pipe, layer):.1f} ms", flush=True)
+        pipe.close()
+    finally:
+        store.close()
