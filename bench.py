@@ -74,7 +74,6 @@ def bench_decode(args, torch, L, gen, cfg):
     Wr = gen.router_weight(cfg, 0, dev)
     biases = {}
     dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
-    timer = EventTimer(torch, args.steps * 4)
     s = torch.cuda.current_stream()
 
     def bias(step):
@@ -87,20 +86,21 @@ def bench_decode(args, torch, L, gen, cfg):
         dl.step(step, 0, xs[step], Wr, bias(step), s)
     torch.cuda.synchronize()
     fills0 = dl.n_fills
-    timer.enabled = True
+    L.moe_decoder_profile(dl.dec, True)  # HIP events around every expert-FFN call, on stream s
     lat = []
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     prev = t_start
     for step in range(args.warmup, n_total):
-        dl.step(step, 0, xs[step], Wr, bias(step), s, timer=timer)
+        dl.step(step, 0, xs[step], Wr, bias(step), s)
         now = time.perf_counter()
         lat.append(now - prev)
         prev = now
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     lat[-1] += time.perf_counter() - prev
-    ffn_bytes, ffn_ms, n_ffn = timer.result()
+    ffn_bytes, ffn_ms, n_ffn = L.moe_decoder_ffn_stats(dl.dec)
+    L.moe_decoder_profile(dl.dec, False)
     trace = dl.trace()
     timed = trace[trace[:, 0] >= args.warmup]
     hit_rate = float(timed[:, 3].mean()) if len(timed) else 0.0
@@ -207,6 +207,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many MiB (hardware-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer runs on a single MI355X and this build has no "
@@ -221,6 +223,14 @@ def main():
         print("bench.py times the one-layer bf16 decode workloads", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     res = bench_decode(args, torch, L, gen, cfg)
     ffn = res["ffn"]
     achieved = ffn["bytes"] / (ffn["ms"] * 1e-3) / 1e9 if ffn["ms"] > 0 else 0.0
@@ -239,7 +249,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens_per_step": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "intermediate": cfg.I, "top_k": cfg.k, "cache_slots": cfg.S, "router_zipf_s": cfg.zipf_s},
-        "roofline": {"kernel": "expert FFN (ffn1_decode_bf16 + ffn2_decode_bf16, one moe_ffn call)",
+        "roofline": {"kernel": "decode expert FFN: ffn1_decode_bf16 + ffn2_decode_bf16 (one moe_ffn call)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": round(ffn["bytes"] / max(ffn["n"], 1)),

@@ -269,6 +269,61 @@ int moe_pipe_begin_layer(moe_pipe_t* pipe, int layer, void* compute_stream, void
 int moe_pipe_end_layer(moe_pipe_t* pipe, int layer, void* compute_stream);
 int moe_pipe_copy_ms(moe_pipe_t* pipe, int layer, float* ms);
 
+/* ------------------------------------------------------------------------ *
+ * Decode layer-step driver.
+ *
+ * One call runs a whole decode layer-step -- moe_route, the copy of the
+ * per-expert counts to the host (the only device-to-host round trip),
+ * cache_resolve, cache_fill_async for each wave's misses on the decoder's own
+ * fill stream, moe_ffn for each wave, moe_combine -- with the semantics of
+ * those calls. Page "FreeToken-rtx-4090", phase table row "Decode" (the
+ * shared LRU cache) and component table rows "GPU memory" and "PCIe link".
+ *
+ * moe_decoder_create: `cache` is used (not owned); pool holds blob `key` at
+ *   pool + key*blob_stride (pinned host); slots at slot_base + slot*slot_stride
+ *   (device). `buffers` are caller-owned device buffers sized for T_max tokens:
+ *   topk_idx int32 [T_max,k], topk_w fp32 [T_max,k], logits fp32 [T_max,E] or
+ *   NULL, counts int32 [E], offsets int32 [E+1], perm_src int32 [T_max*k],
+ *   perm_pos int32 [T_max,k], y_perm fp32 [T_max*k,H], route_ws of at least
+ *   moe_route_workspace_size(T_max,H,E,k) bytes and ffn_ws of at least
+ *   moe_ffn_workspace_size(T_max*k,H,I,wfmt) bytes. After a step they hold
+ *   that step's routing.
+ * moe_decoder_step: x [T,H] (dtype), Wr [H,E], bias [E] or NULL, out [T,H] of
+ *   out_dtype; *n_miss (nullable) = fills issued. Blocks the calling thread
+ *   until the counts reach the host; the rest is enqueued on `stream`.
+ *   On a failed fill the affected keys are invalidated (never half-resident).
+ * moe_decoder_profile: when enabled, every FFN call is bracketed by HIP events
+ *   on `stream`; moe_decoder_ffn_stats returns the summed algorithmic bytes
+ *   (expert blobs read + activations read/written), summed milliseconds and
+ *   the number of FFN calls since profiling was enabled.
+ * moe_decoder_fills: total fills issued by this decoder.
+ * ------------------------------------------------------------------------ */
+typedef struct moe_decoder moe_decoder_t;
+typedef struct {
+  int32_t* topk_idx;
+  float* topk_w;
+  float* logits;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm_src;
+  int32_t* perm_pos;
+  float* y_perm;
+  void* route_ws;
+  size_t route_ws_bytes;
+  void* ffn_ws;
+  size_t ffn_ws_bytes;
+} moe_decoder_buffers_t;
+
+moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, int E, int k, int dtype, int wfmt,
+                                  const void* pool, size_t blob_stride, void* slot_base, size_t slot_stride,
+                                  const moe_decoder_buffers_t* buffers, int* status);
+int moe_decoder_destroy(moe_decoder_t* decoder);
+int moe_decoder_step(moe_decoder_t* decoder, int step, int layer, const void* x, int T, const void* Wr,
+                     const float* bias, void* out, int out_dtype, void* stream, int* n_miss);
+int moe_decoder_profile(moe_decoder_t* decoder, int enable);
+int moe_decoder_ffn_stats(moe_decoder_t* decoder, double* bytes, double* ms, int64_t* launches);
+int moe_decoder_fills(const moe_decoder_t* decoder, int64_t* fills);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,8 +23,16 @@ SYMBOLS = [
     "moe_pack_expert", "moe_pool_alloc", "moe_pool_free", "moe_cache_create", "moe_cache_destroy", "cache_resolve",
     "moe_cache_trace", "moe_cache_clear_trace", "moe_cache_invalidate", "moe_cache_slot_of", "moe_cache_stats",
     "cache_fill_async", "moe_ffn_workspace_size", "moe_ffn", "moe_combine", "moe_pipe_create", "moe_pipe_destroy",
-    "moe_pipe_begin_layer", "moe_pipe_end_layer", "moe_pipe_copy_ms",
+    "moe_pipe_begin_layer", "moe_pipe_end_layer", "moe_pipe_copy_ms", "moe_decoder_create", "moe_decoder_destroy",
+    "moe_decoder_step", "moe_decoder_profile", "moe_decoder_ffn_stats", "moe_decoder_fills",
 ]
+
+
+class DecoderBuffers(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("logits", ctypes.c_void_p),
+                ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("perm_src", ctypes.c_void_p),
+                ("perm_pos", ctypes.c_void_p), ("y_perm", ctypes.c_void_p), ("route_ws", ctypes.c_void_p),
+                ("route_ws_bytes", ctypes.c_size_t), ("ffn_ws", ctypes.c_void_p), ("ffn_ws_bytes", ctypes.c_size_t)]
 
 
 class MoEError(RuntimeError):
@@ -77,6 +85,12 @@ _sig("moe_pipe_destroy", I32, P)
 _sig("moe_pipe_begin_layer", I32, P, I32, P, ctypes.POINTER(ctypes.c_void_p))
 _sig("moe_pipe_end_layer", I32, P, I32, P)
 _sig("moe_pipe_copy_ms", I32, P, I32, ctypes.POINTER(ctypes.c_float))
+_sig("moe_decoder_create", P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, SZ, ctypes.POINTER(DecoderBuffers), PI)
+_sig("moe_decoder_destroy", I32, P)
+_sig("moe_decoder_step", I32, P, I32, I32, P, I32, P, P, P, I32, P, PI)
+_sig("moe_decoder_profile", I32, P, I32)
+_sig("moe_decoder_ffn_stats", I32, P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), PI64)
+_sig("moe_decoder_fills", I32, P, PI64)
 
 
 def _check(code, what=""):
@@ -294,3 +308,61 @@ def moe_pipe_copy_ms(pipe, layer):
     ms = ctypes.c_float(0)
     _check(_lib.moe_pipe_copy_ms(pipe.h, layer, ctypes.byref(ms)), "moe_pipe_copy_ms")
     return ms.value
+
+
+# ---------------------------------------------------------------------------
+class MoeDecoder:
+    """Owner of a moe_decoder_t; `bufs` maps DecoderBuffers field names to torch tensors (kept alive here)."""
+
+    def __init__(self, cache, T_max, H, I, E, k, dtype, wfmt, pool, blob_stride, slot_base, slot_stride, bufs):
+        self.keep = bufs
+        b = DecoderBuffers()
+        for name in ("topk_idx", "topk_w", "logits", "counts", "offsets", "perm_src", "perm_pos", "y_perm"):
+            setattr(b, name, _ptr(bufs.get(name)))
+        b.route_ws, b.route_ws_bytes = _ptr(bufs["route_ws"]), bufs["route_ws"].numel()
+        b.ffn_ws, b.ffn_ws_bytes = _ptr(bufs["ffn_ws"]), bufs["ffn_ws"].numel()
+        st = ctypes.c_int(0)
+        self.h = _lib.moe_decoder_create(cache.h, T_max, H, I, E, k, dtype, wfmt, _ptr(pool), blob_stride,
+                                         _ptr(slot_base), slot_stride, ctypes.byref(b), ctypes.byref(st))
+        if not self.h:
+            raise MoEError(st.value, _lib.moe_last_error().decode())
+        self.cache = cache
+
+    def close(self):
+        if self.h:
+            _lib.moe_decoder_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+
+def moe_decoder_create(*a, **kw):
+    return MoeDecoder(*a, **kw)
+
+
+def moe_decoder_destroy(dec):
+    dec.close()
+
+
+def moe_decoder_step(dec, step, layer, x, Wr, bias, out, stream=None):
+    nm = ctypes.c_int(0)
+    _check(_lib.moe_decoder_step(dec.h, step, layer, _ptr(x), x.shape[0], _ptr(Wr), _ptr(bias), _ptr(out),
+                                 _dtype_code(out), _stream(stream), ctypes.byref(nm)), "moe_decoder_step")
+    return nm.value
+
+
+def moe_decoder_profile(dec, enable):
+    _check(_lib.moe_decoder_profile(dec.h, 1 if enable else 0), "moe_decoder_profile")
+
+
+def moe_decoder_ffn_stats(dec):
+    b, m, n = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_int64(0)
+    _check(_lib.moe_decoder_ffn_stats(dec.h, ctypes.byref(b), ctypes.byref(m), ctypes.byref(n)),
+           "moe_decoder_ffn_stats")
+    return b.value, m.value, n.value
+
+
+def moe_decoder_fills(dec):
+    n = ctypes.c_int64(0)
+    _check(_lib.moe_decoder_fills(dec.h, ctypes.byref(n)), "moe_decoder_fills")
+    return n.value

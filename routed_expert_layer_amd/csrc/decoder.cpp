@@ -1,0 +1,233 @@
+// Native decode layer-step: the calls of the C ABI sequenced in C++ so that
+// one layer-step costs one host round trip (the per-expert counts) and no
+// interpreter overhead.
+//
+// Page "FreeToken-rtx-4090", phase table row "Decode": the bottleneck is
+// expert cache misses and the mechanism is the shared LRU cache; the
+// component table's "PCIe link" row: only the missing experts move.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_kernels.hpp"
+
+extern "C" const char* moe_last_error(void);
+
+namespace {
+// Errors go to the library's per-thread message (moe_last_error).
+template <typename... A>
+int dfail(int code, const char* fmt, A... a) {
+  return moe::set_error(code, fmt, a...);
+}
+}  // namespace
+
+struct moe_decoder {
+  moe_cache_t* cache;
+  int Tmax, H, I, E, k, dtype, wfmt;
+  const void* pool;
+  size_t blob_stride, blob_bytes;
+  void* slot_base;
+  size_t slot_stride;
+  moe_decoder_buffers_t b;
+  int32_t* counts_host = nullptr;
+  hipStream_t fill = nullptr;
+  hipEvent_t ev_counts = nullptr;
+  std::vector<int32_t> experts, work_e, work_slot, work_wave;
+  std::vector<moe_miss_t> misses, wave_misses;
+  std::vector<moe_work_t> work;
+  std::vector<int32_t> offs;
+  bool prof = false;
+  std::vector<hipEvent_t> ev_begin, ev_end;
+  std::vector<double> ev_bytes;
+  size_t ev_used = 0;
+  int64_t fills = 0;
+};
+
+extern "C" {
+
+static void decoder_release(moe_decoder_t* d) {
+  if (d->counts_host) (void)hipHostFree(d->counts_host);
+  if (d->fill) (void)hipStreamDestroy(d->fill);
+  if (d->ev_counts) (void)hipEventDestroy(d->ev_counts);
+  for (hipEvent_t e : d->ev_begin) (void)hipEventDestroy(e);
+  for (hipEvent_t e : d->ev_end) (void)hipEventDestroy(e);
+  delete d;
+}
+
+moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, int E, int k, int dtype, int wfmt,
+                                  const void* pool, size_t blob_stride, void* slot_base, size_t slot_stride,
+                                  const moe_decoder_buffers_t* buffers, int* status) {
+  auto bad = [&](int code, const char* msg) -> moe_decoder_t* {
+    if (status) *status = dfail(code, "moe_decoder_create: %s", msg);
+    return nullptr;
+  };
+  if (!cache || !pool || !slot_base || !buffers) return bad(MOE_EINVAL, "null argument");
+  if (T_max < 1 || H < 1 || I < 1 || E < 1 || k < 1 || k > E) return bad(MOE_EINVAL, "bad sizes");
+  const size_t blob = moe_expert_bytes(wfmt, H, I);
+  if (blob == 0) return bad(MOE_EINVAL, "unsupported weight format or shape");
+  if (blob_stride < blob || slot_stride < blob) return bad(MOE_EINVAL, "stride smaller than an expert blob");
+  const moe_decoder_buffers_t& b = *buffers;
+  if (!b.topk_idx || !b.topk_w || !b.counts || !b.offsets || !b.perm_src || !b.perm_pos || !b.y_perm ||
+      !b.route_ws || !b.ffn_ws)
+    return bad(MOE_EINVAL, "null device buffer");
+  if (b.route_ws_bytes < moe_route_workspace_size(T_max, H, E, k)) return bad(MOE_EINVAL, "route workspace too small");
+  if (b.ffn_ws_bytes < moe_ffn_workspace_size(T_max * k, H, I, wfmt)) return bad(MOE_EINVAL, "FFN workspace too small");
+  moe_decoder_t* d = new (std::nothrow) moe_decoder();
+  if (!d) return bad(MOE_ENOMEM, "out of host memory");
+  d->cache = cache;
+  d->Tmax = T_max; d->H = H; d->I = I; d->E = E; d->k = k; d->dtype = dtype; d->wfmt = wfmt;
+  d->pool = pool; d->blob_stride = blob_stride; d->blob_bytes = blob;
+  d->slot_base = slot_base; d->slot_stride = slot_stride;
+  d->b = b;
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&d->counts_host), sizeof(int32_t) * E, hipHostMallocDefault);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&d->fill, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&d->ev_counts, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    decoder_release(d);
+    if (status) *status = dfail(MOE_EHIP, "moe_decoder_create: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  d->experts.reserve(E);
+  d->offs.resize(E + 1);
+  if (status) *status = MOE_OK;
+  return d;
+}
+
+int moe_decoder_destroy(moe_decoder_t* d) {
+  if (!d) return MOE_OK;
+  if (d->fill) (void)hipStreamSynchronize(d->fill);
+  decoder_release(d);
+  return MOE_OK;
+}
+
+static int record_ffn_event(moe_decoder_t* d, bool begin, hipStream_t s, double bytes) {
+  if (begin) {
+    if (d->ev_used == d->ev_begin.size()) {
+      hipEvent_t a, c;
+      if (hipEventCreate(&a) != hipSuccess) return MOE_EHIP;
+      if (hipEventCreate(&c) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return MOE_EHIP;
+      }
+      d->ev_begin.push_back(a);
+      d->ev_end.push_back(c);
+      d->ev_bytes.push_back(0.0);
+    }
+    return hipEventRecord(d->ev_begin[d->ev_used], s) == hipSuccess ? MOE_OK : MOE_EHIP;
+  }
+  d->ev_bytes[d->ev_used] = bytes;
+  hipError_t e = hipEventRecord(d->ev_end[d->ev_used], s);
+  ++d->ev_used;
+  return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T, const void* Wr, const float* bias,
+                     void* out, int out_dtype, void* stream, int* n_miss) {
+  if (!d || !x || !Wr || !out) return dfail(MOE_EINVAL, "moe_decoder_step: null argument");
+  if (T < 1 || T > d->Tmax) return dfail(MOE_EINVAL, "moe_decoder_step: T=%d outside [1, %d]", T, d->Tmax);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const moe_decoder_buffers_t& b = d->b;
+  int rc = moe_route(x, d->dtype, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w, b.logits, b.counts, b.offsets,
+                     b.perm_src, b.perm_pos, b.route_ws, b.route_ws_bytes, stream);
+  if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
+  // the one device -> host round trip of the step: per-expert counts
+  hipError_t e = hipMemcpyAsync(d->counts_host, b.counts, sizeof(int32_t) * d->E, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipEventRecord(d->ev_counts, s);
+  if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: counts copy: %s", hipGetErrorString(e));
+  while ((e = hipEventQuery(d->ev_counts)) == hipErrorNotReady) {
+  }
+  if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: counts wait: %s", hipGetErrorString(e));
+  d->experts.clear();
+  int run = 0;
+  for (int i = 0; i < d->E; ++i) {
+    d->offs[i] = run;
+    run += d->counts_host[i];
+    if (d->counts_host[i] > 0) d->experts.push_back(i);
+  }
+  d->offs[d->E] = run;
+  const int n = (int)d->experts.size();
+  d->work_e.resize(n);
+  d->work_slot.resize(n);
+  d->work_wave.resize(n);
+  d->misses.resize(n);
+  int nm = 0, nw = 0;
+  rc = cache_resolve(d->cache, step, layer, d->experts.data(), n, d->work_e.data(), d->work_slot.data(),
+                     d->work_wave.data(), d->misses.data(), &nm, &nw);
+  if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
+  for (int w = 0; w < nw; ++w) {
+    d->wave_misses.clear();
+    for (int i = 0; i < nm; ++i)
+      if (d->misses[i].wave == w) d->wave_misses.push_back(d->misses[i]);
+    if (!d->wave_misses.empty()) {
+      rc = cache_fill_async(d->cache, d->wave_misses.data(), (int)d->wave_misses.size(), d->pool, d->blob_stride,
+                            d->blob_bytes, d->slot_base, d->slot_stride, d->fill, stream);
+      if (rc != MOE_OK) {
+        // this wave's and every later wave's misses were never copied: unmap them
+        const std::string msg = moe_last_error();
+        for (int i = 0; i < nm; ++i)
+          if (d->misses[i].wave >= w) (void)moe_cache_invalidate(d->cache, d->misses[i].key);
+        return dfail(rc, "moe_decoder_step: %s", msg.c_str());
+      }
+      d->fills += (int64_t)d->wave_misses.size();
+    }
+    d->work.clear();
+    int rows = 0;
+    for (int i = 0; i < n; ++i) {
+      if (d->work_wave[i] != w) continue;
+      const int ex = d->work_e[i];
+      d->work.push_back(moe_work_t{ex, d->work_slot[i], d->offs[ex], d->counts_host[ex]});
+      rows += d->counts_host[ex];
+    }
+    if (d->prof && record_ffn_event(d, true, s, 0) != MOE_OK)
+      return dfail(MOE_EHIP, "moe_decoder_step: profiling event");
+    rc = moe_ffn(x, d->dtype, b.perm_src, d->work.data(), (int)d->work.size(), d->slot_base, d->slot_stride, d->wfmt,
+                 d->H, d->I, b.y_perm, b.ffn_ws, b.ffn_ws_bytes, MOE_FFN_AUTO, stream);
+    if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
+    if (d->prof) {
+      const double a = d->dtype == MOE_DT_BF16 ? 2.0 : 4.0, h = d->wfmt == MOE_W_F32 ? 4.0 : 2.0;
+      const double bytes = (double)d->work.size() * (double)d->blob_bytes +
+                           (double)rows * (d->H * a + 2.0 * d->I * h + d->H * 4.0);
+      if (record_ffn_event(d, false, s, bytes) != MOE_OK) return dfail(MOE_EHIP, "moe_decoder_step: profiling event");
+    }
+  }
+  rc = moe_combine(b.y_perm, b.perm_pos, b.topk_w, T, d->k, d->H, out, out_dtype, stream);
+  if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
+  if (n_miss) *n_miss = nm;
+  return MOE_OK;
+}
+
+int moe_decoder_profile(moe_decoder_t* d, int enable) {
+  if (!d) return dfail(MOE_EINVAL, "moe_decoder_profile: null decoder");
+  d->prof = enable != 0;
+  d->ev_used = 0;
+  return MOE_OK;
+}
+
+int moe_decoder_ffn_stats(moe_decoder_t* d, double* bytes, double* ms, int64_t* launches) {
+  if (!d || !bytes || !ms || !launches) return dfail(MOE_EINVAL, "moe_decoder_ffn_stats: null argument");
+  double tb = 0, tm = 0;
+  for (size_t i = 0; i < d->ev_used; ++i) {
+    float m = 0;
+    hipError_t e = hipEventSynchronize(d->ev_end[i]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&m, d->ev_begin[i], d->ev_end[i]);
+    if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_ffn_stats: %s", hipGetErrorString(e));
+    tb += d->ev_bytes[i];
+    tm += m;
+  }
+  *bytes = tb;
+  *ms = tm;
+  *launches = (int64_t)d->ev_used;
+  return MOE_OK;
+}
+
+int moe_decoder_fills(const moe_decoder_t* d, int64_t* fills) {
+  if (!d || !fills) return dfail(MOE_EINVAL, "moe_decoder_fills: null argument");
+  *fills = d->fills;
+  return MOE_OK;
+}
+
+}  // extern "C"

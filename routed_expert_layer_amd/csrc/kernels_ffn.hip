@@ -8,6 +8,8 @@
 // matrix-core instruction whose other operand holds the (<= 16) tokens.
 // Prefill (many rows per expert) runs a tiled matrix-core GEMM with both
 // operands staged in LDS.
+#include <cstring>
+
 #include "dev_common.hpp"
 #include "moe_kernels.hpp"
 
@@ -266,13 +268,16 @@ __global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restri
 // PHASE 1: A = gate/up rows (N = 2I, K = H), B = x rows through perm_src,
 //          epilogue silu(gate) * up -> bf16 h.
 // PHASE 2: A = down rows (N = H, K = I), B = h rows, epilogue -> fp32 y.
+// PHASE 0: the router: A = Wr^T rows (N = E, K = H), B = x rows in order,
+//          epilogue -> fp32 logits + bias.
 // ---------------------------------------------------------------------------
 template <int PHASE>
 __global__ __launch_bounds__(256, 2) void ffn_gemm_bf16(const uint16_t* __restrict__ bsrc,
                                                        const int32_t* __restrict__ perm_src, const WorkArgs wa,
                                                        const char* __restrict__ slot_base, size_t slot_stride,
                                                        size_t mat_off, int N, int K, int H, int I,
-                                                       uint16_t* __restrict__ hout, float* __restrict__ yout) {
+                                                       uint16_t* __restrict__ hout, float* __restrict__ yout,
+                                                       const float* __restrict__ bias) {
   __shared__ __attribute__((aligned(16))) char lds[2][32768];
   const int NTB = N / kGemmBN;
   const int mtg = blockIdx.x / NTB, nt = blockIdx.x - (blockIdx.x / NTB) * NTB;
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_bf16(const uint16_t* __restri
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wn = wave & 1, wm = wave >> 1;
   const int KC = K / 32, KT = K / 64;
-  const int ldb = (PHASE == 1) ? H : I;
+  const int ldb = (PHASE == 2) ? I : H;
 
   // A (weights): 16 fragments per stage, 4 per thread.
   const char* abase = slot_base + (size_t)it.x * slot_stride + mat_off;
@@ -370,8 +375,18 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_bf16(const uint16_t* __restri
         const uint32_t packed =
             (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
         *reinterpret_cast<uint32_t*>(hout + row * I + i0) = packed;
-      } else {
+      } else if constexpr (PHASE == 2) {
         *reinterpret_cast<f32x4_t*>(yout + row * H + 16 * ntile + 4 * (lane >> 4)) = s;
+      } else {
+        const int n0 = 16 * ntile + 4 * (lane >> 4);
+        f32x4_t o = s;
+        if (bias) {
+          o[0] += bias[n0];
+          o[1] += bias[n0 + 1];
+          o[2] += bias[n0 + 2];
+          o[3] += bias[n0 + 3];
+        }
+        *reinterpret_cast<f32x4_t*>(yout + row * N + n0) = o;
       }
     }
   }
@@ -438,12 +453,27 @@ hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& 
   if (tot == 0) return hipSuccess;
   hipLaunchKernelGGL(ffn_gemm_bf16<1>, dim3(tot * ((2 * I) / kGemmBN)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), perm_src, wa, slot_base, slot_stride, L.p1, 2 * I, H, H, I,
-                     static_cast<uint16_t*>(hbuf), y);
+                     static_cast<uint16_t*>(hbuf), y, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(ffn_gemm_bf16<2>, dim3(tot * (H / kGemmBN)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(hbuf), perm_src, wa, slot_base, slot_stride, L.p2, H, I, H, I,
-                     static_cast<uint16_t*>(hbuf), y);
+                     static_cast<uint16_t*>(hbuf), y, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_gemm(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
+                              hipStream_t s) {
+  WorkArgs wa;
+  memset(&wa, 0, sizeof wa);
+  wa.n = 1;
+  wa.item[0] = make_int4(0, 0, T, 0);
+  wa.tile_prefix[0] = 0;
+  wa.tile_prefix[1] = (T + kGemmBM - 1) / kGemmBM;
+  wa.total_tiles = wa.tile_prefix[1];
+  hipLaunchKernelGGL(ffn_gemm_bf16<0>, dim3(wa.total_tiles * (E / kGemmBN)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), nullptr, wa, static_cast<const char*>(wrt), 0, 0, E, H, H, 0,
+                     nullptr, logits, bias);
   return hipGetLastError();
 }
 

@@ -42,32 +42,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-// bf16 blob: one thread per 16-byte fragment chunk.
-__global__ void pack_bf16_kernel(const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W3,
-                                 const uint16_t* __restrict__ W2, int H, int I, char* __restrict__ blob, size_t p2_off) {
+// Fragment order of a [K, N] row-major bf16 matrix taken by columns: row
+// tile t holds columns 16t..16t+15; one thread per 16-byte chunk.
+__global__ void pack_frag_kernel(const uint16_t* __restrict__ W, int K, int N, char* __restrict__ dst) {
   const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t n1 = (size_t)(2 * I / 16) * (H / 32) * 64;
-  const size_t n2 = (size_t)(H / 16) * (I / 32) * 64;
-  if (q >= n1 + n2) return;
+  const int KC = K / 32;
+  if (q >= (size_t)(N / 16) * KC * 64) return;
+  const int l = (int)(q % 64), c = (int)((q / 64) % KC), t = (int)(q / (64 * (size_t)KC));
+  const int n = 16 * t + (l % 16);
+  const int kb = 32 * c + 8 * (l / 16);
   uint16_t v[8];
-  if (q < n1) {
-    const int KC = H / 32;
-    const int l = (int)(q % 64), c = (int)((q / 64) % KC), t = (int)(q / (64 * (size_t)KC));
-    int mat, i;
-    p1_row_source(16 * t + (l % 16), mat, i);
-    const uint16_t* W = mat ? W3 : W1;
-    const int kb = 32 * c + 8 * (l / 16);
-    for (int j = 0; j < 8; ++j) v[j] = W[(size_t)(kb + j) * I + i];
-    *reinterpret_cast<uint4*>(blob + q * 16) = *reinterpret_cast<uint4*>(v);
-  } else {
-    const size_t q2 = q - n1;
-    const int KC = I / 32;
-    const int l = (int)(q2 % 64), c = (int)((q2 / 64) % KC), t = (int)(q2 / (64 * (size_t)KC));
-    const int n = 16 * t + (l % 16);
-    const int kb = 32 * c + 8 * (l / 16);
-    for (int j = 0; j < 8; ++j) v[j] = W2[(size_t)(kb + j) * H + n];
-    *reinterpret_cast<uint4*>(blob + p2_off + q2 * 16) = *reinterpret_cast<uint4*>(v);
-  }
+  for (int j = 0; j < 8; ++j) v[j] = W[(size_t)(kb + j) * N + n];
+  *reinterpret_cast<uint4*>(dst + q * 16) = *reinterpret_cast<uint4*>(v);
+}
+
+// Gate/up matrix of a bf16 blob (rows interleaved as p1_row_source says).
+__global__ void pack_p1_bf16_kernel(const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W3, int H, int I,
+                                    char* __restrict__ blob) {
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int KC = H / 32;
+  if (q >= (size_t)(2 * I / 16) * KC * 64) return;
+  const int l = (int)(q % 64), c = (int)((q / 64) % KC), t = (int)(q / (64 * (size_t)KC));
+  int mat, i;
+  p1_row_source(16 * t + (l % 16), mat, i);
+  const uint16_t* W = mat ? W3 : W1;
+  const int kb = 32 * c + 8 * (l / 16);
+  uint16_t v[8];
+  for (int j = 0; j < 8; ++j) v[j] = W[(size_t)(kb + j) * I + i];
+  *reinterpret_cast<uint4*>(blob + q * 16) = *reinterpret_cast<uint4*>(v);
 }
 
 __device__ __forceinline__ uint32_t pack_word(const int8_t* Q, int ld, int col, int k0) {
@@ -141,6 +143,13 @@ hipError_t launch_combine(const float* y_perm, const int32_t* perm_pos, const fl
   return hipGetLastError();
 }
 
+hipError_t launch_pack_fragments(const void* W, int K, int N, void* dst, hipStream_t s) {
+  const size_t n = (size_t)(N / 16) * (K / 32) * 64;
+  hipLaunchKernelGGL(pack_frag_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(W), K, N, static_cast<char*>(dst));
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(int wfmt, int H, int I, const void* W1, const void* W3, const void* W2, const void* s1,
                        const void* s3, const void* s2, void* blob, hipStream_t s) {
   const BlobLayout L = blob_layout(wfmt, H, I);
@@ -153,11 +162,12 @@ hipError_t launch_pack(int wfmt, int H, int I, const void* W1, const void* W3, c
     return e;
   }
   if (wfmt == 1) {
-    const size_t n = (size_t)(2 * I / 16) * (H / 32) * 64 + (size_t)(H / 16) * (I / 32) * 64;
-    hipLaunchKernelGGL(pack_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W3),
-                       static_cast<const uint16_t*>(W2), H, I, b, L.p2);
-    return hipGetLastError();
+    const size_t n1 = (size_t)(2 * I / 16) * (H / 32) * 64;
+    hipLaunchKernelGGL(pack_p1_bf16_kernel, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W3), H, I, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_pack_fragments(W2, I, H, b + L.p2, s);
   }
   // int4 (alignment padding between sections is never read)
   const size_t n = (size_t)(2 * I / 16) * (H / 128) * 64 + (size_t)(H / 16) * (I / 128) * 64 +

@@ -228,27 +228,178 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode-size batches (T <= 16, E <= 512): two launches in total.
+// ---------------------------------------------------------------------------
+constexpr int kSmallT = 16;
+constexpr int kSmallE = 512;
+constexpr int kSmallChunk = 64;  // rows of Wr per block
+
+// partial[z][t][e] = sum over the block's 64 rows of x[t,h] Wr[h,e]; each
+// thread owns expert columns, the block's x slice sits in LDS.
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_small_partial(const void* __restrict__ x, const void* __restrict__ Wr,
+                                                            int T, int H, int E, float* __restrict__ partial) {
+  __shared__ float xs[kSmallT][kSmallChunk];
+  const int h0 = blockIdx.x * kSmallChunk;
+  const int nh = min(kSmallChunk, H - h0);
+  for (int i = threadIdx.x; i < T * kSmallChunk; i += 256) {
+    const int t = i / kSmallChunk, h = i - t * kSmallChunk;
+    xs[t][h] = h < nh ? ldv<BF16>(x, (size_t)t * H + h0 + h) : 0.f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    float acc[kSmallT];
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t) acc[t] = 0.f;
+#pragma unroll 8
+    for (int h = 0; h < nh; ++h) {
+      const float w = ldv<BF16>(Wr, (size_t)(h0 + h) * E + e);
+#pragma unroll
+      for (int t = 0; t < kSmallT; ++t)
+        if (t < T) acc[t] = fmaf(xs[t][h], w, acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t)
+      if (t < T) partial[((size_t)blockIdx.x * T + t) * E + e] = acc[t];
+  }
+}
+
+// One block: logits = sum of the partials + bias (fixed order), top-k of
+// every token by one wave each, then the grouping of the <= 16 tokens.
+__global__ __launch_bounds__(1024) void route_finish_small(const float* __restrict__ partial, int nsplit,
+                                                           const float* __restrict__ bias, int T, int E, int k,
+                                                           int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                                           float* __restrict__ logits, int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ perm_src,
+                                                           int32_t* __restrict__ perm_pos) {
+  __shared__ float lg[kSmallT * kSmallE];
+  __shared__ int32_t sidx[kSmallT * 16];
+  __shared__ unsigned long long bm[kSmallE];
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t soff[kSmallE];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < E; e += 1024) bm[e] = 0ull;
+  for (int i = tid; i < T * E; i += 1024) {
+    const int t = i / E, e = i - t * E;
+    const float* p = partial + (size_t)t * E + e;
+    const size_t zs = (size_t)T * E;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    int z = 0;
+    for (; z + 4 <= nsplit; z += 4) {
+      a0 += p[(size_t)z * zs];
+      a1 += p[(size_t)(z + 1) * zs];
+      a2 += p[(size_t)(z + 2) * zs];
+      a3 += p[(size_t)(z + 3) * zs];
+    }
+    for (; z < nsplit; ++z) a0 += p[(size_t)z * zs];
+    float l = (a0 + a1) + (a2 + a3);
+    if (bias) l += bias[e];
+    lg[i] = l;
+    if (logits) logits[i] = l;
+  }
+  __syncthreads();
+  if (wave < T) {
+    const int t = wave;
+    uint64_t key[kSmallE / 64];
+#pragma unroll
+    for (int v = 0; v < kSmallE / 64; ++v) {
+      const int e = v * 64 + lane;
+      key[v] = e < E ? (((uint64_t)float_key(lg[t * E + e]) << 32) | (uint32_t)(~(uint32_t)e)) : 0ull;
+    }
+    float v0 = 0.f, den = 0.f, my_v = 0.f;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+      uint64_t local = 0;
+#pragma unroll
+      for (int v = 0; v < kSmallE / 64; ++v) local = key[v] > local ? key[v] : local;
+      const uint64_t best = wave_max_u64(local);
+#pragma unroll
+      for (int v = 0; v < kSmallE / 64; ++v)
+        if (key[v] == best) key[v] = 0;
+      const float val = key_float((uint32_t)(best >> 32));
+      if (j == 0) v0 = val;
+      den += expf(val - v0);
+      if (lane == j) {
+        my_e = (int)(~(uint32_t)best);
+        my_v = val;
+      }
+    }
+    if (lane < k) {
+      topk_idx[t * k + lane] = my_e;
+      topk_w[t * k + lane] = expf(my_v - v0) / den;
+      sidx[t * k + lane] = my_e;
+      atomicOr(&bm[my_e], 1ull << t);
+    }
+  }
+  __syncthreads();
+  // counts and their exclusive prefix over experts (block scan)
+  const int c = tid < E ? __popcll(bm[tid]) : 0;
+  int v = c;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int n = __shfl_up(v, d);
+    if (lane >= d) v += n;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  const int excl = before + v - c;
+  if (tid < E) {
+    counts[tid] = c;
+    offsets[tid] = excl;
+    soff[tid] = excl;
+  }
+  if (tid == 0) offsets[E] = T * k;
+  __syncthreads();
+  // positions: rank of a token inside its expert = earlier tokens in its mask
+  if (tid < T * k) {
+    const int t = tid / k, e = sidx[tid];
+    const int pos = soff[e] + __popcll(bm[e] & ((1ull << t) - 1ull));
+    perm_pos[tid] = pos;
+    perm_src[pos] = t;
+  }
+}
+
 struct RoutePlan {
+  int mode;  // 0: small (decode) path, 1: matrix-core path, 2: general VALU path
   int gx, gy, nsplit, hchunk;
-  size_t partial_bytes, hist_off, bits_off, total;
+  size_t partial_bytes, hist_off, bits_off, wrt_off, total;
 };
 
-RoutePlan plan_route(int T, int H, int E) {
+bool gemm_router_ok(bool bf16, int T, int H, int E) {
+  return bf16 && T > 64 && E % kGemmBN == 0 && H % 64 == 0;
+}
+
+RoutePlan plan_route(int T, int H, int E, bool bf16) {
   RoutePlan p{};
-  p.gx = (E + 63) / 64;
-  p.gy = (T + kRouterTok - 1) / kRouterTok;
-  const int blocks = p.gx * (p.gy > 0 ? p.gy : 1);
-  int ns = (512 + blocks - 1) / blocks;
-  const int max_ns = H / 32 > 0 ? H / 32 : 1;
-  if (ns > max_ns) ns = max_ns;
-  if (ns < 1) ns = 1;
-  p.hchunk = (H + ns - 1) / ns;
-  p.nsplit = (H + p.hchunk - 1) / p.hchunk;
   const int nchunks = (T + 63) / 64;
-  p.partial_bytes = align_up((size_t)p.nsplit * T * E * sizeof(float), 256);
+  if (T <= kSmallT && E <= kSmallE) {
+    p.mode = 0;
+    p.nsplit = (H + kSmallChunk - 1) / kSmallChunk;
+    p.partial_bytes = align_up((size_t)p.nsplit * (T > 0 ? T : 1) * E * sizeof(float), 256);
+  } else if (gemm_router_ok(bf16, T, H, E)) {
+    p.mode = 1;
+    p.nsplit = 1;
+    p.partial_bytes = align_up((size_t)T * E * sizeof(float), 256);
+  } else {
+    p.mode = 2;
+    p.gx = (E + 63) / 64;
+    p.gy = (T + kRouterTok - 1) / kRouterTok;
+    const int blocks = p.gx * (p.gy > 0 ? p.gy : 1);
+    int ns = (512 + blocks - 1) / blocks;
+    const int max_ns = H / 32 > 0 ? H / 32 : 1;
+    if (ns > max_ns) ns = max_ns;
+    if (ns < 1) ns = 1;
+    p.hchunk = (H + ns - 1) / ns;
+    p.nsplit = (H + p.hchunk - 1) / p.hchunk;
+    p.partial_bytes = align_up((size_t)p.nsplit * T * E * sizeof(float), 256);
+  }
   p.hist_off = p.partial_bytes;
   p.bits_off = align_up(p.hist_off + (size_t)nchunks * E * sizeof(int32_t), 256);
-  p.total = align_up(p.bits_off + (size_t)nchunks * E * sizeof(uint64_t), 256) + 256;
+  p.wrt_off = align_up(p.bits_off + (size_t)nchunks * E * sizeof(uint64_t), 256);
+  p.total = p.wrt_off + (p.mode == 1 ? align_up((size_t)H * E * 2, 256) : 0) + 256;
   return p;
 }
 
@@ -256,30 +407,48 @@ RoutePlan plan_route(int T, int H, int E) {
 
 size_t route_workspace_bytes(int T, int H, int E, int k) {
   (void)k;
-  return plan_route(T, H, E).total;
+  // sized for the larger of the two element types
+  const size_t a = plan_route(T, H, E, true).total, b = plan_route(T, H, E, false).total;
+  return a > b ? a : b;
 }
 
 hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
                         int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s) {
-  const RoutePlan p = plan_route(T, H, E);
+  const RoutePlan p = plan_route(T, H, E, bf16);
   char* w = static_cast<char*>(ws);
   float* partial = reinterpret_cast<float*>(w);
   int32_t* hist = reinterpret_cast<int32_t*>(w + p.hist_off);
   uint64_t* bits = reinterpret_cast<uint64_t*>(w + p.bits_off);
-  if (T > 0) {
+  hipError_t err;
+  if (p.mode == 0) {
+    if (T > 0) {
+      if (bf16)
+        hipLaunchKernelGGL(router_small_partial<true>, dim3(p.nsplit), dim3(256), 0, s, x, Wr, T, H, E, partial);
+      else
+        hipLaunchKernelGGL(router_small_partial<false>, dim3(p.nsplit), dim3(256), 0, s, x, Wr, T, H, E, partial);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(route_finish_small, dim3(1), dim3(1024), 0, s, partial, T > 0 ? p.nsplit : 0, bias, T, E, k,
+                       topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos);
+    return hipGetLastError();
+  }
+  if (p.mode == 1) {
+    void* wrt = w + p.wrt_off;
+    if ((err = launch_pack_fragments(Wr, H, E, wrt, s)) != hipSuccess) return err;
+    if ((err = launch_router_gemm(x, wrt, bias, T, H, E, partial, s)) != hipSuccess) return err;
+  } else {
     dim3 grid(p.gx, p.gy, p.nsplit);
     if (bf16)
       hipLaunchKernelGGL(router_partial_kernel<true>, grid, dim3(256), 0, s, x, Wr, T, H, E, p.hchunk, partial);
     else
       hipLaunchKernelGGL(router_partial_kernel<false>, grid, dim3(256), 0, s, x, Wr, T, H, E, p.hchunk, partial);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, partial, p.nsplit, bias, T, E, k, topk_idx,
-                       topk_w, logits);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  // mode 1 has the bias already added by the GEMM epilogue
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, partial, p.nsplit, p.mode == 1 ? nullptr : bias,
+                     T, E, k, topk_idx, topk_w, logits);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   int nwaves = 16;
   while (nwaves > 1 && (size_t)nwaves * E * 8 + (E + 1) * 4 > 64 * 1024) nwaves /= 2;
   const size_t lds = (size_t)nwaves * E * 8 + (size_t)(E + 1) * 4;

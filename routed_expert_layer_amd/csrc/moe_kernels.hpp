@@ -90,6 +90,15 @@ hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, c
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,
                               size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s);
 bool prefill_supported(int wfmt, int H, int I);
+// Matrix-core router for long batches: Wr [H, E] bf16 is first rearranged into
+// fragment order (rows = experts, K = H) in the workspace, then
+// logits[t, e] = x[t, :] . Wr[:, e] + bias[e] (fp32) by the GEMM kernel.
+hipError_t launch_pack_fragments(const void* W, int K, int N, void* dst, hipStream_t s);
+hipError_t launch_router_gemm(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
+                              hipStream_t s);
+// Sets the calling thread's moe_last_error() message; returns `code`.
+int set_error(int code, const char* fmt, ...);
+
 constexpr int kGemmBM = 128;  // tokens per GEMM tile
 constexpr int kGemmBN = 128;  // output rows per GEMM tile
 

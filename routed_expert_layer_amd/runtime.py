@@ -118,8 +118,9 @@ class RouteBuffers:
 class DecodeLayer:
     """Decode path: route -> host LRU -> fills -> grouped FFN -> combine, for one cache."""
 
-    def __init__(self, store, n_slots, T, k, act, device="cuda", keep_logits=False):
+    def __init__(self, store, n_slots, T, k, act, device="cuda", keep_logits=False, native=True):
         self.store, self.S, self.k = store, n_slots, k
+        self.native = native
         self.H, self.I, self.E = store.H, store.I, store.E
         self.act = act
         self.rb = RouteBuffers(T, self.H, self.E, k, device, keep_logits)
@@ -131,7 +132,20 @@ class DecodeLayer:
                                   device=device)
         self.out = torch.empty((T, self.H), dtype=torch.float32, device=device)
         self.fill_stream = torch.cuda.Stream(device=device)
-        self.n_fills = 0
+        self._fills = 0
+        self.dec = None
+        if native:
+            rb = self.rb
+            bufs = dict(topk_idx=rb.topk_idx, topk_w=rb.topk_w, logits=rb.logits, counts=rb.counts,
+                        offsets=rb.offsets, perm_src=rb.perm_src, perm_pos=rb.perm_pos, y_perm=self.y_perm,
+                        route_ws=rb.ws, ffn_ws=self.ffn_ws)
+            self.dec = L.MoeDecoder(self.cache, T, self.H, self.I, self.E, k,
+                                    L.MOE_DT_BF16 if act == "bf16" else L.MOE_DT_F32, store.wfmt, store.pool,
+                                    store.stride, self.slots, store.stride, bufs)
+
+    @property
+    def n_fills(self):
+        return L.moe_decoder_fills(self.dec) if self.dec is not None else self._fills
 
     def algorithmic_bytes(self, work):
         """Bytes the expert FFN must move for a work list: each listed expert's
@@ -147,6 +161,9 @@ class DecodeLayer:
         timer.end(stream, algorithmic_bytes) around every expert-FFN call."""
         s = stream or torch.cuda.current_stream()
         T = x.shape[0]
+        if self.dec is not None:
+            L.moe_decoder_step(self.dec, step, layer, x, Wr, bias, self.out[:T], s)
+            return self.out[:T]
         rb = self.rb
         rb.route(x, Wr, bias, s)
         counts, off = rb.fetch_counts(s)
@@ -157,7 +174,7 @@ class DecodeLayer:
             if len(m):
                 L.cache_fill_async(self.cache, m, self.store.pool, self.store.stride, self.store.blob, self.slots,
                                    self.store.stride, self.fill_stream, s)
-                self.n_fills += len(m)
+                self._fills += len(m)
             sel = wwave == w
             e = we[sel]
             work = np.stack([e, wslot[sel], off[e], counts[e]], axis=1).astype(np.int32)

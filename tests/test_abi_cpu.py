@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: exported symbols, argument validation and
+error codes, and the host LRU policy (cache_resolve) against the oracle's
+simulator, bit-exact. No compute call is made."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from routed_expert_layer_amd import _lib
+    return _lib
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if not n.startswith("if")))
+
+
+def test_every_declared_symbol_is_exported(L):
+    declared = header_functions()
+    assert len(declared) >= 30
+    lib = ctypes.CDLL(L.LIB_PATH)
+    missing = [n for n in declared if not hasattr(lib, n)]
+    assert not missing, f"declared in include/moe.h but not exported: {missing}"
+    assert sorted(L.SYMBOLS) == declared, "binding symbol list differs from the header"
+    assert L.moe_abi_version() >= 1
+
+
+def test_expert_bytes(L):
+    assert L.moe_expert_bytes(L.MOE_W_BF16, 4096, 2048) == 3 * 4096 * 2048 * 2
+    assert L.moe_expert_bytes(L.MOE_W_F32, 256, 128) == 3 * 256 * 128 * 4
+    b = L.moe_expert_bytes(L.MOE_W_INT4, 4096, 2048)
+    codes, scales = 3 * 4096 * 2048 // 2, 3 * 4096 * 2048 // 128 * 2
+    assert codes + scales <= b < codes + scales + 4 * 256
+    # unsupported shapes are rejected with size 0
+    assert L.moe_expert_bytes(L.MOE_W_BF16, 100, 2048) == 0
+    assert L.moe_expert_bytes(L.MOE_W_INT4, 4096, 200) == 0
+    assert L.moe_expert_bytes(7, 64, 64) == 0
+
+
+@pytest.mark.parametrize("S,E,Lyr,max_active,steps", [(8, 16, 1, 14, 64), (64, 256, 1, 6, 200), (16, 32, 6, 10, 40),
+                                                      (3, 12, 2, 9, 50), (1, 4, 1, 4, 30)])
+def test_cache_resolve_matches_oracle(L, S, E, Lyr, max_active, steps):
+    r = np.random.default_rng(S + E + Lyr)
+    cache = L.MoeCache(Lyr, E, S)
+    sim = oracle.SharedLRU(S)
+    zipf = 1.0 / np.arange(1, E + 1) ** 1.2
+    for step in range(steps):
+        for layer in range(Lyr):
+            n = int(r.integers(1, max_active + 1))
+            ex = np.sort(r.choice(E, size=n, replace=False, p=zipf / zipf.sum())).astype(np.int32)
+            we, wslot, wwave, misses, nw = L.cache_resolve(cache, step, layer, ex)
+            waves, recs = sim.resolve(step, layer, E, ex)
+            assert nw == len(waves)
+            flat = [(e, s, w) for w, wv in enumerate(waves) for (e, s) in wv]
+            assert list(zip(we.tolist(), wslot.tolist(), wwave.tolist())) == flat
+            exp_m = [[rc.key, rc.slot, rc.victim, rc.wave] for rc in recs if not rc.hit]
+            assert misses.tolist() == exp_m
+    tr = L.moe_cache_trace(cache)
+    ref = np.array([[r.step, r.layer, r.key, r.hit, r.slot, r.victim, r.wave] for r in sim.trace])
+    assert np.array_equal(tr, ref)
+    h, m = L.moe_cache_stats(cache)
+    assert h == int(ref[:, 3].sum()) and m == len(ref) - h
+
+
+def test_cache_errors_and_invalidate(L):
+    with pytest.raises(L.MoEError) as ei:
+        L.MoeCache(1, 8, 0)
+    assert ei.value.code == L.MOE_ECAPACITY
+    with pytest.raises(L.MoEError) as ei:
+        L.MoeCache(0, 8, 4)
+    assert ei.value.code == L.MOE_EINVAL
+    c = L.MoeCache(2, 8, 4)
+    for bad, why in [([3, 1], "unsorted"), ([2, 2], "duplicate"), ([8], "expert range"), ([-1], "negative")]:
+        with pytest.raises(L.MoEError) as ei:
+            L.cache_resolve(c, 0, 0, bad)
+        assert ei.value.code == L.MOE_EINVAL, why
+    with pytest.raises(L.MoEError):
+        L.cache_resolve(c, 0, 2, [1])  # layer out of range
+    # a failed fill is undone by invalidating the key: its slot is free again
+    we, ws, _, misses, _ = L.cache_resolve(c, 0, 1, [0, 3, 5])
+    assert ws.tolist() == [0, 1, 2]
+    L.moe_cache_invalidate(c, 1 * 8 + 3)
+    assert L.moe_cache_slot_of(c, 1 * 8 + 3) == -1
+    with pytest.raises(L.MoEError):
+        L.moe_cache_invalidate(c, 1 * 8 + 3)  # not resident any more
+    _, ws, _, misses, _ = L.cache_resolve(c, 1, 0, [7])
+    assert ws.tolist() == [1] and misses.tolist() == [[7, 1, -1, 0]]  # lowest free slot
+    L.moe_cache_clear_trace(c)
+    assert len(L.moe_cache_trace(c)) == 0
+
+
+def test_argument_validation_without_gpu(L):
+    lib = L._lib
+    # routing: k > E, bad dtype, workspace too small -- all rejected before any launch
+    assert lib.moe_route(None, 1, None, None, 4, 64, 8, 9, None, None, None, 1, 1, None, None, 1, 1 << 20, None) \
+        == L.MOE_EINVAL
+    assert lib.moe_route(1, 5, 1, None, 4, 64, 8, 2, 1, 1, None, 1, 1, 1, 1, 1, 1 << 20, None) == L.MOE_EINVAL
+    assert lib.moe_route(1, 1, 1, None, 4, 64, 8, 2, 1, 1, None, 1, 1, 1, 1, 1, 16, None) == L.MOE_EINVAL
+    assert "workspace" in L.moe_last_error()
+    # FFN: dtype / format mismatch, bad mode, slot stride smaller than a blob
+    w = np.array([[0, 0, 0, 1]], np.int32)
+    assert lib.moe_ffn(1, L.MOE_DT_F32, 1, w.ctypes.data, 1, 1, 1 << 30, L.MOE_W_BF16, 256, 128, 1, 1, 1 << 30, 0,
+                       None) == L.MOE_EINVAL
+    assert lib.moe_ffn(1, L.MOE_DT_BF16, 1, w.ctypes.data, 1, 1, 1 << 30, L.MOE_W_BF16, 256, 128, 1, 1, 1 << 30, 9,
+                       None) == L.MOE_EINVAL
+    assert lib.moe_ffn(1, L.MOE_DT_BF16, 1, w.ctypes.data, 1, 1, 1024, L.MOE_W_BF16, 256, 128, 1, 1, 1 << 30, 0,
+                       None) == L.MOE_EINVAL
+    # prefill GEMM on shapes it does not tile (H % 128 != 0) is refused, not attempted
+    assert lib.moe_ffn(1, L.MOE_DT_BF16, 1, w.ctypes.data, 1, 1, 1 << 30, L.MOE_W_BF16, 96, 128, 1, 1, 1 << 30,
+                       L.MOE_FFN_PREFILL, None) == L.MOE_EINVAL
+    # combine: bad output dtype
+    assert lib.moe_combine(1, 1, 1, 2, 2, 8, 1, 9, None) == L.MOE_EINVAL
+    # fills: slot index beyond the cache
+    c = L.MoeCache(1, 8, 2)
+    m = np.array([[0, 5, -1, 0]], np.int32)
+    assert lib.cache_fill_async(c.h, m.ctypes.data, 1, 1, 64, 64, 1, 64, None, None) == L.MOE_EINVAL
+    # pipe and decoder: null arguments
+    st = ctypes.c_int(0)
+    assert lib.moe_pipe_create(None, 64, 64, 2, ctypes.byref(st)) is None and st.value == L.MOE_EINVAL
+    assert lib.moe_decoder_create(None, 1, 64, 64, 8, 2, 1, 1, None, 0, None, 0, None, ctypes.byref(st)) is None
+    assert st.value == L.MOE_EINVAL
+    assert lib.moe_decoder_step(None, 0, 0, None, 1, None, None, None, 0, None, None) == L.MOE_EINVAL

@@ -41,6 +41,9 @@ ROUTE_CASES = [
     ("k_eq_e", "tiny_f32_h256_e16", dict(name="kE", T=70, E=8, k=8)),
     ("e_not_mult64_bf16", "decode_bf16_h4096_e256", dict(name="e100", T=130, H=256, E=100, k=5, zipf_s=1.5)),
     ("t0", "tiny_f32_h256_e16", dict(name="t0", T=0)),
+    ("small_t16_e512", "decode_bf16_h4096_e256", dict(name="s16", T=16, H=256, E=512, k=8)),
+    ("gemm_router_t300", "decode_bf16_h4096_e256", dict(name="g300", T=300, H=512, E=256, k=6, zipf_s=0.0)),
+    ("gemm_router_t1000", "decode_bf16_h4096_e256", dict(name="g1000", T=1000, H=1024, E=128, k=8, zipf_s=1.5)),
 ]
 
 

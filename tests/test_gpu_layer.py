@@ -62,13 +62,17 @@ def make_store(cfg, layers):
     return store
 
 
-def run_decode(cfg, steps, out_check, check_all_outputs=False):
-    """Drive DecodeLayer over `steps` x all layers; check routing, trace, and sampled outputs."""
+def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True):
+    """Drive DecodeLayer over `steps` x all layers; check routing, trace, and sampled outputs.
+
+    native=True runs each layer-step through the library's decode driver
+    (moe_decoder_step); native=False sequences the individual C-ABI calls from
+    Python."""
     from routed_expert_layer_amd.runtime import DecodeLayer
-    print(f"decode {cfg.name}: L={cfg.L} T={cfg.T} steps={steps} S={cfg.S} {cfg.wfmt}", flush=True)
+    print(f"decode {cfg.name}: L={cfg.L} T={cfg.T} steps={steps} S={cfg.S} {cfg.wfmt} native={native}", flush=True)
     store = make_store(cfg, range(cfg.L))
     try:
-        dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev, keep_logits=True)
+        dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev, keep_logits=True, native=native)
         Wr = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
         sim = oracle.SharedLRU(cfg.S)
         experts64 = {}
@@ -102,9 +106,10 @@ def run_decode(cfg, steps, out_check, check_all_outputs=False):
         store.close()
 
 
-def test_tiny_fp32_all_steps():
+@pytest.mark.parametrize("native", [True, False], ids=["driver", "python"])
+def test_tiny_fp32_all_steps(native):
     cfg = CONFIGS["tiny_f32_h256_e16"]
-    ref = run_decode(cfg, cfg.steps, set(), check_all_outputs=True)
+    ref = run_decode(cfg, cfg.steps, set(), check_all_outputs=True, native=native)
     assert (ref[:, 6] > 0).any(), "the tiny config should exercise multi-wave layer-steps"
 
 
