@@ -53,6 +53,20 @@ class EventTimer:
         return sum(self.work), sum(ms), len(ms)
 
 
+def measured_traffic(root):
+    """HBM bytes per FFN call from the committed counter summary, if the kernel sources are unchanged since."""
+    import hashlib
+    path = os.path.join(root, "profiles", "decode_ffn_hbm_traffic.json")
+    try:
+        j = json.load(open(path))
+        for rel, digest in j["sources_sha256"].items():
+            if hashlib.sha256(open(os.path.join(root, rel), "rb").read()).hexdigest() != digest:
+                return None
+        return int(j["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def percentile(xs, p):
     xs = sorted(xs)
     if not xs:
@@ -251,7 +265,8 @@ def main():
                    "intermediate": cfg.I, "top_k": cfg.k, "cache_slots": cfg.S, "router_zipf_s": cfg.zipf_s},
         "roofline": {"kernel": "decode expert FFN: ffn1_decode_bf16 + ffn2_decode_bf16 (one moe_ffn call)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
                      "algorithmic_bytes_per_launch": round(ffn["bytes"] / max(ffn["n"], 1)),
                      "avg_launch_us": round(ffn["ms"] * 1e3 / max(ffn["n"], 1), 2), "launches": ffn["n"]},
         "decode": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res["decode"].items()},
