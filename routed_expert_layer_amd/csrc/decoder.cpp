@@ -33,7 +33,8 @@ struct moe_decoder {
   void* slot_base;
   size_t slot_stride;
   moe_decoder_buffers_t b;
-  int32_t* counts_host = nullptr;
+  int32_t* counts_host = nullptr;  // pinned, host address
+  int32_t* counts_dev = nullptr;   // the same memory as seen by kernels
   hipStream_t fill = nullptr;
   hipEvent_t ev_counts = nullptr;
   std::vector<int32_t> experts, work_e, work_slot, work_wave;
@@ -66,7 +67,9 @@ moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, i
     return nullptr;
   };
   if (!cache || !pool || !slot_base || !buffers) return bad(MOE_EINVAL, "null argument");
-  if (T_max < 1 || H < 1 || I < 1 || E < 1 || k < 1 || k > E) return bad(MOE_EINVAL, "bad sizes");
+  if (T_max < 1 || H < 1 || I < 1 || E < 1 || E > 1024 || k < 1 || k > 16 || k > E || H % 8 != 0)
+    return bad(MOE_EINVAL, "bad sizes");
+  if (dtype != MOE_DT_F32 && dtype != MOE_DT_BF16) return bad(MOE_EINVAL, "bad activation dtype");
   const size_t blob = moe_expert_bytes(wfmt, H, I);
   if (blob == 0) return bad(MOE_EINVAL, "unsupported weight format or shape");
   if (blob_stride < blob || slot_stride < blob) return bad(MOE_EINVAL, "stride smaller than an expert blob");
@@ -83,7 +86,10 @@ moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, i
   d->pool = pool; d->blob_stride = blob_stride; d->blob_bytes = blob;
   d->slot_base = slot_base; d->slot_stride = slot_stride;
   d->b = b;
-  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&d->counts_host), sizeof(int32_t) * E, hipHostMallocDefault);
+  // fine-grained (coherent) pinned memory that the routing kernels write directly
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&d->counts_host), sizeof(int32_t) * E,
+                               hipHostMallocMapped | hipHostMallocCoherent);
+  if (e == hipSuccess) e = hipHostGetDevicePointer(reinterpret_cast<void**>(&d->counts_dev), d->counts_host, 0);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&d->fill, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&d->ev_counts, hipEventDisableTiming);
   if (e != hipSuccess) {
@@ -131,13 +137,14 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   if (T < 1 || T > d->Tmax) return dfail(MOE_EINVAL, "moe_decoder_step: T=%d outside [1, %d]", T, d->Tmax);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const moe_decoder_buffers_t& b = d->b;
-  int rc = moe_route(x, d->dtype, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w, b.logits, b.counts, b.offsets,
-                     b.perm_src, b.perm_pos, b.route_ws, b.route_ws_bytes, stream);
-  if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
-  // the one device -> host round trip of the step: per-expert counts
-  hipError_t e = hipMemcpyAsync(d->counts_host, b.counts, sizeof(int32_t) * d->E, hipMemcpyDeviceToHost, s);
+  // routing; the kernels also store the per-expert counts straight into the
+  // host-mapped pinned buffer: the one device -> host transfer of the step
+  hipError_t e = moe::launch_route(x, d->dtype == MOE_DT_BF16, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w,
+                                   b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s,
+                                   d->counts_dev);
   if (e == hipSuccess) e = hipEventRecord(d->ev_counts, s);
-  if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: counts copy: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: routing: %s", hipGetErrorString(e));
+  int rc;
   while ((e = hipEventQuery(d->ev_counts)) == hipErrorNotReady) {
   }
   if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: counts wait: %s", hipGetErrorString(e));

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
                                                        int nwaves, int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
                                                        int32_t* __restrict__ perm_pos, int32_t* __restrict__ hist,
-                                                       uint64_t* __restrict__ bits) {
+                                                       uint64_t* __restrict__ bits, int32_t* __restrict__ counts_mirror) {
   extern __shared__ uint64_t smem[];  // nwaves * E masks, then E+1 ints
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nchunks = (T + 63) / 64;
@@ -197,6 +197,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     for (int e = 0; e < E; ++e) {
       const int v = cnt[e];
       counts[e] = v;
+      if (counts_mirror) counts_mirror[e] = v;
       offsets[e] = run;
       cnt[e] = run;
       run += v;
@@ -235,12 +236,17 @@ constexpr int kSmallT = 16;
 constexpr int kSmallE = 512;
 constexpr int kSmallChunk = 64;  // rows of Wr per block
 
-// partial[z][t][e] = sum over the block's 64 rows of x[t,h] Wr[h,e]; each
-// thread owns expert columns, the block's x slice sits in LDS.
+// partial[z][t][e] = sum over the block's 64 rows of x[t,h] Wr[h,e]. Wave w
+// takes rows w, w+4, ..., w+60 of the block; lane l takes experts 4l..4l+3
+// (+256 per pass), so each row is read as one coalesced 8-byte-per-lane
+// access (bf16) and all 16 of a lane's row loads are in flight together. The
+// four waves' sums are added in LDS in wave order.
 template <bool BF16>
 __global__ __launch_bounds__(256) void router_small_partial(const void* __restrict__ x, const void* __restrict__ Wr,
                                                             int T, int H, int E, float* __restrict__ partial) {
   __shared__ float xs[kSmallT][kSmallChunk];
+  __shared__ float red[4][1024];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h0 = blockIdx.x * kSmallChunk;
   const int nh = min(kSmallChunk, H - h0);
   for (int i = threadIdx.x; i < T * kSmallChunk; i += 256) {
@@ -248,21 +254,91 @@ __global__ __launch_bounds__(256) void router_small_partial(const void* __restri
     xs[t][h] = h < nh ? ldv<BF16>(x, (size_t)t * H + h0 + h) : 0.f;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
-    float acc[kSmallT];
+  const int tb = 1024 / (4 * 64);  // tokens per LDS reduction pass for one 256-expert slab: 4
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    const int e = e0 + 4 * lane;
+    float w[16][4];
 #pragma unroll
-    for (int t = 0; t < kSmallT; ++t) acc[t] = 0.f;
-#pragma unroll 8
-    for (int h = 0; h < nh; ++h) {
-      const float w = ldv<BF16>(Wr, (size_t)(h0 + h) * E + e);
+    for (int i = 0; i < 16; ++i) {
+      const int h = wave + 4 * i;
 #pragma unroll
-      for (int t = 0; t < kSmallT; ++t)
-        if (t < T) acc[t] = fmaf(xs[t][h], w, acc[t]);
+      for (int c = 0; c < 4; ++c) w[i][c] = 0.f;
+      if (h < nh) {
+        const size_t base = (size_t)(h0 + h) * E + e;
+        if (e + 3 < E && (E & 3) == 0) {
+          if constexpr (BF16) {
+            const uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(Wr) + base);
+            w[i][0] = __uint_as_float(v.x << 16);
+            w[i][1] = __uint_as_float(v.x & 0xFFFF0000u);
+            w[i][2] = __uint_as_float(v.y << 16);
+            w[i][3] = __uint_as_float(v.y & 0xFFFF0000u);
+          } else {
+            const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(Wr) + base);
+            w[i][0] = v.x;
+            w[i][1] = v.y;
+            w[i][2] = v.z;
+            w[i][3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (e + c < E) w[i][c] = ldv<BF16>(Wr, base + c);
+        }
+      }
     }
+    for (int t0 = 0; t0 < T; t0 += tb) {
+      float acc[4][4];
 #pragma unroll
-    for (int t = 0; t < kSmallT; ++t)
-      if (t < T) partial[((size_t)blockIdx.x * T + t) * E + e] = acc[t];
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[tt][c] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = wave + 4 * i;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (t0 + tt < T && h < kSmallChunk) {
+            const float xv = xs[t0 + tt][h];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[tt][c] = fmaf(xv, w[i][c], acc[tt][c]);
+          }
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) red[wave][(tt * 64 + lane) * 4 + c] = acc[tt][c];
+      __syncthreads();
+      // 256 threads: thread -> (token tt, expert column) of this slab
+      for (int q = threadIdx.x; q < 4 * 256; q += 256) {
+        const int tt = q >> 8, col = q & 255;
+        const int t = t0 + tt, ee = e0 + col;
+        if (t < T && ee < E) {
+          const int idx = (tt * 64 + (col >> 2)) * 4 + (col & 3);
+          const float sum = ((red[0][idx] + red[1][idx]) + red[2][idx]) + red[3][idx];
+          partial[((size_t)blockIdx.x * T + t) * E + ee] = sum;
+        }
+      }
+      __syncthreads();
+    }
   }
+}
+
+// Sum of p[z * stride] for z in [z0, z1), 16 independent accumulators added
+// in a fixed order at the end.
+__device__ __forceinline__ float sum_partials(const float* __restrict__ p, size_t stride, int z0, int z1) {
+  float a[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) a[u] = 0.f;
+  int z = z0;
+  for (; z + 16 <= z1; z += 16) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) a[u] += p[(size_t)(z + u) * stride];
+  }
+  for (int u = 0; z < z1; ++z, ++u) a[u] += p[(size_t)z * stride];
+#pragma unroll
+  for (int u = 1; u < 16; ++u) a[0] += a[u];
+  return a[0];
 }
 
 // One block: logits = sum of the partials + bias (fixed order), top-k of
@@ -273,31 +349,43 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
                                                            float* __restrict__ logits, int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm_src,
-                                                           int32_t* __restrict__ perm_pos) {
+                                                           int32_t* __restrict__ perm_pos,
+                                                           int32_t* __restrict__ counts_mirror) {
   __shared__ float lg[kSmallT * kSmallE];
   __shared__ int32_t sidx[kSmallT * 16];
   __shared__ unsigned long long bm[kSmallE];
   __shared__ int32_t wsum[16];
   __shared__ int32_t soff[kSmallE];
+  __shared__ float zsum[1024];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int e = tid; e < E; e += 1024) bm[e] = 0ull;
-  for (int i = tid; i < T * E; i += 1024) {
-    const int t = i / E, e = i - t * E;
-    const float* p = partial + (size_t)t * E + e;
-    const size_t zs = (size_t)T * E;
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    int z = 0;
-    for (; z + 4 <= nsplit; z += 4) {
-      a0 += p[(size_t)z * zs];
-      a1 += p[(size_t)(z + 1) * zs];
-      a2 += p[(size_t)(z + 2) * zs];
-      a3 += p[(size_t)(z + 3) * zs];
+  // logits: G threads per (t, e) each add a contiguous range of the partials
+  // (16 loads in flight), then the G range sums are added in range order.
+  {
+    const int n = T * E;
+    const int G = n <= 256 ? 4 : (n <= 512 ? 2 : 1);
+    const int zper = (nsplit + G - 1) / G;
+    if (G > 1) {
+      if (tid < n * G) {
+        const int i = tid % n, g = tid / n;
+        zsum[tid] = sum_partials(partial + i, (size_t)n, g * zper, min(nsplit, (g + 1) * zper));
+      }
+      __syncthreads();
+      if (tid < n) {
+        float l = 0.f;
+        for (int g = 0; g < G; ++g) l += zsum[g * n + tid];
+        if (bias) l += bias[tid % E];
+        lg[tid] = l;
+        if (logits) logits[tid] = l;
+      }
+    } else {
+      for (int i = tid; i < n; i += 1024) {
+        float l = sum_partials(partial + i, (size_t)n, 0, nsplit);
+        if (bias) l += bias[i % E];
+        lg[i] = l;
+        if (logits) logits[i] = l;
+      }
     }
-    for (; z < nsplit; ++z) a0 += p[(size_t)z * zs];
-    float l = (a0 + a1) + (a2 + a3);
-    if (bias) l += bias[e];
-    lg[i] = l;
-    if (logits) logits[i] = l;
   }
   __syncthreads();
   if (wave < T) {
@@ -350,6 +438,7 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
     counts[tid] = c;
     offsets[tid] = excl;
     soff[tid] = excl;
+    if (counts_mirror) counts_mirror[tid] = c;
   }
   if (tid == 0) offsets[E] = T * k;
   __syncthreads();
@@ -414,7 +503,7 @@ size_t route_workspace_bytes(int T, int H, int E, int k) {
 
 hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
-                        int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s) {
+                        int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s, int32_t* counts_mirror) {
   const RoutePlan p = plan_route(T, H, E, bf16);
   char* w = static_cast<char*>(ws);
   float* partial = reinterpret_cast<float*>(w);
@@ -430,7 +519,7 @@ hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* b
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     hipLaunchKernelGGL(route_finish_small, dim3(1), dim3(1024), 0, s, partial, T > 0 ? p.nsplit : 0, bias, T, E, k,
-                       topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos);
+                       topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos, counts_mirror);
     return hipGetLastError();
   }
   if (p.mode == 1) {
@@ -453,7 +542,7 @@ hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* b
   while (nwaves > 1 && (size_t)nwaves * E * 8 + (E + 1) * 4 > 64 * 1024) nwaves /= 2;
   const size_t lds = (size_t)nwaves * E * 8 + (size_t)(E + 1) * 4;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, topk_idx, T, E, k, nwaves, counts, offsets, perm_src,
-                     perm_pos, hist, bits);
+                     perm_pos, hist, bits, counts_mirror);
   return hipGetLastError();
 }
 

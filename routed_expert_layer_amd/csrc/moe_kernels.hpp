@@ -75,7 +75,8 @@ struct WorkArgs {
 size_t route_workspace_bytes(int T, int H, int E, int k);
 hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
-                        int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s);
+                        int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s,
+                        int32_t* counts_mirror = nullptr);  // optional host-mapped copy of counts
 
 hipError_t launch_pack(int wfmt, int H, int I, const void* W1, const void* W3, const void* W2,
                        const void* s1, const void* s3, const void* s2, void* blob, hipStream_t s);
