@@ -79,8 +79,8 @@ def bench_decode(args, torch, L, gen, cfg):
     from routed_expert_layer_amd.runtime import DecodeLayer, ExpertStore
     dev = "cuda"
     t0 = time.time()
-    store = ExpertStore(cfg.L, cfg.E, cfg.H, cfg.I, cfg.wfmt)
-    for layer in range(cfg.L):
+    store = ExpertStore(cfg.L, cfg.E, cfg.H, cfg.I, cfg.wfmt, phys_layers=cfg.pool_layers)
+    for layer in range(store.P):
         store.pack_layer(layer, lambda e: gen.expert_weights(cfg, layer, e, dev))
     print(f"[bench] pool {store.nbytes / 1e9:.2f} GB packed in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     n_total = args.warmup + args.steps
@@ -126,7 +126,7 @@ def bench_decode(args, torch, L, gen, cfg):
     torch.cuda.synchronize()
     e0.record(fs)
     misses = [[key, slot, -1, 0] for slot, key in enumerate(range(n_copy))]
-    L.cache_fill_async(dl.cache, misses, store.pool, store.stride, store.blob, dl.slots, store.stride, fs, fs)
+    L.cache_fill_async(dl.cache, misses, store.layer_ptrs, store.stride, store.blob, dl.slots, store.stride, fs, fs)
     e1.record(fs)
     torch.cuda.synchronize()
     fill_gbs = n_copy * store.blob / (e0.elapsed_time(e1) * 1e-3) / 1e9

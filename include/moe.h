@@ -184,7 +184,9 @@ int moe_cache_stats(const moe_cache_t* cache, int64_t* hits, int64_t* misses);
  * can be copied into the cache and executed on the GPU).
  *
  * cache_fill_async: for each miss, copies blob `key` of the pool
- * (pool + key*blob_stride, blob_bytes bytes; pinned host memory) to slot
+ * (layer_pool[key / E] + (key % E)*blob_stride, blob_bytes bytes; pinned host
+ * memory; layer_pool holds the L per-layer base addresses, which may repeat
+ * when layers share weights) to slot
  * `slot` (slot_base + slot*slot_stride; device). Ordering: the copies start
  * only after all work enqueued on compute_stream before this call (which
  * includes every earlier reader of a victim slot), run on fill_stream, and
@@ -194,7 +196,7 @@ int moe_cache_stats(const moe_cache_t* cache, int64_t* hits, int64_t* misses);
  * should then moe_cache_invalidate the affected keys).
  * ------------------------------------------------------------------------ */
 int cache_fill_async(moe_cache_t* cache, const moe_miss_t* misses, int n,
-                     const void* pool, size_t blob_stride, size_t blob_bytes,
+                     const void* const* layer_pool, size_t blob_stride, size_t blob_bytes,
                      void* slot_base, size_t slot_stride,
                      void* fill_stream, void* compute_stream);
 
@@ -249,8 +251,9 @@ int moe_combine(const float* y_perm, const int32_t* perm_pos, const float* topk_
  * GPU computes the current layer.
  *
  * A pipe owns two device buffers of layer_bytes each (allocated at create)
- * and copies layer l's experts (pool + l*layer_stride, layer_bytes bytes,
- * pinned host) into buffer l % 2 on its own copy stream.
+ * and copies layer l's experts (layer_src[l], layer_bytes bytes, pinned host;
+ * the array holds n_layers addresses and is copied at create) into buffer
+ * l % 2 on its own copy stream.
  * moe_pipe_begin_layer(l, compute_stream): makes compute_stream wait until
  *   layer l is resident (starting its copy if it was not started), then starts
  *   the copy of layer l+1 into the other buffer once the compute of layer l-1
@@ -262,8 +265,7 @@ int moe_combine(const float* y_perm, const int32_t* perm_pos, const float* topk_
  * Layers must be visited in order 0, 1, ..., n_layers-1.
  * ------------------------------------------------------------------------ */
 typedef struct moe_pipe moe_pipe_t;
-moe_pipe_t* moe_pipe_create(const void* pool, size_t layer_stride, size_t layer_bytes,
-                            int n_layers, int* status);
+moe_pipe_t* moe_pipe_create(const void* const* layer_src, size_t layer_bytes, int n_layers, int* status);
 int moe_pipe_destroy(moe_pipe_t* pipe);
 int moe_pipe_begin_layer(moe_pipe_t* pipe, int layer, void* compute_stream, void** buffer);
 int moe_pipe_end_layer(moe_pipe_t* pipe, int layer, void* compute_stream);
@@ -279,8 +281,9 @@ int moe_pipe_copy_ms(moe_pipe_t* pipe, int layer, float* ms);
  * those calls. Page "FreeToken-rtx-4090", phase table row "Decode" (the
  * shared LRU cache) and component table rows "GPU memory" and "PCIe link".
  *
- * moe_decoder_create: `cache` is used (not owned); pool holds blob `key` at
- *   pool + key*blob_stride (pinned host); slots at slot_base + slot*slot_stride
+ * moe_decoder_create: `cache` is used (not owned); blob `key` is at
+ *   layer_pool[key / E] + (key % E)*blob_stride (pinned host; the array of the
+ *   cache's L layer addresses is copied); slots at slot_base + slot*slot_stride
  *   (device). `buffers` are caller-owned device buffers sized for T_max tokens:
  *   topk_idx int32 [T_max,k], topk_w fp32 [T_max,k], logits fp32 [T_max,E] or
  *   NULL, counts int32 [E], offsets int32 [E+1], perm_src int32 [T_max*k],
@@ -315,7 +318,8 @@ typedef struct {
 } moe_decoder_buffers_t;
 
 moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, int E, int k, int dtype, int wfmt,
-                                  const void* pool, size_t blob_stride, void* slot_base, size_t slot_stride,
+                                  const void* const* layer_pool, size_t blob_stride, void* slot_base,
+                                  size_t slot_stride,
                                   const moe_decoder_buffers_t* buffers, int* status);
 int moe_decoder_destroy(moe_decoder_t* decoder);
 int moe_decoder_step(moe_decoder_t* decoder, int step, int layer, const void* x, int T, const void* Wr,

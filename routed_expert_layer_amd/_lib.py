@@ -76,11 +76,11 @@ _sig("moe_cache_clear_trace", I32, P)
 _sig("moe_cache_invalidate", I32, P, I32)
 _sig("moe_cache_slot_of", I32, P, I32, PI)
 _sig("moe_cache_stats", I32, P, PI64, PI64)
-_sig("cache_fill_async", I32, P, P, I32, P, SZ, SZ, P, SZ, P, P)
+_sig("cache_fill_async", I32, P, P, I32, P, SZ, SZ, P, SZ, P, P)  # layer_pool: array of L addresses
 _sig("moe_ffn_workspace_size", SZ, I32, I32, I32, I32)
 _sig("moe_ffn", I32, P, I32, P, P, I32, P, SZ, I32, I32, I32, P, P, SZ, I32, P)
 _sig("moe_combine", I32, P, P, P, I32, I32, I32, P, I32, P)
-_sig("moe_pipe_create", P, P, SZ, SZ, I32, PI)
+_sig("moe_pipe_create", P, P, SZ, I32, PI)
 _sig("moe_pipe_destroy", I32, P)
 _sig("moe_pipe_begin_layer", I32, P, I32, P, ctypes.POINTER(ctypes.c_void_p))
 _sig("moe_pipe_end_layer", I32, P, I32, P)
@@ -241,10 +241,17 @@ def moe_cache_stats(cache):
     return h.value, m.value
 
 
-def cache_fill_async(cache, misses, pool, blob_stride, blob_bytes, slot_base, slot_stride, fill_stream=None,
+def layer_table(addrs):
+    """uint64 array of per-layer host addresses (the `const void* const*` the ABI takes)."""
+    return np.ascontiguousarray(np.asarray(addrs, dtype=np.uint64))
+
+
+def cache_fill_async(cache, misses, layer_pool, blob_stride, blob_bytes, slot_base, slot_stride, fill_stream=None,
                      compute_stream=None):
+    """layer_pool: per-layer base addresses of the pool (see layer_table)."""
     ms = np.ascontiguousarray(np.asarray(misses, dtype=np.int32).reshape(-1, 4))
-    _check(_lib.cache_fill_async(cache.h, ms.ctypes.data if len(ms) else None, len(ms), _ptr(pool), blob_stride,
+    lp = layer_table(layer_pool)
+    _check(_lib.cache_fill_async(cache.h, ms.ctypes.data if len(ms) else None, len(ms), lp.ctypes.data, blob_stride,
                                  blob_bytes, _ptr(slot_base), slot_stride, _stream(fill_stream),
                                  _stream(compute_stream)), "cache_fill_async")
 
@@ -272,9 +279,10 @@ def moe_combine(y_perm, perm_pos, topk_w, out, stream=None):
 
 # ---------------------------------------------------------------------------
 class MoePipe:
-    def __init__(self, pool, layer_stride, layer_bytes, n_layers):
+    def __init__(self, layer_src, layer_bytes):
         st = ctypes.c_int(0)
-        self.h = _lib.moe_pipe_create(_ptr(pool), layer_stride, layer_bytes, n_layers, ctypes.byref(st))
+        lp = layer_table(layer_src)
+        self.h = _lib.moe_pipe_create(lp.ctypes.data, layer_bytes, len(lp), ctypes.byref(st))
         if not self.h:
             raise MoEError(st.value, _lib.moe_last_error().decode())
 
@@ -286,8 +294,8 @@ class MoePipe:
     __del__ = close
 
 
-def moe_pipe_create(pool, layer_stride, layer_bytes, n_layers):
-    return MoePipe(pool, layer_stride, layer_bytes, n_layers)
+def moe_pipe_create(layer_src, layer_bytes):
+    return MoePipe(layer_src, layer_bytes)
 
 
 def moe_pipe_destroy(pipe):
@@ -314,7 +322,7 @@ def moe_pipe_copy_ms(pipe, layer):
 class MoeDecoder:
     """Owner of a moe_decoder_t; `bufs` maps DecoderBuffers field names to torch tensors (kept alive here)."""
 
-    def __init__(self, cache, T_max, H, I, E, k, dtype, wfmt, pool, blob_stride, slot_base, slot_stride, bufs):
+    def __init__(self, cache, T_max, H, I, E, k, dtype, wfmt, layer_pool, blob_stride, slot_base, slot_stride, bufs):
         self.keep = bufs
         b = DecoderBuffers()
         for name in ("topk_idx", "topk_w", "logits", "counts", "offsets", "perm_src", "perm_pos", "y_perm"):
@@ -322,7 +330,8 @@ class MoeDecoder:
         b.route_ws, b.route_ws_bytes = _ptr(bufs["route_ws"]), bufs["route_ws"].numel()
         b.ffn_ws, b.ffn_ws_bytes = _ptr(bufs["ffn_ws"]), bufs["ffn_ws"].numel()
         st = ctypes.c_int(0)
-        self.h = _lib.moe_decoder_create(cache.h, T_max, H, I, E, k, dtype, wfmt, _ptr(pool), blob_stride,
+        lp = layer_table(layer_pool)
+        self.h = _lib.moe_decoder_create(cache.h, T_max, H, I, E, k, dtype, wfmt, lp.ctypes.data, blob_stride,
                                          _ptr(slot_base), slot_stride, ctypes.byref(b), ctypes.byref(st))
         if not self.h:
             raise MoEError(st.value, _lib.moe_last_error().decode())

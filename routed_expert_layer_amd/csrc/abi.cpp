@@ -54,8 +54,8 @@ struct moe_cache {
 };
 
 struct moe_pipe {
-  const char* pool;
-  size_t stride, bytes;
+  std::vector<const char*> src;
+  size_t bytes;
   int L;
   void* buf[2] = {nullptr, nullptr};
   hipStream_t copy = nullptr;
@@ -64,6 +64,14 @@ struct moe_pipe {
   int next_begin = 0;  // next layer expected by begin_layer
   int next_end = 0;    // next layer expected by end_layer
 };
+
+// Internal accessors for the decode driver (C++ linkage).
+int moe_cache_layers(const moe_cache_t* c, int* n_layers) {
+  if (!c || !n_layers) return MOE_EINVAL;
+  *n_layers = c->L;
+  return MOE_OK;
+}
+int moe_cache_experts(const moe_cache_t* c) { return c ? c->E : -1; }
 
 extern "C" {
 
@@ -238,9 +246,10 @@ int moe_cache_stats(const moe_cache_t* c, int64_t* hits, int64_t* misses) {
 // ---------------------------------------------------------------------------
 // Fills
 // ---------------------------------------------------------------------------
-int cache_fill_async(moe_cache_t* c, const moe_miss_t* misses, int n, const void* pool, size_t blob_stride,
-                     size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream, void* compute_stream) {
-  if (!c || n < 0 || (n > 0 && (!misses || !pool || !slot_base)) || blob_bytes > slot_stride ||
+int cache_fill_async(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
+                     size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
+                     void* compute_stream) {
+  if (!c || n < 0 || (n > 0 && (!misses || !layer_pool || !slot_base)) || blob_bytes > slot_stride ||
       blob_bytes > blob_stride)
     return fail(MOE_EINVAL, "cache_fill_async: bad argument");
   if (n == 0) return MOE_OK;
@@ -259,11 +268,13 @@ int cache_fill_async(moe_cache_t* c, const moe_miss_t* misses, int n, const void
     if (e == hipSuccess) e = hipStreamWaitEvent(fs, c->ev_war, 0);
     if (e != hipSuccess) return hip_fail(e, "cache_fill_async: ordering after compute");
   }
-  const char* src = static_cast<const char*>(pool);
   char* dst = static_cast<char*>(slot_base);
   for (int i = 0; i < n; ++i) {
-    e = hipMemcpyAsync(dst + (size_t)misses[i].slot * slot_stride, src + (size_t)misses[i].key * blob_stride,
-                       blob_bytes, hipMemcpyHostToDevice, fs);
+    const int layer = misses[i].key / c->E, ex = misses[i].key % c->E;
+    const char* src = static_cast<const char*>(layer_pool[layer]);
+    if (!src) return fail(MOE_EINVAL, "cache_fill_async: no pool address for layer %d", layer);
+    e = hipMemcpyAsync(dst + (size_t)misses[i].slot * slot_stride, src + (size_t)ex * blob_stride, blob_bytes,
+                       hipMemcpyHostToDevice, fs);
     if (e != hipSuccess) return hip_fail(e, "cache_fill_async: copy");
   }
   if (split) {
@@ -363,8 +374,10 @@ static void pipe_release(moe_pipe_t* p) {
   delete p;
 }
 
-moe_pipe_t* moe_pipe_create(const void* pool, size_t layer_stride, size_t layer_bytes, int n_layers, int* status) {
-  if (!pool || n_layers <= 0 || layer_bytes == 0 || layer_bytes > layer_stride) {
+moe_pipe_t* moe_pipe_create(const void* const* layer_src, size_t layer_bytes, int n_layers, int* status) {
+  bool ok = layer_src && n_layers > 0 && layer_bytes > 0;
+  for (int l = 0; ok && l < n_layers; ++l) ok = layer_src[l] != nullptr;
+  if (!ok) {
     if (status) *status = fail(MOE_EINVAL, "moe_pipe_create: bad argument");
     return nullptr;
   }
@@ -373,8 +386,7 @@ moe_pipe_t* moe_pipe_create(const void* pool, size_t layer_stride, size_t layer_
     if (status) *status = fail(MOE_ENOMEM, "moe_pipe_create: out of host memory");
     return nullptr;
   }
-  p->pool = static_cast<const char*>(pool);
-  p->stride = layer_stride;
+  for (int l = 0; l < n_layers; ++l) p->src.push_back(static_cast<const char*>(layer_src[l]));
   p->bytes = layer_bytes;
   p->L = n_layers;
   p->copied.assign(n_layers, nullptr);
@@ -414,7 +426,7 @@ static hipError_t pipe_start_copy(moe_pipe_t* p, int l) {
   if (l >= 2) e = hipStreamWaitEvent(p->copy, p->done[l - 2], 0);  // buffer l%2 was last read by layer l-2
   if (e == hipSuccess) e = hipEventRecord(p->started[l], p->copy);
   if (e == hipSuccess)
-    e = hipMemcpyAsync(p->buf[l & 1], p->pool + (size_t)l * p->stride, p->bytes, hipMemcpyHostToDevice, p->copy);
+    e = hipMemcpyAsync(p->buf[l & 1], p->src[l], p->bytes, hipMemcpyHostToDevice, p->copy);
   if (e == hipSuccess) e = hipEventRecord(p->copied[l], p->copy);
   if (e == hipSuccess) p->next_copy = l + 1;
   return e;

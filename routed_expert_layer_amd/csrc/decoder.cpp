@@ -16,6 +16,8 @@
 #include "moe_kernels.hpp"
 
 extern "C" const char* moe_last_error(void);
+int moe_cache_layers(const moe_cache_t* c, int* n_layers);
+int moe_cache_experts(const moe_cache_t* c);
 
 namespace {
 // Errors go to the library's per-thread message (moe_last_error).
@@ -28,7 +30,7 @@ int dfail(int code, const char* fmt, A... a) {
 struct moe_decoder {
   moe_cache_t* cache;
   int Tmax, H, I, E, k, dtype, wfmt;
-  const void* pool;
+  std::vector<const void*> layer_pool;
   size_t blob_stride, blob_bytes;
   void* slot_base;
   size_t slot_stride;
@@ -60,13 +62,13 @@ static void decoder_release(moe_decoder_t* d) {
 }
 
 moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, int E, int k, int dtype, int wfmt,
-                                  const void* pool, size_t blob_stride, void* slot_base, size_t slot_stride,
-                                  const moe_decoder_buffers_t* buffers, int* status) {
+                                  const void* const* layer_pool, size_t blob_stride, void* slot_base,
+                                  size_t slot_stride, const moe_decoder_buffers_t* buffers, int* status) {
   auto bad = [&](int code, const char* msg) -> moe_decoder_t* {
     if (status) *status = dfail(code, "moe_decoder_create: %s", msg);
     return nullptr;
   };
-  if (!cache || !pool || !slot_base || !buffers) return bad(MOE_EINVAL, "null argument");
+  if (!cache || !layer_pool || !slot_base || !buffers) return bad(MOE_EINVAL, "null argument");
   if (T_max < 1 || H < 1 || I < 1 || E < 1 || E > 1024 || k < 1 || k > 16 || k > E || H % 8 != 0)
     return bad(MOE_EINVAL, "bad sizes");
   if (dtype != MOE_DT_F32 && dtype != MOE_DT_BF16) return bad(MOE_EINVAL, "bad activation dtype");
@@ -83,7 +85,19 @@ moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, i
   if (!d) return bad(MOE_ENOMEM, "out of host memory");
   d->cache = cache;
   d->Tmax = T_max; d->H = H; d->I = I; d->E = E; d->k = k; d->dtype = dtype; d->wfmt = wfmt;
-  d->pool = pool; d->blob_stride = blob_stride; d->blob_bytes = blob;
+  int n_layers = 0;
+  if (moe_cache_layers(cache, &n_layers) != MOE_OK || moe_cache_experts(cache) != E) {
+    delete d;
+    return bad(MOE_EINVAL, "cache does not match E");
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    if (!layer_pool[l]) {
+      delete d;
+      return bad(MOE_EINVAL, "null layer pool address");
+    }
+    d->layer_pool.push_back(layer_pool[l]);
+  }
+  d->blob_stride = blob_stride; d->blob_bytes = blob;
   d->slot_base = slot_base; d->slot_stride = slot_stride;
   d->b = b;
   // fine-grained (coherent) pinned memory that the routing kernels write directly
@@ -170,7 +184,8 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
     for (int i = 0; i < nm; ++i)
       if (d->misses[i].wave == w) d->wave_misses.push_back(d->misses[i]);
     if (!d->wave_misses.empty()) {
-      rc = cache_fill_async(d->cache, d->wave_misses.data(), (int)d->wave_misses.size(), d->pool, d->blob_stride,
+      rc = cache_fill_async(d->cache, d->wave_misses.data(), (int)d->wave_misses.size(), d->layer_pool.data(),
+                            d->blob_stride,
                             d->blob_bytes, d->slot_base, d->slot_stride, d->fill, stream);
       if (rc != MOE_OK) {
         // this wave's and every later wave's misses were never copied: unmap them

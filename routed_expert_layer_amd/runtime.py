@@ -33,32 +33,44 @@ def host_view(addr, nbytes):
 
 
 class ExpertStore:
-    """All experts of L layers as packed blobs in one page-locked host pool.
+    """The experts of L layers as packed blobs in page-locked host memory.
 
-    Blob of (layer, expert) sits at key * stride, key = layer * E + expert.
+    One pinned region per physical layer; layer l reads physical layer
+    l % phys_layers (phys_layers < L lets several layers share the same weights
+    when the machine cannot pin a full pool). Blob of expert e of layer l is at
+    layer_ptrs[l] + e * stride.
     """
 
-    def __init__(self, n_layers, E, H, I, wfmt):
+    def __init__(self, n_layers, E, H, I, wfmt, phys_layers=None):
         self.L, self.E, self.H, self.I = n_layers, E, H, I
+        self.P = n_layers if phys_layers is None else phys_layers
         self.wfmt = WFMT[wfmt] if isinstance(wfmt, str) else wfmt
         self.blob = L.moe_expert_bytes(self.wfmt, H, I)
         if self.blob == 0:
             raise ValueError(f"unsupported expert shape {H}x{I} for format {wfmt}")
         self.stride = _align(self.blob, 4096)
-        self.nbytes = n_layers * E * self.stride
-        self.pool = L.moe_pool_alloc(self.nbytes)
-        self.view = host_view(self.pool, self.nbytes)
-
-    def layer_addr(self, layer):
-        return self.pool + layer * self.E * self.stride
+        self.layer_bytes = E * self.stride
+        self.nbytes = self.P * self.layer_bytes
+        self.phys, self.views = [], []
+        try:
+            for _ in range(self.P):
+                a = L.moe_pool_alloc(self.layer_bytes)
+                self.phys.append(a)
+                self.views.append(host_view(a, self.layer_bytes))
+        except Exception:
+            self.close()
+            raise
+        self.layer_ptrs = L.layer_table([self.phys[l % self.P] for l in range(n_layers)])
 
     def pack_layer(self, layer, make_expert, device="cuda", batch=16):
-        """Pack every expert of `layer` into the pool.
+        """Pack every expert of physical layer `layer` into the pool.
 
         make_expert(e) returns canonical device tensors: (W1, W3, W2) for fp32/bf16,
         or a dict with q1, q3, q2 (int8) and s1, s3, s2 (fp16) for int4.
         """
+        assert 0 <= layer < self.P
         stage = torch.empty(batch * self.stride, dtype=torch.uint8, device=device)
+        view = self.views[layer]
         for e0 in range(0, self.E, batch):
             n = min(batch, self.E - e0)
             for j in range(n):
@@ -69,15 +81,15 @@ class ExpertStore:
                                       w["s2"], dst)
                 else:
                     L.moe_pack_expert(self.wfmt, self.H, self.I, w[0], w[1], w[2], None, None, None, dst)
-            off = (layer * self.E + e0) * self.stride
-            self.view[off:off + n * self.stride].copy_(stage[:n * self.stride])
+            off = e0 * self.stride
+            view[off:off + n * self.stride].copy_(stage[:n * self.stride])
         torch.cuda.synchronize()
 
     def close(self):
-        if self.pool:
-            self.view = None
-            L.moe_pool_free(self.pool)
-            self.pool = None
+        self.views = []
+        for a in self.phys:
+            L.moe_pool_free(a)
+        self.phys = []
 
 
 class RouteBuffers:
@@ -140,7 +152,7 @@ class DecodeLayer:
                         offsets=rb.offsets, perm_src=rb.perm_src, perm_pos=rb.perm_pos, y_perm=self.y_perm,
                         route_ws=rb.ws, ffn_ws=self.ffn_ws)
             self.dec = L.MoeDecoder(self.cache, T, self.H, self.I, self.E, k,
-                                    L.MOE_DT_BF16 if act == "bf16" else L.MOE_DT_F32, store.wfmt, store.pool,
+                                    L.MOE_DT_BF16 if act == "bf16" else L.MOE_DT_F32, store.wfmt, store.layer_ptrs,
                                     store.stride, self.slots, store.stride, bufs)
 
     @property
@@ -172,8 +184,8 @@ class DecodeLayer:
         for w in range(n_waves):
             m = misses[misses[:, 3] == w]
             if len(m):
-                L.cache_fill_async(self.cache, m, self.store.pool, self.store.stride, self.store.blob, self.slots,
-                                   self.store.stride, self.fill_stream, s)
+                L.cache_fill_async(self.cache, m, self.store.layer_ptrs, self.store.stride, self.store.blob,
+                                   self.slots, self.store.stride, self.fill_stream, s)
                 self._fills += len(m)
             sel = wwave == w
             e = we[sel]

@@ -127,7 +127,7 @@ def test_argument_validation_without_gpu(L):
     assert lib.cache_fill_async(c.h, m.ctypes.data, 1, 1, 64, 64, 1, 64, None, None) == L.MOE_EINVAL
     # pipe and decoder: null arguments
     st = ctypes.c_int(0)
-    assert lib.moe_pipe_create(None, 64, 64, 2, ctypes.byref(st)) is None and st.value == L.MOE_EINVAL
+    assert lib.moe_pipe_create(None, 64, 2, ctypes.byref(st)) is None and st.value == L.MOE_EINVAL
     assert lib.moe_decoder_create(None, 1, 64, 64, 8, 2, 1, 1, None, 0, None, 0, None, ctypes.byref(st)) is None
     assert st.value == L.MOE_EINVAL
     assert lib.moe_decoder_step(None, 0, 0, None, 1, None, None, None, 0, None, None) == L.MOE_EINVAL

@@ -50,10 +50,11 @@ def oracle_out_rows(x64, idx, l64, tokens, get_expert):
     return out
 
 
-def make_store(cfg, layers):
+def make_store(cfg):
+    """Pinned pool of the config; layers sharing weight sets share pool memory."""
     from routed_expert_layer_amd.runtime import ExpertStore
-    store = ExpertStore(cfg.L, cfg.E, cfg.H, cfg.I, cfg.wfmt)
-    for layer in layers:
+    store = ExpertStore(cfg.L, cfg.E, cfg.H, cfg.I, cfg.wfmt, phys_layers=cfg.pool_layers)
+    for layer in range(store.P):
         print(f"  packing layer {layer} ({cfg.E} experts)", flush=True)
         if cfg.wfmt == "int4":
             store.pack_layer(layer, lambda e: gen.expert_int4(cfg, layer, e, dev))
@@ -70,7 +71,7 @@ def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True):
     Python."""
     from routed_expert_layer_amd.runtime import DecodeLayer
     print(f"decode {cfg.name}: L={cfg.L} T={cfg.T} steps={steps} S={cfg.S} {cfg.wfmt} native={native}", flush=True)
-    store = make_store(cfg, range(cfg.L))
+    store = make_store(cfg)
     try:
         dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev, keep_logits=True, native=native)
         Wr = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
@@ -178,10 +179,9 @@ def test_prefill_16384_double_buffered():
     from routed_expert_layer_amd import _lib as L
     from routed_expert_layer_amd.runtime import PrefillLayer
     cfg = CONFIGS["prefill_db_bf16_t16384_l8"]
-    store = make_store(cfg, range(cfg.L))
+    store = make_store(cfg)
     try:
-        layer_bytes = cfg.E * store.stride
-        pipe = L.MoePipe(store.pool, layer_bytes, layer_bytes, cfg.L)
+        pipe = L.MoePipe(store.layer_ptrs, store.layer_bytes)
         pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, store.stride, dev, keep_logits=True)
         s = torch.cuda.current_stream()
         for layer in range(cfg.L):

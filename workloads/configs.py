@@ -10,6 +10,11 @@ double buffering followed by an int4 decode phase on the same layers.
 Reading of "N(0, 1/sqrt(fan_in))": standard deviation 1/sqrt(fan_in).
 Reading of "router bias drawn Zipf(s)": b_e = -s * ln(rank_e) with rank a
 seeded permutation of 1..E, which makes expert popularity Zipf-skewed.
+
+The 8-layer bf16 pool (8 x 12.88 GB) exceeds the ~64 GiB of page-locked host
+memory the test machines allow, so its layers share four weight sets (layer l
+uses set l % 4); routers and biases stay distinct per layer and every layer is
+still copied in full, so the transfer volume is unchanged.
 """
 from dataclasses import dataclass, field
 from typing import Optional
@@ -32,6 +37,7 @@ class Config:
     S: Optional[int] = None       # cache slots (None: every expert resident)
     phase: str = "decode"  # "decode" | "prefill"
     weights_of: Optional[str] = None  # reuse another config's layer weights
+    pool_layers: Optional[int] = None  # distinct weight sets; layer l uses set l % pool_layers
     group: int = 128       # int4 group size along K
     extra: dict = field(default_factory=dict)
 
@@ -55,11 +61,12 @@ CONFIGS = {
                                       k=6, act="bf16", wfmt="bf16", zipf_s=0.0, phase="prefill"),
     # 8-layer prefill, 16384 tokens per layer, Zipf(1.5) routing, double-buffered layer copies
     "prefill_db_bf16_t16384_l8": Config("prefill_db_bf16_t16384_l8", L=8, T=16384, steps=1, H=4096, E=256,
-                                        I=2048, k=6, act="bf16", wfmt="bf16", zipf_s=1.5, phase="prefill"),
+                                        I=2048, k=6, act="bf16", wfmt="bf16", zipf_s=1.5, phase="prefill",
+                                        pool_layers=4),
     # int4 decode on the same 8 layers, batch 8, 512-entry shared cache
     "decode_int4_t8_l8": Config("decode_int4_t8_l8", L=8, T=8, steps=256, H=4096, E=256, I=2048, k=6,
                                 act="bf16", wfmt="int4", zipf_s=1.5, S=512,
-                                weights_of="prefill_db_bf16_t16384_l8"),
+                                weights_of="prefill_db_bf16_t16384_l8", pool_layers=4),
 }
 
 

@@ -73,12 +73,16 @@ def router_bias(cfg, layer=0, step=0, device="cpu"):
 def expert_weights(cfg, layer, e, device="cpu", dtype=None):
     """Canonical expert weights: W1, W3 [H, I] (std 1/sqrt(H)); W2 [I, H] (std 1/sqrt(I)).
 
+    With cfg.pool_layers set, layer l has the weights of layer l % pool_layers.
+
     `dtype` defaults to the config's storage type (fp32 or bf16). For int4
     configs the bf16 weights of the same (layer, expert) are generated here and
     quantised by :func:`expert_int4`.
     """
     if dtype is None:
         dtype = torch.float32 if cfg.wfmt == "f32" else torch.bfloat16
+    if cfg.pool_layers:
+        layer = layer % cfg.pool_layers
     key = (cfg.seed_name, "W", layer, e)
     W1 = normal((cfg.H, cfg.I), 1.0 / math.sqrt(cfg.H), key + ("W1",), device, dtype)
     W3 = normal((cfg.H, cfg.I), 1.0 / math.sqrt(cfg.H), key + ("W3",), device, dtype)
