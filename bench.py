@@ -12,8 +12,10 @@ trace; the next K steps are timed.
 Also reported: the dominant kernel (the decode expert FFN) against the HBM
 roofline, timed with HIP events on its own stream; the pinned host-to-device
 fill bandwidth; the 4096-token prefill layer's expert GEMM against the bf16
-matrix-core peak; and the CPU oracle on a bounded sample of the same decode
-workload.
+matrix-core peak; the 8-layer 16384-token prefill with double-buffered layer
+copies (GEMM TFLOP/s, copy GB/s, how much compute the copies hide); the
+int4 8-layer decode and the 48-layer bf16 decode stack (tokens/s, FFN GB/s,
+hit rate); and the CPU oracle on a bounded sample of the decode workload.
 
 Prints one JSON line.
 """
@@ -176,6 +178,105 @@ def bench_prefill(args, torch, L, gen, cfg, reps=5):
                 group_min=int(pl.last_counts[pl.last_counts > 0].min()), group_max=int(pl.last_counts.max()))
 
 
+def bench_prefill_pipeline(args, torch, L, gen, cfg):
+    """8-layer prefill: layer l+1's experts copy host -> HBM while layer l computes."""
+    from routed_expert_layer_amd.runtime import ExpertStore, PrefillLayer
+    dev = "cuda"
+    store = ExpertStore(cfg.L, cfg.E, cfg.H, cfg.I, cfg.wfmt, phys_layers=cfg.pool_layers)
+    try:
+        for layer in range(store.P):
+            store.pack_layer(layer, lambda e: gen.expert_weights(cfg, layer, e, dev))
+        xs = [gen.tokens(cfg, 0, l, dev) for l in range(cfg.L)]
+        Wrs = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
+        bs = [gen.router_bias(cfg, l, 0, dev) for l in range(cfg.L)]
+        pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, store.stride, dev)
+        s = torch.cuda.current_stream()
+        # warm-up pass (kernels and the copy path), then the timed pass
+        for rep in range(2):
+            pipe = L.MoePipe(store.layer_ptrs, store.layer_bytes)
+            timer = EventTimer(torch, cfg.L)
+            timer.enabled = rep == 1
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cfg.L)]
+            groups = []
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for l in range(cfg.L):
+                base = L.moe_pipe_begin_layer(pipe, l, s)
+                ev[l][0].record(s)
+                pl.forward(xs[l], Wrs[l], bs[l], base, timer=timer)
+                ev[l][1].record(s)
+                L.moe_pipe_end_layer(pipe, l, s)
+                groups.append((int((pl.last_counts > 0).sum()), int(pl.last_counts.max())))
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) * 1e3
+            copy_ms = [L.moe_pipe_copy_ms(pipe, l) for l in range(cfg.L)]
+            comp_ms = [a.elapsed_time(b) for a, b in ev]
+            pipe.close()
+        flops, gemm_ms, n = timer.result()
+        tfs = flops / (gemm_ms * 1e-3) / 1e12
+        exposed = max(0.0, wall - sum(copy_ms))
+        return dict(workload=cfg.name, layers=cfg.L, tokens_per_layer=cfg.T,
+                    gemm_tflops=tfs, mfma_frac=tfs / MFMA_BF16_PEAK_TFS, gemm_ms_per_layer=gemm_ms / n,
+                    layer_compute_ms=sum(comp_ms) / cfg.L, copy_ms_per_layer=sum(copy_ms) / cfg.L,
+                    copy_gbs=store.layer_bytes / (sum(copy_ms) / cfg.L * 1e-3) / 1e9,
+                    copy_frac_pcie=store.layer_bytes / (sum(copy_ms) / cfg.L * 1e-3) / 1e9 / PCIE_PEAK_GBS,
+                    wall_ms=wall, compute_hidden_frac=1.0 - min(1.0, exposed / max(sum(comp_ms), 1e-9)),
+                    prefill_tokens_per_s=cfg.L * cfg.T / (wall * 1e-3) / cfg.L,
+                    active_experts=[g[0] for g in groups], max_group=[g[1] for g in groups],
+                    weight_sets=store.P)
+    finally:
+        store.close()
+
+
+def bench_decode_layers(args, torch, L, gen, cfg, warm, steps):
+    """Multi-layer decode with one shared cache: every step runs all layers."""
+    from routed_expert_layer_amd.runtime import DecodeLayer, ExpertStore
+    dev = "cuda"
+    store = ExpertStore(cfg.L, cfg.E, cfg.H, cfg.I, cfg.wfmt, phys_layers=cfg.pool_layers)
+    try:
+        for layer in range(store.P):
+            if cfg.wfmt == "int4":
+                store.pack_layer(layer, lambda e: gen.expert_int4(cfg, layer, e, dev))
+            else:
+                store.pack_layer(layer, lambda e: gen.expert_weights(cfg, layer, e, dev))
+        n = warm + steps
+        xs = [[gen.tokens(cfg, st, l, dev) for l in range(cfg.L)] for st in range(n)]
+        Wrs = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
+        bias = {}
+
+        def b(l, st):
+            ep = (st // cfg.epoch) if cfg.epoch else 0
+            if (l, ep) not in bias:
+                bias[(l, ep)] = gen.router_bias(cfg, l, st, dev)
+            return bias[(l, ep)]
+
+        dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+        s = torch.cuda.current_stream()
+        for st in range(warm):
+            for l in range(cfg.L):
+                dl.step(st, l, xs[st][l], Wrs[l], b(l, st), s)
+        torch.cuda.synchronize()
+        f0 = dl.n_fills
+        L.moe_decoder_profile(dl.dec, True)
+        t0 = time.perf_counter()
+        for st in range(warm, n):
+            for l in range(cfg.L):
+                dl.step(st, l, xs[st][l], Wrs[l], b(l, st), s)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        fb, fms, fn = L.moe_decoder_ffn_stats(dl.dec)
+        tr = dl.trace()
+        timed = tr[tr[:, 0] >= warm]
+        gbs = fb / (fms * 1e-3) / 1e9
+        return dict(workload=cfg.name, layers=cfg.L, tokens_per_step=cfg.T, steps_timed=steps, steps_warmup=warm,
+                    tokens_per_s=steps * cfg.T / el, ms_per_step=el * 1e3 / steps,
+                    ms_per_layer_step=el * 1e3 / (steps * cfg.L), ffn_gbs=gbs, ffn_hbm_frac=gbs / HBM_PEAK_GBS,
+                    ffn_us_per_call=fms * 1e3 / max(fn, 1), hit_rate=float(timed[:, 3].mean()),
+                    fills_timed=dl.n_fills - f0, weight_sets=store.P)
+    finally:
+        store.close()
+
+
 def cpu_baseline(args, torch, gen, cfg):
     """The oracle, as it stands, on a bounded sample of decode steps (host cores)."""
     import numpy as np
@@ -219,6 +320,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=128)
     ap.add_argument("--workload", default="decode_bf16_h4096_e256")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the int4 8-layer and 48-layer decode sections")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -271,9 +373,17 @@ def main():
                      "avg_launch_us": round(ffn["ms"] * 1e3 / max(ffn["n"], 1), 2), "launches": ffn["n"]},
         "decode": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res["decode"].items()},
     }
+    def rnd(d):
+        return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+
     if not args.no_prefill:
-        p = bench_prefill(args, torch, L, gen, CONFIGS["prefill_bf16_t4096_e256"])
-        out["prefill"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}
+        out["prefill"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_bf16_t4096_e256"]))
+        out["prefill_double_buffered"] = rnd(bench_prefill_pipeline(args, torch, L, gen,
+                                                                    CONFIGS["prefill_db_bf16_t16384_l8"]))
+    if not args.no_extra:
+        out["decode_int4"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["decode_int4_t8_l8"], 64, 128))
+        out["decode_stack48"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["stack48_bf16_h2048_e128"],
+                                                        32, 64))
     if not args.no_cpu_baseline:
         cb = cpu_baseline(args, torch, gen, cfg)
         cb["value"] = round(cb["value"], 4)
