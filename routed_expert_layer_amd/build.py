@@ -8,7 +8,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["kernels_route.hip", "kernels_ffn.hip", "kernels_misc.hip", "abi.cpp", "decoder.cpp", "lru_policy.cpp"]
+SOURCES = ["kernels_route.hip", "kernels_ffn.hip", "kernels_gemm.hip", "kernels_misc.hip", "abi.cpp", "decoder.cpp", "lru_policy.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          # packed fp32 instructions are disabled for all device code

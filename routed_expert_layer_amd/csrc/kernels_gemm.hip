@@ -1,0 +1,221 @@
+// Large-tile grouped GEMM for prefill on bf16 matrix cores.
+//
+// Block tile: 256 weight rows (16 fragment rows) x 128 tokens (8 fragment
+// columns of 16 tokens) x 32 K per stage. Eight waves (two per SIMD) in a
+// 4 x 2 grid, each accumulating a 64 x 64 block in 4 x 4 accumulator
+// fragments; per stage a wave reads 4 + 4 one-KiB fragments from LDS for 16
+// matrix-core instructions.
+// Operands go straight from global memory into LDS in fragment order (the
+// direct-to-LDS load of gfx950, one 1 KiB fragment per wave instruction, no
+// register staging), through six LDS stages, so five stages of loads are in
+// flight while one is consumed; one barrier per stage. Weight fragments are contiguous
+// in the expert blob (1 KiB per wave load); token rows are gathered through
+// perm_src (gate/up), read in order (down projection) or taken from x (router).
+// Blocks are grouped into super-tiles of 32 (8 token tiles x 4 weight tiles
+// when the weight tiles allow) that the dispatcher sends to one XCD together.
+#include <cstring>
+
+#include "dev_common.hpp"
+#include "moe_kernels.hpp"
+
+namespace moe {
+namespace {
+
+// Direct global -> LDS load of one 16-byte chunk per lane into the wave's
+// 1 KiB LDS destination `dst` (lane l writes dst + 16 l).
+__device__ __forceinline__ void load_lds16(const void* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+template <int PHASE, int BM_T>
+__global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict__ bsrc,
+                                                    const int32_t* __restrict__ perm_src, const WorkArgs wa,
+                                                    const char* __restrict__ slot_base, size_t slot_stride,
+                                                    size_t mat_off, int N, int K, int H, int I,
+                                                    uint16_t* __restrict__ hout, float* __restrict__ yout,
+                                                    const float* __restrict__ bias) {
+  constexpr int BN_T = 16;
+  constexpr int NS = 6;                        // LDS stages of 32 K; NS - 1 in flight
+  constexpr int WN = BN_T / 4, WM = BM_T / 2;  // fragments per wave: 4 weight rows x WM token columns
+  constexpr int FA = BN_T, FB = BM_T;          // fragments per stage
+  constexpr int FPW = (FA + FB) / 8;           // fragment loads per wave per stage
+  static_assert((FA + FB) % 8 == 0, "stage must split over 8 waves");
+  constexpr int STAGE = (FA + FB) * 1024;
+  __shared__ __attribute__((aligned(1024))) char lds[NS][STAGE];
+
+  // Super-tile schedule: 32 consecutive slots of one XCD (blocks b with the
+  // same b % 8) form a super-tile of GM token tiles x GN weight tiles of one
+  // expert, so the blocks that run together on an XCD share their operands in
+  // its L2 while they advance through K at the same pace.
+  const int NTB = N / (16 * BN_T);
+  const int sidx = (int)((blockIdx.x >> 8) * 8 + (blockIdx.x & 7));  // super-tile
+  const int w = (int)((blockIdx.x >> 3) & 31);                        // slot in it
+  if (sidx >= wa.total_tiles) return;  // padding (uniform per block)
+  int lo = 0, hi = wa.n - 1;           // item with tile_prefix[item] <= sidx < tile_prefix[item + 1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (wa.tile_prefix[mid] <= sidx) lo = mid; else hi = mid - 1;
+  }
+  const int item = lo;
+  const int4 it = wa.item[item];
+  const int GM = it.w & 0xFF, GN = it.w >> 8;  // this expert's super-tile shape
+  if (w >= GM * GN) return;
+  const int ls = sidx - wa.tile_prefix[item];
+  const int ngroups = NTB / GN;
+  const int mt = (ls / ngroups) * GM + w / GN;
+  const int nt = (ls % ngroups) * GN + (w % GN);
+  if (mt * 16 * BM_T >= it.z) return;  // past the expert's last token tile
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wn = wave & 3, wm = wave >> 2;
+  const int KC = K / 32;
+  const int ldb = (PHASE == 2) ? I : H;
+
+  // This wave loads stage fragments f = wave + 8q (q < FPW): weight fragment
+  // row tile f (f < FA) or token column f - FA. Lane addresses without the K
+  // offset; tokens past the group read a valid row (their columns of the
+  // product are never stored).
+  const char* src[FPW];
+  int kstep[FPW];  // bytes per 32-wide K step
+#pragma unroll
+  for (int q = 0; q < FPW; ++q) {
+    const int f = wave + 8 * q;
+    if (f < FA) {
+      src[q] = slot_base + (size_t)it.x * slot_stride + mat_off + (size_t)(nt * BN_T + f) * KC * 1024 + lane * 16;
+      kstep[q] = 1024;
+    } else {
+      int mloc = mt * (16 * BM_T) + (f - FA) * 16 + (lane & 15);
+      if (mloc >= it.z) mloc = it.z - 1;
+      const size_t row = (PHASE == 1) ? (size_t)perm_src[it.y + mloc] : (size_t)(it.y + mloc);
+      src[q] = reinterpret_cast<const char*>(bsrc + row * ldb + (lane >> 4) * 8);
+      kstep[q] = 64;
+    }
+  }
+  auto issue = [&](int kt) {  // stage kt -> LDS buffer kt % NS
+    char* base = lds[kt % NS];
+#pragma unroll
+    for (int q = 0; q < FPW; ++q) load_lds16(src[q] + (size_t)kt * kstep[q], base + (wave + 8 * q) * 1024);
+  };
+
+  f32x4_t acc[WN][WM];
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = 0; s0 < NS - 1 && s0 < KC; ++s0) issue(s0);
+  for (int kt = 0; kt < KC; ++kt) {
+    // stage kt has landed once at most the later stages' loads are pending
+    if (kt + NS - 2 < KC) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FPW * (NS - 2)) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    // every wave's part of stage kt is in LDS, and every wave is done with
+    // stage kt - 1, whose buffer is refilled next
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + NS - 1 < KC) issue(kt + NS - 1);
+    const char* b = lds[kt % NS];
+    u32x4_t fa[WN], fb[WM];
+#pragma unroll
+    for (int i = 0; i < WN; ++i) fa[i] = *reinterpret_cast<const u32x4_t*>(b + (wn * WN + i) * 1024 + lane * 16);
+#pragma unroll
+    for (int j = 0; j < WM; ++j)
+      fb[j] = *reinterpret_cast<const u32x4_t*>(b + (FA + wm * WM + j) * 1024 + lane * 16);
+#pragma unroll
+    for (int i = 0; i < WN; ++i)
+#pragma unroll
+      for (int j = 0; j < WM; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+  }
+
+  // Epilogue.
+#pragma unroll
+  for (int j = 0; j < WM; ++j) {
+    const int mloc = mt * (16 * BM_T) + (wm * WM + j) * 16 + (lane & 15);
+    if (mloc >= it.z) continue;
+    const size_t row = (size_t)(it.y + mloc);
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const int ntile = nt * BN_T + wn * WN + i;
+      const f32x4_t s = acc[i][j];
+      if constexpr (PHASE == 1) {
+        const int i0 = 8 * ntile + 2 * (lane >> 4);
+        const uint32_t packed =
+            (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
+        *reinterpret_cast<uint32_t*>(hout + row * I + i0) = packed;
+      } else if constexpr (PHASE == 2) {
+        *reinterpret_cast<f32x4_t*>(yout + row * H + 16 * ntile + 4 * (lane >> 4)) = s;
+      } else {
+        const int n0 = 16 * ntile + 4 * (lane >> 4);
+        f32x4_t o = s;
+        if (bias) {
+          o[0] += bias[n0];
+          o[1] += bias[n0 + 1];
+          o[2] += bias[n0 + 2];
+          o[3] += bias[n0 + 3];
+        }
+        *reinterpret_cast<f32x4_t*>(yout + row * N + n0) = o;
+      }
+    }
+  }
+}
+
+template <int PHASE, int BM_T>
+hipError_t launch_gemm2(const void* bsrc, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,
+                        size_t slot_stride, size_t mat_off, int N, int K, int H, int I, void* hout, float* yout,
+                        const float* bias, hipStream_t s) {
+  // Per expert, a super-tile is GM token tiles x GN weight tiles (GM*GN <= 32
+  // block slots): GM = the smallest power of two covering its token tiles,
+  // at most 8; GN = the largest power of two dividing the weight tiles that
+  // fits beside it. Super-tiles per expert: ceil(m tiles / GM) x (n tiles / GN).
+  const int NTB = N / 256;
+  int gn_div = 1;
+  while (gn_div < 16 && NTB % (gn_div * 2) == 0) gn_div *= 2;
+  int tot = 0;
+  for (int i = 0; i < wa.n; ++i) {
+    wa.tile_prefix[i] = tot;
+    const int mtiles = (wa.item[i].z + 16 * BM_T - 1) / (16 * BM_T);
+    int GM = 8;
+    while (GM > 1 && GM / 2 >= mtiles) GM /= 2;
+    const int GN = (32 / GM) < gn_div ? 32 / GM : gn_div;
+    wa.item[i].w = GM | (GN << 8);
+    tot += (mtiles + GM - 1) / GM * (NTB / GN);
+  }
+  wa.tile_prefix[wa.n] = tot;
+  wa.total_tiles = tot;
+  if (tot == 0) return hipSuccess;
+  const int blocks = (tot + 7) / 8 * 256;  // 8 XCDs x 32 slots per round of super-tiles
+  hipLaunchKernelGGL((gemm2_bf16<PHASE, BM_T>), dim3(blocks), dim3(512), 0, s, static_cast<const uint16_t*>(bsrc),
+                     perm_src, wa, slot_base, slot_stride, mat_off, N, K, H, I, static_cast<uint16_t*>(hout), yout,
+                     bias);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm2_supported(int N, int K) { return N % 256 == 0 && K % 32 == 0; }
+
+// Both projections of every listed expert, 256 weight rows x 128 tokens per
+// block (the 256-token variant does not fit two waves per SIMD without
+// spilling accumulators).
+hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const WorkArgs& all, const char* slot_base,
+                               size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s) {
+  const BlobLayout L = blob_layout(1, H, I);
+  WorkArgs wa = all;
+  hipError_t e = launch_gemm2<1, 8>(x, perm_src, wa, slot_base, slot_stride, L.p1, 2 * I, H, H, I, hbuf, y, nullptr, s);
+  if (e == hipSuccess)
+    e = launch_gemm2<2, 8>(hbuf, perm_src, wa, slot_base, slot_stride, L.p2, H, I, H, I, hbuf, y, nullptr, s);
+  return e;
+}
+
+hipError_t launch_router_gemm2(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
+                               hipStream_t s) {
+  WorkArgs wa;
+  memset(&wa, 0, sizeof wa);
+  wa.n = 1;
+  wa.item[0] = make_int4(0, 0, T, 0);
+  return launch_gemm2<0, 8>(x, nullptr, wa, static_cast<const char*>(wrt), 0, 0, E, H, H, 0, nullptr, logits, bias,
+                            s);
+}
+
+}  // namespace moe

@@ -97,6 +97,13 @@ bool prefill_supported(int wfmt, int H, int I);
 hipError_t launch_pack_fragments(const void* W, int K, int N, void* dst, hipStream_t s);
 hipError_t launch_router_gemm(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
                               hipStream_t s);
+// Large-tile GEMM (256 weight rows per block) used when N % 256 == 0.
+bool gemm2_supported(int N, int K);
+hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const WorkArgs& all, const char* slot_base,
+                               size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s);
+hipError_t launch_router_gemm2(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
+                               hipStream_t s);
+
 // Sets the calling thread's moe_last_error() message; returns `code`.
 int set_error(int code, const char* fmt, ...);
 
