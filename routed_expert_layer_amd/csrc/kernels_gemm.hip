@@ -1,14 +1,15 @@
 // Large-tile grouped GEMM for prefill on bf16 matrix cores.
 //
-// Block tile: 256 weight rows (16 fragment rows) x 128 tokens (8 fragment
-// columns of 16 tokens) x 32 K per stage. Eight waves (two per SIMD) in a
-// 4 x 2 grid, each accumulating a 64 x 64 block in 4 x 4 accumulator
-// fragments; per stage a wave reads 4 + 4 one-KiB fragments from LDS for 16
-// matrix-core instructions.
+// Block tile: 256 weight rows (16 fragment rows) x 128 or 256 tokens (8 or
+// 16 fragment columns of 16 tokens) x 32 K per stage. Eight waves (two per
+// SIMD), each accumulating 64 x 64 (4 x 4 accumulator fragments, 128-token
+// tile) or 128 x 64 (8 x 4, 256-token tile); per stage a wave reads 8 or 12
+// one-KiB fragments from LDS for 16 or 32 matrix-core instructions.
 // Operands go straight from global memory into LDS in fragment order (the
 // direct-to-LDS load of gfx950, one 1 KiB fragment per wave instruction, no
-// register staging), through six LDS stages, so five stages of loads are in
-// flight while one is consumed; one barrier per stage. Weight fragments are contiguous
+// register staging), through six (128-token tile) or four (256-token tile)
+// LDS stages, all but one in flight while one is consumed; one barrier per
+// stage. Weight fragments are contiguous
 // in the expert blob (1 KiB per wave load); token rows are gathered through
 // perm_src (gate/up), read in order (down projection) or taken from x (router).
 // Blocks are grouped into super-tiles of 32 (8 token tiles x 4 weight tiles
@@ -35,8 +36,11 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
                                                     uint16_t* __restrict__ hout, float* __restrict__ yout,
                                                     const float* __restrict__ bias) {
   constexpr int BN_T = 16;
-  constexpr int NS = 6;                        // LDS stages of 32 K; NS - 1 in flight
-  constexpr int WN = BN_T / 4, WM = BM_T / 2;  // fragments per wave: 4 weight rows x WM token columns
+  constexpr int NS = BM_T == 16 ? 4 : 6;       // LDS stages of 32 K; NS - 1 in flight
+  constexpr int WN = BM_T == 16 ? 8 : 4;       // weight fragment rows per wave
+  constexpr int WM = 4;                        // token fragment columns per wave
+  constexpr int WAVES_N = BN_T / WN;           // wave grid: WAVES_N x (BM_T / WM) = 8 waves
+  static_assert(WAVES_N * (BM_T / WM) == 8, "eight waves");
   constexpr int FA = BN_T, FB = BM_T;          // fragments per stage
   constexpr int FPW = (FA + FB) / 8;           // fragment loads per wave per stage
   static_assert((FA + FB) % 8 == 0, "stage must split over 8 waves");
@@ -66,7 +70,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   const int nt = (ls % ngroups) * GN + (w % GN);
   if (mt * 16 * BM_T >= it.z) return;  // past the expert's last token tile
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wn = wave & 3, wm = wave >> 2;
+  const int wn = wave % WAVES_N, wm = wave / WAVES_N;
   const int KC = K / 32;
   const int ldb = (PHASE == 2) ? I : H;
 
@@ -195,16 +199,28 @@ hipError_t launch_gemm2(const void* bsrc, const int32_t* perm_src, WorkArgs& wa,
 
 bool gemm2_supported(int N, int K) { return N % 256 == 0 && K % 32 == 0; }
 
-// Both projections of every listed expert, 256 weight rows x 128 tokens per
-// block (the 256-token variant does not fit two waves per SIMD without
-// spilling accumulators).
+// Both projections of every listed expert: groups of more than 256 rows run
+// with 256-token tiles (8 waves of 128 x 64), the others with 128-token tiles
+// (8 waves of 64 x 64).
 hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const WorkArgs& all, const char* slot_base,
                                size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s) {
   const BlobLayout L = blob_layout(1, H, I);
-  WorkArgs wa = all;
-  hipError_t e = launch_gemm2<1, 8>(x, perm_src, wa, slot_base, slot_stride, L.p1, 2 * I, H, H, I, hbuf, y, nullptr, s);
-  if (e == hipSuccess)
-    e = launch_gemm2<2, 8>(hbuf, perm_src, wa, slot_base, slot_stride, L.p2, H, I, H, I, hbuf, y, nullptr, s);
+  WorkArgs big, small;
+  memset(&big, 0, sizeof big);
+  memset(&small, 0, sizeof small);
+  for (int i = 0; i < all.n; ++i) {
+    WorkArgs& w = all.item[i].z > 256 ? big : small;
+    w.item[w.n++] = all.item[i];
+  }
+  hipError_t e = hipSuccess;
+  if (big.n && e == hipSuccess)
+    e = launch_gemm2<1, 16>(x, perm_src, big, slot_base, slot_stride, L.p1, 2 * I, H, H, I, hbuf, y, nullptr, s);
+  if (small.n && e == hipSuccess)
+    e = launch_gemm2<1, 8>(x, perm_src, small, slot_base, slot_stride, L.p1, 2 * I, H, H, I, hbuf, y, nullptr, s);
+  if (big.n && e == hipSuccess)
+    e = launch_gemm2<2, 16>(hbuf, perm_src, big, slot_base, slot_stride, L.p2, H, I, H, I, hbuf, y, nullptr, s);
+  if (small.n && e == hipSuccess)
+    e = launch_gemm2<2, 8>(hbuf, perm_src, small, slot_base, slot_stride, L.p2, H, I, H, I, hbuf, y, nullptr, s);
   return e;
 }
 
@@ -214,8 +230,8 @@ hipError_t launch_router_gemm2(const void* x, const void* wrt, const float* bias
   memset(&wa, 0, sizeof wa);
   wa.n = 1;
   wa.item[0] = make_int4(0, 0, T, 0);
-  return launch_gemm2<0, 8>(x, nullptr, wa, static_cast<const char*>(wrt), 0, 0, E, H, H, 0, nullptr, logits, bias,
-                            s);
+  return launch_gemm2<0, 16>(x, nullptr, wa, static_cast<const char*>(wrt), 0, 0, E, H, H, 0, nullptr, logits, bias,
+                             s);
 }
 
 }  // namespace moe
