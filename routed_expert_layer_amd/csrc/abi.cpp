@@ -290,9 +290,11 @@ int cache_fill_async(moe_cache_t* c, const moe_miss_t* misses, int n, const void
 // ---------------------------------------------------------------------------
 size_t moe_ffn_workspace_size(int rows_total, int H, int I, int wfmt) {
   if (rows_total < 0 || !shape_ok(wfmt, H, I)) return 0;
-  const size_t hb = moe::align_up((size_t)rows_total * I * (wfmt == MOE_W_F32 ? 4 : 2), 256);
+  // h: one row of I per routed row, plus one 16-row tile of slack for the
+  // prefill GEMM's tiled h layout
+  const size_t hb = moe::align_up((size_t)(rows_total + 16) * I * (wfmt == MOE_W_F32 ? 4 : 2), 256);
   const size_t xg = (wfmt == MOE_W_INT4) ? moe::align_up((size_t)rows_total * H * 2, 256) : 0;
-  return hb + xg + 256;
+  return hb + xg + 4 * moe::kTableBytes + 256;
 }
 
 int moe_ffn(const void* x, int dtype, const int32_t* perm_src, const moe_work_t* work, int n_work,
@@ -327,8 +329,23 @@ int moe_ffn(const void* x, int dtype, const int32_t* perm_src, const moe_work_t*
   }
   char* ws = static_cast<char*>(workspace);
   void* hbuf = ws;
-  void* xg = ws + moe::align_up((size_t)rows_total * I * (wfmt == MOE_W_F32 ? 4 : 2), 256);
+  void* xg = ws + moe::align_up((size_t)(rows_total + 16) * I * (wfmt == MOE_W_F32 ? 4 : 2), 256);
+  void* tables = static_cast<char*>(xg) + (wfmt == MOE_W_INT4 ? moe::align_up((size_t)rows_total * H * 2, 256) : 0);
   hipStream_t s = as_stream(stream);
+  if (prefill && moe::gemm2_supported(2 * I, H) && moe::gemm2_supported(H, I)) {
+    // large-tile GEMM: the whole work list per launch, from a device table
+    std::vector<int4> items;
+    items.reserve(n_work);
+    for (int i = 0; i < n_work; ++i)
+      if (work[i].rows > 0) items.push_back(make_int4(work[i].slot, work[i].row_begin, work[i].rows, work[i].expert));
+    for (size_t base = 0; base < items.size(); base += moe::kTableItems) {
+      const int n = (int)std::min(items.size() - base, (size_t)moe::kTableItems);
+      hipError_t e = moe::launch_ffn_prefill2(x, perm_src, items.data() + base, n, static_cast<const char*>(slot_base),
+                                              slot_stride, H, I, hbuf, y_perm, tables, s);
+      if (e != hipSuccess) return hip_fail(e, "moe_ffn launch");
+    }
+    return MOE_OK;
+  }
   moe::WorkArgs wa;
   for (int base = 0; base < n_work; base += moe::kMaxItems) {
     std::memset(&wa, 0, sizeof wa);

@@ -442,8 +442,6 @@ hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, c
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,
                               size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s) {
   if (wa.n == 0) return hipSuccess;
-  if (gemm2_supported(2 * I, H) && gemm2_supported(H, I))
-    return launch_ffn_prefill2(x, perm_src, wa, slot_base, slot_stride, H, I, hbuf, y, s);
   const BlobLayout L = blob_layout(1, H, I);
   int tot = 0;
   for (int i = 0; i < wa.n; ++i) {

@@ -14,7 +14,9 @@
 // perm_src (gate/up), read in order (down projection) or taken from x (router).
 // Blocks are grouped into super-tiles of 32 (8 token tiles x 4 weight tiles
 // when the weight tiles allow) that the dispatcher sends to one XCD together.
+#include <algorithm>
 #include <cstring>
+#include <vector>
 
 #include "dev_common.hpp"
 #include "moe_kernels.hpp"
@@ -28,22 +30,27 @@ __device__ __forceinline__ void load_lds16(const void* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
 
-template <int PHASE, int BM_T>
+// The work list comes by value (WorkArgs) or from device memory (GemmTable);
+// both have the same fields.
+__device__ inline const WorkArgs& table_of(const WorkArgs& w) { return w; }
+__device__ inline const GemmTable& table_of(const GemmTable* t) { return *t; }
+
+template <int PHASE, int BM_T, typename Tab>
 __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict__ bsrc,
-                                                    const int32_t* __restrict__ perm_src, const WorkArgs wa,
-                                                    const char* __restrict__ slot_base, size_t slot_stride,
-                                                    size_t mat_off, int N, int K, int H, int I,
-                                                    uint16_t* __restrict__ hout, float* __restrict__ yout,
-                                                    const float* __restrict__ bias) {
+                                                        const int32_t* __restrict__ perm_src, const Tab tab,
+                                                        const char* __restrict__ slot_base, size_t slot_stride,
+                                                        size_t mat_off, int N, int K, int H, int I,
+                                                        uint16_t* __restrict__ hout, float* __restrict__ yout,
+                                                        const float* __restrict__ bias) {
   constexpr int BN_T = 16;
   constexpr int NS = BM_T == 16 ? 4 : 6;       // LDS stages of 32 K; NS - 1 in flight
   constexpr int WN = BM_T == 16 ? 8 : 4;       // weight fragment rows per wave
   constexpr int WM = 4;                        // token fragment columns per wave
   constexpr int WAVES_N = BN_T / WN;           // wave grid: WAVES_N x (BM_T / WM) = 8 waves
-  static_assert(WAVES_N * (BM_T / WM) == 8, "eight waves");
+  static_assert(WAVES_N * (BM_T / WM) == 8, "wave grid");
   constexpr int FA = BN_T, FB = BM_T;          // fragments per stage
   constexpr int FPW = (FA + FB) / 8;           // fragment loads per wave per stage
-  static_assert((FA + FB) % 8 == 0, "stage must split over 8 waves");
+  static_assert((FA + FB) % 8 == 0, "stage must split over the waves");
   constexpr int STAGE = (FA + FB) * 1024;
   __shared__ __attribute__((aligned(1024))) char lds[NS][STAGE];
 
@@ -51,6 +58,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   // same b % 8) form a super-tile of GM token tiles x GN weight tiles of one
   // expert, so the blocks that run together on an XCD share their operands in
   // its L2 while they advance through K at the same pace.
+  const auto& wa = table_of(tab);
   const int NTB = N / (16 * BN_T);
   const int sidx = (int)((blockIdx.x >> 8) * 8 + (blockIdx.x & 7));  // super-tile
   const int w = (int)((blockIdx.x >> 3) & 31);                        // slot in it
@@ -73,6 +81,9 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   const int wn = wave % WAVES_N, wm = wave / WAVES_N;
   const int KC = K / 32;
   const int ldb = (PHASE == 2) ? I : H;
+  // Waves whose token columns all lie past the group skip the matrix-core
+  // work (they still load their share of every stage).
+  const bool active = mt * (16 * BM_T) + wm * WM * 16 < it.z;
 
   // This wave loads stage fragments f = wave + 8q (q < FPW): weight fragment
   // row tile f (f < FA) or token column f - FA. Lane addresses without the K
@@ -89,9 +100,16 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
     } else {
       int mloc = mt * (16 * BM_T) + (f - FA) * 16 + (lane & 15);
       if (mloc >= it.z) mloc = it.z - 1;
-      const size_t row = (PHASE == 1) ? (size_t)perm_src[it.y + mloc] : (size_t)(it.y + mloc);
-      src[q] = reinterpret_cast<const char*>(bsrc + row * ldb + (lane >> 4) * 8);
-      kstep[q] = 64;
+      if constexpr (PHASE == 2) {
+        // h in fragment order: row r, 32-wide K chunk c at ((r/16) * KC + c) KiB
+        const size_t row = (size_t)(it.y + mloc);
+        src[q] = reinterpret_cast<const char*>(bsrc) + (row >> 4) * KC * 1024 + ((row & 15) + 16 * (lane >> 4)) * 16;
+        kstep[q] = 1024;
+      } else {
+        const size_t row = (PHASE == 1) ? (size_t)perm_src[it.y + mloc] : (size_t)(it.y + mloc);
+        src[q] = reinterpret_cast<const char*>(bsrc + row * ldb + (lane >> 4) * 8);
+        kstep[q] = 64;
+      }
     }
   }
   auto issue = [&](int kt) {  // stage kt -> LDS buffer kt % NS
@@ -106,30 +124,50 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < WM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int s0 = 0; s0 < NS - 1 && s0 < KC; ++s0) issue(s0);
-  for (int kt = 0; kt < KC; ++kt) {
-    // stage kt has landed once at most the later stages' loads are pending
-    if (kt + NS - 2 < KC) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FPW * (NS - 2)) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    // every wave's part of stage kt is in LDS, and every wave is done with
-    // stage kt - 1, whose buffer is refilled next
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + NS - 1 < KC) issue(kt + NS - 1);
+  struct Frags {
+    u32x4_t a[WN], b[WM];
+  };
+  auto read_stage = [&](int kt, Frags& f) {
     const char* b = lds[kt % NS];
-    u32x4_t fa[WN], fb[WM];
-#pragma unroll
-    for (int i = 0; i < WN; ++i) fa[i] = *reinterpret_cast<const u32x4_t*>(b + (wn * WN + i) * 1024 + lane * 16);
 #pragma unroll
     for (int j = 0; j < WM; ++j)
-      fb[j] = *reinterpret_cast<const u32x4_t*>(b + (FA + wm * WM + j) * 1024 + lane * 16);
+      f.b[j] = *reinterpret_cast<const u32x4_t*>(b + (FA + wm * WM + j) * 1024 + lane * 16);
 #pragma unroll
-    for (int i = 0; i < WN; ++i)
+    for (int i = 0; i < WN; ++i) f.a[i] = *reinterpret_cast<const u32x4_t*>(b + (wn * WN + i) * 1024 + lane * 16);
+  };
+  auto compute = [&](const Frags& f) {
+    if (active) {
 #pragma unroll
-      for (int j = 0; j < WM; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+      for (int i = 0; i < WN; ++i)
+#pragma unroll
+        for (int j = 0; j < WM; ++j) acc[i][j] = mfma_bf16(f.a[i], f.b[j], acc[i][j]);
+    }
+  };
+
+  {
+    // Two waves per SIMD: while one wave waits for its LDS reads the other
+    // runs matrix-core work; one stage at a time.
+    for (int s0 = 0; s0 < NS - 1 && s0 < KC; ++s0) issue(s0);
+    for (int kt = 0; kt < KC; ++kt) {
+      // stage kt has landed once at most the later stages' loads are pending
+      if (kt + NS - 2 < KC) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FPW * (NS - 2)) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      // every wave's part of stage kt is in LDS, and every wave is done with
+      // stage kt - 1, whose buffer is refilled next
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + NS - 1 < KC) issue(kt + NS - 1);
+      Frags f;
+      read_stage(kt, f);
+      // the wave with matrix-core work issues first; the other wave's loads
+      // and LDS reads fill the gaps
+      __builtin_amdgcn_s_setprio(1);
+      compute(f);
+      __builtin_amdgcn_s_setprio(0);
+    }
   }
 
   // Epilogue.
@@ -143,10 +181,15 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
       const int ntile = nt * BN_T + wn * WN + i;
       const f32x4_t s = acc[i][j];
       if constexpr (PHASE == 1) {
+        // h is stored in the down projection's token-fragment order: row r,
+        // columns 32c + 8g .. +7 at element ((r/16) * (I/32) + c) * 512 +
+        // ((r % 16) + 16 g) * 8.
         const int i0 = 8 * ntile + 2 * (lane >> 4);
         const uint32_t packed =
             (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
-        *reinterpret_cast<uint32_t*>(hout + row * I + i0) = packed;
+        const size_t off = ((row >> 4) * (size_t)(I / 32) + (i0 >> 5)) * 512 + ((row & 15) + 16 * ((i0 & 31) >> 3)) * 8 +
+                           (i0 & 7);
+        *reinterpret_cast<uint32_t*>(hout + off) = packed;
       } else if constexpr (PHASE == 2) {
         *reinterpret_cast<f32x4_t*>(yout + row * H + 16 * ntile + 4 * (lane >> 4)) = s;
       } else {
@@ -164,64 +207,119 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   }
 }
 
-template <int PHASE, int BM_T>
-hipError_t launch_gemm2(const void* bsrc, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,
-                        size_t slot_stride, size_t mat_off, int N, int K, int H, int I, void* hout, float* yout,
-                        const float* bias, hipStream_t s) {
-  // Per expert, a super-tile is GM token tiles x GN weight tiles (GM*GN <= 32
-  // block slots): GM = the smallest power of two covering its token tiles,
-  // at most 8; GN = the largest power of two dividing the weight tiles that
-  // fits beside it. Super-tiles per expert: ceil(m tiles / GM) x (n tiles / GN).
+// Per expert, a super-tile is GM token tiles x GN weight tiles (GM*GN <= 32
+// block slots): GM = the smallest power of two covering its token tiles, at
+// most 8; GN = the largest power of two dividing the weight tiles that fits
+// beside it. Super-tiles per expert: ceil(m tiles / GM) x (n tiles / GN).
+// Fills item[i].w with GM | GN << 8 and tile_prefix; returns the total.
+int plan_supertiles(int4* item, int n, int* tile_prefix, int N, int tile_tokens) {
   const int NTB = N / 256;
   int gn_div = 1;
   while (gn_div < 16 && NTB % (gn_div * 2) == 0) gn_div *= 2;
   int tot = 0;
-  for (int i = 0; i < wa.n; ++i) {
-    wa.tile_prefix[i] = tot;
-    const int mtiles = (wa.item[i].z + 16 * BM_T - 1) / (16 * BM_T);
+  for (int i = 0; i < n; ++i) {
+    tile_prefix[i] = tot;
+    const int mtiles = (item[i].z + tile_tokens - 1) / tile_tokens;
     int GM = 8;
     while (GM > 1 && GM / 2 >= mtiles) GM /= 2;
     const int GN = (32 / GM) < gn_div ? 32 / GM : gn_div;
-    wa.item[i].w = GM | (GN << 8);
+    item[i].w = GM | (GN << 8);
     tot += (mtiles + GM - 1) / GM * (NTB / GN);
   }
-  wa.tile_prefix[wa.n] = tot;
-  wa.total_tiles = tot;
-  if (tot == 0) return hipSuccess;
-  const int blocks = (tot + 7) / 8 * 256;  // 8 XCDs x 32 slots per round of super-tiles
-  hipLaunchKernelGGL((gemm2_bf16<PHASE, BM_T>), dim3(blocks), dim3(512), 0, s, static_cast<const uint16_t*>(bsrc),
-                     perm_src, wa, slot_base, slot_stride, mat_off, N, K, H, I, static_cast<uint16_t*>(hout), yout,
-                     bias);
-  return hipGetLastError();
+  tile_prefix[n] = tot;
+  return tot;
+}
+
+inline int supertile_blocks(int tot) { return (tot + 7) / 8 * 256; }  // 8 XCDs x 32 slots per round
+
+// Up to 64 table entries per upload launch.
+struct TableChunk {
+  int base, count, n, total;
+  int prefix[64];
+  int4 item[64];
+};
+
+__global__ __launch_bounds__(64) void table_upload(const TableChunk c, GemmTable* __restrict__ t) {
+  const int i = threadIdx.x;
+  if (i < c.count) {
+    t->item[c.base + i] = c.item[i];
+    t->tile_prefix[c.base + i] = c.prefix[i];
+  }
+  if (i == 0 && c.base + c.count == c.n) t->tile_prefix[c.n] = c.total;
+  if (i == 0 && c.base == 0) {
+    t->n = c.n;
+    t->total_tiles = c.total;
+  }
+}
+
+hipError_t upload_table(const int4* item, const int* prefix, int n, int total, GemmTable* dst, hipStream_t s) {
+  TableChunk c;
+  for (int base = 0; base < n; base += 64) {
+    memset(&c, 0, sizeof c);
+    c.base = base;
+    c.count = n - base < 64 ? n - base : 64;
+    c.n = n;
+    c.total = total;
+    for (int i = 0; i < c.count; ++i) {
+      c.item[i] = item[base + i];
+      c.prefix[i] = prefix[base + i];
+    }
+    hipLaunchKernelGGL(table_upload, dim3(1), dim3(64), 0, s, c, dst);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
 bool gemm2_supported(int N, int K) { return N % 256 == 0 && K % 32 == 0; }
 
-// Both projections of every listed expert: groups of more than 256 rows run
-// with 256-token tiles (8 waves of 128 x 64), the others with 128-token tiles
-// (8 waves of 64 x 64).
-hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const WorkArgs& all, const char* slot_base,
-                               size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s) {
+// Both projections of every listed expert: groups of more than 256 rows with
+// 256-token tiles (8 waves of 128 x 64), the others with 128-token tiles
+// (8 waves of 64 x 64); one launch per tile size and projection, each with
+// its whole work list in a device table.
+hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const int4* items, int n,
+                               const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
+                               void* tables, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n > kTableItems) return hipErrorInvalidValue;
   const BlobLayout L = blob_layout(1, H, I);
-  WorkArgs big, small;
-  memset(&big, 0, sizeof big);
-  memset(&small, 0, sizeof small);
-  for (int i = 0; i < all.n; ++i) {
-    WorkArgs& w = all.item[i].z > 256 ? big : small;
-    w.item[w.n++] = all.item[i];
+  std::vector<int4> part[2];  // [0] groups of more than 256 rows, [1] the rest
+  for (int i = 0; i < n; ++i) part[items[i].z > 256 ? 0 : 1].push_back(items[i]);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  uint16_t* hb = static_cast<uint16_t*>(hbuf);
+  GemmTable* tab[2][2];  // [part][projection]
+  int tot[2][2] = {{0, 0}, {0, 0}};
+  for (int p = 0; p < 2; ++p) {
+    for (int ph = 0; ph < 2; ++ph) {
+      tab[p][ph] = reinterpret_cast<GemmTable*>(static_cast<char*>(tables) + (2 * p + ph) * kTableBytes);
+      const int m = (int)part[p].size();
+      if (m == 0) continue;
+      std::vector<int4> it(part[p]);
+      std::vector<int> pre(m + 1);
+      tot[p][ph] = plan_supertiles(it.data(), m, pre.data(), ph == 0 ? 2 * I : H, p == 0 ? 256 : 128);
+      hipError_t e = upload_table(it.data(), pre.data(), m, tot[p][ph], tab[p][ph], s);
+      if (e != hipSuccess) return e;
+    }
   }
-  hipError_t e = hipSuccess;
-  if (big.n && e == hipSuccess)
-    e = launch_gemm2<1, 16>(x, perm_src, big, slot_base, slot_stride, L.p1, 2 * I, H, H, I, hbuf, y, nullptr, s);
-  if (small.n && e == hipSuccess)
-    e = launch_gemm2<1, 8>(x, perm_src, small, slot_base, slot_stride, L.p1, 2 * I, H, H, I, hbuf, y, nullptr, s);
-  if (big.n && e == hipSuccess)
-    e = launch_gemm2<2, 16>(hbuf, perm_src, big, slot_base, slot_stride, L.p2, H, I, H, I, hbuf, y, nullptr, s);
-  if (small.n && e == hipSuccess)
-    e = launch_gemm2<2, 8>(hbuf, perm_src, small, slot_base, slot_stride, L.p2, H, I, H, I, hbuf, y, nullptr, s);
-  return e;
+  if (tot[0][0] > 0)
+    hipLaunchKernelGGL((gemm2_bf16<1, 16, const GemmTable*>), dim3(supertile_blocks(tot[0][0])), dim3(512), 0, s, xb,
+                       perm_src, (const GemmTable*)tab[0][0], slot_base, slot_stride, L.p1, 2 * I, H, H, I, hb, y,
+                       nullptr);
+  if (tot[1][0] > 0)
+    hipLaunchKernelGGL((gemm2_bf16<1, 8, const GemmTable*>), dim3(supertile_blocks(tot[1][0])), dim3(512), 0, s, xb,
+                       perm_src, (const GemmTable*)tab[1][0], slot_base, slot_stride, L.p1, 2 * I, H, H, I, hb, y,
+                       nullptr);
+  if (tot[0][1] > 0)
+    hipLaunchKernelGGL((gemm2_bf16<2, 16, const GemmTable*>), dim3(supertile_blocks(tot[0][1])), dim3(512), 0, s, hb,
+                       perm_src, (const GemmTable*)tab[0][1], slot_base, slot_stride, L.p2, H, I, H, I, hb, y,
+                       nullptr);
+  if (tot[1][1] > 0)
+    hipLaunchKernelGGL((gemm2_bf16<2, 8, const GemmTable*>), dim3(supertile_blocks(tot[1][1])), dim3(512), 0, s, hb,
+                       perm_src, (const GemmTable*)tab[1][1], slot_base, slot_stride, L.p2, H, I, H, I, hb, y,
+                       nullptr);
+  return hipGetLastError();
 }
 
 hipError_t launch_router_gemm2(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
@@ -230,8 +328,12 @@ hipError_t launch_router_gemm2(const void* x, const void* wrt, const float* bias
   memset(&wa, 0, sizeof wa);
   wa.n = 1;
   wa.item[0] = make_int4(0, 0, T, 0);
-  return launch_gemm2<0, 16>(x, nullptr, wa, static_cast<const char*>(wrt), 0, 0, E, H, H, 0, nullptr, logits, bias,
-                             s);
+  wa.total_tiles = plan_supertiles(wa.item, 1, wa.tile_prefix, E, 256);
+  if (wa.total_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm2_bf16<0, 16, WorkArgs>), dim3(supertile_blocks(wa.total_tiles)), dim3(512), 0, s,
+                     static_cast<const uint16_t*>(x), nullptr, wa, static_cast<const char*>(wrt), 0, 0, E, H, H, 0,
+                     nullptr, logits, bias);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -69,6 +69,18 @@ struct WorkArgs {
   int4 item[kMaxItems];            // {slot, row_begin, rows, expert}
 };
 
+// Work list of one prefill GEMM launch, in device memory (written by a small
+// upload kernel), so one launch covers every expert of a layer.
+constexpr int kTableItems = 1024;
+struct GemmTable {
+  int n;
+  int total_tiles;
+  int pad_[2];
+  int tile_prefix[kTableItems + 1];  // super-tile prefix sums
+  int4 item[kTableItems];            // {slot, row_begin, rows, GM | GN << 8}
+};
+constexpr size_t kTableBytes = (sizeof(GemmTable) + 255) / 256 * 256;
+
 // ---------------------------------------------------------------------------
 // Launchers (return hipError_t of the launch).
 // ---------------------------------------------------------------------------
@@ -88,6 +100,7 @@ hipError_t launch_combine(const float* y_perm, const int32_t* perm_pos, const fl
 hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, const WorkArgs& wa,
                              const char* slot_base, size_t slot_stride, int H, int I,
                              void* hbuf, void* xg, float* y, hipStream_t s);
+// 128 x 128-tile fallback GEMM for shapes the large-tile GEMM does not take.
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,
                               size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s);
 bool prefill_supported(int wfmt, int H, int I);
@@ -99,8 +112,12 @@ hipError_t launch_router_gemm(const void* x, const void* wrt, const float* bias,
                               hipStream_t s);
 // Large-tile GEMM (256 weight rows per block) used when N % 256 == 0.
 bool gemm2_supported(int N, int K);
-hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const WorkArgs& all, const char* slot_base,
-                               size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s);
+// Both projections of n work items {slot, row_begin, rows, expert} (host
+// array, rows > 0, n <= kTableItems) with four GemmTables at `tables`
+// (4 * kTableBytes of device memory, stream-ordered reuse).
+hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const int4* items, int n,
+                               const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
+                               void* tables, hipStream_t s);
 hipError_t launch_router_gemm2(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
                                hipStream_t s);
 

@@ -118,7 +118,7 @@ FFN_CASES = [
     ("f32_tiny", "f32", 256, 128, [3, 0, 1, 8, 2], "auto"),
     ("bf16_decode", "bf16", 512, 256, [1, 0, 6, 16, 17, 2, 33], "decode"),
     ("bf16_decode_k_odd", "bf16", 384, 160, [5, 1, 0, 9], "decode"),
-    ("bf16_prefill", "bf16", 512, 256, [130, 0, 1, 127, 128, 300, 17], "prefill"),
+    ("bf16_prefill", "bf16", 512, 256, [130, 0, 1, 127, 128, 300, 17, 777], "prefill"),
     ("bf16_prefill_c3shape", "bf16", 2048, 768, [70, 3, 129], "prefill"),
     ("int4_decode", "int4", 512, 256, [1, 8, 0, 3, 20], "decode"),
     ("int4_decode_wide", "int4", 1024, 384, [2, 16, 5], "decode"),
