@@ -102,7 +102,7 @@ def bench_decode(args, torch, L, gen, cfg):
         dl.step(step, 0, xs[step], Wr, bias(step), s)
     torch.cuda.synchronize()
     fills0 = dl.n_fills
-    L.moe_decoder_profile(dl.dec, True)  # HIP events around every expert-FFN call, on stream s
+    L.moe_decoder_profile(dl.dec, 8)  # HIP events around every 8th expert-FFN call, on stream s
     lat = []
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -257,7 +257,7 @@ def bench_decode_layers(args, torch, L, gen, cfg, warm, steps):
                 dl.step(st, l, xs[st][l], Wrs[l], b(l, st), s)
         torch.cuda.synchronize()
         f0 = dl.n_fills
-        L.moe_decoder_profile(dl.dec, True)
+        L.moe_decoder_profile(dl.dec, 8)
         t0 = time.perf_counter()
         for st in range(warm, n):
             for l in range(cfg.L):

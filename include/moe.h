@@ -295,10 +295,12 @@ int moe_pipe_copy_ms(moe_pipe_t* pipe, int layer, float* ms);
  *   out_dtype; *n_miss (nullable) = fills issued. Blocks the calling thread
  *   until the counts reach the host; the rest is enqueued on `stream`.
  *   On a failed fill the affected keys are invalidated (never half-resident).
- * moe_decoder_profile: when enabled, every FFN call is bracketed by HIP events
- *   on `stream`; moe_decoder_ffn_stats returns the summed algorithmic bytes
- *   (expert blobs read + activations read/written), summed milliseconds and
- *   the number of FFN calls since profiling was enabled.
+ * moe_decoder_profile: every > 0 brackets every every-th FFN call (the first,
+ *   then each every-th after it) with HIP events on `stream`; 0 turns it off;
+ *   negative is EINVAL. moe_decoder_ffn_stats returns, over the bracketed
+ *   calls since profiling was last set, the summed algorithmic bytes (expert
+ *   blobs read + activations read/written), the summed milliseconds and the
+ *   number of bracketed calls.
  * moe_decoder_fills: total fills issued by this decoder.
  * ------------------------------------------------------------------------ */
 typedef struct moe_decoder moe_decoder_t;
@@ -324,7 +326,7 @@ moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, i
 int moe_decoder_destroy(moe_decoder_t* decoder);
 int moe_decoder_step(moe_decoder_t* decoder, int step, int layer, const void* x, int T, const void* Wr,
                      const float* bias, void* out, int out_dtype, void* stream, int* n_miss);
-int moe_decoder_profile(moe_decoder_t* decoder, int enable);
+int moe_decoder_profile(moe_decoder_t* decoder, int every);
 int moe_decoder_ffn_stats(moe_decoder_t* decoder, double* bytes, double* ms, int64_t* launches);
 int moe_decoder_fills(const moe_decoder_t* decoder, int64_t* fills);
 

@@ -183,7 +183,7 @@ class MoeCache:
         self.L, self.E, self.S = L, E, S
 
     def close(self):
-        if self.h:
+        if self.h and _lib is not None:  # module globals may be gone at interpreter exit
             _lib.moe_cache_destroy(self.h)
             self.h = None
 
@@ -287,7 +287,7 @@ class MoePipe:
             raise MoEError(st.value, _lib.moe_last_error().decode())
 
     def close(self):
-        if self.h:
+        if self.h and _lib is not None:  # module globals may be gone at interpreter exit
             _lib.moe_pipe_destroy(self.h)
             self.h = None
 
@@ -338,7 +338,7 @@ class MoeDecoder:
         self.cache = cache
 
     def close(self):
-        if self.h:
+        if self.h and _lib is not None:  # module globals may be gone at interpreter exit
             _lib.moe_decoder_destroy(self.h)
             self.h = None
 
@@ -360,8 +360,9 @@ def moe_decoder_step(dec, step, layer, x, Wr, bias, out, stream=None):
     return nm.value
 
 
-def moe_decoder_profile(dec, enable):
-    _check(_lib.moe_decoder_profile(dec.h, 1 if enable else 0), "moe_decoder_profile")
+def moe_decoder_profile(dec, every):
+    """every: bracket every every-th FFN call with HIP events (True = 1, False/0 = off)."""
+    _check(_lib.moe_decoder_profile(dec.h, int(every)), "moe_decoder_profile")
 
 
 def moe_decoder_ffn_stats(dec):

@@ -43,7 +43,8 @@ struct moe_decoder {
   std::vector<moe_miss_t> misses, wave_misses;
   std::vector<moe_work_t> work;
   std::vector<int32_t> offs;
-  bool prof = false;
+  int prof_every = 0;     // bracket every prof_every-th FFN call with events (0: off)
+  int64_t prof_calls = 0;  // FFN calls since profiling was enabled
   std::vector<hipEvent_t> ev_begin, ev_end;
   std::vector<double> ev_bytes;
   size_t ev_used = 0;
@@ -204,12 +205,13 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
       d->work.push_back(moe_work_t{ex, d->work_slot[i], d->offs[ex], d->counts_host[ex]});
       rows += d->counts_host[ex];
     }
-    if (d->prof && record_ffn_event(d, true, s, 0) != MOE_OK)
+    const bool prof = d->prof_every > 0 && d->prof_calls++ % d->prof_every == 0;
+    if (prof && record_ffn_event(d, true, s, 0) != MOE_OK)
       return dfail(MOE_EHIP, "moe_decoder_step: profiling event");
     rc = moe_ffn(x, d->dtype, b.perm_src, d->work.data(), (int)d->work.size(), d->slot_base, d->slot_stride, d->wfmt,
                  d->H, d->I, b.y_perm, b.ffn_ws, b.ffn_ws_bytes, MOE_FFN_AUTO, stream);
     if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
-    if (d->prof) {
+    if (prof) {
       const double a = d->dtype == MOE_DT_BF16 ? 2.0 : 4.0, h = d->wfmt == MOE_W_F32 ? 4.0 : 2.0;
       const double bytes = (double)d->work.size() * (double)d->blob_bytes +
                            (double)rows * (d->H * a + 2.0 * d->I * h + d->H * 4.0);
@@ -222,9 +224,10 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   return MOE_OK;
 }
 
-int moe_decoder_profile(moe_decoder_t* d, int enable) {
-  if (!d) return dfail(MOE_EINVAL, "moe_decoder_profile: null decoder");
-  d->prof = enable != 0;
+int moe_decoder_profile(moe_decoder_t* d, int every) {
+  if (!d || every < 0) return dfail(MOE_EINVAL, "moe_decoder_profile: null decoder or negative period");
+  d->prof_every = every;
+  d->prof_calls = 0;
   d->ev_used = 0;
   return MOE_OK;
 }

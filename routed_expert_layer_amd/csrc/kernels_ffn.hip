@@ -153,7 +153,6 @@ __global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restri
 // int4 decode kernels (x and the SwiGLU product in fp16, codes exact in fp16,
 // one fp16 scale per 128-row block applied to that block's partial sum).
 // ---------------------------------------------------------------------------
-constexpr int kUG = 2;  // 128-row blocks in flight per wave
 
 // Gathered activations, converted to fp16: xg[r, :] = fp16(x[perm_src[r], :]).
 __global__ __launch_bounds__(256) void gather_f16_kernel(const uint16_t* __restrict__ x,
@@ -174,17 +173,17 @@ __global__ __launch_bounds__(256) void gather_f16_kernel(const uint16_t* __restr
   }
 }
 
-__device__ __forceinline__ void int4_block(const char* qp, const char* sp, const uint16_t* br, bool valid,
-                                           f32x4_t& acc) {
+// One 128-wide K block of one 16-row tile: four fp16 matrix-core products of
+// the dequantised codes with the activation fragments b, scaled by the tile
+// rows' block scales and added to acc.
+__device__ __forceinline__ void int4_tile_block(const char* qp, const char* sp, const u32x4_t (&b)[4],
+                                                f32x4_t& acc) {
   const u32x4_t a = ld16_nt(qp);
   // The four fp16 scales are read as two 32-bit words and widened one by one
   // (a two-element fp16 vector view of the 64-bit load was miscompiled into
   // mixed-precision FMAs that all read the first word).
   const uint32_t sc0 = reinterpret_cast<const uint32_t*>(sp)[0];
   const uint32_t sc1 = reinterpret_cast<const uint32_t*>(sp)[1];
-  u32x4_t b[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) b[j] = valid ? ld16(br + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
   f32x4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) t = mfma_f16(int4x8_to_f16x8(a[j]), b[j], t);
@@ -194,70 +193,77 @@ __device__ __forceinline__ void int4_block(const char* qp, const char* sp, const
   acc[3] = fmaf(t[3], f16_bits_to_f32(sc1 >> 16), acc[3]);
 }
 
-__global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restrict__ xg, const WorkArgs wa,
-                                                        const char* __restrict__ slot_base, size_t slot_stride,
-                                                        size_t p1s_off, int H, int I, uint16_t* __restrict__ hbuf) {
-  const int NT = I / 8;
-  const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
-  const int4 it = wa.item[item];
+// Shared body of both int4 projections. A block owns kR consecutive 16-row
+// tiles of one expert; its four waves split K, and each wave applies every
+// activation fragment it loads to all kR tiles (one activation load per kR
+// KiB of codes). Partial sums meet in LDS; wave w finishes tile w.
+// act: fp16 activations [rows, K] (gathered x or h); the finished 16 x 16
+// tile sums go to `emit(tile, m, sum)`.
+constexpr int kR = 4;
+template <typename Emit>
+__device__ __forceinline__ void int4_decode_tiles(const uint16_t* __restrict__ act, const int4 it, int K,
+                                                  const char* q_base, const char* s_base, int tile0, Emit emit) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int KG = H / 128;
+  const int KG = K / 128;
   const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
-  const char* blob = slot_base + (size_t)it.x * slot_stride;
-  const char* qp = blob + (size_t)tile * KG * 1024 + lane * 16;
-  const char* sp = blob + p1s_off + (size_t)tile * KG * 32 + (lane >> 4) * 8;
   const int kq = (lane >> 4) * 8;
-  __shared__ f32x4_t red[4][64];
+  __shared__ f32x4_t red[4][kR][64];
   for (int m0 = 0; m0 < it.z; m0 += 16) {
     const int m = m0 + (lane & 15);
     const bool valid = m < it.z;
-    const uint16_t* xr = xg + (size_t)(it.y + (valid ? m : 0)) * H + kq;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll kUG
-    for (int g = g0; g < g1; ++g) int4_block(qp + (size_t)g * 1024, sp + (size_t)g * 32, xr + 128 * g, valid, acc);
-    red[wave][lane] = acc;
+    const uint16_t* ar = act + (size_t)(it.y + (valid ? m : 0)) * K + kq;
+    f32x4_t acc[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int g = g0; g < g1; ++g) {
+      u32x4_t b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = valid ? ld16(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int r = 0; r < kR; ++r)
+        int4_tile_block(q_base + ((size_t)(tile0 + r) * KG + g) * 1024 + lane * 16,
+                        s_base + ((size_t)(tile0 + r) * KG + g) * 32 + (lane >> 4) * 8, b, acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) red[wave][r][lane] = acc[r];
     __syncthreads();
-    if (wave == 0 && valid) {
-      const f32x4_t s = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-      const int i0 = 8 * tile + 2 * (lane >> 4);
-      const uint32_t packed =
-          (uint32_t)f32_to_f16_bits(silu(s[0]) * s[1]) | ((uint32_t)f32_to_f16_bits(silu(s[2]) * s[3]) << 16);
-      *reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0) = packed;
+    if (valid) {
+      const f32x4_t sum = red[0][wave][lane] + red[1][wave][lane] + red[2][wave][lane] + red[3][wave][lane];
+      emit(tile0 + wave, m, sum);
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restrict__ xg, const WorkArgs wa,
+                                                        const char* __restrict__ slot_base, size_t slot_stride,
+                                                        size_t p1s_off, int H, int I, uint16_t* __restrict__ hbuf) {
+  const int NB = I / 8 / kR;  // blocks per expert
+  const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
+  const int4 it = wa.item[item];
+  const char* blob = slot_base + (size_t)it.x * slot_stride;
+  const int lane = threadIdx.x & 63;
+  int4_decode_tiles(xg, it, H, blob, blob + p1s_off, tile0, [&](int tile, int m, const f32x4_t& s) {
+    const int i0 = 8 * tile + 2 * (lane >> 4);
+    const uint32_t packed =
+        (uint32_t)f32_to_f16_bits(silu(s[0]) * s[1]) | ((uint32_t)f32_to_f16_bits(silu(s[2]) * s[3]) << 16);
+    *reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0) = packed;
+  });
 }
 
 __global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restrict__ hbuf, const WorkArgs wa,
                                                         const char* __restrict__ slot_base, size_t slot_stride,
                                                         size_t p2_off, size_t p2s_off, int H, int I,
                                                         float* __restrict__ y) {
-  const int NT = H / 16;
-  const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
+  const int NB = H / 16 / kR;
+  const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
   const int4 it = wa.item[item];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int KG = I / 128;
-  const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
   const char* blob = slot_base + (size_t)it.x * slot_stride;
-  const char* qp = blob + p2_off + (size_t)tile * KG * 1024 + lane * 16;
-  const char* sp = blob + p2s_off + (size_t)tile * KG * 32 + (lane >> 4) * 8;
-  const int kq = (lane >> 4) * 8;
-  __shared__ f32x4_t red[4][64];
-  for (int m0 = 0; m0 < it.z; m0 += 16) {
-    const int m = m0 + (lane & 15);
-    const bool valid = m < it.z;
-    const uint16_t* hr = hbuf + (size_t)(it.y + (valid ? m : 0)) * I + kq;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll kUG
-    for (int g = g0; g < g1; ++g) int4_block(qp + (size_t)g * 1024, sp + (size_t)g * 32, hr + 128 * g, valid, acc);
-    red[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0 && valid) {
-      const f32x4_t s = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-      *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
-    }
-    __syncthreads();
-  }
+  const int lane = threadIdx.x & 63;
+  int4_decode_tiles(hbuf, it, I, blob + p2_off, blob + p2s_off, tile0, [&](int tile, int m, const f32x4_t& s) {
+    *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -430,11 +436,11 @@ hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, c
                      H, static_cast<uint16_t*>(xg));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ffn1_decode_int4, dim3(wa.n * (I / 8)), dim3(256), 0, s, static_cast<const uint16_t*>(xg), wa,
+  hipLaunchKernelGGL(ffn1_decode_int4, dim3(wa.n * (I / 8 / kR)), dim3(256), 0, s, static_cast<const uint16_t*>(xg), wa,
                      slot_base, slot_stride, L.p1s, H, I, static_cast<uint16_t*>(hbuf));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ffn2_decode_int4, dim3(wa.n * (H / 16)), dim3(256), 0, s, static_cast<const uint16_t*>(hbuf), wa,
+  hipLaunchKernelGGL(ffn2_decode_int4, dim3(wa.n * (H / 16 / kR)), dim3(256), 0, s, static_cast<const uint16_t*>(hbuf), wa,
                      slot_base, slot_stride, L.p2, L.p2s, H, I, y);
   return hipGetLastError();
 }

@@ -249,15 +249,8 @@ __global__ __launch_bounds__(256) void router_small_partial(const void* __restri
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h0 = blockIdx.x * kSmallChunk;
   const int nh = min(kSmallChunk, H - h0);
-  for (int i = threadIdx.x; i < T * kSmallChunk; i += 256) {
-    const int t = i / kSmallChunk, h = i - t * kSmallChunk;
-    xs[t][h] = h < nh ? ldv<BF16>(x, (size_t)t * H + h0 + h) : 0.f;
-  }
-  __syncthreads();
-  const int tb = 1024 / (4 * 64);  // tokens per LDS reduction pass for one 256-expert slab: 4
-  for (int e0 = 0; e0 < E; e0 += 256) {
+  auto load_w = [&](int e0, float (&w)[16][4]) {
     const int e = e0 + 4 * lane;
-    float w[16][4];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int h = wave + 4 * i;
@@ -286,6 +279,19 @@ __global__ __launch_bounds__(256) void router_small_partial(const void* __restri
         }
       }
     }
+  };
+  // The first slab's weight loads go out before the activation barrier, so
+  // both global reads overlap.
+  float w[16][4];
+  load_w(0, w);
+  for (int i = threadIdx.x; i < T * kSmallChunk; i += 256) {
+    const int t = i / kSmallChunk, h = i - t * kSmallChunk;
+    xs[t][h] = h < nh ? ldv<BF16>(x, (size_t)t * H + h0 + h) : 0.f;
+  }
+  __syncthreads();
+  const int tb = 1024 / (4 * 64);  // tokens per LDS reduction pass for one 256-expert slab: 4
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    if (e0 > 0) load_w(e0, w);
     for (int t0 = 0; t0 < T; t0 += tb) {
       float acc[4][4];
 #pragma unroll
@@ -358,6 +364,7 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
   __shared__ int32_t soff[kSmallE];
   __shared__ float zsum[1024];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float bias_first = (bias && tid < T * E) ? bias[tid % E] : 0.f;  // issued early
   for (int e = tid; e < E; e += 1024) bm[e] = 0ull;
   // logits: G threads per (t, e) each add a contiguous range of the partials
   // (16 loads in flight), then the G range sums are added in range order.
@@ -374,14 +381,14 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
       if (tid < n) {
         float l = 0.f;
         for (int g = 0; g < G; ++g) l += zsum[g * n + tid];
-        if (bias) l += bias[tid % E];
+        l += bias_first;
         lg[tid] = l;
         if (logits) logits[tid] = l;
       }
     } else {
       for (int i = tid; i < n; i += 1024) {
         float l = sum_partials(partial + i, (size_t)n, 0, nsplit);
-        if (bias) l += bias[i % E];
+        if (bias) l += i == tid ? bias_first : bias[i % E];
         lg[i] = l;
         if (logits) logits[i] = l;
       }

@@ -131,3 +131,4 @@ def test_argument_validation_without_gpu(L):
     assert lib.moe_decoder_create(None, 1, 64, 64, 8, 2, 1, 1, None, 0, None, 0, None, ctypes.byref(st)) is None
     assert st.value == L.MOE_EINVAL
     assert lib.moe_decoder_step(None, 0, 0, None, 1, None, None, None, 0, None, None) == L.MOE_EINVAL
+    assert lib.moe_decoder_profile(None, 8) == L.MOE_EINVAL
