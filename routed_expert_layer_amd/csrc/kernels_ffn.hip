@@ -468,9 +468,12 @@ hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& 
   return hipGetLastError();
 }
 
-hipError_t launch_router_gemm(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
+int router_gemm_splits(int T, int H, int E) { return gemm2_supported(E, H) ? router_gemm2_splits(T, H, E) : 1; }
+
+hipError_t launch_router_gemm(const void* x, const void* wrt, int T, int H, int E, float* partial, int nsplit,
                               hipStream_t s) {
-  if (gemm2_supported(E, H)) return launch_router_gemm2(x, wrt, bias, T, H, E, logits, s);
+  if (gemm2_supported(E, H)) return launch_router_gemm2(x, wrt, T, H, E, partial, nsplit, s);
+  if (nsplit != 1) return hipErrorInvalidValue;
   WorkArgs wa;
   memset(&wa, 0, sizeof wa);
   wa.n = 1;
@@ -480,7 +483,7 @@ hipError_t launch_router_gemm(const void* x, const void* wrt, const float* bias,
   wa.total_tiles = wa.tile_prefix[1];
   hipLaunchKernelGGL(ffn_gemm_bf16<0>, dim3(wa.total_tiles * (E / kGemmBN)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), nullptr, wa, static_cast<const char*>(wrt), 0, 0, E, H, H, 0,
-                     nullptr, logits, bias);
+                     nullptr, partial, nullptr);
   return hipGetLastError();
 }
 

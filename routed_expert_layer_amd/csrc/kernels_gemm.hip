@@ -81,6 +81,10 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   const int wn = wave % WAVES_N, wm = wave / WAVES_N;
   const int KC = K / 32;
   const int ldb = (PHASE == 2) ? I : H;
+  // The router (PHASE 0) runs split over K: item.x is the split index, K the
+  // split's length; its weight row tiles span all H / 32 chunks.
+  const int KCW = (PHASE == 0) ? ldb / 32 : KC;
+  const int koff = (PHASE == 0) ? it.x * KC : 0;
   // Waves whose token columns all lie past the group skip the matrix-core
   // work (they still load their share of every stage).
   const bool active = mt * (16 * BM_T) + wm * WM * 16 < it.z;
@@ -95,7 +99,8 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   for (int q = 0; q < FPW; ++q) {
     const int f = wave + 8 * q;
     if (f < FA) {
-      src[q] = slot_base + (size_t)it.x * slot_stride + mat_off + (size_t)(nt * BN_T + f) * KC * 1024 + lane * 16;
+      src[q] = slot_base + (size_t)it.x * slot_stride + mat_off + ((size_t)(nt * BN_T + f) * KCW + koff) * 1024 +
+               lane * 16;
       kstep[q] = 1024;
     } else {
       int mloc = mt * (16 * BM_T) + (f - FA) * 16 + (lane & 15);
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
         kstep[q] = 1024;
       } else {
         const size_t row = (PHASE == 1) ? (size_t)perm_src[it.y + mloc] : (size_t)(it.y + mloc);
-        src[q] = reinterpret_cast<const char*>(bsrc + row * ldb + (lane >> 4) * 8);
+        src[q] = reinterpret_cast<const char*>(bsrc + row * ldb + (size_t)koff * 32 + (lane >> 4) * 8);
         kstep[q] = 64;
       }
     }
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
           o[2] += bias[n0 + 2];
           o[3] += bias[n0 + 3];
         }
-        *reinterpret_cast<f32x4_t*>(yout + row * N + n0) = o;
+        *reinterpret_cast<f32x4_t*>(yout + ((size_t)it.x * it.z + row) * N + n0) = o;  // split it.x's slab
       }
     }
   }
@@ -322,17 +327,28 @@ hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const int
   return hipGetLastError();
 }
 
-hipError_t launch_router_gemm2(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
+// Router logits on matrix cores, split over K into `nsplit` slabs of partial
+// sums: partial[(z * T + t) * E + e] over the z-th H / nsplit columns (no
+// bias; the top-k kernel adds the slabs in order, then the bias).
+int router_gemm2_splits(int T, int H, int E) {
+  const int tiles = (T + 127) / 128 * (E / 256);
+  int S = 1;
+  while (S < 16 && tiles * S < 256 && (H / 32) % (2 * S) == 0 && H / 32 / (2 * S) >= 4) S *= 2;
+  return S;
+}
+
+hipError_t launch_router_gemm2(const void* x, const void* wrt, int T, int H, int E, float* partial, int nsplit,
                                hipStream_t s) {
+  if (nsplit < 1 || nsplit > kMaxItems || (H / 32) % nsplit != 0) return hipErrorInvalidValue;
   WorkArgs wa;
   memset(&wa, 0, sizeof wa);
-  wa.n = 1;
-  wa.item[0] = make_int4(0, 0, T, 0);
-  wa.total_tiles = plan_supertiles(wa.item, 1, wa.tile_prefix, E, 256);
+  wa.n = nsplit;
+  for (int z = 0; z < nsplit; ++z) wa.item[z] = make_int4(z, 0, T, 0);
+  wa.total_tiles = plan_supertiles(wa.item, nsplit, wa.tile_prefix, E, 128);
   if (wa.total_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm2_bf16<0, 16, WorkArgs>), dim3(supertile_blocks(wa.total_tiles)), dim3(512), 0, s,
-                     static_cast<const uint16_t*>(x), nullptr, wa, static_cast<const char*>(wrt), 0, 0, E, H, H, 0,
-                     nullptr, logits, bias);
+  hipLaunchKernelGGL((gemm2_bf16<0, 8, WorkArgs>), dim3(supertile_blocks(wa.total_tiles)), dim3(512), 0, s,
+                     static_cast<const uint16_t*>(x), nullptr, wa, static_cast<const char*>(wrt), 0, 0, E, H / nsplit,
+                     H, 0, nullptr, partial, nullptr);
   return hipGetLastError();
 }
 

@@ -149,83 +149,104 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   }
 }
 
-// Grouping by expert in one workgroup. Tokens are taken in chunks of 64 (one
-// wave, one bit per token): for every expert a 64-bit mask of the chunk's
-// tokens that chose it (LDS atomic OR, order independent) gives both the
-// chunk's count and, through a popcount of the lower lanes, each token's
-// rank inside the chunk. Chunk bases are a prefix sum over chunks.
-__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k,
-                                                       int nwaves, int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
-                                                       int32_t* __restrict__ perm_pos, int32_t* __restrict__ hist,
-                                                       uint64_t* __restrict__ bits, int32_t* __restrict__ counts_mirror) {
-  extern __shared__ uint64_t smem[];  // nwaves * E masks, then E+1 ints
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nchunks = (T + 63) / 64;
-  uint64_t* bm = smem + (size_t)wave * E;
-  int32_t* cnt = reinterpret_cast<int32_t*>(smem + (size_t)nwaves * E);
-  const bool active = wave < nwaves;
-  // phase 1: per-chunk masks and counts
-  for (int r = 0; r * nwaves < nchunks; ++r) {
-    const int c = r * nwaves + wave;
-    if (active && c < nchunks)
-      for (int e = lane; e < E; e += 64) bm[e] = 0;
-    __syncthreads();
-    if (active && c < nchunks) {
-      const int t = c * 64 + lane;
-      if (t < T)
-        for (int j = 0; j < k; ++j) atomicOr((unsigned long long*)&bm[topk_idx[(size_t)t * k + j]], 1ull << lane);
-    }
-    __syncthreads();
-    if (active && c < nchunks)
-      for (int e = lane; e < E; e += 64) {
-        const uint64_t b = bm[e];
-        bits[(size_t)c * E + e] = b;
-        hist[(size_t)c * E + e] = __popcll(b);
-      }
-    __syncthreads();
+// Grouping of the T*k selections by expert, stable by token (three kernels
+// over 64-token chunks, every step parallel over chunks or experts).
+// Workspace: bits [nchunks][E] (which tokens of a chunk chose e), hist
+// [E][nchunks] (their count, then the exclusive prefix over chunks).
+
+// Exclusive prefix sum over a 256-thread block; *total gets the block sum.
+__device__ __forceinline__ int block_excl_scan256(int v, int* total) {
+  __shared__ int wsum[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int n = __shfl_up(x, d);
+    if (lane >= d) x += n;
   }
-  // phase 2: totals per expert, exclusive prefix over experts
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int s = 0;
-    for (int c = 0; c < nchunks; ++c) s += hist[(size_t)c * E + e];
-    cnt[e] = s;
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  *total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(256) void chunk_masks_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k,
+                                                          int nchunks, uint64_t* __restrict__ bits,
+                                                          int32_t* __restrict__ hist) {
+  extern __shared__ uint64_t bm[];  // E masks
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) bm[e] = 0ull;
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * k; i += 256) {
+    const int tl = i / k, j = i - tl * k, t = c * 64 + tl;
+    if (t < T) atomicOr((unsigned long long*)&bm[topk_idx[(size_t)t * k + j]], 1ull << tl);
   }
   __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    const uint64_t b = bm[e];
+    bits[(size_t)c * E + e] = b;
+    hist[(size_t)e * nchunks + c] = __popcll(b);
+  }
+}
+
+// One block per expert: its chunk counts become exclusive prefixes, the
+// total is the expert's count.
+__global__ __launch_bounds__(256) void expert_scan_kernel(int32_t* __restrict__ hist, int nchunks,
+                                                          int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ counts_mirror) {
+  int32_t* h = hist + (size_t)blockIdx.x * nchunks;
+  int carry = 0;
+  for (int base = 0; base < nchunks; base += 256) {
+    const int c = base + threadIdx.x;
+    const int v = c < nchunks ? h[c] : 0;
+    int tot;
+    const int ex = block_excl_scan256(v, &tot);
+    if (c < nchunks) h[c] = carry + ex;
+    carry += tot;
+  }
   if (threadIdx.x == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      const int v = cnt[e];
-      counts[e] = v;
-      if (counts_mirror) counts_mirror[e] = v;
-      offsets[e] = run;
-      cnt[e] = run;
-      run += v;
-    }
-    offsets[E] = run;
+    counts[blockIdx.x] = carry;
+    if (counts_mirror) counts_mirror[blockIdx.x] = carry;
   }
-  __syncthreads();
-  // phase 3: base of every (chunk, expert)
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = cnt[e];
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = hist[(size_t)c * E + e];
-      hist[(size_t)c * E + e] = run;
-      run += v;
+}
+
+// One block per chunk: expert offsets (exclusive scan of the counts, redone
+// by every block), then each selection's row = offset of its expert + rows
+// of the expert in earlier chunks + earlier tokens of this chunk.
+__global__ __launch_bounds__(256) void positions_kernel(const int32_t* __restrict__ topk_idx, int T, int E, int k,
+                                                        int nchunks, const int32_t* __restrict__ counts,
+                                                        const uint64_t* __restrict__ bits,
+                                                        const int32_t* __restrict__ hist,
+                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+                                                        int32_t* __restrict__ perm_pos) {
+  extern __shared__ int32_t off[];  // E
+  const int per = (E + 255) / 256;  // experts per thread, contiguous
+  const int e0 = threadIdx.x * per;
+  int local = 0;
+  for (int q = 0; q < per; ++q)
+    if (e0 + q < E) local += counts[e0 + q];
+  int tot;
+  int run = block_excl_scan256(local, &tot);
+  for (int q = 0; q < per; ++q)
+    if (e0 + q < E) {
+      off[e0 + q] = run;
+      if (blockIdx.x == 0) offsets[e0 + q] = run;
+      run += counts[e0 + q];
     }
-  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) offsets[E] = tot;
   __syncthreads();
-  // phase 4: positions
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c = wave; c < nchunks && active; c += nwaves) {
-    const int t = c * 64 + lane;
-    if (t < T)
-      for (int j = 0; j < k; ++j) {
-        const int e = topk_idx[(size_t)t * k + j];
-        const int pos = hist[(size_t)c * E + e] + __popcll(bits[(size_t)c * E + e] & below);
-        perm_pos[(size_t)t * k + j] = pos;
-        perm_src[pos] = t;
-      }
+  const int c = blockIdx.x;
+  for (int i = threadIdx.x; i < 64 * k; i += 256) {
+    const int tl = i / k, j = i - tl * k, t = c * 64 + tl;
+    if (t >= T) continue;
+    const int e = topk_idx[(size_t)t * k + j];
+    const uint64_t below = tl == 0 ? 0ull : (~0ull >> (64 - tl));
+    const int pos = off[e] + hist[(size_t)e * nchunks + c] + __popcll(bits[(size_t)c * E + e] & below);
+    perm_pos[(size_t)t * k + j] = pos;
+    perm_src[pos] = t;
   }
 }
 
@@ -477,8 +498,8 @@ RoutePlan plan_route(int T, int H, int E, bool bf16) {
     p.partial_bytes = align_up((size_t)p.nsplit * (T > 0 ? T : 1) * E * sizeof(float), 256);
   } else if (gemm_router_ok(bf16, T, H, E)) {
     p.mode = 1;
-    p.nsplit = 1;
-    p.partial_bytes = align_up((size_t)T * E * sizeof(float), 256);
+    p.nsplit = router_gemm_splits(T, H, E);
+    p.partial_bytes = align_up((size_t)p.nsplit * T * E * sizeof(float), 256);
   } else {
     p.mode = 2;
     p.gx = (E + 63) / 64;
@@ -532,7 +553,7 @@ hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* b
   if (p.mode == 1) {
     void* wrt = w + p.wrt_off;
     if ((err = launch_pack_fragments(Wr, H, E, wrt, s)) != hipSuccess) return err;
-    if ((err = launch_router_gemm(x, wrt, bias, T, H, E, partial, s)) != hipSuccess) return err;
+    if ((err = launch_router_gemm(x, wrt, T, H, E, partial, p.nsplit, s)) != hipSuccess) return err;
   } else {
     dim3 grid(p.gx, p.gy, p.nsplit);
     if (bf16)
@@ -541,15 +562,19 @@ hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* b
       hipLaunchKernelGGL(router_partial_kernel<false>, grid, dim3(256), 0, s, x, Wr, T, H, E, p.hchunk, partial);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  // mode 1 has the bias already added by the GEMM epilogue
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, partial, p.nsplit, p.mode == 1 ? nullptr : bias,
+  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, partial, p.nsplit, bias,
                      T, E, k, topk_idx, topk_w, logits);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  int nwaves = 16;
-  while (nwaves > 1 && (size_t)nwaves * E * 8 + (E + 1) * 4 > 64 * 1024) nwaves /= 2;
-  const size_t lds = (size_t)nwaves * E * 8 + (size_t)(E + 1) * 4;
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, topk_idx, T, E, k, nwaves, counts, offsets, perm_src,
-                     perm_pos, hist, bits, counts_mirror);
+  const int nchunks = (T + 63) / 64;
+  if (nchunks > 0) {
+    hipLaunchKernelGGL(chunk_masks_kernel, dim3(nchunks), dim3(256), (size_t)E * 8, s, topk_idx, T, E, k, nchunks, bits,
+                       hist);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(expert_scan_kernel, dim3(E), dim3(256), 0, s, hist, nchunks, counts, counts_mirror);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(positions_kernel, dim3(nchunks > 0 ? nchunks : 1), dim3(256), (size_t)E * 4, s, topk_idx, T, E, k,
+                     nchunks, counts, bits, hist, offsets, perm_src, perm_pos);
   return hipGetLastError();
 }
 

@@ -108,7 +108,10 @@ bool prefill_supported(int wfmt, int H, int I);
 // fragment order (rows = experts, K = H) in the workspace, then
 // logits[t, e] = x[t, :] . Wr[:, e] + bias[e] (fp32) by the GEMM kernel.
 hipError_t launch_pack_fragments(const void* W, int K, int N, void* dst, hipStream_t s);
-hipError_t launch_router_gemm(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
+// Writes `nsplit` slabs of partial logits (no bias): partial[(z*T + t)*E + e].
+// router_gemm_splits gives the slab count the launcher will use.
+int router_gemm_splits(int T, int H, int E);
+hipError_t launch_router_gemm(const void* x, const void* wrt, int T, int H, int E, float* partial, int nsplit,
                               hipStream_t s);
 // Large-tile GEMM (256 weight rows per block) used when N % 256 == 0.
 bool gemm2_supported(int N, int K);
@@ -118,7 +121,8 @@ bool gemm2_supported(int N, int K);
 hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const int4* items, int n,
                                const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
                                void* tables, hipStream_t s);
-hipError_t launch_router_gemm2(const void* x, const void* wrt, const float* bias, int T, int H, int E, float* logits,
+int router_gemm2_splits(int T, int H, int E);
+hipError_t launch_router_gemm2(const void* x, const void* wrt, int T, int H, int E, float* partial, int nsplit,
                                hipStream_t s);
 
 // Sets the calling thread's moe_last_error() message; returns `code`.
