@@ -55,15 +55,43 @@ class EventTimer:
         return sum(self.work), sum(ms), len(ms)
 
 
-def measured_traffic(root):
-    """HBM bytes per FFN call from the committed counter summary, if the kernel sources are unchanged since."""
+def _definition(src, signature):
+    """Text of the definition that starts at `signature` (through its matching closing brace)."""
+    i = src.index(signature)
+    j = src.index("{", i)
+    depth = 0
+    for n in range(j, len(src)):
+        if src[n] == "{":
+            depth += 1
+        elif src[n] == "}":
+            depth -= 1
+            if depth == 0:
+                return src[i:n + 1]
+    raise ValueError(signature)
+
+
+def decode_ffn_digest(root):
+    """sha256 over the source text the decode expert-FFN kernels are built from: both kernels, their
+    launcher, the device helpers and the work-list / blob-layout definitions."""
     import hashlib
+    csrc = os.path.join(root, "routed_expert_layer_amd", "csrc")
+    ffn = open(os.path.join(csrc, "kernels_ffn.hip")).read()
+    hdr = open(os.path.join(csrc, "moe_kernels.hpp")).read()
+    parts = [open(os.path.join(csrc, "dev_common.hpp")).read(),
+             _definition(ffn, "__global__ __launch_bounds__(256) void ffn1_decode_bf16("),
+             _definition(ffn, "__global__ __launch_bounds__(256) void ffn2_decode_bf16("),
+             _definition(ffn, "hipError_t launch_ffn_decode("),
+             _definition(hdr, "struct WorkArgs"), _definition(hdr, "inline BlobLayout blob_layout(")]
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()
+
+
+def measured_traffic(root):
+    """HBM bytes per FFN call from the committed counter summary, if the kernels' sources are unchanged since."""
     path = os.path.join(root, "profiles", "decode_ffn_hbm_traffic.json")
     try:
         j = json.load(open(path))
-        for rel, digest in j["sources_sha256"].items():
-            if hashlib.sha256(open(os.path.join(root, rel), "rb").read()).hexdigest() != digest:
-                return None
+        if j["kernel_source_sha256"] != decode_ffn_digest(root):
+            return None
         return int(j["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
