@@ -24,10 +24,17 @@
 namespace moe {
 namespace {
 
-// Direct global -> LDS load of one 16-byte chunk per lane into the wave's
-// 1 KiB LDS destination `dst` (lane l writes dst + 16 l).
-__device__ __forceinline__ void load_lds16(const void* src, char* dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 at their maxima).
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// One 16-byte chunk per lane from base + off (a wave-uniform base, a 32-bit
+// lane offset) straight into the wave's 1 KiB at `lds` (lane l at lds + 16 l),
+// through a raw buffer resource (dword 3 = 0x00020000 for byte-addressed
+// loads on gfx950, no bounds check).
+__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t off, char* lds) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
 }
 
 // The work list comes by value (WorkArgs) or from device memory (GemmTable);
@@ -85,34 +92,36 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   // split's length; its weight row tiles span all H / 32 chunks.
   const int KCW = (PHASE == 0) ? ldb / 32 : KC;
   const int koff = (PHASE == 0) ? it.x * KC : 0;
-  // Waves whose token columns all lie past the group skip the matrix-core
-  // work (they still load their share of every stage).
-  const bool active = mt * (16 * BM_T) + wm * WM * 16 < it.z;
 
   // This wave loads stage fragments f = wave + 8q (q < FPW): weight fragment
-  // row tile f (f < FA) or token column f - FA. Lane addresses without the K
-  // offset; tokens past the group read a valid row (their columns of the
-  // product are never stored).
-  const char* src[FPW];
-  int kstep[FPW];  // bytes per 32-wide K step
+  // row tile f for q < FA / 8, token column f - FA after. Loads are
+  // buffer-addressed (a wave-uniform base plus a 32-bit lane offset): a flat
+  // global -> LDS load would count as a pending flat LDS access and make the
+  // compiler wait for every LDS read before the first matrix-core
+  // instruction. Lane offsets exclude the K step; tokens past the group read
+  // a valid row (their columns of the product are never stored).
+  static_assert(FA % 8 == 0, "weight and token loads split at a fixed q");
+  constexpr int QW = FA / 8;  // weight loads per wave per stage
+  const char* wbase = slot_base + (size_t)it.x * slot_stride + mat_off;
+  uint32_t off[FPW];
+  uint32_t kstep[FPW];  // bytes per 32-wide K step
 #pragma unroll
   for (int q = 0; q < FPW; ++q) {
     const int f = wave + 8 * q;
-    if (f < FA) {
-      src[q] = slot_base + (size_t)it.x * slot_stride + mat_off + ((size_t)(nt * BN_T + f) * KCW + koff) * 1024 +
-               lane * 16;
+    if (q < QW) {
+      off[q] = (uint32_t)(((nt * BN_T + f) * KCW + koff) * 1024 + lane * 16);
       kstep[q] = 1024;
     } else {
       int mloc = mt * (16 * BM_T) + (f - FA) * 16 + (lane & 15);
       if (mloc >= it.z) mloc = it.z - 1;
       if constexpr (PHASE == 2) {
         // h in fragment order: row r, 32-wide K chunk c at ((r/16) * KC + c) KiB
-        const size_t row = (size_t)(it.y + mloc);
-        src[q] = reinterpret_cast<const char*>(bsrc) + (row >> 4) * KC * 1024 + ((row & 15) + 16 * (lane >> 4)) * 16;
+        const uint32_t row = (uint32_t)(it.y + mloc);
+        off[q] = (row >> 4) * (uint32_t)KC * 1024u + ((row & 15) + 16 * (lane >> 4)) * 16;
         kstep[q] = 1024;
       } else {
-        const size_t row = (PHASE == 1) ? (size_t)perm_src[it.y + mloc] : (size_t)(it.y + mloc);
-        src[q] = reinterpret_cast<const char*>(bsrc + row * ldb + (size_t)koff * 32 + (lane >> 4) * 8);
+        const uint32_t row = (PHASE == 1) ? (uint32_t)perm_src[it.y + mloc] : (uint32_t)(it.y + mloc);
+        off[q] = (row * (uint32_t)ldb + (uint32_t)koff * 32 + (lane >> 4) * 8) * 2;
         kstep[q] = 64;
       }
     }
@@ -120,7 +129,9 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   auto issue = [&](int kt) {  // stage kt -> LDS buffer kt % NS
     char* base = lds[kt % NS];
 #pragma unroll
-    for (int q = 0; q < FPW; ++q) load_lds16(src[q] + (size_t)kt * kstep[q], base + (wave + 8 * q) * 1024);
+    for (int q = 0; q < FPW; ++q)
+      buffer_load_lds16(q < QW ? static_cast<const void*>(wbase) : static_cast<const void*>(bsrc),
+                        off[q] + (uint32_t)kt * kstep[q], base + (wave + 8 * q) * 1024);
   };
 
   f32x4_t acc[WN][WM];
@@ -140,13 +151,15 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < WN; ++i) f.a[i] = *reinterpret_cast<const u32x4_t*>(b + (wn * WN + i) * 1024 + lane * 16);
   };
+  // Every wave runs its matrix-core work, also on token columns past the
+  // group (their results are never stored): no branch separates the LDS
+  // reads from the instructions that consume them, so each instruction
+  // waits only for its own operands.
   auto compute = [&](const Frags& f) {
-    if (active) {
 #pragma unroll
-      for (int i = 0; i < WN; ++i)
+    for (int i = 0; i < WN; ++i)
 #pragma unroll
-        for (int j = 0; j < WM; ++j) acc[i][j] = mfma_bf16(f.a[i], f.b[j], acc[i][j]);
-    }
+      for (int j = 0; j < WM; ++j) acc[i][j] = mfma_bf16(f.a[i], f.b[j], acc[i][j]);
   };
 
   {
@@ -156,9 +169,9 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
     for (int kt = 0; kt < KC; ++kt) {
       // stage kt has landed once at most the later stages' loads are pending
       if (kt + NS - 2 < KC) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FPW * (NS - 2)) : "memory");
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 2)));
       } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
       }
       // every wave's part of stage kt is in LDS, and every wave is done with
       // stage kt - 1, whose buffer is refilled next
