@@ -153,6 +153,18 @@ int moe_pool_free(void* pool);
  * Outputs (host arrays of capacity n): work_e[i], work_slot[i], work_wave[i]
  * in access order; misses[0..*n_miss) in access order; *n_waves.
  * Every access is appended to the cache's trace (moe_cache_trace).
+ *
+ * moe_cache_set_split (page "FreeToken-rtx-4090", component table rows "CPU"
+ * and "PCIe link", section "Adaptive Misses"): misses are divided between
+ * GPU fills and CPU execution from measured rates (any common unit, e.g. MB/s
+ * of PCIe fills and of the host expert kernel). Of all misses since the call,
+ * floor(rate_gpu * count / (rate_gpu + rate_cpu)) go to the GPU (carried
+ * remainder); within a layer-step the lowest keys go first. The others are
+ * returned by cache_resolve after the GPU accesses with work_slot = -1 and
+ * work_wave = -1 (run them with moe_cpu_ffn from the pool), are not in
+ * misses[], are not cached and leave the recency order alone; their trace
+ * records have slot = victim = wave = -1. rate_cpu = 0 (the default) fills
+ * every miss. Errors: MOE_EINVAL (negative rates, zero sum, null).
  * Errors: MOE_EINVAL (null, layer or expert out of range, experts not
  * ascending or not unique), MOE_ECAPACITY (S == 0 at create).
  *
@@ -170,6 +182,7 @@ int moe_cache_destroy(moe_cache_t* cache);
 int cache_resolve(moe_cache_t* cache, int step, int layer, const int32_t* experts, int n,
                   int32_t* work_e, int32_t* work_slot, int32_t* work_wave,
                   moe_miss_t* misses, int* n_miss, int* n_waves);
+int moe_cache_set_split(moe_cache_t* cache, int rate_gpu, int rate_cpu);
 int moe_cache_trace(const moe_cache_t* cache, moe_trace_t* out, int64_t max_records, int64_t* n_records);
 int moe_cache_clear_trace(moe_cache_t* cache);
 int moe_cache_invalidate(moe_cache_t* cache, int key);
@@ -329,6 +342,28 @@ int moe_decoder_step(moe_decoder_t* decoder, int step, int layer, const void* x,
 int moe_decoder_profile(moe_decoder_t* decoder, int every);
 int moe_decoder_ffn_stats(moe_decoder_t* decoder, double* bytes, double* ms, int64_t* launches);
 int moe_decoder_fills(const moe_decoder_t* decoder, int64_t* fills);
+
+/* ---------------------------------------------------------------------------
+ * CPU execution of an expert (page "FreeToken-rtx-4090", component table row
+ * "CPU" and section "Adaptive Misses"; page "FreeToken-benchmark", "Adaptive
+ * Misses"): a missing expert may run on the host straight from the pinned
+ * pool instead of being copied to the GPU.
+ *
+ * moe_cpu_ffn: y = (silu(x W1) * (x W3)) W2 for `rows` activation rows, on the
+ *   host CPU, from the expert's bf16 blob (the moe_pack_expert layout).
+ *   blob: host pointer (e.g. inside a moe_pool_alloc region); x: host bf16
+ *   [rows, H] row-major; y: host fp32 [rows, H] row-major, overwritten. The
+ *   SwiGLU product is rounded to bf16 before the down projection, as on the
+ *   GPU. threads: participating threads (<= 0: all, see moe_cpu_threads);
+ *   the library keeps one process-wide pool of worker threads, and calls from
+ *   several host threads at once are serialised by the caller. Synchronous.
+ *   Errors: EINVAL for null pointers, negative rows, or a format other than
+ *   bf16 with H, I multiples of 32. Needs a CPU with AVX-512 BF16.
+ * moe_cpu_threads: the number of threads moe_cpu_ffn can use (workers + the
+ *   calling thread).
+ * ------------------------------------------------------------------------- */
+int moe_cpu_ffn(const void* blob, int wfmt, int H, int I, const void* x, int rows, float* y, int threads);
+int moe_cpu_threads(void);
 
 #ifdef __cplusplus
 }

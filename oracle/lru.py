@@ -20,6 +20,25 @@ touch the cache, so this simulator takes the following reading:
     before the next wave's misses are filled;
   * the cache starts empty.
 
+Misses may also be executed on the CPU straight from the host pool instead of
+being filled (page "FreeToken-rtx-4090", component table rows "CPU" and "PCIe
+link", section "Adaptive Misses"; page "FreeToken-benchmark", "Adaptive
+Misses"): the runtime measures the PCIe fill rate and the host's expert
+processing rate and sends the share rate_gpu / (rate_gpu + rate_cpu) of the
+misses to the GPU. The pages give neither the rounding nor which misses go
+where; reading taken here:
+
+  * the share is realised with a carried remainder: the number of misses sent
+    to the GPU up to and including a layer-step is floor(rate_gpu * (misses up
+    to it) / (rate_gpu + rate_cpu)), so single-miss layer-steps do not all
+    round the same way;
+  * of one layer-step's misses (ascending), the lowest q go to the GPU; the
+    others run on the CPU, are not cached and do not touch the recency order;
+  * the GPU accesses (hits, then GPU misses) form the waves as above; CPU
+    misses are recorded after them with slot, victim and wave -1.
+
+rate_cpu = 0 (the default) fills every miss.
+
 It keeps explicit per-slot last-use stamps rather than an ordered container,
 so that the tests can check it against a textbook ordered-dict LRU.
 """
@@ -38,7 +57,7 @@ class TraceRec:
 
 
 class SharedLRU:
-    def __init__(self, S):
+    def __init__(self, S, rate_gpu=1, rate_cpu=0):
         assert S >= 1
         self.S = S
         self.slot_key = [-1] * S
@@ -46,16 +65,29 @@ class SharedLRU:
         self.key_slot = {}
         self.clock = 0
         self.trace = []
+        self.set_split(rate_gpu, rate_cpu)
+
+    def set_split(self, rate_gpu, rate_cpu):
+        """Integer rates; the share of misses filled is rate_gpu / (rate_gpu + rate_cpu)."""
+        assert rate_gpu >= 0 and rate_cpu >= 0 and rate_gpu + rate_cpu > 0
+        self.rate_gpu, self.rate_cpu = int(rate_gpu), int(rate_cpu)
+        self.missed = 0   # misses seen since the split was set
+        self.to_gpu = 0   # of which sent to the GPU
 
     def resolve(self, step, layer, E, experts):
         """Run one layer-step. Returns (waves, records).
 
-        waves: list of lists of (expert, slot) in access order.
-        records: one TraceRec per accessed key (also appended to self.trace).
+        waves: list of lists of (expert, slot) in access order (GPU work).
+        records: one TraceRec per key of the working set (also appended to
+        self.trace); misses run on the CPU have slot -1.
         """
         keys = sorted({layer * E + int(e) for e in experts})
         hit_set = {kk for kk in keys if kk in self.key_slot}
-        seq = [kk for kk in keys if kk in hit_set] + [kk for kk in keys if kk not in hit_set]
+        missing = [kk for kk in keys if kk not in hit_set]
+        self.missed += len(missing)
+        q = self.rate_gpu * self.missed // (self.rate_gpu + self.rate_cpu) - self.to_gpu
+        self.to_gpu += q
+        seq = [kk for kk in keys if kk in hit_set] + missing[:q]
         waves, recs = [], []
         for pos, key in enumerate(seq):
             wave = pos // self.S
@@ -77,5 +109,7 @@ class SharedLRU:
             self.last_use[slot] = self.clock
             waves[wave].append((key - layer * E, slot))
             recs.append(TraceRec(step, layer, key, int(key in hit_set), slot, victim, wave))
+        for key in missing[q:]:  # executed on the CPU: not cached
+            recs.append(TraceRec(step, layer, key, 0, -1, -1, -1))
         self.trace.extend(recs)
         return waves, recs

@@ -8,7 +8,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["kernels_route.hip", "kernels_ffn.hip", "kernels_gemm.hip", "kernels_misc.hip", "abi.cpp", "decoder.cpp", "lru_policy.cpp"]
+SOURCES = ["kernels_route.hip", "kernels_ffn.hip", "kernels_gemm.hip", "kernels_misc.hip", "abi.cpp", "decoder.cpp", "lru_policy.cpp",
+           "cpu_expert.cpp"]
+# host-only sources with extra flags: the CPU expert kernel uses AVX-512 BF16 dot products
+EXTRA = {"cpu_expert.cpp": ["-mavx512f", "-mavx512bw", "-mavx512vl", "-mavx512bf16"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          # packed fp32 instructions are disabled for all device code
@@ -23,7 +26,7 @@ def build(verbose=False):
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

@@ -72,6 +72,7 @@ int moe_cache_layers(const moe_cache_t* c, int* n_layers) {
   return MOE_OK;
 }
 int moe_cache_experts(const moe_cache_t* c) { return c ? c->E : -1; }
+bool moe_cache_splits(const moe_cache_t* c) { return c && c->lru.splits(); }
 
 extern "C" {
 
@@ -198,14 +199,21 @@ int cache_resolve(moe_cache_t* c, int step, int layer, const int32_t* experts, i
   for (int i = 0; i < n; ++i) {
     const moe::Access& a = acc[i];
     work_e[i] = a.key - layer * c->E;
-    work_slot[i] = a.slot;
+    work_slot[i] = a.slot;  // -1: run on the CPU
     work_wave[i] = a.wave;
     nw = std::max(nw, a.wave + 1);
-    if (!a.hit) misses[nm++] = moe_miss_t{a.key, a.slot, a.victim, a.wave};
+    if (!a.hit && a.slot >= 0) misses[nm++] = moe_miss_t{a.key, a.slot, a.victim, a.wave};
     c->trace.push_back(moe_trace_t{step, layer, a.key, a.hit, a.slot, a.victim, a.wave});
   }
   *n_miss = nm;
   *n_waves = nw;
+  return MOE_OK;
+}
+
+int moe_cache_set_split(moe_cache_t* c, int rate_gpu, int rate_cpu) {
+  if (!c || rate_gpu < 0 || rate_cpu < 0 || rate_gpu + rate_cpu <= 0)
+    return fail(MOE_EINVAL, "moe_cache_set_split: rates must be >= 0 with a positive sum");
+  c->lru.set_split(rate_gpu, rate_cpu);
   return MOE_OK;
 }
 

@@ -21,6 +21,12 @@ void SharedLru::push_mru(int s) {
   mru_ = s;
 }
 
+void SharedLru::set_split(int64_t rate_gpu, int64_t rate_cpu) {
+  rate_gpu_ = rate_gpu;
+  rate_cpu_ = rate_cpu;
+  missed_ = to_gpu_ = 0;
+}
+
 void SharedLru::resolve(const int32_t* keys, int n, std::vector<Access>& out) {
   // Hits are decided before any access of this layer-step is made.
   std::vector<int32_t> order;
@@ -28,7 +34,13 @@ void SharedLru::resolve(const int32_t* keys, int n, std::vector<Access>& out) {
   for (int i = 0; i < n; ++i) if (key_slot_[keys[i]] >= 0) order.push_back(keys[i]);
   const size_t n_hits = order.size();
   for (int i = 0; i < n; ++i) if (key_slot_[keys[i]] < 0) order.push_back(keys[i]);
-  for (size_t pos = 0; pos < order.size(); ++pos) {
+  // GPU share of the misses, with the remainder carried across layer-steps
+  missed_ += (int64_t)(order.size() - n_hits);
+  const int64_t q = rate_gpu_ * missed_ / (rate_gpu_ + rate_cpu_) - to_gpu_;
+  to_gpu_ += q;
+  const size_t n_gpu = n_hits + (size_t)q;
+  misses_ += (int64_t)(order.size() - n_gpu);  // CPU-run misses, recorded last
+  for (size_t pos = 0; pos < n_gpu; ++pos) {
     const int32_t key = order[pos];
     Access a{key, pos < n_hits ? 1 : 0, -1, -1, static_cast<int32_t>(pos / S_)};
     if (a.hit) {
@@ -52,6 +64,7 @@ void SharedLru::resolve(const int32_t* keys, int n, std::vector<Access>& out) {
     push_mru(a.slot);
     out.push_back(a);
   }
+  for (size_t pos = n_gpu; pos < order.size(); ++pos) out.push_back(Access{order[pos], 0, -1, -1, -1});
 }
 
 bool SharedLru::invalidate(int key) {

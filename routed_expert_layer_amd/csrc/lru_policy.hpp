@@ -5,7 +5,10 @@
 // selected experts in one LRU cache shared across layers and tokens. One
 // layer-step touches its working set hits-first then misses, each ascending;
 // a miss takes the lowest free slot, else the least recently used entry's
-// slot; accesses are cut into waves of at most S entries.
+// slot; accesses are cut into waves of at most S entries. Misses may be split
+// between GPU fills and CPU execution (section "Adaptive Misses"): of all
+// misses so far, floor(g * count / (g + c)) go to the GPU, the lowest keys of
+// each layer-step first; CPU-run misses are not cached.
 #pragma once
 #include <cstdint>
 #include <set>
@@ -20,8 +23,12 @@ struct Access {
 class SharedLru {
  public:
   SharedLru(int n_keys, int S);
-  // One layer-step over ascending unique keys; appends to `out` in access order.
+  // One layer-step over ascending unique keys; appends to `out` the GPU
+  // accesses in access order, then the CPU-run misses (slot, victim, wave -1).
   void resolve(const int32_t* keys, int n, std::vector<Access>& out);
+  // Rates (any common unit) of GPU fills and CPU execution; resets the count.
+  void set_split(int64_t rate_gpu, int64_t rate_cpu);
+  bool splits() const { return rate_cpu_ > 0; }
   int slot_of(int key) const { return key_slot_[key]; }
   bool invalidate(int key);  // returns false if the key is not resident
   int capacity() const { return S_; }
@@ -38,6 +45,7 @@ class SharedLru {
   int lru_ = -1, mru_ = -1;
   std::set<int> free_;
   int64_t hits_ = 0, misses_ = 0;
+  int64_t rate_gpu_ = 1, rate_cpu_ = 0, missed_ = 0, to_gpu_ = 0;
 };
 
 }  // namespace moe

@@ -48,12 +48,17 @@ def test_expert_bytes(L):
     assert L.moe_expert_bytes(7, 64, 64) == 0
 
 
-@pytest.mark.parametrize("S,E,Lyr,max_active,steps", [(8, 16, 1, 14, 64), (64, 256, 1, 6, 200), (16, 32, 6, 10, 40),
-                                                      (3, 12, 2, 9, 50), (1, 4, 1, 4, 30)])
-def test_cache_resolve_matches_oracle(L, S, E, Lyr, max_active, steps):
+@pytest.mark.parametrize("S,E,Lyr,max_active,steps,split", [
+    (8, 16, 1, 14, 64, None), (64, 256, 1, 6, 200, None), (16, 32, 6, 10, 40, None), (3, 12, 2, 9, 50, None),
+    (1, 4, 1, 4, 30, None), (8, 16, 1, 14, 64, (1, 3)), (64, 256, 1, 6, 200, (56, 165)), (16, 32, 6, 10, 40, (2, 1)),
+    (3, 12, 2, 9, 50, (0, 1)), (4, 16, 3, 8, 40, (5, 0))])
+def test_cache_resolve_matches_oracle(L, S, E, Lyr, max_active, steps, split):
     r = np.random.default_rng(S + E + Lyr)
     cache = L.MoeCache(Lyr, E, S)
     sim = oracle.SharedLRU(S)
+    if split:
+        L.moe_cache_set_split(cache, *split)
+        sim.set_split(*split)
     zipf = 1.0 / np.arange(1, E + 1) ** 1.2
     for step in range(steps):
         for layer in range(Lyr):
@@ -63,14 +68,19 @@ def test_cache_resolve_matches_oracle(L, S, E, Lyr, max_active, steps):
             waves, recs = sim.resolve(step, layer, E, ex)
             assert nw == len(waves)
             flat = [(e, s, w) for w, wv in enumerate(waves) for (e, s) in wv]
+            flat += [(rc.key - layer * E, -1, -1) for rc in recs if rc.slot < 0]  # run on the CPU
             assert list(zip(we.tolist(), wslot.tolist(), wwave.tolist())) == flat
-            exp_m = [[rc.key, rc.slot, rc.victim, rc.wave] for rc in recs if not rc.hit]
+            exp_m = [[rc.key, rc.slot, rc.victim, rc.wave] for rc in recs if not rc.hit and rc.slot >= 0]
             assert misses.tolist() == exp_m
     tr = L.moe_cache_trace(cache)
     ref = np.array([[r.step, r.layer, r.key, r.hit, r.slot, r.victim, r.wave] for r in sim.trace])
     assert np.array_equal(tr, ref)
     h, m = L.moe_cache_stats(cache)
     assert h == int(ref[:, 3].sum()) and m == len(ref) - h
+    with pytest.raises(L.MoEError):
+        L.moe_cache_set_split(cache, 0, 0)
+    with pytest.raises(L.MoEError):
+        L.moe_cache_set_split(cache, -1, 2)
 
 
 def test_cache_errors_and_invalidate(L):

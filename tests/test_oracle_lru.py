@@ -81,3 +81,65 @@ def test_lru_waves_and_hits_first():
     # wave 1 evicts the entries of wave 0, least recent first
     assert [rc.victim for rc in recs[3:]] == [1, 2, 0]
     assert waves == [[(1, 0), (2, 1), (0, 2)], [(3, 0), (4, 1), (5, 2)]]
+
+
+# ---------------------------------------------------------------------------
+# Misses split between GPU fills and CPU execution
+
+
+@pytest.mark.parametrize("S,E,L,max_active,g,c", [(8, 16, 1, 14, 1, 3), (4, 10, 3, 6, 56, 165), (16, 32, 4, 10, 2, 1),
+                                                  (1, 5, 2, 3, 5, 7), (8, 16, 2, 6, 1, 0)])
+def test_split_against_textbook_and_closed_form(S, E, L, max_active, g, c):
+    """GPU-bound accesses follow a textbook LRU that never sees the CPU-run keys;
+    the filled share is floor(g * misses / (g + c)) after every layer-step."""
+    r = np.random.default_rng(S * 7 + E + g)
+    sim = oracle.SharedLRU(S, g, c)
+    tb = TextbookLRU(S)
+    from fractions import Fraction
+    credit = Fraction(0)  # carried remainder, an independent statement of the rounding
+    missed = filled = 0
+    for step in range(60):
+        for layer in range(L):
+            n = int(r.integers(1, max_active + 1))
+            experts = sorted(r.choice(E, size=n, replace=False).tolist())
+            waves, recs = sim.resolve(step, layer, E, experts)
+            keys = [layer * E + e for e in experts]
+            hits0 = sorted(kk for kk in keys if kk in tb.od)
+            miss0 = sorted(kk for kk in keys if kk not in tb.od)
+            missed += len(miss0)
+            credit += len(miss0) * Fraction(g, g + c)
+            q = int(credit)  # floor (credit >= 0)
+            credit -= q
+            filled += q
+            gpu, cpu = hits0 + miss0[:q], miss0[q:]
+            assert [rc.key for rc in recs] == gpu + cpu
+            for pos, (rc, kk) in enumerate(zip(recs, gpu)):
+                hit, slot, victim = tb.access(kk)
+                assert (rc.hit, rc.slot, rc.victim, rc.wave) == (int(hit), slot, victim, pos // S)
+            for rc in recs[len(gpu):]:
+                assert (rc.hit, rc.slot, rc.victim, rc.wave) == (0, -1, -1, -1)
+                assert rc.key not in tb.od  # never cached
+            assert sum(len(w) for w in waves) == len(gpu)
+    assert filled == g * missed // (g + c)
+
+
+def test_split_all_cpu_never_fills():
+    sim = oracle.SharedLRU(4, 0, 1)
+    for step in range(10):
+        _, recs = sim.resolve(step, 0, 8, [1, 3, 5])
+        assert all(rc.slot == -1 and rc.hit == 0 for rc in recs)
+    assert sim.key_slot == {}
+
+
+def test_split_cpu_misses_leave_cache_untouched():
+    """Replaying only the GPU-bound experts through an unsplit simulator gives the same GPU records."""
+    r = np.random.default_rng(5)
+    sim = oracle.SharedLRU(6, 1, 2)
+    plain = oracle.SharedLRU(6)
+    for step in range(80):
+        experts = sorted(r.choice(20, size=int(r.integers(1, 9)), replace=False).tolist())
+        _, recs = sim.resolve(step, 0, 20, experts)
+        gpu = [rc for rc in recs if rc.slot >= 0]
+        _, recs2 = plain.resolve(step, 0, 20, sorted(rc.key for rc in gpu))
+        assert [(rc.key, rc.hit, rc.slot, rc.victim, rc.wave) for rc in gpu] == \
+            [(rc.key, rc.hit, rc.slot, rc.victim, rc.wave) for rc in recs2]
