@@ -278,29 +278,44 @@ def bench_decode_layers(args, torch, L, gen, cfg, warm, steps):
                 bias[(l, ep)] = gen.router_bias(cfg, l, st, dev)
             return bias[(l, ep)]
 
-        dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
         s = torch.cuda.current_stream()
-        for st in range(warm):
-            for l in range(cfg.L):
-                dl.step(st, l, xs[st][l], Wrs[l], b(l, st), s)
-        torch.cuda.synchronize()
-        f0 = dl.n_fills
-        L.moe_decoder_profile(dl.dec, 8)
-        t0 = time.perf_counter()
-        for st in range(warm, n):
-            for l in range(cfg.L):
-                dl.step(st, l, xs[st][l], Wrs[l], b(l, st), s)
-        torch.cuda.synchronize()
-        el = time.perf_counter() - t0
-        fb, fms, fn = L.moe_decoder_ffn_stats(dl.dec)
-        tr = dl.trace()
-        timed = tr[tr[:, 0] >= warm]
-        gbs = fb / (fms * 1e-3) / 1e9
-        return dict(workload=cfg.name, layers=cfg.L, tokens_per_step=cfg.T, steps_timed=steps, steps_warmup=warm,
-                    tokens_per_s=steps * cfg.T / el, ms_per_step=el * 1e3 / steps,
-                    ms_per_layer_step=el * 1e3 / (steps * cfg.L), ffn_gbs=gbs, ffn_hbm_frac=gbs / HBM_PEAK_GBS,
-                    ffn_us_per_call=fms * 1e3 / max(fn, 1), hit_rate=float(timed[:, 3].mean()),
-                    fills_timed=dl.n_fills - f0, weight_sets=store.P)
+
+        def run(split):
+            dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+            rates = None
+            if split:
+                rates = [int(r) for r in dl.measure_rates()]
+                dl.set_split(*rates)
+            for st in range(warm):
+                for l in range(cfg.L):
+                    dl.step(st, l, xs[st][l], Wrs[l], b(l, st), s)
+            torch.cuda.synchronize()
+            f0, c0 = dl.n_fills, dl.cpu_runs
+            L.moe_decoder_profile(dl.dec, 8)
+            t0 = time.perf_counter()
+            for st in range(warm, n):
+                for l in range(cfg.L):
+                    dl.step(st, l, xs[st][l], Wrs[l], b(l, st), s)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            fb, fms, fn = L.moe_decoder_ffn_stats(dl.dec)
+            tr = dl.trace()
+            timed = tr[tr[:, 0] >= warm]
+            gbs = fb / (fms * 1e-3) / 1e9
+            return dict(tokens_per_s=steps * cfg.T / el, ms_per_step=el * 1e3 / steps,
+                        ms_per_layer_step=el * 1e3 / (steps * cfg.L), ffn_gbs=gbs, ffn_hbm_frac=gbs / HBM_PEAK_GBS,
+                        ffn_us_per_call=fms * 1e3 / max(fn, 1), hit_rate=float(timed[:, 3].mean()),
+                        fills_timed=dl.n_fills - f0, cpu_runs_timed=dl.cpu_runs - c0,
+                        split_rates_mbs=rates)
+
+        res = dict(workload=cfg.name, layers=cfg.L, tokens_per_step=cfg.T, steps_timed=steps, steps_warmup=warm,
+                   weight_sets=store.P)
+        res.update(run(False))
+        if cfg.wfmt == "bf16" and cfg.act == "bf16":
+            # the pages' adaptive misses: the share rate_fill / (rate_fill + rate_cpu) of misses is filled,
+            # the rest runs on the host CPU from the pool (rates measured here)
+            res["cpu_split"] = run(True)
+        return res
     finally:
         store.close()
 

@@ -124,7 +124,9 @@ int moe_route(const void* x, int dtype, const void* Wr, const float* bias,
  *   blob: device out, moe_expert_bytes() bytes; the caller may then copy it
  *   into a pool or a cache slot.
  * moe_pool_alloc: page-locked host memory (hipHostMalloc) for the pool;
- *   returns NULL and sets *status on failure. Free with moe_pool_free.
+ *   returns NULL and sets *status on failure. Free with moe_pool_free. Every
+ *   page is read once by the host threads before returning, so that CPU
+ *   execution from the pool (moe_cpu_ffn) does not pay a first-touch cost.
  * ------------------------------------------------------------------------ */
 size_t moe_expert_bytes(int wfmt, int H, int I);
 int moe_pack_expert(int wfmt, int H, int I, const void* W1, const void* W3, const void* W2,
@@ -308,6 +310,10 @@ int moe_pipe_copy_ms(moe_pipe_t* pipe, int layer, float* ms);
  *   out_dtype; *n_miss (nullable) = fills issued. Blocks the calling thread
  *   until the counts reach the host; the rest is enqueued on `stream`.
  *   On a failed fill the affected keys are invalidated (never half-resident).
+ *   When the cache splits misses (moe_cache_set_split), the misses assigned
+ *   to the CPU run with moe_cpu_ffn from the pool on the calling thread while
+ *   the GPU works on the others (bf16 activations and weights only, else
+ *   MOE_EINVAL); their rows of y_perm are copied in before the combine.
  * moe_decoder_profile: every > 0 brackets every every-th FFN call (the first,
  *   then each every-th after it) with HIP events on `stream`; 0 turns it off;
  *   negative is EINVAL. moe_decoder_ffn_stats returns, over the bracketed
@@ -315,6 +321,7 @@ int moe_pipe_copy_ms(moe_pipe_t* pipe, int layer, float* ms);
  *   blobs read + activations read/written), the summed milliseconds and the
  *   number of bracketed calls.
  * moe_decoder_fills: total fills issued by this decoder.
+ * moe_decoder_cpu_runs: total misses this decoder ran on the CPU.
  * ------------------------------------------------------------------------ */
 typedef struct moe_decoder moe_decoder_t;
 typedef struct {
@@ -342,6 +349,7 @@ int moe_decoder_step(moe_decoder_t* decoder, int step, int layer, const void* x,
 int moe_decoder_profile(moe_decoder_t* decoder, int every);
 int moe_decoder_ffn_stats(moe_decoder_t* decoder, double* bytes, double* ms, int64_t* launches);
 int moe_decoder_fills(const moe_decoder_t* decoder, int64_t* fills);
+int moe_decoder_cpu_runs(const moe_decoder_t* decoder, int64_t* runs);
 
 /* ---------------------------------------------------------------------------
  * CPU execution of an expert (page "FreeToken-rtx-4090", component table row

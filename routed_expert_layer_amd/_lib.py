@@ -25,7 +25,7 @@ SYMBOLS = [
     "cache_fill_async", "moe_ffn_workspace_size", "moe_ffn", "moe_combine", "moe_pipe_create", "moe_pipe_destroy",
     "moe_pipe_begin_layer", "moe_pipe_end_layer", "moe_pipe_copy_ms", "moe_decoder_create", "moe_decoder_destroy",
     "moe_decoder_step", "moe_decoder_profile", "moe_decoder_ffn_stats", "moe_decoder_fills",
-    "moe_cpu_ffn", "moe_cpu_threads", "moe_cache_set_split",
+    "moe_cpu_ffn", "moe_cpu_threads", "moe_cache_set_split", "moe_decoder_cpu_runs",
 ]
 
 
@@ -93,6 +93,7 @@ _sig("moe_decoder_profile", I32, P, I32)
 _sig("moe_cpu_ffn", I32, P, I32, I32, I32, P, I32, P, I32)
 _sig("moe_cpu_threads", I32)
 _sig("moe_cache_set_split", I32, P, I32, I32)
+_sig("moe_decoder_cpu_runs", I32, P, ctypes.POINTER(ctypes.c_int64))
 _sig("moe_decoder_ffn_stats", I32, P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), PI64)
 _sig("moe_decoder_fills", I32, P, PI64)
 
@@ -397,3 +398,9 @@ def moe_cpu_threads():
 def moe_cache_set_split(cache, rate_gpu, rate_cpu):
     """Share of misses filled = rate_gpu / (rate_gpu + rate_cpu); the rest run on the CPU (rate_cpu = 0: all filled)."""
     _check(_lib.moe_cache_set_split(cache.h, int(rate_gpu), int(rate_cpu)), "moe_cache_set_split")
+
+
+def moe_decoder_cpu_runs(dec):
+    n = ctypes.c_int64(0)
+    _check(_lib.moe_decoder_cpu_runs(dec.h, ctypes.byref(n)), "moe_decoder_cpu_runs")
+    return n.value

@@ -140,6 +140,7 @@ void* moe_pool_alloc(size_t bytes, int* status) {
     if (status) *status = fail(MOE_ENOMEM, "moe_pool_alloc(%zu): %s", bytes, hipGetErrorString(e));
     return nullptr;
   }
+  moe::cpu_touch_pages(p, bytes);  // CPU execution from the pool pays no first-touch cost later
   if (status) *status = MOE_OK;
   return p;
 }

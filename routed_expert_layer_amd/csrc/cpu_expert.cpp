@@ -187,3 +187,22 @@ int moe_cpu_ffn(const void* blob, int wfmt, int H, int I, const void* x, int row
 int moe_cpu_threads(void) { return pool().workers() + 1; }
 
 }  // extern "C"
+
+namespace moe {
+
+// Reads one byte of every 4 KiB page of [p, p + bytes) on all pool threads.
+// Pinned memory that only the GPU has written pays a large cost on the CPU's
+// first read of each page (measured: ~10x slower than later reads), which
+// would otherwise land on the first CPU execution of every expert.
+void cpu_touch_pages(const void* p, size_t bytes) {
+  const volatile char* c = static_cast<const volatile char*>(p);
+  const size_t pages = (bytes + 4095) / 4096;
+  std::atomic<unsigned> sink{0};
+  pool().run(pool().workers() + 1, [&](int id, int n) {
+    unsigned acc = 0;
+    for (size_t i = pages * id / n; i < pages * (id + 1) / n; ++i) acc += (unsigned char)c[i * 4096];
+    sink.fetch_add(acc, std::memory_order_relaxed);
+  });
+}
+
+}  // namespace moe

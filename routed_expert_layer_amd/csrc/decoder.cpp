@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cstring>
 #include <new>
 #include <string>
 #include <vector>
@@ -18,6 +19,7 @@
 extern "C" const char* moe_last_error(void);
 int moe_cache_layers(const moe_cache_t* c, int* n_layers);
 int moe_cache_experts(const moe_cache_t* c);
+bool moe_cache_splits(const moe_cache_t* c);
 
 namespace {
 // Errors go to the library's per-thread message (moe_last_error).
@@ -49,12 +51,23 @@ struct moe_decoder {
   std::vector<double> ev_bytes;
   size_t ev_used = 0;
   int64_t fills = 0;
+  // CPU execution of misses (when the cache splits them): pinned copies of
+  // the step's activations and token order, and the CPU results on their way
+  // into y_perm
+  uint16_t* x_host = nullptr;
+  int32_t* perm_host = nullptr;
+  float* y_host = nullptr;
+  std::vector<uint16_t> xg;
+  int64_t cpu_runs = 0;
 };
 
 extern "C" {
 
 static void decoder_release(moe_decoder_t* d) {
   if (d->counts_host) (void)hipHostFree(d->counts_host);
+  if (d->x_host) (void)hipHostFree(d->x_host);
+  if (d->perm_host) (void)hipHostFree(d->perm_host);
+  if (d->y_host) (void)hipHostFree(d->y_host);
   if (d->fill) (void)hipStreamDestroy(d->fill);
   if (d->ev_counts) (void)hipEventDestroy(d->ev_counts);
   for (hipEvent_t e : d->ev_begin) (void)hipEventDestroy(e);
@@ -157,6 +170,26 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   hipError_t e = moe::launch_route(x, d->dtype == MOE_DT_BF16, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w,
                                    b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s,
                                    d->counts_dev);
+  const bool split = moe_cache_splits(d->cache);
+  if (split && e == hipSuccess) {
+    // misses may run on the CPU: it needs this step's activations and token order
+    if (d->dtype != MOE_DT_BF16 || d->wfmt != MOE_W_BF16)
+      return dfail(MOE_EINVAL, "moe_decoder_step: CPU execution of misses needs bf16 activations and weights");
+    if (!d->x_host) {
+      e = hipHostMalloc(reinterpret_cast<void**>(&d->x_host), sizeof(uint16_t) * d->Tmax * d->H, hipHostMallocDefault);
+      if (e == hipSuccess)
+        e = hipHostMalloc(reinterpret_cast<void**>(&d->perm_host), sizeof(int32_t) * d->Tmax * d->k,
+                          hipHostMallocDefault);
+      if (e == hipSuccess)
+        e = hipHostMalloc(reinterpret_cast<void**>(&d->y_host), sizeof(float) * d->Tmax * d->k * d->H,
+                          hipHostMallocDefault);
+      d->xg.resize((size_t)d->Tmax * d->H);
+    }
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(d->x_host, x, sizeof(uint16_t) * T * d->H, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(d->perm_host, b.perm_src, sizeof(int32_t) * T * d->k, hipMemcpyDeviceToHost, s);
+  }
   if (e == hipSuccess) e = hipEventRecord(d->ev_counts, s);
   if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: routing: %s", hipGetErrorString(e));
   int rc;
@@ -218,6 +251,22 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
       if (record_ffn_event(d, false, s, bytes) != MOE_OK) return dfail(MOE_EHIP, "moe_decoder_step: profiling event");
     }
   }
+  // misses run on the CPU, straight from the pool, while the GPU works on the
+  // rest; their rows of y_perm follow on the compute stream before the combine
+  for (int i = 0; i < n; ++i) {
+    if (d->work_slot[i] >= 0) continue;
+    const int ex = d->work_e[i], rows = d->counts_host[ex], r0 = d->offs[ex];
+    for (int r = 0; r < rows; ++r)
+      std::memcpy(d->xg.data() + (size_t)r * d->H, d->x_host + (size_t)d->perm_host[r0 + r] * d->H,
+                  sizeof(uint16_t) * d->H);
+    const char* blob = static_cast<const char*>(d->layer_pool[layer]) + (size_t)ex * d->blob_stride;
+    rc = moe_cpu_ffn(blob, d->wfmt, d->H, d->I, d->xg.data(), rows, d->y_host + (size_t)r0 * d->H, 0);
+    if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
+    e = hipMemcpyAsync(b.y_perm + (size_t)r0 * d->H, d->y_host + (size_t)r0 * d->H, sizeof(float) * rows * d->H,
+                       hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: CPU rows to the GPU: %s", hipGetErrorString(e));
+    ++d->cpu_runs;
+  }
   rc = moe_combine(b.y_perm, b.perm_pos, b.topk_w, T, d->k, d->H, out, out_dtype, stream);
   if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
   if (n_miss) *n_miss = nm;
@@ -252,6 +301,12 @@ int moe_decoder_ffn_stats(moe_decoder_t* d, double* bytes, double* ms, int64_t* 
 int moe_decoder_fills(const moe_decoder_t* d, int64_t* fills) {
   if (!d || !fills) return dfail(MOE_EINVAL, "moe_decoder_fills: null argument");
   *fills = d->fills;
+  return MOE_OK;
+}
+
+int moe_decoder_cpu_runs(const moe_decoder_t* d, int64_t* runs) {
+  if (!d || !runs) return dfail(MOE_EINVAL, "moe_decoder_cpu_runs: null argument");
+  *runs = d->cpu_runs;
   return MOE_OK;
 }
 

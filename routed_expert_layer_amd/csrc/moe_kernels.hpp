@@ -125,6 +125,9 @@ int router_gemm2_splits(int T, int H, int E);
 hipError_t launch_router_gemm2(const void* x, const void* wrt, int T, int H, int E, float* partial, int nsplit,
                                hipStream_t s);
 
+// Host: reads one byte per page of a pool region on the CPU thread pool.
+void cpu_touch_pages(const void* p, size_t bytes);
+
 // Sets the calling thread's moe_last_error() message; returns `code`.
 int set_error(int code, const char* fmt, ...);
 

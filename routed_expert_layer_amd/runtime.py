@@ -14,6 +14,8 @@ computes (phase table, row "Prefill").
 """
 import ctypes
 
+import time
+
 import numpy as np
 import torch
 
@@ -158,6 +160,45 @@ class DecodeLayer:
     @property
     def n_fills(self):
         return L.moe_decoder_fills(self.dec) if self.dec is not None else self._fills
+
+    @property
+    def cpu_runs(self):
+        """Misses executed on the CPU so far."""
+        return L.moe_decoder_cpu_runs(self.dec) if self.dec is not None else 0
+
+    def set_split(self, rate_gpu, rate_cpu):
+        """Divide misses between GPU fills and CPU execution in the ratio of the rates (e.g. MB/s of pinned
+        fills and of the host expert kernel, see measure_rates); rate_cpu = 0 fills every miss."""
+        if rate_cpu and self.dec is None:
+            raise ValueError("CPU execution of misses runs in the native decode driver (native=True)")
+        L.moe_cache_set_split(self.cache, rate_gpu, rate_cpu)
+
+    def measure_rates(self, layer=0, n=4, rows=None):
+        """(fill MB/s, CPU expert MB/s) on this machine: n pinned blobs of `layer` copied to a scratch device
+        buffer on the fill stream, and the host expert kernel on the same blobs with `rows` token rows."""
+        store = self.store
+        n = min(n, store.E)
+        tmp = torch.empty(n * store.stride, dtype=torch.uint8, device=self.slots.device)
+        misses = [[layer * store.E + e, e, -1, 0] for e in range(n)]
+        fs = self.fill_stream
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(fs)
+        L.cache_fill_async(self.cache, misses, store.layer_ptrs, store.stride, store.blob, tmp, store.stride, fs, fs)
+        e1.record(fs)
+        torch.cuda.synchronize()
+        fill_mbs = n * store.blob / (e0.elapsed_time(e1) * 1e-3) / 1e6
+        del tmp
+        rows = rows or self.rb.T
+        x = torch.randn(rows, self.H).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        y = np.empty((rows, self.H), np.float32)
+        base = int(store.layer_ptrs[layer])
+        L.moe_cpu_ffn(base, store.wfmt, self.H, self.I, x, y)  # warm the thread pool
+        t0 = time.perf_counter()
+        for e in range(n):
+            L.moe_cpu_ffn(base + e * store.stride, store.wfmt, self.H, self.I, x, y)
+        cpu_mbs = n * store.blob / (time.perf_counter() - t0) / 1e6
+        return fill_mbs, cpu_mbs
 
     def algorithmic_bytes(self, work):
         """Bytes the expert FFN must move for a work list: each listed expert's

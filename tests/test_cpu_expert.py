@@ -6,8 +6,8 @@ import pytest
 import torch
 
 import oracle
-from blob_layout import bf16_bits, bf16_blob
-from parity import check_close
+from tests.blob_layout import bf16_bits, bf16_blob
+from tests.parity import check_close
 from workloads import gen
 import dataclasses
 

@@ -194,3 +194,16 @@ def test_combine_parity(L, T, k, H, out_bf16):
         check_close(np64(out), ref, "combine bf16", rel_l2=4e-3)
     else:
         check_close(np64(out), ref, "combine", rel_l2=1e-6, max_abs_rms=1e-5)
+
+
+@pytest.mark.gpu
+def test_pack_matches_documented_layout(L):
+    """The GPU packer writes, byte for byte, the blob layout the host expert kernel reads."""
+    from tests.blob_layout import bf16_blob
+    cfg = dataclasses.replace(CONFIGS["decode_bf16_h4096_e256"], name="packlayout", H=512, I=384)
+    W1, W3, W2 = gen.expert_weights(cfg, 0, 2, "cuda")
+    blob = torch.empty(L.moe_expert_bytes(L.MOE_W_BF16, cfg.H, cfg.I), dtype=torch.uint8, device="cuda")
+    L.moe_pack_expert(L.MOE_W_BF16, cfg.H, cfg.I, W1, W3, W2, None, None, None, blob)
+    torch.cuda.synchronize()
+    ref = bf16_blob(W1.cpu(), W3.cpu(), W2.cpu())
+    assert np.array_equal(blob.cpu().numpy().view(np.uint16), ref)

@@ -63,19 +63,26 @@ def make_store(cfg):
     return store
 
 
-def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True):
+def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, split=None, cpu_check=(0, ())):
     """Drive DecodeLayer over `steps` x all layers; check routing, trace, and sampled outputs.
 
     native=True runs each layer-step through the library's decode driver
     (moe_decoder_step); native=False sequences the individual C-ABI calls from
-    Python."""
+    Python. split=(rate_gpu, rate_cpu) divides misses between GPU fills and CPU
+    execution; cpu_check=(n, layers) also checks the outputs of the first n
+    layer-steps of those layers in which some miss ran on the CPU."""
     from routed_expert_layer_amd.runtime import DecodeLayer
-    print(f"decode {cfg.name}: L={cfg.L} T={cfg.T} steps={steps} S={cfg.S} {cfg.wfmt} native={native}", flush=True)
+    print(f"decode {cfg.name}: L={cfg.L} T={cfg.T} steps={steps} S={cfg.S} {cfg.wfmt} native={native} "
+          f"split={split}", flush=True)
     store = make_store(cfg)
     try:
         dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev, keep_logits=True, native=native)
         Wr = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
         sim = oracle.SharedLRU(cfg.S)
+        if split:
+            dl.set_split(*split)
+            sim.set_split(*split)
+        cpu_left, cpu_layers = cpu_check
         experts64 = {}
         for step in range(steps):
             for layer in range(cfg.L):
@@ -89,8 +96,11 @@ def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True):
                 counts, _, _, _ = check_permutation(idx, npi(dl.rb.counts), npi(dl.rb.offsets),
                                                     npi(dl.rb.perm_src[:cfg.T * cfg.k]), npi(dl.rb.perm_pos[:cfg.T]),
                                                     cfg.E)
-                sim.resolve(step, layer, cfg.E, np.nonzero(counts)[0])
-                if check_all_outputs or (step, layer) in out_check:
+                _, recs = sim.resolve(step, layer, cfg.E, np.nonzero(counts)[0])
+                on_cpu = any(rc.slot < 0 for rc in recs)
+                check_cpu = on_cpu and cpu_left > 0 and layer in cpu_layers
+                cpu_left -= int(check_cpu)
+                if check_all_outputs or (step, layer) in out_check or check_cpu:
                     ge = experts64.setdefault(layer, ExpertCache64(cfg, layer))
                     ref = oracle_out_rows(np64(x), idx, l64, list(range(cfg.T)), ge)
                     check_close(np64(out), ref, f"{cfg.name} step {step} layer {layer}")
@@ -98,10 +108,13 @@ def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True):
         ref = np.array([[r.step, r.layer, r.key, r.hit, r.slot, r.victim, r.wave] for r in sim.trace], np.int64)
         assert trace.shape == ref.shape, f"trace length {trace.shape} vs {ref.shape}"
         assert np.array_equal(trace, ref), "cache trace differs from the oracle's LRU"
-        hits, misses = int(ref[:, 3].sum()), int((1 - ref[:, 3]).sum())
+        hits = int(ref[:, 3].sum())
+        cpu = int((ref[:, 4] < 0).sum())
         print(f"  trace ok: {len(ref)} accesses, hit rate {hits / max(len(ref), 1):.3f}, fills {dl.n_fills}, "
-              f"waves>1 in {int((ref[:, 6] > 0).sum())} accesses", flush=True)
-        assert dl.n_fills == misses
+              f"cpu runs {dl.cpu_runs}, waves>1 in {int((ref[:, 6] > 0).sum())} accesses", flush=True)
+        assert dl.n_fills == len(ref) - hits - cpu
+        assert dl.cpu_runs == cpu
+        assert cpu_left <= 0 or not cpu_layers, "no CPU-run layer-step was output-checked"
         return ref
     finally:
         store.close()
@@ -132,6 +145,22 @@ def test_stack48_bf16_cut():
 def test_decode_int4_cut():
     cfg = CONFIGS["decode_int4_t8_l8"]
     run_decode(cfg, 48, {(0, 0), (5, 3), (47, 7)})
+
+
+@pytest.mark.timeout(600)
+def test_split_small_all_outputs():
+    """Misses divided 1:3 between GPU fills and CPU execution; every output checked."""
+    cfg = dataclasses.replace(CONFIGS["decode_bf16_h4096_e256"], name="split_small", L=3, T=4, H=512, I=256, E=32,
+                              k=4, zipf_s=1.0, S=8)
+    ref = run_decode(cfg, 24, set(), check_all_outputs=True, split=(1, 3))
+    assert (ref[:, 4] < 0).sum() > 10 and (ref[:, 3] == 0).sum() > (ref[:, 4] < 0).sum()
+
+
+@pytest.mark.timeout(600)
+def test_stack48_split_cut():
+    """The 48-layer stack with misses divided in the ratio of a measured fill and CPU rate (56 : 165 GB/s)."""
+    cfg = CONFIGS["stack48_bf16_h2048_e128"]
+    run_decode(cfg, 10, {(9, 47)}, split=(56, 165), cpu_check=(4, (0, 1, 2)))
 
 
 def _prefill_check(cfg, layer, pl, x, Wr, b, n_sample=24):
