@@ -149,6 +149,31 @@ def bench_decode(args, torch, L, gen, cfg):
     timed = trace[trace[:, 0] >= args.warmup]
     hit_rate = float(timed[:, 3].mean()) if len(timed) else 0.0
 
+    # the pages' adaptive misses on the same workload: misses divided between fills and CPU execution in the
+    # ratio of the measured fill and CPU rates (reported beside the all-fills run above)
+    dl2 = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+    rates = [int(r) for r in dl2.measure_rates()]
+    dl2.set_split(*rates)
+    for step in range(args.warmup):
+        dl2.step(step, 0, xs[step], Wr, bias(step), s)
+    torch.cuda.synchronize()
+    f2, c2 = dl2.n_fills, dl2.cpu_runs
+    lat2 = []
+    t2 = prev = time.perf_counter()
+    for step in range(args.warmup, n_total):
+        dl2.step(step, 0, xs[step], Wr, bias(step), s)
+        now = time.perf_counter()
+        lat2.append(now - prev)
+        prev = now
+    torch.cuda.synchronize()
+    el2 = time.perf_counter() - t2
+    tr2 = dl2.trace()
+    tm2 = tr2[tr2[:, 0] >= args.warmup]
+    split = dict(tokens_per_s=args.steps * cfg.T / el2, ms_per_step=el2 * 1e3 / args.steps,
+                 step_ms_p50=percentile(lat2, 50) * 1e3, hit_rate=float(tm2[:, 3].mean()) if len(tm2) else 0.0,
+                 fills_timed=dl2.n_fills - f2, cpu_runs_timed=dl2.cpu_runs - c2, split_rates_mbs=rates)
+    del dl2
+
     # pinned host -> HBM fill bandwidth: blobs copied on the fill stream
     fs = dl.fill_stream
     n_copy = min(16, cfg.S)
@@ -168,7 +193,7 @@ def bench_decode(args, torch, L, gen, cfg):
         decode=dict(step_ms_p50=percentile(lat, 50) * 1e3, step_ms_p99=percentile(lat, 99) * 1e3,
                     step_ms_max=max(lat) * 1e3, hit_rate=hit_rate, fills_timed=dl.n_fills - fills0,
                     fills_warmup=fills0, fill_gbs=fill_gbs, fill_frac_pcie=fill_gbs / PCIE_PEAK_GBS,
-                    pool_gb=store.nbytes / 1e9, slots=cfg.S),
+                    pool_gb=store.nbytes / 1e9, slots=cfg.S, cpu_split=split),
     )
 
 
