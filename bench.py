@@ -105,6 +105,61 @@ def percentile(xs, p):
     return xs[i]
 
 
+def bench_device(torch, cfg, store, Wrs, warm, steps, x_of, b_of):
+    """Device-controlled decode (cache control in GPU memory, moe_device_decoder_step): every step is enqueued
+    with no host synchronisation, eagerly and as replays of one graph holding all layers of a token step. The
+    inputs of all steps are staged in HBM first; each step copies its x (and, when the epoch changes, the
+    biases) into the static buffers the graph reads, on the same stream."""
+    from routed_expert_layer_amd.runtime import DeviceDecodeLayer
+    dev = "cuda"
+    n = warm + steps
+    x_all = torch.stack([torch.stack([x_of(st, l) for l in range(cfg.L)]) for st in range(n)])
+    epoch = cfg.epoch or (n + 1)
+    b_all = {ep: torch.stack([b_of(l, ep * epoch) for l in range(cfg.L)]) for ep in sorted({st // epoch
+                                                                                           for st in range(n)})}
+    cs = torch.cuda.Stream()
+
+    def one(graph):
+        dl = DeviceDecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+        xs = torch.empty_like(x_all[0])
+        bs = torch.empty_like(next(iter(b_all.values())))
+        outs = torch.empty((cfg.L, cfg.T, cfg.H), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+        def enqueue():
+            for l in range(cfg.L):
+                dl.step(l, xs[l], Wrs[l], bs[l], cs, out=outs[l])
+
+        g = DeviceDecodeLayer.capture(enqueue, cs) if graph else None
+
+        def run_steps(a, b):
+            ep_prev = None
+            with torch.cuda.stream(cs):
+                for st in range(a, b):
+                    xs.copy_(x_all[st], non_blocking=True)
+                    if st // epoch != ep_prev:
+                        ep_prev = st // epoch
+                        bs.copy_(b_all[ep_prev], non_blocking=True)
+                    if g is not None:
+                        DeviceDecodeLayer.replay(g, cs)
+                    else:
+                        enqueue()
+
+        run_steps(0, warm)
+        h0, m0, _ = dl.stats()
+        t0 = time.perf_counter()
+        run_steps(warm, n)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        h1, m1, _ = dl.stats()
+        if g is not None:
+            g.close()
+        return dict(tokens_per_s=steps * cfg.T / el, ms_per_step=el * 1e3 / steps,
+                    hit_rate=(h1 - h0) / max(h1 - h0 + m1 - m0, 1), fills_timed=m1 - m0)
+
+    return dict(eager=one(False), graph=one(True))
+
+
 def bench_decode(args, torch, L, gen, cfg):
     from routed_expert_layer_amd.runtime import DecodeLayer, ExpertStore
     dev = "cuda"
@@ -174,6 +229,10 @@ def bench_decode(args, torch, L, gen, cfg):
                  fills_timed=dl2.n_fills - f2, cpu_runs_timed=dl2.cpu_runs - c2, split_rates_mbs=rates)
     del dl2
 
+    # the same workload with the cache control in GPU memory (no host round trip per step)
+    device = bench_device(torch, cfg, store, [Wr], args.warmup, args.steps, lambda st, l: xs[st],
+                          lambda l, st: bias(st))
+
     # pinned host -> HBM fill bandwidth: blobs copied on the fill stream
     fs = dl.fill_stream
     n_copy = min(16, cfg.S)
@@ -193,7 +252,7 @@ def bench_decode(args, torch, L, gen, cfg):
         decode=dict(step_ms_p50=percentile(lat, 50) * 1e3, step_ms_p99=percentile(lat, 99) * 1e3,
                     step_ms_max=max(lat) * 1e3, hit_rate=hit_rate, fills_timed=dl.n_fills - fills0,
                     fills_warmup=fills0, fill_gbs=fill_gbs, fill_frac_pcie=fill_gbs / PCIE_PEAK_GBS,
-                    pool_gb=store.nbytes / 1e9, slots=cfg.S, cpu_split=split),
+                    pool_gb=store.nbytes / 1e9, slots=cfg.S, cpu_split=split, device_control=device),
     )
 
 
@@ -336,6 +395,7 @@ def bench_decode_layers(args, torch, L, gen, cfg, warm, steps):
         res = dict(workload=cfg.name, layers=cfg.L, tokens_per_step=cfg.T, steps_timed=steps, steps_warmup=warm,
                    weight_sets=store.P)
         res.update(run(False))
+        res["device_control"] = bench_device(torch, cfg, store, Wrs, warm, steps, lambda st, l: xs[st][l], b)
         if cfg.wfmt == "bf16" and cfg.act == "bf16":
             # the pages' adaptive misses: the share rate_fill / (rate_fill + rate_cpu) of misses is filled,
             # the rest runs on the host CPU from the pool (rates measured here)
@@ -439,11 +499,13 @@ def main():
                      "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
                      "algorithmic_bytes_per_launch": round(ffn["bytes"] / max(ffn["n"], 1)),
                      "avg_launch_us": round(ffn["ms"] * 1e3 / max(ffn["n"], 1), 2), "launches": ffn["n"]},
-        "decode": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res["decode"].items()},
     }
-    def rnd(d):
-        return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
 
+    def rnd(d):
+        return {k: (round(v, 4) if isinstance(v, float) else rnd(v) if isinstance(v, dict) else v)
+                for k, v in d.items()}
+
+    out["decode"] = rnd(res["decode"])
     if not args.no_prefill:
         out["prefill"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_bf16_t4096_e256"]))
         out["prefill_double_buffered"] = rnd(bench_prefill_pipeline(args, torch, L, gen,

@@ -373,6 +373,79 @@ int moe_decoder_cpu_runs(const moe_decoder_t* decoder, int64_t* runs);
 int moe_cpu_ffn(const void* blob, int wfmt, int H, int I, const void* x, int rows, float* y, int threads);
 int moe_cpu_threads(void);
 
+/* ---------------------------------------------------------------------------
+ * Device-controlled decode layer-step and graph capture.
+ *
+ * Page "FreeToken-benchmark", section "Graph Compatibility": routing-dependent
+ * decisions are kept in device-resident control data so that the decode step
+ * can run as captured, replayable GPU work. Here every decision of the step
+ * (which experts, hit or miss, which slot, which victim) is made by kernels
+ * from tables in GPU memory; the host only enqueues.
+ *
+ * moe_device_decoder_create: an L-layer cache of S slots with the policy of
+ *   cache_resolve (hits ascending, then misses ascending; lowest free slot,
+ *   else least recently used), its state held in GPU memory (allocated and
+ *   owned by the decoder; the cache starts empty). Every miss is filled (there
+ *   is no CPU execution on this path). Requires S >= min(E, k*T_max), so that
+ *   a layer-step's experts always fit the cache at once (one wave), and
+ *   E <= 1024. layer_pool: the L per-layer base addresses of moe_pool_alloc
+ *   memory (host; layers may share a base), read by the fill kernel over the
+ *   host link. slot_base/slot_stride, buffers and the other arguments as for
+ *   moe_decoder_create (the decoder never frees them). trace_capacity: number
+ *   of trace records kept in GPU memory (0: none).
+ *   Errors: EINVAL (null, bad sizes, pool address not from moe_pool_alloc),
+ *   ECAPACITY (S too small), ENOMEM (device memory), EHIP.
+ * moe_device_decoder_step: enqueues one layer-step on `stream`: routing (as
+ *   moe_route), the resolve kernel (one workgroup, updates the tables and
+ *   writes the work list and misses to GPU memory), the fill kernel (copies
+ *   the misses' blobs from the pool into their slots; returns at once when
+ *   there are none), the decode expert FFN over the device work list (fixed
+ *   grid for min(E, k*T) items; surplus blocks exit) and the combine into
+ *   `out`. It neither waits for the GPU nor allocates, so the same call can be
+ *   captured with moe_graph_begin/moe_graph_end and replayed: a replay reads
+ *   whatever x, Wr and bias hold at that time. Launch shapes depend only on
+ *   T, so a graph is tied to the T (and layer and buffers) it was captured
+ *   with. Steps on one decoder must run in stream order (one stream, or
+ *   explicit ordering). Errors: EINVAL (null, T or layer out of range), EHIP.
+ * moe_device_decoder_stats: total hits, misses (= fills) and resolve calls.
+ * moe_device_decoder_trace: copies up to max_records trace records (the
+ *   first trace_capacity accesses since the last clear, access order) and
+ *   sets *n_records to the number of accesses traced since then (may exceed
+ *   the capacity). Records are as moe_trace_t with step = the sequence number
+ *   of the resolve call that made them (0, 1, ... from creation) and wave 0.
+ * moe_device_decoder_clear_trace, moe_device_decoder_slot_of: as for the host
+ *   cache. stats, trace and slot_of read GPU memory with blocking copies: call
+ *   them once the stream's steps have completed.
+ *
+ * moe_graph_begin(stream): starts capturing `stream` (a created stream, not
+ *   the default one; thread-local capture mode). moe_graph_end(stream): ends
+ *   the capture and instantiates it. moe_graph_launch: replays the graph on a
+ *   stream. moe_graph_destroy frees it. Errors: EINVAL, EHIP (for example a
+ *   call that is not allowed during capture).
+ * ------------------------------------------------------------------------- */
+typedef struct moe_device_decoder moe_device_decoder_t;
+typedef struct moe_graph moe_graph_t;
+
+moe_device_decoder_t* moe_device_decoder_create(int L, int E, int S, int T_max, int H, int I, int k, int dtype,
+                                                int wfmt, const void* const* layer_pool, size_t blob_stride,
+                                                void* slot_base, size_t slot_stride,
+                                                const moe_decoder_buffers_t* buffers, int64_t trace_capacity,
+                                                int* status);
+int moe_device_decoder_destroy(moe_device_decoder_t* decoder);
+int moe_device_decoder_step(moe_device_decoder_t* decoder, int layer, const void* x, int T, const void* Wr,
+                            const float* bias, void* out, int out_dtype, void* stream);
+int moe_device_decoder_stats(const moe_device_decoder_t* decoder, int64_t* hits, int64_t* misses,
+                             int64_t* resolves);
+int moe_device_decoder_trace(const moe_device_decoder_t* decoder, moe_trace_t* out, int64_t max_records,
+                             int64_t* n_records);
+int moe_device_decoder_clear_trace(moe_device_decoder_t* decoder);
+int moe_device_decoder_slot_of(const moe_device_decoder_t* decoder, int key, int* slot);
+
+int moe_graph_begin(void* stream);
+moe_graph_t* moe_graph_end(void* stream, int* status);
+int moe_graph_launch(moe_graph_t* graph, void* stream);
+int moe_graph_destroy(moe_graph_t* graph);
+
 #ifdef __cplusplus
 }
 #endif

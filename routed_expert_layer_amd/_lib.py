@@ -26,6 +26,9 @@ SYMBOLS = [
     "moe_pipe_begin_layer", "moe_pipe_end_layer", "moe_pipe_copy_ms", "moe_decoder_create", "moe_decoder_destroy",
     "moe_decoder_step", "moe_decoder_profile", "moe_decoder_ffn_stats", "moe_decoder_fills",
     "moe_cpu_ffn", "moe_cpu_threads", "moe_cache_set_split", "moe_decoder_cpu_runs",
+    "moe_device_decoder_create", "moe_device_decoder_destroy", "moe_device_decoder_step", "moe_device_decoder_stats",
+    "moe_device_decoder_trace", "moe_device_decoder_clear_trace", "moe_device_decoder_slot_of",
+    "moe_graph_begin", "moe_graph_end", "moe_graph_launch", "moe_graph_destroy",
 ]
 
 
@@ -96,6 +99,18 @@ _sig("moe_cache_set_split", I32, P, I32, I32)
 _sig("moe_decoder_cpu_runs", I32, P, ctypes.POINTER(ctypes.c_int64))
 _sig("moe_decoder_ffn_stats", I32, P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), PI64)
 _sig("moe_decoder_fills", I32, P, PI64)
+_sig("moe_device_decoder_create", P, I32, I32, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, SZ,
+     ctypes.POINTER(DecoderBuffers), I64, PI)
+_sig("moe_device_decoder_destroy", I32, P)
+_sig("moe_device_decoder_step", I32, P, I32, P, I32, P, P, P, I32, P)
+_sig("moe_device_decoder_stats", I32, P, PI64, PI64, PI64)
+_sig("moe_device_decoder_trace", I32, P, P, I64, PI64)
+_sig("moe_device_decoder_clear_trace", I32, P)
+_sig("moe_device_decoder_slot_of", I32, P, I32, PI)
+_sig("moe_graph_begin", I32, P)
+_sig("moe_graph_end", P, P, PI)
+_sig("moe_graph_launch", I32, P, P)
+_sig("moe_graph_destroy", I32, P)
 
 
 def _check(code, what=""):
@@ -404,3 +419,107 @@ def moe_decoder_cpu_runs(dec):
     n = ctypes.c_int64(0)
     _check(_lib.moe_decoder_cpu_runs(dec.h, ctypes.byref(n)), "moe_decoder_cpu_runs")
     return n.value
+
+
+# ---------------------------------------------------------------------------
+def _decoder_buffers(bufs):
+    b = DecoderBuffers()
+    for name in ("topk_idx", "topk_w", "logits", "counts", "offsets", "perm_src", "perm_pos", "y_perm"):
+        setattr(b, name, _ptr(bufs.get(name)))
+    b.route_ws, b.route_ws_bytes = _ptr(bufs["route_ws"]), bufs["route_ws"].numel()
+    b.ffn_ws, b.ffn_ws_bytes = _ptr(bufs["ffn_ws"]), bufs["ffn_ws"].numel()
+    return b
+
+
+class MoeDeviceDecoder:
+    """Owner of a moe_device_decoder_t; `bufs` as for MoeDecoder (kept alive here)."""
+
+    def __init__(self, L, E, S, T_max, H, I, k, dtype, wfmt, layer_pool, blob_stride, slot_base, slot_stride, bufs,
+                 trace_capacity=0):
+        self.keep = bufs
+        b = _decoder_buffers(bufs)
+        st = ctypes.c_int(0)
+        lp = layer_table(layer_pool)
+        self.h = _lib.moe_device_decoder_create(L, E, S, T_max, H, I, k, dtype, wfmt, lp.ctypes.data, blob_stride,
+                                                _ptr(slot_base), slot_stride, ctypes.byref(b), int(trace_capacity),
+                                                ctypes.byref(st))
+        if not self.h:
+            raise MoEError(st.value, _lib.moe_last_error().decode())
+
+    def close(self):
+        if self.h and _lib is not None:
+            _lib.moe_device_decoder_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+
+def moe_device_decoder_create(*a, **kw):
+    return MoeDeviceDecoder(*a, **kw)
+
+
+def moe_device_decoder_destroy(dec):
+    dec.close()
+
+
+def moe_device_decoder_step(dec, layer, x, Wr, bias, out, stream=None):
+    _check(_lib.moe_device_decoder_step(dec.h, layer, _ptr(x), x.shape[0], _ptr(Wr), _ptr(bias), _ptr(out),
+                                        _dtype_code(out), _stream(stream)), "moe_device_decoder_step")
+
+
+def moe_device_decoder_stats(dec):
+    h, m, r = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(_lib.moe_device_decoder_stats(dec.h, ctypes.byref(h), ctypes.byref(m), ctypes.byref(r)),
+           "moe_device_decoder_stats")
+    return h.value, m.value, r.value
+
+
+def moe_device_decoder_trace(dec, max_records):
+    """int32 [n, 7] (seq, layer, key, hit, slot, victim, wave) and the number of accesses traced."""
+    out = np.zeros((max(int(max_records), 1), 7), np.int32)
+    n = ctypes.c_int64(0)
+    _check(_lib.moe_device_decoder_trace(dec.h, out.ctypes.data, int(max_records), ctypes.byref(n)),
+           "moe_device_decoder_trace")
+    return out[:min(n.value, int(max_records))], n.value
+
+
+def moe_device_decoder_clear_trace(dec):
+    _check(_lib.moe_device_decoder_clear_trace(dec.h), "moe_device_decoder_clear_trace")
+
+
+def moe_device_decoder_slot_of(dec, key):
+    s = ctypes.c_int(0)
+    _check(_lib.moe_device_decoder_slot_of(dec.h, key, ctypes.byref(s)), "moe_device_decoder_slot_of")
+    return s.value
+
+
+class MoeGraph:
+    def __init__(self, h):
+        self.h = h
+
+    def close(self):
+        if self.h and _lib is not None:
+            _lib.moe_graph_destroy(self.h)
+            self.h = None
+
+    __del__ = close
+
+
+def moe_graph_begin(stream):
+    _check(_lib.moe_graph_begin(_stream(stream)), "moe_graph_begin")
+
+
+def moe_graph_end(stream):
+    st = ctypes.c_int(0)
+    h = _lib.moe_graph_end(_stream(stream), ctypes.byref(st))
+    if not h:
+        raise MoEError(st.value, _lib.moe_last_error().decode())
+    return MoeGraph(h)
+
+
+def moe_graph_launch(graph, stream=None):
+    _check(_lib.moe_graph_launch(graph.h, _stream(stream)), "moe_graph_launch")
+
+
+def moe_graph_destroy(graph):
+    graph.close()

@@ -1,0 +1,263 @@
+// Device-controlled decode layer-step: routing, cache resolve, fills, expert
+// FFN and combine enqueued on one stream with every routing-dependent choice
+// made by kernels from device-resident tables, so the step never waits for
+// the host and can be captured into a HIP graph and replayed (page
+// "FreeToken-benchmark", section "Graph Compatibility"). The cache policy is
+// the shared LRU of the host path (page "FreeToken-rtx-4090", section "How the
+// MoE Memory Hierarchy Works"); misses are always filled (the CPU share of
+// "Adaptive Misses" needs the host and stays on the host-driven path).
+#include <hip/hip_runtime.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_kernels.hpp"
+
+extern "C" size_t moe_route_workspace_size(int T, int H, int E, int k);
+
+namespace {
+template <typename... A>
+int dd_fail(int code, const char* fmt, A... a) {
+  return moe::set_error(code, fmt, a...);
+}
+}  // namespace
+
+struct moe_device_decoder {
+  int L, E, S, Tmax, H, I, k, dtype, wfmt;
+  std::vector<const char*> pool;  // device-visible address of each layer's pool
+  size_t blob_stride, blob_bytes;
+  char* slot_base;
+  size_t slot_stride;
+  moe_decoder_buffers_t b;
+  void* mem = nullptr;  // one device allocation holding the control data
+  moe::DevCache c{};
+  int max_items;
+};
+
+struct moe_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+static void dd_release(moe_device_decoder_t* d) {
+  if (d->mem) (void)hipFree(d->mem);
+  delete d;
+}
+
+moe_device_decoder_t* moe_device_decoder_create(int L, int E, int S, int T_max, int H, int I, int k, int dtype,
+                                                int wfmt, const void* const* layer_pool, size_t blob_stride,
+                                                void* slot_base, size_t slot_stride,
+                                                const moe_decoder_buffers_t* buffers, int64_t trace_capacity,
+                                                int* status) {
+  auto bad = [&](int code, const char* msg) -> moe_device_decoder_t* {
+    if (status) *status = dd_fail(code, "moe_device_decoder_create: %s", msg);
+    return nullptr;
+  };
+  if (!layer_pool || !slot_base || !buffers) return bad(MOE_EINVAL, "null argument");
+  if (L < 1 || E < 1 || E > 1024 || (long long)L * E > (1ll << 30) || T_max < 1 || H < 1 || I < 1 || k < 1 ||
+      k > 16 || k > E || H % 8 != 0 || trace_capacity < 0)
+    return bad(MOE_EINVAL, "bad sizes");
+  if (S < 1) return bad(MOE_ECAPACITY, "the cache needs at least one slot");
+  const int max_items = E < k * T_max ? E : k * T_max;
+  if (S < max_items)
+    return bad(MOE_ECAPACITY, "S must be at least min(E, k*T_max): a layer-step's experts must fit the cache at once");
+  if (dtype != MOE_DT_F32 && dtype != MOE_DT_BF16) return bad(MOE_EINVAL, "bad activation dtype");
+  if ((wfmt == MOE_W_F32) != (dtype == MOE_DT_F32)) return bad(MOE_EINVAL, "activation dtype does not match weights");
+  const size_t blob = moe_expert_bytes(wfmt, H, I);
+  if (blob == 0) return bad(MOE_EINVAL, "unsupported weight format or shape");
+  if (blob % 16 != 0) return bad(MOE_EINVAL, "expert blob size not a multiple of 16 bytes");
+  if (blob_stride < blob || slot_stride < blob) return bad(MOE_EINVAL, "stride smaller than an expert blob");
+  const moe_decoder_buffers_t& b = *buffers;
+  if (!b.topk_idx || !b.topk_w || !b.counts || !b.offsets || !b.perm_src || !b.perm_pos || !b.y_perm ||
+      !b.route_ws || !b.ffn_ws)
+    return bad(MOE_EINVAL, "null device buffer");
+  if (b.route_ws_bytes < moe_route_workspace_size(T_max, H, E, k)) return bad(MOE_EINVAL, "route workspace too small");
+  if (b.ffn_ws_bytes < moe_ffn_workspace_size(T_max * k, H, I, wfmt)) return bad(MOE_EINVAL, "FFN workspace too small");
+  moe_device_decoder_t* d = new (std::nothrow) moe_device_decoder();
+  if (!d) return bad(MOE_ENOMEM, "out of host memory");
+  d->L = L; d->E = E; d->S = S; d->Tmax = T_max; d->H = H; d->I = I; d->k = k; d->dtype = dtype; d->wfmt = wfmt;
+  d->blob_stride = blob_stride; d->blob_bytes = blob;
+  d->slot_base = static_cast<char*>(slot_base);
+  d->slot_stride = slot_stride;
+  d->b = b;
+  d->max_items = max_items;
+  for (int l = 0; l < L; ++l) {
+    void* dp = nullptr;
+    if (!layer_pool[l] || hipHostGetDevicePointer(&dp, const_cast<void*>(layer_pool[l]), 0) != hipSuccess || !dp) {
+      dd_release(d);
+      return bad(MOE_EINVAL, "a layer pool address is not pinned host memory from moe_pool_alloc");
+    }
+    d->pool.push_back(static_cast<const char*>(dp));
+  }
+  // control data, 256-byte aligned pieces of one allocation
+  const size_t n_keys = (size_t)L * E;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = moe::align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_slot_of = take(n_keys * 4), o_slot_key = take((size_t)S * 4), o_stamp = take((size_t)S * 8),
+               o_ctl = take(8 * 8), o_work = take((size_t)max_items * 16), o_miss = take((size_t)max_items * 16),
+               o_n = take(2 * 4), o_trace = take((size_t)trace_capacity * 7 * 4);
+  hipError_t e = hipMalloc(&d->mem, off);
+  if (e != hipSuccess) {
+    d->mem = nullptr;
+    dd_release(d);
+    if (status) *status = dd_fail(MOE_ENOMEM, "moe_device_decoder_create: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  char* m = static_cast<char*>(d->mem);
+  moe::DevCache& c = d->c;
+  c.slot_of = reinterpret_cast<int32_t*>(m + o_slot_of);
+  c.slot_key = reinterpret_cast<int32_t*>(m + o_slot_key);
+  c.stamp = reinterpret_cast<uint64_t*>(m + o_stamp);
+  c.ctl = reinterpret_cast<uint64_t*>(m + o_ctl);
+  c.S = S;
+  c.work = reinterpret_cast<int4*>(m + o_work);
+  c.miss = reinterpret_cast<int4*>(m + o_miss);
+  c.n = reinterpret_cast<int32_t*>(m + o_n);
+  c.trace = reinterpret_cast<int32_t*>(m + o_trace);
+  c.trace_cap = trace_capacity;
+  // empty cache: every key unmapped (-1 bytes), every slot free, clocks zero
+  e = hipMemset(m + o_slot_of, 0xFF, o_stamp - o_slot_of);
+  if (e == hipSuccess) e = hipMemset(m + o_stamp, 0, o_trace - o_stamp);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    dd_release(d);
+    if (status) *status = dd_fail(MOE_EHIP, "moe_device_decoder_create: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (status) *status = MOE_OK;
+  return d;
+}
+
+int moe_device_decoder_destroy(moe_device_decoder_t* d) {
+  if (!d) return MOE_OK;
+  (void)hipDeviceSynchronize();
+  dd_release(d);
+  return MOE_OK;
+}
+
+int moe_device_decoder_step(moe_device_decoder_t* d, int layer, const void* x, int T, const void* Wr,
+                            const float* bias, void* out, int out_dtype, void* stream) {
+  if (!d || !x || !Wr || !out) return dd_fail(MOE_EINVAL, "moe_device_decoder_step: null argument");
+  if (T < 1 || T > d->Tmax) return dd_fail(MOE_EINVAL, "moe_device_decoder_step: T=%d outside [1, %d]", T, d->Tmax);
+  if (layer < 0 || layer >= d->L) return dd_fail(MOE_EINVAL, "moe_device_decoder_step: layer %d out of range", layer);
+  if (out_dtype != MOE_DT_F32 && out_dtype != MOE_DT_BF16)
+    return dd_fail(MOE_EINVAL, "moe_device_decoder_step: bad output dtype");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const moe_decoder_buffers_t& b = d->b;
+  const int items = d->E < d->k * T ? d->E : d->k * T;
+  char* ws = static_cast<char*>(b.ffn_ws);
+  void* hbuf = ws;
+  void* xg = ws + moe::align_up((size_t)(d->Tmax * d->k + 16) * d->I * (d->wfmt == MOE_W_F32 ? 4 : 2), 256);
+  hipError_t e = moe::launch_route(x, d->dtype == MOE_DT_BF16, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w,
+                                   b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s, nullptr);
+  if (e == hipSuccess) e = moe::launch_dev_resolve(b.counts, b.offsets, d->E, layer, d->c, s);
+  if (e == hipSuccess)
+    e = moe::launch_dev_fill(d->c, d->pool[layer], d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, s);
+  if (e == hipSuccess)
+    e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->c.n, d->c.work, items, T, d->slot_base, d->slot_stride,
+                                   d->H, d->I, hbuf, xg, b.y_perm, s);
+  if (e == hipSuccess)
+    e = moe::launch_combine(b.y_perm, b.perm_pos, b.topk_w, T, d->k, d->H, out, out_dtype == MOE_DT_BF16, s);
+  if (e != hipSuccess) return dd_fail(MOE_EHIP, "moe_device_decoder_step: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int moe_device_decoder_stats(const moe_device_decoder_t* d, int64_t* hits, int64_t* misses, int64_t* resolves) {
+  if (!d || !hits || !misses || !resolves) return dd_fail(MOE_EINVAL, "moe_device_decoder_stats: null argument");
+  uint64_t ctl[5];
+  hipError_t e = hipMemcpy(ctl, d->c.ctl, sizeof ctl, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return dd_fail(MOE_EHIP, "moe_device_decoder_stats: %s", hipGetErrorString(e));
+  *hits = (int64_t)ctl[1];
+  *misses = (int64_t)ctl[2];
+  *resolves = (int64_t)ctl[3];
+  return MOE_OK;
+}
+
+int moe_device_decoder_trace(const moe_device_decoder_t* d, moe_trace_t* out, int64_t max_records,
+                             int64_t* n_records) {
+  if (!d || !n_records || max_records < 0 || (max_records > 0 && !out))
+    return dd_fail(MOE_EINVAL, "moe_device_decoder_trace: null argument");
+  uint64_t n = 0;
+  hipError_t e = hipMemcpy(&n, d->c.ctl + 4, sizeof n, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return dd_fail(MOE_EHIP, "moe_device_decoder_trace: %s", hipGetErrorString(e));
+  *n_records = (int64_t)n;
+  int64_t m = (int64_t)n < d->c.trace_cap ? (int64_t)n : d->c.trace_cap;
+  if (m > max_records) m = max_records;
+  if (m > 0) {
+    e = hipMemcpy(out, d->c.trace, (size_t)m * sizeof(moe_trace_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return dd_fail(MOE_EHIP, "moe_device_decoder_trace: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+int moe_device_decoder_clear_trace(moe_device_decoder_t* d) {
+  if (!d) return dd_fail(MOE_EINVAL, "moe_device_decoder_clear_trace: null decoder");
+  const uint64_t zero = 0;
+  hipError_t e = hipMemcpy(d->c.ctl + 4, &zero, sizeof zero, hipMemcpyHostToDevice);
+  return e == hipSuccess ? MOE_OK : dd_fail(MOE_EHIP, "moe_device_decoder_clear_trace: %s", hipGetErrorString(e));
+}
+
+int moe_device_decoder_slot_of(const moe_device_decoder_t* d, int key, int* slot) {
+  if (!d || !slot || key < 0 || (long long)key >= (long long)d->L * d->E)
+    return dd_fail(MOE_EINVAL, "moe_device_decoder_slot_of: bad argument");
+  hipError_t e = hipMemcpy(slot, d->c.slot_of + key, sizeof(int32_t), hipMemcpyDeviceToHost);
+  return e == hipSuccess ? MOE_OK : dd_fail(MOE_EHIP, "moe_device_decoder_slot_of: %s", hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// Stream capture into a HIP graph
+// ---------------------------------------------------------------------------
+int moe_graph_begin(void* stream) {
+  if (!stream) return dd_fail(MOE_EINVAL, "moe_graph_begin: capture needs a created stream, not the default one");
+  hipError_t e = hipStreamBeginCapture(reinterpret_cast<hipStream_t>(stream), hipStreamCaptureModeThreadLocal);
+  return e == hipSuccess ? MOE_OK : dd_fail(MOE_EHIP, "moe_graph_begin: %s", hipGetErrorString(e));
+}
+
+moe_graph_t* moe_graph_end(void* stream, int* status) {
+  auto bad = [&](int code, const char* what, hipError_t e) -> moe_graph_t* {
+    if (status) *status = dd_fail(code, "moe_graph_end: %s: %s", what, hipGetErrorString(e));
+    return nullptr;
+  };
+  if (!stream) {
+    if (status) *status = dd_fail(MOE_EINVAL, "moe_graph_end: null stream");
+    return nullptr;
+  }
+  moe_graph_t* g = new (std::nothrow) moe_graph();
+  if (!g) return bad(MOE_ENOMEM, "allocation", hipSuccess);
+  hipError_t e = hipStreamEndCapture(reinterpret_cast<hipStream_t>(stream), &g->graph);
+  if (e != hipSuccess || !g->graph) {
+    delete g;
+    return bad(MOE_EHIP, "end of capture", e);
+  }
+  e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g->graph);
+    delete g;
+    return bad(MOE_EHIP, "instantiate", e);
+  }
+  if (status) *status = MOE_OK;
+  return g;
+}
+
+int moe_graph_launch(moe_graph_t* g, void* stream) {
+  if (!g) return dd_fail(MOE_EINVAL, "moe_graph_launch: null graph");
+  hipError_t e = hipGraphLaunch(g->exec, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_OK : dd_fail(MOE_EHIP, "moe_graph_launch: %s", hipGetErrorString(e));
+}
+
+int moe_graph_destroy(moe_graph_t* g) {
+  if (!g) return MOE_OK;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  delete g;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -16,13 +16,36 @@
 namespace moe {
 namespace {
 
+// Where a decode launch finds its work items {slot, row_begin, rows, expert}:
+// in the kernel arguments (lists resolved on the host; the grid matches the
+// list), or in device memory (lists resolved on the device; the grid is sized
+// for the longest possible list and blocks past the list's length exit).
+struct ArgWork {
+  WorkArgs wa;
+  __device__ __forceinline__ bool get(int i, int4& it) const {
+    it = wa.item[i];
+    return true;
+  }
+};
+struct DevWork {
+  const int32_t* n;
+  const int4* items;
+  __device__ __forceinline__ bool get(int i, int4& it) const {
+    if (i >= *n) return false;
+    it = items[i];
+    return true;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // fp32 weights: plain VALU kernels (small correctness configurations).
 // ---------------------------------------------------------------------------
+template <typename W>
 __global__ __launch_bounds__(256) void ffn1_f32_kernel(const float* __restrict__ x, const int32_t* __restrict__ perm_src,
-                                                       const WorkArgs wa, const char* __restrict__ slot_base,
+                                                       const W wk, const char* __restrict__ slot_base,
                                                        size_t slot_stride, int H, int I, float* __restrict__ hbuf) {
-  const int4 it = wa.item[blockIdx.y];
+  int4 it;
+  if (!wk.get(blockIdx.y, it)) return;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const int m = idx / I, i = idx - (idx / I) * I;
   if (m >= it.z) return;
@@ -37,10 +60,12 @@ __global__ __launch_bounds__(256) void ffn1_f32_kernel(const float* __restrict__
   hbuf[(size_t)(it.y + m) * I + i] = silu(g) * u;
 }
 
-__global__ __launch_bounds__(256) void ffn2_f32_kernel(const float* __restrict__ hbuf, const WorkArgs wa,
+template <typename W>
+__global__ __launch_bounds__(256) void ffn2_f32_kernel(const float* __restrict__ hbuf, const W wk,
                                                        const char* __restrict__ slot_base, size_t slot_stride, int H,
                                                        int I, float* __restrict__ y) {
-  const int4 it = wa.item[blockIdx.y];
+  int4 it;
+  if (!wk.get(blockIdx.y, it)) return;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   const int m = idx / H, n = idx - (idx / H) * H;
   if (m >= it.z) return;
@@ -58,13 +83,15 @@ constexpr int kU = 8;  // fragments in flight per wave
 
 // Gate/up: workgroup = one 16-row tile of P1 (8 gate + 8 up columns) of one
 // item; wave w reduces fragments [KC*w/4, KC*(w+1)/4).
+template <typename W>
 __global__ __launch_bounds__(256) void ffn1_decode_bf16(const uint16_t* __restrict__ x,
-                                                        const int32_t* __restrict__ perm_src, const WorkArgs wa,
+                                                        const int32_t* __restrict__ perm_src, const W wk,
                                                         const char* __restrict__ slot_base, size_t slot_stride, int H,
                                                         int I, uint16_t* __restrict__ hbuf) {
   const int NT = I / 8;
   const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
-  const int4 it = wa.item[item];
+  int4 it;
+  if (!wk.get(item, it)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KC = H / 32;
   const int c0 = (KC * wave) >> 2, c1 = (KC * (wave + 1)) >> 2;
@@ -106,12 +133,14 @@ __global__ __launch_bounds__(256) void ffn1_decode_bf16(const uint16_t* __restri
 }
 
 // Down projection: workgroup = one 16-row tile of P2 (16 output columns).
-__global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restrict__ hbuf, const WorkArgs wa,
+template <typename W>
+__global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restrict__ hbuf, const W wk,
                                                         const char* __restrict__ slot_base, size_t slot_stride,
                                                         size_t p2_off, int H, int I, float* __restrict__ y) {
   const int NT = H / 16;
   const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
-  const int4 it = wa.item[item];
+  int4 it;
+  if (!wk.get(item, it)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KC = I / 32;
   const int c0 = (KC * wave) >> 2, c1 = (KC * (wave + 1)) >> 2;
@@ -155,10 +184,12 @@ __global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 
 // Gathered activations, converted to fp16: xg[r, :] = fp16(x[perm_src[r], :]).
+template <typename W>
 __global__ __launch_bounds__(256) void gather_f16_kernel(const uint16_t* __restrict__ x,
-                                                         const int32_t* __restrict__ perm_src, const WorkArgs wa,
+                                                         const int32_t* __restrict__ perm_src, const W wk,
                                                          int H, uint16_t* __restrict__ xg) {
-  const int4 it = wa.item[blockIdx.y];
+  int4 it;
+  if (!wk.get(blockIdx.y, it)) return;
   const int H8 = H / 8;
   for (int idx = blockIdx.x * 256 + threadIdx.x; idx < it.z * H8; idx += gridDim.x * 256) {
     const int m = idx / H8, c = idx - (idx / H8) * H8;
@@ -236,12 +267,14 @@ __device__ __forceinline__ void int4_decode_tiles(const uint16_t* __restrict__ a
   }
 }
 
-__global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restrict__ xg, const WorkArgs wa,
+template <typename W>
+__global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restrict__ xg, const W wk,
                                                         const char* __restrict__ slot_base, size_t slot_stride,
                                                         size_t p1s_off, int H, int I, uint16_t* __restrict__ hbuf) {
   const int NB = I / 8 / kR;  // blocks per expert
   const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
-  const int4 it = wa.item[item];
+  int4 it;
+  if (!wk.get(item, it)) return;
   const char* blob = slot_base + (size_t)it.x * slot_stride;
   const int lane = threadIdx.x & 63;
   int4_decode_tiles(xg, it, H, blob, blob + p1s_off, tile0, [&](int tile, int m, const f32x4_t& s) {
@@ -252,13 +285,15 @@ __global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restri
   });
 }
 
-__global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restrict__ hbuf, const WorkArgs wa,
+template <typename W>
+__global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restrict__ hbuf, const W wk,
                                                         const char* __restrict__ slot_base, size_t slot_stride,
                                                         size_t p2_off, size_t p2s_off, int H, int I,
                                                         float* __restrict__ y) {
   const int NB = H / 16 / kR;
   const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
-  const int4 it = wa.item[item];
+  int4 it;
+  if (!wk.get(item, it)) return;
   const char* blob = slot_base + (size_t)it.x * slot_stride;
   const int lane = threadIdx.x & 63;
   int4_decode_tiles(hbuf, it, I, blob + p2_off, blob + p2s_off, tile0, [&](int tile, int m, const f32x4_t& s) {
@@ -404,45 +439,67 @@ bool prefill_supported(int wfmt, int H, int I) {
   return wfmt == 1 && (2 * I) % kGemmBN == 0 && H % kGemmBN == 0 && H % 64 == 0 && I % 64 == 0;
 }
 
+namespace {
+
+// The decode kernels of one format for `n_items` work items (the grid's item
+// count) with at most `max_rows` rows each.
+template <typename W>
+hipError_t decode_kernels(int wfmt, const void* x, const int32_t* perm_src, const W& wk, int n_items, int max_rows,
+                          const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y,
+                          hipStream_t s) {
+  const BlobLayout L = blob_layout(wfmt, H, I);
+  if (wfmt == 0) {
+    if (max_rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(ffn1_f32_kernel<W>, dim3((max_rows * I + 255) / 256, n_items), dim3(256), 0, s,
+                       static_cast<const float*>(x), perm_src, wk, slot_base, slot_stride, H, I,
+                       static_cast<float*>(hbuf));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ffn2_f32_kernel<W>, dim3((max_rows * H + 255) / 256, n_items), dim3(256), 0, s,
+                       static_cast<const float*>(hbuf), wk, slot_base, slot_stride, H, I, y);
+    return hipGetLastError();
+  }
+  if (wfmt == 1) {
+    hipLaunchKernelGGL(ffn1_decode_bf16<W>, dim3(n_items * (I / 8)), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                       perm_src, wk, slot_base, slot_stride, H, I, static_cast<uint16_t*>(hbuf));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ffn2_decode_bf16<W>, dim3(n_items * (H / 16)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(hbuf), wk, slot_base, slot_stride, L.p2, H, I, y);
+    return hipGetLastError();
+  }
+  // int4
+  hipLaunchKernelGGL(gather_f16_kernel<W>, dim3(4, n_items), dim3(256), 0, s, static_cast<const uint16_t*>(x), perm_src,
+                     wk, H, static_cast<uint16_t*>(xg));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ffn1_decode_int4<W>, dim3(n_items * (I / 8 / kR)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(xg), wk, slot_base, slot_stride, L.p1s, H, I,
+                     static_cast<uint16_t*>(hbuf));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ffn2_decode_int4<W>, dim3(n_items * (H / 16 / kR)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(hbuf), wk, slot_base, slot_stride, L.p2, L.p2s, H, I, y);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, const WorkArgs& wa,
                              const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y,
                              hipStream_t s) {
   if (wa.n == 0) return hipSuccess;
-  const BlobLayout L = blob_layout(wfmt, H, I);
-  if (wfmt == 0) {
-    int maxrows = 0;
-    for (int i = 0; i < wa.n; ++i) maxrows = wa.item[i].z > maxrows ? wa.item[i].z : maxrows;
-    if (maxrows == 0) return hipSuccess;
-    hipLaunchKernelGGL(ffn1_f32_kernel, dim3((maxrows * I + 255) / 256, wa.n), dim3(256), 0, s,
-                       static_cast<const float*>(x), perm_src, wa, slot_base, slot_stride, H, I,
-                       static_cast<float*>(hbuf));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ffn2_f32_kernel, dim3((maxrows * H + 255) / 256, wa.n), dim3(256), 0, s,
-                       static_cast<const float*>(hbuf), wa, slot_base, slot_stride, H, I, y);
-    return hipGetLastError();
-  }
-  if (wfmt == 1) {
-    hipLaunchKernelGGL(ffn1_decode_bf16, dim3(wa.n * (I / 8)), dim3(256), 0, s, static_cast<const uint16_t*>(x),
-                       perm_src, wa, slot_base, slot_stride, H, I, static_cast<uint16_t*>(hbuf));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(ffn2_decode_bf16, dim3(wa.n * (H / 16)), dim3(256), 0, s, static_cast<const uint16_t*>(hbuf),
-                       wa, slot_base, slot_stride, L.p2, H, I, y);
-    return hipGetLastError();
-  }
-  // int4
-  hipLaunchKernelGGL(gather_f16_kernel, dim3(4, wa.n), dim3(256), 0, s, static_cast<const uint16_t*>(x), perm_src, wa,
-                     H, static_cast<uint16_t*>(xg));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ffn1_decode_int4, dim3(wa.n * (I / 8 / kR)), dim3(256), 0, s, static_cast<const uint16_t*>(xg), wa,
-                     slot_base, slot_stride, L.p1s, H, I, static_cast<uint16_t*>(hbuf));
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ffn2_decode_int4, dim3(wa.n * (H / 16 / kR)), dim3(256), 0, s, static_cast<const uint16_t*>(hbuf), wa,
-                     slot_base, slot_stride, L.p2, L.p2s, H, I, y);
-  return hipGetLastError();
+  int max_rows = 0;
+  for (int i = 0; i < wa.n; ++i) max_rows = wa.item[i].z > max_rows ? wa.item[i].z : max_rows;
+  return decode_kernels(wfmt, x, perm_src, ArgWork{wa}, wa.n, max_rows, slot_base, slot_stride, H, I, hbuf, xg, y, s);
+}
+
+hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
+                                 const int4* items, int max_items, int max_rows, const char* slot_base,
+                                 size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y, hipStream_t s) {
+  if (max_items == 0) return hipSuccess;
+  return decode_kernels(wfmt, x, perm_src, DevWork{n_items, items}, max_items, max_rows, slot_base, slot_stride, H, I,
+                        hbuf, xg, y, s);
 }
 
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,

@@ -100,6 +100,12 @@ hipError_t launch_combine(const float* y_perm, const int32_t* perm_pos, const fl
 hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, const WorkArgs& wa,
                              const char* slot_base, size_t slot_stride, int H, int I,
                              void* hbuf, void* xg, float* y, hipStream_t s);
+// The same kernels with the work list in device memory: *n_items items at
+// `items` (device), at most max_items of them with at most max_rows rows
+// each; launch shapes depend only on max_items and max_rows.
+hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
+                                 const int4* items, int max_items, int max_rows, const char* slot_base,
+                                 size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y, hipStream_t s);
 // 128 x 128-tile fallback GEMM for shapes the large-tile GEMM does not take.
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,
                               size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s);
@@ -124,6 +130,28 @@ hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const int
 int router_gemm2_splits(int T, int H, int E);
 hipError_t launch_router_gemm2(const void* x, const void* wrt, int T, int H, int E, float* partial, int nsplit,
                                hipStream_t s);
+
+// Device-resident cache control (kernels_devctl.hip). All pointers are device
+// memory owned by a device-controlled decoder.
+struct DevCache {
+  int32_t* slot_of;   // [L*E] key -> slot, -1 if not resident
+  int32_t* slot_key;  // [S] slot -> key, -1 if free
+  uint64_t* stamp;    // [S] last use (clock value) of each occupied slot
+  uint64_t* ctl;      // [0] clock, [1] hits, [2] misses, [3] resolve calls, [4] trace records
+  int S;
+  int4* work;         // [max items] {slot, row_begin, rows, expert}: hits, then misses
+  int4* miss;         // [max items] {expert, slot, victim key or -1, key}
+  int32_t* n;         // [0] work items, [1] misses (of the last resolve)
+  int32_t* trace;     // [trace_cap][7] records as moe_trace_t
+  int64_t trace_cap;
+};
+// One layer-step of the policy on the device (one workgroup; E <= 1024).
+hipError_t launch_dev_resolve(const int32_t* counts, const int32_t* offsets, int E, int layer, const DevCache& c,
+                              hipStream_t s);
+// Copies the last resolve's misses from `pool` (device-visible address of the
+// layer's pinned pool) into their slots; fixed grid, exits when there are none.
+hipError_t launch_dev_fill(const DevCache& c, const void* pool, size_t blob_stride, size_t blob_bytes,
+                           void* slot_base, size_t slot_stride, hipStream_t s);
 
 // Host: reads one byte per page of a pool region on the CPU thread pool.
 void cpu_touch_pages(const void* p, size_t bytes);

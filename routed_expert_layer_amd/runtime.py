@@ -244,6 +244,65 @@ class DecodeLayer:
         return L.moe_cache_trace(self.cache)
 
 
+class DeviceDecodeLayer:
+    """Decode path with the cache control in GPU memory (moe_device_decoder_*): routing, the resolve kernel, the
+    fill kernel, the FFN over the device work list and the combine are enqueued with no host synchronisation,
+    so a sequence of layer-steps can be captured once (capture) and replayed (replay) on static buffers."""
+
+    def __init__(self, store, n_slots, T, k, act, device="cuda", keep_logits=False, trace_capacity=0):
+        self.store, self.S, self.k, self.T = store, n_slots, k, T
+        self.H, self.I, self.E = store.H, store.I, store.E
+        self.act = act
+        self.rb = RouteBuffers(T, self.H, self.E, k, device, keep_logits)
+        self.slots = torch.empty(n_slots * store.stride, dtype=torch.uint8, device=device)
+        rows = T * k
+        self.y_perm = torch.empty((max(rows, 1), self.H), dtype=torch.float32, device=device)
+        self.ffn_ws = torch.empty(L.moe_ffn_workspace_size(rows, self.H, self.I, store.wfmt), dtype=torch.uint8,
+                                  device=device)
+        self.out = torch.empty((T, self.H), dtype=torch.float32, device=device)
+        rb = self.rb
+        bufs = dict(topk_idx=rb.topk_idx, topk_w=rb.topk_w, logits=rb.logits, counts=rb.counts, offsets=rb.offsets,
+                    perm_src=rb.perm_src, perm_pos=rb.perm_pos, y_perm=self.y_perm, route_ws=rb.ws,
+                    ffn_ws=self.ffn_ws)
+        self.dec = L.MoeDeviceDecoder(store.L, self.E, n_slots, T, self.H, self.I, k,
+                                      L.MOE_DT_BF16 if act == "bf16" else L.MOE_DT_F32, store.wfmt,
+                                      store.layer_ptrs, store.stride, self.slots, store.stride, bufs, trace_capacity)
+
+    def step(self, layer, x, Wr, bias, stream=None, out=None):
+        """Enqueue one layer-step; returns the output tensor (valid once the stream reaches it)."""
+        s = stream or torch.cuda.current_stream()
+        o = self.out[:x.shape[0]] if out is None else out
+        L.moe_device_decoder_step(self.dec, layer, x, Wr, bias, o, s)
+        return o
+
+    @staticmethod
+    def capture(enqueue, stream):
+        """Record the work `enqueue()` puts on `stream` (a torch.cuda.Stream) into a graph; nothing runs."""
+        L.moe_graph_begin(stream)
+        try:
+            enqueue()
+        finally:
+            g = L.moe_graph_end(stream)
+        return g
+
+    @staticmethod
+    def replay(graph, stream):
+        L.moe_graph_launch(graph, stream)
+
+    def stats(self):
+        """(hits, misses, resolve calls) so far; synchronises the device."""
+        torch.cuda.synchronize()
+        return L.moe_device_decoder_stats(self.dec)
+
+    @property
+    def n_fills(self):
+        return self.stats()[1]
+
+    def trace(self, max_records):
+        torch.cuda.synchronize()
+        return L.moe_device_decoder_trace(self.dec, max_records)
+
+
 class PrefillLayer:
     """Prefill path over a layer whose experts are all resident (blob of expert e at base + e*stride)."""
 
