@@ -9,6 +9,6 @@ imports the product path.
 """
 from .moe import (  # noqa: F401
     router_logits, topk_select, topk_flags, topk_weights, permute, swiglu_expert,
-    expert_outputs, combine, dequant_int4, moe_layer,
+    expert_outputs, combine, dequant_int4, moe_layer, e2m1_value, E2M1, e8m0_value, dequant_mxfp4,
 )
 from .lru import SharedLRU, TraceRec  # noqa: F401

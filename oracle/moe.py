@@ -23,7 +23,10 @@ one for a routed mixture-of-experts layer):
   * expert: SwiGLU, y = (silu(x.W1) * (x.W3)).W2 with W1, W3 [H, I], W2 [I, H];
   * combine: out_t = sum_j w_tj * y_tj;
   * int4 experts: W = q * s, q in [-7, 7], one fp16 scale per 128 rows of K and
-    output column.
+    output column;
+  * MXFP4 experts (the format's name is all the pages give): the OCP MX FP4
+    format, W = E2M1(code) * 2^(scale - 127), one 8-bit scale per 32 rows of K
+    and output column; activations stay bf16.
 Every value is computed in fp64 from the exact values the layer is given.
 """
 import numpy as np
@@ -143,6 +146,35 @@ def dequant_int4(q, s, group=128):
     q = as_f64(q)
     s = as_f64(s)
     return q * np.repeat(s, group, axis=0)
+
+
+def e2m1_value(code):
+    """Value of a 4-bit FP4 (E2M1) code, from its fields: bit 3 sign, bits 2..1
+    exponent (bias 1), bit 0 mantissa; exponent 0 is subnormal (m * 2^-1).
+    OCP Microscaling Formats (MX) v1.0, the FP4 element format. The pages give
+    the format's name only (page "FreeToken-benchmark", model table, the
+    DeepSeek-V4-Flash row: routed experts in MXFP4)."""
+    code = int(code)
+    sign = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+    return sign * mag
+
+
+E2M1 = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e8m0_value(s):
+    """Value of an 8-bit E8M0 block scale: 2^(s - 127); 255 is NaN (same standard)."""
+    s = np.asarray(s, dtype=np.int64)
+    return np.where(s == 255, np.nan, np.ldexp(1.0, s - 127))
+
+
+def dequant_mxfp4(codes, scales, block=32):
+    """W[k, n] = E2M1[codes[k, n]] * 2^(scales[k // block, n] - 127): one scale per
+    `block` consecutive K values of a column (exact in fp64)."""
+    c = as_int(codes)
+    return E2M1[c] * np.repeat(e8m0_value(as_int(scales)), block, axis=0)
 
 
 def expert_outputs(x, offsets, perm_src, get_expert, experts=None):

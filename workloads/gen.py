@@ -109,6 +109,49 @@ def quantize_int4(w, group=128):
     return q, s
 
 
+# FP4 (E2M1) magnitudes in code order 0..7, and the points where round-to-nearest
+# moves from one to the next; ties go to the even code (mantissa bit 0).
+_E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def quantize_mxfp4(w, block=32):
+    """MXFP4 codes along K (dim 0), following the OCP MX v1.0 conversion: per block
+    of `block` values of a column, shared exponent X = floor(log2(max|w|)) - 2 (the
+    largest FP4 exponent), scale byte X + 127 (127 for an all-zero block), codes =
+    round-to-nearest-even of w / 2^X onto the FP4 grid, saturating at 6; the sign
+    is kept (negative values that round to zero give code 8).
+    Returns (codes uint8 [K, N] in 0..15, scales uint8 [K/block, N])."""
+    K, N = w.shape
+    assert K % block == 0
+    wf = w.to(torch.float32).reshape(K // block, block, N)
+    amax = wf.abs().amax(dim=1)                                   # [K/b, N]
+    _, ex = torch.frexp(amax)                                      # amax = m * 2^ex, m in [0.5, 1)
+    shared = torch.where(amax > 0, ex - 3, torch.zeros_like(ex)).clamp(-127, 127)
+    v = torch.ldexp(wf, -shared.unsqueeze(1).to(torch.float32))    # exact: power-of-two scaling
+    a = v.abs()
+    # round to nearest, ties to even code: the boundaries below include their tie on the even side
+    code = torch.zeros_like(a, dtype=torch.int32)
+    code = torch.where(a > 0.25, 1, code)
+    code = torch.where(a >= 0.75, 2, code)
+    code = torch.where(a > 1.25, 3, code)
+    code = torch.where(a >= 1.75, 4, code)
+    code = torch.where(a > 2.5, 5, code)
+    code = torch.where(a >= 3.5, 6, code)
+    code = torch.where(a > 5.0, 7, code)
+    code = code + torch.where(v < 0, 8, 0)
+    return code.to(torch.uint8).reshape(K, N), (shared + 127).to(torch.uint8)
+
+
+def expert_mxfp4(cfg, layer, e, device="cpu"):
+    """MXFP4 expert: dict of codes c1, c3 [H, I], c2 [I, H] (uint8, 0..15) and E8M0 scales
+    s1, s3 [H/32, I], s2 [I/32, H] (uint8), from the bf16 weights of the same (layer, expert)."""
+    W1, W3, W2 = expert_weights(cfg, layer, e, device, torch.bfloat16)
+    c1, s1 = quantize_mxfp4(W1)
+    c3, s3 = quantize_mxfp4(W3)
+    c2, s2 = quantize_mxfp4(W2)
+    return dict(c1=c1, s1=s1, c3=c3, s3=s3, c2=c2, s2=s2)
+
+
 def expert_int4(cfg, layer, e, device="cpu"):
     """int4 expert: dict of codes q1, q3 [H, I], q2 [I, H] and fp16 scales s1, s3 [H/g, I], s2 [I/g, H]."""
     W1, W3, W2 = expert_weights(cfg, layer, e, device, torch.bfloat16)
