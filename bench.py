@@ -349,6 +349,8 @@ def bench_decode_layers(args, torch, L, gen, cfg, warm, steps):
         for layer in range(store.P):
             if cfg.wfmt == "int4":
                 store.pack_layer(layer, lambda e: gen.expert_int4(cfg, layer, e, dev))
+            elif cfg.wfmt == "mxfp4":
+                store.pack_layer(layer, lambda e: gen.expert_mxfp4(cfg, layer, e, dev))
             else:
                 store.pack_layer(layer, lambda e: gen.expert_weights(cfg, layer, e, dev))
         n = warm + steps
@@ -512,6 +514,7 @@ def main():
                                                                     CONFIGS["prefill_db_bf16_t16384_l8"]))
     if not args.no_extra:
         out["decode_int4"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["decode_int4_t8_l8"], 64, 128))
+        out["decode_mxfp4"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["decode_mxfp4_t8_l8"], 64, 128))
         out["decode_stack48"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["stack48_bf16_h2048_e128"],
                                                         32, 64))
     if not args.no_cpu_baseline:

@@ -50,7 +50,7 @@ enum {
 enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
 
 /* Expert weight formats (the layout of one expert blob, see moe_pack_expert). */
-enum { MOE_W_F32 = 0, MOE_W_BF16 = 1, MOE_W_INT4 = 2 };
+enum { MOE_W_F32 = 0, MOE_W_BF16 = 1, MOE_W_INT4 = 2, MOE_W_MXFP4 = 3 };
 
 /* FFN kernel choice for moe_ffn. */
 enum { MOE_FFN_AUTO = 0, MOE_FFN_DECODE = 1, MOE_FFN_PREFILL = 2 };
@@ -114,13 +114,23 @@ int moe_route(const void* x, int dtype, const void* Wr, const float* bias,
  * For MOE_W_INT4 the weights are q * s with int8 codes q in [-7, 7] of the
  * same shapes and fp16 scales s1, s3 [H/128, I], s2 [I/128, H]: one scale per
  * 128 consecutive rows (the reduction dimension K) and output column.
+ * For MOE_W_MXFP4 (page "FreeToken-benchmark", model table: the routed
+ * experts of DeepSeek-V4-Flash are deployed in MXFP4; the format is the OCP
+ * Microscaling FP4 one) the weights are E2M1(c) * 2^(s - 127) with uint8 codes
+ * c in 0..15 (bit 3 sign, bits 2..1 exponent with bias 1, bit 0 mantissa) of
+ * the same shapes and uint8 E8M0 scales s1, s3 [H/32, I], s2 [I/32, H]: one
+ * scale per 32 consecutive rows of K and output column. Supported scale bytes:
+ * 1..254 with every dequantised weight a normal bf16 value (the kernels form
+ * each weight exactly in bf16); activations stay bf16.
  *
  * moe_expert_bytes: size of one blob. Requirements: H and I multiples of 32
- * (bf16), of 128 (int4), I a multiple of 8; any H, I >= 1 for fp32.
+ * (bf16), of 128 (int4, MXFP4), I a multiple of 8; any H, I >= 1 for fp32.
  * moe_pack_expert: writes one blob from canonical device arrays, on `stream`.
  *   MOE_W_F32:  W1, W3, W2 fp32 device;  s1, s3, s2 ignored (NULL)
  *   MOE_W_BF16: W1, W3, W2 bf16 device;  s* ignored
  *   MOE_W_INT4: W1, W3, W2 are int8 codes (device), s1, s3, s2 fp16 device
+ *   MOE_W_MXFP4: W1, W3, W2 are uint8 FP4 codes (device), s1, s3, s2 uint8
+ *               E8M0 scales (device)
  *   blob: device out, moe_expert_bytes() bytes; the caller may then copy it
  *   into a pool or a cache slot.
  * moe_pool_alloc: page-locked host memory (hipHostMalloc) for the pool;
@@ -232,7 +242,9 @@ int cache_fill_async(moe_cache_t* cache, const moe_miss_t* misses, int n,
  * work     HOST array of n_work items {expert, slot, row_begin, rows}; items
  *          must not overlap in rows; rows >= 0
  * slot_base device base of the expert blobs; slot_stride bytes between slots
- * wfmt     MOE_W_F32 (x fp32), MOE_W_BF16 or MOE_W_INT4 (x bf16)
+ * wfmt     MOE_W_F32 (x fp32), MOE_W_BF16, MOE_W_INT4 or MOE_W_MXFP4 (x bf16);
+ *          the tiled GEMM (MOE_FFN_PREFILL) takes bf16 weights only, AUTO
+ *          runs the matrix-vector kernels for the other formats
  * y_perm   device out fp32 [rows_total, H] (only listed rows are written)
  * workspace device scratch, >= moe_ffn_workspace_size(rows_total, H, I, wfmt)
  *          bytes, where rows_total bounds every row index used

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ECAPACITY, MOE_EHIP, MOE_ENOMEM, MOE_ESTATE = 0, -1, -2, -3, -4, -5
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
-MOE_W_F32, MOE_W_BF16, MOE_W_INT4 = 0, 1, 2
+MOE_W_F32, MOE_W_BF16, MOE_W_INT4, MOE_W_MXFP4 = 0, 1, 2, 3
 MOE_FFN_AUTO, MOE_FFN_DECODE, MOE_FFN_PREFILL = 0, 1, 2
 
 # Every symbol include/moe.h declares.

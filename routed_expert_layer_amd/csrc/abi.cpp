@@ -111,7 +111,7 @@ static bool shape_ok(int wfmt, int H, int I) {
   if (H <= 0 || I <= 0) return false;
   if (wfmt == MOE_W_F32) return true;
   if (wfmt == MOE_W_BF16) return H % 32 == 0 && I % 32 == 0;
-  if (wfmt == MOE_W_INT4) return H % 128 == 0 && I % 128 == 0;
+  if (wfmt == MOE_W_INT4 || wfmt == MOE_W_MXFP4) return H % 128 == 0 && I % 128 == 0;
   return false;
 }
 
@@ -124,7 +124,8 @@ int moe_pack_expert(int wfmt, int H, int I, const void* W1, const void* W3, cons
                     const void* s3, const void* s2, void* blob, void* stream) {
   if (!shape_ok(wfmt, H, I)) return fail(MOE_EINVAL, "moe_pack_expert: unsupported format/shape %d %dx%d", wfmt, H, I);
   if (!W1 || !W3 || !W2 || !blob) return fail(MOE_EINVAL, "moe_pack_expert: null pointer argument");
-  if (wfmt == MOE_W_INT4 && (!s1 || !s3 || !s2)) return fail(MOE_EINVAL, "moe_pack_expert: int4 needs scales");
+  if ((wfmt == MOE_W_INT4 || wfmt == MOE_W_MXFP4) && (!s1 || !s3 || !s2))
+    return fail(MOE_EINVAL, "moe_pack_expert: int4 and MXFP4 need scales");
   hipError_t e = moe::launch_pack(wfmt, H, I, W1, W3, W2, s1, s3, s2, blob, as_stream(stream));
   return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_pack_expert");
 }

@@ -302,6 +302,108 @@ __global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 decode kernels (bf16 activations; every FP4 code times its power-of-two
+// block scale is exact in bf16, so the weights enter bf16 matrix-core
+// instructions exactly and the result equals a bf16-weight product with the
+// dequantised weights).
+// ---------------------------------------------------------------------------
+
+// Eight FP4 codes (nibbles in K order) times 2^(e - 127) as the bf16 A operand.
+__device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t w, float scale) {
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return r;
+}
+
+// E8M0 byte (1..254) to the fp32 power of two it encodes.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float((e & 0xFFu) << 23); }
+
+// Shared body of both MXFP4 projections, organised as the int4 one: a block
+// owns kR consecutive 16-row tiles of one expert, its four waves split the
+// 128-wide K blocks, and each activation fragment loaded serves all kR tiles.
+// act: bf16 activations; row m of the group is act_row(m). Finished 16 x 16
+// tile sums go to `emit(tile, m, sum)`.
+template <typename Row, typename Emit>
+__device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, int K, const char* q_base,
+                                                   const char* s_base, int tile0, Emit emit) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int KG = K / 128;
+  const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
+  const int kq = (lane >> 4) * 8;
+  __shared__ f32x4_t red[4][kR][64];
+  for (int m0 = 0; m0 < it.z; m0 += 16) {
+    const int m = m0 + (lane & 15);
+    const bool valid = m < it.z;
+    const uint16_t* ar = act_row(valid ? m : 0) + kq;
+    f32x4_t acc[kR];
+#pragma unroll
+    for (int r = 0; r < kR; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int g = g0; g < g1; ++g) {
+      u32x4_t b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = valid ? ld16(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        const size_t blk = (size_t)(tile0 + r) * KG + g;
+        const u32x4_t a = ld16_nt(q_base + blk * 1024 + lane * 16);
+        const uint32_t sc = *reinterpret_cast<const uint32_t*>(s_base + blk * 64 + (lane & 15) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[r] = mfma_bf16(fp4x8_to_bf16x8(a[j], e8m0_to_f32(sc >> (8 * j))), b[j], acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kR; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (valid) {
+      const f32x4_t sum = red[0][wave][lane] + red[1][wave][lane] + red[2][wave][lane] + red[3][wave][lane];
+      emit(tile0 + wave, m, sum);
+    }
+    __syncthreads();
+  }
+}
+
+template <typename W>
+__global__ __launch_bounds__(256) void ffn1_decode_mxfp4(const uint16_t* __restrict__ x,
+                                                         const int32_t* __restrict__ perm_src, const W wk,
+                                                         const char* __restrict__ slot_base, size_t slot_stride,
+                                                         size_t p1s_off, int H, int I, uint16_t* __restrict__ hbuf) {
+  const int NB = I / 8 / kR;  // blocks per expert
+  const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
+  int4 it;
+  if (!wk.get(item, it)) return;
+  const char* blob = slot_base + (size_t)it.x * slot_stride;
+  const int lane = threadIdx.x & 63;
+  mxfp4_decode_tiles([&](int m) { return x + (size_t)perm_src[it.y + m] * H; }, it, H, blob, blob + p1s_off, tile0,
+                     [&](int tile, int m, const f32x4_t& s) {
+                       const int i0 = 8 * tile + 2 * (lane >> 4);
+                       const uint32_t packed = (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) |
+                                               ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
+                       *reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0) = packed;
+                     });
+}
+
+template <typename W>
+__global__ __launch_bounds__(256) void ffn2_decode_mxfp4(const uint16_t* __restrict__ hbuf, const W wk,
+                                                         const char* __restrict__ slot_base, size_t slot_stride,
+                                                         size_t p2_off, size_t p2s_off, int H, int I,
+                                                         float* __restrict__ y) {
+  const int NB = H / 16 / kR;
+  const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
+  int4 it;
+  if (!wk.get(item, it)) return;
+  const char* blob = slot_base + (size_t)it.x * slot_stride;
+  const int lane = threadIdx.x & 63;
+  mxfp4_decode_tiles([&](int m) { return hbuf + (size_t)(it.y + m) * I; }, it, I, blob + p2_off, blob + p2s_off,
+                     tile0, [&](int tile, int m, const f32x4_t& s) {
+                       *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
+                     });
+}
+
+// ---------------------------------------------------------------------------
 // bf16 prefill GEMM. Tile: 128 weight rows x 128 tokens x 64 K, 4 waves each
 // computing 64 x 64 with 16 matrix-core instructions per 32-wide K chunk.
 // Both operands are staged in LDS in fragment order (two stages), so every
@@ -466,6 +568,16 @@ hipError_t decode_kernels(int wfmt, const void* x, const int32_t* perm_src, cons
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(ffn2_decode_bf16<W>, dim3(n_items * (H / 16)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(hbuf), wk, slot_base, slot_stride, L.p2, H, I, y);
+    return hipGetLastError();
+  }
+  if (wfmt == 3) {
+    hipLaunchKernelGGL(ffn1_decode_mxfp4<W>, dim3(n_items * (I / 8 / kR)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(x), perm_src, wk, slot_base, slot_stride, L.p1s, H, I,
+                       static_cast<uint16_t*>(hbuf));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(ffn2_decode_mxfp4<W>, dim3(n_items * (H / 16 / kR)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(hbuf), wk, slot_base, slot_stride, L.p2, L.p2s, H, I, y);
     return hipGetLastError();
   }
   // int4

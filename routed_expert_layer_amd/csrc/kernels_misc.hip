@@ -130,6 +130,64 @@ __global__ void pack_int4_kernel(const int8_t* __restrict__ Q1, const int8_t* __
   }
 }
 
+// Eight FP4 codes of column `col`, rows k0..k0+7 of a [K, ld] uint8 code
+// matrix, as nibbles in row order (nibble p = code of row k0 + p).
+__device__ __forceinline__ uint32_t pack_fp4_word(const uint8_t* C, int ld, int col, int k0) {
+  uint32_t w = 0;
+  for (int p = 0; p < 8; ++p) w |= ((uint32_t)C[(size_t)(k0 + p) * ld + col] & 0xFu) << (4 * p);
+  return w;
+}
+
+// MXFP4 blob: one thread per 16-byte code chunk, then one per 4-byte scale word.
+__global__ void pack_mxfp4_kernel(const uint8_t* __restrict__ C1, const uint8_t* __restrict__ C3,
+                                  const uint8_t* __restrict__ C2, const uint8_t* __restrict__ S1,
+                                  const uint8_t* __restrict__ S3, const uint8_t* __restrict__ S2, int H, int I,
+                                  char* __restrict__ blob, size_t p1s, size_t p2, size_t p2s) {
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int KG1 = H / 128, KG2 = I / 128;
+  const size_t c1 = (size_t)(2 * I / 16) * KG1 * 64;       // P1 code chunks
+  const size_t c2 = (size_t)(H / 16) * KG2 * 64;           // P2 code chunks
+  const size_t s1n = (size_t)(2 * I / 16) * KG1 * 16;      // P1 scale words
+  const size_t s2n = (size_t)(H / 16) * KG2 * 16;          // P2 scale words
+  if (q < c1) {
+    const int l = (int)(q % 64), g = (int)((q / 64) % KG1), t = (int)(q / (64 * (size_t)KG1));
+    int mat, i;
+    p1_row_source(16 * t + (l % 16), mat, i);
+    const uint8_t* C = mat ? C3 : C1;
+    uint32_t w[4];
+    for (int j = 0; j < 4; ++j) w[j] = pack_fp4_word(C, I, i, 128 * g + 32 * j + 8 * (l / 16));
+    *reinterpret_cast<uint4*>(blob + q * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    return;
+  }
+  size_t r = q - c1;
+  if (r < c2) {
+    const int l = (int)(r % 64), g = (int)((r / 64) % KG2), t = (int)(r / (64 * (size_t)KG2));
+    const int n = 16 * t + (l % 16);
+    uint32_t w[4];
+    for (int j = 0; j < 4; ++j) w[j] = pack_fp4_word(C2, H, n, 128 * g + 32 * j + 8 * (l / 16));
+    *reinterpret_cast<uint4*>(blob + p2 + r * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+    return;
+  }
+  r -= c2;
+  if (r < s1n) {
+    const int rr = (int)(r % 16), g = (int)((r / 16) % KG1), t = (int)(r / (16 * (size_t)KG1));
+    int mat, i;
+    p1_row_source(16 * t + rr, mat, i);
+    const uint8_t* S = mat ? S3 : S1;
+    uint32_t w = 0;
+    for (int j = 0; j < 4; ++j) w |= (uint32_t)S[(size_t)(4 * g + j) * I + i] << (8 * j);
+    reinterpret_cast<uint32_t*>(blob + p1s)[r] = w;
+    return;
+  }
+  r -= s1n;
+  if (r < s2n) {
+    const int rr = (int)(r % 16), g = (int)((r / 16) % KG2), t = (int)(r / (16 * (size_t)KG2));
+    uint32_t w = 0;
+    for (int j = 0; j < 4; ++j) w |= (uint32_t)S2[(size_t)(4 * g + j) * H + 16 * t + rr] << (8 * j);
+    reinterpret_cast<uint32_t*>(blob + p2s)[r] = w;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* y_perm, const int32_t* perm_pos, const float* w, int T, int k, int H,
@@ -168,6 +226,16 @@ hipError_t launch_pack(int wfmt, int H, int I, const void* W1, const void* W3, c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_pack_fragments(W2, I, H, b + L.p2, s);
+  }
+  if (wfmt == 3) {  // MXFP4 (alignment padding between sections is never read)
+    const size_t n = (size_t)(2 * I / 16) * (H / 128) * 64 + (size_t)(H / 16) * (I / 128) * 64 +
+                     (size_t)(2 * I / 16) * (H / 128) * 16 + (size_t)(H / 16) * (I / 128) * 16;
+    hipLaunchKernelGGL(pack_mxfp4_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(W1), static_cast<const uint8_t*>(W3),
+                       static_cast<const uint8_t*>(W2), static_cast<const uint8_t*>(s1),
+                       static_cast<const uint8_t*>(s3), static_cast<const uint8_t*>(s2), H, I, b, L.p1s, L.p2,
+                       L.p2s);
+    return hipGetLastError();
   }
   // int4 (alignment padding between sections is never read)
   const size_t n = (size_t)(2 * I / 16) * (H / 128) * 64 + (size_t)(H / 16) * (I / 128) * 64 +

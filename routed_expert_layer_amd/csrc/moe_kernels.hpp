@@ -28,6 +28,13 @@ namespace moe {
 //   code(k1),code(k3),code(k5),code(k7); nibble = q + 8.
 //   Scales: per row tile and block, the 16 rows' fp16 scales (32 B).
 //   Sections: [P1 codes][P1 scales][P2 codes][P2 scales], 256-B aligned.
+// MXFP4 (MOE_W_MXFP4): the same row order. A row tile is K/128 blocks of
+//   1 KiB of FP4 (E2M1) codes; block g, byte 16*l..16*l+15 = four 32-bit
+//   words, word j holding row (l%16), columns 128g + 32j + 8(l/16) + 0..7
+//   as nibbles in column order (nibble p = bits 4p..4p+3).
+//   Scales: per row tile and block, 64 bytes of E8M0 scales, byte 4r + j =
+//   scale of row r, columns 128g + 32j .. +31 (one scale per 32 of K).
+//   Sections: [P1 codes][P1 scales][P2 codes][P2 scales], 256-B aligned.
 // fp32 (MOE_W_F32): W1 [H,I], W3 [H,I], W2 [I,H] row-major, concatenated.
 // ---------------------------------------------------------------------------
 struct BlobLayout {
@@ -43,6 +50,12 @@ inline BlobLayout blob_layout(int wfmt, int H, int I) {
     b.p1 = 0; b.p2 = 2 * HI * 4; b.bytes = 3 * HI * 4;
   } else if (wfmt == 1) {  // bf16
     b.p1 = 0; b.p2 = 2 * HI * 2; b.bytes = 3 * HI * 2;
+  } else if (wfmt == 3) {  // MXFP4
+    b.p1 = 0;
+    b.p1s = align_up(HI, 256);                                   // 2HI codes * 0.5 B
+    b.p2 = align_up(b.p1s + (size_t)(2 * I / 16) * (H / 128) * 64, 256);
+    b.p2s = align_up(b.p2 + HI / 2, 256);
+    b.bytes = align_up(b.p2s + (size_t)(H / 16) * (I / 128) * 64, 256);
   } else {  // int4
     b.p1 = 0;
     b.p1s = align_up(b.p1 + HI, 256);                       // 2HI codes * 0.5 B

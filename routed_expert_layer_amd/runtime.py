@@ -21,7 +21,7 @@ import torch
 
 from . import _lib as L
 
-WFMT = {"f32": L.MOE_W_F32, "bf16": L.MOE_W_BF16, "int4": L.MOE_W_INT4}
+WFMT = {"f32": L.MOE_W_F32, "bf16": L.MOE_W_BF16, "int4": L.MOE_W_INT4, "mxfp4": L.MOE_W_MXFP4}
 
 
 def _align(v, a):
@@ -68,7 +68,8 @@ class ExpertStore:
         """Pack every expert of physical layer `layer` into the pool.
 
         make_expert(e) returns canonical device tensors: (W1, W3, W2) for fp32/bf16,
-        or a dict with q1, q3, q2 (int8) and s1, s3, s2 (fp16) for int4.
+        a dict with q1, q3, q2 (int8) and s1, s3, s2 (fp16) for int4, or a dict with
+        c1, c3, c2 (uint8 FP4 codes) and s1, s3, s2 (uint8 E8M0 scales) for MXFP4.
         """
         assert 0 <= layer < self.P
         stage = torch.empty(batch * self.stride, dtype=torch.uint8, device=device)
@@ -80,6 +81,9 @@ class ExpertStore:
                 dst = stage[j * self.stride:]
                 if self.wfmt == L.MOE_W_INT4:
                     L.moe_pack_expert(self.wfmt, self.H, self.I, w["q1"], w["q3"], w["q2"], w["s1"], w["s3"],
+                                      w["s2"], dst)
+                elif self.wfmt == L.MOE_W_MXFP4:
+                    L.moe_pack_expert(self.wfmt, self.H, self.I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"],
                                       w["s2"], dst)
                 else:
                     L.moe_pack_expert(self.wfmt, self.H, self.I, w[0], w[1], w[2], None, None, None, dst)

@@ -32,6 +32,11 @@ def small_int4():
                                I=256, k=4, zipf_s=1.0, epoch=6, S=16, weights_of=None, pool_layers=None)
 
 
+def small_mxfp4():
+    return dataclasses.replace(CONFIGS["decode_mxfp4_t8_l8"], name="devsmall_mxfp4", L=2, T=4, steps=24, H=256,
+                               E=16, I=256, k=4, zipf_s=1.0, epoch=6, S=16, weights_of=None, pool_layers=None)
+
+
 def oracle_trace(sim):
     return np.array([[r.step, r.layer, r.key, r.hit, r.slot, r.victim, r.wave] for r in sim.trace], np.int64)
 
@@ -94,6 +99,11 @@ def test_device_small_bf16_all_outputs(S):
 def test_device_small_int4_all_outputs():
     ref = run_device(small_int4(), 24, set(), check_all=True)
     assert (ref[:, 5] >= 0).any(), "the small int4 config should evict"
+
+
+def test_device_small_mxfp4_all_outputs():
+    ref = run_device(small_mxfp4(), 24, set(), check_all=True)
+    assert (ref[:, 5] >= 0).any(), "the small MXFP4 config should evict"
 
 
 @pytest.mark.timeout(600)

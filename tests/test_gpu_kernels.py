@@ -101,6 +101,8 @@ def _experts(cfg, n, wfmt):
     for e in range(n):
         if wfmt == "int4":
             out.append(gen.expert_int4(cfg, 0, e, dev))
+        elif wfmt == "mxfp4":
+            out.append(gen.expert_mxfp4(cfg, 0, e, dev))
         else:
             out.append(gen.expert_weights(cfg, 0, e, dev))
     return out
@@ -110,6 +112,9 @@ def _canon64(w, wfmt, group=128):
     if wfmt == "int4":
         return (oracle.dequant_int4(w["q1"], w["s1"], group), oracle.dequant_int4(w["q3"], w["s3"], group),
                 oracle.dequant_int4(w["q2"], w["s2"], group))
+    if wfmt == "mxfp4":
+        return (oracle.dequant_mxfp4(w["c1"], w["s1"]), oracle.dequant_mxfp4(w["c3"], w["s3"]),
+                oracle.dequant_mxfp4(w["c2"], w["s2"]))
     return tuple(np64(t) for t in w)
 
 
@@ -122,6 +127,8 @@ FFN_CASES = [
     ("bf16_prefill_c3shape", "bf16", 2048, 768, [70, 3, 129], "prefill"),
     ("int4_decode", "int4", 512, 256, [1, 8, 0, 3, 20], "decode"),
     ("int4_decode_wide", "int4", 1024, 384, [2, 16, 5], "decode"),
+    ("mxfp4_decode", "mxfp4", 512, 256, [1, 8, 0, 3, 20], "decode"),
+    ("mxfp4_decode_wide", "mxfp4", 1024, 384, [2, 16, 5, 33], "auto"),
 ]
 
 
@@ -136,7 +143,7 @@ def test_ffn_parity(L, name, wfmt, H, I, rows, mode):
     r = np.random.default_rng(len(name))
     perm_src = np.concatenate([r.integers(0, T, size=n) for n in rows]).astype(np.int32)
     off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
-    wf = {"f32": L.MOE_W_F32, "bf16": L.MOE_W_BF16, "int4": L.MOE_W_INT4}[wfmt]
+    wf = {"f32": L.MOE_W_F32, "bf16": L.MOE_W_BF16, "int4": L.MOE_W_INT4, "mxfp4": L.MOE_W_MXFP4}[wfmt]
     blob = L.moe_expert_bytes(wf, H, I)
     stride = (blob + 4095) // 4096 * 4096
     slot_of = [(e + 1) % E for e in range(E)]  # non-identity slot mapping
@@ -147,6 +154,8 @@ def test_ffn_parity(L, name, wfmt, H, I, rows, mode):
         dst = slots[slot_of[e] * stride:]
         if wfmt == "int4":
             L.moe_pack_expert(wf, H, I, w["q1"], w["q3"], w["q2"], w["s1"], w["s3"], w["s2"], dst)
+        elif wfmt == "mxfp4":
+            L.moe_pack_expert(wf, H, I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"], w["s2"], dst)
         else:
             L.moe_pack_expert(wf, H, I, w[0], w[1], w[2], None, None, None, dst)
     work = np.array([[e, slot_of[e], off[e], rows[e]] for e in range(E)], dtype=np.int32)
@@ -207,3 +216,19 @@ def test_pack_matches_documented_layout(L):
     torch.cuda.synchronize()
     ref = bf16_blob(W1.cpu(), W3.cpu(), W2.cpu())
     assert np.array_equal(blob.cpu().numpy().view(np.uint16), ref)
+
+
+@pytest.mark.gpu
+def test_pack_mxfp4_matches_documented_layout(L):
+    """The GPU packer writes the MXFP4 blob layout the C ABI documents, byte for byte (padding aside)."""
+    from tests.blob_layout import mxfp4_blob
+    cfg = dataclasses.replace(CONFIGS["decode_mxfp4_t8_l8"], name="packmx", H=512, I=384, weights_of=None,
+                              pool_layers=None)
+    w = gen.expert_mxfp4(cfg, 0, 3, "cuda")
+    nb = L.moe_expert_bytes(L.MOE_W_MXFP4, cfg.H, cfg.I)
+    blob = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    L.moe_pack_expert(L.MOE_W_MXFP4, cfg.H, cfg.I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"], w["s2"], blob)
+    torch.cuda.synchronize()
+    ref = mxfp4_blob(*(w[k].cpu().numpy() for k in ("c1", "c3", "c2", "s1", "s3", "s2")))
+    assert len(ref) == nb
+    assert np.array_equal(blob.cpu().numpy(), ref)

@@ -35,6 +35,10 @@ class ExpertCache64:
                 g = self.cfg.group
                 self.d[e] = (oracle.dequant_int4(w["q1"], w["s1"], g), oracle.dequant_int4(w["q3"], w["s3"], g),
                              oracle.dequant_int4(w["q2"], w["s2"], g))
+            elif self.cfg.wfmt == "mxfp4":
+                w = gen.expert_mxfp4(self.cfg, self.layer, e, dev)
+                self.d[e] = (oracle.dequant_mxfp4(w["c1"], w["s1"]), oracle.dequant_mxfp4(w["c3"], w["s3"]),
+                             oracle.dequant_mxfp4(w["c2"], w["s2"]))
             else:
                 self.d[e] = tuple(np64(t) for t in gen.expert_weights(self.cfg, self.layer, e, dev))
         return self.d[e]
@@ -58,6 +62,8 @@ def make_store(cfg):
         print(f"  packing layer {layer} ({cfg.E} experts)", flush=True)
         if cfg.wfmt == "int4":
             store.pack_layer(layer, lambda e: gen.expert_int4(cfg, layer, e, dev))
+        elif cfg.wfmt == "mxfp4":
+            store.pack_layer(layer, lambda e: gen.expert_mxfp4(cfg, layer, e, dev))
         else:
             store.pack_layer(layer, lambda e: gen.expert_weights(cfg, layer, e, dev))
     return store
@@ -144,6 +150,12 @@ def test_stack48_bf16_cut():
 @pytest.mark.timeout(600)
 def test_decode_int4_cut():
     cfg = CONFIGS["decode_int4_t8_l8"]
+    run_decode(cfg, 48, {(0, 0), (5, 3), (47, 7)})
+
+
+@pytest.mark.timeout(600)
+def test_decode_mxfp4_cut():
+    cfg = CONFIGS["decode_mxfp4_t8_l8"]
     run_decode(cfg, 48, {(0, 0), (5, 3), (47, 7)})
 
 

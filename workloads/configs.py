@@ -31,7 +31,7 @@ class Config:
     I: int                 # SwiGLU intermediate size
     k: int                 # experts per token
     act: str               # activation/router dtype: "f32" | "bf16"
-    wfmt: str              # expert weight format: "f32" | "bf16" | "int4"
+    wfmt: str              # expert weight format: "f32" | "bf16" | "int4" | "mxfp4"
     zipf_s: float = 0.0    # router-bias skew (0: no bias)
     epoch: Optional[int] = None   # bias re-permuted every `epoch` steps
     S: Optional[int] = None       # cache slots (None: every expert resident)
@@ -63,6 +63,11 @@ CONFIGS = {
     "prefill_db_bf16_t16384_l8": Config("prefill_db_bf16_t16384_l8", L=8, T=16384, steps=1, H=4096, E=256,
                                         I=2048, k=6, act="bf16", wfmt="bf16", zipf_s=1.5, phase="prefill",
                                         pool_layers=4),
+    # MXFP4 decode on the same 8 layers (the same bf16 weights in the OCP MX FP4 format), batch 8,
+    # 512-entry shared cache
+    "decode_mxfp4_t8_l8": Config("decode_mxfp4_t8_l8", L=8, T=8, steps=256, H=4096, E=256, I=2048, k=6,
+                                 act="bf16", wfmt="mxfp4", zipf_s=1.5, S=512,
+                                 weights_of="prefill_db_bf16_t16384_l8", pool_layers=4),
     # int4 decode on the same 8 layers, batch 8, 512-entry shared cache
     "decode_int4_t8_l8": Config("decode_int4_t8_l8", L=8, T=8, steps=256, H=4096, E=256, I=2048, k=6,
                                 act="bf16", wfmt="int4", zipf_s=1.5, S=512,
