@@ -39,6 +39,20 @@ where; reading taken here:
 
 rate_cpu = 0 (the default) fills every miss.
 
+The cache can be resized at a safe point, between layer-steps (page
+"FreeToken-rtx-4090", runtime layer table, row "GPU memory": cache capacity can
+change during runtime, and the phase table, row "Long sessions"; page
+"FreeToken-benchmark", section "Elastic Cache": capacity is rebuilt without
+reloading the host pool). The pages give no procedure; reading taken here:
+
+  * resizing to S' slots keeps the min(S', resident) most recently used
+    entries, with their recency order, and evicts the others (no trace
+    records; the pool is untouched);
+  * a kept entry in a slot below S' stays in its slot; the kept entries in
+    slots at or above S' move, in ascending order of their old slot, to the
+    lowest free slots below S' (each move is one copy of a blob);
+  * growing adds free slots and moves nothing.
+
 It keeps explicit per-slot last-use stamps rather than an ordered container,
 so that the tests can check it against a textbook ordered-dict LRU.
 """
@@ -113,3 +127,27 @@ class SharedLRU:
             recs.append(TraceRec(step, layer, key, 0, -1, -1, -1))
         self.trace.extend(recs)
         return waves, recs
+
+    def resize(self, S_new):
+        """Resize to S_new slots at a safe point. Returns the moves [(key, old slot, new slot)]."""
+        assert S_new >= 1
+        occupied = [sl for sl in range(self.S) if self.slot_key[sl] != -1]
+        keep = set(sorted(occupied, key=lambda sl: self.last_use[sl], reverse=True)[:S_new])
+        for sl in occupied:
+            if sl not in keep:
+                del self.key_slot[self.slot_key[sl]]
+                self.slot_key[sl] = -1
+                self.last_use[sl] = 0
+        new_key, new_use = [-1] * S_new, [0] * S_new
+        for sl in range(min(self.S, S_new)):
+            new_key[sl], new_use[sl] = self.slot_key[sl], self.last_use[sl]
+        free = [sl for sl in range(S_new) if new_key[sl] == -1]
+        moves = []
+        for sl in range(S_new, self.S):
+            if self.slot_key[sl] != -1:
+                d = free.pop(0)
+                new_key[d], new_use[d] = self.slot_key[sl], self.last_use[sl]
+                self.key_slot[new_key[d]] = d
+                moves.append((new_key[d], sl, d))
+        self.S, self.slot_key, self.last_use = S_new, new_key, new_use
+        return moves

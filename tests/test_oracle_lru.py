@@ -143,3 +143,49 @@ def test_split_cpu_misses_leave_cache_untouched():
         _, recs2 = plain.resolve(step, 0, 20, sorted(rc.key for rc in gpu))
         assert [(rc.key, rc.hit, rc.slot, rc.victim, rc.wave) for rc in gpu] == \
             [(rc.key, rc.hit, rc.slot, rc.victim, rc.wave) for rc in recs2]
+
+
+def _textbook_after(sim, tb, S_new):
+    """A textbook LRU of S_new slots holding the oracle's kept entries, in the textbook's recency order."""
+    t2 = TextbookLRU(S_new)
+    order = list(tb.od.keys())[-S_new:] if S_new < len(tb.od) else list(tb.od.keys())
+    for k in order:
+        t2.od[k] = sim.key_slot[k]
+    t2.free = [s for s in range(S_new) if s not in set(t2.od.values())]
+    return t2
+
+
+@pytest.mark.parametrize("S,S_new,E,L", [(16, 5, 32, 2), (8, 3, 12, 1), (6, 6, 10, 2), (4, 9, 12, 2), (8, 1, 9, 1)])
+def test_resize_keeps_most_recent_and_continues_as_textbook_lru(S, S_new, E, L):
+    r = np.random.default_rng(S * 31 + S_new)
+    sim = oracle.SharedLRU(S)
+    tb = TextbookLRU(S)
+
+    def run(steps, step0, cap):
+        for step in range(step0, step0 + steps):
+            for layer in range(L):
+                n = int(r.integers(1, min(cap, E) + 1))
+                experts = sorted(r.choice(E, size=n, replace=False).tolist())
+                _, recs = sim.resolve(step, layer, E, experts)
+                for rc in recs:
+                    hit, slot, victim = tb.access(rc.key)
+                    assert (rc.hit, rc.slot, rc.victim) == (int(hit), slot, victim)
+
+    run(20, 0, S)
+    before = dict(sim.key_slot)
+    recent = list(tb.od.keys())[-S_new:] if S_new < len(tb.od) else list(tb.od.keys())
+    moves = sim.resize(S_new)
+    # the survivors are exactly the S_new most recently used keys
+    assert set(sim.key_slot) == set(recent)
+    # moves take entries from slots >= S_new to distinct free slots < S_new; the others stay put
+    targets = [d for _, _, d in moves]
+    assert all(f >= S_new and d < S_new and before[k] == f for k, f, d in moves)
+    assert len(set(targets)) == len(targets)
+    stay = {k: s for k, s in before.items() if k in sim.key_slot and s < S_new}
+    assert all(sim.key_slot[k] == s for k, s in stay.items())
+    assert not set(targets) & set(stay.values())
+    if S_new >= S:
+        assert moves == []
+    # afterwards the cache behaves as a textbook LRU of S_new slots holding those keys
+    tb = _textbook_after(sim, tb, S_new)
+    run(20, 20, S_new)
