@@ -182,11 +182,25 @@ int moe_pool_free(void* pool);
  *
  * moe_cache_invalidate: drop a key (e.g. after a failed fill) so that it is
  * not left half-resident; its slot becomes free. MOE_EINVAL if not resident.
+ *
+ * moe_cache_resize (page "FreeToken-rtx-4090", runtime layer table, row "GPU
+ * memory": cache capacity can change during runtime; page
+ * "FreeToken-benchmark", section "Elastic Cache": capacity is rebuilt at safe
+ * points without reloading the host pool): at a point where no layer-step is
+ * in flight, the cache gets S_new slots. The min(S_new, resident) most
+ * recently used entries are kept with their recency order, the others are
+ * evicted (no trace records); a kept entry in a slot below S_new keeps it, the
+ * kept entries at or above S_new move, in ascending old slot, to the lowest
+ * free slots below S_new. moves[0..*n_moves) lists them (key, old slot, new
+ * slot): copy each blob before the slots are used again. Growing moves
+ * nothing. Errors: ECAPACITY (S_new < 1), EINVAL (null, more moves than
+ * max_moves; the cache is then unchanged). moe_cache_capacity: current S.
  * moe_cache_slot_of: *slot = slot of key or -1.
  * A handle must not be used from two threads at once.
  * ------------------------------------------------------------------------ */
 typedef struct moe_cache moe_cache_t;
 typedef struct { int32_t key, slot, victim, wave; } moe_miss_t;
+typedef struct { int32_t key, from_slot, to_slot; } moe_move_t;
 typedef struct { int32_t step, layer, key, hit, slot, victim, wave; } moe_trace_t;
 
 moe_cache_t* moe_cache_create(int L, int E, int S, int* status);
@@ -200,6 +214,8 @@ int moe_cache_clear_trace(moe_cache_t* cache);
 int moe_cache_invalidate(moe_cache_t* cache, int key);
 int moe_cache_slot_of(const moe_cache_t* cache, int key, int* slot);
 int moe_cache_stats(const moe_cache_t* cache, int64_t* hits, int64_t* misses);
+int moe_cache_resize(moe_cache_t* cache, int S_new, moe_move_t* moves, int max_moves, int* n_moves);
+int moe_cache_capacity(const moe_cache_t* cache);
 
 /* ------------------------------------------------------------------------ *
  * Miss fills over the host link.
@@ -334,6 +350,13 @@ int moe_pipe_copy_ms(moe_pipe_t* pipe, int layer, float* ms);
  *   number of bracketed calls.
  * moe_decoder_fills: total fills issued by this decoder.
  * moe_decoder_cpu_runs: total misses this decoder ran on the CPU.
+ * moe_decoder_resize: moe_cache_resize on the decoder's cache, plus the blob
+ *   copies on `stream` (ordered after the decoder's earlier steps on it):
+ *   each move, and when slot_base is not NULL (a new caller-owned buffer of at
+ *   least S_new * slot_stride bytes) every kept entry into it; the decoder
+ *   then uses that buffer (free the old one once the stream has passed the
+ *   copies). slot_base NULL keeps the buffer, which must then hold S_new
+ *   slots. Errors as moe_cache_resize, EHIP.
  * ------------------------------------------------------------------------ */
 typedef struct moe_decoder moe_decoder_t;
 typedef struct {
@@ -362,6 +385,7 @@ int moe_decoder_profile(moe_decoder_t* decoder, int every);
 int moe_decoder_ffn_stats(moe_decoder_t* decoder, double* bytes, double* ms, int64_t* launches);
 int moe_decoder_fills(const moe_decoder_t* decoder, int64_t* fills);
 int moe_decoder_cpu_runs(const moe_decoder_t* decoder, int64_t* runs);
+int moe_decoder_resize(moe_decoder_t* decoder, int S_new, void* slot_base, void* stream);
 
 /* ---------------------------------------------------------------------------
  * CPU execution of an expert (page "FreeToken-rtx-4090", component table row
@@ -425,6 +449,12 @@ int moe_cpu_threads(void);
  *   sets *n_records to the number of accesses traced since then (may exceed
  *   the capacity). Records are as moe_trace_t with step = the sequence number
  *   of the resolve call that made them (0, 1, ... from creation) and wave 0.
+ * moe_device_decoder_resize: the resize of moe_cache_resize (same kept
+ *   entries, slots and moves) on the device tables: waits for `stream` (the
+ *   safe point), plans on the host, copies the blobs as moe_decoder_resize
+ *   does, rewrites the tables (reallocated when S changes), and waits again.
+ *   S_new must stay >= min(E, k*T_max). Graphs captured before a resize read
+ *   the old tables and buffer: capture again. Errors: ECAPACITY, EHIP, ENOMEM.
  * moe_device_decoder_clear_trace, moe_device_decoder_slot_of: as for the host
  *   cache. stats, trace and slot_of read GPU memory with blocking copies: call
  *   them once the stream's steps have completed.
@@ -452,6 +482,7 @@ int moe_device_decoder_trace(const moe_device_decoder_t* decoder, moe_trace_t* o
                              int64_t* n_records);
 int moe_device_decoder_clear_trace(moe_device_decoder_t* decoder);
 int moe_device_decoder_slot_of(const moe_device_decoder_t* decoder, int key, int* slot);
+int moe_device_decoder_resize(moe_device_decoder_t* decoder, int S_new, void* slot_base, void* stream);
 
 int moe_graph_begin(void* stream);
 moe_graph_t* moe_graph_end(void* stream, int* status);

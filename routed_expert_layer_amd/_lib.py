@@ -29,6 +29,7 @@ SYMBOLS = [
     "moe_device_decoder_create", "moe_device_decoder_destroy", "moe_device_decoder_step", "moe_device_decoder_stats",
     "moe_device_decoder_trace", "moe_device_decoder_clear_trace", "moe_device_decoder_slot_of",
     "moe_graph_begin", "moe_graph_end", "moe_graph_launch", "moe_graph_destroy",
+    "moe_cache_resize", "moe_cache_capacity", "moe_decoder_resize", "moe_device_decoder_resize",
 ]
 
 
@@ -111,6 +112,10 @@ _sig("moe_graph_begin", I32, P)
 _sig("moe_graph_end", P, P, PI)
 _sig("moe_graph_launch", I32, P, P)
 _sig("moe_graph_destroy", I32, P)
+_sig("moe_cache_resize", I32, P, I32, P, I32, PI)
+_sig("moe_cache_capacity", I32, P)
+_sig("moe_decoder_resize", I32, P, I32, P, P)
+_sig("moe_device_decoder_resize", I32, P, I32, P, P)
 
 
 def _check(code, what=""):
@@ -523,3 +528,26 @@ def moe_graph_launch(graph, stream=None):
 
 def moe_graph_destroy(graph):
     graph.close()
+
+
+# ---------------------------------------------------------------------------
+def moe_cache_resize(cache, S_new):
+    """Resize the host cache policy; returns int32 [n, 3] moves (key, old slot, new slot)."""
+    cap = max(moe_cache_capacity(cache), 1)
+    out = np.zeros((cap, 3), np.int32)
+    n = ctypes.c_int(0)
+    _check(_lib.moe_cache_resize(cache.h, int(S_new), out.ctypes.data, cap, ctypes.byref(n)), "moe_cache_resize")
+    return out[:n.value]
+
+
+def moe_cache_capacity(cache):
+    return _lib.moe_cache_capacity(cache.h)
+
+
+def moe_decoder_resize(dec, S_new, slot_base=None, stream=None):
+    _check(_lib.moe_decoder_resize(dec.h, int(S_new), _ptr(slot_base), _stream(stream)), "moe_decoder_resize")
+
+
+def moe_device_decoder_resize(dec, S_new, slot_base=None, stream=None):
+    _check(_lib.moe_device_decoder_resize(dec.h, int(S_new), _ptr(slot_base), _stream(stream)),
+           "moe_device_decoder_resize")

@@ -246,6 +246,24 @@ int moe_cache_slot_of(const moe_cache_t* c, int key, int* slot) {
   return MOE_OK;
 }
 
+int moe_cache_resize(moe_cache_t* c, int S_new, moe_move_t* moves, int max_moves, int* n_moves) {
+  if (!c || !n_moves || max_moves < 0 || (max_moves > 0 && !moves))
+    return fail(MOE_EINVAL, "moe_cache_resize: null argument");
+  if (S_new < 1) return fail(MOE_ECAPACITY, "moe_cache_resize: the cache needs at least one slot (S=%d)", S_new);
+  std::vector<moe::Move> mv;
+  moe::SharedLru next = c->lru;  // planned on a copy, so that a short move array changes nothing
+  next.resize(S_new, mv);
+  if ((int)mv.size() > max_moves)
+    return fail(MOE_EINVAL, "moe_cache_resize: %d moves do not fit %d", (int)mv.size(), max_moves);
+  c->lru = std::move(next);
+  c->S = S_new;
+  for (size_t i = 0; i < mv.size(); ++i) moves[i] = moe_move_t{mv[i].key, mv[i].from, mv[i].to};
+  *n_moves = (int)mv.size();
+  return MOE_OK;
+}
+
+int moe_cache_capacity(const moe_cache_t* c) { return c ? c->S : 0; }
+
 int moe_cache_stats(const moe_cache_t* c, int64_t* hits, int64_t* misses) {
   if (!c || !hits || !misses) return fail(MOE_EINVAL, "moe_cache_stats: null pointer");
   *hits = c->lru.hits();

@@ -273,6 +273,44 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   return MOE_OK;
 }
 
+int moe_decoder_resize(moe_decoder_t* d, int S_new, void* slot_base, void* stream) {
+  if (!d) return dfail(MOE_EINVAL, "moe_decoder_resize: null decoder");
+  const int S_old = moe_cache_capacity(d->cache);
+  int n_layers = 0;
+  (void)moe_cache_layers(d->cache, &n_layers);
+  // slots of the resident entries before the resize
+  std::vector<std::pair<int, int>> resident;  // (key, slot)
+  for (int key = 0; key < n_layers * d->E; ++key) {
+    int sl = -1;
+    if (moe_cache_slot_of(d->cache, key, &sl) == MOE_OK && sl >= 0) resident.emplace_back(key, sl);
+  }
+  std::vector<moe_move_t> moves(S_old > 0 ? S_old : 1);
+  int nm = 0;
+  int rc = moe_cache_resize(d->cache, S_new, moves.data(), (int)moves.size(), &nm);
+  if (rc != MOE_OK) return dfail(rc, "moe_decoder_resize: %s", moe_last_error());
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* old_base = static_cast<char*>(d->slot_base);
+  char* new_base = slot_base ? static_cast<char*>(slot_base) : old_base;
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < nm && e == hipSuccess; ++i)
+    e = hipMemcpyAsync(new_base + (size_t)moves[i].to_slot * d->slot_stride,
+                       old_base + (size_t)moves[i].from_slot * d->slot_stride, d->blob_bytes,
+                       hipMemcpyDeviceToDevice, s);
+  if (new_base != old_base) {
+    // entries that keep their slot still change buffer
+    for (const auto& kv : resident) {
+      int sl = -1;
+      (void)moe_cache_slot_of(d->cache, kv.first, &sl);
+      if (sl >= 0 && sl == kv.second && e == hipSuccess)
+        e = hipMemcpyAsync(new_base + (size_t)sl * d->slot_stride, old_base + (size_t)sl * d->slot_stride,
+                           d->blob_bytes, hipMemcpyDeviceToDevice, s);
+    }
+  }
+  if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_resize: copy: %s", hipGetErrorString(e));
+  d->slot_base = new_base;
+  return MOE_OK;
+}
+
 int moe_decoder_profile(moe_decoder_t* d, int every) {
   if (!d || every < 0) return dfail(MOE_EINVAL, "moe_decoder_profile: null decoder or negative period");
   d->prof_every = every;

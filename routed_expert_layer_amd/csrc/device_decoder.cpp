@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/moe.h"
+#include "lru_policy.hpp"
 #include "moe_kernels.hpp"
 
 extern "C" size_t moe_route_workspace_size(int T, int H, int E, int k);
@@ -34,6 +35,44 @@ struct moe_device_decoder {
   moe::DevCache c{};
   int max_items;
 };
+
+namespace {
+// Offsets of the control data in its allocation (256-byte aligned pieces).
+struct CtlLayout {
+  size_t slot_of, slot_key, stamp, ctl, work, miss, n, trace, total;
+};
+CtlLayout ctl_layout(size_t n_keys, int S, int max_items, int64_t trace_cap) {
+  CtlLayout o{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = moe::align_up(off + bytes, 256);
+    return at;
+  };
+  o.slot_of = take(n_keys * 4);
+  o.slot_key = take((size_t)S * 4);
+  o.stamp = take((size_t)S * 8);
+  o.ctl = take(8 * 8);
+  o.work = take((size_t)max_items * 16);
+  o.miss = take((size_t)max_items * 16);
+  o.n = take(2 * 4);
+  o.trace = take((size_t)trace_cap * 7 * 4);
+  o.total = off;
+  return o;
+}
+void point_into(moe::DevCache& c, char* m, const CtlLayout& o, int S, int64_t trace_cap) {
+  c.slot_of = reinterpret_cast<int32_t*>(m + o.slot_of);
+  c.slot_key = reinterpret_cast<int32_t*>(m + o.slot_key);
+  c.stamp = reinterpret_cast<uint64_t*>(m + o.stamp);
+  c.ctl = reinterpret_cast<uint64_t*>(m + o.ctl);
+  c.S = S;
+  c.work = reinterpret_cast<int4*>(m + o.work);
+  c.miss = reinterpret_cast<int4*>(m + o.miss);
+  c.n = reinterpret_cast<int32_t*>(m + o.n);
+  c.trace = reinterpret_cast<int32_t*>(m + o.trace);
+  c.trace_cap = trace_cap;
+}
+}  // namespace
 
 struct moe_graph {
   hipGraph_t graph = nullptr;
@@ -93,38 +132,19 @@ moe_device_decoder_t* moe_device_decoder_create(int L, int E, int S, int T_max, 
     d->pool.push_back(static_cast<const char*>(dp));
   }
   // control data, 256-byte aligned pieces of one allocation
-  const size_t n_keys = (size_t)L * E;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off = moe::align_up(off + bytes, 256);
-    return o;
-  };
-  const size_t o_slot_of = take(n_keys * 4), o_slot_key = take((size_t)S * 4), o_stamp = take((size_t)S * 8),
-               o_ctl = take(8 * 8), o_work = take((size_t)max_items * 16), o_miss = take((size_t)max_items * 16),
-               o_n = take(2 * 4), o_trace = take((size_t)trace_capacity * 7 * 4);
-  hipError_t e = hipMalloc(&d->mem, off);
+  const CtlLayout o = ctl_layout((size_t)L * E, S, max_items, trace_capacity);
+  hipError_t e = hipMalloc(&d->mem, o.total);
   if (e != hipSuccess) {
     d->mem = nullptr;
     dd_release(d);
     if (status) *status = dd_fail(MOE_ENOMEM, "moe_device_decoder_create: %s", hipGetErrorString(e));
     return nullptr;
   }
+  point_into(d->c, static_cast<char*>(d->mem), o, S, trace_capacity);
   char* m = static_cast<char*>(d->mem);
-  moe::DevCache& c = d->c;
-  c.slot_of = reinterpret_cast<int32_t*>(m + o_slot_of);
-  c.slot_key = reinterpret_cast<int32_t*>(m + o_slot_key);
-  c.stamp = reinterpret_cast<uint64_t*>(m + o_stamp);
-  c.ctl = reinterpret_cast<uint64_t*>(m + o_ctl);
-  c.S = S;
-  c.work = reinterpret_cast<int4*>(m + o_work);
-  c.miss = reinterpret_cast<int4*>(m + o_miss);
-  c.n = reinterpret_cast<int32_t*>(m + o_n);
-  c.trace = reinterpret_cast<int32_t*>(m + o_trace);
-  c.trace_cap = trace_capacity;
   // empty cache: every key unmapped (-1 bytes), every slot free, clocks zero
-  e = hipMemset(m + o_slot_of, 0xFF, o_stamp - o_slot_of);
-  if (e == hipSuccess) e = hipMemset(m + o_stamp, 0, o_trace - o_stamp);
+  e = hipMemset(m + o.slot_of, 0xFF, o.stamp - o.slot_of);
+  if (e == hipSuccess) e = hipMemset(m + o.stamp, 0, o.trace - o.stamp);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     dd_release(d);
@@ -166,6 +186,70 @@ int moe_device_decoder_step(moe_device_decoder_t* d, int layer, const void* x, i
   if (e == hipSuccess)
     e = moe::launch_combine(b.y_perm, b.perm_pos, b.topk_w, T, d->k, d->H, out, out_dtype == MOE_DT_BF16, s);
   if (e != hipSuccess) return dd_fail(MOE_EHIP, "moe_device_decoder_step: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int moe_device_decoder_resize(moe_device_decoder_t* d, int S_new, void* slot_base, void* stream) {
+  if (!d) return dd_fail(MOE_EINVAL, "moe_device_decoder_resize: null decoder");
+  if (S_new < d->max_items)
+    return dd_fail(MOE_ECAPACITY, "moe_device_decoder_resize: S must stay at least min(E, k*T_max) = %d",
+                   d->max_items);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // safe point: every step enqueued so far has finished
+  hipError_t e = hipStreamSynchronize(s);
+  const int S_old = d->S;
+  const size_t n_keys = (size_t)d->L * d->E;
+  std::vector<int32_t> slot_key(S_old);
+  std::vector<uint64_t> stamp(S_old);
+  if (e == hipSuccess) e = hipMemcpy(slot_key.data(), d->c.slot_key, (size_t)S_old * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(stamp.data(), d->c.stamp, (size_t)S_old * 8, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return dd_fail(MOE_EHIP, "moe_device_decoder_resize: %s", hipGetErrorString(e));
+  std::vector<int32_t> new_key, origin, evicted;
+  std::vector<moe::Move> moves;
+  moe::plan_resize(slot_key, stamp, S_new, new_key, origin, moves, evicted);
+  std::vector<uint64_t> new_stamp(S_new, 0);
+  std::vector<int32_t> slot_of(n_keys, -1);
+  for (int sl = 0; sl < S_new; ++sl)
+    if (origin[sl] >= 0) {
+      new_stamp[sl] = stamp[origin[sl]];
+      slot_of[new_key[sl]] = sl;
+    }
+  // the blobs: moved entries, and every kept entry when the buffer changes
+  char* old_base = d->slot_base;
+  char* new_base = slot_base ? static_cast<char*>(slot_base) : old_base;
+  for (int sl = 0; sl < S_new && e == hipSuccess; ++sl)
+    if (origin[sl] >= 0 && (origin[sl] != sl || new_base != old_base))
+      e = hipMemcpyAsync(new_base + (size_t)sl * d->slot_stride, old_base + (size_t)origin[sl] * d->slot_stride,
+                         d->blob_bytes, hipMemcpyDeviceToDevice, s);
+  // the tables, in a new allocation when the slot count changes
+  void* mem = d->mem;
+  const CtlLayout o_old = ctl_layout(n_keys, S_old, d->max_items, d->c.trace_cap);
+  const CtlLayout o_new = ctl_layout(n_keys, S_new, d->max_items, d->c.trace_cap);
+  if (e == hipSuccess && S_new != S_old) {
+    e = hipMalloc(&mem, o_new.total);
+    if (e != hipSuccess) return dd_fail(MOE_ENOMEM, "moe_device_decoder_resize: %s", hipGetErrorString(e));
+    // counters, work lists and trace keep their contents
+    e = hipMemcpyAsync(static_cast<char*>(mem) + o_new.ctl, static_cast<char*>(d->mem) + o_old.ctl,
+                       o_old.total - o_old.ctl, hipMemcpyDeviceToDevice, s);
+  }
+  char* m = static_cast<char*>(mem);
+  if (e == hipSuccess) e = hipMemcpyAsync(m + o_new.slot_of, slot_of.data(), n_keys * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(m + o_new.slot_key, new_key.data(), (size_t)S_new * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(m + o_new.stamp, new_stamp.data(), (size_t)S_new * 8, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // host vectors are read by the copies
+  if (e != hipSuccess) {
+    if (mem != d->mem) (void)hipFree(mem);
+    return dd_fail(MOE_EHIP, "moe_device_decoder_resize: %s", hipGetErrorString(e));
+  }
+  if (mem != d->mem) {
+    (void)hipFree(d->mem);
+    d->mem = mem;
+  }
+  point_into(d->c, m, o_new, S_new, d->c.trace_cap);
+  d->S = S_new;
+  d->slot_base = new_base;
   return MOE_OK;
 }
 

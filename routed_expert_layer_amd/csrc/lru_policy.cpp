@@ -1,5 +1,7 @@
 #include "lru_policy.hpp"
 
+#include <algorithm>
+
 namespace moe {
 
 SharedLru::SharedLru(int n_keys, int S)
@@ -75,6 +77,67 @@ bool SharedLru::invalidate(int key) {
   slot_key_[s] = -1;
   free_.insert(s);
   return true;
+}
+
+void plan_resize(const std::vector<int32_t>& slot_key, const std::vector<uint64_t>& recency, int S_new,
+                 std::vector<int32_t>& new_key, std::vector<int32_t>& origin, std::vector<Move>& moves,
+                 std::vector<int32_t>& evicted) {
+  const int S_old = (int)slot_key.size();
+  std::vector<int> occ;
+  for (int s = 0; s < S_old; ++s)
+    if (slot_key[s] >= 0) occ.push_back(s);
+  std::sort(occ.begin(), occ.end(), [&](int a, int b) { return recency[a] > recency[b]; });
+  std::vector<char> keep(S_old, 0);
+  for (size_t i = 0; i < occ.size(); ++i) {
+    if ((int)i < S_new) keep[occ[i]] = 1;
+    else evicted.push_back(slot_key[occ[i]]);
+  }
+  new_key.assign(S_new, -1);
+  origin.assign(S_new, -1);
+  for (int s = 0; s < S_old && s < S_new; ++s)
+    if (keep[s]) {
+      new_key[s] = slot_key[s];
+      origin[s] = s;
+    }
+  int next_free = 0;
+  for (int s = S_new; s < S_old; ++s) {
+    if (!keep[s]) continue;
+    while (new_key[next_free] >= 0) ++next_free;  // a kept entry above S_new implies a free slot below
+    new_key[next_free] = slot_key[s];
+    origin[next_free] = s;
+    moves.push_back(Move{slot_key[s], s, next_free});
+  }
+}
+
+void SharedLru::resize(int S_new, std::vector<Move>& moves) {
+  // recency rank of every occupied slot, from the list (least recent first)
+  std::vector<uint64_t> rank(S_, 0);
+  std::vector<int> order;  // occupied slots, least recent first
+  uint64_t r = 1;
+  for (int s = lru_; s >= 0; s = next_[s]) {
+    rank[s] = r++;
+    order.push_back(s);
+  }
+  std::vector<int32_t> new_key, origin, evicted;
+  plan_resize(slot_key_, rank, S_new, new_key, origin, moves, evicted);
+  for (int32_t k : evicted) key_slot_[k] = -1;
+  std::vector<int> new_of(S_, -1);  // old slot -> new slot of kept entries
+  for (int s = 0; s < S_new; ++s) {
+    if (origin[s] >= 0) {
+      new_of[origin[s]] = s;
+      key_slot_[new_key[s]] = s;
+    }
+  }
+  S_ = S_new;
+  slot_key_ = new_key;
+  prev_.assign(S_new, -1);
+  next_.assign(S_new, -1);
+  lru_ = mru_ = -1;
+  for (int s : order)
+    if (new_of[s] >= 0) push_mru(new_of[s]);
+  free_.clear();
+  for (int s = 0; s < S_new; ++s)
+    if (slot_key_[s] < 0) free_.insert(s);
 }
 
 }  // namespace moe

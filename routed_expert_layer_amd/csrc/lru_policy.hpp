@@ -20,6 +20,21 @@ struct Access {
   int32_t key, hit, slot, victim, wave;
 };
 
+struct Move {
+  int32_t key, from, to;
+};
+
+// Resize of a slot table at a safe point (page "FreeToken-benchmark", section
+// "Elastic Cache"): the min(S_new, resident) most recent entries are kept
+// (recency[s]: larger = more recent, for occupied slots); a kept entry below
+// S_new stays in its slot, the kept entries at or above S_new move, in
+// ascending old slot, to the lowest free slots below S_new. Outputs:
+// new_key[S_new] (-1 free), origin[S_new] (old slot of each new slot's entry,
+// -1 if free), the moves, and the keys evicted.
+void plan_resize(const std::vector<int32_t>& slot_key, const std::vector<uint64_t>& recency, int S_new,
+                 std::vector<int32_t>& new_key, std::vector<int32_t>& origin, std::vector<Move>& moves,
+                 std::vector<int32_t>& evicted);
+
 class SharedLru {
  public:
   SharedLru(int n_keys, int S);
@@ -31,6 +46,8 @@ class SharedLru {
   bool splits() const { return rate_cpu_ > 0; }
   int slot_of(int key) const { return key_slot_[key]; }
   bool invalidate(int key);  // returns false if the key is not resident
+  // Resize to S_new slots (plan_resize); recency order kept. Appends the moves.
+  void resize(int S_new, std::vector<Move>& moves);
   int capacity() const { return S_; }
   int64_t hits() const { return hits_; }
   int64_t misses() const { return misses_; }

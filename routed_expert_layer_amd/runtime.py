@@ -170,6 +170,33 @@ class DecodeLayer:
         """Misses executed on the CPU so far."""
         return L.moe_decoder_cpu_runs(self.dec) if self.dec is not None else 0
 
+    def resize(self, n_slots, stream=None):
+        """Change the cache to n_slots slots between layer-steps (the most recently used entries stay); a larger
+        cache gets a new slot buffer, into which the kept blobs are copied on the stream."""
+        s = stream or torch.cuda.current_stream()
+        new = None
+        if n_slots > self.S:
+            new = torch.empty(n_slots * self.store.stride, dtype=torch.uint8, device=self.slots.device)
+        if self.dec is not None:
+            L.moe_decoder_resize(self.dec, n_slots, new, s)
+        else:
+            old = self.slots
+            moves = L.moe_cache_resize(self.cache, n_slots)
+            st = self.store.stride
+            with torch.cuda.stream(s):
+                dst = old if new is None else new
+                if new is not None:
+                    for key in range(self.store.L * self.E):
+                        sl = L.moe_cache_slot_of(self.cache, key)
+                        if sl >= 0 and not any(m[0] == key for m in moves):
+                            dst[sl * st:(sl + 1) * st].copy_(old[sl * st:(sl + 1) * st])
+                for key, a, b in moves:
+                    dst[b * st:(b + 1) * st].copy_(old[a * st:(a + 1) * st])
+        if new is not None:
+            self.keep_old = self.slots  # read by copies on the stream
+            self.slots = new
+        self.S = n_slots
+
     def set_split(self, rate_gpu, rate_cpu):
         """Divide misses between GPU fills and CPU execution in the ratio of the rates (e.g. MB/s of pinned
         fills and of the host expert kernel, see measure_rates); rate_cpu = 0 fills every miss."""
@@ -271,6 +298,18 @@ class DeviceDecodeLayer:
         self.dec = L.MoeDeviceDecoder(store.L, self.E, n_slots, T, self.H, self.I, k,
                                       L.MOE_DT_BF16 if act == "bf16" else L.MOE_DT_F32, store.wfmt,
                                       store.layer_ptrs, store.stride, self.slots, store.stride, bufs, trace_capacity)
+
+    def resize(self, n_slots, stream=None):
+        """Change the cache to n_slots slots at a safe point (waits for the stream); a larger cache gets a new
+        slot buffer. Graphs captured earlier must be captured again."""
+        s = stream or torch.cuda.current_stream()
+        new = None
+        if n_slots > self.S:
+            new = torch.empty(n_slots * self.store.stride, dtype=torch.uint8, device=self.slots.device)
+        L.moe_device_decoder_resize(self.dec, n_slots, new, s)
+        if new is not None:
+            self.slots = new  # the copies have finished: the call waits for them
+        self.S = n_slots
 
     def step(self, layer, x, Wr, bias, stream=None, out=None):
         """Enqueue one layer-step; returns the output tensor (valid once the stream reaches it)."""

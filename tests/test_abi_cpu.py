@@ -142,3 +142,35 @@ def test_argument_validation_without_gpu(L):
     assert st.value == L.MOE_EINVAL
     assert lib.moe_decoder_step(None, 0, 0, None, 1, None, None, None, 0, None, None) == L.MOE_EINVAL
     assert lib.moe_decoder_profile(None, 8) == L.MOE_EINVAL
+
+
+@pytest.mark.parametrize("S,sizes,E,Lyr,max_active", [
+    (16, [5, 12, 1, 16], 32, 2, 5), (8, [8, 3, 20], 16, 1, 3), (64, [10, 64], 256, 1, 6), (4, [2, 9], 12, 3, 2)])
+def test_cache_resize_matches_oracle(L, S, sizes, E, Lyr, max_active):
+    """Resizes between layer-steps: moves, capacity and every later access equal the oracle's."""
+    r = np.random.default_rng(S * 7 + E)
+    cache = L.MoeCache(Lyr, E, S)
+    sim = oracle.SharedLRU(S)
+    zipf = 1.0 / np.arange(1, E + 1) ** 1.1
+    step = 0
+    for S_new in [None] + sizes:
+        if S_new is not None:
+            moves = L.moe_cache_resize(cache, S_new)
+            ref = sim.resize(S_new)
+            assert moves.tolist() == [list(m) for m in ref]
+            assert L.moe_cache_capacity(cache) == S_new
+            for key in range(Lyr * E):
+                assert L.moe_cache_slot_of(cache, key) == sim.key_slot.get(key, -1)
+        for _ in range(15):
+            for layer in range(Lyr):
+                n = int(r.integers(1, max_active + 1))
+                ex = np.sort(r.choice(E, size=n, replace=False, p=zipf / zipf.sum())).astype(np.int32)
+                L.cache_resolve(cache, step, layer, ex)
+                sim.resolve(step, layer, E, ex)
+            step += 1
+    tr = L.moe_cache_trace(cache)
+    ref = np.array([[q.step, q.layer, q.key, q.hit, q.slot, q.victim, q.wave] for q in sim.trace])
+    assert np.array_equal(tr, ref)
+    with pytest.raises(L.MoEError) as ei:
+        L.moe_cache_resize(cache, 0)
+    assert ei.value.code == L.MOE_ECAPACITY

@@ -51,7 +51,7 @@ def device_trace(dl, L, cap):
     return t
 
 
-def run_device(cfg, steps, out_check, check_all=False, trace_cap=1 << 16):
+def run_device(cfg, steps, out_check, check_all=False, trace_cap=1 << 16, resizes=None):
     """Eager device-controlled steps over all layers; routing, trace and outputs against the oracle."""
     from routed_expert_layer_amd.runtime import DeviceDecodeLayer
     print(f"device decode {cfg.name}: L={cfg.L} T={cfg.T} steps={steps} S={cfg.S} {cfg.wfmt}", flush=True)
@@ -62,6 +62,9 @@ def run_device(cfg, steps, out_check, check_all=False, trace_cap=1 << 16):
         sim = oracle.SharedLRU(cfg.S)
         experts64 = {}
         for step in range(steps):
+            if resizes and step in resizes:
+                dl.resize(resizes[step])
+                sim.resize(resizes[step])
             for layer in range(cfg.L):
                 b = gen.router_bias(cfg, layer, step, dev)
                 x = gen.tokens(cfg, step, layer, dev)
@@ -94,6 +97,12 @@ def run_device(cfg, steps, out_check, check_all=False, trace_cap=1 << 16):
 def test_device_small_bf16_all_outputs(S):
     ref = run_device(small_bf16(S), 40, set(), check_all=True)
     assert (ref[:, 5] >= 0).any(), "the small config should evict"
+
+
+def test_device_resize_all_outputs():
+    """Shrink to the smallest allowed size (k*T), then grow into a new buffer, between steps."""
+    ref = run_device(small_bf16(10), 36, set(), check_all=True, resizes={12: 6, 24: 14})
+    assert (ref[:, 5] >= 0).any()
 
 
 def test_device_small_int4_all_outputs():

@@ -69,7 +69,8 @@ def make_store(cfg):
     return store
 
 
-def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, split=None, cpu_check=(0, ())):
+def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, split=None, cpu_check=(0, ()),
+               resizes=None):
     """Drive DecodeLayer over `steps` x all layers; check routing, trace, and sampled outputs.
 
     native=True runs each layer-step through the library's decode driver
@@ -91,6 +92,9 @@ def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, spli
         cpu_left, cpu_layers = cpu_check
         experts64 = {}
         for step in range(steps):
+            if resizes and step in resizes:
+                dl.resize(resizes[step])
+                sim.resize(resizes[step])
             for layer in range(cfg.L):
                 b = gen.router_bias(cfg, layer, step, dev)
                 x = gen.tokens(cfg, step, layer, dev)
@@ -157,6 +161,15 @@ def test_decode_int4_cut():
 def test_decode_mxfp4_cut():
     cfg = CONFIGS["decode_mxfp4_t8_l8"]
     run_decode(cfg, 48, {(0, 0), (5, 3), (47, 7)})
+
+
+@pytest.mark.parametrize("native", [True, False], ids=["driver", "python"])
+def test_resize_small_all_outputs(native):
+    """The cache shrinks (entries above the new size move), then grows into a new buffer; every output and
+    the whole trace against the oracle."""
+    cfg = dataclasses.replace(CONFIGS["decode_bf16_h4096_e256"], name="resize_small", L=3, T=3, H=256, I=128, E=16,
+                              k=2, zipf_s=1.2, epoch=8, S=10)
+    run_decode(cfg, 36, set(), check_all_outputs=True, native=native, resizes={12: 4, 24: 14})
 
 
 @pytest.mark.timeout(600)
