@@ -259,24 +259,30 @@ def bench_decode(args, torch, L, gen, cfg):
 def bench_prefill(args, torch, L, gen, cfg, reps=5):
     from routed_expert_layer_amd.runtime import PrefillLayer
     dev = "cuda"
-    blob = L.moe_expert_bytes(L.MOE_W_BF16, cfg.H, cfg.I)
+    wf = L.MOE_W_MXFP4 if cfg.wfmt == "mxfp4" else L.MOE_W_BF16
+    blob = L.moe_expert_bytes(wf, cfg.H, cfg.I)
     stride = (blob + 4095) // 4096 * 4096
     buf = torch.empty(cfg.E * stride, dtype=torch.uint8, device=dev)
     for e in range(cfg.E):
-        W1, W3, W2 = gen.expert_weights(cfg, 0, e, dev)
-        L.moe_pack_expert(L.MOE_W_BF16, cfg.H, cfg.I, W1, W3, W2, None, None, None, buf[e * stride:])
-    pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, stride, dev)
+        if wf == L.MOE_W_MXFP4:
+            w = gen.expert_mxfp4(cfg, 0, e, dev)
+            L.moe_pack_expert(wf, cfg.H, cfg.I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"], w["s2"],
+                              buf[e * stride:])
+        else:
+            W1, W3, W2 = gen.expert_weights(cfg, 0, e, dev)
+            L.moe_pack_expert(wf, cfg.H, cfg.I, W1, W3, W2, None, None, None, buf[e * stride:])
+    pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, stride, dev, wfmt=wf)
     Wr = gen.router_weight(cfg, 0, dev)
     b = gen.router_bias(cfg, 0, 0, dev)
     x = gen.tokens(cfg, 0, 0, dev)
     for _ in range(2):
-        pl.forward(x, Wr, b, buf)
+        pl.forward(x, Wr, b, buf, wfmt=wf)
     timer = EventTimer(torch, reps)
     timer.enabled = True
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(reps):
-        pl.forward(x, Wr, b, buf, timer=timer)
+        pl.forward(x, Wr, b, buf, wfmt=wf, timer=timer)
     torch.cuda.synchronize()
     layer_ms = (time.perf_counter() - t0) * 1e3 / reps
     flops, ms, n = timer.result()
@@ -510,6 +516,7 @@ def main():
     out["decode"] = rnd(res["decode"])
     if not args.no_prefill:
         out["prefill"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_bf16_t4096_e256"]))
+        out["prefill_mxfp4"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_mxfp4_t4096_e256"]))
         out["prefill_double_buffered"] = rnd(bench_prefill_pipeline(args, torch, L, gen,
                                                                     CONFIGS["prefill_db_bf16_t16384_l8"]))
     if not args.no_extra:

@@ -259,8 +259,9 @@ int cache_fill_async(moe_cache_t* cache, const moe_miss_t* misses, int n,
  *          must not overlap in rows; rows >= 0
  * slot_base device base of the expert blobs; slot_stride bytes between slots
  * wfmt     MOE_W_F32 (x fp32), MOE_W_BF16, MOE_W_INT4 or MOE_W_MXFP4 (x bf16);
- *          the tiled GEMM (MOE_FFN_PREFILL) takes bf16 weights only, AUTO
- *          runs the matrix-vector kernels for the other formats
+ *          the tiled GEMM (MOE_FFN_PREFILL) takes bf16 weights (H % 128,
+ *          I % 64 == 0) and MXFP4 weights (H % 256 == 0); AUTO runs the
+ *          matrix-vector kernels for the other formats
  * y_perm   device out fp32 [rows_total, H] (only listed rows are written)
  * workspace device scratch, >= moe_ffn_workspace_size(rows_total, H, I, wfmt)
  *          bytes, where rows_total bounds every row index used

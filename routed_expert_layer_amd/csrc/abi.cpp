@@ -348,18 +348,35 @@ int moe_ffn(const void* x, int dtype, const int32_t* perm_src, const moe_work_t*
   if (ws_bytes < moe_ffn_workspace_size(rows_total, H, I, wfmt))
     return fail(MOE_EINVAL, "moe_ffn: workspace too small for %d rows", rows_total);
   bool prefill = false;
+  const bool gemm_ok = wfmt == MOE_W_MXFP4 ? moe::prefill_mxfp4_supported(H, I) : moe::prefill_supported(wfmt, H, I);
   if (mode == MOE_FFN_PREFILL) {
-    if (!moe::prefill_supported(wfmt, H, I))
-      return fail(MOE_EINVAL, "moe_ffn: prefill GEMM needs bf16 weights, H %% 128 == 0 and I %% 64 == 0");
+    if (!gemm_ok)
+      return fail(MOE_EINVAL,
+                  "moe_ffn: prefill GEMM needs bf16 weights with H %% 128 == 0 and I %% 64 == 0, or MXFP4 weights "
+                  "with H %% 256 == 0");
     prefill = true;
   } else if (mode == MOE_FFN_AUTO) {
-    prefill = max_rows > 32 && moe::prefill_supported(wfmt, H, I);
+    prefill = max_rows > 32 && gemm_ok;
   }
   char* ws = static_cast<char*>(workspace);
   void* hbuf = ws;
   void* xg = ws + moe::align_up((size_t)(rows_total + 16) * I * (wfmt == MOE_W_F32 ? 4 : 2), 256);
   void* tables = static_cast<char*>(xg) + (wfmt == MOE_W_INT4 ? moe::align_up((size_t)rows_total * H * 2, 256) : 0);
   hipStream_t s = as_stream(stream);
+  if (prefill && wfmt == MOE_W_MXFP4) {
+    std::vector<int4> items;
+    items.reserve(n_work);
+    for (int i = 0; i < n_work; ++i)
+      if (work[i].rows > 0) items.push_back(make_int4(work[i].slot, work[i].row_begin, work[i].rows, work[i].expert));
+    for (size_t base = 0; base < items.size(); base += moe::kTableItems) {
+      const int n = (int)std::min(items.size() - base, (size_t)moe::kTableItems);
+      hipError_t e = moe::launch_ffn_prefill_mxfp4(x, perm_src, items.data() + base, n,
+                                                   static_cast<const char*>(slot_base), slot_stride, H, I, hbuf,
+                                                   y_perm, tables, s);
+      if (e != hipSuccess) return hip_fail(e, "moe_ffn launch");
+    }
+    return MOE_OK;
+  }
   if (prefill && moe::gemm2_supported(2 * I, H) && moe::gemm2_supported(H, I)) {
     // large-tile GEMM: the whole work list per launch, from a device table
     std::vector<int4> items;

@@ -225,6 +225,167 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same grouped GEMM with MXFP4 weights (FP4 codes, one E8M0 scale per 32
+// of K; the MOE_W_MXFP4 blob layout): 256 weight rows x 128 tokens per block
+// and 128 K per stage (one 1 KiB code block per 16-row tile). Per stage each
+// of the eight waves loads two code blocks, its two tiles' 64-byte scale
+// blocks (eight lanes) and one 16-token fragment for each of the four 32-K
+// sub-blocks, all straight into LDS (49 KiB per stage, three stages). Waves
+// turn the codes of their four weight tiles into bf16 with the block scale
+// folded in (exact) per 32-K sub-block and run 4 x 4 bf16 matrix-core
+// products on them; the weight bytes crossing HBM and LDS are a quarter of
+// the bf16 kernel's.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4_t mx_a_operand(uint32_t codes, uint32_t scale_byte) {
+  const float sc = __uint_as_float((scale_byte & 0xFFu) << 23);
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+  return r;
+}
+
+template <int PHASE>
+__global__ __launch_bounds__(512, 1) void gemm_mxfp4(const uint16_t* __restrict__ bsrc,
+                                                      const int32_t* __restrict__ perm_src,
+                                                      const GemmTable* __restrict__ tab,
+                                                      const char* __restrict__ slot_base, size_t slot_stride,
+                                                      size_t code_off, size_t scale_off, int N, int K, int I,
+                                                      int H, uint16_t* __restrict__ hout, float* __restrict__ yout) {
+  constexpr int BN_T = 16, BM_T = 8, NS = 3, WN = 4, WM = 4, WAVES_N = 4, KSUB = 4;
+  constexpr int CODE = BN_T * 1024, SCL = BN_T * 64, TOK = BM_T * KSUB * 1024;
+  constexpr int STAGE = CODE + SCL + TOK;
+  constexpr int FPW = 7;  // per wave per stage: 2 code blocks, 1 scale load, 4 token fragments
+  __shared__ __attribute__((aligned(1024))) char lds[NS][STAGE];
+
+  const GemmTable& wa = *tab;
+  const int NTB = N / (16 * BN_T);
+  const int sidx = (int)((blockIdx.x >> 8) * 8 + (blockIdx.x & 7));
+  const int w = (int)((blockIdx.x >> 3) & 31);
+  if (sidx >= wa.total_tiles) return;
+  int lo = 0, hi = wa.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (wa.tile_prefix[mid] <= sidx) lo = mid; else hi = mid - 1;
+  }
+  const int4 it = wa.item[lo];
+  const int GM = it.w & 0xFF, GN = it.w >> 8;
+  if (w >= GM * GN) return;
+  const int ls = sidx - wa.tile_prefix[lo];
+  const int ngroups = NTB / GN;
+  const int mt = (ls / ngroups) * GM + w / GN;
+  const int nt = (ls % ngroups) * GN + (w % GN);
+  if (mt * 16 * BM_T >= it.z) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wn = wave % WAVES_N, wm = wave / WAVES_N;
+  const int KG = K / 128;  // stages
+  const int KC = K / 32;
+  const int ldb = (PHASE == 2) ? I : H;
+  const char* blob = slot_base + (size_t)it.x * slot_stride;
+
+  // load offsets at stage 0 and their step per stage
+  uint32_t off[FPW], kstep[FPW];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {  // code blocks of weight tiles wave + 8q
+    off[q] = (uint32_t)((((size_t)nt * BN_T + wave + 8 * q) * KG) * 1024 + lane * 16);
+    kstep[q] = 1024;
+  }
+  // scale blocks of the same two tiles: lanes 0..3 tile `wave`, lanes 4..7 tile wave + 8
+  off[2] = (uint32_t)((((size_t)nt * BN_T + wave + 8 * (lane >> 2 & 1)) * KG) * 64 + (lane & 3) * 16);
+  kstep[2] = 64;
+  {
+    int mloc = mt * (16 * BM_T) + wave * 16 + (lane & 15);
+    if (mloc >= it.z) mloc = it.z - 1;
+    const uint32_t row = PHASE == 1 ? (uint32_t)perm_src[it.y + mloc] : (uint32_t)(it.y + mloc);
+#pragma unroll
+    for (int j = 0; j < KSUB; ++j) {  // token fragment (sub-block j, token tile `wave`)
+      if constexpr (PHASE == 2) {
+        off[3 + j] = (row >> 4) * (uint32_t)KC * 1024u + (uint32_t)j * 1024u + ((row & 15) + 16 * (lane >> 4)) * 16;
+        kstep[3 + j] = 4096;
+      } else {
+        off[3 + j] = (row * (uint32_t)ldb + (uint32_t)j * 32 + (lane >> 4) * 8) * 2;
+        kstep[3 + j] = 256;
+      }
+    }
+  }
+  auto issue = [&](int kt) {
+    char* base = lds[kt % NS];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      buffer_load_lds16(blob + code_off, off[q] + (uint32_t)kt * kstep[q], base + (wave + 8 * q) * 1024);
+    if (lane < 8) buffer_load_lds16(blob + scale_off, off[2] + (uint32_t)kt * kstep[2], base + CODE + wave * 128);
+#pragma unroll
+    for (int j = 0; j < KSUB; ++j)
+      buffer_load_lds16(bsrc, off[3 + j] + (uint32_t)kt * kstep[3 + j], base + CODE + SCL + (j * BM_T + wave) * 1024);
+  };
+
+  f32x4_t acc[WN][WM];
+#pragma unroll
+  for (int i = 0; i < WN; ++i)
+#pragma unroll
+    for (int j = 0; j < WM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = 0; s0 < NS - 1 && s0 < KG; ++s0) issue(s0);
+  for (int kt = 0; kt < KG; ++kt) {
+    if (kt + NS - 2 < KG) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 2)));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + NS - 1 < KG) issue(kt + NS - 1);
+    const char* b = lds[kt % NS];
+    u32x4_t codes[WN];
+    uint32_t scl[WN];
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const int ta = wn * WN + i;  // weight tile of this wave
+      codes[i] = *reinterpret_cast<const u32x4_t*>(b + ta * 1024 + lane * 16);
+      scl[i] = *reinterpret_cast<const uint32_t*>(b + CODE + (ta & 7) * 128 + (ta >> 3) * 64 + (lane & 15) * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < KSUB; ++j) {
+      u32x4_t bf[WM];
+#pragma unroll
+      for (int jj = 0; jj < WM; ++jj)
+        bf[jj] = *reinterpret_cast<const u32x4_t*>(b + CODE + SCL + (j * BM_T + wm * WM + jj) * 1024 + lane * 16);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < WN; ++i) {
+        const u32x4_t a = mx_a_operand(codes[i][j], scl[i] >> (8 * j));
+#pragma unroll
+        for (int jj = 0; jj < WM; ++jj) acc[i][jj] = mfma_bf16(a, bf[jj], acc[i][jj]);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < WM; ++j) {
+    const int mloc = mt * (16 * BM_T) + (wm * WM + j) * 16 + (lane & 15);
+    if (mloc >= it.z) continue;
+    const size_t row = (size_t)(it.y + mloc);
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      const int ntile = nt * BN_T + wn * WN + i;
+      const f32x4_t sv = acc[i][j];
+      if constexpr (PHASE == 1) {
+        const int i0 = 8 * ntile + 2 * (lane >> 4);
+        const uint32_t packed =
+            (uint32_t)f32_to_bf16(silu(sv[0]) * sv[1]) | ((uint32_t)f32_to_bf16(silu(sv[2]) * sv[3]) << 16);
+        const size_t o = ((row >> 4) * (size_t)(I / 32) + (i0 >> 5)) * 512 + ((row & 15) + 16 * ((i0 & 31) >> 3)) * 8 +
+                         (i0 & 7);
+        *reinterpret_cast<uint32_t*>(hout + o) = packed;
+      } else {
+        *reinterpret_cast<f32x4_t*>(yout + row * H + 16 * ntile + 4 * (lane >> 4)) = sv;
+      }
+    }
+  }
+}
+
 // Per expert, a super-tile is GM token tiles x GN weight tiles (GM*GN <= 32
 // block slots): GM = the smallest power of two covering its token tiles, at
 // most 8; GN = the largest power of two dividing the weight tiles that fits
@@ -337,6 +498,37 @@ hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const int
     hipLaunchKernelGGL((gemm2_bf16<2, 8, const GemmTable*>), dim3(supertile_blocks(tot[1][1])), dim3(512), 0, s, hb,
                        perm_src, (const GemmTable*)tab[1][1], slot_base, slot_stride, L.p2, H, I, H, I, hb, y,
                        nullptr);
+  return hipGetLastError();
+}
+
+bool prefill_mxfp4_supported(int H, int I) { return H % 256 == 0 && I % 128 == 0; }
+
+// Both projections of every listed expert with MXFP4 weights: 128-token
+// tiles, one launch per projection, the work list in a device table.
+hipError_t launch_ffn_prefill_mxfp4(const void* x, const int32_t* perm_src, const int4* items, int n,
+                                    const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
+                                    void* tables, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n > kTableItems || !prefill_mxfp4_supported(H, I)) return hipErrorInvalidValue;
+  const BlobLayout L = blob_layout(3, H, I);
+  int tot[2] = {0, 0};
+  GemmTable* tab[2];
+  for (int ph = 0; ph < 2; ++ph) {
+    tab[ph] = reinterpret_cast<GemmTable*>(static_cast<char*>(tables) + ph * kTableBytes);
+    std::vector<int4> it(items, items + n);
+    std::vector<int> pre(n + 1);
+    tot[ph] = plan_supertiles(it.data(), n, pre.data(), ph == 0 ? 2 * I : H, 128);
+    hipError_t e = upload_table(it.data(), pre.data(), n, tot[ph], tab[ph], s);
+    if (e != hipSuccess) return e;
+  }
+  uint16_t* hb = static_cast<uint16_t*>(hbuf);
+  if (tot[0] > 0)
+    hipLaunchKernelGGL(gemm_mxfp4<1>, dim3(supertile_blocks(tot[0])), dim3(512), 0, s,
+                       static_cast<const uint16_t*>(x), perm_src, (const GemmTable*)tab[0], slot_base, slot_stride,
+                       L.p1, L.p1s, 2 * I, H, I, H, hb, y);
+  if (tot[1] > 0)
+    hipLaunchKernelGGL(gemm_mxfp4<2>, dim3(supertile_blocks(tot[1])), dim3(512), 0, s, hb, perm_src,
+                       (const GemmTable*)tab[1], slot_base, slot_stride, L.p2, L.p2s, H, I, I, H, hb, y);
   return hipGetLastError();
 }
 

@@ -140,6 +140,11 @@ bool gemm2_supported(int N, int K);
 hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const int4* items, int n,
                                const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
                                void* tables, hipStream_t s);
+// The same with MXFP4 weights (128-token tiles; two GemmTables at `tables`).
+bool prefill_mxfp4_supported(int H, int I);
+hipError_t launch_ffn_prefill_mxfp4(const void* x, const int32_t* perm_src, const int4* items, int n,
+                                    const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
+                                    void* tables, hipStream_t s);
 int router_gemm2_splits(int T, int H, int E);
 hipError_t launch_router_gemm2(const void* x, const void* wrt, int T, int H, int E, float* partial, int nsplit,
                                hipStream_t s);

@@ -349,13 +349,13 @@ class DeviceDecodeLayer:
 class PrefillLayer:
     """Prefill path over a layer whose experts are all resident (blob of expert e at base + e*stride)."""
 
-    def __init__(self, H, I, E, k, T, stride, device="cuda", keep_logits=False, mode=L.MOE_FFN_AUTO):
+    def __init__(self, H, I, E, k, T, stride, device="cuda", keep_logits=False, mode=L.MOE_FFN_AUTO,
+                 wfmt=L.MOE_W_BF16):
         self.H, self.I, self.E, self.k, self.stride, self.mode = H, I, E, k, stride, mode
         self.rb = RouteBuffers(T, H, E, k, device, keep_logits)
         rows = T * k
         self.y_perm = torch.empty((max(rows, 1), H), dtype=torch.float32, device=device)
-        self.ffn_ws = torch.empty(L.moe_ffn_workspace_size(rows, H, I, L.MOE_W_BF16), dtype=torch.uint8,
-                                  device=device)
+        self.ffn_ws = torch.empty(L.moe_ffn_workspace_size(rows, H, I, wfmt), dtype=torch.uint8, device=device)
         self.out = torch.empty((T, H), dtype=torch.float32, device=device)
         self.last_counts = None
 

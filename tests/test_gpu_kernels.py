@@ -128,7 +128,10 @@ FFN_CASES = [
     ("int4_decode", "int4", 512, 256, [1, 8, 0, 3, 20], "decode"),
     ("int4_decode_wide", "int4", 1024, 384, [2, 16, 5], "decode"),
     ("mxfp4_decode", "mxfp4", 512, 256, [1, 8, 0, 3, 20], "decode"),
-    ("mxfp4_decode_wide", "mxfp4", 1024, 384, [2, 16, 5, 33], "auto"),
+    ("mxfp4_decode_wide", "mxfp4", 1024, 384, [2, 16, 5, 33], "decode"),
+    ("mxfp4_prefill", "mxfp4", 512, 256, [130, 0, 1, 127, 128, 300, 17, 777], "prefill"),
+    ("mxfp4_prefill_c3shape", "mxfp4", 2048, 768, [70, 3, 129], "prefill"),
+    ("mxfp4_auto_mixed", "mxfp4", 512, 384, [40, 2, 250], "auto"),
 ]
 
 

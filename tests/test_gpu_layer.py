@@ -228,6 +228,28 @@ def test_prefill_4096_resident():
     print(f"  tokens per expert: min {counts.min()} max {counts.max()} mean {counts.mean():.1f}", flush=True)
 
 
+@pytest.mark.timeout(600)
+def test_prefill_4096_mxfp4_resident():
+    from routed_expert_layer_amd import _lib as L
+    from routed_expert_layer_amd.runtime import PrefillLayer
+    cfg = CONFIGS["prefill_mxfp4_t4096_e256"]
+    blob = L.moe_expert_bytes(L.MOE_W_MXFP4, cfg.H, cfg.I)
+    stride = (blob + 4095) // 4096 * 4096
+    buf = torch.empty(cfg.E * stride, dtype=torch.uint8, device=dev)
+    for e in range(cfg.E):
+        w = gen.expert_mxfp4(cfg, 0, e, dev)
+        L.moe_pack_expert(L.MOE_W_MXFP4, cfg.H, cfg.I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"], w["s2"],
+                          buf[e * stride:])
+    pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, stride, dev, keep_logits=True, wfmt=L.MOE_W_MXFP4)
+    Wr = gen.router_weight(cfg, 0, dev)
+    b = gen.router_bias(cfg, 0, 0, dev)
+    x = gen.tokens(cfg, 0, 0, dev)
+    pl.forward(x, Wr, b, buf, wfmt=L.MOE_W_MXFP4)
+    torch.cuda.synchronize()
+    counts = _prefill_check(cfg, 0, pl, x, Wr, b)
+    print(f"  tokens per expert: min {counts.min()} max {counts.max()} mean {counts.mean():.1f}", flush=True)
+
+
 @pytest.mark.timeout(900)
 def test_prefill_16384_double_buffered():
     from routed_expert_layer_amd import _lib as L

@@ -59,6 +59,10 @@ CONFIGS = {
     # 4096-token prefill chunk, all experts resident, unbiased router
     "prefill_bf16_t4096_e256": Config("prefill_bf16_t4096_e256", L=1, T=4096, steps=1, H=4096, E=256, I=2048,
                                       k=6, act="bf16", wfmt="bf16", zipf_s=0.0, phase="prefill"),
+    # the same 4096-token chunk with the same experts in MXFP4
+    "prefill_mxfp4_t4096_e256": Config("prefill_mxfp4_t4096_e256", L=1, T=4096, steps=1, H=4096, E=256, I=2048,
+                                       k=6, act="bf16", wfmt="mxfp4", zipf_s=0.0, phase="prefill",
+                                       weights_of="prefill_bf16_t4096_e256"),
     # 8-layer prefill, 16384 tokens per layer, Zipf(1.5) routing, double-buffered layer copies
     "prefill_db_bf16_t16384_l8": Config("prefill_db_bf16_t16384_l8", L=8, T=16384, steps=1, H=4096, E=256,
                                         I=2048, k=6, act="bf16", wfmt="bf16", zipf_s=1.5, phase="prefill",
