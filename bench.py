@@ -302,12 +302,15 @@ def bench_prefill_pipeline(args, torch, L, gen, cfg):
     dev = "cuda"
     store = ExpertStore(cfg.L, cfg.E, cfg.H, cfg.I, cfg.wfmt, phys_layers=cfg.pool_layers)
     try:
+        mx = cfg.wfmt == "mxfp4"
         for layer in range(store.P):
-            store.pack_layer(layer, lambda e: gen.expert_weights(cfg, layer, e, dev))
+            store.pack_layer(layer, (lambda e: gen.expert_mxfp4(cfg, layer, e, dev)) if mx else
+                             (lambda e: gen.expert_weights(cfg, layer, e, dev)))
         xs = [gen.tokens(cfg, 0, l, dev) for l in range(cfg.L)]
         Wrs = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
         bs = [gen.router_bias(cfg, l, 0, dev) for l in range(cfg.L)]
-        pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, store.stride, dev)
+        wf = store.wfmt
+        pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, store.stride, dev, wfmt=wf)
         s = torch.cuda.current_stream()
         # warm-up pass (kernels and the copy path), then the timed pass
         for rep in range(2):
@@ -321,7 +324,7 @@ def bench_prefill_pipeline(args, torch, L, gen, cfg):
             for l in range(cfg.L):
                 base = L.moe_pipe_begin_layer(pipe, l, s)
                 ev[l][0].record(s)
-                pl.forward(xs[l], Wrs[l], bs[l], base, timer=timer)
+                pl.forward(xs[l], Wrs[l], bs[l], base, wfmt=wf, timer=timer)
                 ev[l][1].record(s)
                 L.moe_pipe_end_layer(pipe, l, s)
                 groups.append((int((pl.last_counts > 0).sum()), int(pl.last_counts.max())))
@@ -519,6 +522,8 @@ def main():
         out["prefill_mxfp4"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_mxfp4_t4096_e256"]))
         out["prefill_double_buffered"] = rnd(bench_prefill_pipeline(args, torch, L, gen,
                                                                     CONFIGS["prefill_db_bf16_t16384_l8"]))
+        out["prefill_double_buffered_mxfp4"] = rnd(bench_prefill_pipeline(args, torch, L, gen,
+                                                                          CONFIGS["prefill_db_mxfp4_t16384_l8"]))
     if not args.no_extra:
         out["decode_int4"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["decode_int4_t8_l8"], 64, 128))
         out["decode_mxfp4"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["decode_mxfp4_t8_l8"], 64, 128))

@@ -251,21 +251,22 @@ def test_prefill_4096_mxfp4_resident():
 
 
 @pytest.mark.timeout(900)
-def test_prefill_16384_double_buffered():
+@pytest.mark.parametrize("name", ["prefill_db_bf16_t16384_l8", "prefill_db_mxfp4_t16384_l8"])
+def test_prefill_16384_double_buffered(name):
     from routed_expert_layer_amd import _lib as L
     from routed_expert_layer_amd.runtime import PrefillLayer
-    cfg = CONFIGS["prefill_db_bf16_t16384_l8"]
+    cfg = CONFIGS[name]
     store = make_store(cfg)
     try:
         pipe = L.MoePipe(store.layer_ptrs, store.layer_bytes)
-        pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, store.stride, dev, keep_logits=True)
+        pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, store.stride, dev, keep_logits=True, wfmt=store.wfmt)
         s = torch.cuda.current_stream()
         for layer in range(cfg.L):
             Wr = gen.router_weight(cfg, layer, dev)
             b = gen.router_bias(cfg, layer, 0, dev)
             x = gen.tokens(cfg, 0, layer, dev)
             base = L.moe_pipe_begin_layer(pipe, layer, s)
-            pl.forward(x, Wr, b, base)
+            pl.forward(x, Wr, b, base, wfmt=store.wfmt)
             L.moe_pipe_end_layer(pipe, layer, s)
             torch.cuda.synchronize()
             counts = _prefill_check(cfg, layer, pl, x, Wr, b, n_sample=8)

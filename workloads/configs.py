@@ -67,6 +67,10 @@ CONFIGS = {
     "prefill_db_bf16_t16384_l8": Config("prefill_db_bf16_t16384_l8", L=8, T=16384, steps=1, H=4096, E=256,
                                         I=2048, k=6, act="bf16", wfmt="bf16", zipf_s=1.5, phase="prefill",
                                         pool_layers=4),
+    # the same 8-layer prefill with MXFP4 experts (eight distinct weight sets: 27.4 GB of pool)
+    "prefill_db_mxfp4_t16384_l8": Config("prefill_db_mxfp4_t16384_l8", L=8, T=16384, steps=1, H=4096, E=256,
+                                         I=2048, k=6, act="bf16", wfmt="mxfp4", zipf_s=1.5, phase="prefill",
+                                         weights_of="prefill_db_bf16_t16384_l8"),
     # MXFP4 decode on the same 8 layers (the same bf16 weights in the OCP MX FP4 format), batch 8,
     # 512-entry shared cache
     "decode_mxfp4_t8_l8": Config("decode_mxfp4_t8_l8", L=8, T=8, steps=256, H=4096, E=256, I=2048, k=6,
