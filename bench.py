@@ -72,7 +72,7 @@ def _definition(src, signature):
 
 def decode_ffn_digest(root):
     """sha256 over the source text the decode expert-FFN kernels are built from: both kernels, their
-    launcher, the device helpers and the work-list / blob-layout definitions."""
+    launchers, the work sources, the device helpers and the work-list / blob-layout definitions."""
     import hashlib
     csrc = os.path.join(root, "routed_expert_layer_amd", "csrc")
     ffn = open(os.path.join(csrc, "kernels_ffn.hip")).read()
@@ -81,6 +81,8 @@ def decode_ffn_digest(root):
              _definition(ffn, "__global__ __launch_bounds__(256) void ffn1_decode_bf16("),
              _definition(ffn, "__global__ __launch_bounds__(256) void ffn2_decode_bf16("),
              _definition(ffn, "hipError_t launch_ffn_decode("),
+             _definition(ffn, "hipError_t decode_kernels("), _definition(ffn, "struct ArgWork"),
+             _definition(ffn, "struct DevWork"),
              _definition(hdr, "struct WorkArgs"), _definition(hdr, "inline BlobLayout blob_layout(")]
     return hashlib.sha256("\n".join(parts).encode()).hexdigest()
 
@@ -160,6 +162,40 @@ def bench_device(torch, cfg, store, Wrs, warm, steps, x_of, b_of):
     return dict(eager=one(False), graph=one(True))
 
 
+def decode_variants(args, torch, cfg, store, Wr, xs, bias):
+    """The one-layer decode workload with the pages' adaptive misses (misses divided between fills and CPU
+    execution in the ratio of the measured fill and CPU rates) and with the cache control in GPU memory."""
+    from routed_expert_layer_amd.runtime import DecodeLayer
+    dev = "cuda"
+    s = torch.cuda.current_stream()
+    n_total = args.warmup + args.steps
+    dl2 = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+    rates = [int(r) for r in dl2.measure_rates()]
+    dl2.set_split(*rates)
+    for step in range(args.warmup):
+        dl2.step(step, 0, xs[step], Wr, bias(step), s)
+    torch.cuda.synchronize()
+    f2, c2 = dl2.n_fills, dl2.cpu_runs
+    lat2 = []
+    t2 = prev = time.perf_counter()
+    for step in range(args.warmup, n_total):
+        dl2.step(step, 0, xs[step], Wr, bias(step), s)
+        now = time.perf_counter()
+        lat2.append(now - prev)
+        prev = now
+    torch.cuda.synchronize()
+    el2 = time.perf_counter() - t2
+    tr2 = dl2.trace()
+    tm2 = tr2[tr2[:, 0] >= args.warmup]
+    split = dict(tokens_per_s=args.steps * cfg.T / el2, ms_per_step=el2 * 1e3 / args.steps,
+                 step_ms_p50=percentile(lat2, 50) * 1e3, hit_rate=float(tm2[:, 3].mean()) if len(tm2) else 0.0,
+                 fills_timed=dl2.n_fills - f2, cpu_runs_timed=dl2.cpu_runs - c2, split_rates_mbs=rates)
+    del dl2
+    device = bench_device(torch, cfg, store, [Wr], args.warmup, args.steps, lambda st, l: xs[st],
+                          lambda l, st: bias(st))
+    return split, device
+
+
 def bench_decode(args, torch, L, gen, cfg):
     from routed_expert_layer_amd.runtime import DecodeLayer, ExpertStore
     dev = "cuda"
@@ -204,34 +240,9 @@ def bench_decode(args, torch, L, gen, cfg):
     timed = trace[trace[:, 0] >= args.warmup]
     hit_rate = float(timed[:, 3].mean()) if len(timed) else 0.0
 
-    # the pages' adaptive misses on the same workload: misses divided between fills and CPU execution in the
-    # ratio of the measured fill and CPU rates (reported beside the all-fills run above)
-    dl2 = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
-    rates = [int(r) for r in dl2.measure_rates()]
-    dl2.set_split(*rates)
-    for step in range(args.warmup):
-        dl2.step(step, 0, xs[step], Wr, bias(step), s)
-    torch.cuda.synchronize()
-    f2, c2 = dl2.n_fills, dl2.cpu_runs
-    lat2 = []
-    t2 = prev = time.perf_counter()
-    for step in range(args.warmup, n_total):
-        dl2.step(step, 0, xs[step], Wr, bias(step), s)
-        now = time.perf_counter()
-        lat2.append(now - prev)
-        prev = now
-    torch.cuda.synchronize()
-    el2 = time.perf_counter() - t2
-    tr2 = dl2.trace()
-    tm2 = tr2[tr2[:, 0] >= args.warmup]
-    split = dict(tokens_per_s=args.steps * cfg.T / el2, ms_per_step=el2 * 1e3 / args.steps,
-                 step_ms_p50=percentile(lat2, 50) * 1e3, hit_rate=float(tm2[:, 3].mean()) if len(tm2) else 0.0,
-                 fills_timed=dl2.n_fills - f2, cpu_runs_timed=dl2.cpu_runs - c2, split_rates_mbs=rates)
-    del dl2
-
-    # the same workload with the cache control in GPU memory (no host round trip per step)
-    device = bench_device(torch, cfg, store, [Wr], args.warmup, args.steps, lambda st, l: xs[st],
-                          lambda l, st: bias(st))
+    split = device = None
+    if not args.no_variants:
+        split, device = decode_variants(args, torch, cfg, store, Wr, xs, bias)
 
     # pinned host -> HBM fill bandwidth: blobs copied on the fill stream
     fs = dl.fill_stream
@@ -460,6 +471,8 @@ def main():
     ap.add_argument("--workload", default="decode_bf16_h4096_e256")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the int4 8-layer and 48-layer decode sections")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="one-layer decode without its CPU-split and device-controlled variants (counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -504,7 +517,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens_per_step": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "intermediate": cfg.I, "top_k": cfg.k, "cache_slots": cfg.S, "router_zipf_s": cfg.zipf_s},
-        "roofline": {"kernel": "decode expert FFN: ffn1_decode_bf16 + ffn2_decode_bf16 (one moe_ffn call)",
+        "roofline": {"kernel": "decode expert FFN: ffn1_decode_bf16 + ffn2_decode_bf16 (one moe_ffn call, work list in the kernel arguments)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),
