@@ -239,6 +239,10 @@ def bench_decode(args, torch, L, gen, cfg):
     trace = dl.trace()
     timed = trace[trace[:, 0] >= args.warmup]
     hit_rate = float(timed[:, 3].mean()) if len(timed) else 0.0
+    # steps that needed no fill: the layer's throughput without PCIe in the step
+    miss_steps = set(int(v) for v in timed[timed[:, 3] == 0][:, 0])
+    hit_lat = [lat[i] for i in range(len(lat)) if args.warmup + i not in miss_steps]
+    no_fill_tps = cfg.T * len(hit_lat) / sum(hit_lat) if hit_lat else 0.0
 
     split = device = None
     if not args.no_variants:
@@ -260,7 +264,8 @@ def bench_decode(args, torch, L, gen, cfg):
         value=args.steps * cfg.T / elapsed,
         ms_per_step=elapsed * 1e3 / args.steps,
         ffn=dict(bytes=ffn_bytes, ms=ffn_ms, n=n_ffn),
-        decode=dict(step_ms_p50=percentile(lat, 50) * 1e3, step_ms_p99=percentile(lat, 99) * 1e3,
+        decode=dict(tokens_per_s_no_fill_steps=no_fill_tps, no_fill_steps=len(hit_lat),
+                    step_ms_p50=percentile(lat, 50) * 1e3, step_ms_p99=percentile(lat, 99) * 1e3,
                     step_ms_max=max(lat) * 1e3, hit_rate=hit_rate, fills_timed=dl.n_fills - fills0,
                     fills_warmup=fills0, fill_gbs=fill_gbs, fill_frac_pcie=fill_gbs / PCIE_PEAK_GBS,
                     pool_gb=store.nbytes / 1e9, slots=cfg.S, cpu_split=split, device_control=device),
