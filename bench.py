@@ -239,9 +239,12 @@ def bench_decode(args, torch, L, gen, cfg):
     trace = dl.trace()
     timed = trace[trace[:, 0] >= args.warmup]
     hit_rate = float(timed[:, 3].mean()) if len(timed) else 0.0
-    # steps that needed no fill: the layer's throughput without PCIe in the step
+    # steps that needed no fill: the layer's throughput without PCIe in the step. A step's host-side
+    # interval ends when its counts reach the host, which waits for the previous step's FFN and fills:
+    # a fill in step t shows in the interval of step t + 1, so both are left out.
     miss_steps = set(int(v) for v in timed[timed[:, 3] == 0][:, 0])
-    hit_lat = [lat[i] for i in range(len(lat)) if args.warmup + i not in miss_steps]
+    hit_lat = [lat[i] for i in range(len(lat))
+               if args.warmup + i not in miss_steps and args.warmup + i - 1 not in miss_steps]
     no_fill_tps = cfg.T * len(hit_lat) / sum(hit_lat) if hit_lat else 0.0
 
     split = device = None
@@ -522,7 +525,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens_per_step": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "intermediate": cfg.I, "top_k": cfg.k, "cache_slots": cfg.S, "router_zipf_s": cfg.zipf_s},
-        "roofline": {"kernel": "decode expert FFN: ffn1_decode_bf16 + ffn2_decode_bf16 (one moe_ffn call, work list in the kernel arguments)",
+        "roofline": {"kernel": "decode expert FFN: ffn1_decode_bf16 + ffn2_decode_bf16 (the moe_ffn call of a layer-step with all six experts resident; work list in the kernel arguments)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),

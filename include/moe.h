@@ -339,12 +339,18 @@ int moe_pipe_copy_ms(moe_pipe_t* pipe, int layer, float* ms);
  *   out_dtype; *n_miss (nullable) = fills issued. Blocks the calling thread
  *   until the counts reach the host; the rest is enqueued on `stream`.
  *   On a failed fill the affected keys are invalidated (never half-resident).
+ *   Within a wave the FFN of the hits is enqueued before the stream waits for
+ *   the wave's fills, so it runs while the misses are copied; the misses'
+ *   FFN follows the copies (page "FreeToken-rtx-4090": transfers overlap
+ *   computation instead of each expert movement being waited for).
  *   When the cache splits misses (moe_cache_set_split), the misses assigned
  *   to the CPU run with moe_cpu_ffn from the pool on the calling thread while
  *   the GPU works on the others (bf16 activations and weights only, else
  *   MOE_EINVAL); their rows of y_perm are copied in before the combine.
- * moe_decoder_profile: every > 0 brackets every every-th FFN call (the first,
- *   then each every-th after it) with HIP events on `stream`; 0 turns it off;
+ * moe_decoder_profile: every > 0 brackets every every-th FFN call of a
+ *   layer-step whose experts were all resident (one wave, no fills; the
+ *   first such call, then each every-th after it) with HIP events on
+ *   `stream`; 0 turns it off;
  *   negative is EINVAL. moe_decoder_ffn_stats returns, over the bracketed
  *   calls since profiling was last set, the summed algorithmic bytes (expert
  *   blobs read + activations read/written), the summed milliseconds and the

@@ -274,9 +274,34 @@ int moe_cache_stats(const moe_cache_t* c, int64_t* hits, int64_t* misses) {
 // ---------------------------------------------------------------------------
 // Fills
 // ---------------------------------------------------------------------------
+}  // extern "C"
+
+// The copies of cache_fill_async, ordered after every earlier reader on the
+// compute stream; *done (the cache's event) marks their end on the fill
+// stream, and the compute stream is not yet made to wait for it.
+int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
+                       size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
+                       void* compute_stream, hipEvent_t* done);
+
+extern "C" {
+
 int cache_fill_async(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
                      size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
                      void* compute_stream) {
+  hipEvent_t done = nullptr;
+  const int rc = cache_fill_enqueue(c, misses, n, layer_pool, blob_stride, blob_bytes, slot_base, slot_stride,
+                                    fill_stream, compute_stream, &done);
+  if (rc != MOE_OK || !done) return rc;
+  hipError_t e = hipStreamWaitEvent(as_stream(compute_stream), done, 0);
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "cache_fill_async: ordering before compute");
+}
+
+}  // extern "C"
+
+int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
+                       size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
+                       void* compute_stream, hipEvent_t* done) {
+  *done = nullptr;
   if (!c || n < 0 || (n > 0 && (!misses || !layer_pool || !slot_base)) || blob_bytes > slot_stride ||
       blob_bytes > blob_stride)
     return fail(MOE_EINVAL, "cache_fill_async: bad argument");
@@ -307,11 +332,13 @@ int cache_fill_async(moe_cache_t* c, const moe_miss_t* misses, int n, const void
   }
   if (split) {
     e = hipEventRecord(c->ev_done, fs);
-    if (e == hipSuccess) e = hipStreamWaitEvent(cs, c->ev_done, 0);
-    if (e != hipSuccess) return hip_fail(e, "cache_fill_async: ordering before compute");
+    if (e != hipSuccess) return hip_fail(e, "cache_fill_async: completion event");
+    *done = c->ev_done;
   }
   return MOE_OK;
 }
+
+extern "C" {
 
 // ---------------------------------------------------------------------------
 // Expert FFN

@@ -20,6 +20,9 @@ extern "C" const char* moe_last_error(void);
 int moe_cache_layers(const moe_cache_t* c, int* n_layers);
 int moe_cache_experts(const moe_cache_t* c);
 bool moe_cache_splits(const moe_cache_t* c);
+int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
+                       size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
+                       void* compute_stream, hipEvent_t* done);
 
 namespace {
 // Errors go to the library's per-thread message (moe_last_error).
@@ -217,10 +220,10 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
     d->wave_misses.clear();
     for (int i = 0; i < nm; ++i)
       if (d->misses[i].wave == w) d->wave_misses.push_back(d->misses[i]);
+    hipEvent_t filled = nullptr;
     if (!d->wave_misses.empty()) {
-      rc = cache_fill_async(d->cache, d->wave_misses.data(), (int)d->wave_misses.size(), d->layer_pool.data(),
-                            d->blob_stride,
-                            d->blob_bytes, d->slot_base, d->slot_stride, d->fill, stream);
+      rc = cache_fill_enqueue(d->cache, d->wave_misses.data(), (int)d->wave_misses.size(), d->layer_pool.data(),
+                              d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, d->fill, stream, &filled);
       if (rc != MOE_OK) {
         // this wave's and every later wave's misses were never copied: unmap them
         const std::string msg = moe_last_error();
@@ -230,25 +233,45 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
       }
       d->fills += (int64_t)d->wave_misses.size();
     }
-    d->work.clear();
-    int rows = 0;
-    for (int i = 0; i < n; ++i) {
-      if (d->work_wave[i] != w) continue;
-      const int ex = d->work_e[i];
-      d->work.push_back(moe_work_t{ex, d->work_slot[i], d->offs[ex], d->counts_host[ex]});
-      rows += d->counts_host[ex];
-    }
-    const bool prof = d->prof_every > 0 && d->prof_calls++ % d->prof_every == 0;
-    if (prof && record_ffn_event(d, true, s, 0) != MOE_OK)
-      return dfail(MOE_EHIP, "moe_decoder_step: profiling event");
-    rc = moe_ffn(x, d->dtype, b.perm_src, d->work.data(), (int)d->work.size(), d->slot_base, d->slot_stride, d->wfmt,
-                 d->H, d->I, b.y_perm, b.ffn_ws, b.ffn_ws_bytes, MOE_FFN_AUTO, stream);
-    if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
-    if (prof) {
-      const double a = d->dtype == MOE_DT_BF16 ? 2.0 : 4.0, h = d->wfmt == MOE_W_F32 ? 4.0 : 2.0;
-      const double bytes = (double)d->work.size() * (double)d->blob_bytes +
-                           (double)rows * (d->H * a + 2.0 * d->I * h + d->H * 4.0);
-      if (record_ffn_event(d, false, s, bytes) != MOE_OK) return dfail(MOE_EHIP, "moe_decoder_step: profiling event");
+    // the wave in access order: its hits, then its misses (the last wave_misses.size() items); the hits'
+    // FFN runs while the misses are being copied, the misses' FFN once the copies are done
+    int wave_items = 0;
+    for (int i = 0; i < n; ++i) wave_items += d->work_wave[i] == w;
+    const int n_miss_w = (int)d->wave_misses.size();
+    const int split_at = filled ? wave_items - n_miss_w : wave_items;
+    for (int part = 0; part < 2; ++part) {
+      if (part == 1) {
+        if (!filled) break;
+        e = hipStreamWaitEvent(s, filled, 0);
+        if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: wait for fills: %s", hipGetErrorString(e));
+      }
+      d->work.clear();
+      int rows = 0, pos = 0;
+      for (int i = 0; i < n; ++i) {
+        if (d->work_wave[i] != w) continue;
+        const bool take = part == 0 ? pos < split_at : pos >= split_at;
+        ++pos;
+        if (!take) continue;
+        const int ex = d->work_e[i];
+        d->work.push_back(moe_work_t{ex, d->work_slot[i], d->offs[ex], d->counts_host[ex]});
+        rows += d->counts_host[ex];
+      }
+      if (d->work.empty()) continue;
+      // profiled calls: the FFN of a whole layer-step whose experts were all resident
+      const bool whole = nw == 1 && !filled;
+      const bool prof = whole && d->prof_every > 0 && d->prof_calls++ % d->prof_every == 0;
+      if (prof && record_ffn_event(d, true, s, 0) != MOE_OK)
+        return dfail(MOE_EHIP, "moe_decoder_step: profiling event");
+      rc = moe_ffn(x, d->dtype, b.perm_src, d->work.data(), (int)d->work.size(), d->slot_base, d->slot_stride,
+                   d->wfmt, d->H, d->I, b.y_perm, b.ffn_ws, b.ffn_ws_bytes, MOE_FFN_AUTO, stream);
+      if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
+      if (prof) {
+        const double a = d->dtype == MOE_DT_BF16 ? 2.0 : 4.0, h = d->wfmt == MOE_W_F32 ? 4.0 : 2.0;
+        const double bytes = (double)d->work.size() * (double)d->blob_bytes +
+                             (double)rows * (d->H * a + 2.0 * d->I * h + d->H * 4.0);
+        if (record_ffn_event(d, false, s, bytes) != MOE_OK)
+          return dfail(MOE_EHIP, "moe_decoder_step: profiling event");
+      }
     }
   }
   // misses run on the CPU, straight from the pool, while the GPU works on the
