@@ -174,3 +174,57 @@ def test_cache_resize_matches_oracle(L, S, sizes, E, Lyr, max_active):
     with pytest.raises(L.MoEError) as ei:
         L.moe_cache_resize(cache, 0)
     assert ei.value.code == L.MOE_ECAPACITY
+
+
+def test_device_decoder_and_graph_validation_without_gpu(L):
+    """The device-controlled decoder, graph and resize entry points reject bad arguments before any HIP call."""
+    lib = L._lib
+    st = ctypes.c_int(0)
+    bufs = L.DecoderBuffers()  # all-null buffers
+    pool = np.array([1, 1], np.uint64)  # two layer addresses (never read: creation fails earlier)
+    args = dict(L=2, E=16, S=6, T=3, H=256, I=128, k=2, dt=L.MOE_DT_BF16, wf=L.MOE_W_BF16)
+
+    def create(**kw):
+        a = dict(args, **kw)
+        return lib.moe_device_decoder_create(a["L"], a["E"], a["S"], a["T"], a["H"], a["I"], a["k"], a["dt"], a["wf"],
+                                             pool.ctypes.data, 1 << 20, 1, 1 << 20, ctypes.byref(bufs), 0,
+                                             ctypes.byref(st))
+
+    # a layer-step's experts must fit the cache at once: S >= min(E, k*T)
+    assert create(S=5) is None and st.value == L.MOE_ECAPACITY
+    assert "min(E, k*T_max)" in L.moe_last_error()
+    assert create(S=0) is None and st.value == L.MOE_ECAPACITY
+    assert create(E=2000) is None and st.value == L.MOE_EINVAL          # resolve kernel: one thread per expert
+    assert create(k=17) is None and st.value == L.MOE_EINVAL
+    assert create(dt=L.MOE_DT_F32) is None and st.value == L.MOE_EINVAL  # fp32 activations need fp32 weights
+    assert create(wf=9) is None and st.value == L.MOE_EINVAL
+    assert create() is None and st.value == L.MOE_EINVAL                 # null device buffers
+    assert lib.moe_device_decoder_create(2, 16, 6, 3, 256, 128, 2, 1, 1, None, 1 << 20, 1, 1 << 20,
+                                         ctypes.byref(bufs), 0, ctypes.byref(st)) is None
+    assert st.value == L.MOE_EINVAL
+    # calls on a null decoder or with null arguments
+    assert lib.moe_device_decoder_step(None, 0, 1, 1, 1, 1, 1, 0, None) == L.MOE_EINVAL
+    assert lib.moe_device_decoder_resize(None, 8, None, None) == L.MOE_EINVAL
+    h, m, r = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    assert lib.moe_device_decoder_stats(None, ctypes.byref(h), ctypes.byref(m), ctypes.byref(r)) == L.MOE_EINVAL
+    assert lib.moe_device_decoder_trace(None, None, 0, ctypes.byref(h)) == L.MOE_EINVAL
+    assert lib.moe_device_decoder_slot_of(None, 0, ctypes.byref(st)) == L.MOE_EINVAL
+    assert lib.moe_device_decoder_destroy(None) == L.MOE_OK
+    # graphs: capture needs a created stream; null graphs are refused, destroying NULL is a no-op
+    assert lib.moe_graph_begin(None) == L.MOE_EINVAL
+    assert lib.moe_graph_end(None, ctypes.byref(st)) is None and st.value == L.MOE_EINVAL
+    assert lib.moe_graph_launch(None, None) == L.MOE_EINVAL
+    assert lib.moe_graph_destroy(None) == L.MOE_OK
+    # resize of the host policy: null handle and a move array that is too short leave the cache unchanged
+    assert lib.moe_cache_resize(None, 4, None, 0, ctypes.byref(st)) == L.MOE_EINVAL
+    assert lib.moe_decoder_resize(None, 4, None, None) == L.MOE_EINVAL
+    c = L.MoeCache(1, 8, 4)
+    L.cache_resolve(c, 0, 0, np.array([0, 1, 2, 3], np.int32))
+    L.cache_resolve(c, 1, 0, np.array([2], np.int32))  # 2 becomes the most recent
+    moves = np.zeros((4, 3), np.int32)
+    assert lib.moe_cache_resize(c.h, 2, moves.ctypes.data, 0, ctypes.byref(st)) == L.MOE_EINVAL
+    assert L.moe_cache_capacity(c) == 4 and L.moe_cache_slot_of(c, 3) == 3
+    mv = L.moe_cache_resize(c, 2)  # keeps 2 (slot 2) and 3 (slot 3): both move below the new size
+    assert L.moe_cache_capacity(c) == 2
+    assert mv.tolist() == [[2, 2, 0], [3, 3, 1]]
+    assert [L.moe_cache_slot_of(c, k) for k in range(4)] == [-1, -1, 0, 1]
