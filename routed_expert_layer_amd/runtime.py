@@ -208,7 +208,7 @@ class DecodeLayer:
         """(fill MB/s, CPU expert MB/s) on this machine: n pinned blobs of `layer` copied to a scratch device
         buffer on the fill stream, and the host expert kernel on the same blobs with `rows` token rows."""
         store = self.store
-        n = min(n, store.E - 1)
+        n = max(1, min(n, store.E - 1))
         tmp = torch.empty(n * store.stride, dtype=torch.uint8, device=self.slots.device)
         misses = [[layer * store.E + e, e, -1, 0] for e in range(n)]
         fs = self.fill_stream
