@@ -55,7 +55,7 @@ CtlLayout ctl_layout(size_t n_keys, int S, int max_items, int64_t trace_cap) {
   o.ctl = take(8 * 8);
   o.work = take((size_t)max_items * 16);
   o.miss = take((size_t)max_items * 16);
-  o.n = take(2 * 4);
+  o.n = take(3 * 4);
   o.trace = take((size_t)trace_cap * 7 * 4);
   o.total = off;
   return o;
@@ -178,11 +178,19 @@ int moe_device_decoder_step(moe_device_decoder_t* d, int layer, const void* x, i
   hipError_t e = moe::launch_route(x, d->dtype == MOE_DT_BF16, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w,
                                    b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s, nullptr);
   if (e == hipSuccess) e = moe::launch_dev_resolve(b.counts, b.offsets, d->E, layer, d->c, s);
-  if (e == hipSuccess)
-    e = moe::launch_dev_fill(d->c, d->pool[layer], d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, s);
-  if (e == hipSuccess)
+  if (d->wfmt == MOE_W_F32) {
+    // fp32 experts: the misses are copied first, then every item runs from its slot
+    if (e == hipSuccess)
+      e = moe::launch_dev_fill(d->c, d->pool[layer], d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, s);
+    if (e == hipSuccess)
+      e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->c.n, d->c.work, items, T, d->slot_base,
+                                     d->slot_stride, d->H, d->I, hbuf, xg, b.y_perm, s);
+  } else if (e == hipSuccess) {
+    // one pass: the hits run from their slots while the misses stream from the pool over the host link and
+    // are written through into their slots
     e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->c.n, d->c.work, items, T, d->slot_base, d->slot_stride,
-                                   d->H, d->I, hbuf, xg, b.y_perm, s);
+                                   d->H, d->I, hbuf, xg, b.y_perm, s, d->c.n + 2, d->pool[layer], d->blob_stride);
+  }
   if (e == hipSuccess)
     e = moe::launch_combine(b.y_perm, b.perm_pos, b.topk_w, T, d->k, d->H, out, out_dtype == MOE_DT_BF16, s);
   if (e != hipSuccess) return dd_fail(MOE_EHIP, "moe_device_decoder_step: %s", hipGetErrorString(e));

@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kResolveThreads) void dev_resolve_kernel(const int3
   if (t == 0) {
     c.n[0] = n_hit + n_miss;
     c.n[1] = n_miss;
+    c.n[2] = n_hit;
     c.ctl[0] = clock0 + n_hit + n_miss;
     c.ctl[1] += n_hit;
     c.ctl[2] += n_miss;

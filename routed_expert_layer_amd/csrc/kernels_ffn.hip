@@ -20,22 +20,47 @@ namespace {
 // in the kernel arguments (lists resolved on the host; the grid matches the
 // list), or in device memory (lists resolved on the device; the grid is sized
 // for the longest possible list and blocks past the list's length exit).
+// src() gives the address item i's blob is read from and sets `fill` to an
+// address the kernel also writes every byte it reads to (nullptr: none).
 struct ArgWork {
   WorkArgs wa;
   __device__ __forceinline__ bool get(int i, int4& it) const {
     it = wa.item[i];
     return true;
   }
+  __device__ __forceinline__ const char* src(int, const int4& it, const char* slot_base, size_t slot_stride,
+                                             char*& fill) const {
+    fill = nullptr;
+    return slot_base + (size_t)it.x * slot_stride;
+  }
 };
+// With `pool` set, items from *n_hit on are misses: their blob is read from the
+// host pool (pool + expert * pool_stride, device-visible pinned memory) and
+// written through into their slot, so the fill and the FFN are one pass.
 struct DevWork {
   const int32_t* n;
   const int4* items;
+  const int32_t* n_hit;
+  const char* pool;
+  size_t pool_stride;
   __device__ __forceinline__ bool get(int i, int4& it) const {
     if (i >= *n) return false;
     it = items[i];
     return true;
   }
+  __device__ __forceinline__ const char* src(int i, const int4& it, const char* slot_base, size_t slot_stride,
+                                             char*& fill) const {
+    char* slot = const_cast<char*>(slot_base) + (size_t)it.x * slot_stride;
+    if (pool != nullptr && i >= *n_hit) {
+      fill = slot;
+      return pool + (size_t)it.w * pool_stride;
+    }
+    fill = nullptr;
+    return slot;
+  }
 };
+
+__device__ __forceinline__ void st16(char* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 
 // ---------------------------------------------------------------------------
 // fp32 weights: plain VALU kernels (small correctness configurations).
@@ -95,7 +120,10 @@ __global__ __launch_bounds__(256) void ffn1_decode_bf16(const uint16_t* __restri
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KC = H / 32;
   const int c0 = (KC * wave) >> 2, c1 = (KC * (wave + 1)) >> 2;
-  const char* wp = slot_base + (size_t)it.x * slot_stride + (size_t)tile * KC * 1024 + lane * 16;
+  char* fill;
+  const size_t toff = (size_t)tile * KC * 1024 + lane * 16;
+  const char* wp = wk.src(item, it, slot_base, slot_stride, fill) + toff;
+  char* fp = fill ? fill + toff : nullptr;
   const int kq = (lane >> 4) * 8;
   __shared__ f32x4_t red[4][64];
   for (int m0 = 0; m0 < it.z; m0 += 16) {
@@ -111,11 +139,15 @@ __global__ __launch_bounds__(256) void ffn1_decode_bf16(const uint16_t* __restri
         a[u] = ld16_nt(wp + (size_t)(c + u) * 1024);
         b[u] = valid ? ld16(xr + (c + u) * 32) : u32x4_t{0u, 0u, 0u, 0u};
       }
+      if (fp)
+#pragma unroll
+        for (int u = 0; u < kU; ++u) st16(fp + (size_t)(c + u) * 1024, a[u]);
 #pragma unroll
       for (int u = 0; u < kU; ++u) acc = mfma_bf16(a[u], b[u], acc);
     }
     for (; c < c1; ++c) {
       const u32x4_t a = ld16_nt(wp + (size_t)c * 1024);
+      if (fp) st16(fp + (size_t)c * 1024, a);
       const u32x4_t b = valid ? ld16(xr + c * 32) : u32x4_t{0u, 0u, 0u, 0u};
       acc = mfma_bf16(a, b, acc);
     }
@@ -144,7 +176,10 @@ __global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restri
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KC = I / 32;
   const int c0 = (KC * wave) >> 2, c1 = (KC * (wave + 1)) >> 2;
-  const char* wp = slot_base + (size_t)it.x * slot_stride + p2_off + (size_t)tile * KC * 1024 + lane * 16;
+  char* fill;
+  const size_t toff = p2_off + (size_t)tile * KC * 1024 + lane * 16;
+  const char* wp = wk.src(item, it, slot_base, slot_stride, fill) + toff;
+  char* fp = fill ? fill + toff : nullptr;
   const int kq = (lane >> 4) * 8;
   __shared__ f32x4_t red[4][64];
   for (int m0 = 0; m0 < it.z; m0 += 16) {
@@ -160,11 +195,15 @@ __global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restri
         a[u] = ld16_nt(wp + (size_t)(c + u) * 1024);
         b[u] = valid ? ld16(hr + (c + u) * 32) : u32x4_t{0u, 0u, 0u, 0u};
       }
+      if (fp)
+#pragma unroll
+        for (int u = 0; u < kU; ++u) st16(fp + (size_t)(c + u) * 1024, a[u]);
 #pragma unroll
       for (int u = 0; u < kU; ++u) acc = mfma_bf16(a[u], b[u], acc);
     }
     for (; c < c1; ++c) {
       const u32x4_t a = ld16_nt(wp + (size_t)c * 1024);
+      if (fp) st16(fp + (size_t)c * 1024, a);
       const u32x4_t b = valid ? ld16(hr + c * 32) : u32x4_t{0u, 0u, 0u, 0u};
       acc = mfma_bf16(a, b, acc);
     }
@@ -208,13 +247,20 @@ __global__ __launch_bounds__(256) void gather_f16_kernel(const uint16_t* __restr
 // the dequantised codes with the activation fragments b, scaled by the tile
 // rows' block scales and added to acc.
 __device__ __forceinline__ void int4_tile_block(const char* qp, const char* sp, const u32x4_t (&b)[4],
-                                                f32x4_t& acc) {
+                                                f32x4_t& acc, char* qf, char* sf) {
   const u32x4_t a = ld16_nt(qp);
   // The four fp16 scales are read as two 32-bit words and widened one by one
   // (a two-element fp16 vector view of the 64-bit load was miscompiled into
   // mixed-precision FMAs that all read the first word).
   const uint32_t sc0 = reinterpret_cast<const uint32_t*>(sp)[0];
   const uint32_t sc1 = reinterpret_cast<const uint32_t*>(sp)[1];
+  if (qf) {  // write-through of a miss: the codes by every lane, each 8-byte scale group by one lane
+    st16(qf, a);
+    if ((threadIdx.x & 15) == 0) {
+      reinterpret_cast<uint32_t*>(sf)[0] = sc0;
+      reinterpret_cast<uint32_t*>(sf)[1] = sc1;
+    }
+  }
   f32x4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) t = mfma_f16(int4x8_to_f16x8(a[j]), b[j], t);
@@ -233,7 +279,8 @@ __device__ __forceinline__ void int4_tile_block(const char* qp, const char* sp, 
 constexpr int kR = 4;
 template <typename Emit>
 __device__ __forceinline__ void int4_decode_tiles(const uint16_t* __restrict__ act, const int4 it, int K,
-                                                  const char* q_base, const char* s_base, int tile0, Emit emit) {
+                                                  const char* q_base, const char* s_base, char* qf_base,
+                                                  char* sf_base, int tile0, Emit emit) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KG = K / 128;
   const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
@@ -253,8 +300,12 @@ __device__ __forceinline__ void int4_decode_tiles(const uint16_t* __restrict__ a
       for (int j = 0; j < 4; ++j) b[j] = valid ? ld16(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int r = 0; r < kR; ++r)
-        int4_tile_block(q_base + ((size_t)(tile0 + r) * KG + g) * 1024 + lane * 16,
-                        s_base + ((size_t)(tile0 + r) * KG + g) * 32 + (lane >> 4) * 8, b, acc[r]);
+      {
+        const size_t qo = ((size_t)(tile0 + r) * KG + g) * 1024 + lane * 16;
+        const size_t so = ((size_t)(tile0 + r) * KG + g) * 32 + (lane >> 4) * 8;
+        int4_tile_block(q_base + qo, s_base + so, b, acc[r], qf_base ? qf_base + qo : nullptr,
+                        sf_base ? sf_base + so : nullptr);
+      }
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) red[wave][r][lane] = acc[r];
@@ -275,9 +326,11 @@ __global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restri
   const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
   int4 it;
   if (!wk.get(item, it)) return;
-  const char* blob = slot_base + (size_t)it.x * slot_stride;
+  char* fill;
+  const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   const int lane = threadIdx.x & 63;
-  int4_decode_tiles(xg, it, H, blob, blob + p1s_off, tile0, [&](int tile, int m, const f32x4_t& s) {
+  int4_decode_tiles(xg, it, H, blob, blob + p1s_off, fill, fill ? fill + p1s_off : nullptr, tile0,
+                    [&](int tile, int m, const f32x4_t& s) {
     const int i0 = 8 * tile + 2 * (lane >> 4);
     const uint32_t packed =
         (uint32_t)f32_to_f16_bits(silu(s[0]) * s[1]) | ((uint32_t)f32_to_f16_bits(silu(s[2]) * s[3]) << 16);
@@ -294,9 +347,11 @@ __global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restri
   const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
   int4 it;
   if (!wk.get(item, it)) return;
-  const char* blob = slot_base + (size_t)it.x * slot_stride;
+  char* fill;
+  const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   const int lane = threadIdx.x & 63;
-  int4_decode_tiles(hbuf, it, I, blob + p2_off, blob + p2s_off, tile0, [&](int tile, int m, const f32x4_t& s) {
+  int4_decode_tiles(hbuf, it, I, blob + p2_off, blob + p2s_off, fill ? fill + p2_off : nullptr,
+                    fill ? fill + p2s_off : nullptr, tile0, [&](int tile, int m, const f32x4_t& s) {
     *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
   });
 }
@@ -328,7 +383,8 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_floa
 // tile sums go to `emit(tile, m, sum)`.
 template <typename Row, typename Emit>
 __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, int K, const char* q_base,
-                                                   const char* s_base, int tile0, Emit emit) {
+                                                   const char* s_base, char* qf_base, char* sf_base, int tile0,
+                                                   Emit emit) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KG = K / 128;
   const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
@@ -351,6 +407,10 @@ __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, i
         const size_t blk = (size_t)(tile0 + r) * KG + g;
         const u32x4_t a = ld16_nt(q_base + blk * 1024 + lane * 16);
         const uint32_t sc = *reinterpret_cast<const uint32_t*>(s_base + blk * 64 + (lane & 15) * 4);
+        if (qf_base) {  // write-through of a miss: codes by every lane, the scale block by lanes 0..15
+          st16(qf_base + blk * 1024 + lane * 16, a);
+          if (lane < 16) *reinterpret_cast<uint32_t*>(sf_base + blk * 64 + lane * 4) = sc;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[r] = mfma_bf16(fp4x8_to_bf16x8(a[j], e8m0_to_f32(sc >> (8 * j))), b[j], acc[r]);
       }
@@ -375,9 +435,11 @@ __global__ __launch_bounds__(256) void ffn1_decode_mxfp4(const uint16_t* __restr
   const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
   int4 it;
   if (!wk.get(item, it)) return;
-  const char* blob = slot_base + (size_t)it.x * slot_stride;
+  char* fill;
+  const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   const int lane = threadIdx.x & 63;
-  mxfp4_decode_tiles([&](int m) { return x + (size_t)perm_src[it.y + m] * H; }, it, H, blob, blob + p1s_off, tile0,
+  mxfp4_decode_tiles([&](int m) { return x + (size_t)perm_src[it.y + m] * H; }, it, H, blob, blob + p1s_off, fill,
+                     fill ? fill + p1s_off : nullptr, tile0,
                      [&](int tile, int m, const f32x4_t& s) {
                        const int i0 = 8 * tile + 2 * (lane >> 4);
                        const uint32_t packed = (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) |
@@ -395,10 +457,11 @@ __global__ __launch_bounds__(256) void ffn2_decode_mxfp4(const uint16_t* __restr
   const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
   int4 it;
   if (!wk.get(item, it)) return;
-  const char* blob = slot_base + (size_t)it.x * slot_stride;
+  char* fill;
+  const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   const int lane = threadIdx.x & 63;
   mxfp4_decode_tiles([&](int m) { return hbuf + (size_t)(it.y + m) * I; }, it, I, blob + p2_off, blob + p2s_off,
-                     tile0, [&](int tile, int m, const f32x4_t& s) {
+                     fill ? fill + p2_off : nullptr, fill ? fill + p2s_off : nullptr, tile0, [&](int tile, int m, const f32x4_t& s) {
                        *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
                      });
 }
@@ -608,10 +671,12 @@ hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, c
 
 hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
                                  const int4* items, int max_items, int max_rows, const char* slot_base,
-                                 size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y, hipStream_t s) {
+                                 size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y, hipStream_t s,
+                                 const int32_t* n_hit, const char* pool, size_t pool_stride) {
   if (max_items == 0) return hipSuccess;
-  return decode_kernels(wfmt, x, perm_src, DevWork{n_items, items}, max_items, max_rows, slot_base, slot_stride, H, I,
-                        hbuf, xg, y, s);
+  if (wfmt == 0 && pool != nullptr) return hipErrorInvalidValue;  // the fp32 kernels do not write through
+  return decode_kernels(wfmt, x, perm_src, DevWork{n_items, items, n_hit, pool, pool_stride}, max_items, max_rows,
+                        slot_base, slot_stride, H, I, hbuf, xg, y, s);
 }
 
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,

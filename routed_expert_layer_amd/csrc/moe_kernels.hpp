@@ -115,10 +115,14 @@ hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, c
                              void* hbuf, void* xg, float* y, hipStream_t s);
 // The same kernels with the work list in device memory: *n_items items at
 // `items` (device), at most max_items of them with at most max_rows rows
-// each; launch shapes depend only on max_items and max_rows.
+// each; launch shapes depend only on max_items and max_rows. With `pool`
+// set (not for fp32), items from *n_hit on are misses whose blob is read
+// from pool + expert * pool_stride and written through into their slot.
 hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
                                  const int4* items, int max_items, int max_rows, const char* slot_base,
-                                 size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y, hipStream_t s);
+                                 size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y, hipStream_t s,
+                                 const int32_t* n_hit = nullptr, const char* pool = nullptr,
+                                 size_t pool_stride = 0);
 // 128 x 128-tile fallback GEMM for shapes the large-tile GEMM does not take.
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,
                               size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s);
@@ -159,7 +163,7 @@ struct DevCache {
   int S;
   int4* work;         // [max items] {slot, row_begin, rows, expert}: hits, then misses
   int4* miss;         // [max items] {expert, slot, victim key or -1, key}
-  int32_t* n;         // [0] work items, [1] misses (of the last resolve)
+  int32_t* n;         // [0] work items, [1] misses, [2] hits (of the last resolve)
   int32_t* trace;     // [trace_cap][7] records as moe_trace_t
   int64_t trace_cap;
 };
