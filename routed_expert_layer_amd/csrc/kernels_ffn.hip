@@ -106,6 +106,39 @@ __global__ __launch_bounds__(256) void ffn2_f32_kernel(const float* __restrict__
 // ---------------------------------------------------------------------------
 constexpr int kU = 8;  // fragments in flight per wave
 
+// One wave's share of a tile: the sum over fragments [c0, c1) (1 KiB apart
+// from wp) of each fragment times the activation fragment at ar + 32c. With
+// WT every weight fragment is also stored at the same offset from fp (the
+// write-through of a miss); the stores follow each batch's loads, and the
+// variant without them keeps its loads free to move.
+template <bool WT>
+__device__ __forceinline__ f32x4_t bf16_wave_dot(const char* wp, char* fp, const uint16_t* ar, bool valid, int c0,
+                                                 int c1) {
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  int c = c0;
+  for (; c + kU <= c1; c += kU) {
+    u32x4_t a[kU], b[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      a[u] = ld16_nt(wp + (size_t)(c + u) * 1024);
+      b[u] = valid ? ld16(ar + (c + u) * 32) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if constexpr (WT) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) st16(fp + (size_t)(c + u) * 1024, a[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) acc = mfma_bf16(a[u], b[u], acc);
+  }
+  for (; c < c1; ++c) {
+    const u32x4_t a = ld16_nt(wp + (size_t)c * 1024);
+    const u32x4_t b = valid ? ld16(ar + c * 32) : u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (WT) st16(fp + (size_t)c * 1024, a);
+    acc = mfma_bf16(a, b, acc);
+  }
+  return acc;
+}
+
 // Gate/up: workgroup = one 16-row tile of P1 (8 gate + 8 up columns) of one
 // item; wave w reduces fragments [KC*w/4, KC*(w+1)/4).
 template <typename W>
@@ -130,27 +163,8 @@ __global__ __launch_bounds__(256) void ffn1_decode_bf16(const uint16_t* __restri
     const int m = m0 + (lane & 15);
     const bool valid = m < it.z;
     const uint16_t* xr = x + (size_t)(valid ? perm_src[it.y + m] : 0) * H + kq;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    int c = c0;
-    for (; c + kU <= c1; c += kU) {
-      u32x4_t a[kU], b[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        a[u] = ld16_nt(wp + (size_t)(c + u) * 1024);
-        b[u] = valid ? ld16(xr + (c + u) * 32) : u32x4_t{0u, 0u, 0u, 0u};
-      }
-      if (fp)
-#pragma unroll
-        for (int u = 0; u < kU; ++u) st16(fp + (size_t)(c + u) * 1024, a[u]);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) acc = mfma_bf16(a[u], b[u], acc);
-    }
-    for (; c < c1; ++c) {
-      const u32x4_t a = ld16_nt(wp + (size_t)c * 1024);
-      if (fp) st16(fp + (size_t)c * 1024, a);
-      const u32x4_t b = valid ? ld16(xr + c * 32) : u32x4_t{0u, 0u, 0u, 0u};
-      acc = mfma_bf16(a, b, acc);
-    }
+    const f32x4_t acc =
+        fp ? bf16_wave_dot<true>(wp, fp, xr, valid, c0, c1) : bf16_wave_dot<false>(wp, nullptr, xr, valid, c0, c1);
     red[wave][lane] = acc;
     __syncthreads();
     if (wave == 0 && valid) {
@@ -186,27 +200,8 @@ __global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restri
     const int m = m0 + (lane & 15);
     const bool valid = m < it.z;
     const uint16_t* hr = hbuf + (size_t)(it.y + (valid ? m : 0)) * I + kq;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    int c = c0;
-    for (; c + kU <= c1; c += kU) {
-      u32x4_t a[kU], b[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        a[u] = ld16_nt(wp + (size_t)(c + u) * 1024);
-        b[u] = valid ? ld16(hr + (c + u) * 32) : u32x4_t{0u, 0u, 0u, 0u};
-      }
-      if (fp)
-#pragma unroll
-        for (int u = 0; u < kU; ++u) st16(fp + (size_t)(c + u) * 1024, a[u]);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) acc = mfma_bf16(a[u], b[u], acc);
-    }
-    for (; c < c1; ++c) {
-      const u32x4_t a = ld16_nt(wp + (size_t)c * 1024);
-      if (fp) st16(fp + (size_t)c * 1024, a);
-      const u32x4_t b = valid ? ld16(hr + c * 32) : u32x4_t{0u, 0u, 0u, 0u};
-      acc = mfma_bf16(a, b, acc);
-    }
+    const f32x4_t acc =
+        fp ? bf16_wave_dot<true>(wp, fp, hr, valid, c0, c1) : bf16_wave_dot<false>(wp, nullptr, hr, valid, c0, c1);
     red[wave][lane] = acc;
     __syncthreads();
     if (wave == 0 && valid) {
@@ -244,23 +239,10 @@ __global__ __launch_bounds__(256) void gather_f16_kernel(const uint16_t* __restr
 }
 
 // One 128-wide K block of one 16-row tile: four fp16 matrix-core products of
-// the dequantised codes with the activation fragments b, scaled by the tile
-// rows' block scales and added to acc.
-__device__ __forceinline__ void int4_tile_block(const char* qp, const char* sp, const u32x4_t (&b)[4],
-                                                f32x4_t& acc, char* qf, char* sf) {
-  const u32x4_t a = ld16_nt(qp);
-  // The four fp16 scales are read as two 32-bit words and widened one by one
-  // (a two-element fp16 vector view of the 64-bit load was miscompiled into
-  // mixed-precision FMAs that all read the first word).
-  const uint32_t sc0 = reinterpret_cast<const uint32_t*>(sp)[0];
-  const uint32_t sc1 = reinterpret_cast<const uint32_t*>(sp)[1];
-  if (qf) {  // write-through of a miss: the codes by every lane, each 8-byte scale group by one lane
-    st16(qf, a);
-    if ((threadIdx.x & 15) == 0) {
-      reinterpret_cast<uint32_t*>(sf)[0] = sc0;
-      reinterpret_cast<uint32_t*>(sf)[1] = sc1;
-    }
-  }
+// the dequantised codes a with the activation fragments b, scaled by the tile
+// rows' block scales (four fp16 in sc0, sc1) and added to acc.
+__device__ __forceinline__ void int4_tile_mac(const u32x4_t& a, uint32_t sc0, uint32_t sc1, const u32x4_t (&b)[4],
+                                              f32x4_t& acc) {
   f32x4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) t = mfma_f16(int4x8_to_f16x8(a[j]), b[j], t);
@@ -275,9 +257,11 @@ __device__ __forceinline__ void int4_tile_block(const char* qp, const char* sp, 
 // activation fragment it loads to all kR tiles (one activation load per kR
 // KiB of codes). Partial sums meet in LDS; wave w finishes tile w.
 // act: fp16 activations [rows, K] (gathered x or h); the finished 16 x 16
-// tile sums go to `emit(tile, m, sum)`.
+// tile sums go to `emit(tile, m, sum)`. With WT every code and scale loaded
+// is also stored at the same offset from qf_base / sf_base (the write-through
+// of a miss), after each K block's loads.
 constexpr int kR = 4;
-template <typename Emit>
+template <bool WT, typename Emit>
 __device__ __forceinline__ void int4_decode_tiles(const uint16_t* __restrict__ act, const int4 it, int K,
                                                   const char* q_base, const char* s_base, char* qf_base,
                                                   char* sf_base, int tile0, Emit emit) {
@@ -298,14 +282,33 @@ __device__ __forceinline__ void int4_decode_tiles(const uint16_t* __restrict__ a
       u32x4_t b[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = valid ? ld16(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+      u32x4_t a[kR];
+      uint32_t sc0[kR], sc1[kR];
 #pragma unroll
-      for (int r = 0; r < kR; ++r)
-      {
-        const size_t qo = ((size_t)(tile0 + r) * KG + g) * 1024 + lane * 16;
-        const size_t so = ((size_t)(tile0 + r) * KG + g) * 32 + (lane >> 4) * 8;
-        int4_tile_block(q_base + qo, s_base + so, b, acc[r], qf_base ? qf_base + qo : nullptr,
-                        sf_base ? sf_base + so : nullptr);
+      for (int r = 0; r < kR; ++r) {
+        const size_t blk = (size_t)(tile0 + r) * KG + g;
+        a[r] = ld16_nt(q_base + blk * 1024 + lane * 16);
+        // The four fp16 scales are read as two 32-bit words and widened one by
+        // one (a two-element fp16 vector view of the 64-bit load was
+        // miscompiled into mixed-precision FMAs that all read the first word).
+        const uint32_t* sp = reinterpret_cast<const uint32_t*>(s_base + blk * 32 + (lane >> 4) * 8);
+        sc0[r] = sp[0];
+        sc1[r] = sp[1];
       }
+      if constexpr (WT) {  // codes by every lane, each 8-byte scale group by one lane
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+          const size_t blk = (size_t)(tile0 + r) * KG + g;
+          st16(qf_base + blk * 1024 + lane * 16, a[r]);
+          if ((lane & 15) == 0) {
+            uint32_t* sf = reinterpret_cast<uint32_t*>(sf_base + blk * 32 + (lane >> 4) * 8);
+            sf[0] = sc0[r];
+            sf[1] = sc1[r];
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kR; ++r) int4_tile_mac(a[r], sc0[r], sc1[r], b, acc[r]);
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) red[wave][r][lane] = acc[r];
@@ -329,13 +332,16 @@ __global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restri
   char* fill;
   const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   const int lane = threadIdx.x & 63;
-  int4_decode_tiles(xg, it, H, blob, blob + p1s_off, fill, fill ? fill + p1s_off : nullptr, tile0,
-                    [&](int tile, int m, const f32x4_t& s) {
+  const auto emit = [&](int tile, int m, const f32x4_t& s) {
     const int i0 = 8 * tile + 2 * (lane >> 4);
     const uint32_t packed =
         (uint32_t)f32_to_f16_bits(silu(s[0]) * s[1]) | ((uint32_t)f32_to_f16_bits(silu(s[2]) * s[3]) << 16);
     *reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0) = packed;
-  });
+  };
+  if (fill)
+    int4_decode_tiles<true>(xg, it, H, blob, blob + p1s_off, fill, fill + p1s_off, tile0, emit);
+  else
+    int4_decode_tiles<false>(xg, it, H, blob, blob + p1s_off, nullptr, nullptr, tile0, emit);
 }
 
 template <typename W>
@@ -350,10 +356,13 @@ __global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restri
   char* fill;
   const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   const int lane = threadIdx.x & 63;
-  int4_decode_tiles(hbuf, it, I, blob + p2_off, blob + p2s_off, fill ? fill + p2_off : nullptr,
-                    fill ? fill + p2s_off : nullptr, tile0, [&](int tile, int m, const f32x4_t& s) {
+  const auto emit = [&](int tile, int m, const f32x4_t& s) {
     *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
-  });
+  };
+  if (fill)
+    int4_decode_tiles<true>(hbuf, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0, emit);
+  else
+    int4_decode_tiles<false>(hbuf, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit);
 }
 
 // ---------------------------------------------------------------------------
@@ -380,8 +389,10 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_floa
 // owns kR consecutive 16-row tiles of one expert, its four waves split the
 // 128-wide K blocks, and each activation fragment loaded serves all kR tiles.
 // act: bf16 activations; row m of the group is act_row(m). Finished 16 x 16
-// tile sums go to `emit(tile, m, sum)`.
-template <typename Row, typename Emit>
+// tile sums go to `emit(tile, m, sum)`. With WT every code and scale loaded
+// is also stored at the same offset from qf_base / sf_base (the write-through
+// of a miss), after each K block's loads.
+template <bool WT, typename Row, typename Emit>
 __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, int K, const char* q_base,
                                                    const char* s_base, char* qf_base, char* sf_base, int tile0,
                                                    Emit emit) {
@@ -402,18 +413,27 @@ __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, i
       u32x4_t b[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = valid ? ld16(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+      u32x4_t a[kR];
+      uint32_t sc[kR];
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
         const size_t blk = (size_t)(tile0 + r) * KG + g;
-        const u32x4_t a = ld16_nt(q_base + blk * 1024 + lane * 16);
-        const uint32_t sc = *reinterpret_cast<const uint32_t*>(s_base + blk * 64 + (lane & 15) * 4);
-        if (qf_base) {  // write-through of a miss: codes by every lane, the scale block by lanes 0..15
-          st16(qf_base + blk * 1024 + lane * 16, a);
-          if (lane < 16) *reinterpret_cast<uint32_t*>(sf_base + blk * 64 + lane * 4) = sc;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[r] = mfma_bf16(fp4x8_to_bf16x8(a[j], e8m0_to_f32(sc >> (8 * j))), b[j], acc[r]);
+        a[r] = ld16_nt(q_base + blk * 1024 + lane * 16);
+        sc[r] = *reinterpret_cast<const uint32_t*>(s_base + blk * 64 + (lane & 15) * 4);
       }
+      if constexpr (WT) {  // codes by every lane, the scale block by lanes 0..15
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+          const size_t blk = (size_t)(tile0 + r) * KG + g;
+          st16(qf_base + blk * 1024 + lane * 16, a[r]);
+          if (lane < 16) *reinterpret_cast<uint32_t*>(sf_base + blk * 64 + lane * 4) = sc[r];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kR; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[r] = mfma_bf16(fp4x8_to_bf16x8(a[r][j], e8m0_to_f32(sc[r] >> (8 * j))), b[j], acc[r]);
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) red[wave][r][lane] = acc[r];
@@ -438,14 +458,17 @@ __global__ __launch_bounds__(256) void ffn1_decode_mxfp4(const uint16_t* __restr
   char* fill;
   const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   const int lane = threadIdx.x & 63;
-  mxfp4_decode_tiles([&](int m) { return x + (size_t)perm_src[it.y + m] * H; }, it, H, blob, blob + p1s_off, fill,
-                     fill ? fill + p1s_off : nullptr, tile0,
-                     [&](int tile, int m, const f32x4_t& s) {
-                       const int i0 = 8 * tile + 2 * (lane >> 4);
-                       const uint32_t packed = (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) |
-                                               ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
-                       *reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0) = packed;
-                     });
+  const auto row = [&](int m) { return x + (size_t)perm_src[it.y + m] * H; };
+  const auto emit = [&](int tile, int m, const f32x4_t& s) {
+    const int i0 = 8 * tile + 2 * (lane >> 4);
+    const uint32_t packed =
+        (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
+    *reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0) = packed;
+  };
+  if (fill)
+    mxfp4_decode_tiles<true>(row, it, H, blob, blob + p1s_off, fill, fill + p1s_off, tile0, emit);
+  else
+    mxfp4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, tile0, emit);
 }
 
 template <typename W>
@@ -460,10 +483,14 @@ __global__ __launch_bounds__(256) void ffn2_decode_mxfp4(const uint16_t* __restr
   char* fill;
   const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   const int lane = threadIdx.x & 63;
-  mxfp4_decode_tiles([&](int m) { return hbuf + (size_t)(it.y + m) * I; }, it, I, blob + p2_off, blob + p2s_off,
-                     fill ? fill + p2_off : nullptr, fill ? fill + p2s_off : nullptr, tile0, [&](int tile, int m, const f32x4_t& s) {
-                       *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
-                     });
+  const auto row = [&](int m) { return hbuf + (size_t)(it.y + m) * I; };
+  const auto emit = [&](int tile, int m, const f32x4_t& s) {
+    *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
+  };
+  if (fill)
+    mxfp4_decode_tiles<true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0, emit);
+  else
+    mxfp4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit);
 }
 
 // ---------------------------------------------------------------------------
