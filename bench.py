@@ -72,7 +72,7 @@ def _definition(src, signature):
 
 def decode_ffn_digest(root):
     """sha256 over the source text the decode expert-FFN kernels are built from: both kernels, their
-    launchers, the work sources, the device helpers and the work-list / blob-layout definitions."""
+    wave loop, launchers, the work sources, the device helpers and the work-list / blob-layout definitions."""
     import hashlib
     csrc = os.path.join(root, "routed_expert_layer_amd", "csrc")
     ffn = open(os.path.join(csrc, "kernels_ffn.hip")).read()
@@ -82,7 +82,8 @@ def decode_ffn_digest(root):
              _definition(ffn, "__global__ __launch_bounds__(256) void ffn2_decode_bf16("),
              _definition(ffn, "hipError_t launch_ffn_decode("),
              _definition(ffn, "hipError_t decode_kernels("), _definition(ffn, "struct ArgWork"),
-             _definition(ffn, "struct DevWork"),
+             _definition(ffn, "struct DevWork"), _definition(ffn, "f32x4_t bf16_wave_dot("),
+             _definition(ffn, "void st16("), ffn[ffn.index("constexpr int kU ="):].split("\n", 1)[0],
              _definition(hdr, "struct WorkArgs"), _definition(hdr, "inline BlobLayout blob_layout(")]
     return hashlib.sha256("\n".join(parts).encode()).hexdigest()
 
