@@ -8,8 +8,9 @@
 // Operands go straight from global memory into LDS in fragment order (the
 // direct-to-LDS load of gfx950, one 1 KiB fragment per wave instruction, no
 // register staging), through six (128-token tile) or four (256-token tile)
-// LDS stages, all but one in flight while one is consumed; one barrier per
-// stage. Weight fragments are contiguous
+// LDS stages, all in flight; a wave reads the next stage's fragments into a
+// second register set while its matrix-core instructions consume the current
+// one; one barrier per stage. Weight fragments are contiguous
 // in the expert blob (1 KiB per wave load); token rows are gathered through
 // perm_src (gate/up), read in order (down projection) or taken from x (router).
 // Blocks are grouped into super-tiles of 32 (8 token tiles x 4 weight tiles
@@ -27,6 +28,8 @@ namespace {
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 at their maxima).
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// ... and for lgkmcnt <= n only (vmcnt and expcnt at their maxima).
+constexpr int lgkmcnt_only(int n) { return 15 | (3 << 14) | (7 << 4) | ((n & 15) << 8); }
 
 // One 16-byte chunk per lane from base + off (a wave-uniform base, a 32-bit
 // lane offset) straight into the wave's 1 KiB at `lds` (lane l at lds + 16 l),
@@ -126,12 +129,13 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
       }
     }
   }
-  auto issue = [&](int kt) {  // stage kt -> LDS buffer kt % NS
-    char* base = lds[kt % NS];
+  // Stage `stage` -> LDS buffer `buf`.
+  auto issue = [&](int stage, int buf) {
+    char* base = lds[buf];
 #pragma unroll
     for (int q = 0; q < FPW; ++q)
       buffer_load_lds16(q < QW ? static_cast<const void*>(wbase) : static_cast<const void*>(bsrc),
-                        off[q] + (uint32_t)kt * kstep[q], base + (wave + 8 * q) * 1024);
+                        off[q] + (uint32_t)stage * kstep[q], base + (wave + 8 * q) * 1024);
   };
 
   f32x4_t acc[WN][WM];
@@ -152,9 +156,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
     for (int i = 0; i < WN; ++i) f.a[i] = *reinterpret_cast<const u32x4_t*>(b + (wn * WN + i) * 1024 + lane * 16);
   };
   // Every wave runs its matrix-core work, also on token columns past the
-  // group (their results are never stored): no branch separates the LDS
-  // reads from the instructions that consume them, so each instruction
-  // waits only for its own operands.
+  // group (their results are never stored).
   auto compute = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < WN; ++i)
@@ -162,30 +164,45 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
       for (int j = 0; j < WM; ++j) acc[i][j] = mfma_bf16(f.a[i], f.b[j], acc[i][j]);
   };
 
-  {
-    // Two waves per SIMD: while one wave waits for its LDS reads the other
-    // runs matrix-core work; one stage at a time.
-    for (int s0 = 0; s0 < NS - 1 && s0 < KC; ++s0) issue(s0);
-    for (int kt = 0; kt < KC; ++kt) {
-      // stage kt has landed once at most the later stages' loads are pending
-      if (kt + NS - 2 < KC) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 2)));
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-      }
-      // every wave's part of stage kt is in LDS, and every wave is done with
-      // stage kt - 1, whose buffer is refilled next
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (kt + NS - 1 < KC) issue(kt + NS - 1);
-      Frags f;
-      read_stage(kt, f);
-      // the wave with matrix-core work issues first; the other wave's loads
-      // and LDS reads fill the gaps
-      __builtin_amdgcn_s_setprio(1);
-      compute(f);
-      __builtin_amdgcn_s_setprio(0);
+  // All NS buffers are in flight. In step kt a wave computes on stage kt's
+  // fragments (read into registers during step kt - 1) while it reads stage
+  // kt + 1's, so LDS latency hides behind matrix-core work; after the step's
+  // barrier (every wave's loads of stage kt + 1 have landed and every wave
+  // has finished reading stage kt) stage kt's buffer is refilled with stage
+  // kt + NS. Stage numbers past the last are clamped to it (valid addresses,
+  // results unused), so each step is one basic block for any K and the
+  // compiler can interleave the reads with the matrix-core instructions.
+  auto step = [&](int kt, Frags& cur, Frags& nxt) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 2)));  // this wave's loads of stage kt + 1 landed
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));              // and its reads of stage kt completed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(kt + NS, KC - 1), kt % NS);
+    read_stage(min(kt + 1, KC - 1), nxt);
+    __builtin_amdgcn_s_setprio(1);
+    compute(cur);
+    // one LDS read, then a share of the matrix-core instructions, in turn
+#pragma unroll
+    for (int q = 0; q < WN + WM; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (WN * WM) / (WN + WM), 0);
     }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  {
+    for (int s0 = 0; s0 < NS; ++s0) issue(min(s0, KC - 1), s0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 1)));  // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    Frags f0, f1;
+    read_stage(0, f0);
+    int kt = 0;
+    for (; kt + 1 < KC; kt += 2) {
+      step(kt, f0, f1);
+      step(kt + 1, f1, f0);
+    }
+    if (kt < KC) step(kt, f0, f1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));  // the clamped loads past the end have landed too
   }
 
   // Epilogue.
