@@ -27,6 +27,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
+PEAK_CLOCK_GHZ = 2.4         # the clock the matrix-core peak is quoted at
 PCIE_PEAK_GBS = 63.0         # PCIe Gen5 x16, one direction
 
 
@@ -276,6 +277,30 @@ def bench_decode(args, torch, L, gen, cfg):
     )
 
 
+class ClockRecord:
+    """Mean shader clock of the prefill expert GEMMs enqueued while it is active (moe_clock_record)."""
+
+    def __init__(self, torch, L):
+        self.L = L
+        self.sums = torch.zeros(2, dtype=torch.int64, device="cuda")
+
+    def __enter__(self):
+        self.L.moe_clock_record(self.sums)
+        return self
+
+    def __exit__(self, *exc):
+        self.L.moe_clock_record(None)
+
+    def ghz(self):
+        cyc, ticks = (int(v) for v in self.sums.cpu())
+        return cyc / ticks / 10.0 if ticks > 0 else None
+
+
+def at_clock(tfs, ghz):
+    """Share of the matrix-core peak scaled to the measured clock."""
+    return tfs / (MFMA_BF16_PEAK_TFS * ghz / PEAK_CLOCK_GHZ) if ghz else None
+
+
 def bench_prefill(args, torch, L, gen, cfg, reps=5):
     from routed_expert_layer_amd.runtime import PrefillLayer
     dev = "cuda"
@@ -301,9 +326,10 @@ def bench_prefill(args, torch, L, gen, cfg, reps=5):
     timer.enabled = True
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(reps):
-        pl.forward(x, Wr, b, buf, wfmt=wf, timer=timer)
-    torch.cuda.synchronize()
+    with ClockRecord(torch, L) as clk:
+        for _ in range(reps):
+            pl.forward(x, Wr, b, buf, wfmt=wf, timer=timer)
+        torch.cuda.synchronize()
     layer_ms = (time.perf_counter() - t0) * 1e3 / reps
     flops, ms, n = timer.result()
     active = int((pl.last_counts > 0).sum())
@@ -311,7 +337,8 @@ def bench_prefill(args, torch, L, gen, cfg, reps=5):
     wbytes = active * blob
     del buf
     return dict(workload=cfg.name, tokens=cfg.T, layer_ms=layer_ms, gemm_ms=ms / n, tflops=tfs,
-                mfma_frac=tfs / MFMA_BF16_PEAK_TFS, weight_gbs=wbytes / (ms / n * 1e-3) / 1e9,
+                mfma_frac=tfs / MFMA_BF16_PEAK_TFS, gemm_clock_ghz=clk.ghz(), mfma_frac_at_clock=at_clock(tfs, clk.ghz()),
+                weight_gbs=wbytes / (ms / n * 1e-3) / 1e9,
                 hbm_frac=wbytes / (ms / n * 1e-3) / 1e9 / HBM_PEAK_GBS, active_experts=active,
                 group_min=int(pl.last_counts[pl.last_counts > 0].min()), group_max=int(pl.last_counts.max()))
 
@@ -333,6 +360,7 @@ def bench_prefill_pipeline(args, torch, L, gen, cfg):
         pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, store.stride, dev, wfmt=wf)
         s = torch.cuda.current_stream()
         # warm-up pass (kernels and the copy path), then the timed pass
+        clk = ClockRecord(torch, L)
         for rep in range(2):
             pipe = L.MoePipe(store.layer_ptrs, store.layer_bytes)
             timer = EventTimer(torch, cfg.L)
@@ -341,6 +369,8 @@ def bench_prefill_pipeline(args, torch, L, gen, cfg):
             groups = []
             torch.cuda.synchronize()
             t0 = time.perf_counter()
+            if rep == 1:
+                clk.__enter__()
             for l in range(cfg.L):
                 base = L.moe_pipe_begin_layer(pipe, l, s)
                 ev[l][0].record(s)
@@ -349,6 +379,8 @@ def bench_prefill_pipeline(args, torch, L, gen, cfg):
                 L.moe_pipe_end_layer(pipe, l, s)
                 groups.append((int((pl.last_counts > 0).sum()), int(pl.last_counts.max())))
             torch.cuda.synchronize()
+            if rep == 1:
+                clk.__exit__()
             wall = (time.perf_counter() - t0) * 1e3
             copy_ms = [L.moe_pipe_copy_ms(pipe, l) for l in range(cfg.L)]
             comp_ms = [a.elapsed_time(b) for a, b in ev]
@@ -357,7 +389,8 @@ def bench_prefill_pipeline(args, torch, L, gen, cfg):
         tfs = flops / (gemm_ms * 1e-3) / 1e12
         exposed = max(0.0, wall - sum(copy_ms))
         return dict(workload=cfg.name, layers=cfg.L, tokens_per_layer=cfg.T,
-                    gemm_tflops=tfs, mfma_frac=tfs / MFMA_BF16_PEAK_TFS, gemm_ms_per_layer=gemm_ms / n,
+                    gemm_tflops=tfs, mfma_frac=tfs / MFMA_BF16_PEAK_TFS, gemm_clock_ghz=clk.ghz(),
+                    mfma_frac_at_clock=at_clock(tfs, clk.ghz()), gemm_ms_per_layer=gemm_ms / n,
                     layer_compute_ms=sum(comp_ms) / cfg.L, copy_ms_per_layer=sum(copy_ms) / cfg.L,
                     copy_gbs=store.layer_bytes / (sum(copy_ms) / cfg.L * 1e-3) / 1e9,
                     copy_frac_pcie=store.layer_bytes / (sum(copy_ms) / cfg.L * 1e-3) / 1e9 / PCIE_PEAK_GBS,

@@ -316,6 +316,24 @@ int moe_pipe_end_layer(moe_pipe_t* pipe, int layer, void* compute_stream);
 int moe_pipe_copy_ms(moe_pipe_t* pipe, int layer, float* ms);
 
 /* ------------------------------------------------------------------------ *
+ * Clock diagnostic of the prefill expert GEMMs.
+ *
+ * Matrix-core throughput is quoted against the datasheet peak at 2.4 GHz; under
+ * sustained matrix-core load the shader clock drops below that (power limit),
+ * so a second figure against the peak at the clock the kernels actually ran
+ * at needs that clock. moe_clock_record(sums): sums is a device pointer to two
+ * uint64 (the caller zeroes them) or NULL (off). While it is set, every block
+ * of the prefill expert GEMM launches (moe_ffn in prefill mode, bf16 and
+ * MXFP4 weights; not the router) adds the shader-clock cycles and the 100 MHz
+ * real-time ticks it spent from its start to the end of its main loop to
+ * sums[0] and sums[1] with device atomics, so sums[0] / sums[1] * 0.1 is the
+ * time-weighted mean clock in GHz. The setting is process-wide and read when
+ * a launch is enqueued: set it while no other thread enqueues prefill work,
+ * keep the buffer alive until those launches have finished. Returns MOE_OK.
+ * ------------------------------------------------------------------------ */
+int moe_clock_record(unsigned long long* sums);
+
+/* ------------------------------------------------------------------------ *
  * Decode layer-step driver.
  *
  * One call runs a whole decode layer-step -- moe_route, the copy of the

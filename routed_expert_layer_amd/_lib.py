@@ -23,7 +23,7 @@ SYMBOLS = [
     "moe_pack_expert", "moe_pool_alloc", "moe_pool_free", "moe_cache_create", "moe_cache_destroy", "cache_resolve",
     "moe_cache_trace", "moe_cache_clear_trace", "moe_cache_invalidate", "moe_cache_slot_of", "moe_cache_stats",
     "cache_fill_async", "moe_ffn_workspace_size", "moe_ffn", "moe_combine", "moe_pipe_create", "moe_pipe_destroy",
-    "moe_pipe_begin_layer", "moe_pipe_end_layer", "moe_pipe_copy_ms", "moe_decoder_create", "moe_decoder_destroy",
+    "moe_pipe_begin_layer", "moe_pipe_end_layer", "moe_pipe_copy_ms", "moe_clock_record", "moe_decoder_create", "moe_decoder_destroy",
     "moe_decoder_step", "moe_decoder_profile", "moe_decoder_ffn_stats", "moe_decoder_fills",
     "moe_cpu_ffn", "moe_cpu_threads", "moe_cache_set_split", "moe_decoder_cpu_runs",
     "moe_device_decoder_create", "moe_device_decoder_destroy", "moe_device_decoder_step", "moe_device_decoder_stats",
@@ -90,6 +90,7 @@ _sig("moe_pipe_destroy", I32, P)
 _sig("moe_pipe_begin_layer", I32, P, I32, P, ctypes.POINTER(ctypes.c_void_p))
 _sig("moe_pipe_end_layer", I32, P, I32, P)
 _sig("moe_pipe_copy_ms", I32, P, I32, ctypes.POINTER(ctypes.c_float))
+_sig("moe_clock_record", I32, P)
 _sig("moe_decoder_create", P, P, I32, I32, I32, I32, I32, I32, I32, P, SZ, P, SZ, ctypes.POINTER(DecoderBuffers), PI)
 _sig("moe_decoder_destroy", I32, P)
 _sig("moe_decoder_step", I32, P, I32, I32, P, I32, P, P, P, I32, P, PI)
@@ -341,6 +342,11 @@ def moe_pipe_copy_ms(pipe, layer):
     ms = ctypes.c_float(0)
     _check(_lib.moe_pipe_copy_ms(pipe.h, layer, ctypes.byref(ms)), "moe_pipe_copy_ms")
     return ms.value
+
+
+def moe_clock_record(sums):
+    """sums: a device tensor of two int64 (zeroed by the caller), or None to turn the record off."""
+    _check(_lib.moe_clock_record(_ptr(sums) if sums is not None else None), "moe_clock_record")
 
 
 # ---------------------------------------------------------------------------

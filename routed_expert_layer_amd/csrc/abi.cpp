@@ -547,6 +547,11 @@ int moe_pipe_end_layer(moe_pipe_t* p, int layer, void* compute_stream) {
   return MOE_OK;
 }
 
+int moe_clock_record(unsigned long long* sums) {
+  moe::set_clock_sums(sums);
+  return MOE_OK;
+}
+
 int moe_pipe_copy_ms(moe_pipe_t* p, int layer, float* ms) {
   if (!p || !ms || layer < 0 || layer >= p->next_copy) return fail(MOE_EINVAL, "moe_pipe_copy_ms: bad layer");
   hipError_t e = hipEventElapsedTime(ms, p->started[layer], p->copied[layer]);

@@ -40,6 +40,17 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t off
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
 }
 
+// Adds the shader-clock cycles and 100 MHz real-time ticks since (c0, r0) to
+// sums[0] and sums[1] (the clock diagnostic; one call per block).
+__device__ __forceinline__ void record_clock(unsigned long long* sums, unsigned long long c0, unsigned long long r0) {
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  atomicAdd(sums, c1 - c0);
+  atomicAdd(sums + 1, r1 - r0);
+}
+
+// Process-wide target of the clock diagnostic (nullptr: off).
+unsigned long long* g_clock_sums = nullptr;
+
 // The work list comes by value (WorkArgs) or from device memory (GemmTable);
 // both have the same fields.
 __device__ inline const WorkArgs& table_of(const WorkArgs& w) { return w; }
@@ -51,7 +62,9 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
                                                         const char* __restrict__ slot_base, size_t slot_stride,
                                                         size_t mat_off, int N, int K, int H, int I,
                                                         uint16_t* __restrict__ hout, float* __restrict__ yout,
-                                                        const float* __restrict__ bias) {
+                                                        const float* __restrict__ bias,
+                                                        unsigned long long* __restrict__ clock_sums) {
+  const unsigned long long c_start = __builtin_amdgcn_s_memtime(), r_start = __builtin_amdgcn_s_memrealtime();
   constexpr int BN_T = 16;
   constexpr int NS = BM_T == 16 ? 4 : 6;       // LDS stages of 32 K; NS - 1 in flight
   constexpr int WN = BM_T == 16 ? 8 : 4;       // weight fragment rows per wave
@@ -204,6 +217,7 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
     if (kt < KC) step(kt, f0, f1);
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));  // the clamped loads past the end have landed too
   }
+  if (clock_sums != nullptr && tid == 0) record_clock(clock_sums, c_start, r_start);
 
   // Epilogue.
 #pragma unroll
@@ -270,7 +284,9 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp4(const uint16_t* __restrict_
                                                       const GemmTable* __restrict__ tab,
                                                       const char* __restrict__ slot_base, size_t slot_stride,
                                                       size_t code_off, size_t scale_off, int N, int K, int I,
-                                                      int H, uint16_t* __restrict__ hout, float* __restrict__ yout) {
+                                                      int H, uint16_t* __restrict__ hout, float* __restrict__ yout,
+                                                      unsigned long long* __restrict__ clock_sums) {
+  const unsigned long long c_start = __builtin_amdgcn_s_memtime(), r_start = __builtin_amdgcn_s_memrealtime();
   constexpr int BN_T = 16, BM_T = 8, NS = 3, WN = 4, WM = 4, WAVES_N = 4, KSUB = 4;
   constexpr int CODE = BN_T * 1024, SCL = BN_T * 64, TOK = BM_T * KSUB * 1024;
   constexpr int STAGE = CODE + SCL + TOK;
@@ -379,6 +395,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp4(const uint16_t* __restrict_
       __builtin_amdgcn_s_setprio(0);
     }
   }
+  if (clock_sums != nullptr && threadIdx.x == 0) record_clock(clock_sums, c_start, r_start);
 
 #pragma unroll
   for (int j = 0; j < WM; ++j) {
@@ -471,6 +488,8 @@ hipError_t upload_table(const int4* item, const int* prefix, int n, int total, G
 
 bool gemm2_supported(int N, int K) { return N % 256 == 0 && K % 32 == 0; }
 
+void set_clock_sums(unsigned long long* sums) { g_clock_sums = sums; }
+
 // Both projections of every listed expert: groups of more than 256 rows with
 // 256-token tiles (8 waves of 128 x 64), the others with 128-token tiles
 // (8 waves of 64 x 64); one launch per tile size and projection, each with
@@ -502,19 +521,19 @@ hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const int
   if (tot[0][0] > 0)
     hipLaunchKernelGGL((gemm2_bf16<1, 16, const GemmTable*>), dim3(supertile_blocks(tot[0][0])), dim3(512), 0, s, xb,
                        perm_src, (const GemmTable*)tab[0][0], slot_base, slot_stride, L.p1, 2 * I, H, H, I, hb, y,
-                       nullptr);
+                       nullptr, g_clock_sums);
   if (tot[1][0] > 0)
     hipLaunchKernelGGL((gemm2_bf16<1, 8, const GemmTable*>), dim3(supertile_blocks(tot[1][0])), dim3(512), 0, s, xb,
                        perm_src, (const GemmTable*)tab[1][0], slot_base, slot_stride, L.p1, 2 * I, H, H, I, hb, y,
-                       nullptr);
+                       nullptr, g_clock_sums);
   if (tot[0][1] > 0)
     hipLaunchKernelGGL((gemm2_bf16<2, 16, const GemmTable*>), dim3(supertile_blocks(tot[0][1])), dim3(512), 0, s, hb,
                        perm_src, (const GemmTable*)tab[0][1], slot_base, slot_stride, L.p2, H, I, H, I, hb, y,
-                       nullptr);
+                       nullptr, g_clock_sums);
   if (tot[1][1] > 0)
     hipLaunchKernelGGL((gemm2_bf16<2, 8, const GemmTable*>), dim3(supertile_blocks(tot[1][1])), dim3(512), 0, s, hb,
                        perm_src, (const GemmTable*)tab[1][1], slot_base, slot_stride, L.p2, H, I, H, I, hb, y,
-                       nullptr);
+                       nullptr, g_clock_sums);
   return hipGetLastError();
 }
 
@@ -542,10 +561,11 @@ hipError_t launch_ffn_prefill_mxfp4(const void* x, const int32_t* perm_src, cons
   if (tot[0] > 0)
     hipLaunchKernelGGL(gemm_mxfp4<1>, dim3(supertile_blocks(tot[0])), dim3(512), 0, s,
                        static_cast<const uint16_t*>(x), perm_src, (const GemmTable*)tab[0], slot_base, slot_stride,
-                       L.p1, L.p1s, 2 * I, H, I, H, hb, y);
+                       L.p1, L.p1s, 2 * I, H, I, H, hb, y, g_clock_sums);
   if (tot[1] > 0)
     hipLaunchKernelGGL(gemm_mxfp4<2>, dim3(supertile_blocks(tot[1])), dim3(512), 0, s, hb, perm_src,
-                       (const GemmTable*)tab[1], slot_base, slot_stride, L.p2, L.p2s, H, I, I, H, hb, y);
+                       (const GemmTable*)tab[1], slot_base, slot_stride, L.p2, L.p2s, H, I, I, H, hb, y,
+                       g_clock_sums);
   return hipGetLastError();
 }
 
@@ -570,7 +590,7 @@ hipError_t launch_router_gemm2(const void* x, const void* wrt, int T, int H, int
   if (wa.total_tiles == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm2_bf16<0, 8, WorkArgs>), dim3(supertile_blocks(wa.total_tiles)), dim3(512), 0, s,
                      static_cast<const uint16_t*>(x), nullptr, wa, static_cast<const char*>(wrt), 0, 0, E, H / nsplit,
-                     H, 0, nullptr, partial, nullptr);
+                     H, 0, nullptr, partial, nullptr, nullptr);
   return hipGetLastError();
 }
 

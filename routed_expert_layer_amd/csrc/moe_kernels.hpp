@@ -138,6 +138,11 @@ hipError_t launch_router_gemm(const void* x, const void* wrt, int T, int H, int 
                               hipStream_t s);
 // Large-tile GEMM (256 weight rows per block) used when N % 256 == 0.
 bool gemm2_supported(int N, int K);
+// Clock diagnostic: while `sums` (device, two uint64) is set, every block of
+// the prefill expert GEMMs adds the shader-clock cycles and 100 MHz real-time
+// ticks it spent up to its epilogue to sums[0] and sums[1]; nullptr turns it
+// off. Process-wide, read at each launch.
+void set_clock_sums(unsigned long long* sums);
 // Both projections of n work items {slot, row_begin, rows, expert} (host
 // array, rows > 0, n <= kTableItems) with four GemmTables at `tables`
 // (4 * kTableBytes of device memory, stream-ordered reuse).

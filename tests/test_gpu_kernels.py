@@ -179,6 +179,50 @@ def test_ffn_parity(L, name, wfmt, H, I, rows, mode):
         check_close(yg[a:b], ref, f"{name} expert {e}")
 
 
+@pytest.mark.parametrize("wfmt", ["bf16", "mxfp4"])
+def test_clock_record_leaves_prefill_unchanged(L, wfmt):
+    # the clock diagnostic only adds counters: the GEMM output is bit-identical with it on, the counters
+    # give a plausible shader clock, and once it is off they stay as they are
+    print(f"clock record case: {wfmt}", flush=True)
+    H, I, rows = 512, 256, [130, 0, 300, 17]
+    E = len(rows)
+    cfg = cfg_like("tiny_f32_h256_e16", name=f"clk_{wfmt}", H=H, I=I, E=E, act="bf16", wfmt=wfmt)
+    T = max(rows)
+    x = gen.tokens(cfg, 0, 0, dev, T=T)
+    r = np.random.default_rng(7)
+    perm_src = torch.from_numpy(np.concatenate([r.integers(0, T, size=n) for n in rows]).astype(np.int32)).to(dev)
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    wf = L.MOE_W_MXFP4 if wfmt == "mxfp4" else L.MOE_W_BF16
+    stride = (L.moe_expert_bytes(wf, H, I) + 4095) // 4096 * 4096
+    slots = torch.zeros(E * stride, dtype=torch.uint8, device=dev)
+    for e, w in enumerate(_experts(cfg, E, wfmt)):
+        if wfmt == "mxfp4":
+            L.moe_pack_expert(wf, H, I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"], w["s2"], slots[e * stride:])
+        else:
+            L.moe_pack_expert(wf, H, I, w[0], w[1], w[2], None, None, None, slots[e * stride:])
+    work = np.array([[e, e, off[e], rows[e]] for e in range(E)], dtype=np.int32)
+    n = int(off[-1])
+    ws = torch.empty(L.moe_ffn_workspace_size(n, H, I, wf), dtype=torch.uint8, device=dev)
+    ys = []
+    sums = torch.zeros(2, dtype=torch.int64, device=dev)
+    for record in (False, True, False):
+        y = torch.full((n, H), float("nan"), dtype=torch.float32, device=dev)
+        L.moe_clock_record(sums if record else None)
+        try:
+            L.moe_ffn(x, perm_src, work, slots, stride, wf, H, I, y, ws, L.MOE_FFN_PREFILL)
+            torch.cuda.synchronize()
+        finally:
+            L.moe_clock_record(None)
+        ys.append(y)
+        if record:
+            cyc, ticks = (int(v) for v in sums.cpu())
+            assert cyc > 0 and ticks > 0
+            assert 0.3 < cyc / ticks / 10.0 < 3.5, (cyc, ticks)
+            after_on = (cyc, ticks)
+    assert tuple(int(v) for v in sums.cpu()) == after_on
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+
+
 def test_ffn_zero_work_is_noop(L):
     y = torch.zeros((4, 256), dtype=torch.float32, device=dev)
     ws = torch.empty(1024, dtype=torch.uint8, device=dev)
