@@ -515,6 +515,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the int4 8-layer and 48-layer decode sections")
     ap.add_argument("--no-variants", action="store_true",
                     help="one-layer decode without its CPU-split and device-controlled variants (counter runs)")
+    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 prefill sections")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -574,11 +575,13 @@ def main():
     out["decode"] = rnd(res["decode"])
     if not args.no_prefill:
         out["prefill"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_bf16_t4096_e256"]))
-        out["prefill_mxfp4"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_mxfp4_t4096_e256"]))
+        if not args.no_mxfp4:
+            out["prefill_mxfp4"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_mxfp4_t4096_e256"]))
         out["prefill_double_buffered"] = rnd(bench_prefill_pipeline(args, torch, L, gen,
                                                                     CONFIGS["prefill_db_bf16_t16384_l8"]))
-        out["prefill_double_buffered_mxfp4"] = rnd(bench_prefill_pipeline(args, torch, L, gen,
-                                                                          CONFIGS["prefill_db_mxfp4_t16384_l8"]))
+        if not args.no_mxfp4:
+            out["prefill_double_buffered_mxfp4"] = rnd(bench_prefill_pipeline(args, torch, L, gen,
+                                                                              CONFIGS["prefill_db_mxfp4_t16384_l8"]))
     if not args.no_extra:
         out["decode_int4"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["decode_int4_t8_l8"], 64, 128))
         out["decode_mxfp4"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["decode_mxfp4_t8_l8"], 64, 128))

@@ -182,29 +182,40 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   // kt + 1's, so LDS latency hides behind matrix-core work; after the step's
   // barrier (every wave's loads of stage kt + 1 have landed and every wave
   // has finished reading stage kt) stage kt's buffer is refilled with stage
-  // kt + NS. Stage numbers past the last are clamped to it (valid addresses,
-  // results unused), so each step is one basic block for any K and the
-  // compiler can interleave the reads with the matrix-core instructions.
+  // kt + NS. The read past the last stage repeats the last one (results
+  // unused), so the reads and the matrix-core instructions of a step form
+  // one basic block for any K and the compiler can interleave them.
   auto step = [&](int kt, Frags& cur, Frags& nxt) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 2)));  // this wave's loads of stage kt + 1 landed
-    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));              // and its reads of stage kt completed
+    // this wave's loads of stage kt + 1 landed: at most the stages kt + 2 ..
+    // kt + NS - 1 still in flight, or, near the end where fewer were issued,
+    // none
+    if (kt + NS - 1 < KC) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 2)));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    }
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));  // and its reads of stage kt completed
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    issue(min(kt + NS, KC - 1), kt % NS);
+    if (kt + NS < KC) issue(kt + NS, kt % NS);
     read_stage(min(kt + 1, KC - 1), nxt);
-    __builtin_amdgcn_s_setprio(1);
     compute(cur);
-    // one LDS read, then a share of the matrix-core instructions, in turn
+    // one LDS read, then a share of the matrix-core instructions, in turn (no
+    // priority changes in between: they would fence the scheduler)
 #pragma unroll
     for (int q = 0; q < WN + WM; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, (WN * WM) / (WN + WM), 0);
     }
-    __builtin_amdgcn_s_setprio(0);
   };
   {
-    for (int s0 = 0; s0 < NS; ++s0) issue(min(s0, KC - 1), s0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 1)));  // stage 0 landed
+    for (int s0 = 0; s0 < NS && s0 < KC; ++s0) issue(s0, s0);
+    // stage 0 landed
+    if (KC >= NS) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 1)));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    }
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     Frags f0, f1;
@@ -215,7 +226,6 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
       step(kt + 1, f1, f0);
     }
     if (kt < KC) step(kt, f0, f1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));  // the clamped loads past the end have landed too
   }
   if (clock_sums != nullptr && tid == 0) record_clock(clock_sums, c_start, r_start);
 
