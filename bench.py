@@ -456,9 +456,28 @@ def bench_decode_layers(args, torch, L, gen, cfg, warm, steps):
                         fills_timed=dl.n_fills - f0, cpu_runs_timed=dl.cpu_runs - c0,
                         split_rates_mbs=rates)
 
+        def epochs():
+            # the whole workload from a cold cache, every miss filled: the miss rate of each epoch (the router
+            # bias is re-drawn at every epoch start) and the end-to-end rate, fills included
+            dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for st in range(cfg.steps):
+                for l in range(cfg.L):
+                    dl.step(st, l, xs[st][l] if st < n else gen.tokens(cfg, st, l, dev), Wrs[l], b(l, st), s)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            tr = dl.trace()
+            ep = tr[:, 0] // cfg.epoch
+            return dict(steps=cfg.steps, epoch_steps=cfg.epoch, tokens_per_s=cfg.steps * cfg.T / el,
+                        fills=int(dl.n_fills), fill_gb=dl.n_fills * store.blob / 1e9,
+                        miss_rate_per_epoch=[float(1.0 - tr[ep == e, 3].mean()) for e in range(int(ep.max()) + 1)])
+
         res = dict(workload=cfg.name, layers=cfg.L, tokens_per_step=cfg.T, steps_timed=steps, steps_warmup=warm,
                    weight_sets=store.P)
         res.update(run(False))
+        if cfg.epoch:
+            res["epochs"] = epochs()
         res["device_control"] = bench_device(torch, cfg, store, Wrs, warm, steps, lambda st, l: xs[st][l], b)
         if cfg.wfmt == "bf16" and cfg.act == "bf16":
             # the pages' adaptive misses: the share rate_fill / (rate_fill + rate_cpu) of misses is filled,
