@@ -101,6 +101,11 @@ def measured_traffic(root):
         return None
 
 
+def section(name):
+    """One progress line per bench section (stderr), so a long run shows where it is."""
+    print(f"[bench] {name}", file=sys.stderr, flush=True)
+
+
 def percentile(xs, p):
     xs = sorted(xs)
     if not xs:
@@ -534,7 +539,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the int4 8-layer and 48-layer decode sections")
     ap.add_argument("--no-variants", action="store_true",
                     help="one-layer decode without its CPU-split and device-controlled variants (counter runs)")
-    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 prefill sections")
+    ap.add_argument("--no-mxfp4", action="store_true", help="skip the MXFP4 prefill and decode sections")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 48-layer decode section")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -561,6 +567,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    section("decode")
     res = bench_decode(args, torch, L, gen, cfg)
     ffn = res["ffn"]
     achieved = ffn["bytes"] / (ffn["ms"] * 1e-3) / 1e9 if ffn["ms"] > 0 else 0.0
@@ -593,20 +600,31 @@ def main():
 
     out["decode"] = rnd(res["decode"])
     if not args.no_prefill:
+        section("prefill")
         out["prefill"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_bf16_t4096_e256"]))
         if not args.no_mxfp4:
+            section("prefill_mxfp4")
             out["prefill_mxfp4"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_mxfp4_t4096_e256"]))
+        section("prefill_double_buffered")
         out["prefill_double_buffered"] = rnd(bench_prefill_pipeline(args, torch, L, gen,
                                                                     CONFIGS["prefill_db_bf16_t16384_l8"]))
         if not args.no_mxfp4:
+            section("prefill_double_buffered_mxfp4")
             out["prefill_double_buffered_mxfp4"] = rnd(bench_prefill_pipeline(args, torch, L, gen,
                                                                               CONFIGS["prefill_db_mxfp4_t16384_l8"]))
     if not args.no_extra:
+        section("decode_int4")
         out["decode_int4"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["decode_int4_t8_l8"], 64, 128))
-        out["decode_mxfp4"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["decode_mxfp4_t8_l8"], 64, 128))
-        out["decode_stack48"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["stack48_bf16_h2048_e128"],
-                                                        32, 64))
+        if not args.no_mxfp4:
+            section("decode_mxfp4")
+            out["decode_mxfp4"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["decode_mxfp4_t8_l8"], 64,
+                                                          128))
+        if not args.no_stack:
+            section("decode_stack48")
+            out["decode_stack48"] = rnd(bench_decode_layers(args, torch, L, gen, CONFIGS["stack48_bf16_h2048_e128"],
+                                                            32, 64))
     if not args.no_cpu_baseline:
+        section("cpu_baseline")
         cb = cpu_baseline(args, torch, gen, cfg)
         cb["value"] = round(cb["value"], 4)
         out["cpu_baseline"] = cb

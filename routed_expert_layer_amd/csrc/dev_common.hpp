@@ -46,18 +46,35 @@ __device__ __forceinline__ f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                 0, 0);
 }
 
+// (x & m) | c in one instruction (the compiler emits an and and an or). At
+// most one scalar operand per vector instruction: the mask comes from a
+// scalar register, the constant from a vector register.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
+
 // Eight int4 codes (nibble order k0,k2,k4,k6,k1,k3,k5,k7, stored as q+8) to
-// eight fp16 values in k order: 1024 + nibble is exact in fp16 (0x6400 | n),
-// and subtracting 1032 leaves q exactly.
+// eight fp16 values in k order. A nibble n placed in the low mantissa bits of
+// 1024 (0x6400 | n) is 1024 + n exactly, and 1024 + n - 1032 = q. A nibble
+// left four bits up (0x6400 | n << 4) is 1024 + 16 n, and (1024 + 16 n) / 16
+// - 72 = q, one fused multiply-add whose exact result needs no rounding; so
+// of the four nibble pairs of a word only the upper two need a shift (one,
+// shared), and each pair costs one and-or and one packed fp16 operation.
 __device__ __forceinline__ u32x4_t int4x8_to_f16x8(uint32_t w) {
+  const uint32_t magic = 0x64006400u;
   const f16x2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const f16x2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t hi = w >> 8;
   u32x4_t r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint32_t v = ((w >> (4 * p)) & 0x000F000Fu) | 0x64006400u;
-    f16x2_t h = __builtin_bit_cast(f16x2_t, v) - off;
-    r[p] = __builtin_bit_cast(uint32_t, h);
-  }
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, and_or(w, 0x000F000Fu, magic)) - off);
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, and_or(w, 0x00F000F0u, magic)),
+                                                                sixteenth, off16));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, and_or(hi, 0x000F000Fu, magic)) - off);
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, and_or(hi, 0x00F000F0u, magic)),
+                                                                sixteenth, off16));
   return r;
 }
 
