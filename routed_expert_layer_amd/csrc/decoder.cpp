@@ -7,6 +7,7 @@
 // component table's "PCIe link" row: only the missing experts move.
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -44,6 +45,7 @@ struct moe_decoder {
   int32_t* counts_dev = nullptr;   // the same memory as seen by kernels
   hipStream_t fill = nullptr;
   hipEvent_t ev_counts = nullptr;
+  int32_t route_seq = 0;  // number of the last routing launch (published by the kernel after the counts)
   std::vector<int32_t> experts, work_e, work_slot, work_wave;
   std::vector<moe_miss_t> misses, wave_misses;
   std::vector<moe_work_t> work;
@@ -118,8 +120,10 @@ moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, i
   d->slot_base = slot_base; d->slot_stride = slot_stride;
   d->b = b;
   // fine-grained (coherent) pinned memory that the routing kernels write directly
-  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&d->counts_host), sizeof(int32_t) * E,
+  // E counts and the routing kernel's completion number after them
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&d->counts_host), sizeof(int32_t) * (E + 1),
                                hipHostMallocMapped | hipHostMallocCoherent);
+  if (e == hipSuccess) d->counts_host[E] = 0;
   if (e == hipSuccess) e = hipHostGetDevicePointer(reinterpret_cast<void**>(&d->counts_dev), d->counts_host, 0);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&d->fill, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&d->ev_counts, hipEventDisableTiming);
@@ -170,9 +174,10 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   const moe_decoder_buffers_t& b = d->b;
   // routing; the kernels also store the per-expert counts straight into the
   // host-mapped pinned buffer: the one device -> host transfer of the step
+  const int32_t seq = d->route_seq = d->route_seq == INT32_MAX ? 1 : d->route_seq + 1;
   hipError_t e = moe::launch_route(x, d->dtype == MOE_DT_BF16, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w,
                                    b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s,
-                                   d->counts_dev);
+                                   d->counts_dev, seq);
   const bool split = moe_cache_splits(d->cache);
   if (split && e == hipSuccess) {
     // misses may run on the CPU: it needs this step's activations and token order
@@ -196,7 +201,21 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   if (e == hipSuccess) e = hipEventRecord(d->ev_counts, s);
   if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: routing: %s", hipGetErrorString(e));
   int rc;
-  while ((e = hipEventQuery(d->ev_counts)) == hipErrorNotReady) {
+  if (!split) {
+    // the counts are complete once the routing kernel has published this step's number after them (decode
+    // batches); other routing paths publish none and end the wait through the event
+    for (unsigned spin = 1;; ++spin) {
+      if (__atomic_load_n(d->counts_host + d->E, __ATOMIC_ACQUIRE) == seq) break;
+      if ((spin & 255u) == 0) {
+        e = hipEventQuery(d->ev_counts);
+        if (e != hipErrorNotReady) break;
+        e = hipSuccess;
+      }
+    }
+  } else {
+    // with misses on the CPU the host also needs the activations and token order copied after the routing
+    while ((e = hipEventQuery(d->ev_counts)) == hipErrorNotReady) {
+    }
   }
   if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: counts wait: %s", hipGetErrorString(e));
   d->experts.clear();

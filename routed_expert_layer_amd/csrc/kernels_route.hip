@@ -377,7 +377,7 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm_src,
                                                            int32_t* __restrict__ perm_pos,
-                                                           int32_t* __restrict__ counts_mirror) {
+                                                           int32_t* __restrict__ counts_mirror, int32_t mirror_seq) {
   __shared__ float lg[kSmallT * kSmallE];
   __shared__ int32_t sidx[kSmallT * 16];
   __shared__ unsigned long long bm[kSmallE];
@@ -477,6 +477,13 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
     perm_pos[tid] = pos;
     perm_src[pos] = t;
   }
+  if (counts_mirror) {
+    // the host may read the mirror as soon as it sees this step's number after
+    // it: every thread's mirror write is made visible system-wide first
+    __threadfence_system();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(counts_mirror + E, mirror_seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
 }
 
 struct RoutePlan {
@@ -531,7 +538,8 @@ size_t route_workspace_bytes(int T, int H, int E, int k) {
 
 hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
-                        int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s, int32_t* counts_mirror) {
+                        int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s, int32_t* counts_mirror,
+                        int32_t mirror_seq) {
   const RoutePlan p = plan_route(T, H, E, bf16);
   char* w = static_cast<char*>(ws);
   float* partial = reinterpret_cast<float*>(w);
@@ -547,7 +555,7 @@ hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* b
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     hipLaunchKernelGGL(route_finish_small, dim3(1), dim3(1024), 0, s, partial, T > 0 ? p.nsplit : 0, bias, T, E, k,
-                       topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos, counts_mirror);
+                       topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos, counts_mirror, mirror_seq);
     return hipGetLastError();
   }
   if (p.mode == 1) {

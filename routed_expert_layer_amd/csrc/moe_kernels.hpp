@@ -101,7 +101,9 @@ size_t route_workspace_bytes(int T, int H, int E, int k);
 hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
                         int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s,
-                        int32_t* counts_mirror = nullptr);  // optional host-mapped copy of counts
+                        // optional host-mapped copy of counts, E + 1 int32: for batches of at most 16 tokens and
+                        // 512 experts, mirror[E] receives mirror_seq once the E counts before it are visible
+                        int32_t* counts_mirror = nullptr, int32_t mirror_seq = 0);
 
 hipError_t launch_pack(int wfmt, int H, int I, const void* W1, const void* W3, const void* W2,
                        const void* s1, const void* s3, const void* s2, void* blob, hipStream_t s);
