@@ -277,7 +277,6 @@ __device__ __forceinline__ void int4_decode_tiles(const uint16_t* __restrict__ a
     f32x4_t acc[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
     for (int g = g0; g < g1; ++g) {
       u32x4_t b[4];
 #pragma unroll
@@ -408,7 +407,6 @@ __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, i
     f32x4_t acc[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
     for (int g = g0; g < g1; ++g) {
       u32x4_t b[4];
 #pragma unroll
