@@ -73,12 +73,18 @@ def _definition(src, signature):
 
 def decode_ffn_digest(root):
     """sha256 over the source text the decode expert-FFN kernels are built from: both kernels, their
-    wave loop, launchers, the work sources, the device helpers and the work-list / blob-layout definitions."""
+    wave loop, launchers, the work sources, the device helpers they call and the work-list / blob-layout
+    definitions."""
     import hashlib
     csrc = os.path.join(root, "routed_expert_layer_amd", "csrc")
     ffn = open(os.path.join(csrc, "kernels_ffn.hip")).read()
     hdr = open(os.path.join(csrc, "moe_kernels.hpp")).read()
-    parts = [open(os.path.join(csrc, "dev_common.hpp")).read(),
+    dev = open(os.path.join(csrc, "dev_common.hpp")).read()
+    # the device helpers those kernels use: vector types, bf16 rounding, SiLU, loads, the bf16 product
+    helpers = [line for line in dev.splitlines() if line.startswith("typedef")]
+    helpers += [_definition(dev, sig) for sig in ("uint16_t f32_to_bf16(", "float silu(", "u32x4_t ld16(",
+                                                  "u32x4_t ld16_nt(", "f32x4_t mfma_bf16(")]
+    parts = ["\n".join(helpers),
              _definition(ffn, "__global__ __launch_bounds__(256) void ffn1_decode_bf16("),
              _definition(ffn, "__global__ __launch_bounds__(256) void ffn2_decode_bf16("),
              _definition(ffn, "hipError_t launch_ffn_decode("),
