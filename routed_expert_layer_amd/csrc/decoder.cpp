@@ -42,10 +42,11 @@ struct moe_decoder {
   size_t slot_stride;
   moe_decoder_buffers_t b;
   int32_t* counts_host = nullptr;  // pinned, host address
+  std::vector<int32_t> counts;     // this step's counts, read from counts_host
   int32_t* counts_dev = nullptr;   // the same memory as seen by kernels
   hipStream_t fill = nullptr;
   hipEvent_t ev_counts = nullptr;
-  int32_t route_seq = 0;  // number of the last routing launch (published by the kernel after the counts)
+  int32_t route_seq = 0;  // number of the last routing launch (1..65535, carried by each count word)
   std::vector<int32_t> experts, work_e, work_slot, work_wave;
   std::vector<moe_miss_t> misses, wave_misses;
   std::vector<moe_work_t> work;
@@ -120,10 +121,10 @@ moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, i
   d->slot_base = slot_base; d->slot_stride = slot_stride;
   d->b = b;
   // fine-grained (coherent) pinned memory that the routing kernels write directly
-  // E counts and the routing kernel's completion number after them
-  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&d->counts_host), sizeof(int32_t) * (E + 1),
+  hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&d->counts_host), sizeof(int32_t) * E,
                                hipHostMallocMapped | hipHostMallocCoherent);
-  if (e == hipSuccess) d->counts_host[E] = 0;
+  if (e == hipSuccess) std::memset(d->counts_host, 0, sizeof(int32_t) * E);
+  d->counts.assign(E, 0);
   if (e == hipSuccess) e = hipHostGetDevicePointer(reinterpret_cast<void**>(&d->counts_dev), d->counts_host, 0);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&d->fill, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&d->ev_counts, hipEventDisableTiming);
@@ -174,7 +175,8 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   const moe_decoder_buffers_t& b = d->b;
   // routing; the kernels also store the per-expert counts straight into the
   // host-mapped pinned buffer: the one device -> host transfer of the step
-  const int32_t seq = d->route_seq = d->route_seq == INT32_MAX ? 1 : d->route_seq + 1;
+  const int32_t seq = d->route_seq = d->route_seq >= 65535 ? 1 : d->route_seq + 1;
+  const bool tagged = moe::route_small_path(T, d->E);
   hipError_t e = moe::launch_route(x, d->dtype == MOE_DT_BF16, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w,
                                    b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s,
                                    d->counts_dev, seq);
@@ -201,29 +203,39 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   if (e == hipSuccess) e = hipEventRecord(d->ev_counts, s);
   if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: routing: %s", hipGetErrorString(e));
   int rc;
-  if (!split) {
-    // the counts are complete once the routing kernel has published this step's number after them (decode
-    // batches); other routing paths publish none and end the wait through the event
+  if (tagged && !split) {
+    // decode batches: every count word carries this step's number, so the counts are complete once all of
+    // them show it (the event is polled too, so a failed launch still ends the wait)
     for (unsigned spin = 1;; ++spin) {
-      if (__atomic_load_n(d->counts_host + d->E, __ATOMIC_ACQUIRE) == seq) break;
-      if ((spin & 255u) == 0) {
+      int e_ok = 0;
+      for (int i = 0; i < d->E; ++i)
+        e_ok += ((uint32_t)__atomic_load_n(d->counts_host + i, __ATOMIC_ACQUIRE) >> 16) == (uint32_t)seq;
+      if (e_ok == d->E) break;
+      if ((spin & 63u) == 0) {
         e = hipEventQuery(d->ev_counts);
         if (e != hipErrorNotReady) break;
         e = hipSuccess;
       }
     }
   } else {
-    // with misses on the CPU the host also needs the activations and token order copied after the routing
+    // larger batches, or misses on the CPU, which also need the activations and token order copied after
+    // the routing: the event
     while ((e = hipEventQuery(d->ev_counts)) == hipErrorNotReady) {
     }
   }
   if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: counts wait: %s", hipGetErrorString(e));
+  for (int i = 0; i < d->E; ++i) {
+    const uint32_t w = (uint32_t)__atomic_load_n(d->counts_host + i, __ATOMIC_ACQUIRE);
+    if (tagged && (w >> 16) != (uint32_t)seq)
+      return dfail(MOE_EHIP, "moe_decoder_step: routing counts of step %d missing for expert %d", step, i);
+    d->counts[i] = tagged ? (int32_t)(w & 0xFFFFu) : (int32_t)w;
+  }
   d->experts.clear();
   int run = 0;
   for (int i = 0; i < d->E; ++i) {
     d->offs[i] = run;
-    run += d->counts_host[i];
-    if (d->counts_host[i] > 0) d->experts.push_back(i);
+    run += d->counts[i];
+    if (d->counts[i] > 0) d->experts.push_back(i);
   }
   d->offs[d->E] = run;
   const int n = (int)d->experts.size();
@@ -272,8 +284,8 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
         ++pos;
         if (!take) continue;
         const int ex = d->work_e[i];
-        d->work.push_back(moe_work_t{ex, d->work_slot[i], d->offs[ex], d->counts_host[ex]});
-        rows += d->counts_host[ex];
+        d->work.push_back(moe_work_t{ex, d->work_slot[i], d->offs[ex], d->counts[ex]});
+        rows += d->counts[ex];
       }
       if (d->work.empty()) continue;
       // profiled calls: the FFN of a whole layer-step whose experts were all resident
@@ -297,7 +309,7 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   // rest; their rows of y_perm follow on the compute stream before the combine
   for (int i = 0; i < n; ++i) {
     if (d->work_slot[i] >= 0) continue;
-    const int ex = d->work_e[i], rows = d->counts_host[ex], r0 = d->offs[ex];
+    const int ex = d->work_e[i], rows = d->counts[ex], r0 = d->offs[ex];
     for (int r = 0; r < rows; ++r)
       std::memcpy(d->xg.data() + (size_t)r * d->H, d->x_host + (size_t)d->perm_host[r0 + r] * d->H,
                   sizeof(uint16_t) * d->H);

@@ -466,7 +466,9 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
     counts[tid] = c;
     offsets[tid] = excl;
     soff[tid] = excl;
-    if (counts_mirror) counts_mirror[tid] = c;
+    // the host-mapped copy carries this launch's number in its upper half, so
+    // each word shows by itself that it is current (no fence or flag needed)
+    if (counts_mirror) counts_mirror[tid] = (int32_t)(((uint32_t)mirror_seq << 16) | (uint32_t)c);
   }
   if (tid == 0) offsets[E] = T * k;
   __syncthreads();
@@ -476,13 +478,6 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
     const int pos = soff[e] + __popcll(bm[e] & ((1ull << t) - 1ull));
     perm_pos[tid] = pos;
     perm_src[pos] = t;
-  }
-  if (counts_mirror) {
-    // the host may read the mirror as soon as it sees this step's number after
-    // it: every thread's mirror write is made visible system-wide first
-    __threadfence_system();
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(counts_mirror + E, mirror_seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
@@ -528,6 +523,8 @@ RoutePlan plan_route(int T, int H, int E, bool bf16) {
 }
 
 }  // namespace
+
+bool route_small_path(int T, int E) { return T <= kSmallT && E <= kSmallE; }
 
 size_t route_workspace_bytes(int T, int H, int E, int k) {
   (void)k;

@@ -101,9 +101,12 @@ size_t route_workspace_bytes(int T, int H, int E, int k);
 hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
                         int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s,
-                        // optional host-mapped copy of counts, E + 1 int32: for batches of at most 16 tokens and
-                        // 512 experts, mirror[E] receives mirror_seq once the E counts before it are visible
+                        // optional host-mapped copy of counts: for batches of at most 16 tokens and 512 experts
+                        // (route_small_path) each word is (mirror_seq << 16) | count, mirror_seq in 1..65535;
+                        // for other batches plain counts
                         int32_t* counts_mirror = nullptr, int32_t mirror_seq = 0);
+// Whether launch_route takes the decode-size path (and tags its counts mirror).
+bool route_small_path(int T, int E);
 
 hipError_t launch_pack(int wfmt, int H, int I, const void* W1, const void* W3, const void* W2,
                        const void* s1, const void* s3, const void* s2, void* blob, hipStream_t s);
