@@ -553,7 +553,7 @@ def main():
                     help="first run a plain device-to-device copy of this many MiB (hardware-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the layer runs on a single MI355X and this build has no "
+        print("bench.py measures one GPU only: the layer runs on a single MI355X and the library has no "
               "multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
