@@ -307,6 +307,24 @@ class ClockRecord:
         return cyc / ticks / 10.0 if ticks > 0 else None
 
 
+GROUP_BINS = [1, 2, 17, 65, 129, 257, 1025, 4097, 1 << 31]  # rows per active expert: 1, 2-16, 17-64, ...
+
+
+def group_stats(counts):
+    """Tokens per active expert of a layer (or several): percentiles and a coarse histogram."""
+    import numpy as np
+    c = np.asarray(counts).reshape(-1)
+    c = c[c > 0]
+    if c.size == 0:
+        return dict(active=0)
+    hist = np.histogram(c, bins=GROUP_BINS)[0]
+    labels = [f"{a}" if b == a + 1 else f"{a}-{b - 1}" if b < (1 << 31) else f">={a}"
+              for a, b in zip(GROUP_BINS[:-1], GROUP_BINS[1:])]
+    return dict(active=int(c.size), min=int(c.min()), p10=float(np.percentile(c, 10)),
+                p50=float(np.percentile(c, 50)), p90=float(np.percentile(c, 90)), max=int(c.max()),
+                histogram={lab: int(n) for lab, n in zip(labels, hist) if n})
+
+
 def at_clock(tfs, ghz):
     """Share of the matrix-core peak scaled to the measured clock."""
     return tfs / (MFMA_BF16_PEAK_TFS * ghz / PEAK_CLOCK_GHZ) if ghz else None
@@ -351,7 +369,8 @@ def bench_prefill(args, torch, L, gen, cfg, reps=5):
                 mfma_frac=tfs / MFMA_BF16_PEAK_TFS, gemm_clock_ghz=clk.ghz(), mfma_frac_at_clock=at_clock(tfs, clk.ghz()),
                 weight_gbs=wbytes / (ms / n * 1e-3) / 1e9,
                 hbm_frac=wbytes / (ms / n * 1e-3) / 1e9 / HBM_PEAK_GBS, active_experts=active,
-                group_min=int(pl.last_counts[pl.last_counts > 0].min()), group_max=int(pl.last_counts.max()))
+                group_min=int(pl.last_counts[pl.last_counts > 0].min()), group_max=int(pl.last_counts.max()),
+                tokens_per_expert=group_stats(pl.last_counts))
 
 
 def bench_prefill_pipeline(args, torch, L, gen, cfg):
@@ -378,6 +397,7 @@ def bench_prefill_pipeline(args, torch, L, gen, cfg):
             timer.enabled = rep == 1
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cfg.L)]
             groups = []
+            layer_counts = []
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             if rep == 1:
@@ -389,6 +409,7 @@ def bench_prefill_pipeline(args, torch, L, gen, cfg):
                 ev[l][1].record(s)
                 L.moe_pipe_end_layer(pipe, l, s)
                 groups.append((int((pl.last_counts > 0).sum()), int(pl.last_counts.max())))
+                layer_counts.append(pl.last_counts.copy())
             torch.cuda.synchronize()
             if rep == 1:
                 clk.__exit__()
@@ -408,6 +429,7 @@ def bench_prefill_pipeline(args, torch, L, gen, cfg):
                     wall_ms=wall, compute_hidden_frac=1.0 - min(1.0, exposed / max(sum(comp_ms), 1e-9)),
                     prefill_tokens_per_s=cfg.L * cfg.T / (wall * 1e-3) / cfg.L,
                     active_experts=[g[0] for g in groups], max_group=[g[1] for g in groups],
+                    tokens_per_expert=group_stats(layer_counts),
                     weight_sets=store.P)
     finally:
         store.close()
