@@ -521,6 +521,15 @@ def bench_decode_layers(args, torch, L, gen, cfg, warm, steps):
         store.close()
 
 
+def blas_threads(torch):
+    """Threads the oracle's numpy BLAS uses."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        return torch.get_num_threads()
+
+
 def cpu_baseline(args, torch, gen, cfg):
     """The oracle, as it stands, on a bounded sample of decode steps (host cores)."""
     import numpy as np
@@ -547,14 +556,80 @@ def cpu_baseline(args, torch, gen, cfg):
         step += 1
         if len(store) > 24:
             store.clear()
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        cores = torch.get_num_threads()
-    return dict(value=steps * cfg.T / spent, unit="tokens/s", cores=cores, kind="oracle",
+    return dict(value=steps * cfg.T / spent, unit="tokens/s", cores=blas_threads(torch), kind="oracle",
                 sample=f"{steps} decode steps (1 token each) of {cfg.name}, numpy fp64, "
                        f"{spent:.1f} s of oracle time; expert weights converted from bf16 inside the oracle")
+
+
+def cpu_baselines_all(args, torch, gen):
+    """The oracle, as it stands, per unit of the other workloads (host cores): per layer-step of the 48-layer
+    stack and of the int4 8-layer decode (bounded samples), and per prefill layer of the 4096-token chunk and
+    of one 16384-token layer. Routing and weight generation before each timed call are untimed input
+    preparation; the oracle's own dequantisation and conversions are timed."""
+    import numpy as np
+    import oracle
+    from workloads import CONFIGS
+    out = {}
+
+    def host_bf16(t):
+        return t.cpu()
+
+    def layer_step_rate(cfg, int4):
+        Wrs, spent, n = {}, 0.0, 0
+        for i in range(4096):
+            st, layer = (i * 37) % cfg.steps, (i * 5) % cfg.L
+            if layer not in Wrs:
+                Wrs[layer] = gen.router_weight(cfg, layer, "cuda").cpu()
+            x = gen.tokens(cfg, st, layer, "cuda").cpu()
+            b = gen.router_bias(cfg, layer, st, "cpu")
+            idx = oracle.topk_select(oracle.router_logits(x, Wrs[layer], b), cfg.k)
+            raw = {}
+            for e in np.unique(idx):
+                if int4:
+                    w = gen.expert_int4(cfg, layer, int(e), "cuda")
+                    raw[int(e)] = {k_: v.cpu() for k_, v in w.items()}
+                else:
+                    raw[int(e)] = tuple(host_bf16(t) for t in gen.expert_weights(cfg, layer, int(e), "cuda"))
+
+            def get_expert(e):
+                if int4:
+                    w = raw[int(e)]
+                    return (oracle.dequant_int4(w["q1"], w["s1"], cfg.group), oracle.dequant_int4(w["q3"], w["s3"], cfg.group),
+                            oracle.dequant_int4(w["q2"], w["s2"], cfg.group))
+                return raw[int(e)]
+            t0 = time.perf_counter()
+            oracle.moe_layer(x, Wrs[layer], b, cfg.k, get_expert)
+            spent += time.perf_counter() - t0
+            n += 1
+            if spent >= args.cpu_seconds:
+                break
+        per = spent / n
+        return dict(value=cfg.T / (per * cfg.L), unit="tokens/s", cores=blas_threads(torch), kind="oracle",
+                    sample=f"{n} layer-steps of {cfg.name} ({cfg.T} tokens, {cfg.L} layers per token step), "
+                           f"{spent:.1f} s of oracle time, {per * 1e3:.1f} ms per layer-step")
+
+    def prefill_rate(cfg):
+        Wr = gen.router_weight(cfg, 0, "cuda").cpu()
+        b = gen.router_bias(cfg, 0, 0, "cpu")
+        x = gen.tokens(cfg, 0, 0, "cuda").cpu()
+        idx = oracle.topk_select(oracle.router_logits(x, Wr, b), cfg.k)
+        raw = {int(e): tuple(host_bf16(t) for t in gen.expert_weights(cfg, 0, int(e), "cuda")) for e in np.unique(idx)}
+        t0 = time.perf_counter()
+        oracle.moe_layer(x, Wr, b, cfg.k, lambda e: raw[int(e)])
+        el = time.perf_counter() - t0
+        return dict(value=cfg.T / el, unit="tokens/s", cores=blas_threads(torch), kind="oracle",
+                    sample=f"one whole layer of {cfg.name} ({cfg.T} tokens, {len(raw)} active experts), "
+                           f"{el:.1f} s of oracle time")
+
+    section("cpu_baseline stack48")
+    out["stack48_bf16_h2048_e128"] = layer_step_rate(CONFIGS["stack48_bf16_h2048_e128"], False)
+    section("cpu_baseline int4 decode")
+    out["decode_int4_t8_l8"] = layer_step_rate(CONFIGS["decode_int4_t8_l8"], True)
+    section("cpu_baseline prefill 4096")
+    out["prefill_bf16_t4096_e256"] = prefill_rate(CONFIGS["prefill_bf16_t4096_e256"])
+    section("cpu_baseline prefill 16384")
+    out["prefill_db_bf16_t16384_l8"] = prefill_rate(CONFIGS["prefill_db_bf16_t16384_l8"])
+    return out
 
 
 def main():
@@ -571,6 +646,8 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the 48-layer decode section")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-all", action="store_true",
+                    help="also time the oracle on the stack, int4 decode and prefill workloads (a few minutes)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB (hardware-counter calibration)")
     args = ap.parse_args()
@@ -656,6 +733,8 @@ def main():
         cb = cpu_baseline(args, torch, gen, cfg)
         cb["value"] = round(cb["value"], 4)
         out["cpu_baseline"] = cb
+        if args.cpu_all:
+            out["cpu_baseline_other_workloads"] = rnd(cpu_baselines_all(args, torch, gen))
     print(json.dumps(out), flush=True)
 
 
