@@ -450,19 +450,23 @@ int moe_cpu_threads(void);
  *   is no CPU execution on this path). Requires S >= min(E, k*T_max), so that
  *   a layer-step's experts always fit the cache at once (one wave), and
  *   E <= 1024. layer_pool: the L per-layer base addresses of moe_pool_alloc
- *   memory (host; layers may share a base), read by the fill kernel over the
- *   host link. slot_base/slot_stride, buffers and the other arguments as for
- *   moe_decoder_create (the decoder never frees them). trace_capacity: number
- *   of trace records kept in GPU memory (0: none).
+ *   memory (host; layers may share a base), read over the host link by the
+ *   FFN (fp32 experts: by the fill kernel). slot_base/slot_stride, buffers
+ *   and the other arguments as for moe_decoder_create (the decoder never
+ *   frees them). trace_capacity: number of trace records kept in GPU memory
+ *   (0: none).
  *   Errors: EINVAL (null, bad sizes, pool address not from moe_pool_alloc),
  *   ECAPACITY (S too small), ENOMEM (device memory), EHIP.
  * moe_device_decoder_step: enqueues one layer-step on `stream`: routing (as
  *   moe_route), the resolve kernel (one workgroup, updates the tables and
- *   writes the work list and misses to GPU memory), the fill kernel (copies
- *   the misses' blobs from the pool into their slots; returns at once when
- *   there are none), the decode expert FFN over the device work list (fixed
- *   grid for min(E, k*T) items; surplus blocks exit) and the combine into
- *   `out`. It neither waits for the GPU nor allocates, so the same call can be
+ *   writes the work list, hits first, and the number of hits to GPU memory),
+ *   the decode expert FFN over the device work list (fixed grid for
+ *   min(E, k*T) items; surplus blocks exit) and the combine into `out`. For
+ *   bf16, int4 and MXFP4 experts the FFN reads each hit from its slot and
+ *   each miss from the pool over the host link, writing the miss's blob
+ *   through into its slot as it goes (the fill); for fp32 experts a fill
+ *   kernel first copies the misses' blobs into their slots (returning at once
+ *   when there are none) and the FFN then reads every item from its slot. It neither waits for the GPU nor allocates, so the same call can be
  *   captured with moe_graph_begin/moe_graph_end and replayed: a replay reads
  *   whatever x, Wr and bias hold at that time. Launch shapes depend only on
  *   T, so a graph is tied to the T (and layer and buffers) it was captured
