@@ -126,14 +126,30 @@ def _check(code, what=""):
 
 
 def _ptr(t):
-    """Device/host address of a torch tensor, numpy array, int address or None."""
+    """Address of a contiguous torch tensor or numpy array, an int address (taken as given) or None."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
     if isinstance(t, np.ndarray):
+        if not t.flags["C_CONTIGUOUS"]:
+            raise ValueError("the library takes C-contiguous arrays")
         return t.ctypes.data
+    if not t.is_contiguous():
+        raise ValueError("the library takes contiguous tensors")
     return t.data_ptr()
+
+
+def _dptr(t):
+    """Address of GPU memory: a contiguous GPU tensor, an int address (taken as given) or None. A host tensor
+    or array here would be read by a kernel as a device address, so it is refused."""
+    if t is not None and not isinstance(t, int) and (isinstance(t, np.ndarray) or not t.is_cuda):
+        raise ValueError("the library takes a GPU tensor for this argument")
+    return _ptr(t)
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
 
 
 def _stream(s):
@@ -170,9 +186,9 @@ def moe_route_workspace_size(T, H, E, k):
 def moe_route(x, Wr, bias, k, topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos, workspace, stream=None):
     T, H = x.shape
     E = Wr.shape[1]
-    _check(_lib.moe_route(_ptr(x), _dtype_code(x), _ptr(Wr), _ptr(bias), T, H, E, k, _ptr(topk_idx), _ptr(topk_w),
-                          _ptr(logits), _ptr(counts), _ptr(offsets), _ptr(perm_src), _ptr(perm_pos), _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _stream(stream)), "moe_route")
+    _check(_lib.moe_route(_dptr(x), _dtype_code(x), _dptr(Wr), _dptr(bias), T, H, E, k, _dptr(topk_idx),
+                          _dptr(topk_w), _dptr(logits), _dptr(counts), _dptr(offsets), _dptr(perm_src),
+                          _dptr(perm_pos), _dptr(workspace), _nbytes(workspace), _stream(stream)), "moe_route")
 
 
 # ---------------------------------------------------------------------------
@@ -181,7 +197,7 @@ def moe_expert_bytes(wfmt, H, I):
 
 
 def moe_pack_expert(wfmt, H, I, W1, W3, W2, s1, s3, s2, blob, stream=None):
-    _check(_lib.moe_pack_expert(wfmt, H, I, _ptr(W1), _ptr(W3), _ptr(W2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(blob),
+    _check(_lib.moe_pack_expert(wfmt, H, I, _dptr(W1), _dptr(W3), _dptr(W2), _dptr(s1), _dptr(s3), _dptr(s2), _dptr(blob),
                                 _stream(stream)), "moe_pack_expert")
 
 
@@ -278,7 +294,7 @@ def cache_fill_async(cache, misses, layer_pool, blob_stride, blob_bytes, slot_ba
     ms = np.ascontiguousarray(np.asarray(misses, dtype=np.int32).reshape(-1, 4))
     lp = layer_table(layer_pool)
     _check(_lib.cache_fill_async(cache.h, ms.ctypes.data if len(ms) else None, len(ms), lp.ctypes.data, blob_stride,
-                                 blob_bytes, _ptr(slot_base), slot_stride, _stream(fill_stream),
+                                 blob_bytes, _dptr(slot_base), slot_stride, _stream(fill_stream),
                                  _stream(compute_stream)), "cache_fill_async")
 
 
@@ -291,15 +307,15 @@ def moe_ffn(x, perm_src, work, slot_base, slot_stride, wfmt, H, I, y_perm, works
             stream=None):
     """work: int32 array [n, 4] of (expert, slot, row_begin, rows)."""
     w = np.ascontiguousarray(np.asarray(work, dtype=np.int32).reshape(-1, 4))
-    _check(_lib.moe_ffn(_ptr(x), _dtype_code(x), _ptr(perm_src), w.ctypes.data if len(w) else None, len(w),
-                        _ptr(slot_base), slot_stride, wfmt, H, I, _ptr(y_perm), _ptr(workspace),
-                        workspace.numel() * workspace.element_size(), mode, _stream(stream)), "moe_ffn")
+    _check(_lib.moe_ffn(_dptr(x), _dtype_code(x), _dptr(perm_src), w.ctypes.data if len(w) else None, len(w),
+                        _dptr(slot_base), slot_stride, wfmt, H, I, _dptr(y_perm), _dptr(workspace),
+                        _nbytes(workspace), mode, _stream(stream)), "moe_ffn")
 
 
 def moe_combine(y_perm, perm_pos, topk_w, out, stream=None):
     T, k = perm_pos.shape
     H = y_perm.shape[1]
-    _check(_lib.moe_combine(_ptr(y_perm), _ptr(perm_pos), _ptr(topk_w), T, k, H, _ptr(out), _dtype_code(out),
+    _check(_lib.moe_combine(_dptr(y_perm), _dptr(perm_pos), _dptr(topk_w), T, k, H, _dptr(out), _dtype_code(out),
                             _stream(stream)), "moe_combine")
 
 
@@ -346,24 +362,30 @@ def moe_pipe_copy_ms(pipe, layer):
 
 def moe_clock_record(sums):
     """sums: a device tensor of two int64 (zeroed by the caller), or None to turn the record off."""
-    _check(_lib.moe_clock_record(_ptr(sums) if sums is not None else None), "moe_clock_record")
+    _check(_lib.moe_clock_record(_dptr(sums)), "moe_clock_record")
 
 
 # ---------------------------------------------------------------------------
+def _decoder_buffers(bufs):
+    """DecoderBuffers from a dict of GPU tensors (names as the struct's fields)."""
+    b = DecoderBuffers()
+    for name in ("topk_idx", "topk_w", "logits", "counts", "offsets", "perm_src", "perm_pos", "y_perm"):
+        setattr(b, name, _dptr(bufs.get(name)))
+    b.route_ws, b.route_ws_bytes = _dptr(bufs["route_ws"]), _nbytes(bufs["route_ws"])
+    b.ffn_ws, b.ffn_ws_bytes = _dptr(bufs["ffn_ws"]), _nbytes(bufs["ffn_ws"])
+    return b
+
+
 class MoeDecoder:
     """Owner of a moe_decoder_t; `bufs` maps DecoderBuffers field names to torch tensors (kept alive here)."""
 
     def __init__(self, cache, T_max, H, I, E, k, dtype, wfmt, layer_pool, blob_stride, slot_base, slot_stride, bufs):
         self.keep = bufs
-        b = DecoderBuffers()
-        for name in ("topk_idx", "topk_w", "logits", "counts", "offsets", "perm_src", "perm_pos", "y_perm"):
-            setattr(b, name, _ptr(bufs.get(name)))
-        b.route_ws, b.route_ws_bytes = _ptr(bufs["route_ws"]), bufs["route_ws"].numel()
-        b.ffn_ws, b.ffn_ws_bytes = _ptr(bufs["ffn_ws"]), bufs["ffn_ws"].numel()
+        b = _decoder_buffers(bufs)
         st = ctypes.c_int(0)
         lp = layer_table(layer_pool)
         self.h = _lib.moe_decoder_create(cache.h, T_max, H, I, E, k, dtype, wfmt, lp.ctypes.data, blob_stride,
-                                         _ptr(slot_base), slot_stride, ctypes.byref(b), ctypes.byref(st))
+                                         _dptr(slot_base), slot_stride, ctypes.byref(b), ctypes.byref(st))
         if not self.h:
             raise MoEError(st.value, _lib.moe_last_error().decode())
         self.cache = cache
@@ -386,7 +408,7 @@ def moe_decoder_destroy(dec):
 
 def moe_decoder_step(dec, step, layer, x, Wr, bias, out, stream=None):
     nm = ctypes.c_int(0)
-    _check(_lib.moe_decoder_step(dec.h, step, layer, _ptr(x), x.shape[0], _ptr(Wr), _ptr(bias), _ptr(out),
+    _check(_lib.moe_decoder_step(dec.h, step, layer, _dptr(x), x.shape[0], _dptr(Wr), _dptr(bias), _dptr(out),
                                  _dtype_code(out), _stream(stream), ctypes.byref(nm)), "moe_decoder_step")
     return nm.value
 
@@ -433,15 +455,6 @@ def moe_decoder_cpu_runs(dec):
 
 
 # ---------------------------------------------------------------------------
-def _decoder_buffers(bufs):
-    b = DecoderBuffers()
-    for name in ("topk_idx", "topk_w", "logits", "counts", "offsets", "perm_src", "perm_pos", "y_perm"):
-        setattr(b, name, _ptr(bufs.get(name)))
-    b.route_ws, b.route_ws_bytes = _ptr(bufs["route_ws"]), bufs["route_ws"].numel()
-    b.ffn_ws, b.ffn_ws_bytes = _ptr(bufs["ffn_ws"]), bufs["ffn_ws"].numel()
-    return b
-
-
 class MoeDeviceDecoder:
     """Owner of a moe_device_decoder_t; `bufs` as for MoeDecoder (kept alive here)."""
 
@@ -452,7 +465,7 @@ class MoeDeviceDecoder:
         st = ctypes.c_int(0)
         lp = layer_table(layer_pool)
         self.h = _lib.moe_device_decoder_create(L, E, S, T_max, H, I, k, dtype, wfmt, lp.ctypes.data, blob_stride,
-                                                _ptr(slot_base), slot_stride, ctypes.byref(b), int(trace_capacity),
+                                                _dptr(slot_base), slot_stride, ctypes.byref(b), int(trace_capacity),
                                                 ctypes.byref(st))
         if not self.h:
             raise MoEError(st.value, _lib.moe_last_error().decode())
@@ -474,7 +487,7 @@ def moe_device_decoder_destroy(dec):
 
 
 def moe_device_decoder_step(dec, layer, x, Wr, bias, out, stream=None):
-    _check(_lib.moe_device_decoder_step(dec.h, layer, _ptr(x), x.shape[0], _ptr(Wr), _ptr(bias), _ptr(out),
+    _check(_lib.moe_device_decoder_step(dec.h, layer, _dptr(x), x.shape[0], _dptr(Wr), _dptr(bias), _dptr(out),
                                         _dtype_code(out), _stream(stream)), "moe_device_decoder_step")
 
 
@@ -551,9 +564,9 @@ def moe_cache_capacity(cache):
 
 
 def moe_decoder_resize(dec, S_new, slot_base=None, stream=None):
-    _check(_lib.moe_decoder_resize(dec.h, int(S_new), _ptr(slot_base), _stream(stream)), "moe_decoder_resize")
+    _check(_lib.moe_decoder_resize(dec.h, int(S_new), _dptr(slot_base), _stream(stream)), "moe_decoder_resize")
 
 
 def moe_device_decoder_resize(dec, S_new, slot_base=None, stream=None):
-    _check(_lib.moe_device_decoder_resize(dec.h, int(S_new), _ptr(slot_base), _stream(stream)),
+    _check(_lib.moe_device_decoder_resize(dec.h, int(S_new), _dptr(slot_base), _stream(stream)),
            "moe_device_decoder_resize")

@@ -228,3 +228,23 @@ def test_device_decoder_and_graph_validation_without_gpu(L):
     assert L.moe_cache_capacity(c) == 2
     assert mv.tolist() == [[2, 2, 0], [3, 3, 1]]
     assert [L.moe_cache_slot_of(c, k) for k in range(4)] == [-1, -1, 0, 1]
+
+
+def test_binding_refuses_host_and_strided_tensors(L):
+    """Device arguments must be GPU tensors and every tensor contiguous: the binding raises before the
+    library sees an address that a kernel would misread."""
+    import torch
+    y = torch.zeros((6, 8), dtype=torch.float32)
+    pos = torch.zeros((1, 6), dtype=torch.int32)
+    w = torch.zeros((1, 6), dtype=torch.float32)
+    out = torch.zeros((1, 8), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.moe_combine(y, pos, w, out)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L._dptr(np.zeros(4, np.float32))
+    with pytest.raises(ValueError, match="contiguous"):
+        L._ptr(torch.zeros((4, 4)).t())
+    with pytest.raises(ValueError, match="contiguous"):
+        L._ptr(np.zeros((4, 4), np.float32).T)
+    assert L._dptr(None) is None and L._dptr(1 << 20) == 1 << 20
+    assert L._ptr(y) == y.data_ptr()
