@@ -17,6 +17,7 @@
 // when the weight tiles allow) that the dispatcher sends to one XCD together.
 #include <algorithm>
 #include <cstring>
+#include <type_traits>
 #include <vector>
 
 #include "dev_common.hpp"
@@ -160,22 +161,32 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   struct Frags {
     u32x4_t a[WN], b[WM];
   };
-  auto read_stage = [&](int kt, Frags& f) {
-    const char* b = lds[kt % NS];
+  // The K loop is instantiated for JM = the number of this wave's token
+  // fragments that hold at least one row of the group (0 .. WM, uniform per
+  // wave): fragments wholly past the group get no LDS reads and no
+  // matrix-core work, which lowers the power drawn by partial tiles (a
+  // 96-row group in a 128-token tile, the last tile of a large group, small
+  // groups). The products kept are the same instructions in the same order,
+  // so the results do not change.
+  auto k_loop = [&](auto jm_const) {
+    constexpr int JM = decltype(jm_const)::value;
+    auto read_stage = [&](int kt, Frags& f) {
+      const char* b = lds[kt % NS];
 #pragma unroll
-    for (int j = 0; j < WM; ++j)
-      f.b[j] = *reinterpret_cast<const u32x4_t*>(b + (FA + wm * WM + j) * 1024 + lane * 16);
+      for (int j = 0; j < JM; ++j)
+        f.b[j] = *reinterpret_cast<const u32x4_t*>(b + (FA + wm * WM + j) * 1024 + lane * 16);
+      if constexpr (JM > 0) {
 #pragma unroll
-    for (int i = 0; i < WN; ++i) f.a[i] = *reinterpret_cast<const u32x4_t*>(b + (wn * WN + i) * 1024 + lane * 16);
-  };
-  // Every wave runs its matrix-core work, also on token columns past the
-  // group (their results are never stored).
-  auto compute = [&](const Frags& f) {
+        for (int i = 0; i < WN; ++i)
+          f.a[i] = *reinterpret_cast<const u32x4_t*>(b + (wn * WN + i) * 1024 + lane * 16);
+      }
+    };
+    auto compute = [&](const Frags& f) {
 #pragma unroll
-    for (int i = 0; i < WN; ++i)
+      for (int i = 0; i < WN; ++i)
 #pragma unroll
-      for (int j = 0; j < WM; ++j) acc[i][j] = mfma_bf16(f.a[i], f.b[j], acc[i][j]);
-  };
+        for (int j = 0; j < JM; ++j) acc[i][j] = mfma_bf16(f.a[i], f.b[j], acc[i][j]);
+    };
 
   // All NS buffers are in flight. In step kt a wave computes on stage kt's
   // fragments (read into registers during step kt - 1) while it reads stage
@@ -185,30 +196,31 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   // kt + NS. The read past the last stage repeats the last one (results
   // unused), so the reads and the matrix-core instructions of a step form
   // one basic block for any K and the compiler can interleave them.
-  auto step = [&](int kt, Frags& cur, Frags& nxt) {
-    // this wave's loads of stage kt + 1 landed: at most the stages kt + 2 ..
-    // kt + NS - 1 still in flight, or, near the end where fewer were issued,
-    // none
-    if (kt + NS - 1 < KC) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 2)));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-    }
-    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));  // and its reads of stage kt completed
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + NS < KC) issue(kt + NS, kt % NS);
-    read_stage(min(kt + 1, KC - 1), nxt);
-    compute(cur);
-    // one LDS read, then a share of the matrix-core instructions, in turn (no
-    // priority changes in between: they would fence the scheduler)
+    auto step = [&](int kt, Frags& cur, Frags& nxt) {
+      // this wave's loads of stage kt + 1 landed: at most the stages kt + 2 ..
+      // kt + NS - 1 still in flight, or, near the end where fewer were
+      // issued, none
+      if (kt + NS - 1 < KC) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 2)));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+      }
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_only(0));  // and its reads of stage kt completed
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + NS < KC) issue(kt + NS, kt % NS);
+      read_stage(min(kt + 1, KC - 1), nxt);
+      compute(cur);
+      // one LDS read, then a share of the matrix-core instructions, in turn
+      // (no priority changes in between: they would fence the scheduler)
+      if constexpr (JM > 0) {
 #pragma unroll
-    for (int q = 0; q < WN + WM; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, (WN * WM) / (WN + WM), 0);
-    }
-  };
-  {
+        for (int q = 0; q < WN + JM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, (WN * JM) / (WN + JM), 0);
+        }
+      }
+    };
     for (int s0 = 0; s0 < NS && s0 < KC; ++s0) issue(s0, s0);
     // stage 0 landed
     if (KC >= NS) {
@@ -226,6 +238,16 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
       step(kt + 1, f1, f0);
     }
     if (kt < KC) step(kt, f0, f1);
+  };
+  static_assert(WM == 4, "the dispatch below covers 0 .. 4 fragments");
+  const int rows_here = it.z - (mt * 16 * BM_T + wm * WM * 16);
+  const int jm = rows_here <= 0 ? 0 : min(WM, (rows_here + 15) / 16);
+  switch (jm) {
+    case 0: k_loop(std::integral_constant<int, 0>{}); break;
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    case 3: k_loop(std::integral_constant<int, 3>{}); break;
+    default: k_loop(std::integral_constant<int, 4>{}); break;
   }
   if (clock_sums != nullptr && tid == 0) record_clock(clock_sums, c_start, r_start);
 
