@@ -393,39 +393,59 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp4(const uint16_t* __restrict_
     for (int j = 0; j < WM; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int s0 = 0; s0 < NS - 1 && s0 < KG; ++s0) issue(s0);
-  for (int kt = 0; kt < KG; ++kt) {
-    if (kt + NS - 2 < KG) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 2)));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-    }
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + NS - 1 < KG) issue(kt + NS - 1);
-    const char* b = lds[kt % NS];
-    u32x4_t codes[WN];
-    uint32_t scl[WN];
-#pragma unroll
-    for (int i = 0; i < WN; ++i) {
-      const int ta = wn * WN + i;  // weight tile of this wave
-      codes[i] = *reinterpret_cast<const u32x4_t*>(b + ta * 1024 + lane * 16);
-      scl[i] = *reinterpret_cast<const uint32_t*>(b + CODE + (ta & 7) * 128 + (ta >> 3) * 64 + (lane & 15) * 4);
-    }
-#pragma unroll
-    for (int j = 0; j < KSUB; ++j) {
-      u32x4_t bf[WM];
-#pragma unroll
-      for (int jj = 0; jj < WM; ++jj)
-        bf[jj] = *reinterpret_cast<const u32x4_t*>(b + CODE + SCL + (j * BM_T + wm * WM + jj) * 1024 + lane * 16);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int i = 0; i < WN; ++i) {
-        const u32x4_t a = mx_a_operand(codes[i][j], scl[i] >> (8 * j));
-#pragma unroll
-        for (int jj = 0; jj < WM; ++jj) acc[i][jj] = mfma_bf16(a, bf[jj], acc[i][jj]);
+  // As in the bf16 GEMM, the K loop is instantiated for JM = the number of
+  // this wave's token fragments holding rows of the group: fragments past the
+  // group get no LDS reads and no products, and a wave with none of the
+  // group's rows converts no codes either. Kept products are unchanged.
+  auto k_loop = [&](auto jm_const) {
+    constexpr int JM = decltype(jm_const)::value;
+    for (int kt = 0; kt < KG; ++kt) {
+      if (kt + NS - 2 < KG) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(FPW * (NS - 2)));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
       }
-      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + NS - 1 < KG) issue(kt + NS - 1);
+      if constexpr (JM > 0) {
+        const char* b = lds[kt % NS];
+        u32x4_t codes[WN];
+        uint32_t scl[WN];
+#pragma unroll
+        for (int i = 0; i < WN; ++i) {
+          const int ta = wn * WN + i;  // weight tile of this wave
+          codes[i] = *reinterpret_cast<const u32x4_t*>(b + ta * 1024 + lane * 16);
+          scl[i] = *reinterpret_cast<const uint32_t*>(b + CODE + (ta & 7) * 128 + (ta >> 3) * 64 + (lane & 15) * 4);
+        }
+#pragma unroll
+        for (int j = 0; j < KSUB; ++j) {
+          u32x4_t bf[JM];
+#pragma unroll
+          for (int jj = 0; jj < JM; ++jj)
+            bf[jj] =
+                *reinterpret_cast<const u32x4_t*>(b + CODE + SCL + (j * BM_T + wm * WM + jj) * 1024 + lane * 16);
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int i = 0; i < WN; ++i) {
+            const u32x4_t a = mx_a_operand(codes[i][j], scl[i] >> (8 * j));
+#pragma unroll
+            for (int jj = 0; jj < JM; ++jj) acc[i][jj] = mfma_bf16(a, bf[jj], acc[i][jj]);
+          }
+          __builtin_amdgcn_s_setprio(0);
+        }
+      }
     }
+  };
+  static_assert(WM == 4, "the dispatch below covers 0 .. 4 fragments");
+  const int rows_here = it.z - (mt * 16 * BM_T + wm * WM * 16);
+  const int jm = rows_here <= 0 ? 0 : min(WM, (rows_here + 15) / 16);
+  switch (jm) {
+    case 0: k_loop(std::integral_constant<int, 0>{}); break;
+    case 1: k_loop(std::integral_constant<int, 1>{}); break;
+    case 2: k_loop(std::integral_constant<int, 2>{}); break;
+    case 3: k_loop(std::integral_constant<int, 3>{}); break;
+    default: k_loop(std::integral_constant<int, 4>{}); break;
   }
   if (clock_sums != nullptr && threadIdx.x == 0) record_clock(clock_sums, c_start, r_start);
 
