@@ -125,12 +125,16 @@ FFN_CASES = [
     ("bf16_decode_k_odd", "bf16", 384, 160, [5, 1, 0, 9], "decode"),
     ("bf16_prefill", "bf16", 512, 256, [130, 0, 1, 127, 128, 300, 17, 777], "prefill"),
     ("bf16_prefill_c3shape", "bf16", 2048, 768, [70, 3, 129], "prefill"),
+    # partial last tiles whose waves hold 1, 2, 3 or 4 token fragments of the group (the GEMMs run a K loop
+    # per count): 128-token tiles for 40, 110, 200 rows, 256-token tiles for 276 and 356 rows
+    ("bf16_prefill_partial", "bf16", 512, 256, [40, 110, 276, 356, 200], "prefill"),
     ("int4_decode", "int4", 512, 256, [1, 8, 0, 3, 20], "decode"),
     ("int4_decode_wide", "int4", 1024, 384, [2, 16, 5], "decode"),
     ("mxfp4_decode", "mxfp4", 512, 256, [1, 8, 0, 3, 20], "decode"),
     ("mxfp4_decode_wide", "mxfp4", 1024, 384, [2, 16, 5, 33], "decode"),
     ("mxfp4_prefill", "mxfp4", 512, 256, [130, 0, 1, 127, 128, 300, 17, 777], "prefill"),
     ("mxfp4_prefill_c3shape", "mxfp4", 2048, 768, [70, 3, 129], "prefill"),
+    ("mxfp4_prefill_partial", "mxfp4", 512, 256, [40, 110, 276, 356, 200], "prefill"),
     ("mxfp4_auto_mixed", "mxfp4", 512, 384, [40, 2, 250], "auto"),
 ]
 
