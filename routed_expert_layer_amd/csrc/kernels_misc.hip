@@ -14,7 +14,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int n = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (n >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if ((H & 3) == 0) {
+  if ((H & 3) == 0 && k <= 8) {
+    // every row position and weight first, then every row load, so the k
+    // loads of a thread are in flight together; the sum keeps the order below
+    int p[8];
+    float wj[8];
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) {
+        p[j] = perm_pos[(size_t)t * k + j];
+        wj[j] = w[(size_t)t * k + j];
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) v[j] = *reinterpret_cast<const float4*>(y + (size_t)p[j] * H + n);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) {
+        acc.x = fmaf(wj[j], v[j].x, acc.x);
+        acc.y = fmaf(wj[j], v[j].y, acc.y);
+        acc.z = fmaf(wj[j], v[j].z, acc.z);
+        acc.w = fmaf(wj[j], v[j].w, acc.w);
+      }
+  } else if ((H & 3) == 0) {
     for (int j = 0; j < k; ++j) {
       const int p = perm_pos[(size_t)t * k + j];
       const float wj = w[(size_t)t * k + j];
