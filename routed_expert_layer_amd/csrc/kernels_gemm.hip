@@ -497,39 +497,61 @@ int plan_supertiles(int4* item, int n, int* tile_prefix, int N, int tile_tokens)
 
 inline int supertile_blocks(int tot) { return (tot + 7) / 8 * 256; }  // 8 XCDs x 32 slots per round
 
-// Up to 64 table entries per upload launch.
+// Up to 64 entries of both projections' tables per upload launch: the two
+// share the items' slot and rows and differ in the super-tile shape (item.w)
+// and the prefix sums.
 struct TableChunk {
-  int base, count, n, total;
-  int prefix[64];
-  int4 item[64];
+  int base, count, n, total[2];
+  int prefix[2][64];
+  int4 item[64];  // .w: the gate/up GEMM's GM | GN << 8
+  int w2[64];     // the down GEMM's GM | GN << 8
 };
 
-__global__ __launch_bounds__(64) void table_upload(const TableChunk c, GemmTable* __restrict__ t) {
+__global__ __launch_bounds__(64) void table_upload(const TableChunk c, GemmTable* __restrict__ t1,
+                                                   GemmTable* __restrict__ t2) {
   const int i = threadIdx.x;
   if (i < c.count) {
-    t->item[c.base + i] = c.item[i];
-    t->tile_prefix[c.base + i] = c.prefix[i];
+    const int4 it = c.item[i];
+    t1->item[c.base + i] = it;
+    t2->item[c.base + i] = make_int4(it.x, it.y, it.z, c.w2[i]);
+    t1->tile_prefix[c.base + i] = c.prefix[0][i];
+    t2->tile_prefix[c.base + i] = c.prefix[1][i];
   }
-  if (i == 0 && c.base + c.count == c.n) t->tile_prefix[c.n] = c.total;
+  if (i == 0 && c.base + c.count == c.n) {
+    t1->tile_prefix[c.n] = c.total[0];
+    t2->tile_prefix[c.n] = c.total[1];
+  }
   if (i == 0 && c.base == 0) {
-    t->n = c.n;
-    t->total_tiles = c.total;
+    t1->n = c.n;
+    t1->total_tiles = c.total[0];
+    t2->n = c.n;
+    t2->total_tiles = c.total[1];
   }
 }
 
-hipError_t upload_table(const int4* item, const int* prefix, int n, int total, GemmTable* dst, hipStream_t s) {
+// Plans both projections of the n items (gate/up N = 2I, down N = H; tiles
+// of tile_tokens) and writes their tables; tot receives the super-tile counts.
+hipError_t plan_and_upload(const int4* items, int n, int H, int I, int tile_tokens, GemmTable* t1, GemmTable* t2,
+                           int (&tot)[2], hipStream_t s) {
+  std::vector<int4> it1(items, items + n), it2(items, items + n);
+  std::vector<int> pre1(n + 1), pre2(n + 1);
+  tot[0] = plan_supertiles(it1.data(), n, pre1.data(), 2 * I, tile_tokens);
+  tot[1] = plan_supertiles(it2.data(), n, pre2.data(), H, tile_tokens);
   TableChunk c;
   for (int base = 0; base < n; base += 64) {
     memset(&c, 0, sizeof c);
     c.base = base;
     c.count = n - base < 64 ? n - base : 64;
     c.n = n;
-    c.total = total;
+    c.total[0] = tot[0];
+    c.total[1] = tot[1];
     for (int i = 0; i < c.count; ++i) {
-      c.item[i] = item[base + i];
-      c.prefix[i] = prefix[base + i];
+      c.item[i] = it1[base + i];
+      c.w2[i] = it2[base + i].w;
+      c.prefix[0][i] = pre1[base + i];
+      c.prefix[1][i] = pre2[base + i];
     }
-    hipLaunchKernelGGL(table_upload, dim3(1), dim3(64), 0, s, c, dst);
+    hipLaunchKernelGGL(table_upload, dim3(1), dim3(64), 0, s, c, t1, t2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -559,16 +581,12 @@ hipError_t launch_ffn_prefill2(const void* x, const int32_t* perm_src, const int
   GemmTable* tab[2][2];  // [part][projection]
   int tot[2][2] = {{0, 0}, {0, 0}};
   for (int p = 0; p < 2; ++p) {
-    for (int ph = 0; ph < 2; ++ph) {
+    for (int ph = 0; ph < 2; ++ph)
       tab[p][ph] = reinterpret_cast<GemmTable*>(static_cast<char*>(tables) + (2 * p + ph) * kTableBytes);
-      const int m = (int)part[p].size();
-      if (m == 0) continue;
-      std::vector<int4> it(part[p]);
-      std::vector<int> pre(m + 1);
-      tot[p][ph] = plan_supertiles(it.data(), m, pre.data(), ph == 0 ? 2 * I : H, p == 0 ? 256 : 128);
-      hipError_t e = upload_table(it.data(), pre.data(), m, tot[p][ph], tab[p][ph], s);
-      if (e != hipSuccess) return e;
-    }
+    const int m = (int)part[p].size();
+    if (m == 0) continue;
+    hipError_t e = plan_and_upload(part[p].data(), m, H, I, p == 0 ? 256 : 128, tab[p][0], tab[p][1], tot[p], s);
+    if (e != hipSuccess) return e;
   }
   if (tot[0][0] > 0)
     hipLaunchKernelGGL((gemm2_bf16<1, 16, const GemmTable*>), dim3(supertile_blocks(tot[0][0])), dim3(512), 0, s, xb,
@@ -601,14 +619,9 @@ hipError_t launch_ffn_prefill_mxfp4(const void* x, const int32_t* perm_src, cons
   const BlobLayout L = blob_layout(3, H, I);
   int tot[2] = {0, 0};
   GemmTable* tab[2];
-  for (int ph = 0; ph < 2; ++ph) {
-    tab[ph] = reinterpret_cast<GemmTable*>(static_cast<char*>(tables) + ph * kTableBytes);
-    std::vector<int4> it(items, items + n);
-    std::vector<int> pre(n + 1);
-    tot[ph] = plan_supertiles(it.data(), n, pre.data(), ph == 0 ? 2 * I : H, 128);
-    hipError_t e = upload_table(it.data(), pre.data(), n, tot[ph], tab[ph], s);
-    if (e != hipSuccess) return e;
-  }
+  for (int ph = 0; ph < 2; ++ph) tab[ph] = reinterpret_cast<GemmTable*>(static_cast<char*>(tables) + ph * kTableBytes);
+  hipError_t e = plan_and_upload(items, n, H, I, 128, tab[0], tab[1], tot, s);
+  if (e != hipSuccess) return e;
   uint16_t* hb = static_cast<uint16_t*>(hbuf);
   if (tot[0] > 0)
     hipLaunchKernelGGL(gemm_mxfp4<1>, dim3(supertile_blocks(tot[0])), dim3(512), 0, s,
