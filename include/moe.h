@@ -244,6 +244,15 @@ int cache_fill_async(moe_cache_t* cache, const moe_miss_t* misses, int n,
 /* ------------------------------------------------------------------------ *
  * Grouped expert FFN.
  *
+ * Page "FreeToken-rtx-4090", section "How the MoE Memory Hierarchy Works": an
+ * expert is one complete layer-and-expert unit, executed through the same
+ * logical mapping wherever it is resident, and the GPU executes the experts
+ * held in its cache (the paragraph after the component table: a missing
+ * expert is either filled into the cache and run on the GPU or run on the
+ * CPU). The pages do not write the expert's arithmetic; this call computes a
+ * SwiGLU expert (gate on x W1, up on x W3, down W2), the grouped form the
+ * layer is specified with.
+ *
  * Runs each listed expert on its group of rows:
  *   for row r in [row_begin, row_begin + rows) of item i (expert blob at
  *   slot_base + slot*slot_stride):
@@ -277,8 +286,35 @@ int moe_ffn(const void* x, int dtype, const int32_t* perm_src,
             const void* slot_base, size_t slot_stride, int wfmt, int H, int I,
             float* y_perm, void* workspace, size_t ws_bytes, int mode, void* stream);
 
+/* moe_ffn_grouped: the same computation for every expert e in 0..E-1 with
+ * counts[e] > 0, its group being rows offsets[e] .. offsets[e]+counts[e]-1 of
+ * the grouped layout, with the work list read from DEVICE memory (counts and
+ * offsets as moe_route writes them) and planned on the GPU, so the call
+ * neither waits for the GPU nor copies control data (page "FreeToken-rtx-4090",
+ * phase table row "Prefill": a layer's experts are computed as a whole once
+ * the layer is resident). Always the tiled matrix-core GEMM.
+ *   counts  device int32 [E]; offsets device int32 [E+1] (only [0, E) read)
+ *   slot_of device int32 [E]: slot of expert e's blob, or NULL for slot e
+ *   n_slots slots at slot_base; rows_max bounds every row (e.g. T*k)
+ *   wfmt    MOE_W_BF16 (H and 2I multiples of 256, I of 32) or MOE_W_MXFP4
+ *           (H % 256 == 0, I % 128 == 0); x bf16 [T, H]
+ *   workspace >= moe_ffn_workspace_size(rows_max, H, I, wfmt) bytes
+ * A group whose rows reach past rows_max, or whose slot is outside
+ * [0, n_slots), is not computed (its rows of y_perm are left as they were).
+ * Errors: MOE_EINVAL for null pointers, unsupported shapes or formats, E
+ * outside 1..1024; MOE_EHIP if a launch fails. */
+int moe_ffn_grouped(const void* x, int dtype, const int32_t* perm_src, const int32_t* counts,
+                    const int32_t* offsets, const int32_t* slot_of, int E, int n_slots, int rows_max,
+                    const void* slot_base, size_t slot_stride, int wfmt, int H, int I, float* y_perm,
+                    void* workspace, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ *
- * Weighted combine: out[t, :] = sum_{j=0..k-1} topk_w[t,j] * y_perm[perm_pos[t,j], :]
+ * Weighted combine. Page "FreeToken-rtx-4090", section "How the MoE Memory
+ * Hierarchy Works": a token activates a small subset of a layer's routed
+ * experts (six of 256 in the model described); the layer's output for the
+ * token is their outputs weighted by the router (the pages do not write the
+ * sum; the weights are moe_route's renormalised softmax):
+ *   out[t, :] = sum_{j=0..k-1} topk_w[t,j] * y_perm[perm_pos[t,j], :]
  * summed in ascending j in fp32 (no atomics: the result is deterministic).
  * y_perm device fp32 [T*k, H]; perm_pos device int32 [T, k]; topk_w device
  * fp32 [T, k]; out device [T, H] of out_dtype (MOE_DT_F32 or MOE_DT_BF16).
@@ -411,6 +447,25 @@ int moe_decoder_ffn_stats(moe_decoder_t* decoder, double* bytes, double* ms, int
 int moe_decoder_fills(const moe_decoder_t* decoder, int64_t* fills);
 int moe_decoder_cpu_runs(const moe_decoder_t* decoder, int64_t* runs);
 int moe_decoder_resize(moe_decoder_t* decoder, int S_new, void* slot_base, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Prefill layer.
+ *
+ * Page "FreeToken-rtx-4090", phase table row "Prefill" and the paragraph after
+ * it: prefill activates a broad part of a layer's experts, and the layer is
+ * computed from a buffer holding all of them (a moe_pipe buffer or any
+ * resident copy). One call enqueues, on `stream`, moe_route, moe_ffn_grouped
+ * with the routing's device counts and offsets (expert e's blob at
+ * layer_base + e*blob_stride) and moe_combine into `out` [T, H] (out_dtype);
+ * nothing waits for the GPU, copies control data or allocates. `b` holds the
+ * caller's device buffers as for moe_decoder_create, sized for T tokens
+ * (logits may be NULL); after the call they hold the layer's routing and
+ * y_perm. Requirements and errors as moe_route and moe_ffn_grouped (bf16
+ * activations; bf16 or MXFP4 experts).
+ * ------------------------------------------------------------------------- */
+int moe_prefill_layer(const void* x, int dtype, const void* Wr, const float* bias, int T, int H, int E, int k,
+                      int I, int wfmt, const void* layer_base, size_t blob_stride, const moe_decoder_buffers_t* b,
+                      void* out, int out_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
  * CPU execution of an expert (page "FreeToken-rtx-4090", component table row

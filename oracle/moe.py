@@ -145,7 +145,8 @@ def dequant_int4(q, s, group=128):
     """W[k, n] = q[k, n] * s[k // group, n] (exact in fp64)."""
     q = as_f64(q)
     s = as_f64(s)
-    return q * np.repeat(s, group, axis=0)
+    K, N = q.shape
+    return (q.reshape(K // group, group, N) * s[:, None, :]).reshape(K, N)
 
 
 def e2m1_value(code):
@@ -173,8 +174,11 @@ def e8m0_value(s):
 def dequant_mxfp4(codes, scales, block=32):
     """W[k, n] = E2M1[codes[k, n]] * 2^(scales[k // block, n] - 127): one scale per
     `block` consecutive K values of a column (exact in fp64)."""
-    c = as_int(codes)
-    return E2M1[c] * np.repeat(e8m0_value(as_int(scales)), block, axis=0)
+    c = codes.detach().cpu().numpy() if hasattr(codes, "detach") else np.asarray(codes)
+    K, N = c.shape
+    w = E2M1[c].reshape(K // block, block, N)
+    w *= e8m0_value(as_int(scales))[:, None, :]
+    return w.reshape(K, N)
 
 
 def expert_outputs(x, offsets, perm_src, get_expert, experts=None):

@@ -30,6 +30,7 @@ SYMBOLS = [
     "moe_device_decoder_trace", "moe_device_decoder_clear_trace", "moe_device_decoder_slot_of",
     "moe_graph_begin", "moe_graph_end", "moe_graph_launch", "moe_graph_destroy",
     "moe_cache_resize", "moe_cache_capacity", "moe_decoder_resize", "moe_device_decoder_resize",
+    "moe_ffn_grouped", "moe_prefill_layer",
 ]
 
 
@@ -84,6 +85,7 @@ _sig("moe_cache_stats", I32, P, PI64, PI64)
 _sig("cache_fill_async", I32, P, P, I32, P, SZ, SZ, P, SZ, P, P)  # layer_pool: array of L addresses
 _sig("moe_ffn_workspace_size", SZ, I32, I32, I32, I32)
 _sig("moe_ffn", I32, P, I32, P, P, I32, P, SZ, I32, I32, I32, P, P, SZ, I32, P)
+_sig("moe_ffn_grouped", I32, P, I32, P, P, P, P, I32, I32, I32, P, SZ, I32, I32, I32, P, P, SZ, P)
 _sig("moe_combine", I32, P, P, P, I32, I32, I32, P, I32, P)
 _sig("moe_pipe_create", P, P, SZ, I32, PI)
 _sig("moe_pipe_destroy", I32, P)
@@ -116,6 +118,8 @@ _sig("moe_graph_destroy", I32, P)
 _sig("moe_cache_resize", I32, P, I32, P, I32, PI)
 _sig("moe_cache_capacity", I32, P)
 _sig("moe_decoder_resize", I32, P, I32, P, P)
+_sig("moe_prefill_layer", I32, P, I32, P, P, I32, I32, I32, I32, I32, I32, P, SZ, ctypes.POINTER(DecoderBuffers), P,
+     I32, P)
 _sig("moe_device_decoder_resize", I32, P, I32, P, P)
 
 
@@ -312,6 +316,16 @@ def moe_ffn(x, perm_src, work, slot_base, slot_stride, wfmt, H, I, y_perm, works
                         _nbytes(workspace), mode, _stream(stream)), "moe_ffn")
 
 
+def moe_ffn_grouped(x, perm_src, counts, offsets, slot_of, n_slots, rows_max, slot_base, slot_stride, wfmt, H, I,
+                    y_perm, workspace, stream=None):
+    """counts [E], offsets [E+1], slot_of [E] or None: device int32 tensors (the work list stays on the GPU)."""
+    E = counts.shape[0]
+    _check(_lib.moe_ffn_grouped(_dptr(x), _dtype_code(x), _dptr(perm_src), _dptr(counts), _dptr(offsets),
+                                _dptr(slot_of), E, n_slots, rows_max, _dptr(slot_base), slot_stride, wfmt, H, I,
+                                _dptr(y_perm), _dptr(workspace), _nbytes(workspace), _stream(stream)),
+           "moe_ffn_grouped")
+
+
 def moe_combine(y_perm, perm_pos, topk_w, out, stream=None):
     T, k = perm_pos.shape
     H = y_perm.shape[1]
@@ -423,6 +437,20 @@ def moe_decoder_ffn_stats(dec):
     _check(_lib.moe_decoder_ffn_stats(dec.h, ctypes.byref(b), ctypes.byref(m), ctypes.byref(n)),
            "moe_decoder_ffn_stats")
     return b.value, m.value, n.value
+
+
+def moe_prefill_layer(x, Wr, bias, k, I, wfmt, layer_base, blob_stride, bufs, out, stream=None):
+    """bufs: a DecoderBuffers (see decoder_buffers) whose tensors the caller keeps alive."""
+    T, H = x.shape
+    E = Wr.shape[1]
+    _check(_lib.moe_prefill_layer(_dptr(x), _dtype_code(x), _dptr(Wr), _dptr(bias), T, H, E, k, I, wfmt,
+                                  _dptr(layer_base), blob_stride, ctypes.byref(bufs), _dptr(out), _dtype_code(out),
+                                  _stream(stream)), "moe_prefill_layer")
+
+
+def decoder_buffers(bufs):
+    """The DecoderBuffers struct for a dict of GPU tensors (names as its fields)."""
+    return _decoder_buffers(bufs)
 
 
 def moe_decoder_fills(dec):

@@ -348,8 +348,7 @@ size_t moe_ffn_workspace_size(int rows_total, int H, int I, int wfmt) {
   // h: one row of I per routed row, plus one 16-row tile of slack for the
   // prefill GEMM's tiled h layout
   const size_t hb = moe::align_up((size_t)(rows_total + 16) * I * (wfmt == MOE_W_F32 ? 4 : 2), 256);
-  const size_t xg = (wfmt == MOE_W_INT4) ? moe::align_up((size_t)rows_total * H * 2, 256) : 0;
-  return hb + xg + 4 * moe::kTableBytes + 256;
+  return hb + 4 * moe::kTableBytes + 256;
 }
 
 int moe_ffn(const void* x, int dtype, const int32_t* perm_src, const moe_work_t* work, int n_work,
@@ -387,8 +386,7 @@ int moe_ffn(const void* x, int dtype, const int32_t* perm_src, const moe_work_t*
   }
   char* ws = static_cast<char*>(workspace);
   void* hbuf = ws;
-  void* xg = ws + moe::align_up((size_t)(rows_total + 16) * I * (wfmt == MOE_W_F32 ? 4 : 2), 256);
-  void* tables = static_cast<char*>(xg) + (wfmt == MOE_W_INT4 ? moe::align_up((size_t)rows_total * H * 2, 256) : 0);
+  void* tables = ws + moe::align_up((size_t)(rows_total + 16) * I * (wfmt == MOE_W_F32 ? 4 : 2), 256);
   hipStream_t s = as_stream(stream);
   if (prefill && wfmt == MOE_W_MXFP4) {
     std::vector<int4> items;
@@ -431,10 +429,37 @@ int moe_ffn(const void* x, int dtype, const int32_t* perm_src, const moe_work_t*
     hipError_t e = prefill ? moe::launch_ffn_prefill(x, perm_src, wa, static_cast<const char*>(slot_base), slot_stride,
                                                      H, I, hbuf, y_perm, s)
                            : moe::launch_ffn_decode(wfmt, x, perm_src, wa, static_cast<const char*>(slot_base),
-                                                    slot_stride, H, I, hbuf, xg, y_perm, s);
+                                                    slot_stride, H, I, hbuf, y_perm, s);
     if (e != hipSuccess) return hip_fail(e, "moe_ffn launch");
   }
   return MOE_OK;
+}
+
+int moe_ffn_grouped(const void* x, int dtype, const int32_t* perm_src, const int32_t* counts, const int32_t* offsets,
+                    const int32_t* slot_of, int E, int n_slots, int rows_max, const void* slot_base,
+                    size_t slot_stride, int wfmt, int H, int I, float* y_perm, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  if (!moe::grouped_supported(wfmt, H, I))
+    return fail(MOE_EINVAL,
+                "moe_ffn_grouped: needs bf16 weights with H and 2I multiples of 256 and I of 32, or MXFP4 weights "
+                "with H %% 256 == 0 and I %% 128 == 0 (got format %d, %dx%d)",
+                wfmt, H, I);
+  if (dtype != MOE_DT_BF16) return fail(MOE_EINVAL, "moe_ffn_grouped: activations must be bf16");
+  if (E < 1 || E > 1024 || n_slots < 1 || rows_max < 0)
+    return fail(MOE_EINVAL, "moe_ffn_grouped: bad sizes E=%d n_slots=%d rows_max=%d", E, n_slots, rows_max);
+  if (!x || !perm_src || !counts || !offsets || !slot_base || !y_perm || !workspace)
+    return fail(MOE_EINVAL, "moe_ffn_grouped: null pointer argument");
+  const size_t blob = moe::blob_layout(wfmt, H, I).bytes;
+  if (slot_stride < blob) return fail(MOE_EINVAL, "moe_ffn_grouped: slot_stride %zu < blob size %zu", slot_stride, blob);
+  if (ws_bytes < moe_ffn_workspace_size(rows_max, H, I, wfmt))
+    return fail(MOE_EINVAL, "moe_ffn_grouped: workspace too small for %d rows", rows_max);
+  if (rows_max == 0) return MOE_OK;
+  char* ws = static_cast<char*>(workspace);
+  const size_t hb = moe::align_up((size_t)(rows_max + 16) * I * 2, 256);
+  hipError_t e = moe::launch_ffn_grouped(wfmt, x, perm_src, counts, offsets, slot_of, E, n_slots, rows_max,
+                                         static_cast<const char*>(slot_base), slot_stride, H, I, ws, y_perm, ws + hb,
+                                         as_stream(stream));
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_ffn_grouped launch");
 }
 
 // ---------------------------------------------------------------------------
@@ -545,6 +570,29 @@ int moe_pipe_end_layer(moe_pipe_t* p, int layer, void* compute_stream) {
   if (e != hipSuccess) return hip_fail(e, "moe_pipe_end_layer");
   p->next_end = layer + 1;
   return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Prefill layer: routing, grouped FFN over the device work list, combine
+// ---------------------------------------------------------------------------
+int moe_prefill_layer(const void* x, int dtype, const void* Wr, const float* bias, int T, int H, int E, int k, int I,
+                      int wfmt, const void* layer_base, size_t blob_stride, const moe_decoder_buffers_t* b, void* out,
+                      int out_dtype, void* stream) {
+  if (!b) return fail(MOE_EINVAL, "moe_prefill_layer: null buffers");
+  if (T < 0 || H <= 0 || E <= 0 || k <= 0 || (long long)T * k > (1ll << 30))
+    return fail(MOE_EINVAL, "moe_prefill_layer: bad sizes T=%d H=%d E=%d k=%d", T, H, E, k);
+  if (!moe::grouped_supported(wfmt, H, I) || dtype != MOE_DT_BF16)
+    return fail(MOE_EINVAL, "moe_prefill_layer: needs bf16 activations and bf16 or MXFP4 experts of a shape the "
+                            "grouped GEMM takes (format %d, %dx%d)", wfmt, H, I);
+  if (T > 0 && (!out || !b->y_perm || !layer_base)) return fail(MOE_EINVAL, "moe_prefill_layer: null pointer");
+  if (out_dtype != MOE_DT_F32 && out_dtype != MOE_DT_BF16) return fail(MOE_EINVAL, "moe_prefill_layer: bad out dtype");
+  int rc = moe_route(x, dtype, Wr, bias, T, H, E, k, b->topk_idx, b->topk_w, b->logits, b->counts, b->offsets,
+                     b->perm_src, b->perm_pos, b->route_ws, b->route_ws_bytes, stream);
+  if (rc != MOE_OK || T == 0) return rc;
+  rc = moe_ffn_grouped(x, dtype, b->perm_src, b->counts, b->offsets, nullptr, E, E, T * k, layer_base, blob_stride,
+                       wfmt, H, I, b->y_perm, b->ffn_ws, b->ffn_ws_bytes, stream);
+  if (rc != MOE_OK) return rc;
+  return moe_combine(b->y_perm, b->perm_pos, b->topk_w, T, k, H, out, out_dtype, stream);
 }
 
 int moe_clock_record(unsigned long long* sums) {

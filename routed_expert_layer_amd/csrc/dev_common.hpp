@@ -41,10 +41,6 @@ __device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
 }
-__device__ __forceinline__ f32x4_t mfma_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
-                                                0, 0);
-}
 
 // (x & m) | c in one instruction (the compiler emits an and and an or). At
 // most one scalar operand per vector instruction: the mask comes from a
@@ -55,26 +51,18 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
   return r;
 }
 
-// Eight int4 codes (nibble order k0,k2,k4,k6,k1,k3,k5,k7, stored as q+8) to
-// eight fp16 values in k order. A nibble n placed in the low mantissa bits of
-// 1024 (0x6400 | n) is 1024 + n exactly, and 1024 + n - 1032 = q. A nibble
-// left four bits up (0x6400 | n << 4) is 1024 + 16 n, and (1024 + 16 n) / 16
-// - 72 = q, one fused multiply-add whose exact result needs no rounding; so
-// of the four nibble pairs of a word only the upper two need a shift (one,
-// shared), and each pair costs one and-or and one packed fp16 operation.
-__device__ __forceinline__ u32x4_t int4x8_to_f16x8(uint32_t w) {
-  const uint32_t magic = 0x64006400u;
-  const f16x2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const f16x2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const f16x2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  const uint32_t hi = w >> 8;
+// Eight int4 codes (nibble order k0,k2,k4,k6,k1,k3,k5,k7, nibble n = q + 8) to eight bf16 values
+// 1 + n/16 in k order: nibble n placed in the top four mantissa bits of 1.0
+// (0x3F80 | n << 3) is 1 + n/16 exactly, so one shift and one and-or per pair
+// of codes and no arithmetic. Since 1 + n/16 = 1.5 + q/16, a sum over a block
+// of K is sum(q x) = 16 sum((1 + n/16) x) - 24 sum(x).
+__device__ __forceinline__ u32x4_t int4x8_to_bf16x8_biased(uint32_t w) {
+  const uint32_t one = 0x3F803F80u, mask = 0x00780078u;
   u32x4_t r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, and_or(w, 0x000F000Fu, magic)) - off);
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, and_or(w, 0x00F000F0u, magic)),
-                                                                sixteenth, off16));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, and_or(hi, 0x000F000Fu, magic)) - off);
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, and_or(hi, 0x00F000F0u, magic)),
-                                                                sixteenth, off16));
+  r[0] = and_or(w << 3, mask, one);   // nibbles 0, 4: k0, k1
+  r[1] = and_or(w >> 1, mask, one);   // nibbles 1, 5: k2, k3
+  r[2] = and_or(w >> 5, mask, one);   // nibbles 2, 6: k4, k5
+  r[3] = and_or(w >> 9, mask, one);   // nibbles 3, 7: k6, k7
   return r;
 }
 

@@ -174,7 +174,6 @@ int moe_device_decoder_step(moe_device_decoder_t* d, int layer, const void* x, i
   const int items = d->E < d->k * T ? d->E : d->k * T;
   char* ws = static_cast<char*>(b.ffn_ws);
   void* hbuf = ws;
-  void* xg = ws + moe::align_up((size_t)(d->Tmax * d->k + 16) * d->I * (d->wfmt == MOE_W_F32 ? 4 : 2), 256);
   hipError_t e = moe::launch_route(x, d->dtype == MOE_DT_BF16, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w,
                                    b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s, nullptr);
   if (e == hipSuccess) e = moe::launch_dev_resolve(b.counts, b.offsets, d->E, layer, d->c, s);
@@ -184,12 +183,12 @@ int moe_device_decoder_step(moe_device_decoder_t* d, int layer, const void* x, i
       e = moe::launch_dev_fill(d->c, d->pool[layer], d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, s);
     if (e == hipSuccess)
       e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->c.n, d->c.work, items, T, d->slot_base,
-                                     d->slot_stride, d->H, d->I, hbuf, xg, b.y_perm, s);
+                                     d->slot_stride, d->H, d->I, hbuf, b.y_perm, s);
   } else if (e == hipSuccess) {
     // one pass: the hits run from their slots while the misses stream from the pool over the host link and
     // are written through into their slots
     e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->c.n, d->c.work, items, T, d->slot_base, d->slot_stride,
-                                   d->H, d->I, hbuf, xg, b.y_perm, s, d->c.n + 2, d->pool[layer], d->blob_stride);
+                                   d->H, d->I, hbuf, b.y_perm, s, d->c.n + 2, d->pool[layer], d->blob_stride);
   }
   if (e == hipSuccess)
     e = moe::launch_combine(b.y_perm, b.perm_pos, b.topk_w, T, d->k, d->H, out, out_dtype == MOE_DT_BF16, s);

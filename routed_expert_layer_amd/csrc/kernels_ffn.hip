@@ -45,7 +45,9 @@ struct DevWork {
   size_t pool_stride;
   __device__ __forceinline__ bool get(int i, int4& it) const {
     if (i >= *n) return false;
-    it = items[i];
+    const int4 v = items[i];  // the same item for the whole block: keep it in scalar registers
+    it = make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                   __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
     return true;
   }
   __device__ __forceinline__ const char* src(int i, const int4& it, const char* slot_base, size_t slot_stride,
@@ -61,6 +63,28 @@ struct DevWork {
 };
 
 __device__ __forceinline__ void st16(char* p, const u32x4_t& v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+
+// Write-through of a miss (its blob read over the host link and stored into its slot as the FFN uses it):
+// after the stores, wait until every memory operation of the wave has completed, before any loaded register
+// is used. The compiler's wait counts take the wave's loads and stores to complete in issue order; with loads
+// from host memory and stores to HBM, registers were read before their loads had returned (seen as NaN
+// outputs of the int4 miss path), and a full wait does not depend on that order.
+__device__ __forceinline__ void drain_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// The result of a chain of matrix-core products moved to vector registers (which waits for the chain), with no
+// instruction scheduled across that point.
+__device__ __forceinline__ void matrix_chain_done(f32x4_t& v) {
+  asm volatile("" : "+v"(v));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// A pointer every lane of the wave holds (a work item's blob) moved to scalar registers, as a buffer resource
+// needs.
+__device__ __forceinline__ char* uniform(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<char*>(((uint64_t)hi << 32) | lo);
+}
 
 // ---------------------------------------------------------------------------
 // fp32 weights: plain VALU kernels (small correctness configurations).
@@ -126,6 +150,7 @@ __device__ __forceinline__ f32x4_t bf16_wave_dot(const char* wp, char* fp, const
     if constexpr (WT) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) st16(fp + (size_t)(c + u) * 1024, a[u]);
+      drain_memory();
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) acc = mfma_bf16(a[u], b[u], acc);
@@ -133,7 +158,10 @@ __device__ __forceinline__ f32x4_t bf16_wave_dot(const char* wp, char* fp, const
   for (; c < c1; ++c) {
     const u32x4_t a = ld16_nt(wp + (size_t)c * 1024);
     const u32x4_t b = valid ? ld16(ar + c * 32) : u32x4_t{0u, 0u, 0u, 0u};
-    if constexpr (WT) st16(fp + (size_t)c * 1024, a);
+    if constexpr (WT) {
+      st16(fp + (size_t)c * 1024, a);
+      drain_memory();
+    }
     acc = mfma_bf16(a, b, acc);
   }
   return acc;
@@ -213,102 +241,118 @@ __global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// int4 decode kernels (x and the SwiGLU product in fp16, codes exact in fp16,
-// one fp16 scale per 128-row block applied to that block's partial sum).
+// int4 decode kernels (bf16 activations and SwiGLU product as in the bf16
+// path; codes enter bf16 matrix-core products exactly as 1 + n/16, and each
+// 128-row block's sum is formed as 16 t - 24 u in fp32 -- t the product with
+// the biased codes, u the block's sum of the activations -- times that
+// block's fp16 scale).
 // ---------------------------------------------------------------------------
 
-// Gathered activations, converted to fp16: xg[r, :] = fp16(x[perm_src[r], :]).
-template <typename W>
-__global__ __launch_bounds__(256) void gather_f16_kernel(const uint16_t* __restrict__ x,
-                                                         const int32_t* __restrict__ perm_src, const W wk,
-                                                         int H, uint16_t* __restrict__ xg) {
-  int4 it;
-  if (!wk.get(blockIdx.y, it)) return;
-  const int H8 = H / 8;
-  for (int idx = blockIdx.x * 256 + threadIdx.x; idx < it.z * H8; idx += gridDim.x * 256) {
-    const int m = idx / H8, c = idx - (idx / H8) * H8;
-    const u32x4_t v = ld16(x + (size_t)perm_src[it.y + m] * H + 8 * c);
-    u32x4_t o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float lo = __uint_as_float(v[p] << 16), hi = __uint_as_float(v[p] & 0xFFFF0000u);
-      o[p] = (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
-    }
-    *reinterpret_cast<u32x4_t*>(xg + (size_t)(it.y + m) * H + 8 * c) = o;
-  }
-}
-
-// One 128-wide K block of one 16-row tile: four fp16 matrix-core products of
-// the dequantised codes a with the activation fragments b, scaled by the tile
-// rows' block scales (four fp16 in sc0, sc1) and added to acc.
-__device__ __forceinline__ void int4_tile_mac(const u32x4_t& a, uint32_t sc0, uint32_t sc1, const u32x4_t (&b)[4],
-                                              f32x4_t& acc) {
-  f32x4_t t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) t = mfma_f16(int4x8_to_f16x8(a[j]), b[j], t);
-  acc[0] = fmaf(t[0], f16_bits_to_f32(sc0 & 0xFFFFu), acc[0]);
-  acc[1] = fmaf(t[1], f16_bits_to_f32(sc0 >> 16), acc[1]);
-  acc[2] = fmaf(t[2], f16_bits_to_f32(sc1 & 0xFFFFu), acc[2]);
-  acc[3] = fmaf(t[3], f16_bits_to_f32(sc1 >> 16), acc[3]);
-}
+// The registers of one 128-wide K block: activation fragments, and the codes
+// and the four rows' scales of each of the block's kR tiles.
+constexpr int kR = 4;
+struct Int4Stage {
+  u32x4_t b[4];
+  u32x4_t a[kR];
+  uint32_t sc0[kR], sc1[kR];
+};
 
 // Shared body of both int4 projections. A block owns kR consecutive 16-row
 // tiles of one expert; its four waves split K, and each wave applies every
 // activation fragment it loads to all kR tiles (one activation load per kR
-// KiB of codes). Partial sums meet in LDS; wave w finishes tile w.
-// act: fp16 activations [rows, K] (gathered x or h); the finished 16 x 16
+// KiB of codes). A wave keeps the next K block's loads in flight while it
+// works on the current one. Partial sums meet in LDS; wave w finishes tile w.
+// act_row(m): bf16 activations of row m of the group; the finished 16 x 16
 // tile sums go to `emit(tile, m, sum)`. With WT every code and scale loaded
 // is also stored at the same offset from qf_base / sf_base (the write-through
 // of a miss), after each K block's loads.
-constexpr int kR = 4;
-template <bool WT, typename Emit>
-__device__ __forceinline__ void int4_decode_tiles(const uint16_t* __restrict__ act, const int4 it, int K,
-                                                  const char* q_base, const char* s_base, char* qf_base,
-                                                  char* sf_base, int tile0, Emit emit) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+template <bool WT, typename Row, typename Emit>
+__device__ __forceinline__ void int4_decode_tiles(Row act_row, const int4 it, int K, const char* q_base,
+                                                  const char* s_base, char* qf_base, char* sf_base, int tile0,
+                                                  Emit emit) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int KG = K / 128;
   const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
   const int kq = (lane >> 4) * 8;
+  const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  // Codes and scales through buffer resources: one lane offset in a vector register, the (uniform) block
+  // offsets in scalar registers, so a wave's loads of two K blocks cost few address registers.
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(uniform(q_base), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(uniform(s_base), (short)0, -1, 0x00020000);
+  const int vq = lane * 16, vs = (lane >> 4) * 8;
   __shared__ f32x4_t red[4][kR][64];
   for (int m0 = 0; m0 < it.z; m0 += 16) {
     const int m = m0 + (lane & 15);
     const bool valid = m < it.z;
-    const uint16_t* ar = act + (size_t)(it.y + (valid ? m : 0)) * K + kq;
+    const uint16_t* ar = act_row(valid ? m : 0) + kq;
     f32x4_t acc[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int g = g0; g < g1; ++g) {
-      u32x4_t b[4];
+    // Lanes past the group read the group's first row: a token's column of a product depends only on its own
+    // activation column, and the columns of those lanes are never stored.
+    auto load = [&](int g, Int4Stage& st) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = valid ? ld16(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
-      u32x4_t a[kR];
-      uint32_t sc0[kR], sc1[kR];
+      for (int j = 0; j < 4; ++j) st.b[j] = ld16(ar + 128 * g + 32 * j);
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
-        const size_t blk = (size_t)(tile0 + r) * KG + g;
-        a[r] = ld16_nt(q_base + blk * 1024 + lane * 16);
+        const int blk = (tile0 + r) * KG + g;
+        st.a[r] = __builtin_amdgcn_raw_buffer_load_b128(rq, vq, blk * 1024, 2);  // non-temporal
         // The four fp16 scales are read as two 32-bit words and widened one by
         // one (a two-element fp16 vector view of the 64-bit load was
         // miscompiled into mixed-precision FMAs that all read the first word).
-        const uint32_t* sp = reinterpret_cast<const uint32_t*>(s_base + blk * 32 + (lane >> 4) * 8);
-        sc0[r] = sp[0];
-        sc1[r] = sp[1];
+        const u32x2_t sc = __builtin_amdgcn_raw_buffer_load_b64(rs, vs, blk * 32, 0);
+        st.sc0[r] = sc[0];
+        st.sc1[r] = sc[1];
       }
       if constexpr (WT) {  // codes by every lane, each 8-byte scale group by one lane
+        const __amdgpu_buffer_rsrc_t wq = __builtin_amdgcn_make_buffer_rsrc(uniform(qf_base), (short)0, -1,
+                                                                            0x00020000);
+        const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(uniform(sf_base), (short)0, -1,
+                                                                            0x00020000);
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
-          const size_t blk = (size_t)(tile0 + r) * KG + g;
-          st16(qf_base + blk * 1024 + lane * 16, a[r]);
+          const int blk = (tile0 + r) * KG + g;
+          __builtin_amdgcn_raw_buffer_store_b128(st.a[r], wq, vq, blk * 1024, 0);
           if ((lane & 15) == 0) {
-            uint32_t* sf = reinterpret_cast<uint32_t*>(sf_base + blk * 32 + (lane >> 4) * 8);
-            sf[0] = sc0[r];
-            sf[1] = sc1[r];
+            __builtin_amdgcn_raw_buffer_store_b32(st.sc0[r], ws, vs, blk * 32, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(st.sc1[r], ws, vs + 4, blk * 32, 0);
           }
         }
+        drain_memory();
       }
+    };
+    // Each chain of four dependent products is read out before the next chain starts (matrix_chain_done), so
+    // the first, independent product of a chain never waits in the matrix pipe behind the previous chain while
+    // the conversions that follow it rewrite its A-operand registers: with the chains back to back, the first
+    // tile's results came out wrong (seen on the miss path at K = 256, where a wave has one K block).
+    auto compute = [&](const Int4Stage& st) {
+      f32x4_t u = {0.f, 0.f, 0.f, 0.f};  // every row: the block's sum of this token's activations
 #pragma unroll
-      for (int r = 0; r < kR; ++r) int4_tile_mac(a[r], sc0[r], sc1[r], b, acc[r]);
+      for (int j = 0; j < 4; ++j) u = mfma_bf16(ones, st.b[j], u);
+      matrix_chain_done(u);
+      const float u24 = -24.f * u[0];
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        f32x4_t t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t = mfma_bf16(int4x8_to_bf16x8_biased(st.a[r][j]), st.b[j], t);
+        matrix_chain_done(t);
+        acc[r][0] = fmaf(fmaf(t[0], 16.f, u24), f16_bits_to_f32(st.sc0[r] & 0xFFFFu), acc[r][0]);
+        acc[r][1] = fmaf(fmaf(t[1], 16.f, u24), f16_bits_to_f32(st.sc0[r] >> 16), acc[r][1]);
+        acc[r][2] = fmaf(fmaf(t[2], 16.f, u24), f16_bits_to_f32(st.sc1[r] & 0xFFFFu), acc[r][2]);
+        acc[r][3] = fmaf(fmaf(t[3], 16.f, u24), f16_bits_to_f32(st.sc1[r] >> 16), acc[r][3]);
+      }
+    };
+    Int4Stage s0, s1;
+    int g = g0;
+    if (g < g1) load(g, s0);
+    for (; g + 1 < g1; g += 2) {
+      load(g + 1, s1);
+      compute(s0);
+      if (g + 2 < g1) load(g + 2, s0);
+      compute(s1);
     }
+    if (g < g1) compute(s0);
 #pragma unroll
     for (int r = 0; r < kR; ++r) red[wave][r][lane] = acc[r];
     __syncthreads();
@@ -321,7 +365,8 @@ __device__ __forceinline__ void int4_decode_tiles(const uint16_t* __restrict__ a
 }
 
 template <typename W>
-__global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restrict__ xg, const W wk,
+__global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ perm_src, const W wk,
                                                         const char* __restrict__ slot_base, size_t slot_stride,
                                                         size_t p1s_off, int H, int I, uint16_t* __restrict__ hbuf) {
   const int NB = I / 8 / kR;  // blocks per expert
@@ -331,16 +376,17 @@ __global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restri
   char* fill;
   const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   const int lane = threadIdx.x & 63;
+  const auto row = [&](int m) { return x + (size_t)perm_src[it.y + m] * H; };
   const auto emit = [&](int tile, int m, const f32x4_t& s) {
     const int i0 = 8 * tile + 2 * (lane >> 4);
     const uint32_t packed =
-        (uint32_t)f32_to_f16_bits(silu(s[0]) * s[1]) | ((uint32_t)f32_to_f16_bits(silu(s[2]) * s[3]) << 16);
+        (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
     *reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0) = packed;
   };
   if (fill)
-    int4_decode_tiles<true>(xg, it, H, blob, blob + p1s_off, fill, fill + p1s_off, tile0, emit);
+    int4_decode_tiles<true>(row, it, H, blob, blob + p1s_off, fill, fill + p1s_off, tile0, emit);
   else
-    int4_decode_tiles<false>(xg, it, H, blob, blob + p1s_off, nullptr, nullptr, tile0, emit);
+    int4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, tile0, emit);
 }
 
 template <typename W>
@@ -355,13 +401,14 @@ __global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restri
   char* fill;
   const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   const int lane = threadIdx.x & 63;
+  const auto row = [&](int m) { return hbuf + (size_t)(it.y + m) * I; };
   const auto emit = [&](int tile, int m, const f32x4_t& s) {
     *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
   };
   if (fill)
-    int4_decode_tiles<true>(hbuf, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0, emit);
+    int4_decode_tiles<true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0, emit);
   else
-    int4_decode_tiles<false>(hbuf, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit);
+    int4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit);
 }
 
 // ---------------------------------------------------------------------------
@@ -426,6 +473,7 @@ __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, i
           st16(qf_base + blk * 1024 + lane * 16, a[r]);
           if (lane < 16) *reinterpret_cast<uint32_t*>(sf_base + blk * 64 + lane * 4) = sc[r];
         }
+        drain_memory();
       }
 #pragma unroll
       for (int r = 0; r < kR; ++r)
@@ -635,7 +683,7 @@ namespace {
 // count) with at most `max_rows` rows each.
 template <typename W>
 hipError_t decode_kernels(int wfmt, const void* x, const int32_t* perm_src, const W& wk, int n_items, int max_rows,
-                          const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y,
+                          const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
                           hipStream_t s) {
   const BlobLayout L = blob_layout(wfmt, H, I);
   if (wfmt == 0) {
@@ -669,14 +717,10 @@ hipError_t decode_kernels(int wfmt, const void* x, const int32_t* perm_src, cons
     return hipGetLastError();
   }
   // int4
-  hipLaunchKernelGGL(gather_f16_kernel<W>, dim3(4, n_items), dim3(256), 0, s, static_cast<const uint16_t*>(x), perm_src,
-                     wk, H, static_cast<uint16_t*>(xg));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(ffn1_decode_int4<W>, dim3(n_items * (I / 8 / kR)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(xg), wk, slot_base, slot_stride, L.p1s, H, I,
+                     static_cast<const uint16_t*>(x), perm_src, wk, slot_base, slot_stride, L.p1s, H, I,
                      static_cast<uint16_t*>(hbuf));
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(ffn2_decode_int4<W>, dim3(n_items * (H / 16 / kR)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(hbuf), wk, slot_base, slot_stride, L.p2, L.p2s, H, I, y);
@@ -686,22 +730,22 @@ hipError_t decode_kernels(int wfmt, const void* x, const int32_t* perm_src, cons
 }  // namespace
 
 hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, const WorkArgs& wa,
-                             const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y,
+                             const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
                              hipStream_t s) {
   if (wa.n == 0) return hipSuccess;
   int max_rows = 0;
   for (int i = 0; i < wa.n; ++i) max_rows = wa.item[i].z > max_rows ? wa.item[i].z : max_rows;
-  return decode_kernels(wfmt, x, perm_src, ArgWork{wa}, wa.n, max_rows, slot_base, slot_stride, H, I, hbuf, xg, y, s);
+  return decode_kernels(wfmt, x, perm_src, ArgWork{wa}, wa.n, max_rows, slot_base, slot_stride, H, I, hbuf, y, s);
 }
 
 hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
                                  const int4* items, int max_items, int max_rows, const char* slot_base,
-                                 size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y, hipStream_t s,
+                                 size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s,
                                  const int32_t* n_hit, const char* pool, size_t pool_stride) {
   if (max_items == 0) return hipSuccess;
   if (wfmt == 0 && pool != nullptr) return hipErrorInvalidValue;  // the fp32 kernels do not write through
   return decode_kernels(wfmt, x, perm_src, DevWork{n_items, items, n_hit, pool, pool_stride}, max_items, max_rows,
-                        slot_base, slot_stride, H, I, hbuf, xg, y, s);
+                        slot_base, slot_stride, H, I, hbuf, y, s);
 }
 
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,

@@ -57,14 +57,13 @@ unsigned long long* g_clock_sums = nullptr;
 __device__ inline const WorkArgs& table_of(const WorkArgs& w) { return w; }
 __device__ inline const GemmTable& table_of(const GemmTable* t) { return *t; }
 
+// One block tile (super-tile `sidx`, slot `w` in it) of the kernel below.
 template <int PHASE, int BM_T, typename Tab>
-__global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict__ bsrc,
-                                                        const int32_t* __restrict__ perm_src, const Tab tab,
-                                                        const char* __restrict__ slot_base, size_t slot_stride,
-                                                        size_t mat_off, int N, int K, int H, int I,
-                                                        uint16_t* __restrict__ hout, float* __restrict__ yout,
-                                                        const float* __restrict__ bias,
-                                                        unsigned long long* __restrict__ clock_sums) {
+__device__ __forceinline__ void gemm2_tile(const uint16_t* __restrict__ bsrc, const int32_t* __restrict__ perm_src,
+                                           const Tab& tab, const char* __restrict__ slot_base, size_t slot_stride,
+                                           size_t mat_off, int N, int K, int H, int I, uint16_t* __restrict__ hout,
+                                           float* __restrict__ yout, const float* __restrict__ bias,
+                                           unsigned long long* __restrict__ clock_sums, const int sidx, const int w) {
   const unsigned long long c_start = __builtin_amdgcn_s_memtime(), r_start = __builtin_amdgcn_s_memrealtime();
   constexpr int BN_T = 16;
   constexpr int NS = BM_T == 16 ? 4 : 6;       // LDS stages of 32 K; NS - 1 in flight
@@ -84,9 +83,6 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   // its L2 while they advance through K at the same pace.
   const auto& wa = table_of(tab);
   const int NTB = N / (16 * BN_T);
-  const int sidx = (int)((blockIdx.x >> 8) * 8 + (blockIdx.x & 7));  // super-tile
-  const int w = (int)((blockIdx.x >> 3) & 31);                        // slot in it
-  if (sidx >= wa.total_tiles) return;  // padding (uniform per block)
   int lo = 0, hi = wa.n - 1;           // item with tile_prefix[item] <= sidx < tile_prefix[item + 1]
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -101,7 +97,11 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   const int mt = (ls / ngroups) * GM + w / GN;
   const int nt = (ls % ngroups) * GN + (w % GN);
   if (mt * 16 * BM_T >= it.z) return;  // past the expert's last token tile
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the thread index passes through an empty asm so that nothing derived from it is hoisted out of the
+  // kernel's loop over tiles (live across the whole tile, it would cost registers)
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = tid >> 6, lane = tid & 63;
   const int wn = wave % WAVES_N, wm = wave / WAVES_N;
   const int KC = K / 32;
   const int ldb = (PHASE == 2) ? I : H;
@@ -288,6 +288,29 @@ __global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict_
   }
 }
 
+// Block b works on super-tiles (b / 256) * 8 + b % 8, then that plus 8 * (grid / 256), and so on, in slot
+// (b / 8) % 32 of each: with a grid of exactly the planned rounds every block does one tile; a smaller grid (a
+// multiple of 256) serves a work list planned on the device whose size the host does not know. Rounds keep the
+// blocks of a super-tile on one XCD (the block index modulo 8 selects it). Every exit is uniform per block.
+template <int PHASE, int BM_T, typename Tab>
+__global__ __launch_bounds__(512, 1) void gemm2_bf16(const uint16_t* __restrict__ bsrc,
+                                                        const int32_t* __restrict__ perm_src, const Tab tab,
+                                                        const char* __restrict__ slot_base, size_t slot_stride,
+                                                        size_t mat_off, int N, int K, int H, int I,
+                                                        uint16_t* __restrict__ hout, float* __restrict__ yout,
+                                                        const float* __restrict__ bias,
+                                                        unsigned long long* __restrict__ clock_sums) {
+  const int first = (int)(blockIdx.x >> 8), rounds = (int)(gridDim.x >> 8);
+  const int total = table_of(tab).total_tiles;
+  for (int r = first;; r += rounds) {
+    const int sidx = r * 8 + (int)(blockIdx.x & 7);
+    if (sidx >= total) break;
+    if (r != first) __syncthreads();  // every wave is done with the previous tile's LDS stages
+    gemm2_tile<PHASE, BM_T, Tab>(bsrc, perm_src, tab, slot_base, slot_stride, mat_off, N, K, H, I, hout, yout, bias,
+                                 clock_sums, sidx, (int)((blockIdx.x >> 3) & 31));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The same grouped GEMM with MXFP4 weights (FP4 codes, one E8M0 scale per 32
 // of K; the MOE_W_MXFP4 blob layout): 256 weight rows x 128 tokens per block
@@ -310,14 +333,13 @@ __device__ __forceinline__ u32x4_t mx_a_operand(uint32_t codes, uint32_t scale_b
   return r;
 }
 
+// One block tile (super-tile `sidx`, slot `w` in it) of the kernel below.
 template <int PHASE>
-__global__ __launch_bounds__(512, 1) void gemm_mxfp4(const uint16_t* __restrict__ bsrc,
-                                                      const int32_t* __restrict__ perm_src,
-                                                      const GemmTable* __restrict__ tab,
-                                                      const char* __restrict__ slot_base, size_t slot_stride,
-                                                      size_t code_off, size_t scale_off, int N, int K, int I,
-                                                      int H, uint16_t* __restrict__ hout, float* __restrict__ yout,
-                                                      unsigned long long* __restrict__ clock_sums) {
+__device__ __forceinline__ void mxfp4_tile(const uint16_t* __restrict__ bsrc, const int32_t* __restrict__ perm_src,
+                                           const GemmTable* __restrict__ tab, const char* __restrict__ slot_base,
+                                           size_t slot_stride, size_t code_off, size_t scale_off, int N, int K, int I,
+                                           int H, uint16_t* __restrict__ hout, float* __restrict__ yout,
+                                           unsigned long long* __restrict__ clock_sums, const int sidx, const int w) {
   const unsigned long long c_start = __builtin_amdgcn_s_memtime(), r_start = __builtin_amdgcn_s_memrealtime();
   constexpr int BN_T = 16, BM_T = 8, NS = 3, WN = 4, WM = 4, WAVES_N = 4, KSUB = 4;
   constexpr int CODE = BN_T * 1024, SCL = BN_T * 64, TOK = BM_T * KSUB * 1024;
@@ -327,9 +349,6 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp4(const uint16_t* __restrict_
 
   const GemmTable& wa = *tab;
   const int NTB = N / (16 * BN_T);
-  const int sidx = (int)((blockIdx.x >> 8) * 8 + (blockIdx.x & 7));
-  const int w = (int)((blockIdx.x >> 3) & 31);
-  if (sidx >= wa.total_tiles) return;
   int lo = 0, hi = wa.n - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -343,7 +362,11 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp4(const uint16_t* __restrict_
   const int mt = (ls / ngroups) * GM + w / GN;
   const int nt = (ls % ngroups) * GN + (w % GN);
   if (mt * 16 * BM_T >= it.z) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the thread index passes through an empty asm so that nothing derived from it is hoisted out of the
+  // kernel's loop over tiles (live across the whole tile, it would cost registers)
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int wave = tid >> 6, lane = tid & 63;
   const int wn = wave % WAVES_N, wm = wave / WAVES_N;
   const int KG = K / 128;  // stages
   const int KC = K / 32;
@@ -472,24 +495,52 @@ __global__ __launch_bounds__(512, 1) void gemm_mxfp4(const uint16_t* __restrict_
   }
 }
 
+// Rounds of super-tiles per block as for gemm2_bf16.
+template <int PHASE>
+__global__ __launch_bounds__(512, 1) void gemm_mxfp4(const uint16_t* __restrict__ bsrc,
+                                                      const int32_t* __restrict__ perm_src,
+                                                      const GemmTable* __restrict__ tab,
+                                                      const char* __restrict__ slot_base, size_t slot_stride,
+                                                      size_t code_off, size_t scale_off, int N, int K, int I,
+                                                      int H, uint16_t* __restrict__ hout, float* __restrict__ yout,
+                                                      unsigned long long* __restrict__ clock_sums) {
+  const int first = (int)(blockIdx.x >> 8), rounds = (int)(gridDim.x >> 8);
+  const int total = tab->total_tiles;
+  for (int r = first;; r += rounds) {
+    const int sidx = r * 8 + (int)(blockIdx.x & 7);
+    if (sidx >= total) break;
+    if (r != first) __syncthreads();  // every wave is done with the previous tile's LDS stages
+    mxfp4_tile<PHASE>(bsrc, perm_src, tab, slot_base, slot_stride, code_off, scale_off, N, K, I, H, hout, yout,
+                      clock_sums, sidx, (int)((blockIdx.x >> 3) & 31));
+  }
+}
+
 // Per expert, a super-tile is GM token tiles x GN weight tiles (GM*GN <= 32
 // block slots): GM = the smallest power of two covering its token tiles, at
 // most 8; GN = the largest power of two dividing the weight tiles that fits
 // beside it. Super-tiles per expert: ceil(m tiles / GM) x (n tiles / GN).
-// Fills item[i].w with GM | GN << 8 and tile_prefix; returns the total.
-int plan_supertiles(int4* item, int n, int* tile_prefix, int N, int tile_tokens) {
+// Returns that count for a group of `rows` rows (0 for none) and sets
+// shape = GM | GN << 8. Host planner and device planner use the same rule.
+__host__ __device__ inline int supertiles_of(int rows, int N, int tile_tokens, int& shape) {
   const int NTB = N / 256;
   int gn_div = 1;
   while (gn_div < 16 && NTB % (gn_div * 2) == 0) gn_div *= 2;
+  const int mtiles = (rows + tile_tokens - 1) / tile_tokens;
+  int GM = 8;
+  while (GM > 1 && GM / 2 >= mtiles) GM /= 2;
+  const int GN = (32 / GM) < gn_div ? 32 / GM : gn_div;
+  shape = GM | (GN << 8);
+  return rows > 0 ? (mtiles + GM - 1) / GM * (NTB / GN) : 0;
+}
+
+// Fills item[i].w with GM | GN << 8 and tile_prefix; returns the total.
+int plan_supertiles(int4* item, int n, int* tile_prefix, int N, int tile_tokens) {
   int tot = 0;
   for (int i = 0; i < n; ++i) {
     tile_prefix[i] = tot;
-    const int mtiles = (item[i].z + tile_tokens - 1) / tile_tokens;
-    int GM = 8;
-    while (GM > 1 && GM / 2 >= mtiles) GM /= 2;
-    const int GN = (32 / GM) < gn_div ? 32 / GM : gn_div;
-    item[i].w = GM | (GN << 8);
-    tot += (mtiles + GM - 1) / GM * (NTB / GN);
+    int shape = 0;
+    tot += supertiles_of(item[i].z, N, tile_tokens, shape);
+    item[i].w = shape;
   }
   tile_prefix[n] = tot;
   return tot;
@@ -556,6 +607,83 @@ hipError_t plan_and_upload(const int4* items, int n, int H, int I, int tile_toke
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Device planner of the grouped GEMM's work list: one block, thread e for
+// expert e (E <= 1024). Expert e has counts[e] rows from offsets[e] of the
+// grouped layout and its blob at slot slot_of[e] (slot_of NULL: slot e).
+// Groups go to part 0 when they have more than `split` rows, to part 1 when
+// they have 1..split rows; for each part and projection (N1 = gate/up rows,
+// N2 = down rows) the items are written in ascending expert order with the
+// super-tile prefix sums of supertiles_of, as the host planner writes them.
+// A group that would reach past row `rows_max` or whose slot lies outside
+// [0, n_slots) is left out (its rows are not computed).
+__global__ __launch_bounds__(1024) void plan_tables_kernel(const int32_t* __restrict__ counts,
+                                                           const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ slot_of, int E, int n_slots,
+                                                           int rows_max, int N1, int N2, int split, int tt0, int tt1,
+                                                           char* __restrict__ tables) {
+  constexpr int NV = 6;  // member of part 0, part 1; super-tiles (part 0, N1), (0, N2), (1, N1), (1, N2)
+  __shared__ int wave_tot[16][NV];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  int rows = 0, begin = 0, slot = 0;
+  if (e < E) {
+    rows = counts[e];
+    begin = offsets[e];
+    slot = slot_of ? slot_of[e] : e;
+    if (rows < 0 || begin < 0 || (long long)begin + rows > rows_max || slot < 0 || slot >= n_slots) rows = 0;
+  }
+  const int part = rows > split ? 0 : (rows > 0 ? 1 : -1);
+  int shape[2][2] = {{0, 0}, {0, 0}};
+  int v[NV] = {part == 0, part == 1, 0, 0, 0, 0};
+  if (part >= 0) {
+    const int tt = part == 0 ? tt0 : tt1;
+    v[2 + 2 * part] = supertiles_of(rows, N1, tt, shape[part][0]);
+    v[3 + 2 * part] = supertiles_of(rows, N2, tt, shape[part][1]);
+  }
+  int inc[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    int x = v[i];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    inc[i] = x;
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) wave_tot[wave][i] = inc[i];
+  }
+  __syncthreads();
+  int ex[NV], tot[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    int before = 0, all = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      if (w < wave) before += wave_tot[w][i];
+      all += wave_tot[w][i];
+    }
+    ex[i] = before + inc[i] - v[i];
+    tot[i] = all;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+      GemmTable* t = reinterpret_cast<GemmTable*>(tables + (2 * p + ph) * kTableBytes);
+      if (part == p) {
+        t->item[ex[p]] = make_int4(slot, begin, rows, shape[p][ph]);
+        t->tile_prefix[ex[p]] = ex[2 + 2 * p + ph];
+      }
+      if (e == 0) {
+        t->n = tot[p];
+        t->total_tiles = tot[2 + 2 * p + ph];
+        t->tile_prefix[tot[p]] = tot[2 + 2 * p + ph];
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -631,6 +759,55 @@ hipError_t launch_ffn_prefill_mxfp4(const void* x, const int32_t* perm_src, cons
     hipLaunchKernelGGL(gemm_mxfp4<2>, dim3(supertile_blocks(tot[1])), dim3(512), 0, s, hb, perm_src,
                        (const GemmTable*)tab[1], slot_base, slot_stride, L.p2, L.p2s, H, I, I, H, hb, y,
                        g_clock_sums);
+  return hipGetLastError();
+}
+
+bool grouped_supported(int wfmt, int H, int I) {
+  if (wfmt == 1) return gemm2_supported(2 * I, H) && gemm2_supported(H, I);
+  if (wfmt == 3) return prefill_mxfp4_supported(H, I);
+  return false;
+}
+
+// Both projections of every expert with rows, the work list planned on the
+// device from counts and offsets (no host synchronisation): bf16 weights in
+// the two tile sizes of launch_ffn_prefill2, MXFP4 weights in 128-token tiles.
+// Each GEMM launch is one round of 256 blocks (one per CU) that loops over
+// the super-tiles the planner wrote.
+hipError_t launch_ffn_grouped(int wfmt, const void* x, const int32_t* perm_src, const int32_t* counts,
+                              const int32_t* offsets, const int32_t* slot_of, int E, int n_slots, int rows_max,
+                              const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
+                              void* tables, hipStream_t s) {
+  if (E < 1 || E > kTableItems || !grouped_supported(wfmt, H, I)) return hipErrorInvalidValue;
+  const bool mx = wfmt == 3;
+  char* tb = static_cast<char*>(tables);
+  hipLaunchKernelGGL(plan_tables_kernel, dim3(1), dim3((E + 63) / 64 * 64), 0, s, counts, offsets, slot_of, E,
+                     n_slots, rows_max, 2 * I, H, mx ? 0 : 256, mx ? 128 : 256, 128, tb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const GemmTable* tab[2][2];
+  for (int p = 0; p < 2; ++p)
+    for (int ph = 0; ph < 2; ++ph) tab[p][ph] = reinterpret_cast<const GemmTable*>(tb + (2 * p + ph) * kTableBytes);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  uint16_t* hb = static_cast<uint16_t*>(hbuf);
+  const dim3 grid(256), block(512);
+  if (mx) {
+    // split 0 puts every group with rows into part 0, planned with 128-token tiles
+    const BlobLayout L = blob_layout(3, H, I);
+    hipLaunchKernelGGL(gemm_mxfp4<1>, grid, block, 0, s, xb, perm_src, tab[0][0], slot_base, slot_stride, L.p1,
+                       L.p1s, 2 * I, H, I, H, hb, y, g_clock_sums);
+    hipLaunchKernelGGL(gemm_mxfp4<2>, grid, block, 0, s, hb, perm_src, tab[0][1], slot_base, slot_stride, L.p2,
+                       L.p2s, H, I, I, H, hb, y, g_clock_sums);
+    return hipGetLastError();
+  }
+  const BlobLayout L = blob_layout(1, H, I);
+  hipLaunchKernelGGL((gemm2_bf16<1, 16, const GemmTable*>), grid, block, 0, s, xb, perm_src, tab[0][0], slot_base,
+                     slot_stride, L.p1, 2 * I, H, H, I, hb, y, nullptr, g_clock_sums);
+  hipLaunchKernelGGL((gemm2_bf16<1, 8, const GemmTable*>), grid, block, 0, s, xb, perm_src, tab[1][0], slot_base,
+                     slot_stride, L.p1, 2 * I, H, H, I, hb, y, nullptr, g_clock_sums);
+  hipLaunchKernelGGL((gemm2_bf16<2, 16, const GemmTable*>), grid, block, 0, s, hb, perm_src, tab[0][1], slot_base,
+                     slot_stride, L.p2, H, I, H, I, hb, y, nullptr, g_clock_sums);
+  hipLaunchKernelGGL((gemm2_bf16<2, 8, const GemmTable*>), grid, block, 0, s, hb, perm_src, tab[1][1], slot_base,
+                     slot_stride, L.p2, H, I, H, I, hb, y, nullptr, g_clock_sums);
   return hipGetLastError();
 }
 

@@ -117,7 +117,7 @@ hipError_t launch_combine(const float* y_perm, const int32_t* perm_pos, const fl
 // FFN: decode (matrix-vector) kernels for groups of <= 16*? rows, prefill GEMM otherwise.
 hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, const WorkArgs& wa,
                              const char* slot_base, size_t slot_stride, int H, int I,
-                             void* hbuf, void* xg, float* y, hipStream_t s);
+                             void* hbuf, float* y, hipStream_t s);
 // The same kernels with the work list in device memory: *n_items items at
 // `items` (device), at most max_items of them with at most max_rows rows
 // each; launch shapes depend only on max_items and max_rows. With `pool`
@@ -125,7 +125,7 @@ hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, c
 // from pool + expert * pool_stride and written through into their slot.
 hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
                                  const int4* items, int max_items, int max_rows, const char* slot_base,
-                                 size_t slot_stride, int H, int I, void* hbuf, void* xg, float* y, hipStream_t s,
+                                 size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s,
                                  const int32_t* n_hit = nullptr, const char* pool = nullptr,
                                  size_t pool_stride = 0);
 // 128 x 128-tile fallback GEMM for shapes the large-tile GEMM does not take.
@@ -159,6 +159,19 @@ bool prefill_mxfp4_supported(int H, int I);
 hipError_t launch_ffn_prefill_mxfp4(const void* x, const int32_t* perm_src, const int4* items, int n,
                                     const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
                                     void* tables, hipStream_t s);
+// Shapes the device-planned grouped GEMM takes: bf16 with 2I and H multiples
+// of 256 (I a multiple of 32), MXFP4 as prefill_mxfp4_supported.
+bool grouped_supported(int wfmt, int H, int I);
+// Both projections of every expert e of 0..E-1 with counts[e] > 0 rows at
+// offsets[e] of the grouped layout (device arrays, e.g. moe_route's), blob at
+// slot slot_of[e] (device, NULL: e) of slot_base; the work list is planned on
+// the device into the four GemmTables at `tables`, so nothing waits for the
+// GPU. Groups reaching past rows_max or with a slot outside [0, n_slots) are
+// skipped.
+hipError_t launch_ffn_grouped(int wfmt, const void* x, const int32_t* perm_src, const int32_t* counts,
+                              const int32_t* offsets, const int32_t* slot_of, int E, int n_slots, int rows_max,
+                              const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
+                              void* tables, hipStream_t s);
 int router_gemm2_splits(int T, int H, int E);
 hipError_t launch_router_gemm2(const void* x, const void* wrt, int T, int H, int E, float* partial, int nsplit,
                                hipStream_t s);

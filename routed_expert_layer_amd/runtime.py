@@ -113,6 +113,7 @@ class RouteBuffers:
         self.perm_pos = torch.empty((T, k), **i32)
         self.ws = torch.empty(L.moe_route_workspace_size(T, H, E, k), dtype=torch.uint8, device=device)
         self.counts_host = torch.empty(E, dtype=torch.int32, pin_memory=True)
+        self.offsets_host = torch.empty(E + 1, dtype=torch.int32, pin_memory=True)
 
     def route(self, x, Wr, bias, stream=None):
         T = x.shape[0]
@@ -122,23 +123,27 @@ class RouteBuffers:
                     self.perm_pos[:T], self.ws, stream)
 
     def fetch_counts(self, stream=None):
-        """Device-to-host copy of the per-expert counts; waits for it (the one sync point)."""
+        """Device-to-host copies of the per-expert counts and offsets the routing kernels wrote; waits for them."""
         s = stream or torch.cuda.current_stream()
         with torch.cuda.stream(s):
             self.counts_host.copy_(self.counts, non_blocking=True)
+            self.offsets_host.copy_(self.offsets, non_blocking=True)
         s.synchronize()
-        c = self.counts_host.numpy().astype(np.int64)
-        off = np.zeros(len(c) + 1, np.int64)
-        np.cumsum(c, out=off[1:])
-        return c, off
+        return self.counts_host.numpy().astype(np.int64), self.offsets_host.numpy().astype(np.int64)
+
+    def buffer_dict(self, y_perm, ffn_ws):
+        """The device buffers of a layer call (DecoderBuffers field names)."""
+        return dict(topk_idx=self.topk_idx, topk_w=self.topk_w, logits=self.logits, counts=self.counts,
+                    offsets=self.offsets, perm_src=self.perm_src, perm_pos=self.perm_pos, y_perm=y_perm,
+                    route_ws=self.ws, ffn_ws=ffn_ws)
 
 
 class DecodeLayer:
-    """Decode path: route -> host LRU -> fills -> grouped FFN -> combine, for one cache."""
+    """Decode path: route -> host LRU -> fills -> grouped FFN -> combine, for one cache, one call per layer-step
+    through the library's decode driver (moe_decoder_step)."""
 
-    def __init__(self, store, n_slots, T, k, act, device="cuda", keep_logits=False, native=True):
+    def __init__(self, store, n_slots, T, k, act, device="cuda", keep_logits=False):
         self.store, self.S, self.k = store, n_slots, k
-        self.native = native
         self.H, self.I, self.E = store.H, store.I, store.E
         self.act = act
         self.rb = RouteBuffers(T, self.H, self.E, k, device, keep_logits)
@@ -150,25 +155,18 @@ class DecodeLayer:
                                   device=device)
         self.out = torch.empty((T, self.H), dtype=torch.float32, device=device)
         self.fill_stream = torch.cuda.Stream(device=device)
-        self._fills = 0
-        self.dec = None
-        if native:
-            rb = self.rb
-            bufs = dict(topk_idx=rb.topk_idx, topk_w=rb.topk_w, logits=rb.logits, counts=rb.counts,
-                        offsets=rb.offsets, perm_src=rb.perm_src, perm_pos=rb.perm_pos, y_perm=self.y_perm,
-                        route_ws=rb.ws, ffn_ws=self.ffn_ws)
-            self.dec = L.MoeDecoder(self.cache, T, self.H, self.I, self.E, k,
-                                    L.MOE_DT_BF16 if act == "bf16" else L.MOE_DT_F32, store.wfmt, store.layer_ptrs,
-                                    store.stride, self.slots, store.stride, bufs)
+        self.dec = L.MoeDecoder(self.cache, T, self.H, self.I, self.E, k,
+                                L.MOE_DT_BF16 if act == "bf16" else L.MOE_DT_F32, store.wfmt, store.layer_ptrs,
+                                store.stride, self.slots, store.stride, self.rb.buffer_dict(self.y_perm, self.ffn_ws))
 
     @property
     def n_fills(self):
-        return L.moe_decoder_fills(self.dec) if self.dec is not None else self._fills
+        return L.moe_decoder_fills(self.dec)
 
     @property
     def cpu_runs(self):
         """Misses executed on the CPU so far."""
-        return L.moe_decoder_cpu_runs(self.dec) if self.dec is not None else 0
+        return L.moe_decoder_cpu_runs(self.dec)
 
     def resize(self, n_slots, stream=None):
         """Change the cache to n_slots slots between layer-steps (the most recently used entries stay); a larger
@@ -177,21 +175,7 @@ class DecodeLayer:
         new = None
         if n_slots > self.S:
             new = torch.empty(n_slots * self.store.stride, dtype=torch.uint8, device=self.slots.device)
-        if self.dec is not None:
-            L.moe_decoder_resize(self.dec, n_slots, new, s)
-        else:
-            old = self.slots
-            moves = L.moe_cache_resize(self.cache, n_slots)
-            st = self.store.stride
-            with torch.cuda.stream(s):
-                dst = old if new is None else new
-                if new is not None:
-                    for key in range(self.store.L * self.E):
-                        sl = L.moe_cache_slot_of(self.cache, key)
-                        if sl >= 0 and not any(m[0] == key for m in moves):
-                            dst[sl * st:(sl + 1) * st].copy_(old[sl * st:(sl + 1) * st])
-                for key, a, b in moves:
-                    dst[b * st:(b + 1) * st].copy_(old[a * st:(a + 1) * st])
+        L.moe_decoder_resize(self.dec, n_slots, new, s)
         if new is not None:
             self.keep_old = self.slots  # read by copies on the stream
             self.slots = new
@@ -200,8 +184,6 @@ class DecodeLayer:
     def set_split(self, rate_gpu, rate_cpu):
         """Divide misses between GPU fills and CPU execution in the ratio of the rates (e.g. MB/s of pinned
         fills and of the host expert kernel, see measure_rates); rate_cpu = 0 fills every miss."""
-        if rate_cpu and self.dec is None:
-            raise ValueError("CPU execution of misses runs in the native decode driver (native=True)")
         L.moe_cache_set_split(self.cache, rate_gpu, rate_cpu)
 
     def measure_rates(self, layer=0, n=4, rows=None):
@@ -232,44 +214,11 @@ class DecodeLayer:
         cpu_mbs = n * store.blob / (time.perf_counter() - t0) / 1e6
         return fill_mbs, cpu_mbs
 
-    def algorithmic_bytes(self, work):
-        """Bytes the expert FFN must move for a work list: each listed expert's
-        weights once, plus its rows of x (read), the SwiGLU product (write and
-        read) and y (write)."""
-        a = 2 if self.act == "bf16" else 4
-        h = 2 if self.store.wfmt != L.MOE_W_F32 else 4
-        rows = int(np.sum(work[:, 3]))
-        return len(work) * self.store.blob + rows * (self.H * a + 2 * self.I * h + self.H * 4)
-
-    def step(self, step, layer, x, Wr, bias, stream=None, timer=None):
-        """One layer-step. `timer`, if given, gets timer.begin(stream) and
-        timer.end(stream, algorithmic_bytes) around every expert-FFN call."""
+    def step(self, step, layer, x, Wr, bias, stream=None):
+        """One layer-step (blocks until the step's counts reach the host; the rest is enqueued on the stream)."""
         s = stream or torch.cuda.current_stream()
         T = x.shape[0]
-        if self.dec is not None:
-            L.moe_decoder_step(self.dec, step, layer, x, Wr, bias, self.out[:T], s)
-            return self.out[:T]
-        rb = self.rb
-        rb.route(x, Wr, bias, s)
-        counts, off = rb.fetch_counts(s)
-        experts = np.nonzero(counts)[0].astype(np.int32)
-        we, wslot, wwave, misses, n_waves = L.cache_resolve(self.cache, step, layer, experts)
-        for w in range(n_waves):
-            m = misses[misses[:, 3] == w]
-            if len(m):
-                L.cache_fill_async(self.cache, m, self.store.layer_ptrs, self.store.stride, self.store.blob,
-                                   self.slots, self.store.stride, self.fill_stream, s)
-                self._fills += len(m)
-            sel = wwave == w
-            e = we[sel]
-            work = np.stack([e, wslot[sel], off[e], counts[e]], axis=1).astype(np.int32)
-            if timer is not None:
-                timer.begin(s)
-            L.moe_ffn(x, rb.perm_src, work, self.slots, self.store.stride, self.store.wfmt, self.H, self.I,
-                      self.y_perm, self.ffn_ws, L.MOE_FFN_AUTO, s)
-            if timer is not None:
-                timer.end(s, self.algorithmic_bytes(work))
-        L.moe_combine(self.y_perm, rb.perm_pos[:T], rb.topk_w[:T], self.out[:T], s)
+        L.moe_decoder_step(self.dec, step, layer, x, Wr, bias, self.out[:T], s)
         return self.out[:T]
 
     def trace(self):
@@ -348,32 +297,39 @@ class DeviceDecodeLayer:
 
 
 class PrefillLayer:
-    """Prefill path over a layer whose experts are all resident (blob of expert e at base + e*stride)."""
+    """Prefill path over a layer whose experts are all resident (blob of expert e at base + e*stride): one
+    moe_prefill_layer call enqueues routing, the grouped GEMM over the work list planned on the GPU and the
+    combine; nothing waits for the GPU."""
 
-    def __init__(self, H, I, E, k, T, stride, device="cuda", keep_logits=False, mode=L.MOE_FFN_AUTO,
-                 wfmt=L.MOE_W_BF16):
-        self.H, self.I, self.E, self.k, self.stride, self.mode = H, I, E, k, stride, mode
+    def __init__(self, H, I, E, k, T, stride, device="cuda", keep_logits=False, wfmt=L.MOE_W_BF16):
+        self.H, self.I, self.E, self.k, self.stride, self.wfmt = H, I, E, k, stride, wfmt
         self.rb = RouteBuffers(T, H, E, k, device, keep_logits)
         rows = T * k
         self.y_perm = torch.empty((max(rows, 1), H), dtype=torch.float32, device=device)
         self.ffn_ws = torch.empty(L.moe_ffn_workspace_size(rows, H, I, wfmt), dtype=torch.uint8, device=device)
         self.out = torch.empty((T, H), dtype=torch.float32, device=device)
-        self.last_counts = None
+        self.bufs = L.decoder_buffers(self.rb.buffer_dict(self.y_perm, self.ffn_ws))
 
-    def forward(self, x, Wr, bias, layer_base, wfmt=L.MOE_W_BF16, stream=None, timer=None):
+    def forward(self, x, Wr, bias, layer_base, stream=None, timer=None):
+        """Enqueue the layer on the stream; returns the output tensor (valid once the stream reaches it).
+        With `timer`, the same three steps are enqueued as separate calls (moe_route, moe_ffn_grouped,
+        moe_combine) and timer.begin/end(stream, expert FLOPs) bracket the grouped FFN."""
         s = stream or torch.cuda.current_stream()
         T = x.shape[0]
         rb = self.rb
+        if timer is None:
+            L.moe_prefill_layer(x, Wr, bias, self.k, self.I, self.wfmt, layer_base, self.stride, self.bufs,
+                                self.out[:T], s)
+            return self.out[:T]
         rb.route(x, Wr, bias, s)
-        counts, off = rb.fetch_counts(s)
-        self.last_counts = counts
-        e = np.nonzero(counts)[0]
-        work = np.stack([e, e, off[e], counts[e]], axis=1).astype(np.int32)
-        if timer is not None:
-            timer.begin(s)
-        L.moe_ffn(x, rb.perm_src, work, layer_base, self.stride, wfmt, self.H, self.I, self.y_perm, self.ffn_ws,
-                  self.mode, s)
-        if timer is not None:
-            timer.end(s, 6.0 * self.H * self.I * int(counts.sum()))  # expert FLOPs of the routed pairs
+        timer.begin(s)
+        self.ffn(x, layer_base, T, s)
+        timer.end(s, 6.0 * self.H * self.I * T * self.k)  # expert FLOPs of the T*k routed pairs
         L.moe_combine(self.y_perm, rb.perm_pos[:T], rb.topk_w[:T], self.out[:T], s)
         return self.out[:T]
+
+    def ffn(self, x, layer_base, T=None, stream=None):
+        """The grouped expert FFN alone on the routing the buffers hold."""
+        T = x.shape[0] if T is None else T
+        L.moe_ffn_grouped(x, self.rb.perm_src, self.rb.counts, self.rb.offsets, None, self.E, T * self.k,
+                          layer_base, self.stride, self.wfmt, self.H, self.I, self.y_perm, self.ffn_ws, stream)

@@ -16,6 +16,7 @@ import oracle
 REL_L2 = 1e-2
 MAX_ABS_RMS = 5e-2
 W_ATOL = 1e-5
+FLAG_GAP = 1e-4
 
 
 def np64(t):
@@ -44,11 +45,25 @@ def check_close(got, ref, what="", rel_l2=REL_L2, max_abs_rms=MAX_ABS_RMS):
 def check_routing(gpu_idx, gpu_w, logits64, k):
     """Sets equal on unflagged tokens; GPU weights match the fp64 softmax over the GPU's own set."""
     gpu_idx = np.asarray(gpu_idx, dtype=np.int64)
+    T, E = logits64.shape
+    assert gpu_idx.shape == (T, k), f"selection shape {gpu_idx.shape} != {(T, k)}"
+    assert np.all((gpu_idx >= 0) & (gpu_idx < E)), "expert index out of range"
+    if T:
+        srt = np.sort(gpu_idx, axis=1)
+        assert np.all(np.diff(srt, axis=1) > 0), "a token selected the same expert twice"
     ref_idx = oracle.topk_select(logits64, k)
     flags = oracle.topk_flags(logits64, k)
     same = np.array([set(a) == set(b) for a, b in zip(gpu_idx.tolist(), ref_idx.tolist())], dtype=bool)
     bad = np.nonzero(~same & ~flags)[0]
     assert len(bad) == 0, f"top-k sets differ on {len(bad)} unflagged tokens, e.g. {bad[:5]}"
+    # a differing set on a flagged token must still be a top-k up to the flag's gap: every chosen logit at least
+    # every unchosen one minus the gap
+    for t in np.nonzero(~same)[0]:
+        chosen = np.zeros(E, dtype=bool)
+        chosen[gpu_idx[t]] = True
+        lo = logits64[t, chosen].min()
+        hi = logits64[t, ~chosen].max() if k < E else -np.inf
+        assert lo >= hi - FLAG_GAP, f"token {t}: selection is not a top-{k} (chosen min {lo}, unchosen max {hi})"
     # weights of the GPU's selection, in its order, from fp64 logits
     w_ref = oracle.topk_weights(logits64, gpu_idx)
     dw = np.max(np.abs(np.asarray(gpu_w, dtype=np.float64) - w_ref)) if gpu_w.size else 0.0

@@ -248,3 +248,39 @@ def test_binding_refuses_host_and_strided_tensors(L):
         L._ptr(np.zeros((4, 4), np.float32).T)
     assert L._dptr(None) is None and L._dptr(1 << 20) == 1 << 20
     assert L._ptr(y) == y.data_ptr()
+
+
+def test_grouped_ffn_and_prefill_layer_validation_without_gpu(L):
+    """moe_ffn_grouped and moe_prefill_layer refuse unsupported formats, shapes, sizes and null arguments
+    before any launch."""
+    lib = L._lib
+    ws = L.moe_ffn_workspace_size(4096 * 6, 4096, 2048, L.MOE_W_BF16)
+    assert ws > 0
+
+    def grouped(**kw):
+        a = dict(x=1, dt=L.MOE_DT_BF16, ps=1, c=1, o=1, so=None, E=256, ns=256, rows=4096 * 6, base=1,
+                 stride=1 << 26, wf=L.MOE_W_BF16, H=4096, I=2048, y=1, w=1, wsb=ws)
+        a.update(kw)
+        return lib.moe_ffn_grouped(a["x"], a["dt"], a["ps"], a["c"], a["o"], a["so"], a["E"], a["ns"], a["rows"],
+                                   a["base"], a["stride"], a["wf"], a["H"], a["I"], a["y"], a["w"], a["wsb"], None)
+
+    assert grouped(wf=L.MOE_W_INT4) == L.MOE_EINVAL          # no GEMM for int4 experts
+    assert grouped(wf=L.MOE_W_F32, dt=L.MOE_DT_F32) == L.MOE_EINVAL
+    assert grouped(H=4096 + 128) == L.MOE_EINVAL             # H not a multiple of 256
+    assert grouped(dt=L.MOE_DT_F32) == L.MOE_EINVAL          # bf16 activations only
+    assert grouped(E=0) == L.MOE_EINVAL and grouped(E=1025) == L.MOE_EINVAL
+    assert grouped(ns=0) == L.MOE_EINVAL and grouped(rows=-1) == L.MOE_EINVAL
+    assert grouped(c=None) == L.MOE_EINVAL and grouped(o=None) == L.MOE_EINVAL and grouped(x=None) == L.MOE_EINVAL
+    assert grouped(stride=1024) == L.MOE_EINVAL              # slot stride below one blob
+    assert grouped(wsb=ws - 1) == L.MOE_EINVAL
+    assert "workspace" in L.moe_last_error()
+    assert grouped(rows=0) == L.MOE_OK                       # nothing to compute, nothing launched
+    bufs = L.DecoderBuffers()
+    assert lib.moe_prefill_layer(1, L.MOE_DT_BF16, 1, None, 16, 4096, 256, 6, 2048, L.MOE_W_BF16, 1, 1 << 26,
+                                 None, 1, L.MOE_DT_F32, None) == L.MOE_EINVAL   # null buffer struct
+    assert lib.moe_prefill_layer(1, L.MOE_DT_BF16, 1, None, 16, 4096, 256, 6, 2048, L.MOE_W_INT4, 1, 1 << 26,
+                                 ctypes.byref(bufs), 1, L.MOE_DT_F32, None) == L.MOE_EINVAL
+    assert lib.moe_prefill_layer(1, L.MOE_DT_BF16, 1, None, 16, 4096, 256, 6, 2048, L.MOE_W_BF16, 1, 1 << 26,
+                                 ctypes.byref(bufs), 1, L.MOE_DT_F32, None) == L.MOE_EINVAL   # null y_perm
+    assert lib.moe_prefill_layer(1, L.MOE_DT_BF16, 1, None, -1, 4096, 256, 6, 2048, L.MOE_W_BF16, 1, 1 << 26,
+                                 ctypes.byref(bufs), 1, L.MOE_DT_F32, None) == L.MOE_EINVAL

@@ -59,9 +59,12 @@ def run_device(cfg, steps, out_check, check_all=False, trace_cap=1 << 16, resize
     try:
         dl = DeviceDecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev, trace_capacity=trace_cap)
         Wr = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
+        Wr64 = [np64(w) for w in Wr]
         sim = oracle.SharedLRU(cfg.S)
         experts64 = {}
         for step in range(steps):
+            if steps >= 128 and (step + 1) % 128 == 0:
+                print(f"  step {step + 1}/{steps}", flush=True)
             if resizes and step in resizes:
                 dl.resize(resizes[step])
                 sim.resize(resizes[step])
@@ -70,7 +73,7 @@ def run_device(cfg, steps, out_check, check_all=False, trace_cap=1 << 16, resize
                 x = gen.tokens(cfg, step, layer, dev)
                 out = dl.step(layer, x, Wr[layer], b)
                 torch.cuda.synchronize()
-                l64 = oracle.router_logits(x, Wr[layer], b)
+                l64 = oracle.router_logits(x, Wr64[layer], b)
                 idx = npi(dl.rb.topk_idx[:cfg.T])
                 check_routing(idx, np64(dl.rb.topk_w[:cfg.T]), l64, cfg.k)
                 counts, _, _, _ = check_permutation(idx, npi(dl.rb.counts), npi(dl.rb.offsets),
@@ -118,7 +121,13 @@ def test_device_small_mxfp4_all_outputs():
 @pytest.mark.timeout(600)
 def test_device_decode_bf16_full():
     cfg = CONFIGS["decode_bf16_h4096_e256"]
-    run_device(cfg, 384, {(s, 0) for s in (0, 1, 2, 63, 200, 383)})
+    run_device(cfg, cfg.steps, {(s, 0) for s in (0, 1, 2, 63, 200, 383, 1023)})
+
+
+@pytest.mark.timeout(900)
+def test_device_decode_int4_full():
+    cfg = CONFIGS["decode_int4_t8_l8"]
+    run_device(cfg, cfg.steps, {(0, 2), (130, 2), (255, 2)})
 
 
 def test_graph_replay_equals_eager():
@@ -170,16 +179,18 @@ def test_graph_replay_equals_eager():
 
 @pytest.mark.timeout(900)
 def test_stack48_device_graph():
-    """48-layer stack through one captured 48-layer graph: trace against the oracle and sampled outputs."""
+    """48-layer stack through one captured 48-layer graph, across the bias re-draw at step 128: trace against
+    the oracle and sampled outputs (some right after the re-draw)."""
     from routed_expert_layer_amd.runtime import DeviceDecodeLayer
     cfg = CONFIGS["stack48_bf16_h2048_e128"]
-    steps = 12
+    steps = 136
     r = np.random.default_rng(5)
     sample = {(int(s), int(l)) for s, l in zip(r.integers(0, steps, 5), r.integers(0, cfg.L, 5))}
+    sample |= {(128, 0), (129, 47)}
     print(f"stack48 graph: {steps} steps, output samples {sorted(sample)}", flush=True)
     store = make_store(cfg)
     try:
-        dl = DeviceDecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev, trace_capacity=1 << 16)
+        dl = DeviceDecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev, trace_capacity=1 << 18)
         Wr = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
         xs = [torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev) for _ in range(cfg.L)]
         bs = [torch.empty(cfg.E, dtype=torch.float32, device=dev) for _ in range(cfg.L)]
@@ -199,6 +210,7 @@ def test_stack48_device_graph():
             graph = DeviceDecodeLayer.capture(enqueue, cs)
         sim = oracle.SharedLRU(cfg.S)
         experts64 = {}
+        Wr64 = [np64(w) for w in Wr]
         for step in range(steps):
             for l in range(cfg.L):
                 xs[l].copy_(gen.tokens(cfg, step, l, dev))
@@ -206,9 +218,11 @@ def test_stack48_device_graph():
             torch.cuda.synchronize()
             DeviceDecodeLayer.replay(graph, cs)
             cs.synchronize()
+            if (step + 1) % 32 == 0:
+                print(f"  step {step + 1}/{steps}", flush=True)
             for l in range(cfg.L):
                 idx = npi(topk[l])
-                l64 = oracle.router_logits(xs[l], Wr[l], bs[l])
+                l64 = oracle.router_logits(xs[l], Wr64[l], bs[l])
                 check_routing(idx, np64(topw[l]), l64, cfg.k)
                 sim.resolve(step, l, cfg.E, np.unique(idx))
                 if (step, l) in sample:
@@ -216,7 +230,7 @@ def test_stack48_device_graph():
                     ref = oracle_out_rows(np64(xs[l]), idx, l64, list(range(cfg.T)), ge)
                     check_close(np64(outs[l]), ref, f"stack48 graph step {step} layer {l}")
         ref = oracle_trace(sim)
-        got = device_trace(dl, cfg.L, 1 << 16)
+        got = device_trace(dl, cfg.L, 1 << 18)
         assert np.array_equal(got, ref), "device cache trace differs from the oracle's LRU"
         print(f"  trace ok: {len(ref)} accesses, fills {dl.stats()[1]}", flush=True)
         graph.close()

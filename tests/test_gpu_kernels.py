@@ -183,6 +183,81 @@ def test_ffn_parity(L, name, wfmt, H, I, rows, mode):
         check_close(yg[a:b], ref, f"{name} expert {e}")
 
 
+GROUPED_CASES = [
+    # name, wfmt, H, I, rows per expert (seeded random when an int: that many experts of 0..maxrows rows)
+    ("bf16_ragged", "bf16", 512, 256, [130, 0, 1, 127, 128, 300, 17, 777, 256, 257, 40, 110, 276, 356, 200]),
+    ("bf16_many_rounds", "bf16", 256, 128, (200, 300)),
+    ("bf16_1000_experts", "bf16", 256, 128, (1000, 6)),
+    ("bf16_c3shape", "bf16", 2048, 768, [70, 3, 129, 513]),
+    ("mxfp4_ragged", "mxfp4", 512, 256, [130, 0, 1, 127, 128, 300, 17, 777, 40, 110, 276]),
+    ("mxfp4_many_rounds", "mxfp4", 256, 128, (120, 300)),
+]
+
+
+@pytest.mark.parametrize("name,wfmt,H,I,rows", GROUPED_CASES, ids=[c[0] for c in GROUPED_CASES])
+def test_grouped_ffn_parity(L, name, wfmt, H, I, rows):
+    """moe_ffn_grouped (work list planned on the GPU from device counts and offsets, GEMM blocks looping over
+    super-tiles) against the oracle per group; bit-identical to moe_ffn's host-planned GEMM on the same groups;
+    a group whose slot is out of range and a group reaching past rows_max are left untouched."""
+    if isinstance(rows, tuple):
+        n, mx = rows
+        rows = [int(v) for v in np.random.default_rng(n + mx).integers(0, mx + 1, size=n)]
+    E = len(rows)
+    print(f"grouped ffn case {name}: {wfmt} H={H} I={I} E={E} rows={sum(rows)}", flush=True)
+    cfg = cfg_like("tiny_f32_h256_e16", name=f"grp_{name}", H=H, I=I, E=E, act="bf16", wfmt=wfmt)
+    T = max(40, max(rows))
+    x = gen.tokens(cfg, 0, 0, dev, T=T)
+    r = np.random.default_rng(len(name) + E)
+    perm_src = np.concatenate([r.integers(0, T, size=n) for n in rows]).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    wf = L.MOE_W_MXFP4 if wfmt == "mxfp4" else L.MOE_W_BF16
+    stride = (L.moe_expert_bytes(wf, H, I) + 4095) // 4096 * 4096
+    slot_of = np.array([(e + 3) % E for e in range(E)], np.int32)  # non-identity slot mapping
+    nonempty = [e for e in range(E) if rows[e] > 0]
+    bad_slot = nonempty[len(nonempty) // 2]  # this group's slot is out of range: skipped
+    slot_of[bad_slot] = E
+    rows_total = int(off[-1])
+    last = nonempty[-1]
+    rows_max = rows_total - 1  # the last group reaches past rows_max: skipped
+    slots = torch.zeros(E * stride, dtype=torch.uint8, device=dev)
+    ex = {}
+    for e in nonempty:
+        w = gen.expert_mxfp4(cfg, 0, e, dev) if wfmt == "mxfp4" else gen.expert_weights(cfg, 0, e, dev)
+        ex[e] = w
+        if slot_of[e] >= E:
+            continue
+        dst = slots[int(slot_of[e]) * stride:]
+        if wfmt == "mxfp4":
+            L.moe_pack_expert(wf, H, I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"], w["s2"], dst)
+        else:
+            L.moe_pack_expert(wf, H, I, w[0], w[1], w[2], None, None, None, dst)
+    y = torch.full((rows_total, H), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(L.moe_ffn_workspace_size(rows_total, H, I, wf), dtype=torch.uint8, device=dev)
+    ps = torch.from_numpy(perm_src).to(dev)
+    counts_d = torch.tensor(rows, dtype=torch.int32, device=dev)
+    off_d = torch.from_numpy(off.astype(np.int32)).to(dev)
+    L.moe_ffn_grouped(x, ps, counts_d, off_d, torch.from_numpy(slot_of).to(dev), E, rows_max, slots, stride, wf,
+                      H, I, y, ws)
+    torch.cuda.synchronize()
+    yg = np64(y)
+    x64 = np64(x)
+    for e in nonempty:
+        a, b = off[e], off[e + 1]
+        if e in (bad_slot, last):
+            assert np.all(np.isnan(yg[a:b])), f"{name}: skipped group {e} was written"
+            continue
+        ref = oracle.swiglu_expert(x64[perm_src[a:b]], *_canon64(ex[e], wfmt))
+        check_close(yg[a:b], ref, f"{name} expert {e}")
+    # the host-planned GEMM on the same groups gives the same bits
+    work = np.array([[e, slot_of[e], off[e], rows[e]] for e in nonempty if e not in (bad_slot, last)], np.int32)
+    y2 = torch.full((rows_total, H), float("nan"), dtype=torch.float32, device=dev)
+    ws2 = torch.empty(L.moe_ffn_workspace_size(rows_total, H, I, wf), dtype=torch.uint8, device=dev)
+    L.moe_ffn(x, ps, work, slots, stride, wf, H, I, y2, ws2, L.MOE_FFN_PREFILL)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(y, nan=7.0), torch.nan_to_num(y2, nan=7.0)), \
+        f"{name}: device-planned and host-planned GEMMs differ"
+
+
 @pytest.mark.parametrize("wfmt", ["bf16", "mxfp4"])
 def test_clock_record_leaves_prefill_unchanged(L, wfmt):
     # the clock diagnostic only adds counters: the GEMM output is bit-identical with it on, the counters

@@ -71,26 +71,31 @@ def make_store(cfg):
 
 def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, split=None, cpu_check=(0, ()),
                resizes=None):
-    """Drive DecodeLayer over `steps` x all layers; check routing, trace, and sampled outputs.
+    """Drive a decode layer over `steps` x all layers; check routing, trace, and sampled outputs.
 
     native=True runs each layer-step through the library's decode driver
     (moe_decoder_step); native=False sequences the individual C-ABI calls from
-    Python. split=(rate_gpu, rate_cpu) divides misses between GPU fills and CPU
-    execution; cpu_check=(n, layers) also checks the outputs of the first n
-    layer-steps of those layers in which some miss ran on the CPU."""
+    Python (tests/sequenced.py). split=(rate_gpu, rate_cpu) divides misses
+    between GPU fills and CPU execution; cpu_check=(n, layers) also checks the
+    outputs of the first n layer-steps of those layers in which some miss ran
+    on the CPU."""
     from routed_expert_layer_amd.runtime import DecodeLayer
+    from tests.sequenced import SequencedDecodeLayer
     print(f"decode {cfg.name}: L={cfg.L} T={cfg.T} steps={steps} S={cfg.S} {cfg.wfmt} native={native} "
-          f"split={split}", flush=True)
+          f"split={split} output checks={len(out_check) if not check_all_outputs else 'all'}", flush=True)
     store = make_store(cfg)
     try:
-        dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev, keep_logits=True, native=native)
+        cls = DecodeLayer if native else SequencedDecodeLayer
+        dl = cls(store, cfg.S, cfg.T, cfg.k, cfg.act, dev, keep_logits=True)
         Wr = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
+        Wr64 = [np64(w) for w in Wr]
         sim = oracle.SharedLRU(cfg.S)
         if split:
             dl.set_split(*split)
             sim.set_split(*split)
         cpu_left, cpu_layers = cpu_check
         experts64 = {}
+        n_checked = 0
         for step in range(steps):
             if resizes and step in resizes:
                 dl.resize(resizes[step])
@@ -100,7 +105,7 @@ def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, spli
                 x = gen.tokens(cfg, step, layer, dev)
                 out = dl.step(step, layer, x, Wr[layer], b)
                 torch.cuda.synchronize()
-                l64 = oracle.router_logits(x, Wr[layer], b)
+                l64 = oracle.router_logits(x, Wr64[layer], b)
                 idx = npi(dl.rb.topk_idx[:cfg.T])
                 check_routing(idx, np64(dl.rb.topk_w[:cfg.T]), l64, cfg.k)
                 counts, _, _, _ = check_permutation(idx, npi(dl.rb.counts), npi(dl.rb.offsets),
@@ -114,6 +119,10 @@ def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, spli
                     ge = experts64.setdefault(layer, ExpertCache64(cfg, layer))
                     ref = oracle_out_rows(np64(x), idx, l64, list(range(cfg.T)), ge)
                     check_close(np64(out), ref, f"{cfg.name} step {step} layer {layer}")
+                    n_checked += 1
+            if steps >= 64 and (step + 1) % 64 == 0:
+                print(f"  step {step + 1}/{steps}: routing and grouping match, {n_checked} outputs checked",
+                      flush=True)
         trace = dl.trace()
         ref = np.array([[r.step, r.layer, r.key, r.hit, r.slot, r.victim, r.wave] for r in sim.trace], np.int64)
         assert trace.shape == ref.shape, f"trace length {trace.shape} vs {ref.shape}"
@@ -121,13 +130,28 @@ def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, spli
         hits = int(ref[:, 3].sum())
         cpu = int((ref[:, 4] < 0).sum())
         print(f"  trace ok: {len(ref)} accesses, hit rate {hits / max(len(ref), 1):.3f}, fills {dl.n_fills}, "
-              f"cpu runs {dl.cpu_runs}, waves>1 in {int((ref[:, 6] > 0).sum())} accesses", flush=True)
+              f"cpu runs {dl.cpu_runs}, waves>1 in {int((ref[:, 6] > 0).sum())} accesses, "
+              f"{n_checked} layer-step outputs checked", flush=True)
         assert dl.n_fills == len(ref) - hits - cpu
         assert dl.cpu_runs == cpu
         assert cpu_left <= 0 or not cpu_layers, "no CPU-run layer-step was output-checked"
         return ref
     finally:
         store.close()
+
+
+def epoch_samples(cfg, steps, per_epoch, seed):
+    """(step, layer) output checks: the first step of every epoch (the bias has just been re-drawn) and
+    `per_epoch` seeded steps inside each epoch, each at a seeded layer."""
+    r = np.random.default_rng(seed)
+    epoch = cfg.epoch or steps
+    out = set()
+    for e0 in range(0, steps, epoch):
+        e1 = min(e0 + epoch, steps)
+        out.add((e0, int(r.integers(0, cfg.L))))
+        for st in r.choice(np.arange(e0 + 1, e1), size=min(per_epoch, e1 - e0 - 1), replace=False):
+            out.add((int(st), int(r.integers(0, cfg.L))))
+    return out
 
 
 @pytest.mark.parametrize("native", [True, False], ids=["driver", "python"])
@@ -140,27 +164,31 @@ def test_tiny_fp32_all_steps(native):
 @pytest.mark.timeout(600)
 def test_decode_bf16_full():
     cfg = CONFIGS["decode_bf16_h4096_e256"]
-    run_decode(cfg, cfg.steps, {(s, 0) for s in (0, 1, 2, 63, 511, 1023)})
+    run_decode(cfg, cfg.steps, {(s, 0) for s in (0, 1, 2, 63, 255, 511, 767, 1023)})
 
 
-@pytest.mark.timeout(600)
-def test_stack48_bf16_cut():
+@pytest.mark.timeout(900)
+def test_stack48_bf16_full():
+    """All 512 steps of the 48-layer stack: routing, grouping and the whole cache trace bit-exact across the
+    bias re-draws at steps 128, 256 and 384, outputs sampled in every epoch (including its first step)."""
     cfg = CONFIGS["stack48_bf16_h2048_e128"]
-    r = np.random.default_rng(3)
-    sample = {(int(s), int(l)) for s, l in zip(r.integers(0, 40, 6), r.integers(0, 48, 6))}
-    run_decode(cfg, 40, sample)
+    sample = epoch_samples(cfg, cfg.steps, 2, seed=3)
+    ref = run_decode(cfg, cfg.steps, sample)
+    for e0 in range(0, cfg.steps, cfg.epoch):
+        ep = ref[(ref[:, 0] >= e0) & (ref[:, 0] < e0 + cfg.epoch)]
+        print(f"  epoch from step {e0}: miss rate {1 - ep[:, 3].mean():.4f} over {len(ep)} accesses", flush=True)
 
 
-@pytest.mark.timeout(600)
-def test_decode_int4_cut():
+@pytest.mark.timeout(900)
+def test_decode_int4_full():
     cfg = CONFIGS["decode_int4_t8_l8"]
-    run_decode(cfg, 48, {(0, 0), (5, 3), (47, 7)})
+    run_decode(cfg, cfg.steps, {(0, 0), (100, 0), (255, 0), (1, 5), (128, 5), (254, 5)})
 
 
-@pytest.mark.timeout(600)
-def test_decode_mxfp4_cut():
+@pytest.mark.timeout(900)
+def test_decode_mxfp4_full():
     cfg = CONFIGS["decode_mxfp4_t8_l8"]
-    run_decode(cfg, 48, {(0, 0), (5, 3), (47, 7)})
+    run_decode(cfg, cfg.steps, {(0, 0), (100, 0), (255, 0), (1, 5), (128, 5), (254, 5)})
 
 
 @pytest.mark.parametrize("native", [True, False], ids=["driver", "python"])
@@ -188,71 +216,122 @@ def test_stack48_split_cut():
     run_decode(cfg, 10, {(9, 47)}, split=(56, 165), cpu_check=(4, (0, 1, 2)))
 
 
-def _prefill_check(cfg, layer, pl, x, Wr, b, n_sample=24):
-    T = cfg.T
+def oracle_group_rows(x64, perm_src, offsets, rows, get_expert):
+    """Oracle rows of y_perm (row r = the output of r's expert for token perm_src[r]), evaluated one expert
+    at a time over all requested rows of its group. Returns (sorted unique rows, values)."""
+    rows = np.unique(np.asarray(rows, dtype=np.int64))
+    e_of = np.searchsorted(offsets, rows, side="right") - 1
+    y = np.zeros((len(rows), x64.shape[1]))
+    for e in np.unique(e_of):
+        sel = e_of == e
+        y[sel] = oracle.swiglu_expert(x64[perm_src[rows[sel]]], *get_expert(e))
+    return rows, y
+
+
+class LayerCopy:
+    """Device copies of one prefill layer's routing, y_perm and output, taken on the stream right after the
+    layer, so that later layers can reuse the buffers before anything is read on the host."""
+
+    def __init__(self, pl, T):
+        rb = pl.rb
+        self.idx, self.w = rb.topk_idx[:T].clone(), rb.topk_w[:T].clone()
+        self.counts, self.offsets = rb.counts.clone(), rb.offsets.clone()
+        self.perm_src, self.perm_pos = rb.perm_src[:T * pl.k].clone(), rb.perm_pos[:T].clone()
+        self.y_perm, self.out = pl.y_perm[:T * pl.k].clone(), pl.out[:T].clone()
+
+
+def prefill_check(cfg, layer, got, x, Wr, b, n_tokens=None, tile_rows=256):
+    """Routing and grouping of every token; outputs of every token (n_tokens None) or of a seeded sample of
+    n_tokens tokens plus the tokens of the largest and smallest groups; and the y_perm rows of the first and
+    last `tile_rows`-row tile of the largest group and of every row of one group whose size is not a multiple
+    of 128 (a partial tile). The oracle evaluates each expert once over all requested rows of its group."""
+    T, k = cfg.T, cfg.k
     l64 = oracle.router_logits(x, Wr, b)
-    idx = npi(pl.rb.topk_idx[:T])
-    check_routing(idx, np64(pl.rb.topk_w[:T]), l64, cfg.k)
-    check_permutation(idx, npi(pl.rb.counts), npi(pl.rb.offsets), npi(pl.rb.perm_src[:T * cfg.k]),
-                      npi(pl.rb.perm_pos[:T]), cfg.E)
-    r = np.random.default_rng(1000 + layer)
-    tokens = sorted(r.choice(T, n_sample, replace=False).tolist())
-    # include tokens of the smallest and largest groups
-    counts = npi(pl.rb.counts)
-    for e in (int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30)))):
-        tokens.append(int(np.nonzero((idx == e).any(1))[0][0]))
-    tokens = sorted(set(tokens))
-    ref = oracle_out_rows(np64(x), idx, l64, tokens, ExpertCache64(cfg, layer, cap=64))
-    check_close(np64(pl.out[tokens]), ref, f"{cfg.name} layer {layer}")
+    idx = npi(got.idx)
+    check_routing(idx, np64(got.w), l64, k)
+    counts, offsets, perm_pos, perm_src = check_permutation(idx, npi(got.counts), npi(got.offsets),
+                                                            npi(got.perm_src), npi(got.perm_pos), cfg.E)
+    if n_tokens is None:
+        tokens = np.arange(T)
+    else:
+        r = np.random.default_rng(1000 + layer)
+        tokens = list(r.choice(T, n_tokens, replace=False))
+        for e in (int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 1 << 30)))):
+            tokens.append(int(np.nonzero((idx == e).any(1))[0][0]))
+        tokens = np.unique(np.asarray(tokens))
+    rows = [perm_pos[tokens].reshape(-1)]
+    big = int(np.argmax(counts))
+    c0, o0 = int(counts[big]), int(offsets[big])
+    last = o0 + (c0 - 1) // tile_rows * tile_rows
+    rows += [np.arange(o0, o0 + min(tile_rows, c0)), np.arange(last, o0 + c0)]
+    partial = [e for e in np.argsort(-counts) if counts[e] > 0 and counts[e] % 128 != 0 and e != big]
+    if partial:
+        e = int(partial[0])
+        rows.append(np.arange(offsets[e], offsets[e] + counts[e]))
+    x64 = np64(x)
+    ge = ExpertCache64(cfg, layer, cap=8)
+    rr, yref = oracle_group_rows(x64, perm_src, offsets, np.concatenate(rows), ge)
+    y_got = np64(got.y_perm[torch.as_tensor(rr, device=got.y_perm.device)])
+    check_close(y_got, yref, f"{cfg.name} layer {layer}: {len(rr)} y_perm rows")
+    # outputs of the sampled tokens from the oracle's rows on the GPU's selection
+    pos = {int(r_): n for n, r_ in enumerate(rr)}
+    w = oracle.topk_weights(l64[tokens], idx[tokens])
+    out_ref = np.zeros((len(tokens), cfg.H))
+    for j in range(k):
+        out_ref += w[:, j:j + 1] * yref[[pos[int(p)] for p in perm_pos[tokens, j]]]
+    out_got = np64(got.out[torch.as_tensor(tokens, device=got.out.device)])
+    check_close(out_got, out_ref, f"{cfg.name} layer {layer}: {len(tokens)} token outputs")
+    part = f" + partial group of {counts[partial[0]]}" if partial else ""
+    print(f"  layer {layer}: {len(tokens)} tokens and {len(rr)} y_perm rows match (largest group {c0} rows, "
+          f"first and last tile{part}); active experts {int((counts > 0).sum())}", flush=True)
     return counts
 
 
-@pytest.mark.timeout(600)
-def test_prefill_4096_resident():
+def pack_resident(cfg, wf):
     from routed_expert_layer_amd import _lib as L
-    from routed_expert_layer_amd.runtime import PrefillLayer
-    cfg = CONFIGS["prefill_bf16_t4096_e256"]
-    blob = L.moe_expert_bytes(L.MOE_W_BF16, cfg.H, cfg.I)
+    blob = L.moe_expert_bytes(wf, cfg.H, cfg.I)
     stride = (blob + 4095) // 4096 * 4096
     buf = torch.empty(cfg.E * stride, dtype=torch.uint8, device=dev)
     for e in range(cfg.E):
-        W1, W3, W2 = gen.expert_weights(cfg, 0, e, dev)
-        L.moe_pack_expert(L.MOE_W_BF16, cfg.H, cfg.I, W1, W3, W2, None, None, None, buf[e * stride:])
-    pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, stride, dev, keep_logits=True)
+        if wf == L.MOE_W_MXFP4:
+            w = gen.expert_mxfp4(cfg, 0, e, dev)
+            L.moe_pack_expert(wf, cfg.H, cfg.I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"], w["s2"],
+                              buf[e * stride:])
+        else:
+            W1, W3, W2 = gen.expert_weights(cfg, 0, e, dev)
+            L.moe_pack_expert(wf, cfg.H, cfg.I, W1, W3, W2, None, None, None, buf[e * stride:])
+    return buf, stride
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["prefill_bf16_t4096_e256", "prefill_mxfp4_t4096_e256"])
+def test_prefill_4096_every_token(name):
+    """The 4096-token chunk with all experts resident, one moe_prefill_layer call: every token's output and
+    every y_perm row against the oracle."""
+    from routed_expert_layer_amd import _lib as L
+    from routed_expert_layer_amd.runtime import PrefillLayer
+    cfg = CONFIGS[name]
+    wf = L.MOE_W_MXFP4 if cfg.wfmt == "mxfp4" else L.MOE_W_BF16
+    print(f"prefill {cfg.name}: T={cfg.T}, every token", flush=True)
+    buf, stride = pack_resident(cfg, wf)
+    pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, stride, dev, keep_logits=True, wfmt=wf)
     Wr = gen.router_weight(cfg, 0, dev)
     b = gen.router_bias(cfg, 0, 0, dev)
     x = gen.tokens(cfg, 0, 0, dev)
     pl.forward(x, Wr, b, buf)
+    got = LayerCopy(pl, cfg.T)
     torch.cuda.synchronize()
-    counts = _prefill_check(cfg, 0, pl, x, Wr, b)
-    print(f"  tokens per expert: min {counts.min()} max {counts.max()} mean {counts.mean():.1f}", flush=True)
-
-
-@pytest.mark.timeout(600)
-def test_prefill_4096_mxfp4_resident():
-    from routed_expert_layer_amd import _lib as L
-    from routed_expert_layer_amd.runtime import PrefillLayer
-    cfg = CONFIGS["prefill_mxfp4_t4096_e256"]
-    blob = L.moe_expert_bytes(L.MOE_W_MXFP4, cfg.H, cfg.I)
-    stride = (blob + 4095) // 4096 * 4096
-    buf = torch.empty(cfg.E * stride, dtype=torch.uint8, device=dev)
-    for e in range(cfg.E):
-        w = gen.expert_mxfp4(cfg, 0, e, dev)
-        L.moe_pack_expert(L.MOE_W_MXFP4, cfg.H, cfg.I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"], w["s2"],
-                          buf[e * stride:])
-    pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, stride, dev, keep_logits=True, wfmt=L.MOE_W_MXFP4)
-    Wr = gen.router_weight(cfg, 0, dev)
-    b = gen.router_bias(cfg, 0, 0, dev)
-    x = gen.tokens(cfg, 0, 0, dev)
-    pl.forward(x, Wr, b, buf, wfmt=L.MOE_W_MXFP4)
-    torch.cuda.synchronize()
-    counts = _prefill_check(cfg, 0, pl, x, Wr, b)
+    counts = prefill_check(cfg, 0, got, x, Wr, b, n_tokens=None)  # every token, so every y_perm row
     print(f"  tokens per expert: min {counts.min()} max {counts.max()} mean {counts.mean():.1f}", flush=True)
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["prefill_db_bf16_t16384_l8", "prefill_db_mxfp4_t16384_l8"])
 def test_prefill_16384_double_buffered(name):
+    """Eight 16384-token layers through the double buffer, enqueued back to back with no host wait: layer
+    l+2's copy into the buffer layer l read must wait for layer l's compute (the pipe's ordering), or the
+    outputs of layer l would be computed from the wrong weights. Each layer's results are copied on the stream
+    and all are checked at the end: routing of every token, 1024 sampled token outputs and the tile rows."""
     from routed_expert_layer_amd import _lib as L
     from routed_expert_layer_amd.runtime import PrefillLayer
     cfg = CONFIGS[name]
@@ -261,17 +340,23 @@ def test_prefill_16384_double_buffered(name):
         pipe = L.MoePipe(store.layer_ptrs, store.layer_bytes)
         pl = PrefillLayer(cfg.H, cfg.I, cfg.E, cfg.k, cfg.T, store.stride, dev, keep_logits=True, wfmt=store.wfmt)
         s = torch.cuda.current_stream()
+        xs = [gen.tokens(cfg, 0, layer, dev) for layer in range(cfg.L)]
+        Wrs = [gen.router_weight(cfg, layer, dev) for layer in range(cfg.L)]
+        bs = [gen.router_bias(cfg, layer, 0, dev) for layer in range(cfg.L)]
+        torch.cuda.synchronize()
+        got = []
         for layer in range(cfg.L):
-            Wr = gen.router_weight(cfg, layer, dev)
-            b = gen.router_bias(cfg, layer, 0, dev)
-            x = gen.tokens(cfg, 0, layer, dev)
             base = L.moe_pipe_begin_layer(pipe, layer, s)
-            pl.forward(x, Wr, b, base, wfmt=store.wfmt)
+            pl.forward(xs[layer], Wrs[layer], bs[layer], base, stream=s)
             L.moe_pipe_end_layer(pipe, layer, s)
-            torch.cuda.synchronize()
-            counts = _prefill_check(cfg, layer, pl, x, Wr, b, n_sample=8)
-            print(f"  layer {layer}: active experts {int((counts > 0).sum())}, max group {counts.max()}, "
-                  f"copy {L.moe_pipe_copy_ms(pipe, layer):.1f} ms", flush=True)
+            got.append(LayerCopy(pl, cfg.T))
+        print(f"  {cfg.L} layers enqueued", flush=True)
+        torch.cuda.synchronize()
+        # 1024 tokens per layer with bf16 experts; fewer with MXFP4, whose oracle weights cost more to form
+        n_tok = 1024 if cfg.wfmt == "bf16" else 256
+        for layer in range(cfg.L):
+            prefill_check(cfg, layer, got[layer], xs[layer], Wrs[layer], bs[layer], n_tokens=n_tok)
+            print(f"    copy {L.moe_pipe_copy_ms(pipe, layer):.1f} ms", flush=True)
         pipe.close()
     finally:
         store.close()
