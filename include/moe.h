@@ -99,6 +99,25 @@ int moe_route(const void* x, int dtype, const void* Wr, const float* bias,
               int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_pos,
               void* workspace, size_t ws_bytes, void* stream);
 
+/* moe_route_noalloc: moe_route without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The routing kernels' scratch is a
+ * device array of MOE_ROUTE_NOALLOC_MAX_BYTES that the library holds on every
+ * GPU it runs on until the process ends; the call allocates nothing and
+ * enqueues only kernels. Arguments, results and errors as moe_route, plus
+ * MOE_ECAPACITY when moe_route_workspace_size(T, H, E, k) exceeds
+ * MOE_ROUTE_NOALLOC_MAX_BYTES (64 MiB: every batch up to 16384 tokens at H 4096,
+ * E 256 fits; 16384 tokens at E 1024 do not).
+ * All calls on one GPU share that scratch: calls that overlap on one GPU
+ * (different streams, or different host threads) race and must be ordered by
+ * the caller. */
+#define MOE_ROUTE_NOALLOC_MAX_BYTES (64u << 20)
+int moe_route_noalloc(const void* x, int dtype, const void* Wr, const float* bias,
+                      int T, int H, int E, int k,
+                      int32_t* topk_idx, float* topk_w, float* logits,
+                      int32_t* counts, int32_t* offsets, int32_t* perm_src, int32_t* perm_pos,
+                      void* stream);
+
 /* ------------------------------------------------------------------------ *
  * Expert blobs and the host pool.
  *

@@ -30,7 +30,7 @@ SYMBOLS = [
     "moe_device_decoder_trace", "moe_device_decoder_clear_trace", "moe_device_decoder_slot_of",
     "moe_graph_begin", "moe_graph_end", "moe_graph_launch", "moe_graph_destroy",
     "moe_cache_resize", "moe_cache_capacity", "moe_decoder_resize", "moe_device_decoder_resize",
-    "moe_ffn_grouped", "moe_prefill_layer",
+    "moe_ffn_grouped", "moe_prefill_layer", "moe_route_noalloc",
 ]
 
 
@@ -70,6 +70,7 @@ _sig("moe_last_error", ctypes.c_char_p)
 _sig("moe_abi_version", I32)
 _sig("moe_route_workspace_size", SZ, I32, I32, I32, I32)
 _sig("moe_route", I32, P, I32, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P, SZ, P)
+_sig("moe_route_noalloc", I32, P, I32, P, P, I32, I32, I32, I32, P, P, P, P, P, P, P, P)
 _sig("moe_expert_bytes", SZ, I32, I32, I32)
 _sig("moe_pack_expert", I32, I32, I32, I32, P, P, P, P, P, P, P, P)
 _sig("moe_pool_alloc", P, SZ, PI)
@@ -193,6 +194,15 @@ def moe_route(x, Wr, bias, k, topk_idx, topk_w, logits, counts, offsets, perm_sr
     _check(_lib.moe_route(_dptr(x), _dtype_code(x), _dptr(Wr), _dptr(bias), T, H, E, k, _dptr(topk_idx),
                           _dptr(topk_w), _dptr(logits), _dptr(counts), _dptr(offsets), _dptr(perm_src),
                           _dptr(perm_pos), _dptr(workspace), _nbytes(workspace), _stream(stream)), "moe_route")
+
+
+def moe_route_noalloc(x, Wr, bias, k, topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos, stream=None):
+    """moe_route with the library's own per-GPU scratch instead of a workspace argument."""
+    T, H = x.shape
+    E = Wr.shape[1]
+    _check(_lib.moe_route_noalloc(_dptr(x), _dtype_code(x), _dptr(Wr), _dptr(bias), T, H, E, k, _dptr(topk_idx),
+                                  _dptr(topk_w), _dptr(logits), _dptr(counts), _dptr(offsets), _dptr(perm_src),
+                                  _dptr(perm_pos), _stream(stream)), "moe_route_noalloc")
 
 
 # ---------------------------------------------------------------------------

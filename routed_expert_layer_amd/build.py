@@ -9,7 +9,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["kernels_route.hip", "kernels_ffn.hip", "kernels_gemm.hip", "kernels_misc.hip", "kernels_devctl.hip",
-           "abi.cpp", "decoder.cpp", "device_decoder.cpp", "lru_policy.cpp", "cpu_expert.cpp"]
+           "noalloc.hip", "abi.cpp", "decoder.cpp", "device_decoder.cpp", "lru_policy.cpp", "cpu_expert.cpp"]
 # host-only sources with extra flags: the CPU expert kernel uses AVX-512 BF16 dot products
 EXTRA = {"cpu_expert.cpp": ["-mavx512f", "-mavx512bw", "-mavx512vl", "-mavx512bf16"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
