@@ -209,6 +209,81 @@ def decode_variants(args, torch, cfg, store, Wr, xs, bias):
     return split, device
 
 
+def full_trace(args, torch, L, cfg, store, Wr, xs, bias, split=False):
+    """Every step of the one-layer decode workload from a cold cache (whatever --steps/--warmup say): tokens/s,
+    fills, hit rate and per-step latency percentiles over the whole trace, fills included. With split, misses
+    are divided between fills and CPU execution in the ratio of the rates measured on this machine."""
+    from routed_expert_layer_amd.runtime import DecodeLayer
+    dev = "cuda"
+    s = torch.cuda.current_stream()
+    from workloads import gen
+    n = cfg.steps
+    x_all = [xs[st] if st < len(xs) else gen.tokens(cfg, st, 0, dev) for st in range(n)]
+    dl = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+    rates = None
+    if split:
+        rates = [int(r) for r in dl.measure_rates()]
+        dl.set_split(*rates)
+    torch.cuda.synchronize()
+    lat = []
+    t0 = prev = time.perf_counter()
+    for st in range(n):
+        dl.step(st, 0, x_all[st], Wr, bias(st), s)
+        now = time.perf_counter()
+        lat.append(now - prev)
+        prev = now
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    lat[-1] += time.perf_counter() - prev
+    tr = dl.trace()
+    return dict(steps=n, tokens_per_s=n * cfg.T / el, ms_per_step=el * 1e3 / n, fills=int(dl.n_fills),
+                cpu_runs=int(dl.cpu_runs), hit_rate=float(tr[:, 3].mean()),
+                step_ms_p50=percentile(lat, 50) * 1e3, step_ms_p99=percentile(lat, 99) * 1e3,
+                step_ms_max=max(lat) * 1e3, split_rates_mbs=rates)
+
+
+def mall_flushed_roofline(torch, L, dl, cfg, store, x, reps=40):
+    """The decode expert FFN of six resident experts, one call at a time with the last-level cache (256 MB)
+    flushed before each: a 512 MB buffer is written on the stream between calls, so the experts' 302 MB come
+    from HBM. HIP events around each call on the stream it runs on; the same calls back to back (experts warm
+    in that cache) for comparison."""
+    import numpy as np
+    dev = "cuda"
+    s = torch.cuda.current_stream()
+    keys = [k for k in range(cfg.E) if L.moe_cache_slot_of(dl.cache, k) >= 0][:cfg.k]
+    if len(keys) < cfg.k:
+        return None
+    work = np.array([[k, L.moe_cache_slot_of(dl.cache, k), j, 1] for j, k in enumerate(keys)], np.int32)
+    perm_src = torch.zeros(cfg.k, dtype=torch.int32, device=dev)
+    y = torch.empty((cfg.k, cfg.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(L.moe_ffn_workspace_size(cfg.k, cfg.H, cfg.I, store.wfmt), dtype=torch.uint8, device=dev)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    alg = len(keys) * store.blob + cfg.k * (cfg.H * 2 + 2 * cfg.I * 2 + cfg.H * 4)
+
+    def run(flush):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i in range(reps + 3):
+            if flush:
+                scratch.fill_(i & 0xFF)
+            if i >= 3:
+                ev[i - 3][0].record(s)
+            L.moe_ffn(x, perm_src, work, dl.slots, store.stride, store.wfmt, cfg.H, cfg.I, y, ws, L.MOE_FFN_DECODE, s)
+            if i >= 3:
+                ev[i - 3][1].record(s)
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in ev) * 1e3 / reps
+        return us
+
+    us_f, us_w = run(True), run(False)
+    del scratch
+    return dict(kernel="ffn1_decode_bf16 + ffn2_decode_bf16, six resident experts, one call at a time",
+                algorithmic_bytes_per_launch=alg, launches=reps,
+                flushed=dict(avg_launch_us=round(us_f, 2), achieved_gbs=round(alg / us_f / 1e3, 1),
+                             frac=round(alg / us_f / 1e3 / HBM_PEAK_GBS, 4)),
+                cache_warm=dict(avg_launch_us=round(us_w, 2), achieved_gbs=round(alg / us_w / 1e3, 1),
+                                frac=round(alg / us_w / 1e3 / HBM_PEAK_GBS, 4)))
+
+
 def bench_decode(args, torch, L, gen, cfg):
     from routed_expert_layer_amd.runtime import DecodeLayer, ExpertStore
     dev = "cuda"
@@ -234,7 +309,9 @@ def bench_decode(args, torch, L, gen, cfg):
         dl.step(step, 0, xs[step], Wr, bias(step), s)
     torch.cuda.synchronize()
     fills0 = dl.n_fills
-    L.moe_decoder_profile(dl.dec, 8)  # HIP events around every 8th expert-FFN call, on stream s
+    # HIP events around the expert-FFN calls of no-fill steps, on stream s: every 8th in long runs (the events
+    # then barely touch the step time), every one in short runs (so the sample is not a handful of calls)
+    L.moe_decoder_profile(dl.dec, 8 if args.steps > 256 else 1)
     lat = []
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -264,6 +341,11 @@ def bench_decode(args, torch, L, gen, cfg):
     if not args.no_variants:
         split, device = decode_variants(args, torch, cfg, store, Wr, xs, bias)
 
+    full = full_trace(args, torch, L, cfg, store, Wr, xs, bias)
+    if not args.no_variants:
+        full["cpu_split"] = full_trace(args, torch, L, cfg, store, Wr, xs, bias, split=True)
+    flushed = mall_flushed_roofline(torch, L, dl, cfg, store, xs[0])
+
     # pinned host -> HBM fill bandwidth: blobs copied on the fill stream
     fs = dl.fill_stream
     n_copy = min(16, cfg.S)
@@ -284,7 +366,9 @@ def bench_decode(args, torch, L, gen, cfg):
                     step_ms_p50=percentile(lat, 50) * 1e3, step_ms_p99=percentile(lat, 99) * 1e3,
                     step_ms_max=max(lat) * 1e3, hit_rate=hit_rate, fills_timed=dl.n_fills - fills0,
                     fills_warmup=fills0, fill_gbs=fill_gbs, fill_frac_pcie=fill_gbs / PCIE_PEAK_GBS,
-                    pool_gb=store.nbytes / 1e9, slots=cfg.S, cpu_split=split, device_control=device),
+                    pool_gb=store.nbytes / 1e9, slots=cfg.S, cpu_split=split, device_control=device,
+                    full_trace=full),
+        roofline_mall_flushed=flushed,
     )
 
 
@@ -534,6 +618,63 @@ def bench_decode_layers(args, torch, L, gen, cfg, warm, steps):
         store.close()
 
 
+def profile_mxfp4(args, torch, L, gen):
+    """A short run of the MXFP4 kernels for hardware-counter profiles, with every input made on the host CPU:
+    no GPU work runs in the process but the library's kernels (the packer included) and the copies of their
+    inputs. 16 distinct experts are generated and each packed into 16 of the 256 slots of a layer (the
+    kernels' traffic and timing depend on the weights' values only through their statistics). Runs the
+    4096-token MXFP4 prefill layer 3 times, one 16384-token Zipf(1.5) layer twice (groups of up to ~16k rows)
+    and 48 decode FFN calls (14 experts, 48 rows: 8 tokens, top 6) on windows rotating over the 256 slots."""
+    import numpy as np
+    from routed_expert_layer_amd.runtime import PrefillLayer
+    from workloads import CONFIGS
+    dev = "cuda"
+    cfg = CONFIGS["prefill_mxfp4_t4096_e256"]
+    wf = L.MOE_W_MXFP4
+    blob = L.moe_expert_bytes(wf, cfg.H, cfg.I)
+    stride = (blob + 4095) // 4096 * 4096
+    buf = torch.empty(cfg.E * stride, dtype=torch.uint8, device=dev)
+    for e in range(16):
+        w = {k: v.to(dev) for k, v in gen.expert_mxfp4(cfg, 0, e, "cpu").items()}
+        for r in range(16):
+            slot = e + 16 * r
+            L.moe_pack_expert(wf, cfg.H, cfg.I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"], w["s2"],
+                              buf[slot * stride:])
+        section(f"profile_mxfp4: expert {e} packed")
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    out = {}
+    for name, T in (("prefill_mxfp4_t4096_e256", 4096), ("prefill_db_mxfp4_t16384_l8", 16384)):
+        c = CONFIGS[name]
+        x = gen.tokens(c, 0, 0, "cpu").to(dev)
+        Wr = gen.router_weight(c, 0, "cpu").to(dev)
+        b = gen.router_bias(c, 0, 0, "cpu").to(dev)
+        pl = PrefillLayer(c.H, c.I, c.E, c.k, T, stride, dev, wfmt=wf)
+        reps = 3 if T == 4096 else 2
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            pl.forward(x, Wr, b, buf, s)
+        torch.cuda.synchronize()
+        out[name] = dict(layers=reps, ms_per_layer=(time.perf_counter() - t0) * 1e3 / reps)
+        del pl
+        section(f"profile_mxfp4: {name} done")
+    # decode FFN: 8 tokens, 48 rows over 14 experts
+    x = gen.tokens(CONFIGS["decode_mxfp4_t8_l8"], 0, 0, "cpu").to(dev)
+    rows = [8, 6, 5, 4, 4, 3, 3, 3, 3, 2, 2, 2, 2, 1]
+    off = np.concatenate([[0], np.cumsum(rows)])
+    r = np.random.default_rng(0)
+    perm_src = torch.from_numpy(np.concatenate([r.integers(0, 8, n) for n in rows]).astype(np.int32)).to(dev)
+    y = torch.empty((int(off[-1]), cfg.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(L.moe_ffn_workspace_size(int(off[-1]), cfg.H, cfg.I, wf), dtype=torch.uint8, device=dev)
+    for i in range(48):
+        work = np.array([[(i * 14 + j) % cfg.E, (i * 14 + j) % cfg.E, off[j], rows[j]] for j in range(14)], np.int32)
+        L.moe_ffn(x, perm_src, work, buf, stride, wf, cfg.H, cfg.I, y, ws, L.MOE_FFN_DECODE, s)
+    torch.cuda.synchronize()
+    out["decode_ffn_calls"] = 48
+    return out
+
+
 def blas_threads(torch):
     """Threads the oracle's numpy BLAS uses."""
     try:
@@ -614,7 +755,7 @@ def cpu_baselines_all(args, torch, gen):
             oracle.moe_layer(x, Wrs[layer], b, cfg.k, get_expert)
             spent += time.perf_counter() - t0
             n += 1
-            if spent >= args.cpu_seconds:
+            if spent >= args.cpu_seconds / 2:
                 break
         per = spent / n
         return dict(value=cfg.T / (per * cfg.L), unit="tokens/s", cores=blas_threads(torch), kind="oracle",
@@ -659,10 +800,13 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the 48-layer decode section")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--cpu-all", action="store_true",
-                    help="also time the oracle on the stack, int4 decode and prefill workloads (a few minutes)")
+    ap.add_argument("--no-cpu-all", action="store_true",
+                    help="time the oracle on the one-layer decode only (not per layer-step of the stack and the "
+                         "int4 decode, nor per prefill layer)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain device-to-device copy of this many MiB (hardware-counter calibration)")
+    ap.add_argument("--profile-mxfp4", action="store_true",
+                    help="only a short run of the MXFP4 kernels on inputs made on the host (counter profiles)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer runs on a single MI355X and the library has no "
@@ -685,6 +829,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.profile_mxfp4:
+        print(json.dumps({"profile_mxfp4": profile_mxfp4(args, torch, L, gen)}), flush=True)
+        return
     section("decode")
     res = bench_decode(args, torch, L, gen, cfg)
     ffn = res["ffn"]
@@ -717,6 +864,7 @@ def main():
                 for k, v in d.items()}
 
     out["decode"] = rnd(res["decode"])
+    out["roofline_mall_flushed"] = res["roofline_mall_flushed"]
     if not args.no_prefill:
         section("prefill")
         out["prefill"] = rnd(bench_prefill(args, torch, L, gen, CONFIGS["prefill_bf16_t4096_e256"]))
@@ -746,7 +894,7 @@ def main():
         cb = cpu_baseline(args, torch, gen, cfg)
         cb["value"] = round(cb["value"], 4)
         out["cpu_baseline"] = cb
-        if args.cpu_all:
+        if not args.no_cpu_all:
             out["cpu_baseline_other_workloads"] = rnd(cpu_baselines_all(args, torch, gen))
     print(json.dumps(out), flush=True)
 

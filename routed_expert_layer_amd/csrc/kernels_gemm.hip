@@ -789,25 +789,35 @@ hipError_t launch_ffn_grouped(int wfmt, const void* x, const int32_t* perm_src, 
     for (int ph = 0; ph < 2; ++ph) tab[p][ph] = reinterpret_cast<const GemmTable*>(tb + (2 * p + ph) * kTableBytes);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   uint16_t* hb = static_cast<uint16_t*>(hbuf);
-  const dim3 grid(256), block(512);
+  const dim3 block(512);
+  // Rounds of 256 blocks per launch: a block whose slot a super-tile leaves empty moves on to its next round,
+  // so with a single round those blocks' CUs would idle; with 32 / (fewest slots a super-tile can fill) rounds
+  // the blocks of empty slots exit and others take their CUs.
+  const auto grid = [](int N, int gm_min) {
+    int GM = gm_min, shape = 0;
+    supertiles_of(GM * 128, N, 128, shape);  // shape of the smallest super-tile a group of this part gets
+    const int fill = (shape & 0xFF) * (shape >> 8);
+    return dim3(256 * (fill >= 32 ? 1 : 32 / fill));
+  };
   if (mx) {
     // split 0 puts every group with rows into part 0, planned with 128-token tiles
     const BlobLayout L = blob_layout(3, H, I);
-    hipLaunchKernelGGL(gemm_mxfp4<1>, grid, block, 0, s, xb, perm_src, tab[0][0], slot_base, slot_stride, L.p1,
-                       L.p1s, 2 * I, H, I, H, hb, y, g_clock_sums);
-    hipLaunchKernelGGL(gemm_mxfp4<2>, grid, block, 0, s, hb, perm_src, tab[0][1], slot_base, slot_stride, L.p2,
+    hipLaunchKernelGGL(gemm_mxfp4<1>, grid(2 * I, 1), block, 0, s, xb, perm_src, tab[0][0], slot_base, slot_stride,
+                       L.p1, L.p1s, 2 * I, H, I, H, hb, y, g_clock_sums);
+    hipLaunchKernelGGL(gemm_mxfp4<2>, grid(H, 1), block, 0, s, hb, perm_src, tab[0][1], slot_base, slot_stride, L.p2,
                        L.p2s, H, I, I, H, hb, y, g_clock_sums);
     return hipGetLastError();
   }
+  // part 0 groups (more than 256 rows) have at least two 256-token tiles, part 1 groups one or two 128-token tiles
   const BlobLayout L = blob_layout(1, H, I);
-  hipLaunchKernelGGL((gemm2_bf16<1, 16, const GemmTable*>), grid, block, 0, s, xb, perm_src, tab[0][0], slot_base,
-                     slot_stride, L.p1, 2 * I, H, H, I, hb, y, nullptr, g_clock_sums);
-  hipLaunchKernelGGL((gemm2_bf16<1, 8, const GemmTable*>), grid, block, 0, s, xb, perm_src, tab[1][0], slot_base,
-                     slot_stride, L.p1, 2 * I, H, H, I, hb, y, nullptr, g_clock_sums);
-  hipLaunchKernelGGL((gemm2_bf16<2, 16, const GemmTable*>), grid, block, 0, s, hb, perm_src, tab[0][1], slot_base,
-                     slot_stride, L.p2, H, I, H, I, hb, y, nullptr, g_clock_sums);
-  hipLaunchKernelGGL((gemm2_bf16<2, 8, const GemmTable*>), grid, block, 0, s, hb, perm_src, tab[1][1], slot_base,
-                     slot_stride, L.p2, H, I, H, I, hb, y, nullptr, g_clock_sums);
+  hipLaunchKernelGGL((gemm2_bf16<1, 16, const GemmTable*>), grid(2 * I, 2), block, 0, s, xb, perm_src, tab[0][0],
+                     slot_base, slot_stride, L.p1, 2 * I, H, H, I, hb, y, nullptr, g_clock_sums);
+  hipLaunchKernelGGL((gemm2_bf16<1, 8, const GemmTable*>), grid(2 * I, 1), block, 0, s, xb, perm_src, tab[1][0],
+                     slot_base, slot_stride, L.p1, 2 * I, H, H, I, hb, y, nullptr, g_clock_sums);
+  hipLaunchKernelGGL((gemm2_bf16<2, 16, const GemmTable*>), grid(H, 2), block, 0, s, hb, perm_src, tab[0][1],
+                     slot_base, slot_stride, L.p2, H, I, H, I, hb, y, nullptr, g_clock_sums);
+  hipLaunchKernelGGL((gemm2_bf16<2, 8, const GemmTable*>), grid(H, 1), block, 0, s, hb, perm_src, tab[1][1],
+                     slot_base, slot_stride, L.p2, H, I, H, I, hb, y, nullptr, g_clock_sums);
   return hipGetLastError();
 }
 
