@@ -128,6 +128,19 @@ class SharedLRU:
         self.trace.extend(recs)
         return waves, recs
 
+    def drop(self, key):
+        """Unmap a key whose fill failed: its slot becomes free, so the next miss
+        takes it if it is the lowest free slot. Page "FreeToken-rtx-4090",
+        component table, row "PCIe link": a miss moves as one complete expert,
+        so an entry whose copy did not happen must not stay resident. Returns
+        False if the key was not resident."""
+        slot = self.key_slot.pop(key, None)
+        if slot is None:
+            return False
+        self.slot_key[slot] = -1
+        self.last_use[slot] = 0
+        return True
+
     def resize(self, S_new):
         """Resize to S_new slots at a safe point. Returns the moves [(key, old slot, new slot)]."""
         assert S_new >= 1

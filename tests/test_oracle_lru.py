@@ -189,3 +189,42 @@ def test_resize_keeps_most_recent_and_continues_as_textbook_lru(S, S_new, E, L):
     # afterwards the cache behaves as a textbook LRU of S_new slots holding those keys
     tb = _textbook_after(sim, tb, S_new)
     run(20, 20, S_new)
+
+
+@pytest.mark.parametrize("S,E,L,max_active,seed", [(8, 16, 1, 14, 1), (6, 24, 2, 6, 2), (3, 9, 3, 4, 3)])
+def test_drop_matches_textbook_with_key_deleted(S, E, L, max_active, seed):
+    """A dropped key (failed fill) leaves the cache as a textbook LRU from which
+    that key was deleted: same hits, slots and victims afterwards."""
+    r = np.random.default_rng(seed)
+    sim = oracle.SharedLRU(S)
+    tb = TextbookLRU(S)
+    dropped = 0
+    for step in range(40):
+        for layer in range(L):
+            n = int(r.integers(1, max_active + 1))
+            experts = sorted(r.choice(E, size=n, replace=False).tolist())
+            _, recs = sim.resolve(step, layer, E, experts)
+            for rc in recs:
+                hit, slot, victim = tb.access(rc.key)
+                assert (rc.hit, rc.slot, rc.victim) == (int(hit), slot, victim)
+            # drop the misses of this layer-step from a random position on, as a failed batch of fills does
+            misses = [rc.key for rc in recs if not rc.hit]
+            if misses and r.random() < 0.3:
+                for key in misses[int(r.integers(0, len(misses))):]:
+                    slot = tb.od.pop(key)
+                    tb.free.append(slot)
+                    assert sim.drop(key)
+                    assert key not in sim.key_slot and sim.slot_key[slot] == -1
+                    dropped += 1
+    assert dropped > 0
+    assert not sim.drop(E * L)  # never resident
+
+
+def test_drop_frees_lowest_slot_for_next_miss():
+    sim = oracle.SharedLRU(4)
+    sim.resolve(0, 0, 8, [0, 1, 2, 3])          # slots 0..3
+    assert sim.drop(1)                           # slot 1 free
+    _, recs = sim.resolve(1, 0, 8, [5])
+    assert (recs[0].hit, recs[0].slot, recs[0].victim) == (0, 1, -1)
+    _, recs = sim.resolve(2, 0, 8, [1])          # 1 is a miss again; evicts the LRU entry (key 0, slot 0)
+    assert (recs[0].hit, recs[0].slot, recs[0].victim) == (0, 0, 0)
