@@ -609,7 +609,7 @@ def bench_decode_layers(args, torch, L, gen, cfg, warm, steps):
         if cfg.epoch:
             res["epochs"] = epochs()
         res["device_control"] = bench_device(torch, cfg, store, Wrs, warm, steps, lambda st, l: xs[st][l], b)
-        if cfg.wfmt == "bf16" and cfg.act == "bf16":
+        if cfg.act == "bf16":
             # the pages' adaptive misses: the share rate_fill / (rate_fill + rate_cpu) of misses is filled,
             # the rest runs on the host CPU from the pool (rates measured here)
             res["cpu_split"] = run(True)

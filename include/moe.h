@@ -252,8 +252,19 @@ int moe_cache_capacity(const moe_cache_t* cache);
  * includes every earlier reader of a victim slot), run on fill_stream, and
  * work enqueued on compute_stream after this call waits for them.
  * fill_stream may equal compute_stream. Uses the cache's own events.
- * Errors: MOE_EINVAL (null), MOE_EHIP (copy or event failure; the caller
- * should then moe_cache_invalidate the affected keys).
+ * Errors: MOE_EINVAL (null, key or slot out of range, no pool address for a
+ * layer), MOE_EHIP (copy or event failure). On any error no key of the batch
+ * is left mapped to a slot its copy did not reach (page "FreeToken-rtx-4090",
+ * component table, row "PCIe link": a miss moves as one complete expert): the
+ * failed miss and every later one are dropped from the cache as by
+ * moe_cache_invalidate (their slots become free); copies issued before the
+ * failure keep their keys, and later compute-stream work is still ordered
+ * after them (if the ordering itself fails, the whole batch is dropped).
+ * Debug: with MOE_DEBUG_POISON_FILLS=1 in the environment when the cache is
+ * created, every fill first sets its slot's blob_bytes to 0xFF (NaN in bf16,
+ * fp32 and in the int4 and MXFP4 scales), so a read not ordered after the
+ * copy, or a copy overwriting a slot still being read, shows as non-finite
+ * output.
  * ------------------------------------------------------------------------ */
 int cache_fill_async(moe_cache_t* cache, const moe_miss_t* misses, int n,
                      const void* const* layer_pool, size_t blob_stride, size_t blob_bytes,
@@ -418,8 +429,9 @@ int moe_clock_record(unsigned long long* sums);
  *   computation instead of each expert movement being waited for).
  *   When the cache splits misses (moe_cache_set_split), the misses assigned
  *   to the CPU run with moe_cpu_ffn from the pool on the calling thread while
- *   the GPU works on the others (bf16 activations and weights only, else
- *   MOE_EINVAL); their rows of y_perm are copied in before the combine.
+ *   the GPU works on the others (bf16 activations with bf16, int4 or MXFP4
+ *   weights, else MOE_EINVAL); their rows of y_perm are copied in before the
+ *   combine.
  * moe_decoder_profile: every > 0 brackets every every-th FFN call of a
  *   layer-step whose experts were all resident (one wave, no fills; the
  *   first such call, then each every-th after it) with HIP events on
@@ -493,15 +505,21 @@ int moe_prefill_layer(const void* x, int dtype, const void* Wr, const float* bia
  * pool instead of being copied to the GPU.
  *
  * moe_cpu_ffn: y = (silu(x W1) * (x W3)) W2 for `rows` activation rows, on the
- *   host CPU, from the expert's bf16 blob (the moe_pack_expert layout).
+ *   host CPU, from the expert's blob (the moe_pack_expert layout) in bf16,
+ *   int4 or MXFP4. The 4-bit formats are read as the GPU reads them: int4
+ *   codes enter bf16 dot products as 1 + n/16 and each 128-row block's sum
+ *   is 16 t - 24 u (u: the activations' sum over the block) times its fp16
+ *   scale; MXFP4 codes enter as their E2M1 values and the E8M0 scale
+ *   multiplies each 32-row partial sum.
  *   blob: host pointer (e.g. inside a moe_pool_alloc region); x: host bf16
  *   [rows, H] row-major; y: host fp32 [rows, H] row-major, overwritten. The
  *   SwiGLU product is rounded to bf16 before the down projection, as on the
  *   GPU. threads: participating threads (<= 0: all, see moe_cpu_threads);
  *   the library keeps one process-wide pool of worker threads, and calls from
  *   several host threads at once are serialised by the caller. Synchronous.
- *   Errors: EINVAL for null pointers, negative rows, or a format other than
- *   bf16 with H, I multiples of 32. Needs a CPU with AVX-512 BF16.
+ *   Errors: EINVAL for null pointers, negative rows, fp32 weights, or H, I
+ *   not multiples of 32 (bf16) or 128 (int4, MXFP4). Needs a CPU with
+ *   AVX-512 BF16.
  * moe_cpu_threads: the number of threads moe_cpu_ffn can use (workers + the
  *   calling thread).
  * ------------------------------------------------------------------------- */

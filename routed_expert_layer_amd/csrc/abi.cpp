@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -50,7 +51,14 @@ struct moe_cache {
   moe::SharedLru lru;
   std::vector<moe_trace_t> trace;
   hipEvent_t ev_war = nullptr, ev_done = nullptr;
-  moe_cache(int L_, int E_, int S_) : L(L_), E(E_), S(S_), lru(L_ * E_, S_) {}
+  // MOE_DEBUG_POISON_FILLS=1 at creation: every fill first sets its slot's
+  // bytes to 0xFF (NaN in bf16, fp32 and the fp16 / E8M0 scales), so a read
+  // that is not ordered after the fill shows up as non-finite output.
+  bool poison = false;
+  moe_cache(int L_, int E_, int S_) : L(L_), E(E_), S(S_), lru(L_ * E_, S_) {
+    const char* v = std::getenv("MOE_DEBUG_POISON_FILLS");
+    poison = v && v[0] == '1';
+  }
 };
 
 struct moe_pipe {
@@ -293,7 +301,9 @@ int cache_fill_async(moe_cache_t* c, const moe_miss_t* misses, int n, const void
                                     fill_stream, compute_stream, &done);
   if (rc != MOE_OK || !done) return rc;
   hipError_t e = hipStreamWaitEvent(as_stream(compute_stream), done, 0);
-  return e == hipSuccess ? MOE_OK : hip_fail(e, "cache_fill_async: ordering before compute");
+  if (e == hipSuccess) return MOE_OK;
+  for (int i = 0; i < n; ++i) (void)c->lru.invalidate(misses[i].key);  // no reader would wait for the copies
+  return hip_fail(e, "cache_fill_async: ordering before compute");
 }
 
 }  // extern "C"
@@ -302,40 +312,73 @@ int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const vo
                        size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
                        void* compute_stream, hipEvent_t* done) {
   *done = nullptr;
-  if (!c || n < 0 || (n > 0 && (!misses || !layer_pool || !slot_base)) || blob_bytes > slot_stride ||
-      blob_bytes > blob_stride)
-    return fail(MOE_EINVAL, "cache_fill_async: bad argument");
+  if (!c || n < 0 || (n > 0 && !misses)) return fail(MOE_EINVAL, "cache_fill_async: bad argument");
   if (n == 0) return MOE_OK;
+  // Whatever fails below, no key of the batch may stay mapped to a slot that
+  // its copy has not reached (or that no reader is ordered after).
+  const auto drop_from = [&](int i0, int rc) {
+    for (int j = i0; j < n; ++j)
+      if (misses[j].key >= 0 && misses[j].key < c->L * c->E) (void)c->lru.invalidate(misses[j].key);
+    return rc;
+  };
+  if (!layer_pool || !slot_base || blob_bytes > slot_stride || blob_bytes > blob_stride)
+    return drop_from(0, fail(MOE_EINVAL, "cache_fill_async: bad argument"));
   for (int i = 0; i < n; ++i)
     if (misses[i].key < 0 || misses[i].key >= c->L * c->E || misses[i].slot < 0 || misses[i].slot >= c->S)
-      return fail(MOE_EINVAL, "cache_fill_async: miss %d has key %d slot %d out of range", i, misses[i].key,
-                  misses[i].slot);
+      return drop_from(0, fail(MOE_EINVAL, "cache_fill_async: miss %d has key %d slot %d out of range", i,
+                               misses[i].key, misses[i].slot));
   hipStream_t fs = as_stream(fill_stream), cs = as_stream(compute_stream);
   hipError_t e = hipSuccess;
   if (!c->ev_war) e = hipEventCreateWithFlags(&c->ev_war, hipEventDisableTiming);
   if (e == hipSuccess && !c->ev_done) e = hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming);
-  if (e != hipSuccess) return hip_fail(e, "cache_fill_async: event create");
+  if (e != hipSuccess) return drop_from(0, hip_fail(e, "cache_fill_async: event create"));
   const bool split = fs != cs;
   if (split) {
     e = hipEventRecord(c->ev_war, cs);
     if (e == hipSuccess) e = hipStreamWaitEvent(fs, c->ev_war, 0);
-    if (e != hipSuccess) return hip_fail(e, "cache_fill_async: ordering after compute");
+    if (e != hipSuccess) return drop_from(0, hip_fail(e, "cache_fill_async: ordering after compute"));
   }
   char* dst = static_cast<char*>(slot_base);
-  for (int i = 0; i < n; ++i) {
+  std::vector<int32_t> keys(n);
+  for (int i = 0; i < n; ++i) keys[i] = misses[i].key;
+  int rc = MOE_OK;
+  const auto copy = [&](int i) {
     const int layer = misses[i].key / c->E, ex = misses[i].key % c->E;
     const char* src = static_cast<const char*>(layer_pool[layer]);
-    if (!src) return fail(MOE_EINVAL, "cache_fill_async: no pool address for layer %d", layer);
-    e = hipMemcpyAsync(dst + (size_t)misses[i].slot * slot_stride, src + (size_t)ex * blob_stride, blob_bytes,
-                       hipMemcpyHostToDevice, fs);
-    if (e != hipSuccess) return hip_fail(e, "cache_fill_async: copy");
-  }
+    if (!src) {
+      rc = fail(MOE_EINVAL, "cache_fill_async: no pool address for layer %d", layer);
+      return false;
+    }
+    char* slot = dst + (size_t)misses[i].slot * slot_stride;
+    if (c->poison) {  // debug: a read of the slot before the copy lands sees NaN
+      e = moe::launch_poison(slot, blob_bytes, fs);
+      if (e != hipSuccess) {
+        rc = hip_fail(e, "cache_fill_async: poison");
+        return false;
+      }
+    }
+    e = hipMemcpyAsync(slot, src + (size_t)ex * blob_stride, blob_bytes, hipMemcpyHostToDevice, fs);
+    if (e != hipSuccess) {
+      rc = hip_fail(e, "cache_fill_async: copy");
+      return false;
+    }
+    return true;
+  };
+  // A miss whose copy is not issued, and every later one, is dropped here;
+  // the copies issued before it keep their keys.
+  const int issued = moe::issue_fills(c->lru, keys.data(), n, copy);
   if (split) {
     e = hipEventRecord(c->ev_done, fs);
-    if (e != hipSuccess) return hip_fail(e, "cache_fill_async: completion event");
+    if (e != hipSuccess) return drop_from(0, issued < n ? rc : hip_fail(e, "cache_fill_async: completion event"));
+    if (issued < n) {
+      // the call fails, so the caller will not wait: order later readers of
+      // the issued copies after them here
+      e = hipStreamWaitEvent(cs, c->ev_done, 0);
+      return e == hipSuccess ? rc : drop_from(0, rc);
+    }
     *done = c->ev_done;
   }
-  return MOE_OK;
+  return rc;
 }
 
 extern "C" {

@@ -141,16 +141,184 @@ void tile_dot(const uint16_t* frag, int KC, const uint16_t* act, size_t ld, int 
     for (int q = 0; q < 4; ++q) quad_sums(acc[q][r], &res[r][4 * q]);
 }
 
+// int4 and MXFP4 blobs: a 16-row tile is K/128 blocks of 1 KiB of 4-bit
+// codes; block byte 16 l .. 16 l + 15 (lane l) holds four 32-bit words, word j
+// being row l % 16 at K 128 g + 32 j + 8 (l / 16) .. + 7. A 64-byte run m of
+// a block (lanes 4m .. 4m+3) is rows 4 (m % 4) .. + 3 at K group s = m / 4;
+// its 16 words, turned into four vectors of bf16 pairs (pair p = the codes of
+// K 2p and 2p + 1 of each word), meet the activation pairs of the same K in
+// one vdpbf16ps each. Lane 4i + j of accumulator q then sums row 4q + i over
+// its word j, so the per-block scales apply lane by lane and the four j lanes
+// are added once at the end.
+enum class Q4 { kInt4, kMxfp4 };
+
+// Activation pairs for every (K block g, group s, pair p) of one row, as the
+// 16 words the code vectors need (word 4i + j = the bf16 pair at K 128 g +
+// 32 j + 8 s + 2 p), and, for int4, the row's sum over each K block.
+struct Q4Act {
+  std::vector<__m512i> pairs;  // [KG][4][4]
+  std::vector<float> block_sum;  // [KG]
+};
+
+void q4_activations(const uint16_t* xr, int K, Q4Act& a) {
+  const int KG = K / 128;
+  a.pairs.resize((size_t)KG * 16);
+  a.block_sum.resize(KG);
+  for (int g = 0; g < KG; ++g) {
+    float sum = 0.f;
+    for (int k = 0; k < 128; ++k) {
+      const uint32_t u = (uint32_t)xr[128 * g + k] << 16;
+      float f;
+      std::memcpy(&f, &u, 4);
+      sum += f;
+    }
+    a.block_sum[g] = sum;
+    for (int s = 0; s < 4; ++s)
+      for (int p = 0; p < 4; ++p) {
+        alignas(64) uint32_t w[16];
+        for (int j = 0; j < 4; ++j) {
+          uint32_t v;
+          std::memcpy(&v, xr + 128 * g + 32 * j + 8 * s + 2 * p, 4);
+          for (int i = 0; i < 4; ++i) w[4 * i + j] = v;
+        }
+        a.pairs[(size_t)(g * 4 + s) * 4 + p] = _mm512_load_si512(w);
+      }
+  }
+}
+
+// The four bf16-pair vectors of 16 code words. int4 (nibbles k0,k2,k4,k6,
+// k1,k3,k5,k7, nibble n = q + 8): nibble n in the top mantissa bits of 1.0 is
+// 1 + n/16 exactly, so a block's sum is 16 t - 24 u (u the activations' sum).
+// MXFP4 (nibbles in K order): each nibble indexes the E2M1 values as bf16.
+template <Q4 F>
+inline void q4_codes_to_bf16(__m512i w, __m512i out[4]) {
+  if constexpr (F == Q4::kInt4) {
+    const __m512i m = _mm512_set1_epi32(0x00780078), one = _mm512_set1_epi32(0x3F803F80);
+    out[0] = _mm512_ternarylogic_epi32(_mm512_slli_epi32(w, 3), m, one, 0xEA);  // (a & b) | c
+    out[1] = _mm512_ternarylogic_epi32(_mm512_srli_epi32(w, 1), m, one, 0xEA);
+    out[2] = _mm512_ternarylogic_epi32(_mm512_srli_epi32(w, 5), m, one, 0xEA);
+    out[3] = _mm512_ternarylogic_epi32(_mm512_srli_epi32(w, 9), m, one, 0xEA);
+  } else {
+    // E2M1 codes 0..15 as bf16: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives
+    const __m512i lut = _mm512_set_epi16(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, (short)0xC0C0, (short)0xC080,
+                                         (short)0xC040, (short)0xC000, (short)0xBFC0, (short)0xBF80, (short)0xBF00,
+                                         (short)0x8000, 0x40C0, 0x4080, 0x4040, 0x4000, 0x3FC0, 0x3F80, 0x3F00, 0);
+    const __m512i lo = _mm512_set1_epi32(0xF), hi = _mm512_set1_epi32(0xF0000);
+    for (int p = 0; p < 4; ++p) {
+      const __m512i t = _mm512_srli_epi32(w, 8 * p);
+      const __m512i idx = _mm512_ternarylogic_epi32(_mm512_and_si512(t, lo), _mm512_slli_epi32(t, 12), hi, 0xF8);
+      out[p] = _mm512_permutexvar_epi16(idx, lut);  // a | (b & c)
+    }
+  }
+}
+
+// One 16-row tile of an int4 or MXFP4 matrix (KG blocks at `codes`, their
+// scale blocks at `scales`) against nr <= kRB rows of activations; res[r][16].
+template <Q4 F>
+void tile_dot_q4(const char* codes, const char* scales, int KG, const Q4Act* act, int nr, float res[kRB][16]) {
+  __m512 tot[4][kRB];
+  for (int q = 0; q < 4; ++q)
+    for (int r = 0; r < kRB; ++r) tot[q][r] = _mm512_setzero_ps();
+  // lane 4i + j of scale vector q belongs to row 4q + i
+  alignas(64) int32_t rowidx[4][16];
+  for (int q = 0; q < 4; ++q)
+    for (int l = 0; l < 16; ++l) rowidx[q][l] = 4 * q + l / 4;
+  for (int g = 0; g < KG; ++g) {
+    __m512 acc[4][kRB];
+    for (int q = 0; q < 4; ++q)
+      for (int r = 0; r < kRB; ++r) acc[q][r] = _mm512_setzero_ps();
+    const char* blk = codes + (size_t)g * 1024;
+    for (int m = 0; m < 16; ++m) {
+      __m512i a[4];
+      q4_codes_to_bf16<F>(_mm512_loadu_si512(blk + 64 * m), a);
+      const int q = m & 3, s = m >> 2;
+      for (int r = 0; r < nr; ++r) {
+        const __m512i* b = &act[r].pairs[(size_t)(g * 4 + s) * 4];
+        for (int p = 0; p < 4; ++p) acc[q][r] = _mm512_dpbf16_ps(acc[q][r], (__m512bh)a[p], (__m512bh)b[p]);
+      }
+    }
+    if constexpr (F == Q4::kInt4) {
+      // 16 fp16 scales, row r in lane r
+      const __m512 sc = _mm512_cvtph_ps(_mm256_loadu_si256(reinterpret_cast<const __m256i*>(scales + 32 * g)));
+      for (int q = 0; q < 4; ++q) {
+        const __m512 sq = _mm512_permutexvar_ps(_mm512_load_si512(rowidx[q]), sc);
+        for (int r = 0; r < nr; ++r) {
+          // the four j lanes of a row share -24 u
+          const __m512 t = _mm512_fmadd_ps(acc[q][r], _mm512_set1_ps(16.f), _mm512_set1_ps(-6.f * act[r].block_sum[g]));
+          tot[q][r] = _mm512_fmadd_ps(sq, t, tot[q][r]);
+        }
+      }
+    } else {
+      // byte 4 r + j of the 64-byte block: row r, K chunk j; byte 16 q + l is lane l of vector q
+      for (int q = 0; q < 4; ++q) {
+        const __m512i e = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(scales + 64 * g + 16 * q)));
+        const __m512 sq = _mm512_castsi512_ps(_mm512_slli_epi32(e, 23));  // 2^(e - 127)
+        for (int r = 0; r < nr; ++r) tot[q][r] = _mm512_fmadd_ps(sq, acc[q][r], tot[q][r]);
+      }
+    }
+  }
+  for (int r = 0; r < nr; ++r)
+    for (int q = 0; q < 4; ++q) quad_sums(tot[q][r], &res[r][4 * q]);
+}
+
+template <Q4 F>
+void cpu_ffn_q4(const char* blob, int wfmt, int H, int I, const uint16_t* xa, int rows, float* y, int threads) {
+  const moe::BlobLayout lay = moe::blob_layout(wfmt, H, I);
+  const size_t sblk = F == Q4::kInt4 ? 32 : 64;  // scale bytes per tile and K block
+  const int KG1 = H / 128, NT1 = 2 * I / 16, KG2 = I / 128, NT2 = H / 16;
+  std::vector<Q4Act> ax(rows), ah(rows);
+  for (int r = 0; r < rows; ++r) q4_activations(xa + (size_t)r * H, H, ax[r]);
+  std::vector<uint16_t> h((size_t)rows * I);
+  pool().run(threads, [&](int id, int n) {
+    float res[kRB][16];
+    for (int t = (int)((long)NT1 * id / n); t < (int)((long)NT1 * (id + 1) / n); ++t)
+      for (int r0 = 0; r0 < rows; r0 += kRB) {
+        const int nr = rows - r0 < kRB ? rows - r0 : kRB;
+        tile_dot_q4<F>(blob + lay.p1 + (size_t)t * KG1 * 1024, blob + lay.p1s + (size_t)t * KG1 * sblk, KG1,
+                       ax.data() + r0, nr, res);
+        for (int r = 0; r < nr; ++r)
+          for (int q = 0; q < 4; ++q)
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const float gv = res[r][4 * q + 2 * s2], uv = res[r][4 * q + 2 * s2 + 1];
+              h[(size_t)(r0 + r) * I + 8 * t + 2 * q + s2] = f32_to_bf16_rne(silu(gv) * uv);
+            }
+      }
+  });
+  for (int r = 0; r < rows; ++r) q4_activations(h.data() + (size_t)r * I, I, ah[r]);
+  pool().run(threads, [&](int id, int n) {
+    float res[kRB][16];
+    for (int t = (int)((long)NT2 * id / n); t < (int)((long)NT2 * (id + 1) / n); ++t)
+      for (int r0 = 0; r0 < rows; r0 += kRB) {
+        const int nr = rows - r0 < kRB ? rows - r0 : kRB;
+        tile_dot_q4<F>(blob + lay.p2 + (size_t)t * KG2 * 1024, blob + lay.p2s + (size_t)t * KG2 * sblk, KG2,
+                       ah.data() + r0, nr, res);
+        for (int r = 0; r < nr; ++r) std::memcpy(y + (size_t)(r0 + r) * H + 16 * t, res[r], 16 * sizeof(float));
+      }
+  });
+}
+
 }  // namespace
 
 extern "C" {
 
 int moe_cpu_ffn(const void* blob, int wfmt, int H, int I, const void* x, int rows, float* y, int threads) {
   if (!blob || (rows > 0 && (!x || !y)) || rows < 0) return moe::set_error(MOE_EINVAL, "moe_cpu_ffn: null pointer");
-  if (wfmt != MOE_W_BF16 || H <= 0 || I <= 0 || H % 32 != 0 || I % 32 != 0)
-    return moe::set_error(MOE_EINVAL, "moe_cpu_ffn: needs bf16 weights with H, I multiples of 32");
+  const bool q4 = wfmt == MOE_W_INT4 || wfmt == MOE_W_MXFP4;
+  if ((wfmt != MOE_W_BF16 && !q4) || H <= 0 || I <= 0 || H % (q4 ? 128 : 32) != 0 || I % (q4 ? 128 : 32) != 0)
+    return moe::set_error(MOE_EINVAL,
+                          "moe_cpu_ffn: needs bf16 weights with H, I multiples of 32, or int4 / MXFP4 weights "
+                          "with H, I multiples of 128");
   if (rows == 0) return MOE_OK;
   if (threads <= 0) threads = pool().workers() + 1;
+  if (q4) {
+    const char* b = static_cast<const char*>(blob);
+    const uint16_t* xq = static_cast<const uint16_t*>(x);
+    if (wfmt == MOE_W_INT4)
+      cpu_ffn_q4<Q4::kInt4>(b, wfmt, H, I, xq, rows, y, threads);
+    else
+      cpu_ffn_q4<Q4::kMxfp4>(b, wfmt, H, I, xq, rows, y, threads);
+    return MOE_OK;
+  }
   const uint16_t* p1 = static_cast<const uint16_t*>(blob);
   const uint16_t* p2 = p1 + (size_t)2 * H * I;
   const uint16_t* xa = static_cast<const uint16_t*>(x);

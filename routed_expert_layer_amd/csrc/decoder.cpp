@@ -183,8 +183,9 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   const bool split = moe_cache_splits(d->cache);
   if (split && e == hipSuccess) {
     // misses may run on the CPU: it needs this step's activations and token order
-    if (d->dtype != MOE_DT_BF16 || d->wfmt != MOE_W_BF16)
-      return dfail(MOE_EINVAL, "moe_decoder_step: CPU execution of misses needs bf16 activations and weights");
+    if (d->dtype != MOE_DT_BF16 || d->wfmt == MOE_W_F32)
+      return dfail(MOE_EINVAL,
+                   "moe_decoder_step: CPU execution of misses needs bf16 activations and bf16, int4 or MXFP4 weights");
     if (!d->x_host) {
       e = hipHostMalloc(reinterpret_cast<void**>(&d->x_host), sizeof(uint16_t) * d->Tmax * d->H, hipHostMallocDefault);
       if (e == hipSuccess)
@@ -256,10 +257,11 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
       rc = cache_fill_enqueue(d->cache, d->wave_misses.data(), (int)d->wave_misses.size(), d->layer_pool.data(),
                               d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, d->fill, stream, &filled);
       if (rc != MOE_OK) {
-        // this wave's and every later wave's misses were never copied: unmap them
+        // the fill call has unmapped this wave's misses that it could not copy; the later waves' misses
+        // were never copied: unmap them too
         const std::string msg = moe_last_error();
         for (int i = 0; i < nm; ++i)
-          if (d->misses[i].wave >= w) (void)moe_cache_invalidate(d->cache, d->misses[i].key);
+          if (d->misses[i].wave > w) (void)moe_cache_invalidate(d->cache, d->misses[i].key);
         return dfail(rc, "moe_decoder_step: %s", msg.c_str());
       }
       d->fills += (int64_t)d->wave_misses.size();
@@ -274,7 +276,11 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
       if (part == 1) {
         if (!filled) break;
         e = hipStreamWaitEvent(s, filled, 0);
-        if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: wait for fills: %s", hipGetErrorString(e));
+        if (e != hipSuccess) {  // no reader would wait for this wave's copies, and later waves get none
+          for (int i = 0; i < nm; ++i)
+            if (d->misses[i].wave >= w) (void)moe_cache_invalidate(d->cache, d->misses[i].key);
+          return dfail(MOE_EHIP, "moe_decoder_step: wait for fills: %s", hipGetErrorString(e));
+        }
       }
       d->work.clear();
       int rows = 0, pos = 0;

@@ -155,14 +155,25 @@ __device__ __forceinline__ f32x4_t bf16_wave_dot(const char* wp, char* fp, const
 #pragma unroll
     for (int u = 0; u < kU; ++u) acc = mfma_bf16(a[u], b[u], acc);
   }
-  for (; c < c1; ++c) {
-    const u32x4_t a = ld16_nt(wp + (size_t)c * 1024);
-    const u32x4_t b = valid ? ld16(ar + c * 32) : u32x4_t{0u, 0u, 0u, 0u};
+  // The n < kU remaining fragments also go out as one batch: slots past the
+  // end load the last fragment again (a cache hit) against a zero activation.
+  const int n = c1 - c;
+  if (n > 0) {
+    u32x4_t a[kU], b[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int cu = c + (u < n ? u : n - 1);
+      a[u] = ld16_nt(wp + (size_t)cu * 1024);
+      b[u] = (valid && u < n) ? ld16(ar + cu * 32) : u32x4_t{0u, 0u, 0u, 0u};
+    }
     if constexpr (WT) {
-      st16(fp + (size_t)c * 1024, a);
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (u < n) st16(fp + (size_t)(c + u) * 1024, a[u]);
       drain_memory();
     }
-    acc = mfma_bf16(a, b, acc);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) acc = mfma_bf16(a[u], b[u], acc);
   }
   return acc;
 }
@@ -249,19 +260,19 @@ __global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 
 // The registers of one 128-wide K block: activation fragments, and the codes
-// and the four rows' scales of each of the block's kR tiles.
-constexpr int kR = 4;
+// and the four rows' scales of each of the block's kRI tiles.
+constexpr int kRI = 4;  // 16-row tiles per int4 block
 struct Int4Stage {
   u32x4_t b[4];
-  u32x4_t a[kR];
-  uint32_t sc0[kR], sc1[kR];
+  u32x4_t a[kRI];
+  uint32_t sc0[kRI], sc1[kRI];
 };
 
-// Shared body of both int4 projections. A block owns kR consecutive 16-row
+// Shared body of both int4 projections. A block owns kRI consecutive 16-row
 // tiles of one expert; its four waves split K, and each wave applies every
-// activation fragment it loads to all kR tiles (one activation load per kR
+// activation fragment it loads to all kRI tiles (one activation load per kRI
 // KiB of codes). A wave keeps the next K block's loads in flight while it
-// works on the current one. Partial sums meet in LDS; wave w finishes tile w.
+// works on the current one. Partial sums meet in LDS; wave w finishes tiles w, w + 4, ...
 // act_row(m): bf16 activations of row m of the group; the finished 16 x 16
 // tile sums go to `emit(tile, m, sum)`. With WT every code and scale loaded
 // is also stored at the same offset from qf_base / sf_base (the write-through
@@ -280,21 +291,21 @@ __device__ __forceinline__ void int4_decode_tiles(Row act_row, const int4 it, in
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(uniform(q_base), (short)0, -1, 0x00020000);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(uniform(s_base), (short)0, -1, 0x00020000);
   const int vq = lane * 16, vs = (lane >> 4) * 8;
-  __shared__ f32x4_t red[4][kR][64];
+  __shared__ f32x4_t red[4][kRI][64];
   for (int m0 = 0; m0 < it.z; m0 += 16) {
     const int m = m0 + (lane & 15);
     const bool valid = m < it.z;
     const uint16_t* ar = act_row(valid ? m : 0) + kq;
-    f32x4_t acc[kR];
+    f32x4_t acc[kRI];
 #pragma unroll
-    for (int r = 0; r < kR; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < kRI; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // Lanes past the group read the group's first row: a token's column of a product depends only on its own
     // activation column, and the columns of those lanes are never stored.
     auto load = [&](int g, Int4Stage& st) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) st.b[j] = ld16(ar + 128 * g + 32 * j);
 #pragma unroll
-      for (int r = 0; r < kR; ++r) {
+      for (int r = 0; r < kRI; ++r) {
         const int blk = (tile0 + r) * KG + g;
         st.a[r] = __builtin_amdgcn_raw_buffer_load_b128(rq, vq, blk * 1024, 2);  // non-temporal
         // The four fp16 scales are read as two 32-bit words and widened one by
@@ -310,7 +321,7 @@ __device__ __forceinline__ void int4_decode_tiles(Row act_row, const int4 it, in
         const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(uniform(sf_base), (short)0, -1,
                                                                             0x00020000);
 #pragma unroll
-        for (int r = 0; r < kR; ++r) {
+        for (int r = 0; r < kRI; ++r) {
           const int blk = (tile0 + r) * KG + g;
           __builtin_amdgcn_raw_buffer_store_b128(st.a[r], wq, vq, blk * 1024, 0);
           if ((lane & 15) == 0) {
@@ -332,7 +343,7 @@ __device__ __forceinline__ void int4_decode_tiles(Row act_row, const int4 it, in
       matrix_chain_done(u);
       const float u24 = -24.f * u[0];
 #pragma unroll
-      for (int r = 0; r < kR; ++r) {
+      for (int r = 0; r < kRI; ++r) {
         f32x4_t t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) t = mfma_bf16(int4x8_to_bf16x8_biased(st.a[r][j]), st.b[j], t);
@@ -354,11 +365,14 @@ __device__ __forceinline__ void int4_decode_tiles(Row act_row, const int4 it, in
     }
     if (g < g1) compute(s0);
 #pragma unroll
-    for (int r = 0; r < kR; ++r) red[wave][r][lane] = acc[r];
+    for (int r = 0; r < kRI; ++r) red[wave][r][lane] = acc[r];
     __syncthreads();
     if (valid) {
-      const f32x4_t sum = red[0][wave][lane] + red[1][wave][lane] + red[2][wave][lane] + red[3][wave][lane];
-      emit(tile0 + wave, m, sum);
+#pragma unroll
+      for (int t = wave; t < kRI; t += 4) {
+        const f32x4_t sum = red[0][t][lane] + red[1][t][lane] + red[2][t][lane] + red[3][t][lane];
+        emit(tile0 + t, m, sum);
+      }
     }
     __syncthreads();
   }
@@ -369,8 +383,8 @@ __global__ __launch_bounds__(256) void ffn1_decode_int4(const uint16_t* __restri
                                                         const int32_t* __restrict__ perm_src, const W wk,
                                                         const char* __restrict__ slot_base, size_t slot_stride,
                                                         size_t p1s_off, int H, int I, uint16_t* __restrict__ hbuf) {
-  const int NB = I / 8 / kR;  // blocks per expert
-  const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
+  const int NB = I / 8 / kRI;  // blocks per expert
+  const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kRI;
   int4 it;
   if (!wk.get(item, it)) return;
   char* fill;
@@ -394,8 +408,8 @@ __global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restri
                                                         const char* __restrict__ slot_base, size_t slot_stride,
                                                         size_t p2_off, size_t p2s_off, int H, int I,
                                                         float* __restrict__ y) {
-  const int NB = H / 16 / kR;
-  const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kR;
+  const int NB = H / 16 / kRI;
+  const int item = blockIdx.x / NB, tile0 = (blockIdx.x - item * NB) * kRI;
   int4 it;
   if (!wk.get(item, it)) return;
   char* fill;
@@ -417,6 +431,8 @@ __global__ __launch_bounds__(256) void ffn2_decode_int4(const uint16_t* __restri
 // instructions exactly and the result equals a bf16-weight product with the
 // dequantised weights).
 // ---------------------------------------------------------------------------
+
+constexpr int kR = 4;  // 16-row tiles per MXFP4 block
 
 // Eight FP4 codes (nibbles in K order) times 2^(e - 127) as the bf16 A operand.
 __device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t w, float scale) {
@@ -717,12 +733,12 @@ hipError_t decode_kernels(int wfmt, const void* x, const int32_t* perm_src, cons
     return hipGetLastError();
   }
   // int4
-  hipLaunchKernelGGL(ffn1_decode_int4<W>, dim3(n_items * (I / 8 / kR)), dim3(256), 0, s,
+  hipLaunchKernelGGL(ffn1_decode_int4<W>, dim3(n_items * (I / 8 / kRI)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), perm_src, wk, slot_base, slot_stride, L.p1s, H, I,
                      static_cast<uint16_t*>(hbuf));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ffn2_decode_int4<W>, dim3(n_items * (H / 16 / kR)), dim3(256), 0, s,
+  hipLaunchKernelGGL(ffn2_decode_int4<W>, dim3(n_items * (H / 16 / kRI)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(hbuf), wk, slot_base, slot_stride, L.p2, L.p2s, H, I, y);
   return hipGetLastError();
 }

@@ -224,6 +224,26 @@ hipError_t launch_combine(const float* y_perm, const int32_t* perm_pos, const fl
   return hipGetLastError();
 }
 
+// Sets n bytes at p to 0xFF: 16-byte stores over the aligned body, single
+// bytes for a ragged head and tail; fixed grid, grid-stride loop.
+__global__ __launch_bounds__(256) void poison_kernel(char* __restrict__ p, size_t n) {
+  const size_t head = (16 - (reinterpret_cast<uintptr_t>(p) & 15)) & 15;
+  const size_t h = head < n ? head : n;
+  const size_t body = (n - h) / 16;
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (size_t)gridDim.x * blockDim.x;
+  uint4* b = reinterpret_cast<uint4*>(p + h);
+  for (size_t i = tid; i < body; i += stride) b[i] = make_uint4(~0u, ~0u, ~0u, ~0u);
+  if (tid < h) p[tid] = (char)0xFF;
+  const size_t tail0 = h + body * 16;
+  if (tid < n - tail0) p[tail0 + tid] = (char)0xFF;
+}
+
+hipError_t launch_poison(void* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(poison_kernel, dim3(1024), dim3(256), 0, s, static_cast<char*>(p), n);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_fragments(const void* W, int K, int N, void* dst, hipStream_t s) {
   const size_t n = (size_t)(N / 16) * (K / 32) * 64;
   hipLaunchKernelGGL(pack_frag_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,

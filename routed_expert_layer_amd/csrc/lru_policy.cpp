@@ -79,6 +79,15 @@ bool SharedLru::invalidate(int key) {
   return true;
 }
 
+int issue_fills(SharedLru& lru, const int32_t* keys, int n, const std::function<bool(int)>& copy) {
+  for (int i = 0; i < n; ++i) {
+    if (copy(i)) continue;
+    for (int j = i; j < n; ++j) (void)lru.invalidate(keys[j]);
+    return i;
+  }
+  return n;
+}
+
 void plan_resize(const std::vector<int32_t>& slot_key, const std::vector<uint64_t>& recency, int S_new,
                  std::vector<int32_t>& new_key, std::vector<int32_t>& origin, std::vector<Move>& moves,
                  std::vector<int32_t>& evicted) {

@@ -11,6 +11,7 @@
 // each layer-step first; CPU-run misses are not cached.
 #pragma once
 #include <cstdint>
+#include <functional>
 #include <set>
 #include <vector>
 
@@ -64,5 +65,14 @@ class SharedLru {
   int64_t hits_ = 0, misses_ = 0;
   int64_t rate_gpu_ = 1, rate_cpu_ = 0, missed_ = 0, to_gpu_ = 0;
 };
+
+// Issues the copies of one batch of misses, in order, through copy(i) (false:
+// the copy of miss i could not be issued). An entry is never left resident
+// without its blob (page "FreeToken-rtx-4090", component table, row "PCIe
+// link": a miss moves as one complete expert): at the first failure, that
+// miss's key and the keys of every later miss of the batch are dropped from
+// the cache (their slots become free); the misses issued before it stay
+// resident. Returns the number of copies issued.
+int issue_fills(SharedLru& lru, const int32_t* keys, int n, const std::function<bool(int)>& copy);
 
 }  // namespace moe

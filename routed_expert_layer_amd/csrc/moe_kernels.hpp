@@ -111,6 +111,9 @@ bool route_small_path(int T, int E);
 hipError_t launch_pack(int wfmt, int H, int I, const void* W1, const void* W3, const void* W2,
                        const void* s1, const void* s3, const void* s2, void* blob, hipStream_t s);
 
+// Debug: n bytes at p set to 0xFF on stream s.
+hipError_t launch_poison(void* p, size_t n, hipStream_t s);
+
 hipError_t launch_combine(const float* y_perm, const int32_t* perm_pos, const float* w, int T, int k, int H,
                           void* out, bool out_bf16, hipStream_t s);
 

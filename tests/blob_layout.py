@@ -74,3 +74,41 @@ def mxfp4_blob(C1, C3, C2, S1, S3, S2):
     blob[o_p2:o_p2 + len(p2c)] = p2c
     blob[o_p2s:o_p2s + len(p2s)] = p2s
     return blob
+
+
+def _int4_blocks(Q):
+    """Q int8 codes in [-7, 7], [N, K] (rows = output rows) -> bytes in block order: tile, 128-wide K block,
+    lane (row + 16 * group of 8), four words (word j = K 32j + 8 * group + 0..7); nibble p < 4 holds K offset
+    2p and nibble p + 4 K offset 2p + 1, each as q + 8."""
+    N, K = Q.shape
+    c = (Q.astype(np.int32) + 8).astype(np.uint32).reshape(N // 16, 16, K // 128, 4, 4, 8)  # t, r, g, j, grp, k
+    c = c.transpose(0, 2, 4, 1, 3, 5)                                  # t, g, grp, r, j, k
+    nib = np.concatenate([c[..., 0::2], c[..., 1::2]], axis=-1)        # nibble order k0 k2 k4 k6 k1 k3 k5 k7
+    words = (nib << (4 * np.arange(8, dtype=np.uint32))).sum(axis=-1, dtype=np.uint32)
+    return np.ascontiguousarray(words).view(np.uint8).reshape(-1)
+
+
+def _int4_scales(S):
+    """S fp16 scales [N, K/128] -> per tile and 128-wide K block, the 16 rows' scales (32 bytes)."""
+    N, KG = S.shape
+    s = S.reshape(N // 16, 16, KG).transpose(0, 2, 1)                  # t, g, r
+    return np.ascontiguousarray(s).view(np.uint8).reshape(-1)
+
+
+def int4_blob(Q1, Q3, Q2, S1, S3, S2):
+    """uint8 blob of an int4 expert from codes Q1, Q3 [H, I], Q2 [I, H] (int8) and fp16 scales S1, S3
+    [H/128, I], S2 [I/128, H] (numpy): sections P1 codes, P1 scales, P2 codes, P2 scales, 256-byte aligned."""
+    p1c = _int4_blocks(p1_rows(Q1, Q3))
+    p1s = _int4_scales(p1_rows(S1, S3))
+    p2c = _int4_blocks(np.ascontiguousarray(Q2.T))
+    p2s = _int4_scales(np.ascontiguousarray(S2.T))
+    o_p1s = _align(len(p1c), 256)
+    o_p2 = _align(o_p1s + len(p1s), 256)
+    o_p2s = _align(o_p2 + len(p2c), 256)
+    total = _align(o_p2s + len(p2s), 256)
+    blob = np.zeros(total, np.uint8)
+    blob[:len(p1c)] = p1c
+    blob[o_p1s:o_p1s + len(p1s)] = p1s
+    blob[o_p2:o_p2 + len(p2c)] = p2c
+    blob[o_p2s:o_p2s + len(p2s)] = p2s
+    return blob

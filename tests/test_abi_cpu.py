@@ -110,6 +110,23 @@ def test_cache_errors_and_invalidate(L):
     assert len(L.moe_cache_trace(c)) == 0
 
 
+def test_failed_fill_leaves_keys_unmapped(L):
+    """cache_fill_async that cannot issue its copies (here: no pool address for the layer; without a GPU the
+    event set-up fails first) drops the batch's keys, so none stays resident without its blob."""
+    c = L.MoeCache(2, 8, 4)
+    _, ws, _, misses, _ = L.cache_resolve(c, 0, 0, [2])
+    _, ws, _, misses, _ = L.cache_resolve(c, 0, 1, [0, 3, 5])
+    assert ws.tolist() == [1, 2, 3] and len(misses) == 3
+    ms = np.ascontiguousarray(np.asarray(misses, np.int32))
+    lp = L.layer_table([0x1000, 0])  # layer 1 has no pool address
+    rc = L._lib.cache_fill_async(c.h, ms.ctypes.data, len(ms), lp.ctypes.data, 4096, 4096, 0x10000, 4096, None, None)
+    assert rc in (L.MOE_EINVAL, L.MOE_EHIP)
+    assert [L.moe_cache_slot_of(c, 8 + e) for e in (0, 3, 5)] == [-1, -1, -1]
+    assert L.moe_cache_slot_of(c, 2) == 0  # an earlier entry is untouched
+    _, ws, _, misses, _ = L.cache_resolve(c, 1, 1, [7])
+    assert ws.tolist() == [1] and misses.tolist() == [[15, 1, -1, 0]]  # lowest free slot
+
+
 def test_argument_validation_without_gpu(L):
     lib = L._lib
     # routing: k > E, bad dtype, workspace too small -- all rejected before any launch

@@ -345,6 +345,22 @@ def test_pack_matches_documented_layout(L):
 
 
 @pytest.mark.gpu
+def test_pack_int4_matches_documented_layout(L):
+    """The GPU packer writes the int4 blob layout the C ABI documents, byte for byte (padding aside)."""
+    from tests.blob_layout import int4_blob
+    cfg = dataclasses.replace(CONFIGS["decode_int4_t8_l8"], name="packi4", H=512, I=384, weights_of=None,
+                              pool_layers=None)
+    w = gen.expert_int4(cfg, 0, 3, "cuda")
+    nb = L.moe_expert_bytes(L.MOE_W_INT4, cfg.H, cfg.I)
+    blob = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    L.moe_pack_expert(L.MOE_W_INT4, cfg.H, cfg.I, w["q1"], w["q3"], w["q2"], w["s1"], w["s3"], w["s2"], blob)
+    torch.cuda.synchronize()
+    ref = int4_blob(*(w[k].cpu().numpy() for k in ("q1", "q3", "q2", "s1", "s3", "s2")))
+    assert len(ref) == nb
+    assert np.array_equal(blob.cpu().numpy(), ref)
+
+
+@pytest.mark.gpu
 def test_pack_mxfp4_matches_documented_layout(L):
     """The GPU packer writes the MXFP4 blob layout the C ABI documents, byte for byte (padding aside)."""
     from tests.blob_layout import mxfp4_blob

@@ -201,12 +201,32 @@ def test_resize_small_all_outputs(native):
 
 
 @pytest.mark.timeout(600)
-def test_split_small_all_outputs():
+@pytest.mark.parametrize("wfmt", ["bf16", "int4", "mxfp4"])
+def test_split_small_all_outputs(wfmt):
     """Misses divided 1:3 between GPU fills and CPU execution; every output checked."""
-    cfg = dataclasses.replace(CONFIGS["decode_bf16_h4096_e256"], name="split_small", L=3, T=4, H=512, I=256, E=32,
-                              k=4, zipf_s=1.0, S=8)
+    cfg = dataclasses.replace(CONFIGS["decode_bf16_h4096_e256"], name=f"split_small_{wfmt}", L=3, T=4, H=512, I=256,
+                              E=32, k=4, zipf_s=1.0, S=8, wfmt=wfmt)
     ref = run_decode(cfg, 24, set(), check_all_outputs=True, split=(1, 3))
     assert (ref[:, 4] < 0).sum() > 10 and (ref[:, 3] == 0).sum() > (ref[:, 4] < 0).sum()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", ["tiny_waves", "split_small"])
+def test_poisoned_fills_all_outputs(case, monkeypatch):
+    """Debug mode: every fill first sets its victim slot to 0xFF bytes (NaN in every weight format), so a kernel
+    that read a slot before its copy landed, or a copy that overwrote a slot still being read, would give
+    non-finite or wrong outputs. Every output of multi-wave layer-steps (the hits' FFN overlapping the copies)
+    and of split layer-steps is checked."""
+    monkeypatch.setenv("MOE_DEBUG_POISON_FILLS", "1")
+    if case == "tiny_waves":
+        cfg = CONFIGS["tiny_f32_h256_e16"]
+        ref = run_decode(cfg, 32, set(), check_all_outputs=True)
+        assert (ref[:, 6] > 0).any()
+    else:
+        cfg = dataclasses.replace(CONFIGS["decode_bf16_h4096_e256"], name="split_small", L=3, T=4, H=512, I=256,
+                                  E=32, k=4, zipf_s=1.0, S=8)
+        ref = run_decode(cfg, 16, set(), check_all_outputs=True, split=(1, 3))
+        assert (ref[:, 4] < 0).any()
 
 
 @pytest.mark.timeout(600)
