@@ -183,6 +183,45 @@ def test_ffn_parity(L, name, wfmt, H, I, rows, mode):
         check_close(yg[a:b], ref, f"{name} expert {e}")
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("wfmt", ["bf16", "int4", "mxfp4"])
+def test_ffn_decode_large_activations(L, wfmt):
+    """Activations 4096 times the usual scale (exact in bf16: a power of two), so that the gate/up sums and the
+    SwiGLU product reach ~1e7, far past the fp16 range: the decode kernels keep them in bf16 / fp32 and still
+    match the oracle."""
+    H, I, rows = 512, 256, [1, 8, 3]
+    cfg = cfg_like("tiny_f32_h256_e16", name=f"ffn_large_{wfmt}", H=H, I=I, E=len(rows), act="bf16", wfmt=wfmt)
+    E, T = len(rows), 12
+    x = (gen.tokens(cfg, 0, 0, dev, T=T).float() * 4096.0).to(torch.bfloat16)
+    r = np.random.default_rng(7)
+    perm_src = np.concatenate([r.integers(0, T, size=n) for n in rows]).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    wf = {"bf16": L.MOE_W_BF16, "int4": L.MOE_W_INT4, "mxfp4": L.MOE_W_MXFP4}[wfmt]
+    stride = (L.moe_expert_bytes(wf, H, I) + 4095) // 4096 * 4096
+    slots = torch.zeros(E * stride, dtype=torch.uint8, device=dev)
+    ex = _experts(cfg, E, wfmt)
+    for e in range(E):
+        w, dst = ex[e], slots[e * stride:]
+        if wfmt == "int4":
+            L.moe_pack_expert(wf, H, I, w["q1"], w["q3"], w["q2"], w["s1"], w["s3"], w["s2"], dst)
+        elif wfmt == "mxfp4":
+            L.moe_pack_expert(wf, H, I, w["c1"], w["c3"], w["c2"], w["s1"], w["s3"], w["s2"], dst)
+        else:
+            L.moe_pack_expert(wf, H, I, w[0], w[1], w[2], None, None, None, dst)
+    work = np.array([[e, e, off[e], rows[e]] for e in range(E)], dtype=np.int32)
+    y = torch.full((int(off[-1]), H), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(L.moe_ffn_workspace_size(int(off[-1]), H, I, wf), dtype=torch.uint8, device=dev)
+    L.moe_ffn(x, torch.from_numpy(perm_src).to(dev), work, slots, stride, wf, H, I, y, ws, L.MOE_FFN_DECODE)
+    torch.cuda.synchronize()
+    yg, x64 = np64(y), np64(x)
+    assert np.isfinite(yg).all()
+    for e in range(E):
+        a, b = off[e], off[e + 1]
+        ref = oracle.swiglu_expert(x64[perm_src[a:b]], *_canon64(ex[e], wfmt))
+        assert np.abs(ref).max() > 1e6  # the range fp16 could not hold
+        check_close(yg[a:b], ref, f"large activations {wfmt} expert {e}")
+
+
 GROUPED_CASES = [
     # name, wfmt, H, I, rows per expert (seeded random when an int: that many experts of 0..maxrows rows)
     ("bf16_ragged", "bf16", 512, 256, [130, 0, 1, 127, 128, 300, 17, 777, 256, 257, 40, 110, 276, 356, 200]),
