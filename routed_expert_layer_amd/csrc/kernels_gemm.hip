@@ -771,8 +771,8 @@ bool grouped_supported(int wfmt, int H, int I) {
 // Both projections of every expert with rows, the work list planned on the
 // device from counts and offsets (no host synchronisation): bf16 weights in
 // the two tile sizes of launch_ffn_prefill2, MXFP4 weights in 128-token tiles.
-// Each GEMM launch is one round of 256 blocks (one per CU) that loops over
-// the super-tiles the planner wrote.
+// Each GEMM launch is a fixed number of rounds of 256 blocks whose blocks
+// loop over the super-tiles the planner wrote.
 hipError_t launch_ffn_grouped(int wfmt, const void* x, const int32_t* perm_src, const int32_t* counts,
                               const int32_t* offsets, const int32_t* slot_of, int E, int n_slots, int rows_max,
                               const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y,
@@ -790,14 +790,17 @@ hipError_t launch_ffn_grouped(int wfmt, const void* x, const int32_t* perm_src, 
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   uint16_t* hb = static_cast<uint16_t*>(hbuf);
   const dim3 block(512);
-  // Rounds of 256 blocks per launch: a block whose slot a super-tile leaves empty moves on to its next round,
-  // so with a single round those blocks' CUs would idle; with 32 / (fewest slots a super-tile can fill) rounds
-  // the blocks of empty slots exit and others take their CUs.
+  // Rounds of 256 blocks per launch. A block whose slot a super-tile leaves empty moves on to its next round,
+  // so with a single round those blocks' CUs would idle: 32 / (fewest slots a super-tile can fill) rounds let
+  // the blocks of empty slots exit and others take their CUs. Eight times that many keeps each block's list of
+  // super-tiles short, so the dispatcher hands the next block to whichever CU frees first and the blocks of a
+  // super-tile stay close to each other in K (one resident 16384-token Zipf layer: 5.24-5.50 ms with the
+  // fewer, longer-lived blocks, 4.95-5.16 ms with these; results bit-identical).
   const auto grid = [](int N, int gm_min) {
     int GM = gm_min, shape = 0;
     supertiles_of(GM * 128, N, 128, shape);  // shape of the smallest super-tile a group of this part gets
     const int fill = (shape & 0xFF) * (shape >> 8);
-    return dim3(256 * (fill >= 32 ? 1 : 32 / fill));
+    return dim3(256 * 8 * (fill >= 32 ? 1 : 32 / fill));
   };
   if (mx) {
     // split 0 puts every group with rows into part 0, planned with 128-token tiles
