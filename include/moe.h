@@ -423,10 +423,19 @@ int moe_clock_record(unsigned long long* sums);
  *   out_dtype; *n_miss (nullable) = fills issued. Blocks the calling thread
  *   until the counts reach the host; the rest is enqueued on `stream`.
  *   On a failed fill the affected keys are invalidated (never half-resident).
- *   Within a wave the FFN of the hits is enqueued before the stream waits for
- *   the wave's fills, so it runs while the misses are copied; the misses'
- *   FFN follows the copies (page "FreeToken-rtx-4090": transfers overlap
- *   computation instead of each expert movement being waited for).
+ *   The hits' FFN never waits for the misses' copies; each wave's misses'
+ *   FFN follows that wave's copies (page "FreeToken-rtx-4090": transfers
+ *   overlap computation instead of each expert movement being waited for).
+ *   For T <= 16 the decoder keeps a copy of the cache's slot table in device
+ *   memory: right after the routing a kernel lists the layer-step's experts
+ *   that the copy shows as resident and their FFN is enqueued at once,
+ *   before the counts reach the host; the host's resolve then checks that
+ *   they are exactly its hits (MOE_EHIP if not) and the copy takes the
+ *   step's fills. The copy is uploaded again whole after any change to the
+ *   cache made other than through this decoder's resolve (invalidation,
+ *   resize); such a change must not happen while a step is being enqueued.
+ *   For T > 16 the hits' FFN of each wave is enqueued after the resolve and
+ *   before the stream waits for the wave's fills.
  *   When the cache splits misses (moe_cache_set_split), the misses assigned
  *   to the CPU run with moe_cpu_ffn from the pool on the calling thread while
  *   the GPU works on the others (bf16 activations with bf16, int4 or MXFP4

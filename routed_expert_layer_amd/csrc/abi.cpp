@@ -81,6 +81,7 @@ int moe_cache_layers(const moe_cache_t* c, int* n_layers) {
 }
 int moe_cache_experts(const moe_cache_t* c) { return c ? c->E : -1; }
 bool moe_cache_splits(const moe_cache_t* c) { return c && c->lru.splits(); }
+uint64_t moe_cache_edits(const moe_cache_t* c) { return c ? c->lru.edits() : 0; }
 
 extern "C" {
 
@@ -285,11 +286,13 @@ int moe_cache_stats(const moe_cache_t* c, int64_t* hits, int64_t* misses) {
 }  // extern "C"
 
 // The copies of cache_fill_async, ordered after every earlier reader on the
-// compute stream; *done (the cache's event) marks their end on the fill
-// stream, and the compute stream is not yet made to wait for it.
+// compute stream (or, with war_after, after that event, which the caller
+// recorded after every reader of the victim slots); *done (the cache's event)
+// marks their end on the fill stream, and the compute stream is not yet made
+// to wait for it.
 int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
                        size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
-                       void* compute_stream, hipEvent_t* done);
+                       void* compute_stream, hipEvent_t* done, hipEvent_t war_after = nullptr);
 
 extern "C" {
 
@@ -310,7 +313,7 @@ int cache_fill_async(moe_cache_t* c, const moe_miss_t* misses, int n, const void
 
 int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
                        size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
-                       void* compute_stream, hipEvent_t* done) {
+                       void* compute_stream, hipEvent_t* done, hipEvent_t war_after) {
   *done = nullptr;
   if (!c || n < 0 || (n > 0 && !misses)) return fail(MOE_EINVAL, "cache_fill_async: bad argument");
   if (n == 0) return MOE_OK;
@@ -334,8 +337,12 @@ int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const vo
   if (e != hipSuccess) return drop_from(0, hip_fail(e, "cache_fill_async: event create"));
   const bool split = fs != cs;
   if (split) {
-    e = hipEventRecord(c->ev_war, cs);
-    if (e == hipSuccess) e = hipStreamWaitEvent(fs, c->ev_war, 0);
+    if (war_after) {
+      e = hipStreamWaitEvent(fs, war_after, 0);
+    } else {
+      e = hipEventRecord(c->ev_war, cs);
+      if (e == hipSuccess) e = hipStreamWaitEvent(fs, c->ev_war, 0);
+    }
     if (e != hipSuccess) return drop_from(0, hip_fail(e, "cache_fill_async: ordering after compute"));
   }
   char* dst = static_cast<char*>(slot_base);

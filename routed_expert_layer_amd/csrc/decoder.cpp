@@ -9,6 +9,7 @@
 
 #include <cstdint>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -21,9 +22,10 @@ extern "C" const char* moe_last_error(void);
 int moe_cache_layers(const moe_cache_t* c, int* n_layers);
 int moe_cache_experts(const moe_cache_t* c);
 bool moe_cache_splits(const moe_cache_t* c);
+uint64_t moe_cache_edits(const moe_cache_t* c);
 int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
                        size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
-                       void* compute_stream, hipEvent_t* done);
+                       void* compute_stream, hipEvent_t* done, hipEvent_t war_after);
 
 namespace {
 // Errors go to the library's per-thread message (moe_last_error).
@@ -65,6 +67,16 @@ struct moe_decoder {
   float* y_host = nullptr;
   std::vector<uint16_t> xg;
   int64_t cpu_runs = 0;
+  // Decode batches (T <= 16): the hits' FFN is enqueued right after the
+  // routing, from a copy of the cache's slot table kept on the GPU, instead
+  // of after the host's resolve; the host's round trip then overlaps it.
+  int32_t* slot_of_dev = nullptr;  // [L*E], the copy the kernels read
+  std::vector<int32_t> slot_of;    // what the GPU copy holds (after the updates enqueued so far)
+  uint64_t slot_of_edits = ~0ull;  // the cache's edit count the copy matches (~0: never uploaded)
+  moe::SlotUpdates pending{};      // updates for the GPU copy, applied by the next routing launch
+  int32_t* hit_n = nullptr;        // device: number of resident-expert items
+  int4* hit_items = nullptr;       // device: [E] items {slot, first row, rows, expert}
+  int n_layers = 0;
 };
 
 extern "C" {
@@ -76,6 +88,8 @@ static void decoder_release(moe_decoder_t* d) {
   if (d->y_host) (void)hipHostFree(d->y_host);
   if (d->fill) (void)hipStreamDestroy(d->fill);
   if (d->ev_counts) (void)hipEventDestroy(d->ev_counts);
+  if (d->slot_of_dev) (void)hipFree(d->slot_of_dev);
+  if (d->hit_n) (void)hipFree(d->hit_n);
   for (hipEvent_t e : d->ev_begin) (void)hipEventDestroy(e);
   for (hipEvent_t e : d->ev_end) (void)hipEventDestroy(e);
   delete d;
@@ -128,6 +142,12 @@ moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, i
   if (e == hipSuccess) e = hipHostGetDevicePointer(reinterpret_cast<void**>(&d->counts_dev), d->counts_host, 0);
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&d->fill, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&d->ev_counts, hipEventDisableTiming);
+  d->n_layers = n_layers;
+  d->slot_of.assign((size_t)n_layers * E, -1);
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&d->slot_of_dev), sizeof(int32_t) * d->slot_of.size());
+  // hit_n, then the items 16-byte aligned
+  if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&d->hit_n), 16 + sizeof(int4) * E);
+  if (e == hipSuccess) d->hit_items = reinterpret_cast<int4*>(reinterpret_cast<char*>(d->hit_n) + 16);
   if (e != hipSuccess) {
     decoder_release(d);
     if (status) *status = dfail(MOE_EHIP, "moe_decoder_create: %s", hipGetErrorString(e));
@@ -167,19 +187,105 @@ static int record_ffn_event(moe_decoder_t* d, bool begin, hipStream_t s, double 
   return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
+// Brings the GPU copy of the slot table in line with the cache when the cache
+// was changed other than by a resolve (invalidation, resize) or has never
+// been copied: a full upload, after the stream has drained so that no queued
+// kernel still reads the copy.
+static int sync_slot_table(moe_decoder_t* d, hipStream_t s) {
+  const uint64_t ed = moe_cache_edits(d->cache);
+  if (ed == d->slot_of_edits) return MOE_OK;
+  for (size_t key = 0; key < d->slot_of.size(); ++key) {
+    int sl = -1;
+    (void)moe_cache_slot_of(d->cache, (int)key, &sl);
+    d->slot_of[key] = sl;
+  }
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess)
+    e = hipMemcpy(d->slot_of_dev, d->slot_of.data(), sizeof(int32_t) * d->slot_of.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: slot table upload: %s", hipGetErrorString(e));
+  d->slot_of_edits = ed;
+  d->pending.n = 0;  // the upload holds them
+  return MOE_OK;
+}
+
+// After the resolve: the experts the GPU listed as resident must be exactly
+// the resolve's hits, in the same slots; then the copy takes this step's
+// fills (the miss's key in its slot, the victim's key out): up to
+// kSlotUpdatesMax of them ride with the next routing launch, the rest go now
+// in their own launches on the stream.
+static int update_slot_table(moe_decoder_t* d, int layer, int n, int nm, hipStream_t s) {
+  for (int i = 0; i < n; ++i) {
+    const int key = layer * d->E + d->work_e[i];
+    bool miss = d->work_slot[i] < 0;
+    for (int j = 0; j < nm && !miss; ++j) miss = d->misses[j].key == key;
+    const int32_t copy = d->slot_of[key];
+    if (miss ? copy >= 0 : copy != d->work_slot[i]) {
+      d->slot_of_edits = ~0ull;  // upload the whole table before the next step
+      return dfail(MOE_EHIP, "moe_decoder_step: the GPU copy of the slot table disagrees with the cache at key %d",
+                   key);
+    }
+  }
+  std::vector<int32_t> touched;
+  for (int j = 0; j < nm; ++j) {
+    const moe_miss_t& m = d->misses[j];
+    if (m.victim >= 0) {
+      d->slot_of[m.victim] = -1;
+      touched.push_back(m.victim);
+    }
+    d->slot_of[m.key] = m.slot;
+    touched.push_back(m.key);
+  }
+  std::sort(touched.begin(), touched.end());
+  touched.erase(std::unique(touched.begin(), touched.end()), touched.end());
+  d->pending.n = (int)std::min<size_t>(moe::kSlotUpdatesMax, touched.size());
+  for (int i = 0; i < d->pending.n; ++i) {
+    d->pending.key[i] = touched[i];
+    d->pending.slot[i] = d->slot_of[touched[i]];
+  }
+  for (size_t i0 = moe::kSlotUpdatesMax; i0 < touched.size(); i0 += moe::kSlotUpdatesMax) {
+    moe::SlotUpdates u;
+    u.n = (int)std::min<size_t>(moe::kSlotUpdatesMax, touched.size() - i0);
+    for (int i = 0; i < u.n; ++i) {
+      u.key[i] = touched[i0 + i];
+      u.slot[i] = d->slot_of[touched[i0 + i]];
+    }
+    const hipError_t e = moe::launch_slot_updates(d->slot_of_dev, u, s);
+    if (e != hipSuccess) {
+      d->slot_of_edits = ~0ull;
+      return dfail(MOE_EHIP, "moe_decoder_step: slot table update: %s", hipGetErrorString(e));
+    }
+  }
+  return MOE_OK;
+}
+
 int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T, const void* Wr, const float* bias,
                      void* out, int out_dtype, void* stream, int* n_miss) {
   if (!d || !x || !Wr || !out) return dfail(MOE_EINVAL, "moe_decoder_step: null argument");
   if (T < 1 || T > d->Tmax) return dfail(MOE_EINVAL, "moe_decoder_step: T=%d outside [1, %d]", T, d->Tmax);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const moe_decoder_buffers_t& b = d->b;
+  // decode batches run the resident experts' FFN ahead of the resolve (below)
+  const bool early_hits = moe::route_small_path(T, d->E);
+  if (early_hits) {
+    const int rc0 = sync_slot_table(d, s);
+    if (rc0 != MOE_OK) return rc0;
+  }
   // routing; the kernels also store the per-expert counts straight into the
   // host-mapped pinned buffer: the one device -> host transfer of the step
   const int32_t seq = d->route_seq = d->route_seq >= 65535 ? 1 : d->route_seq + 1;
   const bool tagged = moe::route_small_path(T, d->E);
+  moe::ResidentList res{};
+  if (early_hits) {
+    res.slot_of = d->slot_of_dev;
+    res.layer = layer;
+    res.n_out = d->hit_n;
+    res.items = d->hit_items;
+    res.updates = d->pending;
+  }
   hipError_t e = moe::launch_route(x, d->dtype == MOE_DT_BF16, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w,
                                    b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s,
-                                   d->counts_dev, seq);
+                                   d->counts_dev, seq, early_hits ? &res : nullptr);
+  if (e == hipSuccess) d->pending.n = 0;
   const bool split = moe_cache_splits(d->cache);
   if (split && e == hipSuccess) {
     // misses may run on the CPU: it needs this step's activations and token order
@@ -203,6 +309,27 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   }
   if (e == hipSuccess) e = hipEventRecord(d->ev_counts, s);
   if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: routing: %s", hipGetErrorString(e));
+  // The experts the GPU copy of the slot table shows as resident are the coming resolve's hits: the routing
+  // kernel lists them and their FFN runs right after the routing, so it overlaps the counts' trip to the host,
+  // the resolve and the fills' set-up instead of following them. The first wave's fills wait only for the work
+  // before this FFN (their victims are never this step's hits); later waves' fills wait for everything before.
+  bool prof_open = false;
+  if (early_hits) {
+    // ev_counts (recorded above, before this FFN) also orders the first wave's fills after the earlier readers
+    // profiled calls: every prof_every-th FFN of a layer-step whose experts were all resident; whether this
+    // step is one is known after the resolve, so the events go out when the next such call is due
+    if (d->prof_every > 0 && d->prof_calls % d->prof_every == 0) {
+      if (record_ffn_event(d, true, s, 0) != MOE_OK) return dfail(MOE_EHIP, "moe_decoder_step: profiling event");
+      prof_open = true;
+    }
+    if (e == hipSuccess)
+      e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->hit_n, d->hit_items, std::min(d->E, d->k * T), T,
+                                     static_cast<const char*>(d->slot_base), d->slot_stride, d->H, d->I, b.ffn_ws,
+                                     b.y_perm, s);
+    if (e == hipSuccess && prof_open) e = hipEventRecord(d->ev_end[d->ev_used], s);
+    if (e != hipSuccess)
+      return dfail(MOE_EHIP, "moe_decoder_step: resident experts' FFN: %s", hipGetErrorString(e));
+  }
   int rc;
   if (tagged && !split) {
     // decode batches: every count word carries this step's number, so the counts are complete once all of
@@ -248,14 +375,65 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   rc = cache_resolve(d->cache, step, layer, d->experts.data(), n, d->work_e.data(), d->work_slot.data(),
                      d->work_wave.data(), d->misses.data(), &nm, &nw);
   if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
-  for (int w = 0; w < nw; ++w) {
+  if (early_hits) {
+    rc = update_slot_table(d, layer, n, nm, s);
+    if (rc != MOE_OK) return rc;
+    int hits = 0, rows = 0;
+    for (int i = 0; i < n; ++i)
+      if (d->work_slot[i] >= 0) {
+        ++hits;
+        rows += d->counts[d->work_e[i]];
+      }
+    const bool whole = nm == 0 && hits > 0;
+    if (d->prof_every > 0 && whole && d->prof_calls++ % d->prof_every == 0 && prof_open) {
+      const double a = d->dtype == MOE_DT_BF16 ? 2.0 : 4.0, h = d->wfmt == MOE_W_F32 ? 4.0 : 2.0;
+      d->ev_bytes[d->ev_used] = (double)hits * (double)d->blob_bytes +
+                                (double)rows * (d->H * a + 2.0 * d->I * h + d->H * 4.0);
+      ++d->ev_used;
+    }
+    // each wave's misses: their fills, then their FFN
+    for (int w = 0; w < nw; ++w) {
+      d->wave_misses.clear();
+      for (int i = 0; i < nm; ++i)
+        if (d->misses[i].wave == w) d->wave_misses.push_back(d->misses[i]);
+      if (d->wave_misses.empty()) continue;
+      hipEvent_t filled = nullptr;
+      rc = cache_fill_enqueue(d->cache, d->wave_misses.data(), (int)d->wave_misses.size(), d->layer_pool.data(),
+                              d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, d->fill, stream, &filled,
+                              w == 0 ? d->ev_counts : nullptr);
+      if (rc != MOE_OK) {
+        const std::string msg = moe_last_error();
+        for (int i = 0; i < nm; ++i)
+          if (d->misses[i].wave > w) (void)moe_cache_invalidate(d->cache, d->misses[i].key);
+        return dfail(rc, "moe_decoder_step: %s", msg.c_str());
+      }
+      d->fills += (int64_t)d->wave_misses.size();
+      if (filled) e = hipStreamWaitEvent(s, filled, 0);
+      if (e != hipSuccess) {
+        for (int i = 0; i < nm; ++i)
+          if (d->misses[i].wave >= w) (void)moe_cache_invalidate(d->cache, d->misses[i].key);
+        return dfail(MOE_EHIP, "moe_decoder_step: wait for fills: %s", hipGetErrorString(e));
+      }
+      d->work.clear();
+      for (const moe_miss_t& m : d->wave_misses) {
+        const int ex = m.key - layer * d->E;
+        d->work.push_back(moe_work_t{ex, m.slot, d->offs[ex], d->counts[ex]});
+      }
+      rc = moe_ffn(x, d->dtype, b.perm_src, d->work.data(), (int)d->work.size(), d->slot_base, d->slot_stride,
+                   d->wfmt, d->H, d->I, b.y_perm, b.ffn_ws, b.ffn_ws_bytes, MOE_FFN_AUTO, stream);
+      if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
+    }
+  }
+  if (!early_hits) d->slot_of_edits = ~0ull;  // this resolve's changes are not in the GPU copy
+  for (int w = 0; w < nw && !early_hits; ++w) {
     d->wave_misses.clear();
     for (int i = 0; i < nm; ++i)
       if (d->misses[i].wave == w) d->wave_misses.push_back(d->misses[i]);
     hipEvent_t filled = nullptr;
     if (!d->wave_misses.empty()) {
       rc = cache_fill_enqueue(d->cache, d->wave_misses.data(), (int)d->wave_misses.size(), d->layer_pool.data(),
-                              d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, d->fill, stream, &filled);
+                              d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, d->fill, stream, &filled,
+                              nullptr);
       if (rc != MOE_OK) {
         // the fill call has unmapped this wave's misses that it could not copy; the later waves' misses
         // were never copied: unmap them too

@@ -66,4 +66,25 @@ __device__ __forceinline__ u32x4_t int4x8_to_bf16x8_biased(uint32_t w) {
   return r;
 }
 
+// Rank of this thread's flag among the set flags of a block of NW waves (in
+// thread order) and their total; `cnt` is LDS scratch of NW ints. Every
+// thread of the block must call it.
+template <int NW>
+__device__ __forceinline__ int block_flag_rank(bool f, int* cnt, int& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint64_t m = __ballot(f);
+  const int below = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) cnt[wv] = __popcll(m);
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < NW; ++w) {
+    const int c = cnt[w];
+    base += w < wv ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return base + below;
+}
+
 }  // namespace moe

@@ -21,23 +21,8 @@ namespace {
 constexpr int kResolveThreads = 1024;
 constexpr uint64_t kOccupied = 1ull << 62;  // slot order key: free slots (their index) before any stamp
 
-// Rank of this thread's flag among the block's set flags (thread order) and
-// their total. `cnt` is LDS scratch of 16 ints.
 __device__ __forceinline__ int flag_rank(bool f, int* cnt, int& total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const uint64_t m = __ballot(f);
-  const int below = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) cnt[wv] = __popcll(m);
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int w = 0; w < kResolveThreads / 64; ++w) {
-    const int c = cnt[w];
-    base += w < wv ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  total = tot;
-  return base + below;
+  return block_flag_rank<kResolveThreads / 64>(f, cnt, total);
 }
 
 __device__ __forceinline__ void wave_argmin(uint64_t& v, int& s) {
@@ -174,7 +159,20 @@ __global__ __launch_bounds__(256) void dev_fill_kernel(const int32_t* __restrict
   }
 }
 
+// slot_of[key] = slot for each of the u.n distinct keys listed.
+__global__ __launch_bounds__(64) void slot_update_kernel(int32_t* __restrict__ slot_of, const SlotUpdates u) {
+  const int i = threadIdx.x;
+  if (i < u.n) slot_of[u.key[i]] = u.slot[i];
+}
+
 }  // namespace
+
+hipError_t launch_slot_updates(int32_t* slot_of, const SlotUpdates& u, hipStream_t s) {
+  if (u.n <= 0) return hipSuccess;
+  if (u.n > kSlotUpdatesMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(slot_update_kernel, dim3(1), dim3(64), 0, s, slot_of, u);
+  return hipGetLastError();
+}
 
 hipError_t launch_dev_resolve(const int32_t* counts, const int32_t* offsets, int E, int layer, const DevCache& c,
                               hipStream_t s) {

@@ -377,7 +377,8 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm_src,
                                                            int32_t* __restrict__ perm_pos,
-                                                           int32_t* __restrict__ counts_mirror, int32_t mirror_seq) {
+                                                           int32_t* __restrict__ counts_mirror, int32_t mirror_seq,
+                                                           const ResidentList res) {
   __shared__ float lg[kSmallT * kSmallE];
   __shared__ int32_t sidx[kSmallT * 16];
   __shared__ unsigned long long bm[kSmallE];
@@ -387,6 +388,9 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const float bias_first = (bias && tid < T * E) ? bias[tid % E] : 0.f;  // issued early
   for (int e = tid; e < E; e += 1024) bm[e] = 0ull;
+  // the slot table copy's pending updates, for the kernels that follow (this kernel reads them from its
+  // arguments, below)
+  if (res.slot_of != nullptr && tid < res.updates.n) res.slot_of[res.updates.key[tid]] = res.updates.slot[tid];
   // logits: G threads per (t, e) each add a contiguous range of the partials
   // (16 loads in flight), then the G range sums are added in range order.
   {
@@ -471,6 +475,21 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
     if (counts_mirror) counts_mirror[tid] = (int32_t)(((uint32_t)mirror_seq << 16) | (uint32_t)c);
   }
   if (tid == 0) offsets[E] = T * k;
+  if (res.slot_of != nullptr) {
+    // the experts with tokens that the slot table copy shows as resident, as FFN work items
+    __shared__ int rcnt[16];
+    int slot = -1;
+    if (tid < E && c > 0) {
+      const int key = res.layer * E + tid;
+      slot = res.slot_of[key];
+      for (int i = 0; i < res.updates.n; ++i)
+        if (res.updates.key[i] == key) slot = res.updates.slot[i];
+    }
+    int total = 0;
+    const int r = block_flag_rank<16>(slot >= 0, rcnt, total);
+    if (slot >= 0) res.items[r] = make_int4(slot, excl, c, tid);
+    if (tid == 0) *res.n_out = total;
+  }
   __syncthreads();
   // positions: rank of a token inside its expert = earlier tokens in its mask
   if (tid < T * k) {
@@ -536,8 +555,14 @@ size_t route_workspace_bytes(int T, int H, int E, int k) {
 hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
                         int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s, int32_t* counts_mirror,
-                        int32_t mirror_seq) {
+                        int32_t mirror_seq, const ResidentList* resident) {
   const RoutePlan p = plan_route(T, H, E, bf16);
+  ResidentList res{};
+  if (resident != nullptr) {
+    if (p.mode != 0 || resident->updates.n < 0 || resident->updates.n > kSlotUpdatesMax)
+      return hipErrorInvalidValue;
+    res = *resident;
+  }
   char* w = static_cast<char*>(ws);
   float* partial = reinterpret_cast<float*>(w);
   int32_t* hist = reinterpret_cast<int32_t*>(w + p.hist_off);
@@ -552,7 +577,7 @@ hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* b
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     hipLaunchKernelGGL(route_finish_small, dim3(1), dim3(1024), 0, s, partial, T > 0 ? p.nsplit : 0, bias, T, E, k,
-                       topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos, counts_mirror, mirror_seq);
+                       topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos, counts_mirror, mirror_seq, res);
     return hipGetLastError();
   }
   if (p.mode == 1) {

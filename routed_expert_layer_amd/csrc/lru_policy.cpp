@@ -76,6 +76,7 @@ bool SharedLru::invalidate(int key) {
   key_slot_[key] = -1;
   slot_key_[s] = -1;
   free_.insert(s);
+  ++edits_;
   return true;
 }
 
@@ -119,6 +120,7 @@ void plan_resize(const std::vector<int32_t>& slot_key, const std::vector<uint64_
 }
 
 void SharedLru::resize(int S_new, std::vector<Move>& moves) {
+  ++edits_;
   // recency rank of every occupied slot, from the list (least recent first)
   std::vector<uint64_t> rank(S_, 0);
   std::vector<int> order;  // occupied slots, least recent first

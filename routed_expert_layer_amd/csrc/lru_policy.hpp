@@ -50,6 +50,10 @@ class SharedLru {
   // Resize to S_new slots (plan_resize); recency order kept. Appends the moves.
   void resize(int S_new, std::vector<Move>& moves);
   int capacity() const { return S_; }
+  // Number of changes to the slot table made other than by resolve
+  // (invalidations and resizes): a copy of the table kept elsewhere is stale
+  // once this moves.
+  uint64_t edits() const { return edits_; }
   int64_t hits() const { return hits_; }
   int64_t misses() const { return misses_; }
 
@@ -64,6 +68,7 @@ class SharedLru {
   std::set<int> free_;
   int64_t hits_ = 0, misses_ = 0;
   int64_t rate_gpu_ = 1, rate_cpu_ = 0, missed_ = 0, to_gpu_ = 0;
+  uint64_t edits_ = 0;
 };
 
 // Issues the copies of one batch of misses, in order, through copy(i) (false:

@@ -98,13 +98,31 @@ constexpr size_t kTableBytes = (sizeof(GemmTable) + 255) / 256 * 256;
 // Launchers (return hipError_t of the launch).
 // ---------------------------------------------------------------------------
 size_t route_workspace_bytes(int T, int H, int E, int k);
+// The host-driven decoder's copy of the cache's slot table on the GPU
+// (slot_of[key], -1: not resident): updates to it (distinct keys), and the
+// list of a layer-step's experts it shows as resident, as FFN work items
+// {slot, first row, rows, expert} in ascending expert order.
+constexpr int kSlotUpdatesMax = 64;
+struct SlotUpdates {
+  int n;
+  int32_t key[kSlotUpdatesMax], slot[kSlotUpdatesMax];
+};
+struct ResidentList {
+  int32_t* slot_of;     // nullptr: no list
+  int layer;
+  int32_t* n_out;
+  int4* items;          // [E]
+  SlotUpdates updates;  // applied to slot_of before the list is made
+};
 hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
                         int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s,
                         // optional host-mapped copy of counts: for batches of at most 16 tokens and 512 experts
                         // (route_small_path) each word is (mirror_seq << 16) | count, mirror_seq in 1..65535;
                         // for other batches plain counts
-                        int32_t* counts_mirror = nullptr, int32_t mirror_seq = 0);
+                        int32_t* counts_mirror = nullptr, int32_t mirror_seq = 0,
+                        // optional, decode-size path only: the resident experts' work list (see ResidentList)
+                        const ResidentList* resident = nullptr);
 // Whether launch_route takes the decode-size path (and tags its counts mirror).
 bool route_small_path(int T, int E);
 
@@ -194,6 +212,8 @@ struct DevCache {
   int64_t trace_cap;
 };
 // One layer-step of the policy on the device (one workgroup; E <= 1024).
+hipError_t launch_slot_updates(int32_t* slot_of, const SlotUpdates& u, hipStream_t s);
+
 hipError_t launch_dev_resolve(const int32_t* counts, const int32_t* offsets, int E, int layer, const DevCache& c,
                               hipStream_t s);
 // Copies the last resolve's misses from `pool` (device-visible address of the
