@@ -287,12 +287,14 @@ int moe_cache_stats(const moe_cache_t* c, int64_t* hits, int64_t* misses) {
 
 // The copies of cache_fill_async, ordered after every earlier reader on the
 // compute stream (or, with war_after, after that event, which the caller
-// recorded after every reader of the victim slots); *done (the cache's event)
-// marks their end on the fill stream, and the compute stream is not yet made
-// to wait for it.
+// recorded after every reader of the victim slots; with readers_done, after
+// nothing: the caller has seen every reader of the victim slots complete);
+// *done (the cache's event) marks their end on the fill stream, and the
+// compute stream is not yet made to wait for it.
 int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
                        size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
-                       void* compute_stream, hipEvent_t* done, hipEvent_t war_after = nullptr);
+                       void* compute_stream, hipEvent_t* done, hipEvent_t war_after = nullptr,
+                       bool readers_done = false);
 
 extern "C" {
 
@@ -313,7 +315,7 @@ int cache_fill_async(moe_cache_t* c, const moe_miss_t* misses, int n, const void
 
 int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
                        size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
-                       void* compute_stream, hipEvent_t* done, hipEvent_t war_after) {
+                       void* compute_stream, hipEvent_t* done, hipEvent_t war_after, bool readers_done) {
   *done = nullptr;
   if (!c || n < 0 || (n > 0 && !misses)) return fail(MOE_EINVAL, "cache_fill_async: bad argument");
   if (n == 0) return MOE_OK;
@@ -336,7 +338,7 @@ int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const vo
   if (e == hipSuccess && !c->ev_done) e = hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming);
   if (e != hipSuccess) return drop_from(0, hip_fail(e, "cache_fill_async: event create"));
   const bool split = fs != cs;
-  if (split) {
+  if (split && !readers_done) {
     if (war_after) {
       e = hipStreamWaitEvent(fs, war_after, 0);
     } else {

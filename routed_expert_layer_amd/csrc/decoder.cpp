@@ -25,7 +25,7 @@ bool moe_cache_splits(const moe_cache_t* c);
 uint64_t moe_cache_edits(const moe_cache_t* c);
 int cache_fill_enqueue(moe_cache_t* c, const moe_miss_t* misses, int n, const void* const* layer_pool,
                        size_t blob_stride, size_t blob_bytes, void* slot_base, size_t slot_stride, void* fill_stream,
-                       void* compute_stream, hipEvent_t* done, hipEvent_t war_after);
+                       void* compute_stream, hipEvent_t* done, hipEvent_t war_after, bool readers_done);
 
 namespace {
 // Errors go to the library's per-thread message (moe_last_error).
@@ -307,7 +307,13 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
     if (e == hipSuccess)
       e = hipMemcpyAsync(d->perm_host, b.perm_src, sizeof(int32_t) * T * d->k, hipMemcpyDeviceToHost, s);
   }
-  if (e == hipSuccess) e = hipEventRecord(d->ev_counts, s);
+  // The counts event: the host waits on it for batches whose counts are not tagged and when misses run on the
+  // CPU. For tagged decode batches with the early hits it is not recorded (every event between two kernels
+  // costs the GPU ~1.5 us): the tagged counts show the routing done, and with it every earlier reader of a slot
+  // (the stream runs in order), so the first wave's fills need no ordering at all; a failed launch is seen by
+  // querying the stream.
+  const bool counts_event = !(early_hits && tagged && !split);
+  if (e == hipSuccess && counts_event) e = hipEventRecord(d->ev_counts, s);
   if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: routing: %s", hipGetErrorString(e));
   // The experts the GPU copy of the slot table shows as resident are the coming resolve's hits: the routing
   // kernel lists them and their FFN runs right after the routing, so it overlaps the counts' trip to the host,
@@ -315,7 +321,7 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   // before this FFN (their victims are never this step's hits); later waves' fills wait for everything before.
   bool prof_open = false;
   if (early_hits) {
-    // ev_counts (recorded above, before this FFN) also orders the first wave's fills after the earlier readers
+    // ev_counts, when recorded (above, before this FFN), also orders the first wave's fills
     // profiled calls: every prof_every-th FFN of a layer-step whose experts were all resident; whether this
     // step is one is known after the resolve, so the events go out when the next such call is due
     if (d->prof_every > 0 && d->prof_calls % d->prof_every == 0) {
@@ -339,8 +345,10 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
       for (int i = 0; i < d->E; ++i)
         e_ok += ((uint32_t)__atomic_load_n(d->counts_host + i, __ATOMIC_ACQUIRE) >> 16) == (uint32_t)seq;
       if (e_ok == d->E) break;
-      if ((spin & 63u) == 0) {
-        e = hipEventQuery(d->ev_counts);
+      // without the event, the stream is queried only after ~2^20 polls (far longer than a routing launch
+      // takes): querying it meanwhile slows the step
+      if ((spin & 63u) == 0 && (counts_event || spin >= (1u << 20))) {
+        e = counts_event ? hipEventQuery(d->ev_counts) : hipStreamQuery(s);
         if (e != hipErrorNotReady) break;
         e = hipSuccess;
       }
@@ -400,7 +408,8 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
       hipEvent_t filled = nullptr;
       rc = cache_fill_enqueue(d->cache, d->wave_misses.data(), (int)d->wave_misses.size(), d->layer_pool.data(),
                               d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, d->fill, stream, &filled,
-                              w == 0 ? d->ev_counts : nullptr);
+                              w == 0 && !counts_event ? nullptr : (w == 0 ? d->ev_counts : nullptr),
+                              w == 0 && !counts_event);
       if (rc != MOE_OK) {
         const std::string msg = moe_last_error();
         for (int i = 0; i < nm; ++i)
@@ -433,7 +442,7 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
     if (!d->wave_misses.empty()) {
       rc = cache_fill_enqueue(d->cache, d->wave_misses.data(), (int)d->wave_misses.size(), d->layer_pool.data(),
                               d->blob_stride, d->blob_bytes, d->slot_base, d->slot_stride, d->fill, stream, &filled,
-                              nullptr);
+                              nullptr, false);
       if (rc != MOE_OK) {
         // the fill call has unmapped this wave's misses that it could not copy; the later waves' misses
         // were never copied: unmap them too
