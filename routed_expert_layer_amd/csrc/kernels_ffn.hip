@@ -34,15 +34,10 @@ struct ArgWork {
     return slot_base + (size_t)it.x * slot_stride;
   }
 };
-// With `pool` set, items from *n_hit on are misses: their blob is read from the
-// host pool (pool + expert * pool_stride, device-visible pinned memory) and
-// written through into their slot, so the fill and the FFN are one pass.
-struct DevWork {
+// A work list in device memory: *n items; the grid is sized for the most there can be and surplus blocks exit.
+struct DevList {
   const int32_t* n;
   const int4* items;
-  const int32_t* n_hit;
-  const char* pool;
-  size_t pool_stride;
   __device__ __forceinline__ bool get(int i, int4& it) const {
     if (i >= *n) return false;
     const int4 v = items[i];  // the same item for the whole block: keep it in scalar registers
@@ -50,6 +45,23 @@ struct DevWork {
                    __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
     return true;
   }
+};
+// Resident experts only: every item's blob is in its slot, so the kernels built for this source have no
+// write-through path (fewer registers, so more waves per SIMD, and half the LDS of the DevWork ones).
+struct DevHits : DevList {
+  __device__ __forceinline__ const char* src(int, const int4& it, const char* slot_base, size_t slot_stride,
+                                             char*& fill) const {
+    fill = nullptr;
+    return slot_base + (size_t)it.x * slot_stride;
+  }
+};
+// With `pool` set, items from *n_hit on are misses: their blob is read from the
+// host pool (pool + expert * pool_stride, device-visible pinned memory) and
+// written through into their slot, so the fill and the FFN are one pass.
+struct DevWork : DevList {
+  const int32_t* n_hit;
+  const char* pool;
+  size_t pool_stride;
   __device__ __forceinline__ const char* src(int i, const int4& it, const char* slot_base, size_t slot_stride,
                                              char*& fill) const {
     char* slot = const_cast<char*>(slot_base) + (size_t)it.x * slot_stride;
@@ -759,9 +771,12 @@ hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_sr
                                  size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s,
                                  const int32_t* n_hit, const char* pool, size_t pool_stride) {
   if (max_items == 0) return hipSuccess;
-  if (wfmt == 0 && pool != nullptr) return hipErrorInvalidValue;  // the fp32 kernels do not write through
-  return decode_kernels(wfmt, x, perm_src, DevWork{n_items, items, n_hit, pool, pool_stride}, max_items, max_rows,
-                        slot_base, slot_stride, H, I, hbuf, y, s);
+  if (pool == nullptr)
+    return decode_kernels(wfmt, x, perm_src, DevHits{{n_items, items}}, max_items, max_rows, slot_base, slot_stride,
+                          H, I, hbuf, y, s);
+  if (wfmt == 0) return hipErrorInvalidValue;  // the fp32 kernels do not write through
+  return decode_kernels(wfmt, x, perm_src, DevWork{{n_items, items}, n_hit, pool, pool_stride}, max_items,
+                        max_rows, slot_base, slot_stride, H, I, hbuf, y, s);
 }
 
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,

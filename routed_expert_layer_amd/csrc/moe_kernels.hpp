@@ -143,7 +143,9 @@ hipError_t launch_ffn_decode(int wfmt, const void* x, const int32_t* perm_src, c
 // `items` (device), at most max_items of them with at most max_rows rows
 // each; launch shapes depend only on max_items and max_rows. With `pool`
 // set (not for fp32), items from *n_hit on are misses whose blob is read
-// from pool + expert * pool_stride and written through into their slot.
+// from pool + expert * pool_stride and written through into their slot;
+// without it every item is resident and the kernels have no write-through
+// path.
 hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
                                  const int4* items, int max_items, int max_rows, const char* slot_base,
                                  size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s,
