@@ -87,13 +87,17 @@ def decode_ffn_digest(root):
     parts = ["\n".join(helpers),
              _definition(ffn, "__global__ __launch_bounds__(256) void ffn1_decode_bf16("),
              _definition(ffn, "__global__ __launch_bounds__(256) void ffn2_decode_bf16("),
+             _definition(ffn, "__global__ __launch_bounds__(1024) void ffn2_combine_bf16("),
+             ffn[ffn.index("constexpr int kFuseWaves ="):].split("\n", 1)[0],
+             _definition(ffn, "bool ffn_combine_ok("), _definition(ffn, "hipError_t launch_ffn_decode_hits_combine("),
              _definition(ffn, "hipError_t launch_ffn_decode("),
              _definition(ffn, "hipError_t launch_ffn_decode_dev("),
              _definition(ffn, "hipError_t decode_kernels("), _definition(ffn, "struct ArgWork"),
              _definition(ffn, "struct DevList"), _definition(ffn, "struct DevHits"),
              _definition(ffn, "struct DevWork"), _definition(ffn, "f32x4_t bf16_wave_dot("),
              _definition(ffn, "void st16("), ffn[ffn.index("constexpr int kU ="):].split("\n", 1)[0],
-             _definition(hdr, "struct WorkArgs"), _definition(hdr, "inline BlobLayout blob_layout(")]
+             _definition(hdr, "struct WorkArgs"), _definition(hdr, "inline BlobLayout blob_layout("),
+             hdr[hdr.index("constexpr int kFuseItems ="):].split("\n", 1)[0]]
     return hashlib.sha256("\n".join(parts).encode()).hexdigest()
 
 
@@ -853,7 +857,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens_per_step": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "intermediate": cfg.I, "top_k": cfg.k, "cache_slots": cfg.S, "router_zipf_s": cfg.zipf_s},
-        "roofline": {"kernel": "decode expert FFN: ffn1_decode_bf16 + ffn2_decode_bf16 (the resident experts' call of a layer-step whose six experts were all resident, enqueued behind the routing with its work list in HBM)",
+        "roofline": {"kernel": "decode expert FFN: ffn1_decode_bf16 + ffn2_combine_bf16 (the resident experts' FFN of a layer-step whose six experts were all resident, enqueued behind the routing with its work list in HBM; the down projection also forms the step's weighted output)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__))),

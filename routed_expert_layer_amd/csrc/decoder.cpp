@@ -262,6 +262,8 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
                      void* out, int out_dtype, void* stream, int* n_miss) {
   if (!d || !x || !Wr || !out) return dfail(MOE_EINVAL, "moe_decoder_step: null argument");
   if (T < 1 || T > d->Tmax) return dfail(MOE_EINVAL, "moe_decoder_step: T=%d outside [1, %d]", T, d->Tmax);
+  if (out_dtype != MOE_DT_F32 && out_dtype != MOE_DT_BF16)
+    return dfail(MOE_EINVAL, "moe_decoder_step: out_dtype %d is neither MOE_DT_F32 nor MOE_DT_BF16", out_dtype);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const moe_decoder_buffers_t& b = d->b;
   // decode batches run the resident experts' FFN ahead of the resolve (below)
@@ -320,6 +322,9 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
   // the resolve and the fills' set-up instead of following them. The first wave's fills wait only for the work
   // before this FFN (their victims are never this step's hits); later waves' fills wait for everything before.
   bool prof_open = false;
+  // bf16 decode steps of few experts: the resident experts' down projection also forms the step's output when
+  // no expert is missing, and the combine launch is then left out
+  const bool fused = early_hits && moe::ffn_combine_ok(d->wfmt, d->H, d->I, std::min(d->E, d->k * T), T, d->k);
   if (early_hits) {
     // ev_counts, when recorded (above, before this FFN), also orders the first wave's fills
     // profiled calls: every prof_every-th FFN of a layer-step whose experts were all resident; whether this
@@ -328,7 +333,12 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
       if (record_ffn_event(d, true, s, 0) != MOE_OK) return dfail(MOE_EHIP, "moe_decoder_step: profiling event");
       prof_open = true;
     }
-    if (e == hipSuccess)
+    if (e == hipSuccess && fused)
+      e = moe::launch_ffn_decode_hits_combine(x, b.perm_src, d->hit_n, d->hit_items, std::min(d->E, d->k * T), T,
+                                              static_cast<const char*>(d->slot_base), d->slot_stride, d->H, d->I,
+                                              b.ffn_ws, b.y_perm, d->hit_n + 1, b.perm_pos, b.topk_w, d->k, out,
+                                              out_dtype == MOE_DT_BF16, s);
+    else if (e == hipSuccess)
       e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->hit_n, d->hit_items, std::min(d->E, d->k * T), T,
                                      static_cast<const char*>(d->slot_base), d->slot_stride, d->H, d->I, b.ffn_ws,
                                      b.y_perm, s);
@@ -396,7 +406,8 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
     if (d->prof_every > 0 && whole && d->prof_calls++ % d->prof_every == 0 && prof_open) {
       const double a = d->dtype == MOE_DT_BF16 ? 2.0 : 4.0, h = d->wfmt == MOE_W_F32 ? 4.0 : 2.0;
       d->ev_bytes[d->ev_used] = (double)hits * (double)d->blob_bytes +
-                                (double)rows * (d->H * a + 2.0 * d->I * h + d->H * 4.0);
+                                (double)rows * (d->H * a + 2.0 * d->I * h + d->H * 4.0) +
+                                (fused ? (double)T * d->H * (out_dtype == MOE_DT_BF16 ? 2.0 : 4.0) : 0.0);
       ++d->ev_used;
     }
     // each wave's misses: their fills, then their FFN
@@ -514,8 +525,10 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
     if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: CPU rows to the GPU: %s", hipGetErrorString(e));
     ++d->cpu_runs;
   }
-  rc = moe_combine(b.y_perm, b.perm_pos, b.topk_w, T, d->k, d->H, out, out_dtype, stream);
-  if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
+  if (!(fused && nm == 0)) {  // with every expert resident the fused launch has written `out`
+    rc = moe_combine(b.y_perm, b.perm_pos, b.topk_w, T, d->k, d->H, out, out_dtype, stream);
+    if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
+  }
   if (n_miss) *n_miss = nm;
   return MOE_OK;
 }

@@ -263,6 +263,95 @@ __global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restri
   }
 }
 
+// Down projection and weighted combine of up to kFuseItems resident experts,
+// in one launch: workgroup = 16 output columns (one 16-row tile of every
+// item's P2), sixteen waves each taking F = I / 512 consecutive fragments of
+// every item, two items per batch of loads. The waves' partial tiles meet in
+// LDS and are summed in wave order; each item's rows go to y as in
+// ffn2_decode_bf16 and to an LDS copy indexed by permuted row. When every
+// expert of the step is listed (*n_active == *wk.n), the block then forms its
+// 16 columns of out[t] = sum over j of w[t, j] y[pos[t, j]], j ascending, the
+// combine kernel's own arithmetic, so the separate combine launch is not
+// needed.
+constexpr int kFuseWaves = 16, kFuseRows = 128;
+template <typename W, int F>
+__global__ __launch_bounds__(1024) void ffn2_combine_bf16(const uint16_t* __restrict__ hbuf, const W wk,
+                                                          const char* __restrict__ slot_base, size_t slot_stride,
+                                                          size_t p2_off, int H, int I, float* __restrict__ y,
+                                                          const int32_t* __restrict__ n_active,
+                                                          const int32_t* __restrict__ perm_pos,
+                                                          const float* __restrict__ topk_w, int T, int k,
+                                                          void* __restrict__ out, int out_bf16) {
+  static_assert(F >= 1 && 2 * F <= kU, "two items' fragments per batch");
+  __shared__ f32x4_t red[kFuseWaves][kFuseItems][64];
+  __shared__ float ylds[kFuseRows][16];
+  const int tile = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int KC = I / 32;
+  const int n = min(*wk.n, kFuseItems);
+  const int m = lane & 15, kq = (lane >> 4) * 8;
+  const size_t toff = p2_off + ((size_t)tile * KC + (size_t)F * wave) * 1024 + lane * 16;
+  for (int i = 0; i < n; i += 2) {
+    const bool two = i + 1 < n;
+    int4 ia, ib;
+    (void)wk.get(i, ia);
+    if (two) (void)wk.get(i + 1, ib);
+    char* fill;
+    const char* wa = wk.src(i, ia, slot_base, slot_stride, fill) + toff;
+    const bool va = m < ia.z;
+    const uint16_t* ha = hbuf + (size_t)(ia.y + (va ? m : 0)) * I + kq + 32 * F * wave;
+    u32x4_t a[2 * F], b[2 * F];
+#pragma unroll
+    for (int u = 0; u < F; ++u) {
+      a[u] = ld16_nt(wa + (size_t)u * 1024);
+      b[u] = va ? ld16(ha + 32 * u) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    if (two) {
+      const char* wb = wk.src(i + 1, ib, slot_base, slot_stride, fill) + toff;
+      const bool vb = m < ib.z;
+      const uint16_t* hb = hbuf + (size_t)(ib.y + (vb ? m : 0)) * I + kq + 32 * F * wave;
+#pragma unroll
+      for (int u = 0; u < F; ++u) {
+        a[F + u] = ld16_nt(wb + (size_t)u * 1024);
+        b[F + u] = vb ? ld16(hb + 32 * u) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < F; ++u) sb = mfma_bf16(a[F + u], b[F + u], sb);
+    }
+#pragma unroll
+    for (int u = 0; u < F; ++u) sa = mfma_bf16(a[u], b[u], sa);
+    red[wave][i][lane] = sa;
+    if (two) red[wave][i + 1][lane] = sb;
+  }
+  __syncthreads();
+  if (wave < n) {  // item `wave`: its 16 x 16 tile summed over the waves in order
+    int4 it;
+    (void)wk.get(wave, it);
+    f32x4_t sum = red[0][wave][lane];
+#pragma unroll
+    for (int v = 1; v < kFuseWaves; ++v) sum += red[v][wave][lane];
+    if (m < it.z) {
+      const int row = it.y + m;
+      *reinterpret_cast<f32x4_t*>(y + (size_t)row * H + 16 * tile + 4 * (lane >> 4)) = sum;
+      *reinterpret_cast<f32x4_t*>(&ylds[row][4 * (lane >> 4)]) = sum;
+    }
+  }
+  __syncthreads();
+  if (*n_active != n) return;  // a missing expert's rows come later; the step's combine runs on its own
+  const int tid = threadIdx.x;
+  if (tid < T * 16) {
+    const int t = tid >> 4, c = tid & 15;
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) acc = fmaf(topk_w[t * k + j], ylds[perm_pos[t * k + j]][c], acc);
+    const size_t o = (size_t)t * H + 16 * tile + c;
+    if (out_bf16)
+      reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16(acc);
+    else
+      reinterpret_cast<float*>(out)[o] = acc;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // int4 decode kernels (bf16 activations and SwiGLU product as in the bf16
 // path; codes enter bf16 matrix-core products exactly as 1 + n/16, and each
@@ -777,6 +866,47 @@ hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_sr
   if (wfmt == 0) return hipErrorInvalidValue;  // the fp32 kernels do not write through
   return decode_kernels(wfmt, x, perm_src, DevWork{{n_items, items}, n_hit, pool, pool_stride}, max_items,
                         max_rows, slot_base, slot_stride, H, I, hbuf, y, s);
+}
+
+bool ffn_combine_ok(int wfmt, int H, int I, int max_items, int T, int k) {
+  return wfmt == 1 && H % 16 == 0 && I % 512 == 0 && I / 512 <= kU / 2 && max_items <= kFuseItems && T >= 1 &&
+         T <= 16 && k >= 1 && T * k <= kFuseRows;
+}
+
+hipError_t launch_ffn_decode_hits_combine(const void* x, const int32_t* perm_src, const int32_t* n_items,
+                                          const int4* items, int max_items, int T, const char* slot_base,
+                                          size_t slot_stride, int H, int I, void* hbuf, float* y_perm,
+                                          const int32_t* n_active, const int32_t* perm_pos, const float* topk_w,
+                                          int k, void* out, bool out_bf16, hipStream_t s) {
+  if (!ffn_combine_ok(1, H, I, max_items, T, k)) return hipErrorInvalidValue;
+  const DevHits wk{{n_items, items}};
+  const BlobLayout L = blob_layout(1, H, I);
+  hipLaunchKernelGGL(ffn1_decode_bf16<DevHits>, dim3(max_items * (I / 8)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), perm_src, wk, slot_base, slot_stride, H, I,
+                     static_cast<uint16_t*>(hbuf));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint16_t* h = static_cast<const uint16_t*>(hbuf);
+  const dim3 grid(H / 16), block(64 * kFuseWaves);
+  switch (I / 512) {
+    case 1:
+      hipLaunchKernelGGL((ffn2_combine_bf16<DevHits, 1>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H,
+                         I, y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
+      break;
+    case 2:
+      hipLaunchKernelGGL((ffn2_combine_bf16<DevHits, 2>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H,
+                         I, y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
+      break;
+    case 3:
+      hipLaunchKernelGGL((ffn2_combine_bf16<DevHits, 3>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H,
+                         I, y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
+      break;
+    default:
+      hipLaunchKernelGGL((ffn2_combine_bf16<DevHits, 4>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H,
+                         I, y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
+      break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,

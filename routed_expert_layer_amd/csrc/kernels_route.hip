@@ -485,10 +485,14 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
       for (int i = 0; i < res.updates.n; ++i)
         if (res.updates.key[i] == key) slot = res.updates.slot[i];
     }
-    int total = 0;
+    int total = 0, active = 0;
     const int r = block_flag_rank<16>(slot >= 0, rcnt, total);
     if (slot >= 0) res.items[r] = make_int4(slot, excl, c, tid);
-    if (tid == 0) *res.n_out = total;
+    (void)block_flag_rank<16>(c > 0, rcnt, active);
+    if (tid == 0) {
+      res.n_out[0] = total;
+      res.n_out[1] = active;
+    }
   }
   __syncthreads();
   // positions: rank of a token inside its expert = earlier tokens in its mask

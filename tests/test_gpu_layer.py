@@ -200,6 +200,49 @@ def test_resize_small_all_outputs(native):
     run_decode(cfg, 36, set(), check_all_outputs=True, native=native, resizes={12: 4, 24: 14})
 
 
+def fused_small(I):
+    """Single-token bf16 steps whose down projection forms the output when every expert is resident (6 slots
+    for 16 experts: steps with and without misses alternate)."""
+    return dataclasses.replace(CONFIGS["decode_bf16_h4096_e256"], name=f"fused_small_i{I}", L=2, T=1, H=256, I=I,
+                               E=16, k=4, zipf_s=1.0, epoch=10, S=6)
+
+
+@pytest.mark.parametrize("I", [512, 1024, 1536, 2048])
+def test_fused_combine_all_outputs(I):
+    """Every output of 40 steps x 2 layers against the oracle, for each fragment share per wave (I / 512)."""
+    cfg = fused_small(I)
+    ref = run_decode(cfg, 40, set(), check_all_outputs=True)
+    assert (ref[:, 3] == 0).sum() > 10 and (ref[:, 3] == 1).sum() > 40
+
+
+def test_fused_combine_bf16_output():
+    """Two identical decoders over one pool, one writing fp32 outputs and one bf16: the bf16 output is the
+    fp32 one rounded to nearest even, on steps with every expert resident (fused combine) and with misses
+    (combine kernel) alike."""
+    from routed_expert_layer_amd import _lib as L
+    from routed_expert_layer_amd.runtime import DecodeLayer
+    cfg = fused_small(2048)
+    store = make_store(cfg)
+    try:
+        A = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+        B = DecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+        Wr = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
+        ob = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+        s = torch.cuda.current_stream()
+        misses = 0
+        for step in range(30):
+            for layer in range(cfg.L):
+                b = gen.router_bias(cfg, layer, step, dev)
+                x = gen.tokens(cfg, step, layer, dev)
+                oa = A.step(step, layer, x, Wr[layer], b)
+                misses += L.moe_decoder_step(B.dec, step, layer, x, Wr[layer], b, ob, s)
+                torch.cuda.synchronize()
+                assert torch.equal(ob, oa.to(torch.bfloat16)), f"step {step} layer {layer}"
+        assert 0 < misses < 30 * cfg.L * cfg.k
+    finally:
+        store.close()
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("wfmt", ["bf16", "int4", "mxfp4"])
 def test_split_small_all_outputs(wfmt):
