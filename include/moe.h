@@ -435,7 +435,12 @@ int moe_clock_record(unsigned long long* sums);
  *   cache made other than through this decoder's resolve (invalidation,
  *   resize); such a change must not happen while a step is being enqueued.
  *   For T > 16 the hits' FFN of each wave is enqueued after the resolve and
- *   before the stream waits for the wave's fills.
+ *   before the stream waits for the wave's fills. With bf16 weights, at most
+ *   8 experts in the step (min(E, k*T) <= 8) and I a multiple of 512 up to
+ *   2048, the resident experts' down projection also writes `out` when no
+ *   expert of the step is missing (the combine's sum, in its order), and no
+ *   combine is launched; y_perm still receives every row.
+ *   out_dtype other than MOE_DT_F32 / MOE_DT_BF16 is MOE_EINVAL.
  *   When the cache splits misses (moe_cache_set_split), the misses assigned
  *   to the CPU run with moe_cpu_ffn from the pool on the calling thread while
  *   the GPU works on the others (bf16 activations with bf16, int4 or MXFP4
