@@ -174,9 +174,13 @@ int moe_device_decoder_step(moe_device_decoder_t* d, int layer, const void* x, i
   const int items = d->E < d->k * T ? d->E : d->k * T;
   char* ws = static_cast<char*>(b.ffn_ws);
   void* hbuf = ws;
+  // decode-size batches: the routing launch's last kernel also runs the resolve (one launch fewer)
+  const bool fused_resolve = moe::route_small_path(T, d->E);
+  const moe::DevStep dstep{d->c, layer};
   hipError_t e = moe::launch_route(x, d->dtype == MOE_DT_BF16, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w,
-                                   b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s, nullptr);
-  if (e == hipSuccess) e = moe::launch_dev_resolve(b.counts, b.offsets, d->E, layer, d->c, s);
+                                   b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s, nullptr, 0,
+                                   nullptr, fused_resolve ? &dstep : nullptr);
+  if (e == hipSuccess && !fused_resolve) e = moe::launch_dev_resolve(b.counts, b.offsets, d->E, layer, d->c, s);
   if (d->wfmt == MOE_W_F32) {
     // fp32 experts: the misses are copied first, then every item runs from its slot
     if (e == hipSuccess)

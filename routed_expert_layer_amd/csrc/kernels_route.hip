@@ -7,6 +7,7 @@
 // l = x.Wr + b, the k largest logits (ties to the lower expert index) and
 // softmax weights renormalised over the selected k.
 #include "dev_common.hpp"
+#include "dev_resolve.hpp"
 #include "moe_kernels.hpp"
 
 namespace moe {
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
                                                            int32_t* __restrict__ perm_src,
                                                            int32_t* __restrict__ perm_pos,
                                                            int32_t* __restrict__ counts_mirror, int32_t mirror_seq,
-                                                           const ResidentList res) {
+                                                           const ResidentList res, const DevStep dev) {
   __shared__ float lg[kSmallT * kSmallE];
   __shared__ int32_t sidx[kSmallT * 16];
   __shared__ unsigned long long bm[kSmallE];
@@ -502,6 +503,10 @@ __global__ __launch_bounds__(1024) void route_finish_small(const float* __restri
     perm_pos[tid] = pos;
     perm_src[pos] = t;
   }
+  // a device-controlled decoder's resolve of this layer-step, from the counts and offsets in LDS
+  if (dev.c.slot_of != nullptr)
+    devctl::resolve_layer_step(
+        tid, E, dev.layer, dev.c, [&](int e) { return __popcll(bm[e]); }, [&](int e) { return soff[e]; });
 }
 
 struct RoutePlan {
@@ -559,13 +564,18 @@ size_t route_workspace_bytes(int T, int H, int E, int k) {
 hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* bias, int T, int H, int E, int k,
                         int32_t* topk_idx, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
                         int32_t* perm_src, int32_t* perm_pos, void* ws, hipStream_t s, int32_t* counts_mirror,
-                        int32_t mirror_seq, const ResidentList* resident) {
+                        int32_t mirror_seq, const ResidentList* resident, const DevStep* dev) {
   const RoutePlan p = plan_route(T, H, E, bf16);
   ResidentList res{};
   if (resident != nullptr) {
     if (p.mode != 0 || resident->updates.n < 0 || resident->updates.n > kSlotUpdatesMax)
       return hipErrorInvalidValue;
     res = *resident;
+  }
+  DevStep dv{};
+  if (dev != nullptr) {
+    if (p.mode != 0 || E > devctl::kResolveThreads) return hipErrorInvalidValue;
+    dv = *dev;
   }
   char* w = static_cast<char*>(ws);
   float* partial = reinterpret_cast<float*>(w);
@@ -581,7 +591,8 @@ hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* b
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     hipLaunchKernelGGL(route_finish_small, dim3(1), dim3(1024), 0, s, partial, T > 0 ? p.nsplit : 0, bias, T, E, k,
-                       topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos, counts_mirror, mirror_seq, res);
+                       topk_idx, topk_w, logits, counts, offsets, perm_src, perm_pos, counts_mirror, mirror_seq, res,
+                       dv);
     return hipGetLastError();
   }
   if (p.mode == 1) {

@@ -107,6 +107,26 @@ struct SlotUpdates {
   int n;
   int32_t key[kSlotUpdatesMax], slot[kSlotUpdatesMax];
 };
+// Device-resident cache control (kernels_devctl.hip). All pointers are device
+// memory owned by a device-controlled decoder.
+struct DevCache {
+  int32_t* slot_of;   // [L*E] key -> slot, -1 if not resident
+  int32_t* slot_key;  // [S] slot -> key, -1 if free
+  uint64_t* stamp;    // [S] last use (clock value) of each occupied slot
+  uint64_t* ctl;      // [0] clock, [1] hits, [2] misses, [3] resolve calls, [4] trace records
+  int S;
+  int4* work;         // [max items] {slot, row_begin, rows, expert}: hits, then misses
+  int4* miss;         // [max items] {expert, slot, victim key or -1, key}
+  int32_t* n;         // [0] work items, [1] misses, [2] hits (of the last resolve)
+  int32_t* trace;     // [trace_cap][7] records as moe_trace_t
+  int64_t trace_cap;
+};
+// A device-controlled decoder's resolve of one layer-step, run by the routing
+// launch itself on the decode-size path.
+struct DevStep {
+  DevCache c;  // c.slot_of == nullptr: none
+  int layer;
+};
 struct ResidentList {
   int32_t* slot_of;     // nullptr: no list
   int layer;
@@ -122,7 +142,10 @@ hipError_t launch_route(const void* x, bool bf16, const void* Wr, const float* b
                         // for other batches plain counts
                         int32_t* counts_mirror = nullptr, int32_t mirror_seq = 0,
                         // optional, decode-size path only: the resident experts' work list (see ResidentList)
-                        const ResidentList* resident = nullptr);
+                        const ResidentList* resident = nullptr,
+                        // optional, decode-size path only: the device-resident cache's resolve of this layer-step
+                        // (as launch_dev_resolve), run at the end of the last routing kernel
+                        const DevStep* dev = nullptr);
 // Whether launch_route takes the decode-size path (and tags its counts mirror).
 bool route_small_path(int T, int E);
 
@@ -213,20 +236,6 @@ int router_gemm2_splits(int T, int H, int E);
 hipError_t launch_router_gemm2(const void* x, const void* wrt, int T, int H, int E, float* partial, int nsplit,
                                hipStream_t s);
 
-// Device-resident cache control (kernels_devctl.hip). All pointers are device
-// memory owned by a device-controlled decoder.
-struct DevCache {
-  int32_t* slot_of;   // [L*E] key -> slot, -1 if not resident
-  int32_t* slot_key;  // [S] slot -> key, -1 if free
-  uint64_t* stamp;    // [S] last use (clock value) of each occupied slot
-  uint64_t* ctl;      // [0] clock, [1] hits, [2] misses, [3] resolve calls, [4] trace records
-  int S;
-  int4* work;         // [max items] {slot, row_begin, rows, expert}: hits, then misses
-  int4* miss;         // [max items] {expert, slot, victim key or -1, key}
-  int32_t* n;         // [0] work items, [1] misses, [2] hits (of the last resolve)
-  int32_t* trace;     // [trace_cap][7] records as moe_trace_t
-  int64_t trace_cap;
-};
 // One layer-step of the policy on the device (one workgroup; E <= 1024).
 hipError_t launch_slot_updates(int32_t* slot_of, const SlotUpdates& u, hipStream_t s);
 
