@@ -564,15 +564,18 @@ int moe_cpu_threads(void);
  *   Errors: EINVAL (null, bad sizes, pool address not from moe_pool_alloc),
  *   ECAPACITY (S too small), ENOMEM (device memory), EHIP.
  * moe_device_decoder_step: enqueues one layer-step on `stream`: routing (as
- *   moe_route), the resolve kernel (one workgroup, updates the tables and
- *   writes the work list, hits first, and the number of hits to GPU memory),
+ *   moe_route), the resolve (one workgroup updates the tables and writes the
+ *   work list, hits first, and the number of hits to GPU memory; for T <= 16
+ *   it runs at the end of the routing launch's last kernel, else as a kernel
+ *   of its own),
  *   the decode expert FFN over the device work list (fixed grid for
  *   min(E, k*T) items; surplus blocks exit) and the combine into `out`. For
  *   bf16, int4 and MXFP4 experts the FFN reads each hit from its slot and
  *   each miss from the pool over the host link, writing the miss's blob
  *   through into its slot as it goes (the fill); for fp32 experts a fill
  *   kernel first copies the misses' blobs into their slots (returning at once
- *   when there are none) and the FFN then reads every item from its slot. It neither waits for the GPU nor allocates, so the same call can be
+ *   when there are none) and the FFN then reads every item from its slot.
+ *   It neither waits for the GPU nor allocates, so the same call can be
  *   captured with moe_graph_begin/moe_graph_end and replayed: a replay reads
  *   whatever x, Wr and bias hold at that time. Launch shapes depend only on
  *   T, so a graph is tied to the T (and layer and buffers) it was captured
