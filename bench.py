@@ -89,7 +89,8 @@ def decode_ffn_digest(root):
              _definition(ffn, "__global__ __launch_bounds__(256) void ffn2_decode_bf16("),
              _definition(ffn, "__global__ __launch_bounds__(1024) void ffn2_combine_bf16("),
              ffn[ffn.index("constexpr int kFuseWaves ="):].split("\n", 1)[0],
-             _definition(ffn, "bool ffn_combine_ok("), _definition(ffn, "hipError_t launch_ffn_decode_hits_combine("),
+             _definition(ffn, "bool ffn_combine_ok("), _definition(ffn, "hipError_t ffn_combine_kernels("),
+             _definition(ffn, "hipError_t launch_ffn_decode_combine("),
              _definition(ffn, "hipError_t launch_ffn_decode("),
              _definition(ffn, "hipError_t launch_ffn_decode_dev("),
              _definition(ffn, "hipError_t decode_kernels("), _definition(ffn, "struct ArgWork"),

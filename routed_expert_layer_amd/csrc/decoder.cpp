@@ -334,10 +334,10 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
       prof_open = true;
     }
     if (e == hipSuccess && fused)
-      e = moe::launch_ffn_decode_hits_combine(x, b.perm_src, d->hit_n, d->hit_items, std::min(d->E, d->k * T), T,
-                                              static_cast<const char*>(d->slot_base), d->slot_stride, d->H, d->I,
-                                              b.ffn_ws, b.y_perm, d->hit_n + 1, b.perm_pos, b.topk_w, d->k, out,
-                                              out_dtype == MOE_DT_BF16, s);
+      e = moe::launch_ffn_decode_combine(x, b.perm_src, d->hit_n, d->hit_items, std::min(d->E, d->k * T), T,
+                                         static_cast<const char*>(d->slot_base), d->slot_stride, d->H, d->I, b.ffn_ws,
+                                         b.y_perm, d->hit_n + 1, b.perm_pos, b.topk_w, d->k, out,
+                                         out_dtype == MOE_DT_BF16, s);
     else if (e == hipSuccess)
       e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->hit_n, d->hit_items, std::min(d->E, d->k * T), T,
                                      static_cast<const char*>(d->slot_base), d->slot_stride, d->H, d->I, b.ffn_ws,

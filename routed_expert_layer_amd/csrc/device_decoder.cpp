@@ -176,6 +176,8 @@ int moe_device_decoder_step(moe_device_decoder_t* d, int layer, const void* x, i
   void* hbuf = ws;
   // decode-size batches: the routing launch's last kernel also runs the resolve (one launch fewer)
   const bool fused_resolve = moe::route_small_path(T, d->E);
+  // bf16 steps of few experts: the down projection forms `out` itself (no combine launch)
+  const bool fused_combine = moe::ffn_combine_ok(d->wfmt, d->H, d->I, items, T, d->k);
   const moe::DevStep dstep{d->c, layer};
   hipError_t e = moe::launch_route(x, d->dtype == MOE_DT_BF16, Wr, bias, T, d->H, d->E, d->k, b.topk_idx, b.topk_w,
                                    b.logits, b.counts, b.offsets, b.perm_src, b.perm_pos, b.route_ws, s, nullptr, 0,
@@ -188,13 +190,18 @@ int moe_device_decoder_step(moe_device_decoder_t* d, int layer, const void* x, i
     if (e == hipSuccess)
       e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->c.n, d->c.work, items, T, d->slot_base,
                                      d->slot_stride, d->H, d->I, hbuf, b.y_perm, s);
+  } else if (e == hipSuccess && fused_combine) {
+    // the same pass, with the down projection also forming `out` (every expert of the step is in the list)
+    e = moe::launch_ffn_decode_combine(x, b.perm_src, d->c.n, d->c.work, items, T, d->slot_base, d->slot_stride, d->H,
+                                       d->I, hbuf, b.y_perm, d->c.n, b.perm_pos, b.topk_w, d->k, out,
+                                       out_dtype == MOE_DT_BF16, s, d->c.n + 2, d->pool[layer], d->blob_stride);
   } else if (e == hipSuccess) {
     // one pass: the hits run from their slots while the misses stream from the pool over the host link and
     // are written through into their slots
     e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->c.n, d->c.work, items, T, d->slot_base, d->slot_stride,
                                    d->H, d->I, hbuf, b.y_perm, s, d->c.n + 2, d->pool[layer], d->blob_stride);
   }
-  if (e == hipSuccess)
+  if (e == hipSuccess && !fused_combine)
     e = moe::launch_combine(b.y_perm, b.perm_pos, b.topk_w, T, d->k, d->H, out, out_dtype == MOE_DT_BF16, s);
   if (e != hipSuccess) return dd_fail(MOE_EHIP, "moe_device_decoder_step: %s", hipGetErrorString(e));
   return MOE_OK;

@@ -54,6 +54,12 @@ struct DevHits : DevList {
     fill = nullptr;
     return slot_base + (size_t)it.x * slot_stride;
   }
+  // src with the number of hits read once by the caller (hits())
+  __device__ __forceinline__ int hits() const { return kFuseItems; }
+  __device__ __forceinline__ const char* src_at(int i, int, const int4& it, const char* slot_base,
+                                                size_t slot_stride, char*& fill) const {
+    return src(i, it, slot_base, slot_stride, fill);
+  }
 };
 // With `pool` set, items from *n_hit on are misses: their blob is read from the
 // host pool (pool + expert * pool_stride, device-visible pinned memory) and
@@ -66,6 +72,18 @@ struct DevWork : DevList {
                                              char*& fill) const {
     char* slot = const_cast<char*>(slot_base) + (size_t)it.x * slot_stride;
     if (pool != nullptr && i >= *n_hit) {
+      fill = slot;
+      return pool + (size_t)it.w * pool_stride;
+    }
+    fill = nullptr;
+    return slot;
+  }
+  // src with the number of hits read once by the caller (hits())
+  __device__ __forceinline__ int hits() const { return pool != nullptr ? *n_hit : kFuseItems; }
+  __device__ __forceinline__ const char* src_at(int i, int nh, const int4& it, const char* slot_base,
+                                                size_t slot_stride, char*& fill) const {
+    char* slot = const_cast<char*>(slot_base) + (size_t)it.x * slot_stride;
+    if (pool != nullptr && i >= nh) {
       fill = slot;
       return pool + (size_t)it.w * pool_stride;
     }
@@ -288,7 +306,9 @@ __global__ __launch_bounds__(1024) void ffn2_combine_bf16(const uint16_t* __rest
   const int tile = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int KC = I / 32;
-  const int n = min(*wk.n, kFuseItems);
+  // the list's size and its hits (later items are misses read from the pool), read once, so that no weight
+  // load in the loop waits on them
+  const int n = min(*wk.n, kFuseItems), nh = wk.hits();
   const int m = lane & 15, kq = (lane >> 4) * 8;
   const size_t toff = p2_off + ((size_t)tile * KC + (size_t)F * wave) * 1024 + lane * 16;
   for (int i = 0; i < n; i += 2) {
@@ -296,8 +316,8 @@ __global__ __launch_bounds__(1024) void ffn2_combine_bf16(const uint16_t* __rest
     int4 ia, ib;
     (void)wk.get(i, ia);
     if (two) (void)wk.get(i + 1, ib);
-    char* fill;
-    const char* wa = wk.src(i, ia, slot_base, slot_stride, fill) + toff;
+    char *fa = nullptr, *fb = nullptr;
+    const char* wa = wk.src_at(i, nh, ia, slot_base, slot_stride, fa) + toff;
     const bool va = m < ia.z;
     const uint16_t* ha = hbuf + (size_t)(ia.y + (va ? m : 0)) * I + kq + 32 * F * wave;
     u32x4_t a[2 * F], b[2 * F];
@@ -306,9 +326,8 @@ __global__ __launch_bounds__(1024) void ffn2_combine_bf16(const uint16_t* __rest
       a[u] = ld16_nt(wa + (size_t)u * 1024);
       b[u] = va ? ld16(ha + 32 * u) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
     if (two) {
-      const char* wb = wk.src(i + 1, ib, slot_base, slot_stride, fill) + toff;
+      const char* wb = wk.src_at(i + 1, nh, ib, slot_base, slot_stride, fb) + toff;
       const bool vb = m < ib.z;
       const uint16_t* hb = hbuf + (size_t)(ib.y + (vb ? m : 0)) * I + kq + 32 * F * wave;
 #pragma unroll
@@ -316,11 +335,25 @@ __global__ __launch_bounds__(1024) void ffn2_combine_bf16(const uint16_t* __rest
         a[F + u] = ld16_nt(wb + (size_t)u * 1024);
         b[F + u] = vb ? ld16(hb + 32 * u) : u32x4_t{0u, 0u, 0u, 0u};
       }
+    }
+    if (fa != nullptr || fb != nullptr) {  // a miss's fragments, read from the pool, go into its slot too
+      if (fa != nullptr) {
+#pragma unroll
+        for (int u = 0; u < F; ++u) st16(fa + toff + (size_t)u * 1024, a[u]);
+      }
+      if (fb != nullptr) {
+#pragma unroll
+        for (int u = 0; u < F; ++u) st16(fb + toff + (size_t)u * 1024, a[F + u]);
+      }
+      drain_memory();
+    }
+    f32x4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < F; ++u) sa = mfma_bf16(a[u], b[u], sa);
+    if (two) {
 #pragma unroll
       for (int u = 0; u < F; ++u) sb = mfma_bf16(a[F + u], b[F + u], sb);
     }
-#pragma unroll
-    for (int u = 0; u < F; ++u) sa = mfma_bf16(a[u], b[u], sa);
     red[wave][i][lane] = sa;
     if (two) red[wave][i + 1][lane] = sb;
   }
@@ -873,40 +906,54 @@ bool ffn_combine_ok(int wfmt, int H, int I, int max_items, int T, int k) {
          T <= 16 && k >= 1 && T * k <= kFuseRows;
 }
 
-hipError_t launch_ffn_decode_hits_combine(const void* x, const int32_t* perm_src, const int32_t* n_items,
-                                          const int4* items, int max_items, int T, const char* slot_base,
-                                          size_t slot_stride, int H, int I, void* hbuf, float* y_perm,
-                                          const int32_t* n_active, const int32_t* perm_pos, const float* topk_w,
-                                          int k, void* out, bool out_bf16, hipStream_t s) {
-  if (!ffn_combine_ok(1, H, I, max_items, T, k)) return hipErrorInvalidValue;
-  const DevHits wk{{n_items, items}};
+namespace {
+
+template <typename W>
+hipError_t ffn_combine_kernels(const W& wk, const void* x, const int32_t* perm_src, int max_items, int T,
+                               const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y_perm,
+                               const int32_t* n_active, const int32_t* perm_pos, const float* topk_w, int k, void* out,
+                               bool out_bf16, hipStream_t s) {
   const BlobLayout L = blob_layout(1, H, I);
-  hipLaunchKernelGGL(ffn1_decode_bf16<DevHits>, dim3(max_items * (I / 8)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), perm_src, wk, slot_base, slot_stride, H, I,
-                     static_cast<uint16_t*>(hbuf));
+  hipLaunchKernelGGL(ffn1_decode_bf16<W>, dim3(max_items * (I / 8)), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                     perm_src, wk, slot_base, slot_stride, H, I, static_cast<uint16_t*>(hbuf));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint16_t* h = static_cast<const uint16_t*>(hbuf);
   const dim3 grid(H / 16), block(64 * kFuseWaves);
   switch (I / 512) {
     case 1:
-      hipLaunchKernelGGL((ffn2_combine_bf16<DevHits, 1>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H,
-                         I, y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
+      hipLaunchKernelGGL((ffn2_combine_bf16<W, 1>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H, I,
+                         y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
       break;
     case 2:
-      hipLaunchKernelGGL((ffn2_combine_bf16<DevHits, 2>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H,
-                         I, y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
+      hipLaunchKernelGGL((ffn2_combine_bf16<W, 2>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H, I,
+                         y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
       break;
     case 3:
-      hipLaunchKernelGGL((ffn2_combine_bf16<DevHits, 3>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H,
-                         I, y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
+      hipLaunchKernelGGL((ffn2_combine_bf16<W, 3>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H, I,
+                         y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
       break;
     default:
-      hipLaunchKernelGGL((ffn2_combine_bf16<DevHits, 4>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H,
-                         I, y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
+      hipLaunchKernelGGL((ffn2_combine_bf16<W, 4>), grid, block, 0, s, h, wk, slot_base, slot_stride, L.p2, H, I,
+                         y_perm, n_active, perm_pos, topk_w, T, k, out, (int)out_bf16);
       break;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ffn_decode_combine(const void* x, const int32_t* perm_src, const int32_t* n_items, const int4* items,
+                                     int max_items, int T, const char* slot_base, size_t slot_stride, int H, int I,
+                                     void* hbuf, float* y_perm, const int32_t* n_active, const int32_t* perm_pos,
+                                     const float* topk_w, int k, void* out, bool out_bf16, hipStream_t s,
+                                     const int32_t* n_hit, const char* pool, size_t pool_stride) {
+  if (!ffn_combine_ok(1, H, I, max_items, T, k)) return hipErrorInvalidValue;
+  if (pool == nullptr)
+    return ffn_combine_kernels(DevHits{{n_items, items}}, x, perm_src, max_items, T, slot_base, slot_stride, H, I,
+                               hbuf, y_perm, n_active, perm_pos, topk_w, k, out, out_bf16, s);
+  return ffn_combine_kernels(DevWork{{n_items, items}, n_hit, pool, pool_stride}, x, perm_src, max_items, T, slot_base,
+                             slot_stride, H, I, hbuf, y_perm, n_active, perm_pos, topk_w, k, out, out_bf16, s);
 }
 
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,

@@ -174,20 +174,23 @@ hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_sr
                                  size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s,
                                  const int32_t* n_hit = nullptr, const char* pool = nullptr,
                                  size_t pool_stride = 0);
-// The bf16 decode FFN of resident experts listed in device memory (at most
-// kFuseItems items, *n_items of them) with the step's weighted combine in the
-// down projection: y_perm gets every listed item's rows, and when
-// *n_active == *n_items (no expert of the step is missing) `out` [T, H]
+// The bf16 decode FFN of the experts listed in device memory (at most
+// kFuseItems items, *n_items of them; with `pool`, items from *n_hit on are
+// misses read from the pool and written through into their slots, as for
+// launch_ffn_decode_dev) with the step's weighted combine in the down
+// projection: y_perm gets every listed item's rows, and when
+// *n_active == *n_items (no expert of the step is left out) `out` [T, H]
 // (fp32, or bf16 with out_bf16) gets the combine's result, summed in the
 // combine kernel's order; otherwise `out` is left alone. ffn_combine_ok
 // tells whether a shape can take this path.
 constexpr int kFuseItems = 8;
 bool ffn_combine_ok(int wfmt, int H, int I, int max_items, int T, int k);
-hipError_t launch_ffn_decode_hits_combine(const void* x, const int32_t* perm_src, const int32_t* n_items,
-                                          const int4* items, int max_items, int T, const char* slot_base,
-                                          size_t slot_stride, int H, int I, void* hbuf, float* y_perm,
-                                          const int32_t* n_active, const int32_t* perm_pos, const float* topk_w,
-                                          int k, void* out, bool out_bf16, hipStream_t s);
+hipError_t launch_ffn_decode_combine(const void* x, const int32_t* perm_src, const int32_t* n_items, const int4* items,
+                                     int max_items, int T, const char* slot_base, size_t slot_stride, int H, int I,
+                                     void* hbuf, float* y_perm, const int32_t* n_active, const int32_t* perm_pos,
+                                     const float* topk_w, int k, void* out, bool out_bf16, hipStream_t s,
+                                     const int32_t* n_hit = nullptr, const char* pool = nullptr,
+                                     size_t pool_stride = 0);
 // 128 x 128-tile fallback GEMM for shapes the large-tile GEMM does not take.
 hipError_t launch_ffn_prefill(const void* x, const int32_t* perm_src, WorkArgs& wa, const char* slot_base,
                               size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s);

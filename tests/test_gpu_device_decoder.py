@@ -130,11 +130,28 @@ def test_device_decode_int4_full():
     run_device(cfg, cfg.steps, {(0, 2), (130, 2), (255, 2)})
 
 
-def test_graph_replay_equals_eager():
+def fused_bf16(I):
+    """Single-token bf16 steps whose down projection forms the output (misses written through on the way)."""
+    return dataclasses.replace(CONFIGS["decode_bf16_h4096_e256"], name=f"devfused_i{I}", L=2, T=1, steps=40, H=256,
+                               E=16, I=I, k=4, zipf_s=1.0, epoch=8, S=6)
+
+
+@pytest.mark.parametrize("I", [512, 2048])
+def test_device_fused_combine_all_outputs(I):
+    """The device step's down projection writes the output, hits and written-through misses alike: every
+    output and the whole trace against the oracle (later hits read the slots the misses were written into)."""
+    cfg = fused_bf16(I)
+    ref = run_device(cfg, cfg.steps, set(), check_all=True)
+    assert (ref[:, 3] == 0).sum() > 10 and (ref[:, 3] == 1).sum() > 40
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["combine", "fused"])
+def test_graph_replay_equals_eager(fused):
     """Two identical device decoders over one pool: A steps eagerly, B replays one captured graph holding all
-    layers; outputs and traces must agree bit for bit on every step, and both with the oracle's trace."""
+    layers; outputs and traces must agree bit for bit on every step, and both with the oracle's trace (with
+    the separate combine, and with the output formed in the down projection)."""
     from routed_expert_layer_amd.runtime import DeviceDecodeLayer
-    cfg = small_bf16(6)
+    cfg = fused_bf16(1024) if fused else small_bf16(6)
     steps = 24
     store = make_store(cfg)
     try:
