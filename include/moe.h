@@ -569,7 +569,9 @@ int moe_cpu_threads(void);
  *   it runs at the end of the routing launch's last kernel, else as a kernel
  *   of its own),
  *   the decode expert FFN over the device work list (fixed grid for
- *   min(E, k*T) items; surplus blocks exit) and the combine into `out`. For
+ *   min(E, k*T) items; surplus blocks exit) and the combine into `out` (for
+ *   bf16 weights with min(E, k*T) <= 8 and I a multiple of 512 up to 2048,
+ *   formed by the down projection itself, with no combine launch). For
  *   bf16, int4 and MXFP4 experts the FFN reads each hit from its slot and
  *   each miss from the pool over the host link, writing the miss's blob
  *   through into its slot as it goes (the fill); for fp32 experts a fill
