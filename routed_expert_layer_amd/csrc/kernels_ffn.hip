@@ -5,7 +5,10 @@
 // from HBM: the matrix-vector kernels give each workgroup one 16-row tile of
 // a weight matrix, split its K range over four waves, and feed every 1 KiB
 // weight fragment straight from a coalesced global load into a 16x16x32
-// matrix-core instruction whose other operand holds the (<= 16) tokens.
+// matrix-core instruction whose other operand holds the (<= 16) tokens. A
+// one-token bf16 step's down projection can instead run one workgroup per 16
+// output columns over all of the step's experts, which lets it also form the
+// step's weighted output (ffn2_combine_bf16).
 // Prefill (many rows per expert) runs a tiled matrix-core GEMM with both
 // operands staged in LDS.
 #include <cstring>
