@@ -347,6 +347,7 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
       return dfail(MOE_EHIP, "moe_decoder_step: resident experts' FFN: %s", hipGetErrorString(e));
   }
   int rc;
+  bool all_resident = false;
   if (tagged && !split) {
     // decode batches: every count word carries this step's number, so the counts are complete once all of
     // them show it (the event is polled too, so a failed launch still ends the wait)
@@ -402,8 +403,10 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
         ++hits;
         rows += d->counts[d->work_e[i]];
       }
-    const bool whole = nm == 0 && hits > 0;
-    if (d->prof_every > 0 && whole && d->prof_calls++ % d->prof_every == 0 && prof_open) {
+    // every expert of the step resident at its start: no fills and none run on the CPU (the resident list
+    // then held all of them, so a fused launch has formed `out`)
+    all_resident = nm == 0 && hits == n && n > 0;
+    if (d->prof_every > 0 && all_resident && d->prof_calls++ % d->prof_every == 0 && prof_open) {
       const double a = d->dtype == MOE_DT_BF16 ? 2.0 : 4.0, h = d->wfmt == MOE_W_F32 ? 4.0 : 2.0;
       d->ev_bytes[d->ev_used] = (double)hits * (double)d->blob_bytes +
                                 (double)rows * (d->H * a + 2.0 * d->I * h + d->H * 4.0) +
@@ -525,7 +528,7 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
     if (e != hipSuccess) return dfail(MOE_EHIP, "moe_decoder_step: CPU rows to the GPU: %s", hipGetErrorString(e));
     ++d->cpu_runs;
   }
-  if (!(fused && nm == 0)) {  // with every expert resident the fused launch has written `out`
+  if (!(fused && all_resident)) {  // with every expert resident the fused launch has written `out`
     rc = moe_combine(b.y_perm, b.perm_pos, b.topk_w, T, d->k, d->H, out, out_dtype, stream);
     if (rc != MOE_OK) return dfail(rc, "moe_decoder_step: %s", moe_last_error());
   }

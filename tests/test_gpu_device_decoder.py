@@ -145,6 +145,32 @@ def test_device_fused_combine_all_outputs(I):
     assert (ref[:, 3] == 0).sum() > 10 and (ref[:, 3] == 1).sum() > 40
 
 
+def test_device_fused_combine_bf16_output():
+    """Two identical device decoders over one pool, one writing fp32 outputs and one bf16: the bf16 output is
+    the fp32 one rounded to nearest even, with the output formed in the down projection."""
+    from routed_expert_layer_amd.runtime import DeviceDecodeLayer
+    cfg = fused_bf16(2048)
+    store = make_store(cfg)
+    try:
+        A = DeviceDecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+        B = DeviceDecodeLayer(store, cfg.S, cfg.T, cfg.k, cfg.act, dev)
+        Wr = [gen.router_weight(cfg, l, dev) for l in range(cfg.L)]
+        oa = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
+        ob = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+        for step in range(30):
+            for layer in range(cfg.L):
+                b = gen.router_bias(cfg, layer, step, dev)
+                x = gen.tokens(cfg, step, layer, dev)
+                A.step(layer, x, Wr[layer], b, out=oa)
+                B.step(layer, x, Wr[layer], b, out=ob)
+                torch.cuda.synchronize()
+                assert torch.equal(ob, oa.to(torch.bfloat16)), f"step {step} layer {layer}"
+        ha, ma, _ = A.stats()
+        assert ma > 0 and (ha, ma) == B.stats()[:2]
+    finally:
+        store.close()
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["combine", "fused"])
 def test_graph_replay_equals_eager(fused):
     """Two identical device decoders over one pool: A steps eagerly, B replays one captured graph holding all

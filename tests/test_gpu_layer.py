@@ -215,6 +215,14 @@ def test_fused_combine_all_outputs(I):
     assert (ref[:, 3] == 0).sum() > 10 and (ref[:, 3] == 1).sum() > 40
 
 
+def test_fused_combine_split_all_outputs():
+    """Single-token steps with misses divided 1:3 between fills and the CPU: steps with every expert resident
+    take the fused combine, the rest the combine kernel after the CPU rows; every output checked."""
+    cfg = fused_small(1024)
+    ref = run_decode(cfg, 40, set(), check_all_outputs=True, split=(1, 3))
+    assert (ref[:, 4] < 0).sum() > 5 and (ref[:, 3] == 1).sum() > 40
+
+
 def test_fused_combine_bf16_output():
     """Two identical decoders over one pool, one writing fp32 outputs and one bf16: the bf16 output is the
     fp32 one rounded to nearest even, on steps with every expert resident (fused combine) and with misses
