@@ -102,9 +102,14 @@ def test_device_small_bf16_all_outputs(S):
     assert (ref[:, 5] >= 0).any(), "the small config should evict"
 
 
-def test_device_resize_all_outputs():
+@pytest.mark.parametrize("fused", [False, True], ids=["combine", "fused"])
+def test_device_resize_all_outputs(fused):
     """Shrink to the smallest allowed size (k*T), then grow into a new buffer, between steps."""
-    ref = run_device(small_bf16(10), 36, set(), check_all=True, resizes={12: 6, 24: 14})
+    if fused:  # one-token steps whose down projection forms the output (k*T = 4)
+        ref = run_device(dataclasses.replace(fused_bf16(1024), S=8), 36, set(), check_all=True,
+                         resizes={12: 4, 24: 10})
+    else:
+        ref = run_device(small_bf16(10), 36, set(), check_all=True, resizes={12: 6, 24: 14})
     assert (ref[:, 5] >= 0).any()
 
 

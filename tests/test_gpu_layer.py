@@ -215,6 +215,12 @@ def test_fused_combine_all_outputs(I):
     assert (ref[:, 3] == 0).sum() > 10 and (ref[:, 3] == 1).sum() > 40
 
 
+def test_fused_combine_resize_all_outputs():
+    """The fused path across a shrink and a grow into a new buffer (the slot table copy is uploaded again)."""
+    cfg = fused_small(512)
+    run_decode(cfg, 36, set(), check_all_outputs=True, resizes={12: 3, 24: 8})
+
+
 def test_fused_combine_split_all_outputs():
     """Single-token steps with misses divided 1:3 between fills and the CPU: steps with every expert resident
     take the fused combine, the rest the combine kernel after the CPU rows; every output checked."""
@@ -262,7 +268,7 @@ def test_split_small_all_outputs(wfmt):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("case", ["tiny_waves", "split_small"])
+@pytest.mark.parametrize("case", ["tiny_waves", "split_small", "fused"])
 def test_poisoned_fills_all_outputs(case, monkeypatch):
     """Debug mode: every fill first sets its victim slot to 0xFF bytes (NaN in every weight format), so a kernel
     that read a slot before its copy landed, or a copy that overwrote a slot still being read, would give
@@ -273,11 +279,14 @@ def test_poisoned_fills_all_outputs(case, monkeypatch):
         cfg = CONFIGS["tiny_f32_h256_e16"]
         ref = run_decode(cfg, 32, set(), check_all_outputs=True)
         assert (ref[:, 6] > 0).any()
-    else:
+    elif case == "split_small":
         cfg = dataclasses.replace(CONFIGS["decode_bf16_h4096_e256"], name="split_small", L=3, T=4, H=512, I=256,
                                   E=32, k=4, zipf_s=1.0, S=8)
         ref = run_decode(cfg, 16, set(), check_all_outputs=True, split=(1, 3))
         assert (ref[:, 4] < 0).any()
+    else:  # single-token steps whose down projection forms the output
+        ref = run_decode(fused_small(1024), 24, set(), check_all_outputs=True)
+        assert (ref[:, 3] == 0).any()
 
 
 @pytest.mark.timeout(600)
