@@ -70,7 +70,7 @@ def make_store(cfg):
 
 
 def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, split=None, cpu_check=(0, ()),
-               resizes=None):
+               resizes=None, invalidate=None):
     """Drive a decode layer over `steps` x all layers; check routing, trace, and sampled outputs.
 
     native=True runs each layer-step through the library's decode driver
@@ -78,7 +78,8 @@ def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, spli
     Python (tests/sequenced.py). split=(rate_gpu, rate_cpu) divides misses
     between GPU fills and CPU execution; cpu_check=(n, layers) also checks the
     outputs of the first n layer-steps of those layers in which some miss ran
-    on the CPU."""
+    on the CPU. invalidate={step: n} unmaps the n lowest resident keys
+    before that step, in the library and in the oracle."""
     from routed_expert_layer_amd.runtime import DecodeLayer
     from tests.sequenced import SequencedDecodeLayer
     print(f"decode {cfg.name}: L={cfg.L} T={cfg.T} steps={steps} S={cfg.S} {cfg.wfmt} native={native} "
@@ -100,6 +101,11 @@ def run_decode(cfg, steps, out_check, check_all_outputs=False, native=True, spli
             if resizes and step in resizes:
                 dl.resize(resizes[step])
                 sim.resize(resizes[step])
+            if invalidate and step in invalidate:
+                from routed_expert_layer_amd import _lib as L
+                for key in sorted(sim.key_slot)[:invalidate[step]]:
+                    L.moe_cache_invalidate(dl.cache, key)
+                    assert sim.drop(key)
             for layer in range(cfg.L):
                 b = gen.router_bias(cfg, layer, step, dev)
                 x = gen.tokens(cfg, step, layer, dev)
@@ -219,6 +225,16 @@ def test_fused_combine_resize_all_outputs():
     """The fused path across a shrink and a grow into a new buffer (the slot table copy is uploaded again)."""
     cfg = fused_small(512)
     run_decode(cfg, 36, set(), check_all_outputs=True, resizes={12: 3, 24: 8})
+
+
+@pytest.mark.parametrize("case", ["fused", "tokens3"])
+def test_invalidate_between_steps_all_outputs(case):
+    """Keys unmapped between steps (moe_cache_invalidate): the GPU copy of the slot table is uploaded again
+    before the next step lists its resident experts; every output and the trace against the oracle."""
+    cfg = fused_small(1024) if case == "fused" else dataclasses.replace(
+        CONFIGS["decode_bf16_h4096_e256"], name="inval_small", L=2, T=3, H=256, I=128, E=16, k=2, zipf_s=1.2,
+        epoch=8, S=10)
+    run_decode(cfg, 30, set(), check_all_outputs=True, invalidate={6: 1, 13: 3, 21: 2})
 
 
 def test_fused_combine_split_all_outputs():
