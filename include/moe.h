@@ -288,10 +288,13 @@ int cache_fill_async(moe_cache_t* cache, const moe_miss_t* misses, int n,
  *   slot_base + slot*slot_stride):
  *     xr = x[perm_src[r], :]
  *     y_perm[r, :] = (silu(xr W1) * (xr W3)) W2          (fp32 out)
- * Accumulation is fp32. In the bf16 matrix-core kernels the SwiGLU product
- * is rounded to bf16 before the W2 product; in the int4 kernel x and that
- * product are rounded to fp16 and the int4 codes enter the matrix product
- * exactly, the fp16 scale being applied to each 128-row partial sum.
+ * Accumulation is fp32. In the matrix-core kernels (bf16, int4 and MXFP4
+ * weights) x enters as given (bf16) and the SwiGLU product is rounded to bf16
+ * before the W2 product. An int4 code q enters the bf16 products exactly as
+ * 1 + (q + 8)/16; a 128-row block's sum over q is recovered in fp32 as
+ * 16 t - 24 u (t that product, u the block's sum of the activations) and
+ * multiplied by the block's fp16 scale. An MXFP4 code times its power-of-two
+ * scale is exact in bf16.
  *
  * x        device [T, H] (dtype as for moe_route)   perm_src device int32 [T*k]
  * work     HOST array of n_work items {expert, slot, row_begin, rows}; items
