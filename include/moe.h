@@ -442,7 +442,11 @@ int moe_clock_record(unsigned long long* sums);
  *   8 experts in the step (min(E, k*T) <= 8) and I a multiple of 512 up to
  *   2048, the resident experts' down projection also writes `out` when no
  *   expert of the step is missing (the combine's sum, in its order), and no
- *   combine is launched; y_perm still receives every row.
+ *   combine is launched; y_perm still receives every row. With int4 weights
+ *   the resident experts' two projections run as one launch whose
+ *   down-projection blocks wait, through flags the decoder owns, for their
+ *   expert's gate/up blocks (so one decoder's steps must stay ordered on one
+ *   stream).
  *   out_dtype other than MOE_DT_F32 / MOE_DT_BF16 is MOE_EINVAL.
  *   When the cache splits misses (moe_cache_set_split), the misses assigned
  *   to the CPU run with moe_cpu_ffn from the pool on the calling thread while

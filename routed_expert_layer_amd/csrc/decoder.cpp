@@ -76,6 +76,8 @@ struct moe_decoder {
   moe::SlotUpdates pending{};      // updates for the GPU copy, applied by the next routing launch
   int32_t* hit_n = nullptr;        // device: number of resident-expert items
   int4* hit_items = nullptr;       // device: [E] items {slot, first row, rows, expert}
+  uint32_t* ffn_flags = nullptr;   // device: hand-off flags of the one-launch quantised FFN (zeroed at creation)
+  uint32_t ffn_seq = 0;            // the last call's flag value
   int n_layers = 0;
 };
 
@@ -90,6 +92,7 @@ static void decoder_release(moe_decoder_t* d) {
   if (d->ev_counts) (void)hipEventDestroy(d->ev_counts);
   if (d->slot_of_dev) (void)hipFree(d->slot_of_dev);
   if (d->hit_n) (void)hipFree(d->hit_n);
+  if (d->ffn_flags) (void)hipFree(d->ffn_flags);
   for (hipEvent_t e : d->ev_begin) (void)hipEventDestroy(e);
   for (hipEvent_t e : d->ev_end) (void)hipEventDestroy(e);
   delete d;
@@ -148,6 +151,11 @@ moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, i
   // hit_n, then the items 16-byte aligned
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&d->hit_n), 16 + sizeof(int4) * E);
   if (e == hipSuccess) d->hit_items = reinterpret_cast<int4*>(reinterpret_cast<char*>(d->hit_n) + 16);
+  if (e == hipSuccess && moe::ffn_fused_ok(wfmt, H, I)) {
+    const size_t fb = sizeof(uint32_t) * moe::ffn_fused_flags(E, I);
+    e = hipMalloc(reinterpret_cast<void**>(&d->ffn_flags), fb);
+    if (e == hipSuccess) e = hipMemset(d->ffn_flags, 0, fb);
+  }
   if (e != hipSuccess) {
     decoder_release(d);
     if (status) *status = dfail(MOE_EHIP, "moe_decoder_create: %s", hipGetErrorString(e));
@@ -338,7 +346,12 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
                                          static_cast<const char*>(d->slot_base), d->slot_stride, d->H, d->I, b.ffn_ws,
                                          b.y_perm, d->hit_n + 1, b.perm_pos, b.topk_w, d->k, out,
                                          out_dtype == MOE_DT_BF16, s);
-    else if (e == hipSuccess)
+    else if (e == hipSuccess && d->ffn_flags != nullptr) {
+      d->ffn_seq = d->ffn_seq == UINT32_MAX ? 1u : d->ffn_seq + 1u;
+      e = moe::launch_ffn_decode_fused(d->wfmt, x, b.perm_src, d->hit_n, d->hit_items, std::min(d->E, d->k * T),
+                                       static_cast<const char*>(d->slot_base), d->slot_stride, d->H, d->I, b.ffn_ws,
+                                       b.y_perm, d->ffn_flags, d->ffn_seq, s);
+    } else if (e == hipSuccess)
       e = moe::launch_ffn_decode_dev(d->wfmt, x, b.perm_src, d->hit_n, d->hit_items, std::min(d->E, d->k * T), T,
                                      static_cast<const char*>(d->slot_base), d->slot_stride, d->H, d->I, b.ffn_ws,
                                      b.y_perm, s);

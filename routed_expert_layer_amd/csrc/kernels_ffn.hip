@@ -396,6 +396,21 @@ __global__ __launch_bounds__(1024) void ffn2_combine_bf16(const uint16_t* __rest
 // block's fp16 scale).
 // ---------------------------------------------------------------------------
 
+// How a quantised kernel reads its 16-byte activation fragments: plain loads, or loads coherent across the
+// device's XCDs (for SwiGLU products another block of the same launch has just written through).
+struct PlainLoad {
+  __device__ __forceinline__ u32x4_t operator()(const uint16_t* p) const { return ld16(p); }
+};
+struct CoherentLoad {
+  const uint16_t* base;  // wave-uniform; every address read lies within 2^32 bytes above it
+  __device__ __forceinline__ u32x4_t operator()(const uint16_t* p) const {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, -1, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((const char*)p - (const char*)base), 0,
+                                                 16);  // sc1: device scope
+  }
+};
+
 // The registers of one 128-wide K block: activation fragments, and the codes
 // and the four rows' scales of each of the block's kRI tiles.
 constexpr int kRI = 4;  // 16-row tiles per int4 block
@@ -414,10 +429,10 @@ struct Int4Stage {
 // tile sums go to `emit(tile, m, sum)`. With WT every code and scale loaded
 // is also stored at the same offset from qf_base / sf_base (the write-through
 // of a miss), after each K block's loads.
-template <bool WT, typename Row, typename Emit>
+template <bool WT, typename Row, typename Emit, typename ALoad = PlainLoad>
 __device__ __forceinline__ void int4_decode_tiles(Row act_row, const int4 it, int K, const char* q_base,
                                                   const char* s_base, char* qf_base, char* sf_base, int tile0,
-                                                  Emit emit) {
+                                                  Emit emit, ALoad aload = ALoad()) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int KG = K / 128;
   const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
@@ -440,7 +455,7 @@ __device__ __forceinline__ void int4_decode_tiles(Row act_row, const int4 it, in
     // activation column, and the columns of those lanes are never stored.
     auto load = [&](int g, Int4Stage& st) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st.b[j] = ld16(ar + 128 * g + 32 * j);
+      for (int j = 0; j < 4; ++j) st.b[j] = aload(ar + 128 * g + 32 * j);
 #pragma unroll
       for (int r = 0; r < kRI; ++r) {
         const int blk = (tile0 + r) * KG + g;
@@ -591,10 +606,10 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_floa
 // tile sums go to `emit(tile, m, sum)`. With WT every code and scale loaded
 // is also stored at the same offset from qf_base / sf_base (the write-through
 // of a miss), after each K block's loads.
-template <bool WT, typename Row, typename Emit>
+template <bool WT, typename Row, typename Emit, typename ALoad = PlainLoad>
 __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, int K, const char* q_base,
                                                    const char* s_base, char* qf_base, char* sf_base, int tile0,
-                                                   Emit emit) {
+                                                   Emit emit, ALoad aload = ALoad()) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KG = K / 128;
   const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
@@ -610,7 +625,7 @@ __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, i
     for (int g = g0; g < g1; ++g) {
       u32x4_t b[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = valid ? ld16(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 4; ++j) b[j] = valid ? aload(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
       u32x4_t a[kR];
       uint32_t sc[kR];
 #pragma unroll
@@ -690,6 +705,83 @@ __global__ __launch_bounds__(256) void ffn2_decode_mxfp4(const uint16_t* __restr
     mxfp4_decode_tiles<true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0, emit);
   else
     mxfp4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit);
+}
+
+// Both projections of a quantised decode step (int4: WF 2, MXFP4: WF 3) in one
+// launch, for lists of resident experts: blocks [0, G1) (G1 = max_items * NB1)
+// run the gate/up tile groups as ffn1_decode_*, the others the down-projection
+// groups as ffn2_decode_*. A gate/up block, once its SwiGLU products are
+// stored, marks its group done for this call (flags[item * NB1 + group] =
+// seq); a down-projection block waits until every group of its item carries
+// seq and then reads the products. Products and flags are written and read
+// with device-scope (sc1) accesses, so the hand-off holds whichever XCDs ran
+// the blocks. A down-projection block waits only for blocks of lower index,
+// and each XCD dispatches its share of the grid in index order, so every
+// gate/up block it waits for has been dispatched, and gate/up blocks wait for
+// nothing: every wait ends. The wait is still bounded (2^18 polls), after
+// which the block goes on and its output is wrong rather than the GPU hung.
+// The launch saves the second launch's start-up and lets down-projection
+// blocks start while the gate/up tail drains.
+constexpr int kQuantTiles = 4;  // tiles per block of both quantised kernels (kRI, kR)
+template <int WF, typename W>
+__global__ __launch_bounds__(256) void ffn_decode_fused(const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ perm_src, const W wk,
+                                                        int max_items, const char* __restrict__ slot_base,
+                                                        size_t slot_stride, size_t p1s_off, size_t p2_off,
+                                                        size_t p2s_off, int H, int I, uint16_t* hbuf,
+                                                        float* __restrict__ y, uint32_t* flags, uint32_t seq) {
+  static_assert(kRI == kQuantTiles && kR == kQuantTiles, "one tile-group size for both formats");
+  const int NB1 = I / 8 / kQuantTiles, NB2 = H / 16 / kQuantTiles;
+  const int G1 = max_items * NB1;
+  const int lane = threadIdx.x & 63;
+  int4 it;
+  char* fill;
+  if ((int)blockIdx.x < G1) {
+    const int item = blockIdx.x / NB1, group = blockIdx.x - item * NB1;
+    if (!wk.get(item, it)) return;
+    const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
+    const auto row = [&](int m) { return x + (size_t)perm_src[it.y + m] * H; };
+    const auto emit = [&](int tile, int m, const f32x4_t& s) {
+      const int i0 = 8 * tile + 2 * (lane >> 4);
+      const uint32_t packed =
+          (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0), packed, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if constexpr (WF == 2)
+      int4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, group * kQuantTiles, emit);
+    else
+      mxfp4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, group * kQuantTiles, emit);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's product stores have completed
+    __syncthreads();                // ... and every wave's
+    if (threadIdx.x == 0)
+      __hip_atomic_store(flags + item * NB1 + group, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int b2 = blockIdx.x - G1, item = b2 / NB2, group = b2 - item * NB2;
+  if (!wk.get(item, it)) return;
+  const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
+  if (threadIdx.x < 64) {  // one wave polls the item's gate/up groups
+    for (int spin = 0; spin < (1 << 18); ++spin) {
+      bool done = true;
+      for (int j = lane; j < NB1; j += 64)
+        done &= __hip_atomic_load(flags + item * NB1 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == seq;
+      if (__all(done)) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+  const auto row = [&](int m) { return hbuf + (size_t)(it.y + m) * I; };
+  const auto emit = [&](int tile, int m, const f32x4_t& s) {
+    *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
+  };
+  const CoherentLoad coh{hbuf};
+  if constexpr (WF == 2)
+    int4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, group * kQuantTiles, emit,
+                             coh);
+  else
+    mxfp4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, group * kQuantTiles, emit,
+                              coh);
 }
 
 // ---------------------------------------------------------------------------
@@ -902,6 +994,33 @@ hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_sr
   if (wfmt == 0) return hipErrorInvalidValue;  // the fp32 kernels do not write through
   return decode_kernels(wfmt, x, perm_src, DevWork{{n_items, items}, n_hit, pool, pool_stride}, max_items,
                         max_rows, slot_base, slot_stride, H, I, hbuf, y, s);
+}
+
+// int4 only: the MXFP4 kernels load each K block's activations when they use it, and with the products read
+// past the XCD caches that wait slowed the one-launch MXFP4 FFN (42.8 vs 40.5 us per 8-token step).
+bool ffn_fused_ok(int wfmt, int H, int I) {
+  return wfmt == 2 && H % (16 * kQuantTiles) == 0 && I % (8 * kQuantTiles) == 0;
+}
+
+size_t ffn_fused_flags(int max_items, int I) { return (size_t)max_items * (I / 8 / kQuantTiles); }
+
+hipError_t launch_ffn_decode_fused(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
+                                   const int4* items, int max_items, const char* slot_base, size_t slot_stride, int H,
+                                   int I, void* hbuf, float* y, uint32_t* flags, uint32_t seq, hipStream_t s) {
+  if (!ffn_fused_ok(wfmt, H, I) || flags == nullptr || seq == 0) return hipErrorInvalidValue;
+  if (max_items == 0) return hipSuccess;
+  const BlobLayout L = blob_layout(wfmt, H, I);
+  const dim3 grid(max_items * (I / 8 / kQuantTiles + H / 16 / kQuantTiles));
+  const DevHits wk{{n_items, items}};
+  if (wfmt == 2)
+    hipLaunchKernelGGL((ffn_decode_fused<2, DevHits>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                       perm_src, wk, max_items, slot_base, slot_stride, L.p1s, L.p2, L.p2s, H, I,
+                       static_cast<uint16_t*>(hbuf), y, flags, seq);
+  else
+    hipLaunchKernelGGL((ffn_decode_fused<3, DevHits>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                       perm_src, wk, max_items, slot_base, slot_stride, L.p1s, L.p2, L.p2s, H, I,
+                       static_cast<uint16_t*>(hbuf), y, flags, seq);
+  return hipGetLastError();
 }
 
 bool ffn_combine_ok(int wfmt, int H, int I, int max_items, int T, int k) {

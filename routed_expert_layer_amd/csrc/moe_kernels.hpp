@@ -174,6 +174,18 @@ hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_sr
                                  size_t slot_stride, int H, int I, void* hbuf, float* y, hipStream_t s,
                                  const int32_t* n_hit = nullptr, const char* pool = nullptr,
                                  size_t pool_stride = 0);
+// Both projections of the quantised (int4, MXFP4) decode FFN of resident
+// experts listed in device memory, as launch_ffn_decode_dev without `pool`,
+// in one launch: the down-projection blocks wait for their expert's gate/up
+// blocks through `flags` (device, ffn_fused_flags(max_items, I) words, zero
+// before the first call, owned by one caller whose calls are stream-ordered;
+// each call passes a new nonzero `seq`). ffn_fused_ok tells whether a format
+// and shape can take this path.
+bool ffn_fused_ok(int wfmt, int H, int I);
+size_t ffn_fused_flags(int max_items, int I);
+hipError_t launch_ffn_decode_fused(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
+                                   const int4* items, int max_items, const char* slot_base, size_t slot_stride, int H,
+                                   int I, void* hbuf, float* y, uint32_t* flags, uint32_t seq, hipStream_t s);
 // The bf16 decode FFN of the experts listed in device memory (at most
 // kFuseItems items, *n_items of them; with `pool`, items from *n_hit on are
 // misses read from the pool and written through into their slots, as for
