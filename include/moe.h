@@ -581,7 +581,9 @@ int moe_cpu_threads(void);
  *   formed by the down projection itself, with no combine launch). For
  *   bf16, int4 and MXFP4 experts the FFN reads each hit from its slot and
  *   each miss from the pool over the host link, writing the miss's blob
- *   through into its slot as it goes (the fill); for fp32 experts a fill
+ *   through into its slot as it goes (the fill; with int4 experts both
+ *   projections run as one launch, numbered by the resolve's call counter);
+ *   for fp32 experts a fill
  *   kernel first copies the misses' blobs into their slots (returning at once
  *   when there are none) and the FFN then reads every item from its slot.
  *   It neither waits for the GPU nor allocates, so the same call can be

@@ -34,6 +34,7 @@ struct moe_device_decoder {
   void* mem = nullptr;  // one device allocation holding the control data
   moe::DevCache c{};
   int max_items;
+  uint32_t* ffn_flags = nullptr;  // hand-off flags of the one-launch int4 FFN (zeroed at creation)
 };
 
 namespace {
@@ -83,6 +84,7 @@ extern "C" {
 
 static void dd_release(moe_device_decoder_t* d) {
   if (d->mem) (void)hipFree(d->mem);
+  if (d->ffn_flags) (void)hipFree(d->ffn_flags);
   delete d;
 }
 
@@ -145,6 +147,11 @@ moe_device_decoder_t* moe_device_decoder_create(int L, int E, int S, int T_max, 
   // empty cache: every key unmapped (-1 bytes), every slot free, clocks zero
   e = hipMemset(m + o.slot_of, 0xFF, o.stamp - o.slot_of);
   if (e == hipSuccess) e = hipMemset(m + o.stamp, 0, o.trace - o.stamp);
+  if (e == hipSuccess && moe::ffn_fused_ok(wfmt, H, I)) {
+    const size_t fb = sizeof(uint32_t) * moe::ffn_fused_flags(max_items, I);
+    e = hipMalloc(reinterpret_cast<void**>(&d->ffn_flags), fb);
+    if (e == hipSuccess) e = hipMemset(d->ffn_flags, 0, fb);
+  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     dd_release(d);
@@ -195,6 +202,11 @@ int moe_device_decoder_step(moe_device_decoder_t* d, int layer, const void* x, i
     e = moe::launch_ffn_decode_combine(x, b.perm_src, d->c.n, d->c.work, items, T, d->slot_base, d->slot_stride, d->H,
                                        d->I, hbuf, b.y_perm, d->c.n, b.perm_pos, b.topk_w, d->k, out,
                                        out_dtype == MOE_DT_BF16, s, d->c.n + 2, d->pool[layer], d->blob_stride);
+  } else if (e == hipSuccess && d->ffn_flags != nullptr) {
+    // the same pass with both projections in one launch; the resolve's call counter numbers the calls
+    e = moe::launch_ffn_decode_fused(d->wfmt, x, b.perm_src, d->c.n, d->c.work, items, d->slot_base, d->slot_stride,
+                                     d->H, d->I, hbuf, b.y_perm, d->ffn_flags, 0, s, d->c.ctl + 3, d->c.n + 2,
+                                     d->pool[layer], d->blob_stride);
   } else if (e == hipSuccess) {
     // one pass: the hits run from their slots while the misses stream from the pool over the host link and
     // are written through into their slots

@@ -26,6 +26,7 @@ namespace {
 // src() gives the address item i's blob is read from and sets `fill` to an
 // address the kernel also writes every byte it reads to (nullptr: none).
 struct ArgWork {
+  static constexpr bool kMayFill = false;
   WorkArgs wa;
   __device__ __forceinline__ bool get(int i, int4& it) const {
     it = wa.item[i];
@@ -52,6 +53,7 @@ struct DevList {
 // Resident experts only: every item's blob is in its slot, so the kernels built for this source have no
 // write-through path (fewer registers, so more waves per SIMD, and half the LDS of the DevWork ones).
 struct DevHits : DevList {
+  static constexpr bool kMayFill = false;
   __device__ __forceinline__ const char* src(int, const int4& it, const char* slot_base, size_t slot_stride,
                                              char*& fill) const {
     fill = nullptr;
@@ -68,6 +70,7 @@ struct DevHits : DevList {
 // host pool (pool + expert * pool_stride, device-visible pinned memory) and
 // written through into their slot, so the fill and the FFN are one pass.
 struct DevWork : DevList {
+  static constexpr bool kMayFill = true;
   const int32_t* n_hit;
   const char* pool;
   size_t pool_stride;
@@ -729,8 +732,12 @@ __global__ __launch_bounds__(256) void ffn_decode_fused(const uint16_t* __restri
                                                         int max_items, const char* __restrict__ slot_base,
                                                         size_t slot_stride, size_t p1s_off, size_t p2_off,
                                                         size_t p2s_off, int H, int I, uint16_t* hbuf,
-                                                        float* __restrict__ y, uint32_t* flags, uint32_t seq) {
+                                                        float* __restrict__ y, uint32_t* flags, uint32_t seq_arg,
+                                                        const uint64_t* seq_dev) {
   static_assert(kRI == kQuantTiles && kR == kQuantTiles, "one tile-group size for both formats");
+  // the call's flag value: given, or from a counter in device memory that each call's earlier work advances
+  // (never 0, the flags' initial value)
+  const uint32_t seq = seq_dev != nullptr ? (uint32_t)(*seq_dev % 0xFFFFFFFFull) + 1u : seq_arg;
   const int NB1 = I / 8 / kQuantTiles, NB2 = H / 16 / kQuantTiles;
   const int G1 = max_items * NB1;
   const int lane = threadIdx.x & 63;
@@ -748,10 +755,18 @@ __global__ __launch_bounds__(256) void ffn_decode_fused(const uint16_t* __restri
       __hip_atomic_store(reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0), packed, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     };
-    if constexpr (WF == 2)
-      int4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, group * kQuantTiles, emit);
-    else
-      mxfp4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, group * kQuantTiles, emit);
+    const int tile0 = group * kQuantTiles;
+    if constexpr (WF == 2) {
+      if (W::kMayFill && fill != nullptr)
+        int4_decode_tiles<true>(row, it, H, blob, blob + p1s_off, fill, fill + p1s_off, tile0, emit);
+      else
+        int4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, tile0, emit);
+    } else {
+      if (W::kMayFill && fill != nullptr)
+        mxfp4_decode_tiles<true>(row, it, H, blob, blob + p1s_off, fill, fill + p1s_off, tile0, emit);
+      else
+        mxfp4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, tile0, emit);
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's product stores have completed
     __syncthreads();                // ... and every wave's
     if (threadIdx.x == 0)
@@ -776,12 +791,20 @@ __global__ __launch_bounds__(256) void ffn_decode_fused(const uint16_t* __restri
     *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
   };
   const CoherentLoad coh{hbuf};
-  if constexpr (WF == 2)
-    int4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, group * kQuantTiles, emit,
-                             coh);
-  else
-    mxfp4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, group * kQuantTiles, emit,
+  const int tile0 = group * kQuantTiles;
+  if constexpr (WF == 2) {
+    if (W::kMayFill && fill != nullptr)
+      int4_decode_tiles<true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0, emit,
                               coh);
+    else
+      int4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit, coh);
+  } else {
+    if (W::kMayFill && fill != nullptr)
+      mxfp4_decode_tiles<true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0, emit,
+                               coh);
+    else
+      mxfp4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit, coh);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1004,23 +1027,39 @@ bool ffn_fused_ok(int wfmt, int H, int I) {
 
 size_t ffn_fused_flags(int max_items, int I) { return (size_t)max_items * (I / 8 / kQuantTiles); }
 
-hipError_t launch_ffn_decode_fused(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
-                                   const int4* items, int max_items, const char* slot_base, size_t slot_stride, int H,
-                                   int I, void* hbuf, float* y, uint32_t* flags, uint32_t seq, hipStream_t s) {
-  if (!ffn_fused_ok(wfmt, H, I) || flags == nullptr || seq == 0) return hipErrorInvalidValue;
-  if (max_items == 0) return hipSuccess;
+namespace {
+
+template <typename W>
+hipError_t fused_kernel(int wfmt, const W& wk, const void* x, const int32_t* perm_src, int max_items,
+                        const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y, uint32_t* flags,
+                        uint32_t seq, const uint64_t* seq_dev, hipStream_t s) {
   const BlobLayout L = blob_layout(wfmt, H, I);
   const dim3 grid(max_items * (I / 8 / kQuantTiles + H / 16 / kQuantTiles));
-  const DevHits wk{{n_items, items}};
   if (wfmt == 2)
-    hipLaunchKernelGGL((ffn_decode_fused<2, DevHits>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(x),
-                       perm_src, wk, max_items, slot_base, slot_stride, L.p1s, L.p2, L.p2s, H, I,
-                       static_cast<uint16_t*>(hbuf), y, flags, seq);
+    hipLaunchKernelGGL((ffn_decode_fused<2, W>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), perm_src, wk,
+                       max_items, slot_base, slot_stride, L.p1s, L.p2, L.p2s, H, I, static_cast<uint16_t*>(hbuf), y,
+                       flags, seq, seq_dev);
   else
-    hipLaunchKernelGGL((ffn_decode_fused<3, DevHits>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(x),
-                       perm_src, wk, max_items, slot_base, slot_stride, L.p1s, L.p2, L.p2s, H, I,
-                       static_cast<uint16_t*>(hbuf), y, flags, seq);
+    hipLaunchKernelGGL((ffn_decode_fused<3, W>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), perm_src, wk,
+                       max_items, slot_base, slot_stride, L.p1s, L.p2, L.p2s, H, I, static_cast<uint16_t*>(hbuf), y,
+                       flags, seq, seq_dev);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ffn_decode_fused(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
+                                   const int4* items, int max_items, const char* slot_base, size_t slot_stride, int H,
+                                   int I, void* hbuf, float* y, uint32_t* flags, uint32_t seq, hipStream_t s,
+                                   const uint64_t* seq_dev, const int32_t* n_hit, const char* pool,
+                                   size_t pool_stride) {
+  if (!ffn_fused_ok(wfmt, H, I) || flags == nullptr || (seq == 0 && seq_dev == nullptr)) return hipErrorInvalidValue;
+  if (max_items == 0) return hipSuccess;
+  if (pool == nullptr)
+    return fused_kernel(wfmt, DevHits{{n_items, items}}, x, perm_src, max_items, slot_base, slot_stride, H, I, hbuf, y,
+                        flags, seq, seq_dev, s);
+  return fused_kernel(wfmt, DevWork{{n_items, items}, n_hit, pool, pool_stride}, x, perm_src, max_items, slot_base,
+                      slot_stride, H, I, hbuf, y, flags, seq, seq_dev, s);
 }
 
 bool ffn_combine_ok(int wfmt, int H, int I, int max_items, int T, int k) {

@@ -176,13 +176,14 @@ def test_device_fused_combine_bf16_output():
         store.close()
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["combine", "fused"])
+@pytest.mark.parametrize("fused", ["combine", "fused", "int4"])
 def test_graph_replay_equals_eager(fused):
     """Two identical device decoders over one pool: A steps eagerly, B replays one captured graph holding all
     layers; outputs and traces must agree bit for bit on every step, and both with the oracle's trace (with
-    the separate combine, and with the output formed in the down projection)."""
+    the separate combine, with the output formed in the down projection, and with int4 experts, whose two
+    projections run as one launch numbered by the resolve's device-side call counter)."""
     from routed_expert_layer_amd.runtime import DeviceDecodeLayer
-    cfg = fused_bf16(1024) if fused else small_bf16(6)
+    cfg = {"combine": small_bf16(6), "fused": fused_bf16(1024), "int4": small_int4()}[fused]
     steps = 24
     store = make_store(cfg)
     try:
