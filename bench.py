@@ -96,6 +96,8 @@ def decode_ffn_digest(root):
              _definition(ffn, "hipError_t decode_kernels("), _definition(ffn, "struct ArgWork"),
              _definition(ffn, "struct DevList"), _definition(ffn, "struct DevHits"),
              _definition(ffn, "struct DevWork"), _definition(ffn, "f32x4_t bf16_wave_dot("),
+             _definition(ffn, "struct PlainLoad"), _definition(ffn, "void bf16_ffn1_tile("),
+             _definition(ffn, "void bf16_ffn2_tile("),
              _definition(ffn, "void st16("), ffn[ffn.index("constexpr int kU ="):].split("\n", 1)[0],
              _definition(hdr, "struct WorkArgs"), _definition(hdr, "inline BlobLayout blob_layout("),
              hdr[hdr.index("constexpr int kFuseItems ="):].split("\n", 1)[0]]

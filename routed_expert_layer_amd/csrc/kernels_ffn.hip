@@ -166,14 +166,30 @@ __global__ __launch_bounds__(256) void ffn2_f32_kernel(const float* __restrict__
 // ---------------------------------------------------------------------------
 constexpr int kU = 8;  // fragments in flight per wave
 
+// How a decode kernel reads its 16-byte activation fragments: plain loads, or loads coherent across the
+// device's XCDs (for SwiGLU products another block of the same launch has just written through).
+struct PlainLoad {
+  __device__ __forceinline__ u32x4_t operator()(const uint16_t* p) const { return ld16(p); }
+};
+struct CoherentLoad {
+  const uint16_t* base;  // wave-uniform; every address read lies within 2^32 bytes above it
+  __device__ __forceinline__ u32x4_t operator()(const uint16_t* p) const {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, -1, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((const char*)p - (const char*)base), 0,
+                                                 16);  // sc1: device scope
+  }
+};
+
+
 // One wave's share of a tile: the sum over fragments [c0, c1) (1 KiB apart
 // from wp) of each fragment times the activation fragment at ar + 32c. With
 // WT every weight fragment is also stored at the same offset from fp (the
 // write-through of a miss); the stores follow each batch's loads, and the
 // variant without them keeps its loads free to move.
-template <bool WT>
+template <bool WT, typename ALoad = PlainLoad>
 __device__ __forceinline__ f32x4_t bf16_wave_dot(const char* wp, char* fp, const uint16_t* ar, bool valid, int c0,
-                                                 int c1) {
+                                                 int c1, ALoad aload = ALoad()) {
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   int c = c0;
   for (; c + kU <= c1; c += kU) {
@@ -181,7 +197,7 @@ __device__ __forceinline__ f32x4_t bf16_wave_dot(const char* wp, char* fp, const
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       a[u] = ld16_nt(wp + (size_t)(c + u) * 1024);
-      b[u] = valid ? ld16(ar + (c + u) * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      b[u] = valid ? aload(ar + (c + u) * 32) : u32x4_t{0u, 0u, 0u, 0u};
     }
     if constexpr (WT) {
 #pragma unroll
@@ -200,7 +216,7 @@ __device__ __forceinline__ f32x4_t bf16_wave_dot(const char* wp, char* fp, const
     for (int u = 0; u < kU; ++u) {
       const int cu = c + (u < n ? u : n - 1);
       a[u] = ld16_nt(wp + (size_t)cu * 1024);
-      b[u] = (valid && u < n) ? ld16(ar + cu * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      b[u] = (valid && u < n) ? aload(ar + cu * 32) : u32x4_t{0u, 0u, 0u, 0u};
     }
     if constexpr (WT) {
 #pragma unroll
@@ -215,16 +231,12 @@ __device__ __forceinline__ f32x4_t bf16_wave_dot(const char* wp, char* fp, const
 }
 
 // Gate/up: workgroup = one 16-row tile of P1 (8 gate + 8 up columns) of one
-// item; wave w reduces fragments [KC*w/4, KC*(w+1)/4).
-template <typename W>
-__global__ __launch_bounds__(256) void ffn1_decode_bf16(const uint16_t* __restrict__ x,
-                                                        const int32_t* __restrict__ perm_src, const W wk,
-                                                        const char* __restrict__ slot_base, size_t slot_stride, int H,
-                                                        int I, uint16_t* __restrict__ hbuf) {
-  const int NT = I / 8;
-  const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
-  int4 it;
-  if (!wk.get(item, it)) return;
+// item; wave w reduces fragments [KC*w/4, KC*(w+1)/4). Each row's pair of
+// SwiGLU products (two bf16 in one word) goes to store(address, word).
+template <typename W, typename Store, typename ALoad = PlainLoad>
+__device__ __forceinline__ void bf16_ffn1_tile(const uint16_t* x, const int32_t* perm_src, const W& wk, int item,
+                                               const int4& it, int tile, const char* slot_base, size_t slot_stride,
+                                               int H, int I, uint16_t* hbuf, Store store, ALoad aload = ALoad()) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KC = H / 32;
   const int c0 = (KC * wave) >> 2, c1 = (KC * (wave + 1)) >> 2;
@@ -238,8 +250,8 @@ __global__ __launch_bounds__(256) void ffn1_decode_bf16(const uint16_t* __restri
     const int m = m0 + (lane & 15);
     const bool valid = m < it.z;
     const uint16_t* xr = x + (size_t)(valid ? perm_src[it.y + m] : 0) * H + kq;
-    const f32x4_t acc =
-        fp ? bf16_wave_dot<true>(wp, fp, xr, valid, c0, c1) : bf16_wave_dot<false>(wp, nullptr, xr, valid, c0, c1);
+    const f32x4_t acc = fp ? bf16_wave_dot<true>(wp, fp, xr, valid, c0, c1, aload)
+                           : bf16_wave_dot<false>(wp, nullptr, xr, valid, c0, c1, aload);
     red[wave][lane] = acc;
     __syncthreads();
     if (wave == 0 && valid) {
@@ -247,21 +259,17 @@ __global__ __launch_bounds__(256) void ffn1_decode_bf16(const uint16_t* __restri
       const int i0 = 8 * tile + 2 * (lane >> 4);
       const uint32_t packed =
           (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
-      *reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0) = packed;
+      store(reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0), packed);
     }
     __syncthreads();
   }
 }
 
 // Down projection: workgroup = one 16-row tile of P2 (16 output columns).
-template <typename W>
-__global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restrict__ hbuf, const W wk,
-                                                        const char* __restrict__ slot_base, size_t slot_stride,
-                                                        size_t p2_off, int H, int I, float* __restrict__ y) {
-  const int NT = H / 16;
-  const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
-  int4 it;
-  if (!wk.get(item, it)) return;
+template <typename W, typename ALoad = PlainLoad>
+__device__ __forceinline__ void bf16_ffn2_tile(const uint16_t* hbuf, const W& wk, int item, const int4& it, int tile,
+                                               const char* slot_base, size_t slot_stride, size_t p2_off, int H,
+                                               int I, float* y, ALoad aload = ALoad()) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KC = I / 32;
   const int c0 = (KC * wave) >> 2, c1 = (KC * (wave + 1)) >> 2;
@@ -275,8 +283,8 @@ __global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restri
     const int m = m0 + (lane & 15);
     const bool valid = m < it.z;
     const uint16_t* hr = hbuf + (size_t)(it.y + (valid ? m : 0)) * I + kq;
-    const f32x4_t acc =
-        fp ? bf16_wave_dot<true>(wp, fp, hr, valid, c0, c1) : bf16_wave_dot<false>(wp, nullptr, hr, valid, c0, c1);
+    const f32x4_t acc = fp ? bf16_wave_dot<true>(wp, fp, hr, valid, c0, c1, aload)
+                           : bf16_wave_dot<false>(wp, nullptr, hr, valid, c0, c1, aload);
     red[wave][lane] = acc;
     __syncthreads();
     if (wave == 0 && valid) {
@@ -285,6 +293,30 @@ __global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restri
     }
     __syncthreads();
   }
+}
+
+template <typename W>
+__global__ __launch_bounds__(256) void ffn1_decode_bf16(const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ perm_src, const W wk,
+                                                        const char* __restrict__ slot_base, size_t slot_stride, int H,
+                                                        int I, uint16_t* __restrict__ hbuf) {
+  const int NT = I / 8;
+  const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
+  int4 it;
+  if (!wk.get(item, it)) return;
+  bf16_ffn1_tile(x, perm_src, wk, item, it, tile, slot_base, slot_stride, H, I, hbuf,
+                 [](uint32_t* p, uint32_t v) { *p = v; });
+}
+
+template <typename W>
+__global__ __launch_bounds__(256) void ffn2_decode_bf16(const uint16_t* __restrict__ hbuf, const W wk,
+                                                        const char* __restrict__ slot_base, size_t slot_stride,
+                                                        size_t p2_off, int H, int I, float* __restrict__ y) {
+  const int NT = H / 16;
+  const int item = blockIdx.x / NT, tile = blockIdx.x - item * NT;
+  int4 it;
+  if (!wk.get(item, it)) return;
+  bf16_ffn2_tile(hbuf, wk, item, it, tile, slot_base, slot_stride, p2_off, H, I, y);
 }
 
 // Down projection and weighted combine of up to kFuseItems resident experts,
@@ -398,21 +430,6 @@ __global__ __launch_bounds__(1024) void ffn2_combine_bf16(const uint16_t* __rest
 // the biased codes, u the block's sum of the activations -- times that
 // block's fp16 scale).
 // ---------------------------------------------------------------------------
-
-// How a quantised kernel reads its 16-byte activation fragments: plain loads, or loads coherent across the
-// device's XCDs (for SwiGLU products another block of the same launch has just written through).
-struct PlainLoad {
-  __device__ __forceinline__ u32x4_t operator()(const uint16_t* p) const { return ld16(p); }
-};
-struct CoherentLoad {
-  const uint16_t* base;  // wave-uniform; every address read lies within 2^32 bytes above it
-  __device__ __forceinline__ u32x4_t operator()(const uint16_t* p) const {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, -1, 0x00020000);
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)((const char*)p - (const char*)base), 0,
-                                                 16);  // sc1: device scope
-  }
-};
 
 // The registers of one 128-wide K block: activation fragments, and the codes
 // and the four rows' scales of each of the block's kRI tiles.
@@ -710,10 +727,12 @@ __global__ __launch_bounds__(256) void ffn2_decode_mxfp4(const uint16_t* __restr
     mxfp4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit);
 }
 
-// Both projections of a quantised decode step (int4: WF 2, MXFP4: WF 3) in one
-// launch, for lists of resident experts: blocks [0, G1) (G1 = max_items * NB1)
-// run the gate/up tile groups as ffn1_decode_*, the others the down-projection
-// groups as ffn2_decode_*. A gate/up block, once its SwiGLU products are
+// Both projections of a decode step (bf16: WF 1, one tile per block; int4: WF
+// 2 and MXFP4: WF 3, four) in one launch, for experts listed in device memory:
+// blocks [0, G1) (G1 = max_items * NB1) run the gate/up tile groups as
+// ffn1_decode_*, the others the down-projection groups as ffn2_decode_*. With
+// a write-through work source, misses are read from the pool and stored into
+// their slots as in those kernels. A gate/up block, once its SwiGLU products are
 // stored, marks its group done for this call (flags[item * NB1 + group] =
 // seq); a down-projection block waits until every group of its item carries
 // seq and then reads the products. Products and flags are written and read
@@ -726,34 +745,24 @@ __global__ __launch_bounds__(256) void ffn2_decode_mxfp4(const uint16_t* __restr
 // The launch saves the second launch's start-up and lets down-projection
 // blocks start while the gate/up tail drains.
 constexpr int kQuantTiles = 4;  // tiles per block of both quantised kernels (kRI, kR)
+// The gate/up part of one block (tile group `group` of item `item`) of ffn_decode_fused, its SwiGLU products
+// stored with device-scope stores.
 template <int WF, typename W>
-__global__ __launch_bounds__(256) void ffn_decode_fused(const uint16_t* __restrict__ x,
-                                                        const int32_t* __restrict__ perm_src, const W wk,
-                                                        int max_items, const char* __restrict__ slot_base,
-                                                        size_t slot_stride, size_t p1s_off, size_t p2_off,
-                                                        size_t p2s_off, int H, int I, uint16_t* hbuf,
-                                                        float* __restrict__ y, uint32_t* flags, uint32_t seq_arg,
-                                                        const uint64_t* seq_dev) {
-  static_assert(kRI == kQuantTiles && kR == kQuantTiles, "one tile-group size for both formats");
-  // the call's flag value: given, or from a counter in device memory that each call's earlier work advances
-  // (never 0, the flags' initial value)
-  const uint32_t seq = seq_dev != nullptr ? (uint32_t)(*seq_dev % 0xFFFFFFFFull) + 1u : seq_arg;
-  const int NB1 = I / 8 / kQuantTiles, NB2 = H / 16 / kQuantTiles;
-  const int G1 = max_items * NB1;
-  const int lane = threadIdx.x & 63;
-  int4 it;
-  char* fill;
-  if ((int)blockIdx.x < G1) {
-    const int item = blockIdx.x / NB1, group = blockIdx.x - item * NB1;
-    if (!wk.get(item, it)) return;
+__device__ __forceinline__ void fused_gate_up(const uint16_t* x, const int32_t* perm_src, const W& wk, int item,
+                                              const int4& it, int group, const char* slot_base, size_t slot_stride,
+                                              size_t p1s_off, int H, int I, uint16_t* hbuf) {
+  const auto store = [](uint32_t* p, uint32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  if constexpr (WF == 1) {
+    bf16_ffn1_tile(x, perm_src, wk, item, it, group, slot_base, slot_stride, H, I, hbuf, store);
+  } else {
+    const int lane = threadIdx.x & 63;
+    char* fill;
     const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
     const auto row = [&](int m) { return x + (size_t)perm_src[it.y + m] * H; };
     const auto emit = [&](int tile, int m, const f32x4_t& s) {
       const int i0 = 8 * tile + 2 * (lane >> 4);
-      const uint32_t packed =
-          (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16);
-      __hip_atomic_store(reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0), packed, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      store(reinterpret_cast<uint32_t*>(hbuf + (size_t)(it.y + m) * I + i0),
+            (uint32_t)f32_to_bf16(silu(s[0]) * s[1]) | ((uint32_t)f32_to_bf16(silu(s[2]) * s[3]) << 16));
     };
     const int tile0 = group * kQuantTiles;
     if constexpr (WF == 2) {
@@ -767,6 +776,62 @@ __global__ __launch_bounds__(256) void ffn_decode_fused(const uint16_t* __restri
       else
         mxfp4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, tile0, emit);
     }
+  }
+}
+
+// The down-projection part of one block of ffn_decode_fused, the products read with device-scope loads.
+template <int WF, typename W>
+__device__ __forceinline__ void fused_down(const W& wk, int item, const int4& it, int group, const char* slot_base,
+                                           size_t slot_stride, size_t p2_off, size_t p2s_off, int H, int I,
+                                           const uint16_t* hbuf, float* y) {
+  const CoherentLoad coh{hbuf};
+  if constexpr (WF == 1) {
+    bf16_ffn2_tile(hbuf, wk, item, it, group, slot_base, slot_stride, p2_off, H, I, y, coh);
+  } else {
+    const int lane = threadIdx.x & 63;
+    char* fill;
+    const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
+    const auto row = [&](int m) { return hbuf + (size_t)(it.y + m) * I; };
+    const auto emit = [&](int tile, int m, const f32x4_t& s) {
+      *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
+    };
+    const int tile0 = group * kQuantTiles;
+    if constexpr (WF == 2) {
+      if (W::kMayFill && fill != nullptr)
+        int4_decode_tiles<true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0,
+                                emit, coh);
+      else
+        int4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit, coh);
+    } else {
+      if (W::kMayFill && fill != nullptr)
+        mxfp4_decode_tiles<true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0,
+                                 emit, coh);
+      else
+        mxfp4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit, coh);
+    }
+  }
+}
+
+template <int WF, typename W>
+__global__ __launch_bounds__(256) void ffn_decode_fused(const uint16_t* __restrict__ x,
+                                                        const int32_t* __restrict__ perm_src, const W wk,
+                                                        int max_items, const char* __restrict__ slot_base,
+                                                        size_t slot_stride, size_t p1s_off, size_t p2_off,
+                                                        size_t p2s_off, int H, int I, uint16_t* hbuf,
+                                                        float* __restrict__ y, uint32_t* flags, uint32_t seq_arg,
+                                                        const uint64_t* seq_dev) {
+  static_assert(kRI == kQuantTiles && kR == kQuantTiles, "one tile-group size for both 4-bit formats");
+  // the call's flag value: given, or from a counter in device memory that each call's earlier work advances
+  // (never 0, the flags' initial value)
+  const uint32_t seq = seq_dev != nullptr ? (uint32_t)(*seq_dev % 0xFFFFFFFFull) + 1u : seq_arg;
+  constexpr int TPB = WF == 1 ? 1 : kQuantTiles;  // tiles per block
+  const int NB1 = I / 8 / TPB, NB2 = H / 16 / TPB;
+  const int G1 = max_items * NB1;
+  int4 it;
+  if ((int)blockIdx.x < G1) {
+    const int item = blockIdx.x / NB1, group = blockIdx.x - item * NB1;
+    if (!wk.get(item, it)) return;
+    fused_gate_up<WF>(x, perm_src, wk, item, it, group, slot_base, slot_stride, p1s_off, H, I, hbuf);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's product stores have completed
     __syncthreads();                // ... and every wave's
     if (threadIdx.x == 0)
@@ -775,8 +840,8 @@ __global__ __launch_bounds__(256) void ffn_decode_fused(const uint16_t* __restri
   }
   const int b2 = blockIdx.x - G1, item = b2 / NB2, group = b2 - item * NB2;
   if (!wk.get(item, it)) return;
-  const char* blob = wk.src(item, it, slot_base, slot_stride, fill);
   if (threadIdx.x < 64) {  // one wave polls the item's gate/up groups
+    const int lane = threadIdx.x;
     for (int spin = 0; spin < (1 << 18); ++spin) {
       bool done = true;
       for (int j = lane; j < NB1; j += 64)
@@ -786,25 +851,7 @@ __global__ __launch_bounds__(256) void ffn_decode_fused(const uint16_t* __restri
     }
   }
   __syncthreads();
-  const auto row = [&](int m) { return hbuf + (size_t)(it.y + m) * I; };
-  const auto emit = [&](int tile, int m, const f32x4_t& s) {
-    *reinterpret_cast<f32x4_t*>(y + (size_t)(it.y + m) * H + 16 * tile + 4 * (lane >> 4)) = s;
-  };
-  const CoherentLoad coh{hbuf};
-  const int tile0 = group * kQuantTiles;
-  if constexpr (WF == 2) {
-    if (W::kMayFill && fill != nullptr)
-      int4_decode_tiles<true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0, emit,
-                              coh);
-    else
-      int4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit, coh);
-  } else {
-    if (W::kMayFill && fill != nullptr)
-      mxfp4_decode_tiles<true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0, emit,
-                               coh);
-    else
-      mxfp4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit, coh);
-  }
+  fused_down<WF>(wk, item, it, group, slot_base, slot_stride, p2_off, p2s_off, H, I, hbuf, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -1019,13 +1066,15 @@ hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_sr
                         max_rows, slot_base, slot_stride, H, I, hbuf, y, s);
 }
 
-// int4 only: the MXFP4 kernels load each K block's activations when they use it, and with the products read
-// past the XCD caches that wait slowed the one-launch MXFP4 FFN (42.8 vs 40.5 us per 8-token step).
+// bf16 and int4; not MXFP4: its kernels load each K block's activations when they use it, and with the
+// products read past the XCD caches that wait slowed the one-launch MXFP4 FFN (42.8 vs 40.5 us per 8-token
+// step).
 bool ffn_fused_ok(int wfmt, int H, int I) {
+  if (wfmt == 1) return H % 32 == 0 && I % 32 == 0;
   return wfmt == 2 && H % (16 * kQuantTiles) == 0 && I % (8 * kQuantTiles) == 0;
 }
 
-size_t ffn_fused_flags(int max_items, int I) { return (size_t)max_items * (I / 8 / kQuantTiles); }
+size_t ffn_fused_flags(int max_items, int I) { return (size_t)max_items * (I / 8); }
 
 namespace {
 
@@ -1034,8 +1083,13 @@ hipError_t fused_kernel(int wfmt, const W& wk, const void* x, const int32_t* per
                         const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y, uint32_t* flags,
                         uint32_t seq, const uint64_t* seq_dev, hipStream_t s) {
   const BlobLayout L = blob_layout(wfmt, H, I);
-  const dim3 grid(max_items * (I / 8 / kQuantTiles + H / 16 / kQuantTiles));
-  if (wfmt == 2)
+  const int tpb = wfmt == 1 ? 1 : kQuantTiles;
+  const dim3 grid(max_items * (I / 8 / tpb + H / 16 / tpb));
+  if (wfmt == 1)
+    hipLaunchKernelGGL((ffn_decode_fused<1, W>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), perm_src, wk,
+                       max_items, slot_base, slot_stride, L.p1s, L.p2, L.p2s, H, I, static_cast<uint16_t*>(hbuf), y,
+                       flags, seq, seq_dev);
+  else if (wfmt == 2)
     hipLaunchKernelGGL((ffn_decode_fused<2, W>), grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), perm_src, wk,
                        max_items, slot_base, slot_stride, L.p1s, L.p2, L.p2s, H, I, static_cast<uint16_t*>(hbuf), y,
                        flags, seq, seq_dev);
