@@ -442,11 +442,11 @@ int moe_clock_record(unsigned long long* sums);
  *   8 experts in the step (min(E, k*T) <= 8) and I a multiple of 512 up to
  *   2048, the resident experts' down projection also writes `out` when no
  *   expert of the step is missing (the combine's sum, in its order), and no
- *   combine is launched; y_perm still receives every row. With int4 weights
- *   the resident experts' two projections run as one launch whose
- *   down-projection blocks wait, through flags the decoder owns, for their
- *   expert's gate/up blocks (so one decoder's steps must stay ordered on one
- *   stream).
+ *   combine is launched; y_perm still receives every row. Otherwise (bf16,
+ *   int4 and MXFP4 weights) the resident experts' two projections run as one
+ *   launch whose down-projection blocks wait, through flags the decoder
+ *   owns, for their expert's gate/up blocks (so one decoder's steps must
+ *   stay ordered on one stream).
  *   out_dtype other than MOE_DT_F32 / MOE_DT_BF16 is MOE_EINVAL.
  *   When the cache splits misses (moe_cache_set_split), the misses assigned
  *   to the CPU run with moe_cpu_ffn from the pool on the calling thread while
@@ -581,8 +581,9 @@ int moe_cpu_threads(void);
  *   formed by the down projection itself, with no combine launch). For
  *   bf16, int4 and MXFP4 experts the FFN reads each hit from its slot and
  *   each miss from the pool over the host link, writing the miss's blob
- *   through into its slot as it goes (the fill; with int4 experts both
- *   projections run as one launch, numbered by the resolve's call counter);
+ *   through into its slot as it goes (the fill; both projections run as one
+ *   launch, numbered by the resolve's call counter, unless the down
+ *   projection forms `out`);
  *   for fp32 experts a fill
  *   kernel first copies the misses' blobs into their slots (returning at once
  *   when there are none) and the FFN then reads every item from its slot.

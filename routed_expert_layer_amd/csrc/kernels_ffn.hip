@@ -626,7 +626,7 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_floa
 // tile sums go to `emit(tile, m, sum)`. With WT every code and scale loaded
 // is also stored at the same offset from qf_base / sf_base (the write-through
 // of a miss), after each K block's loads.
-template <bool WT, typename Row, typename Emit, typename ALoad = PlainLoad>
+template <bool WT, bool PIPE = false, typename Row, typename Emit, typename ALoad = PlainLoad>
 __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, int K, const char* q_base,
                                                    const char* s_base, char* qf_base, char* sf_base, int tile0,
                                                    Emit emit, ALoad aload = ALoad()) {
@@ -634,6 +634,8 @@ __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, i
   const int KG = K / 128;
   const int g0 = (KG * wave) >> 2, g1 = (KG * (wave + 1)) >> 2;
   const int kq = (lane >> 4) * 8;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(uniform(q_base), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(uniform(s_base), (short)0, -1, 0x00020000);
   __shared__ f32x4_t red[4][kR][64];
   for (int m0 = 0; m0 < it.z; m0 += 16) {
     const int m = m0 + (lane & 15);
@@ -642,32 +644,84 @@ __device__ __forceinline__ void mxfp4_decode_tiles(Row act_row, const int4 it, i
     f32x4_t acc[kR];
 #pragma unroll
     for (int r = 0; r < kR; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int g = g0; g < g1; ++g) {
+    // one K block's activation fragments, codes and scales; with PIPE the next block's are loaded before the
+    // current one is used (the one-launch FFN, whose down projection reads its activations past the L2)
+    struct Stage {
       u32x4_t b[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = valid ? aload(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
       u32x4_t a[kR];
       uint32_t sc[kR];
+    };
+    // codes and scales through buffer resources (a lane offset in a vector register, the block offsets in
+    // scalar registers), so two stages of loads cost few address registers
+    auto load = [&](int g, Stage& st) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.b[j] = valid ? aload(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int r = 0; r < kR; ++r) {
-        const size_t blk = (size_t)(tile0 + r) * KG + g;
-        a[r] = ld16_nt(q_base + blk * 1024 + lane * 16);
-        sc[r] = *reinterpret_cast<const uint32_t*>(s_base + blk * 64 + (lane & 15) * 4);
+        const int blk = (tile0 + r) * KG + g;
+        st.a[r] = __builtin_amdgcn_raw_buffer_load_b128(rq, lane * 16, blk * 1024, 2);  // non-temporal
+        st.sc[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane & 15) * 4, blk * 64, 0);
       }
       if constexpr (WT) {  // codes by every lane, the scale block by lanes 0..15
+        const __amdgpu_buffer_rsrc_t wq =
+            __builtin_amdgcn_make_buffer_rsrc(uniform(qf_base), (short)0, -1, 0x00020000);
+        const __amdgpu_buffer_rsrc_t ws =
+            __builtin_amdgcn_make_buffer_rsrc(uniform(sf_base), (short)0, -1, 0x00020000);
 #pragma unroll
         for (int r = 0; r < kR; ++r) {
-          const size_t blk = (size_t)(tile0 + r) * KG + g;
-          st16(qf_base + blk * 1024 + lane * 16, a[r]);
-          if (lane < 16) *reinterpret_cast<uint32_t*>(sf_base + blk * 64 + lane * 4) = sc[r];
+          const int blk = (tile0 + r) * KG + g;
+          __builtin_amdgcn_raw_buffer_store_b128(st.a[r], wq, lane * 16, blk * 1024, 0);
+          if (lane < 16) __builtin_amdgcn_raw_buffer_store_b32(st.sc[r], ws, lane * 4, blk * 64, 0);
         }
         drain_memory();
       }
+    };
+    auto compute = [&](const Stage& st) {
 #pragma unroll
       for (int r = 0; r < kR; ++r)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[r] = mfma_bf16(fp4x8_to_bf16x8(a[r][j], e8m0_to_f32(sc[r] >> (8 * j))), b[j], acc[r]);
+          acc[r] = mfma_bf16(fp4x8_to_bf16x8(st.a[r][j], e8m0_to_f32(st.sc[r] >> (8 * j))), st.b[j], acc[r]);
+    };
+    if constexpr (PIPE) {
+      Stage s0, s1;
+      int g = g0;
+      if (g < g1) load(g, s0);
+      for (; g + 1 < g1; g += 2) {
+        load(g + 1, s1);
+        compute(s0);
+        if (g + 2 < g1) load(g + 2, s0);
+        compute(s1);
+      }
+      if (g < g1) compute(s0);
+    } else {  // one stage through plain loads (four waves per SIMD; faster here than buffer loads)
+      for (int g = g0; g < g1; ++g) {
+        u32x4_t b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = valid ? aload(ar + 128 * g + 32 * j) : u32x4_t{0u, 0u, 0u, 0u};
+        u32x4_t a[kR];
+        uint32_t sc[kR];
+#pragma unroll
+        for (int r = 0; r < kR; ++r) {
+          const size_t blk = (size_t)(tile0 + r) * KG + g;
+          a[r] = ld16_nt(q_base + blk * 1024 + lane * 16);
+          sc[r] = *reinterpret_cast<const uint32_t*>(s_base + blk * 64 + (lane & 15) * 4);
+        }
+        if constexpr (WT) {  // codes by every lane, the scale block by lanes 0..15
+#pragma unroll
+          for (int r = 0; r < kR; ++r) {
+            const size_t blk = (size_t)(tile0 + r) * KG + g;
+            st16(qf_base + blk * 1024 + lane * 16, a[r]);
+            if (lane < 16) *reinterpret_cast<uint32_t*>(sf_base + blk * 64 + lane * 4) = sc[r];
+          }
+          drain_memory();
+        }
+#pragma unroll
+        for (int r = 0; r < kR; ++r)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[r] = mfma_bf16(fp4x8_to_bf16x8(a[r][j], e8m0_to_f32(sc[r] >> (8 * j))), b[j], acc[r]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < kR; ++r) red[wave][r][lane] = acc[r];
@@ -772,9 +826,9 @@ __device__ __forceinline__ void fused_gate_up(const uint16_t* x, const int32_t* 
         int4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, tile0, emit);
     } else {
       if (W::kMayFill && fill != nullptr)
-        mxfp4_decode_tiles<true>(row, it, H, blob, blob + p1s_off, fill, fill + p1s_off, tile0, emit);
+        mxfp4_decode_tiles<true, true>(row, it, H, blob, blob + p1s_off, fill, fill + p1s_off, tile0, emit);
       else
-        mxfp4_decode_tiles<false>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, tile0, emit);
+        mxfp4_decode_tiles<false, true>(row, it, H, blob, blob + p1s_off, nullptr, nullptr, tile0, emit);
     }
   }
 }
@@ -804,10 +858,11 @@ __device__ __forceinline__ void fused_down(const W& wk, int item, const int4& it
         int4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit, coh);
     } else {
       if (W::kMayFill && fill != nullptr)
-        mxfp4_decode_tiles<true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off, tile0,
-                                 emit, coh);
+        mxfp4_decode_tiles<true, true>(row, it, I, blob + p2_off, blob + p2s_off, fill + p2_off, fill + p2s_off,
+                                       tile0, emit, coh);
       else
-        mxfp4_decode_tiles<false>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit, coh);
+        mxfp4_decode_tiles<false, true>(row, it, I, blob + p2_off, blob + p2s_off, nullptr, nullptr, tile0, emit,
+                                        coh);
     }
   }
 }
@@ -1066,12 +1121,9 @@ hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_sr
                         max_rows, slot_base, slot_stride, H, I, hbuf, y, s);
 }
 
-// bf16 and int4; not MXFP4: its kernels load each K block's activations when they use it, and with the
-// products read past the XCD caches that wait slowed the one-launch MXFP4 FFN (42.8 vs 40.5 us per 8-token
-// step).
 bool ffn_fused_ok(int wfmt, int H, int I) {
   if (wfmt == 1) return H % 32 == 0 && I % 32 == 0;
-  return wfmt == 2 && H % (16 * kQuantTiles) == 0 && I % (8 * kQuantTiles) == 0;
+  return (wfmt == 2 || wfmt == 3) && H % (16 * kQuantTiles) == 0 && I % (8 * kQuantTiles) == 0;
 }
 
 size_t ffn_fused_flags(int max_items, int I) { return (size_t)max_items * (I / 8); }
