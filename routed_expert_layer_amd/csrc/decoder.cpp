@@ -76,8 +76,8 @@ struct moe_decoder {
   moe::SlotUpdates pending{};      // updates for the GPU copy, applied by the next routing launch
   int32_t* hit_n = nullptr;        // device: number of resident-expert items
   int4* hit_items = nullptr;       // device: [E] items {slot, first row, rows, expert}
-  uint32_t* ffn_flags = nullptr;   // device: hand-off flags of the one-launch quantised FFN (zeroed at creation)
-  uint32_t ffn_seq = 0;            // the last call's flag value
+  uint64_t* ffn_flags = nullptr;   // device: hand-off flags of the one-launch FFN (zeroed at creation)
+  uint64_t ffn_seq = 0;            // the last call's flag value
   int n_layers = 0;
 };
 
@@ -152,7 +152,7 @@ moe_decoder_t* moe_decoder_create(moe_cache_t* cache, int T_max, int H, int I, i
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&d->hit_n), 16 + sizeof(int4) * E);
   if (e == hipSuccess) d->hit_items = reinterpret_cast<int4*>(reinterpret_cast<char*>(d->hit_n) + 16);
   if (e == hipSuccess && moe::ffn_fused_ok(wfmt, H, I)) {
-    const size_t fb = sizeof(uint32_t) * moe::ffn_fused_flags(E, I);
+    const size_t fb = sizeof(uint64_t) * moe::ffn_fused_flags(E, I);
     e = hipMalloc(reinterpret_cast<void**>(&d->ffn_flags), fb);
     if (e == hipSuccess) e = hipMemset(d->ffn_flags, 0, fb);
   }
@@ -347,7 +347,7 @@ int moe_decoder_step(moe_decoder_t* d, int step, int layer, const void* x, int T
                                          b.y_perm, d->hit_n + 1, b.perm_pos, b.topk_w, d->k, out,
                                          out_dtype == MOE_DT_BF16, s);
     else if (e == hipSuccess && d->ffn_flags != nullptr) {
-      d->ffn_seq = d->ffn_seq == UINT32_MAX ? 1u : d->ffn_seq + 1u;
+      ++d->ffn_seq;
       e = moe::launch_ffn_decode_fused(d->wfmt, x, b.perm_src, d->hit_n, d->hit_items, std::min(d->E, d->k * T),
                                        static_cast<const char*>(d->slot_base), d->slot_stride, d->H, d->I, b.ffn_ws,
                                        b.y_perm, d->ffn_flags, d->ffn_seq, s);

@@ -34,7 +34,7 @@ struct moe_device_decoder {
   void* mem = nullptr;  // one device allocation holding the control data
   moe::DevCache c{};
   int max_items;
-  uint32_t* ffn_flags = nullptr;  // hand-off flags of the one-launch int4 FFN (zeroed at creation)
+  uint64_t* ffn_flags = nullptr;  // hand-off flags of the one-launch FFN (zeroed at creation)
 };
 
 namespace {
@@ -148,7 +148,7 @@ moe_device_decoder_t* moe_device_decoder_create(int L, int E, int S, int T_max, 
   e = hipMemset(m + o.slot_of, 0xFF, o.stamp - o.slot_of);
   if (e == hipSuccess) e = hipMemset(m + o.stamp, 0, o.trace - o.stamp);
   if (e == hipSuccess && moe::ffn_fused_ok(wfmt, H, I)) {
-    const size_t fb = sizeof(uint32_t) * moe::ffn_fused_flags(max_items, I);
+    const size_t fb = sizeof(uint64_t) * moe::ffn_fused_flags(max_items, I);
     e = hipMalloc(reinterpret_cast<void**>(&d->ffn_flags), fb);
     if (e == hipSuccess) e = hipMemset(d->ffn_flags, 0, fb);
   }

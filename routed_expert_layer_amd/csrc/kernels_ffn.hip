@@ -873,12 +873,12 @@ __global__ __launch_bounds__(256) void ffn_decode_fused(const uint16_t* __restri
                                                         int max_items, const char* __restrict__ slot_base,
                                                         size_t slot_stride, size_t p1s_off, size_t p2_off,
                                                         size_t p2s_off, int H, int I, uint16_t* hbuf,
-                                                        float* __restrict__ y, uint32_t* flags, uint32_t seq_arg,
+                                                        float* __restrict__ y, uint64_t* flags, uint64_t seq_arg,
                                                         const uint64_t* seq_dev) {
   static_assert(kRI == kQuantTiles && kR == kQuantTiles, "one tile-group size for both 4-bit formats");
-  // the call's flag value: given, or from a counter in device memory that each call's earlier work advances
-  // (never 0, the flags' initial value)
-  const uint32_t seq = seq_dev != nullptr ? (uint32_t)(*seq_dev % 0xFFFFFFFFull) + 1u : seq_arg;
+  // the call's flag value: given, or one above a counter in device memory that each call's earlier work
+  // advances (never 0, the flags' initial value; 64 bits, so it does not wrap)
+  const uint64_t seq = seq_dev != nullptr ? *seq_dev + 1u : seq_arg;
   constexpr int TPB = WF == 1 ? 1 : kQuantTiles;  // tiles per block
   const int NB1 = I / 8 / TPB, NB2 = H / 16 / TPB;
   const int G1 = max_items * NB1;
@@ -1132,8 +1132,8 @@ namespace {
 
 template <typename W>
 hipError_t fused_kernel(int wfmt, const W& wk, const void* x, const int32_t* perm_src, int max_items,
-                        const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y, uint32_t* flags,
-                        uint32_t seq, const uint64_t* seq_dev, hipStream_t s) {
+                        const char* slot_base, size_t slot_stride, int H, int I, void* hbuf, float* y, uint64_t* flags,
+                        uint64_t seq, const uint64_t* seq_dev, hipStream_t s) {
   const BlobLayout L = blob_layout(wfmt, H, I);
   const int tpb = wfmt == 1 ? 1 : kQuantTiles;
   const dim3 grid(max_items * (I / 8 / tpb + H / 16 / tpb));
@@ -1156,7 +1156,7 @@ hipError_t fused_kernel(int wfmt, const W& wk, const void* x, const int32_t* per
 
 hipError_t launch_ffn_decode_fused(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
                                    const int4* items, int max_items, const char* slot_base, size_t slot_stride, int H,
-                                   int I, void* hbuf, float* y, uint32_t* flags, uint32_t seq, hipStream_t s,
+                                   int I, void* hbuf, float* y, uint64_t* flags, uint64_t seq, hipStream_t s,
                                    const uint64_t* seq_dev, const int32_t* n_hit, const char* pool,
                                    size_t pool_stride) {
   if (!ffn_fused_ok(wfmt, H, I) || flags == nullptr || (seq == 0 && seq_dev == nullptr)) return hipErrorInvalidValue;

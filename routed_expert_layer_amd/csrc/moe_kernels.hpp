@@ -177,17 +177,17 @@ hipError_t launch_ffn_decode_dev(int wfmt, const void* x, const int32_t* perm_sr
 // Both projections of the quantised decode FFN of experts listed in device
 // memory, as launch_ffn_decode_dev (with or without `pool`), in one launch:
 // the down-projection blocks wait for their expert's gate/up blocks through
-// `flags` (device, ffn_fused_flags(max_items, I) words, zero before the first
-// call, owned by one caller whose calls are stream-ordered). Each call needs
-// a flag value no earlier call used: a nonzero `seq`, or with seq_dev set,
-// the value at seq_dev when the call runs (a counter the caller's earlier
-// work advances by one per call; any 64-bit value, mapped to a nonzero
-// 32-bit one). ffn_fused_ok tells whether a format and shape take this path.
+// `flags` (device, ffn_fused_flags(max_items, I) 64-bit words, zero before
+// the first call, owned by one caller whose calls are stream-ordered). Each
+// call needs a flag value no earlier call used: a nonzero `seq`, or with
+// seq_dev set, one above the value at seq_dev when the call runs (a counter
+// the caller's earlier work advances by one per call). ffn_fused_ok tells
+// whether a format and shape take this path.
 bool ffn_fused_ok(int wfmt, int H, int I);
 size_t ffn_fused_flags(int max_items, int I);
 hipError_t launch_ffn_decode_fused(int wfmt, const void* x, const int32_t* perm_src, const int32_t* n_items,
                                    const int4* items, int max_items, const char* slot_base, size_t slot_stride, int H,
-                                   int I, void* hbuf, float* y, uint32_t* flags, uint32_t seq, hipStream_t s,
+                                   int I, void* hbuf, float* y, uint64_t* flags, uint64_t seq, hipStream_t s,
                                    const uint64_t* seq_dev = nullptr, const int32_t* n_hit = nullptr,
                                    const char* pool = nullptr, size_t pool_stride = 0);
 // The bf16 decode FFN of the experts listed in device memory (at most
