@@ -786,8 +786,8 @@ __global__ __launch_bounds__(256) void ffn2_decode_mxfp4(const uint16_t* __restr
 // blocks [0, G1) (G1 = max_items * NB1) run the gate/up tile groups as
 // ffn1_decode_*, the others the down-projection groups as ffn2_decode_*. With
 // a write-through work source, misses are read from the pool and stored into
-// their slots as in those kernels. A gate/up block, once its SwiGLU products are
-// stored, marks its group done for this call (flags[item * NB1 + group] =
+// their slots as in those kernels. A gate/up block, once its SwiGLU products
+// are stored, marks its group done for this call (flags[item * NB1 + group] =
 // seq); a down-projection block waits until every group of its item carries
 // seq and then reads the products. Products and flags are written and read
 // with device-scope (sc1) accesses, so the hand-off holds whichever XCDs ran
@@ -799,6 +799,7 @@ __global__ __launch_bounds__(256) void ffn2_decode_mxfp4(const uint16_t* __restr
 // The launch saves the second launch's start-up and lets down-projection
 // blocks start while the gate/up tail drains.
 constexpr int kQuantTiles = 4;  // tiles per block of both quantised kernels (kRI, kR)
+
 // The gate/up part of one block (tile group `group` of item `item`) of ffn_decode_fused, its SwiGLU products
 // stored with device-scope stores.
 template <int WF, typename W>
